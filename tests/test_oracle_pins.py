@@ -1,0 +1,355 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test compares the oracle with something other than itself: printed
+figures, closed forms, library routines (numpy / scipy), brute force on tiny
+inputs, invariants, or special cases that reduce to a dense SwiGLU MLP.
+"""
+import itertools
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import moe_testutil as U
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def tiny_cfg(synth_mod, **kw):
+    base = dict(name="tiny", T=12, H=64, E=8, k=2, I=32, I_sh=48, seed=77)
+    base.update(kw)
+    return synth_mod.LayerConfig(**base)
+
+
+def make(synth_mod, oracle_mod, cfg):
+    d = synth_mod.layer(cfg)
+    return d, oracle_mod.LayerWeights(cfg, d)
+
+
+# ------------------------------------------------------------------ formats
+
+def test_int4_nibble_order_golden(oracle_mod):
+    g = _gold("int4_nibble_order.json")
+    for case in g["cases"]:
+        vals = oracle_mod.unpack_int4_row(np.array([case["byte"]], np.uint8), 2)
+        assert list(vals) == case["elements"], case
+        assert oracle_mod.pack_int4_row(np.array(case["elements"]))[0] == case["byte"]
+
+
+def test_int4_pack_unpack_exhaustive(oracle_mod):
+    allb = np.arange(256, dtype=np.uint8)
+    vals = oracle_mod.unpack_int4_row(allb, 512)
+    assert np.array_equal(oracle_mod.pack_int4_row(vals), allb)
+    pairs = np.array([(a, b) for a in range(-8, 8) for b in range(-8, 8)], np.int32).ravel()
+    assert np.array_equal(oracle_mod.unpack_int4_row(oracle_mod.pack_int4_row(pairs), pairs.size), pairs)
+    # the numpy decoder of the tests agrees with the oracle's on every byte
+    assert np.array_equal(U.unpack_int4(allb, 512).astype(np.int32), vals)
+
+
+def test_int8_dequant_all_values(oracle_mod):
+    q = np.arange(-128, 128, dtype=np.int8)
+    out = oracle_mod.dequant_row(q, 8, 0.25, 256)
+    assert np.array_equal(out, q.astype(np.float32) * np.float32(0.25))
+
+
+def test_int4_dequant_is_product(oracle_mod):
+    q = np.arange(256, dtype=np.uint8)
+    s = np.float32(0.0037)
+    out = oracle_mod.dequant_row(q, 4, float(s), 512)
+    assert np.array_equal(out, U.unpack_int4(q, 512).astype(np.float32) * s)
+
+
+def test_bf16_rne_golden(oracle_mod):
+    for case in _gold("bf16_rne.json")["cases"]:
+        f = np.array([int(case["f32_bits"], 16)], np.uint32).view(np.float32)[0]
+        assert oracle_mod.f32_to_bf16(float(f)) == int(case["bf16_bits"], 16), case
+    for bits in (0x3F80, 0xC0A0, 0x0001, 0x7F7F):
+        assert np.float32(oracle_mod.bf16_to_f32(bits)) == U.bf16_to_f32(np.array([bits]))[0]
+
+
+def test_page_byte_figures(synth_mod):
+    """Byte accounting of the packed format against the pages' printed sizes."""
+    g = _gold("page_figures.json")
+    ge = g["glm_expert"]
+    cfg = synth_mod.CONFIGS["c3"]
+    q_bytes = 3 * cfg.H * cfg.I // 2
+    assert (cfg.H, cfg.I) == (ge["H"], ge["I"])
+    assert abs(q_bytes / 1e6 - ge["approx_MB"]) / ge["approx_MB"] < ge["rel_tol"]
+    per_expert = q_bytes + 4 * (2 * cfg.I + cfg.H)
+    cr = g["glm_cold_read"]
+    tok = cr["layers"] * cr["experts_per_layer"] * per_expert
+    assert abs(tok / 1e9 - cr["approx_GB"]) / cr["approx_GB"] < cr["rel_tol"]
+    rc = g["glm_routed_expert_count"]
+    assert rc["layers"] * rc["experts_per_layer"] + rc["mtp_head_experts"] == rc["count"]
+    # Nano: the int4 routed experts plus the int8 shared experts fit inside the
+    # ~1.4 GB container and the rest is the ~0.3 GB resident dense part.
+    nc = g["nano_container"]
+    c0 = synth_mod.CONFIGS["c0"]
+    assert (c0.H, c0.E, c0.I, c0.I_sh) == (nc["H"], nc["E"], nc["I"], nc["I_shared"])
+    routed = nc["moe_layers"] * c0.E * (3 * c0.H * c0.I // 2 + 4 * (2 * c0.I + c0.H))
+    shared8 = nc["moe_layers"] * (3 * c0.H * c0.I_sh + 4 * (2 * c0.I_sh + c0.H))
+    assert routed + shared8 < nc["container_GB"] * 1e9
+    assert routed > (nc["container_GB"] - nc["resident_GB"]) * 1e9 * 0.95
+    # the synthetic layer has exactly that many bytes
+    d = synth_mod.experts(c0.with_(E=2))
+    assert d[0].nbytes + d[1].nbytes == 2 * (3 * c0.H * c0.I // 2 + 4 * (2 * c0.I + c0.H))
+
+
+# ------------------------------------------------------------------- router
+
+def test_router_scores_against_library(synth_mod, oracle_mod):
+    cfg = tiny_cfg(synth_mod, T=40, H=256, E=16)
+    x = synth_mod.hidden(cfg)
+    W, bias = synth_mod.router(cfg)
+    z, s, b = oracle_mod.router_scores(cfg, x, W, bias)
+    zf = U.bf16_to_f32(x).astype(np.float64) @ W.astype(np.float64).T
+    # z is the double dot rounded once to f32: within one f32 ulp of numpy's double matmul
+    assert np.all(np.abs(z - zf) <= np.spacing(np.abs(zf).astype(np.float32)))
+    assert np.array_equal(s, expit(z.astype(np.float64)).astype(np.float32))
+    assert np.array_equal(b, s + bias[None, :])
+
+
+def test_router_zero_weights_closed_form(synth_mod, oracle_mod):
+    """W = 0: every score is sigmoid(0) = 1/2, so selection is the top-k of the
+    bias alone (ties -> lower id) and every weight is exactly 1/k."""
+    for k in (1, 2, 4):
+        cfg = tiny_cfg(synth_mod, T=5, E=16, k=k, rsf=2.5)
+        x = synth_mod.hidden(cfg)
+        W = np.zeros((cfg.E, cfg.H), np.float32)
+        bias = np.array([0.1, 0.3, 0.3, -0.2, 0.05, 0.3, 0.0, 0.2, 0.1, -0.1, 0.25, 0.25, 0.0, 0.01, -0.5, 0.2],
+                        np.float32)
+        z, s, b = oracle_mod.router_scores(cfg, x, W, bias)
+        assert np.all(s == 0.5)
+        ids, w, gap, _ = oracle_mod.router(cfg, x, W, bias)
+        order = sorted(range(cfg.E), key=lambda e: (-(np.float32(0.5) + bias[e]), e))[:k]
+        assert all(list(ids[t]) == order for t in range(cfg.T))
+        assert np.all(w == np.float32(1.0 / k))
+
+
+def _brute_select(b_row, s_row, k, n_group, topk_group):
+    E = len(b_row)
+    Eg = E // n_group
+    allowed = list(range(E))
+    if n_group > 1 and topk_group < n_group:
+        # group score: the largest f32 sum over all pairs of distinct experts of the group
+        G = []
+        for g in range(n_group):
+            mem = range(g * Eg, (g + 1) * Eg)
+            G.append(max(np.float32(b_row[a]) + np.float32(b_row[c]) for a, c in itertools.combinations(mem, 2)))
+        best = None
+        for sub in itertools.combinations(range(n_group), topk_group):
+            key = (sum(float(G[g]) for g in sub), [-g for g in sub])
+            if best is None or key > best[0]:
+                best = (key, sub)
+        kept = set(best[1])
+        allowed = [e for e in range(E) if e // Eg in kept]
+    order = sorted(allowed, key=lambda e: (-float(b_row[e]), e))
+    ids = order[:k]
+    ssum = sum(float(s_row[e]) for e in ids)
+    return ids, [float(s_row[e]) / ssum for e in ids]
+
+
+@pytest.mark.parametrize("E,k,ng,kg", [(8, 2, 1, 1), (16, 3, 1, 1), (16, 4, 4, 2), (12, 2, 3, 1), (16, 8, 8, 4)])
+def test_router_brute_force(synth_mod, oracle_mod, E, k, ng, kg):
+    cfg = tiny_cfg(synth_mod, T=64, H=64, E=E, k=k, n_group=ng, topk_group=kg, seed=500 + E + k)
+    x = synth_mod.hidden(cfg)
+    W, bias = synth_mod.router(cfg)
+    W *= 8  # widen the score spread so selections differ across tokens
+    _, s, b = oracle_mod.router_scores(cfg, x, W, bias)
+    ids, w, gap, ggap = oracle_mod.router(cfg, x, W, bias)
+    for t in range(cfg.T):
+        bi, bw = _brute_select(b[t], s[t], k, ng, kg)
+        assert list(ids[t]) == bi, t
+        assert np.allclose(w[t], bw, rtol=1e-6, atol=0)
+        assert abs(float(w[t].astype(np.float64).sum()) - 1.0) < 1e-6
+        assert gap[t] >= 0
+
+
+def test_router_group_no_op_special_case(synth_mod, oracle_mod):
+    """n_group = 1, or keeping every group, is plain top-k."""
+    cfg1 = tiny_cfg(synth_mod, T=64, E=16, k=3)
+    x = synth_mod.hidden(cfg1)
+    W, bias = synth_mod.router(cfg1)
+    ref = oracle_mod.router(cfg1, x, W, bias)
+    for ng in (2, 4, 8):
+        got = oracle_mod.router(cfg1.with_(n_group=ng, topk_group=ng), x, W, bias)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def test_router_gap_definition(synth_mod, oracle_mod):
+    cfg = tiny_cfg(synth_mod, T=32, E=16, k=2)
+    x = synth_mod.hidden(cfg)
+    W, bias = synth_mod.router(cfg)
+    _, s, b = oracle_mod.router_scores(cfg, x, W, bias)
+    ids, _, gap, ggap = oracle_mod.router(cfg, x, W, bias)
+    for t in range(cfg.T):
+        srt = sorted(b[t].tolist(), reverse=True)
+        assert gap[t] == np.float32(np.float32(srt[1]) - np.float32(srt[2]))
+    assert np.all(np.isinf(ggap))
+
+
+# -------------------------------------------------------------- permutation
+
+def test_permute_is_stable_argsort_and_invariants(synth_mod, oracle_mod):
+    cfg = synth_mod.CONFIGS["c0"].with_(T=300)
+    d = synth_mod.layer(cfg)
+    ids, w, _, _ = oracle_mod.router(cfg, d["hidden"], d["router_w"], d["router_bias"])
+    counts, offsets, srt, inv = oracle_mod.permute(cfg, ids)
+    flat = ids.ravel()
+    assert np.array_equal(srt, np.argsort(flat, kind="stable"))
+    assert counts.sum() == cfg.T * cfg.k
+    assert np.array_equal(counts, np.bincount(flat, minlength=cfg.E))
+    assert offsets[0] == 0 and offsets[-1] == cfg.T * cfg.k and np.all(np.diff(offsets) == counts)
+    assert np.array_equal(np.sort(srt), np.arange(cfg.T * cfg.k))
+    assert np.array_equal(inv[srt], np.arange(cfg.T * cfg.k))
+    for e in range(cfg.E):
+        seg = srt[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0) and np.all(flat[seg] == e)
+    # k distinct experts per token
+    assert all(len(set(r)) == cfg.k for r in ids.tolist())
+    assert np.allclose(w.astype(np.float64).sum(1), 1.0, atol=1e-6)
+
+
+# ------------------------------------------------------------------ the FFN
+
+def test_single_expert_is_dense_swiglu(synth_mod, oracle_mod):
+    """E = 1, k = 1, no shared expert: the layer is rsf times a dense SwiGLU MLP."""
+    cfg = tiny_cfg(synth_mod, T=10, E=1, k=1, shared_bits=0, rsf=1.75)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    out, ids, w, _, _ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    assert np.all(ids == 0) and np.all(w == 1.0)
+    x = U.bf16_to_f32(d["hidden"]).astype(np.float64)
+    ref = 1.75 * U.swiglu_mlp(x, *U.expert_mats(cfg, d, 0))
+    assert U.rel_max_err(out, ref) < 2e-6
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_shared_expert_is_dense_swiglu(synth_mod, oracle_mod, bits):
+    cfg = tiny_cfg(synth_mod, T=9, shared_bits=bits, I_sh=80)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    got = oracle_mod.shared_ffn(cfg, d["hidden"], lw)
+    x = U.bf16_to_f32(d["hidden"]).astype(np.float64)
+    ref = U.swiglu_mlp(x, *U.shared_mats(cfg, d))
+    assert U.rel_max_err(got, ref) < 2e-6
+
+
+def test_layer_against_numpy_sparse_sum(synth_mod, oracle_mod):
+    """Whole layer against a numpy evaluation of sum_j rsf*w_j*FFN_{id_j}(x) + shared(x),
+    using the oracle's routing (the router is pinned separately)."""
+    cfg = tiny_cfg(synth_mod, T=16, E=8, k=3, rsf=1.5, n_group=4, topk_group=2)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    out, ids, w, _, _ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    x = U.bf16_to_f32(d["hidden"]).astype(np.float64)
+    mats = [U.expert_mats(cfg, d, e) for e in range(cfg.E)]
+    ref = U.swiglu_mlp(x, *U.shared_mats(cfg, d))
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            ref[t] += 1.5 * float(w[t, j]) * U.swiglu_mlp(x[t:t + 1], *mats[ids[t, j]])[0]
+    assert U.rel_max_err(out, ref) < 2e-6
+
+
+def test_identical_experts_make_routing_irrelevant(synth_mod, oracle_mod):
+    """All experts equal: the routed part is rsf*FFN(x) whatever the routing (sum w = 1)."""
+    cfg = tiny_cfg(synth_mod, T=20, E=8, k=2, shared_bits=0, rsf=2.0)
+    d = synth_mod.layer(cfg)
+    d["experts_q"][:] = d["experts_q"][0]
+    d["experts_qs"][:] = d["experts_qs"][0]
+    lw = oracle_mod.LayerWeights(cfg, d)
+    out, _, _, _, _ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    x = U.bf16_to_f32(d["hidden"]).astype(np.float64)
+    ref = 2.0 * U.swiglu_mlp(x, *U.expert_mats(cfg, d, 0))
+    assert U.rel_max_err(out, ref) < 2e-6
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(E=8, k=3, n_group=4, topk_group=2, rsf=2.5), dict(shared_bits=8)])
+def test_sparse_equals_dense_mask(synth_mod, oracle_mod, kw):
+    cfg = tiny_cfg(synth_mod, **kw)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    sparse, *_ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    dense = oracle_mod.layer_forward_dense(cfg, lw, d["hidden"])
+    assert np.allclose(sparse, dense, rtol=2e-7, atol=1e-9)
+
+
+def test_rsf_linearity(synth_mod, oracle_mod):
+    cfg = tiny_cfg(synth_mod, T=16)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    sh = oracle_mod.shared_ffn(cfg, d["hidden"], lw).astype(np.float64)
+    o1, *_ = oracle_mod.layer_forward(cfg.with_(rsf=1.0), lw, d["hidden"])
+    o3, *_ = oracle_mod.layer_forward(cfg.with_(rsf=3.0), lw, d["hidden"])
+    assert np.allclose(o3 - sh, 3.0 * (o1 - sh), rtol=1e-5, atol=1e-6)
+
+
+def test_residual_adds_input(synth_mod, oracle_mod):
+    cfg = tiny_cfg(synth_mod, T=8)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    o0, *_ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    o1, *_ = oracle_mod.layer_forward(cfg, lw, d["hidden"], residual=True)
+    x = U.bf16_to_f32(d["hidden"])
+    assert np.allclose(o1, o0.astype(np.float64) + x, rtol=0, atol=1e-6)
+
+
+def test_token_subset_matches_full(synth_mod, oracle_mod):
+    cfg = tiny_cfg(synth_mod, T=24, E=8, k=2)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    out, ids, w, _, _ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    toks = np.array([0, 5, 23, 7])
+    assert np.array_equal(oracle_mod.layer_tokens(cfg, lw, d["hidden"], toks), out[toks])
+    assert np.array_equal(oracle_mod.layer_tokens(cfg, lw, d["hidden"], toks, ids, w), out[toks])
+
+
+def test_split_calls_compose_to_layer(synth_mod, oracle_mod):
+    """router -> permute -> expert_ffn (pre-scaled) -> shared -> combine equals the layer."""
+    cfg = tiny_cfg(synth_mod, T=16, rsf=2.0)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    x = d["hidden"]
+    out, *_ = oracle_mod.layer_forward(cfg, lw, x)
+    ids, w, _, _ = oracle_mod.router(cfg, x, d["router_w"], d["router_bias"])
+    counts, offsets, srt, inv = oracle_mod.permute(cfg, ids)
+    y = oracle_mod.expert_ffn(cfg, x, lw, offsets, srt)
+    sh = oracle_mod.shared_ffn(cfg, x, lw)
+    assert np.array_equal(oracle_mod.combine(cfg, y, inv, w, sh), out)
+    ys = oracle_mod.expert_ffn(cfg, x, lw, offsets, srt, pair_scale=(2.0 * w).astype(np.float32).ravel())
+    assert np.allclose(oracle_mod.combine(cfg, ys, inv, None, sh), out, rtol=1e-6, atol=1e-7)
+
+
+def test_integer_sums_exact(synth_mod, oracle_mod):
+    """Integer-valued inputs: the gate/up sums are exact integers equal to numpy's int64 matmul."""
+    cfg = tiny_cfg(synth_mod, T=16, H=128, E=4, k=2, I=64)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    x = synth_mod.small_int_hidden(cfg, 8)
+    ids, _, _, _ = oracle_mod.router(cfg, x, d["router_w"], d["router_bias"])
+    _, offsets, srt, _ = oracle_mod.permute(cfg, ids)
+    g, u = oracle_mod.gateup_int_sums(cfg, x, lw, offsets, srt)
+    xi = U.bf16_to_f32(x).astype(np.int64)
+    mat = cfg.I * cfg.H // 2
+    for r in range(cfg.T * cfg.k):
+        e = int(np.searchsorted(offsets, r, side="right") - 1)
+        t = srt[r] // cfg.k
+        qg = U.unpack_int4(d["experts_q"][e][:mat].reshape(cfg.I, -1), cfg.H).astype(np.int64)
+        qu = U.unpack_int4(d["experts_q"][e][mat:2 * mat].reshape(cfg.I, -1), cfg.H).astype(np.int64)
+        assert np.array_equal(g[r], (qg @ xi[t]).astype(np.float64))
+        assert np.array_equal(u[r], (qu @ xi[t]).astype(np.float64))
+
+
+def test_thread_count_does_not_change_bits(synth_mod, oracle_mod, tmp_path):
+    code = ("import sys, numpy as np; sys.path.insert(0, %r); import synth, oracle;"
+            "cfg = synth.CONFIGS['c0'];"
+            "d = synth.layer(cfg); lw = oracle.LayerWeights(cfg, d);"
+            "o = oracle.layer_forward(cfg, lw, d['hidden'])[0]; np.save(sys.argv[1], o)"
+            % os.path.dirname(GOLD.rstrip('/')).rsplit('/tests', 1)[0])
+    outs = []
+    for n in (1, 5):
+        p = str(tmp_path / f"o{n}.npy")
+        env = dict(os.environ, OMP_NUM_THREADS=str(n))
+        subprocess.run([sys.executable, "-c", code, p], check=True, env=env)
+        outs.append(np.load(p))
+    assert np.array_equal(outs[0], outs[1])
