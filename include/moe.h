@@ -1,0 +1,212 @@
+/*
+ * moe.h -- C ABI of the int4 routed-expert MoE layer forward pass on MI355X (gfx950).
+ *
+ * One Mixture-of-Experts FFN layer as Colibri-Nano and the colibri engine
+ * define it:
+ *   - a sigmoid router with an aux-loss-free selection bias (Colibri-Nano model
+ *     card, "Architecture": sigmoid+bias router, DeepSeek-V3-style aux-loss-free
+ *     balancing; colibri README, "What's implemented": DeepSeek-V3-style sigmoid
+ *     router with noaux_tc and routed_scaling_factor, shared expert);
+ *   - batch-union routing: the pairs are grouped by expert so each unique expert
+ *     is read once and applied to every position routed to it (colibri README,
+ *     "What's implemented": batch-union MoE);
+ *   - SwiGLU experts of three matrices (colibri README at 0d2fb6f, "Never wait for
+ *     the disk twice": an expert's three matrices are stored adjacent) whose
+ *     weights are per-row symmetric packed int4 with one f32 scale per row in a
+ *     sibling .qs tensor (colibri-nano README, "Converting a checkpoint
+ *     yourself");
+ *   - an always-resident shared expert (NanoColibri README, model table) in int4
+ *     or int8 (colibri-nano README: int4 experts, int8 dense);
+ *   - a weighted combine scaled by routed_scaling_factor.
+ *
+ * Conventions for every call below
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     keeps none of them after the call's work completes and allocates nothing.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *     default stream).  Calls return as soon as the work is enqueued; they never
+ *     synchronise and never read device memory back to the host.
+ *   - Shapes and pointers are validated on the host before anything is
+ *     enqueued: a call that returns an error has enqueued nothing.
+ *   - T == 0 is a no-op that returns MOE_OK.
+ *   - Results are deterministic: the same inputs give the same bits, run to run.
+ *   - Calls that share a workspace on different streams race; one workspace per
+ *     stream.
+ *
+ * Layouts (row-major, C order)
+ *   hidden     [T][H] bf16 (raw bits, moe_bf16)
+ *   router_w   [E][H] f32, one row per expert;  router_bias [E] f32
+ *   int4 matrix with `rows` x `cols`: rows of cols/2 bytes, element 2c in the
+ *              low nibble of byte c, element 2c+1 in the high nibble, two's
+ *              complement; int8: rows of cols signed bytes.  One f32 scale per
+ *              row; the weight is q * scale.
+ *   gate, up   per expert [I][H]  (row = intermediate channel, columns = hidden)
+ *   down       per expert [H][I]  (row = output channel, columns = intermediate)
+ *   Expert e of a matrix family starts at q + e*q_stride_bytes with its scales at
+ *   qs + e*qs_stride_floats, so the three matrices of an expert may be stored
+ *   back to back.  q pointers and q strides must be multiples of 16 bytes; qs
+ *   pointers and strides multiples of 4 floats.
+ *   Pairs: p = t*top_k + j is token t's j-th chosen expert (j in descending
+ *   selection-score order).  Sorted rows r list the pairs grouped by expert in
+ *   ascending expert id, pairs of one expert in ascending p.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)       /* inconsistent shape */
+#define MOE_ERR_UNSUPPORTED (-3) /* legal shape the gfx950 kernels do not cover */
+#define MOE_ERR_WORKSPACE (-4)   /* workspace too small */
+#define MOE_ERR_ALIGN (-5)       /* misaligned pointer or stride */
+#define MOE_ERR_HIP (-6)         /* a HIP launch failed */
+
+/* moe_shape.flags */
+#define MOE_OUT_F32 1u      /* out is f32 [T][H]; otherwise bf16 [T][H] rounded to nearest even */
+#define MOE_ADD_RESIDUAL 2u /* moe_layer_forward adds the layer input to the output */
+#define MOE_EXPERT_INT8 4u  /* moe_expert_ffn: gate/up/down are int8 rows (the shared expert of an
+                               int8 dense stack); otherwise packed int4 */
+#define MOE_STAGE_GATEUP_ONLY 0x200u /* moe_expert_ffn, profiling: run only the gate/up + SwiGLU kernel
+                               (h stays in the workspace; y_pairs is not written) */
+#define MOE_TEST_GATEUP_SUMS 0x100u /* moe_expert_ffn, testing only: write the raw integer-weight sums
+                               sum_h x*q of gate into y_pairs[r][0:I] and of up into y_pairs[r][I:2I]
+                               (no scale, no activation, no down projection); needs 2*I <= H, int4 */
+
+/* workspace kinds for moe_workspace_bytes */
+#define MOE_WS_PERMUTE 1
+#define MOE_WS_EXPERT_FFN 2
+#define MOE_WS_LAYER 3
+
+typedef uint16_t moe_bf16; /* raw bfloat16 bits */
+
+typedef struct {
+    int32_t T;          /* tokens in the batch, >= 0 */
+    int32_t H;          /* hidden size */
+    int32_t E;          /* routed experts */
+    int32_t top_k;      /* experts per token, 1 <= top_k <= E */
+    int32_t I;          /* routed expert intermediate size */
+    int32_t I_shared;   /* shared expert intermediate size (ignored when shared_bits == 0) */
+    int32_t shared_bits;/* 0 = no shared expert, 4 = int4, 8 = int8 */
+    int32_t n_group;    /* groups for group-limited selection; 1 = plain top-k */
+    int32_t topk_group; /* groups kept, 1 <= topk_group <= n_group */
+    float routed_scaling_factor; /* multiplies the routed terms (not the shared expert) */
+    uint32_t flags;     /* MOE_OUT_F32 | MOE_ADD_RESIDUAL */
+} moe_shape;
+
+typedef struct {
+    const void *q;            /* packed int4 (u8) or int8 rows */
+    const float *qs;          /* one f32 scale per row */
+    int64_t q_stride_bytes;   /* expert-to-expert distance in q (0 for a single expert) */
+    int64_t qs_stride_floats; /* expert-to-expert distance in qs */
+} moe_qmat;
+
+typedef struct {
+    const float *router_w;    /* [E][H] f32 */
+    const float *router_bias; /* [E] f32; selection only */
+    moe_qmat gate, up, down;  /* routed experts, int4 */
+    moe_qmat sh_gate, sh_up, sh_down; /* shared expert (E = 1), int4 or int8 per shared_bits */
+} moe_weights;
+
+/*
+ * moe_router -- router scores, selection and combine weights.
+ * Defined by: Colibri-Nano model card, "Architecture" (sigmoid+bias router,
+ * DeepSeek-V3-style aux-loss-free balancing) and colibri README, "What's
+ * implemented" (noaux_tc group-limited selection, routed_scaling_factor).
+ *   z[t,e] = sum_h x[t,h] * W[e,h] (f32),  s = 1/(1+exp(-z)),  b = s + bias.
+ *   n_group > 1: groups are contiguous blocks of E/n_group experts; a group
+ *   scores the sum of its two largest b; the topk_group best groups are kept
+ *   (ties -> lower group id).  top_k largest b among kept experts, ties ->
+ *   lower id, listed by descending b.  topk_w[t,j] = s_j / sum_j s_j (sums to
+ *   1; the routed scaling factor is applied by moe_expert_ffn / moe_combine).
+ * Out: topk_ids [T][top_k] i32, topk_w [T][top_k] f32, sel_gap [T] f32
+ *   (nullable): the smaller of b_(k) - b_(k+1) and, when groups are dropped,
+ *   G_(keep) - G_(keep+1); it measures how close the token's selection is to a tie.
+ * The GPU kernels need H % 128 == 0, I % 64 == 0, I_shared % 64 == 0, E <= 256,
+ * top_k <= 64 and n_group <= 64 (else MOE_ERR_UNSUPPORTED; every call checks).
+ * Workspace: the partial logits; moe_workspace_bytes(shape, MOE_WS_PERMUTE) covers it.
+ */
+int moe_router(const moe_shape *shape, const moe_bf16 *hidden, const float *router_w, const float *router_bias,
+               int32_t *topk_ids, float *topk_w, float *sel_gap, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_permute -- group the T*top_k pairs by expert (batch-union; colibri README,
+ * "What's implemented").  A stable counting sort by expert id:
+ *   counts[e] = #pairs routed to e;  offsets[0] = 0, offsets[e+1] = offsets[e] + counts[e];
+ *   sorted_pairs[r] = the pair at sorted row r (pairs of one expert ascending);
+ *   inv_pos[p] = the sorted row of pair p.
+ * Positions come from ordered ranks, not atomics, so the result is bit-exact.
+ * topk_ids must hold ids in [0, E) (not checked on the device).
+ * Out: counts [E], offsets [E+1], sorted_pairs [T*top_k], inv_pos [T*top_k], all i32.
+ * Workspace: moe_workspace_bytes(shape, MOE_WS_PERMUTE).
+ */
+int moe_permute(const moe_shape *shape, const int32_t *topk_ids, int32_t *counts, int32_t *offsets,
+                int32_t *sorted_pairs, int32_t *inv_pos, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_expert_ffn -- the routed experts on their sorted rows.
+ * For sorted row r of expert e (offsets[e] <= r < offsets[e+1]), pair
+ * p = sorted_pairs[r], token t = p / top_k:
+ *   g_i = sg_i * sum_h x[t,h] q_gate[e,i,h],  u_i likewise with up,
+ *   h_i = silu(g_i) * u_i with silu(z) = z / (1 + exp(-z))  (SwiGLU),
+ *   y_pairs[r, c] = pair_scale[p] * sd_c * sum_i h_i q_down[e,c,i].
+ * pair_scale is indexed by pair and nullable (then 1).  Computed with bf16
+ * matrix cores: x and the int4 values are exact in bf16, products accumulate in
+ * f32, h is rounded to bf16 before the down projection.
+ * The shared expert runs through this call as E = 1, top_k = 1 with
+ * offsets = {0, T}, sorted_pairs = identity and gate/up/down = the shared
+ * matrices (shape.I = I_shared; set MOE_EXPERT_INT8 for int8 rows).  gate and
+ * up must use the same expert stride.
+ * Out: y_pairs [T*top_k][H] f32 in sorted order.
+ * Needs H % 128 == 0 and I % 64 == 0.  Workspace: moe_workspace_bytes(shape, MOE_WS_EXPERT_FFN).
+ */
+int moe_expert_ffn(const moe_shape *shape, const moe_bf16 *hidden, const moe_weights *weights,
+                   const int32_t *offsets, const int32_t *sorted_pairs, const float *pair_scale,
+                   float *y_pairs, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_combine -- out[t,c] = sum over j ascending of coef(t,j) * y_pairs[inv_pos[t*top_k+j], c]
+ *                           + shared_out[t,c] + residual[t,c]
+ * with coef = routed_scaling_factor * topk_w[t,j] when topk_w is given, else 1
+ * (pairs already scaled).  shared_out [T][H] f32 and residual [T][H] bf16 are
+ * nullable.  out is f32 or bf16 per MOE_OUT_F32.
+ */
+int moe_combine(const moe_shape *shape, const float *y_pairs, const int32_t *inv_pos, const float *topk_w,
+                const float *shared_out, const moe_bf16 *residual, void *out, void *stream);
+
+/*
+ * moe_layer_forward -- the whole layer: router, permutation, routed experts,
+ * shared expert, combine (and the input added back when MOE_ADD_RESIDUAL).
+ * out: [T][H] f32 or bf16 per MOE_OUT_F32.  The regime (small-batch weight
+ * streaming or tiled grouped GEMM) is chosen from the shape.
+ * Workspace: moe_workspace_bytes(shape, MOE_WS_LAYER).
+ */
+int moe_layer_forward(const moe_shape *shape, const moe_weights *weights, const moe_bf16 *hidden, void *out,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace a call needs for this shape (0 for an invalid shape). */
+size_t moe_workspace_bytes(const moe_shape *shape, int which);
+
+/* Host-side validation only (no device work): MOE_OK or the status a call would return. */
+int moe_validate_shape(const moe_shape *shape);
+
+/* A static string naming a status code. */
+const char *moe_status_string(int status);
+
+/* The layer-forward workspace also exposes, for inspection after a call, the
+ * routing it computed: moe_layer_routing(ws, shape, ...) returns device
+ * pointers into ws (ids [T][k], w [T][k], offsets [E+1], sorted [T*k]).
+ * Pointers stay valid until the workspace is reused. */
+int moe_layer_routing(const moe_shape *shape, void *ws, size_t ws_bytes, int32_t **topk_ids, float **topk_w,
+                      int32_t **offsets, int32_t **sorted_pairs);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,232 @@
+"""Python binding of the MI355X MoE-layer library (libmoe_hip.so, include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch provides device memory and the current stream.  If the HIP
+library is missing, every call raises -- there is no CPU fallback.
+
+The functions mirror the C ABI names:
+  moe_router, moe_permute, moe_expert_ffn, moe_combine, moe_layer_forward,
+  moe_workspace_bytes, moe_validate_shape, moe_status_string, moe_layer_routing
+and ``MoeLayer`` keeps one layer's device weights and workspace.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_hip.so")
+
+MOE_OK = 0
+MOE_ERR_NULL = -1
+MOE_ERR_SHAPE = -2
+MOE_ERR_UNSUPPORTED = -3
+MOE_ERR_WORKSPACE = -4
+MOE_ERR_ALIGN = -5
+MOE_ERR_HIP = -6
+
+MOE_OUT_F32 = 1
+MOE_ADD_RESIDUAL = 2
+MOE_EXPERT_INT8 = 4
+MOE_TEST_GATEUP_SUMS = 0x100
+MOE_STAGE_GATEUP_ONLY = 0x200
+
+MOE_WS_PERMUTE = 1
+MOE_WS_EXPERT_FFN = 2
+MOE_WS_LAYER = 3
+
+EXPORTS = ["moe_router", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+           "moe_workspace_bytes", "moe_validate_shape", "moe_status_string", "moe_layer_routing"]
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
+                ("shared_bits", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
+                ("flags", ctypes.c_uint32)]
+
+
+class MoeQMat(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("qs", ctypes.c_void_p),
+                ("q_stride_bytes", ctypes.c_int64), ("qs_stride_floats", ctypes.c_int64)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("gate", MoeQMat), ("up", MoeQMat), ("down", MoeQMat),
+                ("sh_gate", MoeQMat), ("sh_up", MoeQMat), ("sh_down", MoeQMat)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmoe_hip.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, S, W = ctypes.c_void_p, ctypes.POINTER(MoeShape), ctypes.POINTER(MoeWeights)
+        sz = ctypes.c_size_t
+        sig = {
+            "moe_router": [S, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_permute": [S, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_expert_ffn": [S, vp, W, vp, vp, vp, vp, vp, sz, vp],
+            "moe_combine": [S, vp, vp, vp, vp, vp, vp, vp],
+            "moe_layer_forward": [S, W, vp, vp, vp, sz, vp],
+            "moe_validate_shape": [S],
+            "moe_layer_routing": [S, vp, sz, vp, vp, vp, vp],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.moe_workspace_bytes.argtypes = [S, ctypes.c_int]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().moe_status_string(status).decode()
+
+
+moe_status_string = status_string
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+def shape(T, H, E, top_k, I, I_shared=0, shared_bits=0, n_group=1, topk_group=1, rsf=1.0, flags=0) -> MoeShape:
+    return MoeShape(T, H, E, top_k, I, I_shared, shared_bits, n_group, topk_group, rsf, flags)
+
+
+def shape_of(cfg, T: Optional[int] = None, flags: int = 0) -> MoeShape:
+    """MoeShape of a synth.LayerConfig-like object (fields T,H,E,k,I,I_sh,...)."""
+    return shape(cfg.T if T is None else T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_sh, cfg.shared_bits, cfg.n_group,
+                 cfg.topk_group, cfg.rsf, flags)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def moe_validate_shape(sh: MoeShape) -> int:
+    return load().moe_validate_shape(ctypes.byref(sh))
+
+
+def moe_workspace_bytes(sh: MoeShape, which: int = MOE_WS_LAYER) -> int:
+    return int(load().moe_workspace_bytes(ctypes.byref(sh), which))
+
+
+def moe_router(sh: MoeShape, hidden, router_w, router_bias, topk_ids, topk_w, sel_gap, ws, stream=None):
+    _check(load().moe_router(ctypes.byref(sh), _ptr(hidden), _ptr(router_w), _ptr(router_bias), _ptr(topk_ids),
+                             _ptr(topk_w), _ptr(sel_gap), _ptr(ws), ws.numel() if ws is not None else 0,
+                             _stream(stream)), "moe_router")
+
+
+def moe_permute(sh: MoeShape, topk_ids, counts, offsets, sorted_pairs, inv_pos, ws, stream=None):
+    _check(load().moe_permute(ctypes.byref(sh), _ptr(topk_ids), _ptr(counts), _ptr(offsets), _ptr(sorted_pairs),
+                              _ptr(inv_pos), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_permute")
+
+
+def moe_expert_ffn(sh: MoeShape, hidden, weights: MoeWeights, offsets, sorted_pairs, pair_scale, y_pairs, ws,
+                   stream=None):
+    _check(load().moe_expert_ffn(ctypes.byref(sh), _ptr(hidden), ctypes.byref(weights), _ptr(offsets),
+                                 _ptr(sorted_pairs), _ptr(pair_scale), _ptr(y_pairs), _ptr(ws),
+                                 ws.numel() if ws is not None else 0, _stream(stream)), "moe_expert_ffn")
+
+
+def moe_combine(sh: MoeShape, y_pairs, inv_pos, topk_w, shared_out, residual, out, stream=None):
+    _check(load().moe_combine(ctypes.byref(sh), _ptr(y_pairs), _ptr(inv_pos), _ptr(topk_w), _ptr(shared_out),
+                              _ptr(residual), _ptr(out), _stream(stream)), "moe_combine")
+
+
+def moe_layer_forward(sh: MoeShape, weights: MoeWeights, hidden, out, ws, stream=None):
+    _check(load().moe_layer_forward(ctypes.byref(sh), ctypes.byref(weights), _ptr(hidden), _ptr(out), _ptr(ws),
+                                    ws.numel() if ws is not None else 0, _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_routing(sh: MoeShape, ws):
+    """Device pointers (ints) of ids, w, offsets, sorted inside a layer workspace."""
+    p = [ctypes.c_void_p() for _ in range(4)]
+    _check(load().moe_layer_routing(ctypes.byref(sh), _ptr(ws), ws.numel(), *[ctypes.byref(x) for x in p]),
+           "moe_layer_routing")
+    return [x.value for x in p]
+
+
+def qmat(q, qs, q_stride_bytes: int = 0, qs_stride_floats: int = 0, q_offset: int = 0, qs_offset: int = 0) -> MoeQMat:
+    """A matrix family inside device tensors q (bytes) and qs (f32), at byte / float offsets."""
+    return MoeQMat(_ptr(q) + q_offset, _ptr(qs) + 4 * qs_offset, q_stride_bytes, qs_stride_floats)
+
+
+class MoeLayer:
+    """One layer's weights on the device, in the container layout:
+    experts_q [E, 3*I*H/2] u8 (gate|up|down per expert), experts_qs [E, 2I+H] f32,
+    shared_q / shared_qs likewise for the shared expert, router_w [E,H], router_bias [E]."""
+
+    def __init__(self, cfg, arrays: dict, device="cuda"):
+        import torch
+        self.cfg = cfg
+        dev = torch.device(device)
+
+        def up(a):
+            return None if a is None else torch.from_numpy(a).to(dev)
+
+        self.router_w = up(arrays["router_w"])
+        self.router_bias = up(arrays["router_bias"])
+        self.experts_q = up(arrays["experts_q"])
+        self.experts_qs = up(arrays["experts_qs"])
+        self.shared_q = up(arrays.get("shared_q"))
+        self.shared_qs = up(arrays.get("shared_qs"))
+        H, I, Ish = cfg.H, cfg.I, cfg.I_sh
+        mat = I * H // 2
+        blk, sblk = 3 * mat, 2 * I + H
+        w = MoeWeights()
+        w.router_w = _ptr(self.router_w)
+        w.router_bias = _ptr(self.router_bias)
+        w.gate = qmat(self.experts_q, self.experts_qs, blk, sblk, 0, 0)
+        w.up = qmat(self.experts_q, self.experts_qs, blk, sblk, mat, I)
+        w.down = qmat(self.experts_q, self.experts_qs, blk, sblk, 2 * mat, 2 * I)
+        if cfg.shared_bits:
+            smat = Ish * H // 2 if cfg.shared_bits == 4 else Ish * H
+            w.sh_gate = qmat(self.shared_q, self.shared_qs, 0, 0, 0, 0)
+            w.sh_up = qmat(self.shared_q, self.shared_qs, 0, 0, smat, Ish)
+            w.sh_down = qmat(self.shared_q, self.shared_qs, 0, 0, 2 * smat, 2 * Ish)
+        self.weights = w
+
+    def workspace(self, T: int, flags: int = 0):
+        import torch
+        n = moe_workspace_bytes(shape_of(self.cfg, T, flags), MOE_WS_LAYER)
+        return torch.empty(n, dtype=torch.uint8, device=self.router_w.device)
+
+    def forward(self, hidden, out, ws, flags: int = 0, stream=None):
+        moe_layer_forward(shape_of(self.cfg, hidden.shape[0], flags), self.weights, hidden, out, ws, stream)
+        return out

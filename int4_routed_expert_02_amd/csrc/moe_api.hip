@@ -1,0 +1,344 @@
+// moe_api.hip -- the C ABI (include/moe.h): host-side validation, workspace
+// layout and kernel launches.  Nothing here touches device memory from the host
+// or synchronises; every error is detected before the first enqueue.
+#include <string.h>
+
+#include "moe.h"
+#include "moe_launch.h"
+
+namespace {
+
+using moe::FfnArgs;
+
+constexpr size_t WS_ALIGN = 256;
+
+size_t align_up(size_t v) { return (v + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int validate(const moe_shape *s)
+{
+    if (!s) return MOE_ERR_NULL;
+    if (s->T < 0 || s->H <= 0 || s->E <= 0 || s->top_k <= 0 || s->I <= 0) return MOE_ERR_SHAPE;
+    if (s->top_k > s->E) return MOE_ERR_SHAPE;
+    if (s->H % 2 || s->I % 2) return MOE_ERR_SHAPE;
+    if (s->shared_bits != 0 && s->shared_bits != 4 && s->shared_bits != 8) return MOE_ERR_SHAPE;
+    if (s->shared_bits && (s->I_shared <= 0 || s->I_shared % 2)) return MOE_ERR_SHAPE;
+    if (s->n_group <= 0 || s->E % s->n_group) return MOE_ERR_SHAPE;
+    if (s->topk_group <= 0 || s->topk_group > s->n_group) return MOE_ERR_SHAPE;
+    if (s->n_group > 1 && s->E / s->n_group < 2) return MOE_ERR_SHAPE;
+    if (s->top_k > s->topk_group * (s->E / s->n_group)) return MOE_ERR_SHAPE;
+    if ((int64_t)s->T * s->top_k > INT32_MAX / 2) return MOE_ERR_SHAPE;
+    // what the gfx950 kernels cover
+    if (s->H % 128 || s->I % 64) return MOE_ERR_UNSUPPORTED;
+    if (s->shared_bits && s->I_shared % 64) return MOE_ERR_UNSUPPORTED;
+    if (s->E > 256 || s->top_k > 64 || s->n_group > 64) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int check_qmat(const moe_qmat &m)
+{
+    if (!m.q || !m.qs) return MOE_ERR_NULL;
+    if (!aligned(m.q, 16) || m.q_stride_bytes % 16 || !aligned(m.qs, 16) || m.qs_stride_floats % 4)
+        return MOE_ERR_ALIGN;
+    if (m.q_stride_bytes < 0 || m.qs_stride_floats < 0) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+// Workspace sections, in bytes, each 256-aligned.
+struct Layout {
+    size_t zpart, sbc, ids, w, gap, pscale, counts, offsets, sorted, inv, hbuf, shh, ypair, shy, total;
+};
+
+Layout layout(const moe_shape *s, int which)
+{
+    Layout L;
+    memset(&L, 0, sizeof(L));
+    const size_t T = (size_t)s->T, E = (size_t)s->E, k = (size_t)s->top_k, P = T * k;
+    const int KS = moe::router_ks(s->T, s->H, s->E);
+    const int sbt = moe::superblock_tokens(s->top_k);
+    const size_t nsb = (T + sbt - 1) / sbt;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes ? bytes : 1);
+        return o;
+    };
+    if (which == MOE_WS_PERMUTE) {
+        // router partial logits or permutation histograms (never both at once)
+        const size_t a = (size_t)KS * T * E * 4, b = nsb * E * 4;
+        L.zpart = L.sbc = take(a > b ? a : b);
+    } else if (which == MOE_WS_EXPERT_FFN) {
+        L.hbuf = take(P * (size_t)s->I * 4);
+    } else {
+        L.zpart = take((size_t)KS * T * E * 4);
+        L.sbc = take(nsb * E * 4);
+        L.ids = take(P * 4);
+        L.w = take(P * 4);
+        L.gap = take(T * 4);
+        L.pscale = take(P * 4);
+        L.counts = take(E * 4);
+        L.offsets = take((E + 1) * 4);
+        L.sorted = take(P * 4);
+        L.inv = take(P * 4);
+        L.hbuf = take(P * (size_t)s->I * 4);
+        L.ypair = take(P * (size_t)s->H * 4);
+        if (s->shared_bits) {
+            L.shh = take(T * (size_t)s->I_shared * 4);
+            L.shy = take(T * (size_t)s->H * 4);
+        }
+    }
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off)
+{
+    return (T *)((char *)ws + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int check_ws(const moe_shape *s, int which, void *ws, size_t ws_bytes)
+{
+    const Layout L = layout(s, which);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (!ws) return MOE_ERR_NULL;
+    if (!aligned(ws, WS_ALIGN)) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+// The two grouped GEMMs of one expert family on sorted rows.
+int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qmat &gate, const moe_qmat &up,
+            const moe_qmat &down, int I, const int32_t *offsets, const int32_t *sorted, int E, int kdiv, int rows,
+            const float *pscale, float *hbuf, float *y, hipStream_t st, bool gateup_only = false)
+{
+    if (gate.q_stride_bytes != up.q_stride_bytes || gate.qs_stride_floats != up.qs_stride_floats)
+        return MOE_ERR_UNSUPPORTED;
+    FfnArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A = hidden;
+    g.lda = s->H;
+    g.gather = sorted;
+    g.kdiv = kdiv;
+    g.offsets = offsets;
+    g.E = E;
+    g.M = rows;
+    g.q0 = (const uint8_t *)gate.q;
+    g.s0 = gate.qs;
+    g.q1 = (const uint8_t *)up.q;
+    g.s1 = up.qs;
+    g.qstride = gate.q_stride_bytes;
+    g.sstride = gate.qs_stride_floats;
+    g.K = s->H;
+    g.N = I;
+    g.out = hbuf;
+    g.ldo = I;
+    hipError_t e = moe::launch_ffn(0, wbits, g, rows, offsets ? E : 1, st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (gateup_only) return MOE_OK;
+    FfnArgs d;
+    memset(&d, 0, sizeof(d));
+    d.A = hbuf;
+    d.lda = I;
+    d.gather = nullptr;
+    d.kdiv = 1;
+    d.pair_of_row = sorted;
+    d.offsets = offsets;
+    d.E = E;
+    d.M = rows;
+    d.q0 = (const uint8_t *)down.q;
+    d.s0 = down.qs;
+    d.qstride = down.q_stride_bytes;
+    d.sstride = down.qs_stride_floats;
+    d.K = I;
+    d.N = s->H;
+    d.out = y;
+    d.ldo = s->H;
+    d.pscale = pscale;
+    return hip_status(moe::launch_ffn(1, wbits, d, rows, offsets ? E : 1, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_validate_shape(const moe_shape *shape) { return validate(shape); }
+
+const char *moe_status_string(int status)
+{
+    switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: inconsistent shape";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside what the gfx950 kernels cover";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: misaligned pointer or stride";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+size_t moe_workspace_bytes(const moe_shape *shape, int which)
+{
+    if (validate(shape) != MOE_OK) return 0;
+    if (which != MOE_WS_PERMUTE && which != MOE_WS_EXPERT_FFN && which != MOE_WS_LAYER) return 0;
+    return layout(shape, which).total;
+}
+
+int moe_router(const moe_shape *s, const moe_bf16 *hidden, const float *router_w, const float *router_bias,
+               int32_t *topk_ids, float *topk_w, float *sel_gap, void *ws, size_t ws_bytes, void *stream)
+{
+    int st = validate(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;
+    if (!hidden || !router_w || !router_bias || !topk_ids || !topk_w) return MOE_ERR_NULL;
+    if (!aligned(hidden, 16) || !aligned(router_w, 16)) return MOE_ERR_ALIGN;
+    if ((st = check_ws(s, MOE_WS_PERMUTE, ws, ws_bytes))) return st;
+    const Layout L = layout(s, MOE_WS_PERMUTE);
+    const int KS = moe::router_ks(s->T, s->H, s->E);
+    return hip_status(moe::launch_router(hidden, router_w, router_bias, s->T, s->H, s->E, s->top_k, s->n_group,
+                                         s->topk_group, s->routed_scaling_factor, at<float>(ws, L.zpart), KS,
+                                         topk_ids, topk_w, sel_gap, nullptr, nullptr, (hipStream_t)stream));
+}
+
+int moe_permute(const moe_shape *s, const int32_t *topk_ids, int32_t *counts, int32_t *offsets,
+                int32_t *sorted_pairs, int32_t *inv_pos, void *ws, size_t ws_bytes, void *stream)
+{
+    int st = validate(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;
+    if (!topk_ids || !counts || !offsets || !sorted_pairs || !inv_pos) return MOE_ERR_NULL;
+    if ((st = check_ws(s, MOE_WS_PERMUTE, ws, ws_bytes))) return st;
+    const Layout L = layout(s, MOE_WS_PERMUTE);
+    const int P = s->T * s->top_k;
+    const int sbt = moe::superblock_tokens(s->top_k);
+    const int nsb = (s->T + sbt - 1) / sbt;
+    hipStream_t hs = (hipStream_t)stream;
+    int32_t *bc = at<int32_t>(ws, L.sbc);
+    hipError_t e = moe::launch_pair_hist(topk_ids, P, s->E, sbt * s->top_k, nsb, bc, hs);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(moe::launch_scatter(topk_ids, bc, nsb, P, s->E, sbt * s->top_k, counts, offsets, sorted_pairs,
+                                          inv_pos, hs));
+}
+
+int moe_expert_ffn(const moe_shape *s, const moe_bf16 *hidden, const moe_weights *w, const int32_t *offsets,
+                   const int32_t *sorted_pairs, const float *pair_scale, float *y_pairs, void *ws, size_t ws_bytes,
+                   void *stream)
+{
+    int st = validate(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;
+    if (!hidden || !w || !offsets || !sorted_pairs || !y_pairs) return MOE_ERR_NULL;
+    if (!aligned(hidden, 16) || !aligned(y_pairs, 16)) return MOE_ERR_ALIGN;
+    if ((st = check_qmat(w->gate)) || (st = check_qmat(w->up)) || (st = check_qmat(w->down))) return st;
+    if ((st = check_ws(s, MOE_WS_EXPERT_FFN, ws, ws_bytes))) return st;
+    const Layout L = layout(s, MOE_WS_EXPERT_FFN);
+    const int wbits = (s->flags & MOE_EXPERT_INT8) ? 8 : 4;
+    if (s->flags & MOE_TEST_GATEUP_SUMS) {
+        if (wbits != 4 || 2 * s->I > s->H) return MOE_ERR_UNSUPPORTED;
+        if (w->gate.q_stride_bytes != w->up.q_stride_bytes || w->gate.qs_stride_floats != w->up.qs_stride_floats)
+            return MOE_ERR_UNSUPPORTED;
+        FfnArgs g;
+        memset(&g, 0, sizeof(g));
+        g.A = hidden;
+        g.lda = s->H;
+        g.gather = sorted_pairs;
+        g.kdiv = s->top_k;
+        g.offsets = offsets;
+        g.E = s->E;
+        g.q0 = (const uint8_t *)w->gate.q;
+        g.s0 = w->gate.qs;
+        g.q1 = (const uint8_t *)w->up.q;
+        g.s1 = w->up.qs;
+        g.qstride = w->gate.q_stride_bytes;
+        g.sstride = w->gate.qs_stride_floats;
+        g.K = s->H;
+        g.N = s->I;
+        g.out = y_pairs;
+        g.ldo = s->H;
+        return hip_status(moe::launch_ffn(2, 4, g, s->T * s->top_k, s->E, (hipStream_t)stream));
+    }
+    return run_ffn(s, wbits, hidden, w->gate, w->up, w->down, s->I, offsets, sorted_pairs, s->E, s->top_k,
+                   s->T * s->top_k, pair_scale, at<float>(ws, L.hbuf), y_pairs, (hipStream_t)stream,
+                   (s->flags & MOE_STAGE_GATEUP_ONLY) != 0);
+}
+
+int moe_combine(const moe_shape *s, const float *y_pairs, const int32_t *inv_pos, const float *topk_w,
+                const float *shared_out, const moe_bf16 *residual, void *out, void *stream)
+{
+    int st = validate(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;
+    if (!y_pairs || !inv_pos || !out) return MOE_ERR_NULL;
+    if (!aligned(y_pairs, 16) || !aligned(out, 16) || (shared_out && !aligned(shared_out, 16)) ||
+        (residual && !aligned(residual, 8)))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_combine(y_pairs, inv_pos, topk_w, s->routed_scaling_factor, shared_out, residual,
+                                          out, s->T, s->H, s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0,
+                                          (hipStream_t)stream));
+}
+
+int moe_layer_forward(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out, void *ws,
+                      size_t ws_bytes, void *stream)
+{
+    int st = validate(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;
+    if (!w || !hidden || !out || !w->router_w || !w->router_bias) return MOE_ERR_NULL;
+    if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(w->router_w, 16)) return MOE_ERR_ALIGN;
+    if ((st = check_qmat(w->gate)) || (st = check_qmat(w->up)) || (st = check_qmat(w->down))) return st;
+    if (s->shared_bits &&
+        ((st = check_qmat(w->sh_gate)) || (st = check_qmat(w->sh_up)) || (st = check_qmat(w->sh_down))))
+        return st;
+    if ((st = check_ws(s, MOE_WS_LAYER, ws, ws_bytes))) return st;
+    if (w->gate.q_stride_bytes != w->up.q_stride_bytes || w->gate.qs_stride_floats != w->up.qs_stride_floats)
+        return MOE_ERR_UNSUPPORTED;
+    const Layout L = layout(s, MOE_WS_LAYER);
+    hipStream_t hs = (hipStream_t)stream;
+    const int P = s->T * s->top_k;
+    const int KS = moe::router_ks(s->T, s->H, s->E);
+    const int sbt = moe::superblock_tokens(s->top_k);
+    const int nsb = (s->T + sbt - 1) / sbt;
+    int32_t *ids = at<int32_t>(ws, L.ids), *sbc = at<int32_t>(ws, L.sbc);
+    int32_t *counts = at<int32_t>(ws, L.counts), *offsets = at<int32_t>(ws, L.offsets);
+    int32_t *sorted = at<int32_t>(ws, L.sorted), *inv = at<int32_t>(ws, L.inv);
+    float *pscale = at<float>(ws, L.pscale), *ypair = at<float>(ws, L.ypair);
+
+    hipError_t e = moe::launch_router(hidden, w->router_w, w->router_bias, s->T, s->H, s->E, s->top_k, s->n_group,
+                                      s->topk_group, s->routed_scaling_factor, at<float>(ws, L.zpart), KS, ids,
+                                      at<float>(ws, L.w), at<float>(ws, L.gap), pscale, sbc, hs);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = moe::launch_scatter(ids, sbc, nsb, P, s->E, sbt * s->top_k, counts, offsets, sorted, inv, hs);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    st = run_ffn(s, 4, hidden, w->gate, w->up, w->down, s->I, offsets, sorted, s->E, s->top_k, P, pscale,
+                 at<float>(ws, L.hbuf), ypair, hs);
+    if (st) return st;
+    const float *shy = nullptr;
+    if (s->shared_bits) {
+        st = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr, 1,
+                     1, s->T, nullptr, at<float>(ws, L.shh), at<float>(ws, L.shy), hs);
+        if (st) return st;
+        shy = at<float>(ws, L.shy);
+    }
+    return hip_status(moe::launch_combine(ypair, inv, nullptr, 1.f, shy,
+                                          (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr, out, s->T, s->H,
+                                          s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, hs));
+}
+
+int moe_layer_routing(const moe_shape *s, void *ws, size_t ws_bytes, int32_t **topk_ids, float **topk_w,
+                      int32_t **offsets, int32_t **sorted_pairs)
+{
+    int st = validate(s);
+    if (st) return st;
+    if ((st = check_ws(s, MOE_WS_LAYER, ws, ws_bytes))) return st;
+    const Layout L = layout(s, MOE_WS_LAYER);
+    if (topk_ids) *topk_ids = at<int32_t>(ws, L.ids);
+    if (topk_w) *topk_w = at<float>(ws, L.w);
+    if (offsets) *offsets = at<int32_t>(ws, L.offsets);
+    if (sorted_pairs) *sorted_pairs = at<int32_t>(ws, L.sorted);
+    return MOE_OK;
+}
+
+}  // extern "C"

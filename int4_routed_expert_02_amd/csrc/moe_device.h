@@ -1,0 +1,104 @@
+// moe_device.h -- device helpers shared by the gfx950 kernels of this library.
+//
+// Matrix-core operands: v_mfma_f32_16x16x32_bf16 takes, per lane, 8 bf16 of A
+// (row = lane % 16) and 8 bf16 of B (column = lane % 16); lane group g = lane / 16
+// owns a fixed set of 8 k-slots, the same set in A and B.  The accumulator
+// holds D[4*g + r][lane % 16] in element r.  Any one-to-one assignment of
+// actual k indices to the k-slots is valid as long as A and B use the same one;
+// the int4 path below uses that freedom to make the weight unpack cheap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// round to nearest even (finite values)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Eight packed int4 values -> eight bf16 holding q + 136, in k-slot order
+// (e0,e4),(e1,e5),(e2,e6),(e3,e7) where e_j is nibble j of w.
+// Flipping bit 3 of every nibble turns two's complement q into the offset
+// value n = q + 8 in [0, 15]; the bf16 with bit pattern 0x4300 | n is exactly
+// 128 + n.  One AND-OR per bf16 pair: the caller removes the constant 136 from
+// the dot product with 136 * (sum of the A row).
+constexpr float INT4_BIAS = 136.0f;
+
+__device__ __forceinline__ u32x4 unpack_int4x8(uint32_t w)
+{
+    w ^= 0x88888888u;
+    u32x4 r;
+    r[0] = (w & 0x000F000Fu) | 0x43004300u;
+    r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+    r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+    r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    return r;
+}
+
+// The matching A-side order: eight consecutive bf16 x0..x7 held as dwords
+// d = {x0x1, x2x3, x4x5, x6x7} become {x0x4, x1x5, x2x6, x3x7}.
+__device__ __forceinline__ u32x4 interleave_bf16x8(u32x4 d)
+{
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
+    r[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
+    r[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
+    r[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+    return r;
+}
+
+// Eight int8 values (two dwords, natural order) -> eight exact bf16.
+__device__ __forceinline__ u32x4 unpack_int8x8(u32x2 w)
+{
+    u32x4 r;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        int32_t v = (int32_t)w[d];
+        float f0 = (float)((v << 24) >> 24);
+        float f1 = (float)((v << 16) >> 24);
+        float f2 = (float)((v << 8) >> 24);
+        float f3 = (float)(v >> 24);
+        // small integers are exact in bf16: take the upper halves
+        r[2 * d] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+        r[2 * d + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
+    }
+    return r;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ float wave_sum_f32(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,45 @@
+// moe_launch.h -- host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct FfnArgs {
+    const void *A;  // bf16 rows (gate/up) or f32 rows (down)
+    int lda;
+    const int32_t *gather;
+    int kdiv;
+    const int32_t *pair_of_row;
+    const int32_t *offsets;
+    int E;
+    int M;
+    const uint8_t *q0;
+    const float *s0;
+    const uint8_t *q1;
+    const float *s1;
+    int64_t qstride;
+    int64_t sstride;
+    int K;
+    int N;
+    void *out;
+    int ldo;
+    const float *pscale;
+};
+
+int router_ks(int T, int H, int E);
+int router_select_blocks(int T);
+int superblock_tokens(int k);
+hipError_t launch_router(const uint16_t *x, const float *W, const float *bias, int T, int H, int E, int k,
+                         int n_group, int topk_group, float rsf, float *zpart, int KS, int32_t *ids, float *w,
+                         float *gap, float *pair_scale, int32_t *sbcounts, hipStream_t st);
+hipError_t launch_pair_hist(const int32_t *ids, int P, int E, int chunk, int nblocks, int32_t *bcounts,
+                            hipStream_t st);
+hipError_t launch_scatter(const int32_t *ids, const int32_t *bcounts, int nblocks, int P, int E, int chunk,
+                          int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *inv, hipStream_t st);
+hipError_t launch_ffn(int mode, int wbits, const FfnArgs &a, int rows_total, int groups, hipStream_t st);
+hipError_t launch_combine(const float *y, const int32_t *inv, const float *topk_w, float rsf, const float *sh,
+                          const uint16_t *res, void *out, int T, int H, int k, int out_f32, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,329 @@
+// router.hip -- router logits, sigmoid+bias selection, combine weights, per-block
+// expert histograms.
+//
+// The router is a sigmoid router whose per-expert bias only decides selection
+// (Colibri-Nano model card, "Architecture": sigmoid+bias router with
+// DeepSeek-V3-style aux-loss-free balancing), optionally group-limited
+// ("noaux_tc" in the colibri README's "What's implemented" list).
+//
+// Logits.  z = x . W_e with x in bf16 and W in f32.  Each f32 weight is split
+// exactly into three bf16 parts (w = hi + mid + lo: 8 + 8 + 8 significant
+// bits), so every product x * part is exact in f32 and the dot product runs on
+// bf16 matrix cores with f32 accumulation at three times the bf16 cost.  The K
+// (hidden) dimension may be split over workgroups; the partial sums are added
+// in a fixed order by the selection kernel, so results are deterministic.
+//
+// Selection.  One wavefront per token.  A lane holds up to four experts' scores
+// (lane l holds experts [l*EPL, (l+1)*EPL)); arg-max reductions across the wave
+// break ties toward the lower expert id.
+#include "moe_device.h"
+
+namespace moe {
+
+constexpr int RT_TB = 64;   // tokens per logits tile
+constexpr int RT_EB = 64;   // experts per logits tile
+constexpr int RT_BK = 64;   // hidden columns per k-step
+constexpr int RT_LDA = RT_BK + 8;  // padded LDS row (bf16 elements)
+
+// Split one f32 into three bf16 bit patterns whose exact sum is the input.
+__device__ __forceinline__ void split3(float w, uint32_t &hi, uint32_t &mid, uint32_t &lo)
+{
+    uint32_t u = __float_as_uint(w);
+    uint32_t h = u & 0xFFFF0000u;
+    float r1 = w - __uint_as_float(h);
+    uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
+    float r2 = r1 - __uint_as_float(m);
+    hi = h >> 16;
+    mid = m >> 16;
+    lo = __float_as_uint(r2) >> 16;  // r2 has at most 8 significant bits: exact
+}
+
+// grid: (ceil(T/RT_TB) * ceil(E/RT_EB), KS).  zpart[ks][t][e] f32.
+__global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restrict__ x, const float *__restrict__ W,
+                                                       float *__restrict__ zpart, int T, int H, int E, int ksteps_per_split,
+                                                       int32_t *__restrict__ clear, int clear_n)
+{
+    if (clear && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < clear_n; i += 256) clear[i] = 0;
+    __shared__ uint16_t sA[RT_TB * RT_LDA];
+    __shared__ uint16_t sB[3][RT_EB * RT_LDA];
+
+    const int n_eb = (E + RT_EB - 1) / RT_EB;
+    const int tb = blockIdx.x / n_eb;
+    const int eb = blockIdx.x % n_eb;
+    const int ks = blockIdx.y;
+    const int t0 = tb * RT_TB, e0 = eb * RT_EB;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, each 32 tokens x 32 experts
+
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int kbeg = ks * ksteps_per_split;
+    for (int kt = kbeg; kt < kbeg + ksteps_per_split; ++kt) {
+        const int k0 = kt * RT_BK;
+        // stage x: 64 rows x 64 bf16 = 512 chunks of 16 B, 2 per thread
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            int chunk = tid + c * 256;
+            int r = chunk >> 3, cc = chunk & 7;
+            int t = t0 + r;
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (t < T) v = *(const u32x4 *)(x + (size_t)t * H + k0 + cc * 8);
+            *(u32x4 *)(sA + r * RT_LDA + cc * 8) = v;
+        }
+        // stage W: 64 experts x 64 f32 = 1024 chunks of 4 floats, 4 per thread, split into 3 parts
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            int chunk = tid + c * 256;
+            int r = chunk >> 4, cc = chunk & 15;
+            int e = e0 + r;
+            f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (e < E) v = *(const f32x4 *)(W + (size_t)e * H + k0 + cc * 4);
+            uint32_t h[4], m[4], l[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) split3(v[i], h[i], m[i], l[i]);
+            u32x2 ph = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            u32x2 pm = u32x2{m[0] | (m[1] << 16), m[2] | (m[3] << 16)};
+            u32x2 pl = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+            *(u32x2 *)(sB[0] + r * RT_LDA + cc * 4) = ph;
+            *(u32x2 *)(sB[1] + r * RT_LDA + cc * 4) = pm;
+            *(u32x2 *)(sB[2] + r * RT_LDA + cc * 4) = pl;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < RT_BK; kk += 32) {
+            const int ko = kk + (lane >> 4) * 8;
+            u32x4 a[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = *(const u32x4 *)(sA + (wm * 32 + i * 16 + (lane & 15)) * RT_LDA + ko);
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    u32x4 b = *(const u32x4 *)(sB[p] + (wn * 32 + j * 16 + (lane & 15)) * RT_LDA + ko);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) acc[i][j] = mfma_bf16(a[i], b, acc[i][j]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float *zp = zpart + (size_t)ks * T * E;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                int t = t0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+                int e = e0 + wn * 32 + j * 16 + (lane & 15);
+                if (t < T && e < E) zp[(size_t)t * E + e] = acc[i][j][r];
+            }
+}
+
+struct ArgMax {
+    float v;
+    int i;
+};
+
+// larger value wins; equal values -> lower index; index < 0 means empty
+__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b)
+{
+    if (b.i < 0) return a;
+    if (a.i < 0) return b;
+    if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+    return a;
+}
+
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax a)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        ArgMax b;
+        b.v = __shfl_xor(a.v, o, WAVE);
+        b.i = __shfl_xor(a.i, o, WAVE);
+        a = better(a, b);
+    }
+    return a;
+}
+
+constexpr int SEL_TPW = 4;                 // tokens per wave
+constexpr int SEL_TOKENS = 4 * SEL_TPW;    // tokens per workgroup (4 waves)
+
+// One wave per token.  Writes ids, w, gap and optionally pair_scale (rsf * w
+// per pair).  When sbcounts is given, each workgroup adds the expert histogram
+// of its SEL_TOKENS tokens into sbcounts[superblock][E], a superblock being
+// sb_tokens consecutive tokens (integer atomics: the totals do not depend on
+// the order of the additions).
+template <int EPL>
+__global__ __launch_bounds__(256) void k_router_select(const float *__restrict__ zpart, int KS,
+                                                       const float *__restrict__ bias, int T, int E, int k,
+                                                       int n_group, int topk_group, float rsf,
+                                                       int32_t *__restrict__ ids, float *__restrict__ w,
+                                                       float *__restrict__ gap, float *__restrict__ pair_scale,
+                                                       int32_t *__restrict__ sbcounts, int sb_tokens)
+{
+    __shared__ int32_t hist[256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += 256) hist[e] = 0;
+    __syncthreads();
+
+    for (int it = 0; it < SEL_TPW; ++it) {
+        const int t = blockIdx.x * SEL_TOKENS + wave * SEL_TPW + it;
+        if (t >= T) break;
+        float s[EPL], b[EPL];
+        bool ok[EPL];
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) {
+            int e = lane * EPL + q;
+            ok[q] = e < E;
+            s[q] = 0.f;
+            b[q] = -INFINITY;
+            if (ok[q]) {
+                float z = 0.f;
+                for (int p = 0; p < KS; ++p) z += zpart[((size_t)p * T + t) * E + e];
+                s[q] = 1.0f / (1.0f + expf(-z));
+                b[q] = s[q] + bias[e];
+            }
+        }
+        float ggap = INFINITY;
+        if (n_group > 1 && topk_group < n_group) {
+            const int Eg = E / n_group;
+            float my_g = -INFINITY;  // lane g holds group g's score
+            for (int g = 0; g < n_group; ++g) {
+                ArgMax m1{-INFINITY, -1};
+#pragma unroll
+                for (int q = 0; q < EPL; ++q) {
+                    int e = lane * EPL + q;
+                    if (ok[q] && e / Eg == g) m1 = better(m1, ArgMax{b[q], e});
+                }
+                m1 = wave_argmax(m1);
+                ArgMax m2{-INFINITY, -1};
+#pragma unroll
+                for (int q = 0; q < EPL; ++q) {
+                    int e = lane * EPL + q;
+                    if (ok[q] && e / Eg == g && e != m1.i) m2 = better(m2, ArgMax{b[q], e});
+                }
+                m2 = wave_argmax(m2);
+                if (lane == g) my_g = m1.v + m2.v;
+            }
+            bool kept = false;
+            float last_kept = 0.f;
+            for (int r = 0; r < topk_group; ++r) {
+                ArgMax m = (lane < n_group && !kept) ? ArgMax{my_g, lane} : ArgMax{-INFINITY, -1};
+                m = wave_argmax(m);
+                if (lane == m.i) kept = true;
+                last_kept = m.v;
+            }
+            ArgMax d = (lane < n_group && !kept) ? ArgMax{my_g, lane} : ArgMax{-INFINITY, -1};
+            d = wave_argmax(d);
+            ggap = last_kept - d.v;
+            const uint64_t kept_mask = __ballot(kept);
+#pragma unroll
+            for (int q = 0; q < EPL; ++q) {
+                int e = lane * EPL + q;
+                if (ok[q] && !((kept_mask >> (e / Eg)) & 1ull)) ok[q] = false;
+            }
+        }
+        // top-k by repeated arg-max over the allowed experts
+        float ssum = 0.f;
+        float sel_s = 0.f;  // lane j keeps the unbiased score of selection j
+        float bk = 0.f;
+        for (int j = 0; j < k; ++j) {
+            ArgMax m{-INFINITY, -1};
+#pragma unroll
+            for (int q = 0; q < EPL; ++q)
+                if (ok[q]) m = better(m, ArgMax{b[q], lane * EPL + q});
+            m = wave_argmax(m);
+            bk = m.v;
+            float own = 0.f;
+#pragma unroll
+            for (int q = 0; q < EPL; ++q)
+                if (lane * EPL + q == m.i) {
+                    ok[q] = false;
+                    own = s[q];
+                }
+            const float sj = __shfl(own, m.i / EPL, WAVE);
+            ssum += sj;
+            if (lane == j) sel_s = sj;
+            if (lane == 0) {
+                ids[(size_t)t * k + j] = m.i;
+                atomicAdd(&hist[m.i], 1);
+            }
+        }
+        // the best remaining allowed score, for the tie gap
+        ArgMax nx{-INFINITY, -1};
+#pragma unroll
+        for (int q = 0; q < EPL; ++q)
+            if (ok[q]) nx = better(nx, ArgMax{b[q], lane * EPL + q});
+        nx = wave_argmax(nx);
+        if (lane < k) {
+            const float wj = sel_s / ssum;
+            w[(size_t)t * k + lane] = wj;
+            if (pair_scale) pair_scale[(size_t)t * k + lane] = rsf * wj;
+        }
+        if (lane == 0 && gap) {
+            const float g1 = nx.i >= 0 ? bk - nx.v : INFINITY;
+            gap[t] = fminf(g1, ggap);
+        }
+    }
+    __syncthreads();
+    if (sbcounts) {
+        const int sb = (blockIdx.x * SEL_TOKENS) / sb_tokens;
+        for (int e = tid; e < E; e += 256)
+            if (hist[e]) atomicAdd(&sbcounts[(size_t)sb * E + e], hist[e]);
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+
+int router_ks(int T, int H, int E)
+{
+    const int ksteps = H / RT_BK;
+    const int tiles = ((T + RT_TB - 1) / RT_TB) * ((E + RT_EB - 1) / RT_EB);
+    int ks = 1;
+    for (int c = 1; c <= ksteps; ++c) {
+        if (ksteps % c) continue;
+        ks = c;
+        if (tiles * c >= 256 || ksteps / c <= 2) break;
+    }
+    return ks;
+}
+
+int router_select_blocks(int T) { return (T + SEL_TOKENS - 1) / SEL_TOKENS; }
+
+// tokens per permutation superblock: about 1024 pairs, a multiple of SEL_TOKENS
+int superblock_tokens(int k)
+{
+    int t = (1024 / k) / SEL_TOKENS * SEL_TOKENS;
+    return t < SEL_TOKENS ? SEL_TOKENS : t;
+}
+
+hipError_t launch_router(const uint16_t *x, const float *W, const float *bias, int T, int H, int E, int k,
+                         int n_group, int topk_group, float rsf, float *zpart, int KS, int32_t *ids, float *w,
+                         float *gap, float *pair_scale, int32_t *sbcounts, hipStream_t st)
+{
+    const int ksteps = H / RT_BK;
+    const int sbt = superblock_tokens(k);
+    const int nsb = (T + sbt - 1) / sbt;
+    dim3 g1(((T + RT_TB - 1) / RT_TB) * ((E + RT_EB - 1) / RT_EB), KS);
+    hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, st, x, W, zpart, T, H, E, ksteps / KS, sbcounts,
+                       sbcounts ? nsb * E : 0);
+    const int nb = router_select_blocks(T);
+    if (E <= 64)
+        hipLaunchKernelGGL(k_router_select<1>, dim3(nb), dim3(256), 0, st, zpart, KS, bias, T, E, k, n_group,
+                           topk_group, rsf, ids, w, gap, pair_scale, sbcounts, sbt);
+    else if (E <= 128)
+        hipLaunchKernelGGL(k_router_select<2>, dim3(nb), dim3(256), 0, st, zpart, KS, bias, T, E, k, n_group,
+                           topk_group, rsf, ids, w, gap, pair_scale, sbcounts, sbt);
+    else
+        hipLaunchKernelGGL(k_router_select<4>, dim3(nb), dim3(256), 0, st, zpart, KS, bias, T, E, k, n_group,
+                           topk_group, rsf, ids, w, gap, pair_scale, sbcounts, sbt);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,96 @@
+"""Shared helpers of the GPU parity tests (device upload, workspace views, checks)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import int4_routed_expert_02_amd as moe
+import oracle
+import synth
+
+GAP_EXEMPT = 1e-5    # near-tie exemption of the routing comparison
+W_TOL = 1e-5         # combine-weight tolerance
+OUT_TOL = 1e-2       # max |gpu - oracle| <= OUT_TOL * RMS(oracle)
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(a_u16: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a_u16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def ws_view(ws, ptr: int, n: int, dtype):
+    import torch
+    itemsize = torch.tensor([], dtype=dtype).element_size()
+    off = ptr - ws.data_ptr()
+    return ws[off:off + n * itemsize].view(dtype)
+
+
+def run_layer(cfg, d, flags=moe.MOE_OUT_F32, hidden=None, layer=None):
+    """One moe_layer_forward call; returns output and the routing the GPU computed."""
+    import torch
+    layer = layer or moe.MoeLayer(cfg, d)
+    xh = d["hidden"] if hidden is None else hidden
+    x = dev_bf16(xh)
+    T = x.shape[0]
+    odt = torch.float32 if flags & moe.MOE_OUT_F32 else torch.bfloat16
+    out = torch.empty((T, cfg.H), dtype=odt, device="cuda")
+    ws = layer.workspace(T, flags)
+    layer.forward(x, out, ws, flags)
+    torch.cuda.synchronize()
+    sh = moe.shape_of(cfg, T, flags)
+    pid, pw, poff, psrt = moe.moe_layer_routing(sh, ws)
+    P = T * cfg.k
+    ids = ws_view(ws, pid, P, torch.int32).cpu().numpy().reshape(T, cfg.k)
+    w = ws_view(ws, pw, P, torch.float32).cpu().numpy().reshape(T, cfg.k)
+    offsets = ws_view(ws, poff, cfg.E + 1, torch.int32).cpu().numpy()
+    srt = ws_view(ws, psrt, P, torch.int32).cpu().numpy()
+    return out.float().cpu().numpy(), ids, w, offsets, srt
+
+
+def check_routing(cfg, d, hidden, ids, w, offsets, srt, tag=""):
+    """ids bit-exact and w within W_TOL outside near ties; permutation exact."""
+    o_ids, o_w, gap, ggap = oracle.router(cfg, hidden, d["router_w"], d["router_bias"])
+    exempt = (gap < GAP_EXEMPT) | (ggap < GAP_EXEMPT)
+    keep = ~exempt
+    bad = np.nonzero(np.any(ids[keep] != o_ids[keep], axis=1))[0]
+    assert bad.size == 0, f"{tag}: ids differ on {bad.size} non-exempt tokens, first {np.nonzero(keep)[0][bad[:5]]}"
+    if keep.any():
+        werr = float(np.max(np.abs(w[keep] - o_w[keep])))
+        assert werr <= W_TOL, f"{tag}: weight error {werr}"
+    # exempt tokens: still a valid selection (k distinct ids in range)
+    assert np.all((ids >= 0) & (ids < cfg.E))
+    assert all(len(set(r)) == cfg.k for r in ids.tolist())
+    counts, o_off, o_srt, _ = oracle.permute(cfg, ids)
+    assert np.array_equal(offsets, o_off), f"{tag}: offsets differ"
+    assert np.array_equal(srt, o_srt), f"{tag}: sorted pairs differ"
+    return int(exempt.sum())
+
+
+def check_output(cfg, d, hidden, got, ids, w, tokens=None, residual=False, bf16_out=False, tag=""):
+    """Output rows against the oracle driven by the same routing (ids checked separately)."""
+    lw = oracle.LayerWeights(cfg, d)
+    T = hidden.shape[0]
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    ref = oracle.layer_tokens(cfg, lw, hidden, toks, ids, w, residual=residual).astype(np.float64)
+    g = got[toks].astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    diff = np.abs(g - ref)
+    if bf16_out:
+        # the bf16 store adds up to half an ulp of the value itself
+        diff = np.maximum(diff - np.abs(ref) * 2.0 ** -8, 0.0)
+    err = float(diff.max()) / rms
+    say(f"{tag}: max|gpu-oracle|/rms = {err:.3e} (rms {rms:.4f}, {len(toks)} tokens)")
+    assert err <= OUT_TOL, f"{tag}: {err}"
+    return err
+
+
+def small_cfg(**kw):
+    base = dict(name="small", T=64, H=256, E=16, k=2, I=128, I_sh=256, seed=4242)
+    base.update(kw)
+    return synth.LayerConfig(**base)

@@ -1,0 +1,140 @@
+"""The C ABI library loads and exports every symbol include/moe.h declares, and
+its host-side validation answers without any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import int4_routed_expert_02_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from int4_routed_expert_02_amd import _build
+        _build.build()
+    m.load()
+    return m
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(moe):
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = moe.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(moe.EXPORTS) == set(names)
+
+
+def test_status_strings(moe):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert moe.status_string(code).startswith("MOE_")
+    assert moe.status_string(42) == "unknown status"
+
+
+def good(moe, **kw):
+    base = dict(T=16, H=1024, E=64, top_k=2, I=512, I_shared=2048, shared_bits=4, n_group=1, topk_group=1, rsf=1.0)
+    base.update(kw)
+    return moe.shape(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(top_k=65, E=64), -2),
+    (dict(T=-1), -2),
+    (dict(H=1023), -2),
+    (dict(shared_bits=3), -2),
+    (dict(E=64, n_group=3), -2),
+    (dict(E=64, n_group=8, topk_group=9), -2),
+    (dict(E=64, n_group=8, topk_group=1, top_k=9), -2),
+    (dict(E=8, n_group=8, topk_group=4), -2),
+    (dict(H=1000), -3),
+    (dict(I=500), -3),
+    (dict(I_shared=2000), -3),
+    (dict(E=512, top_k=2), -3),
+    (dict(shared_bits=0, I_shared=0), 0),
+    (dict(E=256, top_k=8, n_group=8, topk_group=4, H=6144, I=2048, rsf=2.5), 0),
+])
+def test_validation(moe, kw, code):
+    assert moe.moe_validate_shape(good(moe, **kw)) == code
+
+
+def test_workspace_sizes(moe):
+    s = good(moe)
+    assert moe.moe_workspace_bytes(s, moe.MOE_WS_LAYER) > 16 * 2 * 1024 * 4
+    assert moe.moe_workspace_bytes(s, moe.MOE_WS_PERMUTE) > 0
+    assert moe.moe_workspace_bytes(s, moe.MOE_WS_EXPERT_FFN) >= 32 * 512 * 2
+    assert moe.moe_workspace_bytes(good(moe, H=1000), moe.MOE_WS_LAYER) == 0
+    assert moe.moe_workspace_bytes(s, 99) == 0
+
+
+FAKE = 1 << 20  # an aligned address that is never dereferenced: every call below fails validation first
+
+
+def test_errors_before_any_enqueue(moe):
+    lib = moe.load()
+    vp = ctypes.c_void_p
+    w = moe.MoeWeights()
+    for f in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+        setattr(w, f, moe.MoeQMat(FAKE, FAKE, 0, 0))
+    w.router_w = FAKE
+    w.router_bias = FAKE
+    s = good(moe)
+    # bad shape
+    assert lib.moe_layer_forward(ctypes.byref(good(moe, H=1023)), ctypes.byref(w), vp(FAKE), vp(FAKE), vp(FAKE),
+                                 1 << 30, None) == moe.MOE_ERR_SHAPE
+    # null hidden
+    assert lib.moe_layer_forward(ctypes.byref(s), ctypes.byref(w), None, vp(FAKE), vp(FAKE), 1 << 30,
+                                 None) == moe.MOE_ERR_NULL
+    # misaligned hidden
+    assert lib.moe_layer_forward(ctypes.byref(s), ctypes.byref(w), vp(FAKE + 2), vp(FAKE), vp(FAKE), 1 << 30,
+                                 None) == moe.MOE_ERR_ALIGN
+    # misaligned weight stride
+    w2 = moe.MoeWeights.from_buffer_copy(w)
+    w2.gate = moe.MoeQMat(FAKE, FAKE, 24, 0)
+    assert lib.moe_layer_forward(ctypes.byref(s), ctypes.byref(w2), vp(FAKE), vp(FAKE), vp(FAKE), 1 << 30,
+                                 None) == moe.MOE_ERR_ALIGN
+    # workspace too small
+    need = moe.moe_workspace_bytes(s, moe.MOE_WS_LAYER)
+    assert lib.moe_layer_forward(ctypes.byref(s), ctypes.byref(w), vp(FAKE), vp(FAKE), vp(FAKE), need - 1,
+                                 None) == moe.MOE_ERR_WORKSPACE
+    # misaligned workspace
+    assert lib.moe_layer_forward(ctypes.byref(s), ctypes.byref(w), vp(FAKE), vp(FAKE), vp(FAKE + 16), need,
+                                 None) == moe.MOE_ERR_ALIGN
+    # gate/up with different expert strides are not covered
+    w3 = moe.MoeWeights.from_buffer_copy(w)
+    w3.up = moe.MoeQMat(FAKE, FAKE, 16, 0)
+    assert lib.moe_layer_forward(ctypes.byref(s), ctypes.byref(w3), vp(FAKE), vp(FAKE), vp(FAKE), need,
+                                 None) == moe.MOE_ERR_UNSUPPORTED
+    # T == 0 is a no-op
+    assert lib.moe_layer_forward(ctypes.byref(good(moe, T=0)), ctypes.byref(w), None, None, None, 0, None) == 0
+    assert lib.moe_router(ctypes.byref(good(moe, T=0)), None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.moe_permute(ctypes.byref(good(moe, T=0)), None, None, None, None, None, None, 0, None) == 0
+    # split calls validate too
+    assert lib.moe_router(ctypes.byref(s), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, vp(FAKE), 0,
+                          None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_combine(ctypes.byref(s), None, vp(FAKE), None, None, None, vp(FAKE), None) == moe.MOE_ERR_NULL
+    assert lib.moe_expert_ffn(ctypes.byref(good(moe, I=1024, flags=moe.MOE_TEST_GATEUP_SUMS)), vp(FAKE), ctypes.byref(w),
+                              vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_product_path_has_no_fallback(moe, tmp_path, monkeypatch):
+    """Without the built library the binding raises instead of computing anything."""
+    import importlib
+    import sys as _sys
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        moe.load()
+    # the package never imports the oracle
+    src = open(os.path.join(ROOT, "int4_routed_expert_02_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("oracle_", "")
+    assert "import oracle" not in src

@@ -1,0 +1,201 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: expert ids bit-exact except near-tie tokens (k-th/(k+1)-th biased score
+gap < 1e-5, or the group boundary gap for group-limited routing); combine
+weights within 1e-5; the permutation bit-exact (compared as the oracle's
+permutation of the GPU's ids); outputs max|gpu - oracle| <= 1e-2 * RMS(oracle)
+against the oracle's f32 math on the dequantised weights.
+"""
+import numpy as np
+import pytest
+
+import int4_routed_expert_02_amd as moe
+import oracle
+import synth
+from gpu_util import (check_output, check_routing, dev_bf16, run_layer, say, small_cfg, ws_view)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.load()
+
+
+SMALL = {
+    "c0": synth.CONFIGS["c0"],
+    "c0_T100_ragged": synth.CONFIGS["c0"].with_(T=100, seed=11),
+    "T1": synth.CONFIGS["c0"].with_(T=1, seed=12),
+    "E8_small": small_cfg(E=8, T=50),
+    "grouped_E32_k4": small_cfg(E=32, k=4, n_group=4, topk_group=2, rsf=2.5, T=64),
+    "grouped_E64_k8_g8": small_cfg(E=64, k=8, n_group=8, topk_group=4, rsf=2.5, T=40, I=64, I_sh=128),
+    "E256_k8_g8": small_cfg(E=256, k=8, n_group=8, topk_group=4, rsf=2.5, T=24, H=256, I=64, I_sh=64),
+    "no_shared": small_cfg(shared_bits=0, T=70),
+    "int8_shared": small_cfg(shared_bits=8, T=70),
+    "c2_shape_T700": synth.CONFIGS["c2"].with_(T=700, seed=21),
+    "c2_shape_T2000": synth.CONFIGS["c2"].with_(T=2000, seed=22),
+    "c4_shape_T1500": synth.CONFIGS["c4"].with_(T=1500, seed=23),
+    "c3_shape_T6": synth.CONFIGS["c3"].with_(T=6, seed=24),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_layer_parity_small(name):
+    cfg = SMALL[name]
+    say(f"[layer parity] {name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} shared={cfg.shared_bits}")
+    d = synth.layer(cfg)
+    got, ids, w, offsets, srt = run_layer(cfg, d)
+    ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag=name)
+    check_output(cfg, d, d["hidden"], got, ids, w, tag=f"{name} (exempt {ex})")
+
+
+def test_many_rows_per_expert_and_empty_experts():
+    """Bias forces every token onto experts 3 and 9: multi-tile experts, 14 empty experts."""
+    cfg = small_cfg(T=300, E=16)
+    d = synth.layer(cfg)
+    d["router_bias"][3] += 10.0
+    d["router_bias"][9] += 9.0
+    got, ids, w, offsets, srt = run_layer(cfg, d)
+    assert set(np.unique(ids)) == {3, 9}
+    check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag="two experts")
+    check_output(cfg, d, d["hidden"], got, ids, w, tag="two experts")
+
+
+def test_bf16_output_with_residual():
+    cfg = synth.CONFIGS["c0"].with_(T=48, seed=31)
+    d = synth.layer(cfg)
+    flags = moe.MOE_ADD_RESIDUAL
+    got, ids, w, offsets, srt = run_layer(cfg, d, flags=flags)
+    check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag="bf16+res")
+    check_output(cfg, d, d["hidden"], got, ids, w, residual=True, bf16_out=True, tag="bf16+res")
+
+
+def test_deterministic_bits():
+    cfg = synth.CONFIGS["c2"].with_(T=1000, seed=41)
+    d = synth.layer(cfg)
+    layer = moe.MoeLayer(cfg, d)
+    a = run_layer(cfg, d, layer=layer)
+    b = run_layer(cfg, d, layer=layer)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("T", [8, 40, 400, 1500])
+def test_integer_exact_gateup_sums(T):
+    """Integer-valued x (|x| <= 8) and int4 weights: every product and partial sum
+    is an integer below 2^24, so the raw gate/up sums are exact and must equal the
+    oracle's bit for bit (this pins the unpack, the k-slot order and the 136*rowsum
+    correction)."""
+    import torch
+    cfg = small_cfg(T=T, E=8, k=2, H=256, I=64, seed=50 + T)
+    d = synth.layer(cfg)
+    x = synth.small_int_hidden(cfg, 8)
+    lw = oracle.LayerWeights(cfg, d)
+    o_ids, _, _, _ = oracle.router(cfg, x, d["router_w"], d["router_bias"])
+    _, offsets, srt, _ = oracle.permute(cfg, o_ids)
+    g_ref, u_ref = oracle.gateup_int_sums(cfg, x, lw, offsets, srt)
+    layer = moe.MoeLayer(cfg, d)
+    sh = moe.shape_of(cfg, T, moe.MOE_TEST_GATEUP_SUMS)
+    y = torch.zeros((T * cfg.k, cfg.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(sh, moe.MOE_WS_EXPERT_FFN), dtype=torch.uint8, device="cuda")
+    moe.moe_expert_ffn(sh, dev_bf16(x), layer.weights, torch.from_numpy(offsets).cuda(),
+                       torch.from_numpy(srt).cuda(), None, y, ws)
+    torch.cuda.synchronize()
+    yc = y.cpu().numpy().astype(np.float64)
+    assert np.array_equal(yc[:, :cfg.I], g_ref)
+    assert np.array_equal(yc[:, cfg.I:2 * cfg.I], u_ref)
+
+
+def test_split_api_matches_oracle():
+    """router -> permute -> expert_ffn (routed, pre-scaled) -> expert_ffn (shared) -> combine."""
+    import torch
+    cfg = synth.CONFIGS["c0"].with_(T=64, seed=61, rsf=1.5)
+    d = synth.layer(cfg)
+    layer = moe.MoeLayer(cfg, d)
+    T, k, E, H = cfg.T, cfg.k, cfg.E, cfg.H
+    sh = moe.shape_of(cfg)
+    x = dev_bf16(d["hidden"])
+    dv = dict(device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, **dv)
+    w = torch.empty((T, k), dtype=torch.float32, **dv)
+    gap = torch.empty((T,), dtype=torch.float32, **dv)
+    wsp = torch.empty(moe.moe_workspace_bytes(sh, moe.MOE_WS_PERMUTE), dtype=torch.uint8, **dv)
+    moe.moe_router(sh, x, layer.router_w, layer.router_bias, ids, w, gap, wsp)
+    counts = torch.empty((E,), dtype=torch.int32, **dv)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, **dv)
+    srt = torch.empty((T * k,), dtype=torch.int32, **dv)
+    inv = torch.empty((T * k,), dtype=torch.int32, **dv)
+    moe.moe_permute(sh, ids, counts, offsets, srt, inv, wsp)
+    torch.cuda.synchronize()
+    ids_c, w_c = ids.cpu().numpy(), w.cpu().numpy()
+    check_routing(cfg, d, d["hidden"], ids_c, w_c, offsets.cpu().numpy(), srt.cpu().numpy(), tag="split")
+    o_counts, _, _, o_inv = oracle.permute(cfg, ids_c)
+    assert np.array_equal(counts.cpu().numpy(), o_counts) and np.array_equal(inv.cpu().numpy(), o_inv)
+    # routed experts, pre-scaled by rsf * w
+    y = torch.empty((T * k, H), dtype=torch.float32, **dv)
+    wsf = torch.empty(moe.moe_workspace_bytes(sh, moe.MOE_WS_EXPERT_FFN), dtype=torch.uint8, **dv)
+    pscale = (w * cfg.rsf).reshape(-1).contiguous()
+    moe.moe_expert_ffn(sh, x, layer.weights, offsets, srt, pscale, y, wsf)
+    # shared expert through the same call: E = 1, k = 1, identity permutation
+    sh1 = moe.shape(T, H, 1, 1, cfg.I_sh, 0, 0, 1, 1, 1.0, 0)
+    w1 = moe.MoeWeights()
+    w1.gate, w1.up, w1.down = layer.weights.sh_gate, layer.weights.sh_up, layer.weights.sh_down
+    off1 = torch.tensor([0, T], dtype=torch.int32, **dv)
+    ident = torch.arange(T, dtype=torch.int32, **dv)
+    ysh = torch.empty((T, H), dtype=torch.float32, **dv)
+    ws1 = torch.empty(moe.moe_workspace_bytes(sh1, moe.MOE_WS_EXPERT_FFN), dtype=torch.uint8, **dv)
+    moe.moe_expert_ffn(sh1, x, w1, off1, ident, None, ysh, ws1)
+    out = torch.empty((T, H), dtype=torch.float32, **dv)
+    moe.moe_combine(moe.shape_of(cfg, flags=moe.MOE_OUT_F32), y, inv, None, ysh, None, out)
+    # and the unscaled form: combine applies rsf * w itself
+    y2 = torch.empty_like(y)
+    moe.moe_expert_ffn(sh, x, layer.weights, offsets, srt, None, y2, wsf)
+    out2 = torch.empty_like(out)
+    moe.moe_combine(moe.shape_of(cfg, flags=moe.MOE_OUT_F32), y2, inv, w, ysh, None, out2)
+    torch.cuda.synchronize()
+    lw = oracle.LayerWeights(cfg, d)
+    ref_sh = oracle.shared_ffn(cfg, d["hidden"], lw)
+    err_sh = np.abs(ysh.cpu().numpy() - ref_sh).max() / np.sqrt(np.mean(ref_sh.astype(np.float64) ** 2))
+    say(f"split: shared expert max err/rms {err_sh:.3e}")
+    assert err_sh <= 1e-2
+    check_output(cfg, d, d["hidden"], out.cpu().numpy(), ids_c, w_c, tag="split pre-scaled")
+    check_output(cfg, d, d["hidden"], out2.cpu().numpy(), ids_c, w_c, tag="split combine-scaled")
+
+
+FULL = ["c0", "c2", "c4", "c3"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    """The full workload in the benchmark's launch configuration (moe_layer_forward,
+    f32 output); routing and permutation checked on every token, outputs on a
+    seeded sample of tokens the oracle computes one by one."""
+    cfg = synth.CONFIGS[name]
+    say(f"[full] {name}: generating T={cfg.T} E={cfg.E} H={cfg.H}")
+    d = synth.layer(cfg)
+    got, ids, w, offsets, srt = run_layer(cfg, d)
+    ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag=name)
+    rng = np.random.default_rng(7)
+    n = min(cfg.T, 24 if cfg.H > 2048 else 64)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n, replace=False)]))
+    check_output(cfg, d, d["hidden"], got, ids, w, tokens=toks, tag=f"{name} (exempt {ex})")
+    counts = np.diff(offsets)
+    say(f"{name}: rows per expert max {counts.max()} min {counts.min()} active {np.count_nonzero(counts)}")
+
+
+def test_decode_stack_teacher_forced():
+    """The benchmark's decode step: 23 stacked layers, T=32, bf16 out with the
+    residual added, each layer checked against the oracle on the GPU's own input
+    to that layer (teacher forcing), all tokens."""
+    import torch
+    cfg = synth.CONFIGS["c1"]
+    x = synth.hidden(cfg, 0)
+    flags = moe.MOE_ADD_RESIDUAL
+    for l in range(cfg.layers):
+        d = synth.layer(cfg, l, with_hidden=False)
+        got, ids, w, offsets, srt = run_layer(cfg, d, flags=flags, hidden=x)
+        check_routing(cfg, d, x, ids, w, offsets, srt, tag=f"c1 layer {l}")
+        check_output(cfg, d, x, got, ids, w, residual=True, bf16_out=True, tag=f"c1 layer {l}")
+        x = torch.from_numpy(got.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
