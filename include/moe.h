@@ -190,6 +190,15 @@ int moe_combine(const moe_shape *shape, const float *y_pairs, const int32_t *inv
 int moe_layer_forward(const moe_shape *shape, const moe_weights *weights, const moe_bf16 *hidden, void *out,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* moe_layer_forward with two HIP events (hipEvent_t as void*, nullable) recorded
+ * on `stream` immediately before and after the expert gate/up kernel: the
+ * grouped gate/up + SwiGLU GEMM of the routed experts (tiled regime) or the
+ * gate/up weight stream of routed and shared experts (small-batch regime).
+ * For measuring that kernel inside a real layer pass; results are identical
+ * to moe_layer_forward. */
+int moe_layer_forward_profiled(const moe_shape *shape, const moe_weights *weights, const moe_bf16 *hidden,
+                               void *out, void *ws, size_t ws_bytes, void *stream, void *ev_start, void *ev_stop);
+
 /* Bytes of workspace a call needs for this shape (0 for an invalid shape). */
 size_t moe_workspace_bytes(const moe_shape *shape, int which);
 
@@ -202,7 +211,10 @@ const char *moe_status_string(int status);
 /* The layer-forward workspace also exposes, for inspection after a call, the
  * routing it computed: moe_layer_routing(ws, shape, ...) returns device
  * pointers into ws (ids [T][k], w [T][k], offsets [E+1], sorted [T*k]).
- * Pointers stay valid until the workspace is reused. */
+ * Pointers stay valid until the workspace is reused.  In the small-batch
+ * regime (T <= 32, H % 1024 == 0, I % 512 == 0, I_shared % 512 == 0) each
+ * expert kernel gathers its own pairs and no sorted list is materialised:
+ * offsets and sorted_pairs are then returned as NULL. */
 int moe_layer_routing(const moe_shape *shape, void *ws, size_t ws_bytes, int32_t **topk_ids, float **topk_w,
                       int32_t **offsets, int32_t **sorted_pairs);
 

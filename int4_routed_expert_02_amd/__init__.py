@@ -37,7 +37,8 @@ MOE_WS_EXPERT_FFN = 2
 MOE_WS_LAYER = 3
 
 EXPORTS = ["moe_router", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_workspace_bytes", "moe_validate_shape", "moe_status_string", "moe_layer_routing"]
+           "moe_layer_forward_profiled", "moe_workspace_bytes", "moe_validate_shape", "moe_status_string",
+           "moe_layer_routing"]
 
 
 class MoeShape(ctypes.Structure):
@@ -84,6 +85,7 @@ def load() -> ctypes.CDLL:
             "moe_expert_ffn": [S, vp, W, vp, vp, vp, vp, vp, sz, vp],
             "moe_combine": [S, vp, vp, vp, vp, vp, vp, vp],
             "moe_layer_forward": [S, W, vp, vp, vp, sz, vp],
+            "moe_layer_forward_profiled": [S, W, vp, vp, vp, sz, vp, vp, vp],
             "moe_validate_shape": [S],
             "moe_layer_routing": [S, vp, sz, vp, vp, vp, vp],
         }
@@ -172,6 +174,13 @@ def moe_combine(sh: MoeShape, y_pairs, inv_pos, topk_w, shared_out, residual, ou
 def moe_layer_forward(sh: MoeShape, weights: MoeWeights, hidden, out, ws, stream=None):
     _check(load().moe_layer_forward(ctypes.byref(sh), ctypes.byref(weights), _ptr(hidden), _ptr(out), _ptr(ws),
                                     ws.numel() if ws is not None else 0, _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_profiled(sh: MoeShape, weights: MoeWeights, hidden, out, ws, ev_start, ev_stop, stream=None):
+    """moe_layer_forward with torch.cuda.Event objects recorded around the expert gate/up kernel."""
+    _check(load().moe_layer_forward_profiled(ctypes.byref(sh), ctypes.byref(weights), _ptr(hidden), _ptr(out),
+                                             _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream),
+                                             ev_start.cuda_event, ev_stop.cuda_event), "moe_layer_forward_profiled")
 
 
 def moe_layer_routing(sh: MoeShape, ws):

@@ -48,7 +48,13 @@ int check_qmat(const moe_qmat &m)
 // Workspace sections, in bytes, each 256-aligned.
 struct Layout {
     size_t zpart, sbc, ids, w, gap, pscale, counts, offsets, sorted, inv, hbuf, shh, ypair, shy, total;
+    bool decode;  // the small-batch path serves this shape (MOE_WS_LAYER)
 };
+
+bool use_decode(const moe_shape *s)
+{
+    return moe::decode_supported(s->T, s->H, s->E, s->top_k, s->I, s->I_shared, s->shared_bits);
+}
 
 Layout layout(const moe_shape *s, int which)
 {
@@ -70,6 +76,20 @@ Layout layout(const moe_shape *s, int which)
         L.zpart = L.sbc = take(a > b ? a : b);
     } else if (which == MOE_WS_EXPERT_FFN) {
         L.hbuf = take(P * (size_t)s->I * 4);
+    } else if (use_decode(s)) {
+        // pair-indexed buffers, no permutation; shy holds the shared expert's
+        // partial sums over 512-column chunks of its intermediate dimension
+        L.decode = true;
+        L.ids = take(P * 4);
+        L.w = take(P * 4);
+        L.gap = take(T * 4);
+        L.pscale = take(P * 4);
+        L.hbuf = take(P * (size_t)s->I * 4);
+        L.ypair = take((size_t)(s->I / 512) * P * (size_t)s->H * 4);
+        if (s->shared_bits) {
+            L.shh = take(T * (size_t)s->I_shared * 4);
+            L.shy = take((size_t)(s->I_shared / 512) * T * (size_t)s->H * 4);
+        }
     } else {
         L.zpart = take((size_t)KS * T * E * 4);
         L.sbc = take(nsb * E * 4);
@@ -109,6 +129,10 @@ int check_ws(const moe_shape *s, int which, void *ws, size_t ws_bytes)
     return MOE_OK;
 }
 
+int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
+                 const int32_t *sorted, int E, int rows, const float *pscale, const float *hbuf, float *y,
+                 hipStream_t st);
+
 // The two grouped GEMMs of one expert family on sorted rows.
 int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qmat &gate, const moe_qmat &up,
             const moe_qmat &down, int I, const int32_t *offsets, const int32_t *sorted, int E, int kdiv, int rows,
@@ -138,6 +162,14 @@ int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qma
     hipError_t e = moe::launch_ffn(0, wbits, g, rows, offsets ? E : 1, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (gateup_only) return MOE_OK;
+    return run_ffn_down(s, wbits, down, I, offsets, sorted, E, rows, pscale, hbuf, y, st);
+}
+
+// The down GEMM on h (f32) of sorted rows.
+int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
+                 const int32_t *sorted, int E, int rows, const float *pscale, const float *hbuf, float *y,
+                 hipStream_t st)
+{
     FfnArgs d;
     memset(&d, 0, sizeof(d));
     d.A = hbuf;
@@ -283,6 +315,12 @@ int moe_combine(const moe_shape *s, const float *y_pairs, const int32_t *inv_pos
 int moe_layer_forward(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out, void *ws,
                       size_t ws_bytes, void *stream)
 {
+    return moe_layer_forward_profiled(s, w, hidden, out, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out,
+                               void *ws, size_t ws_bytes, void *stream, void *ev_start, void *ev_stop)
+{
     int st = validate(s);
     if (st) return st;
     if (s->T == 0) return MOE_OK;
@@ -297,6 +335,55 @@ int moe_layer_forward(const moe_shape *s, const moe_weights *w, const moe_bf16 *
         return MOE_ERR_UNSUPPORTED;
     const Layout L = layout(s, MOE_WS_LAYER);
     hipStream_t hs = (hipStream_t)stream;
+    if (L.decode) {
+        moe::DecLaunch d;
+        memset(&d, 0, sizeof(d));
+        d.x = hidden;
+        d.rw = w->router_w;
+        d.rb = w->router_bias;
+        d.T = s->T;
+        d.H = s->H;
+        d.E = s->E;
+        d.k = s->top_k;
+        d.n_group = s->n_group;
+        d.topk_group = s->topk_group;
+        d.rsf = s->routed_scaling_factor;
+        d.ids = at<int32_t>(ws, L.ids);
+        d.w = at<float>(ws, L.w);
+        d.gap = at<float>(ws, L.gap);
+        d.pscale = at<float>(ws, L.pscale);
+        d.gq = (const uint8_t *)w->gate.q;
+        d.uq = (const uint8_t *)w->up.q;
+        d.dq = (const uint8_t *)w->down.q;
+        d.gs = w->gate.qs;
+        d.us = w->up.qs;
+        d.ds = w->down.qs;
+        d.qstride = w->gate.q_stride_bytes;
+        d.dqstride = w->down.q_stride_bytes;
+        d.sstride = w->gate.qs_stride_floats;
+        d.dsstride = w->down.qs_stride_floats;
+        d.I = s->I;
+        if (s->shared_bits) {
+            d.sgq = (const uint8_t *)w->sh_gate.q;
+            d.suq = (const uint8_t *)w->sh_up.q;
+            d.sdq = (const uint8_t *)w->sh_down.q;
+            d.sgs = w->sh_gate.qs;
+            d.sus = w->sh_up.qs;
+            d.sds = w->sh_down.qs;
+            d.shh = at<float>(ws, L.shh);
+            d.shp = at<float>(ws, L.shy);
+        }
+        d.Ish = s->I_shared;
+        d.sh_bits = s->shared_bits;
+        d.h = at<float>(ws, L.hbuf);
+        d.y = at<float>(ws, L.ypair);
+        d.res = (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr;
+        d.out = out;
+        d.out_f32 = (s->flags & MOE_OUT_F32) ? 1 : 0;
+        d.ev0 = (hipEvent_t)ev_start;
+        d.ev1 = (hipEvent_t)ev_stop;
+        return hip_status(moe::launch_decode(d, hs));
+    }
     const int P = s->T * s->top_k;
     const int KS = moe::router_ks(s->T, s->H, s->E);
     const int sbt = moe::superblock_tokens(s->top_k);
@@ -312,9 +399,16 @@ int moe_layer_forward(const moe_shape *s, const moe_weights *w, const moe_bf16 *
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = moe::launch_scatter(ids, sbc, nsb, P, s->E, sbt * s->top_k, counts, offsets, sorted, inv, hs);
     if (e != hipSuccess) return MOE_ERR_HIP;
+    if (ev_start && hipEventRecord((hipEvent_t)ev_start, hs) != hipSuccess) return MOE_ERR_HIP;
     st = run_ffn(s, 4, hidden, w->gate, w->up, w->down, s->I, offsets, sorted, s->E, s->top_k, P, pscale,
-                 at<float>(ws, L.hbuf), ypair, hs);
+                 at<float>(ws, L.hbuf), ypair, hs, ev_stop != nullptr);
     if (st) return st;
+    if (ev_stop) {
+        // profiled: the routed gate/up kernel ran alone between the events; now the down GEMM
+        if (hipEventRecord((hipEvent_t)ev_stop, hs) != hipSuccess) return MOE_ERR_HIP;
+        st = run_ffn_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, at<float>(ws, L.hbuf), ypair, hs);
+        if (st) return st;
+    }
     const float *shy = nullptr;
     if (s->shared_bits) {
         st = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr, 1,
@@ -336,8 +430,8 @@ int moe_layer_routing(const moe_shape *s, void *ws, size_t ws_bytes, int32_t **t
     const Layout L = layout(s, MOE_WS_LAYER);
     if (topk_ids) *topk_ids = at<int32_t>(ws, L.ids);
     if (topk_w) *topk_w = at<float>(ws, L.w);
-    if (offsets) *offsets = at<int32_t>(ws, L.offsets);
-    if (sorted_pairs) *sorted_pairs = at<int32_t>(ws, L.sorted);
+    if (offsets) *offsets = L.decode ? nullptr : at<int32_t>(ws, L.offsets);
+    if (sorted_pairs) *sorted_pairs = L.decode ? nullptr : at<int32_t>(ws, L.sorted);
     return MOE_OK;
 }
 

@@ -94,6 +94,9 @@ __device__ __forceinline__ u32x4 unpack_int8x8(u32x2 w)
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// z * sigmoid(z) with the hardware reciprocal (about 1 ulp): for epilogues
+__device__ __forceinline__ float fast_silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
 __device__ __forceinline__ float wave_sum_f32(float v)
 {
 #pragma unroll

@@ -28,6 +28,30 @@ struct FfnArgs {
     const float *pscale;
 };
 
+// small-batch regime (decode.hip)
+struct DecLaunch {
+    const uint16_t *x;
+    const float *rw, *rb;
+    int T, H, E, k, n_group, topk_group;
+    float rsf;
+    int32_t *ids;
+    float *w, *gap, *pscale;
+    const uint8_t *gq, *uq, *dq;
+    const float *gs, *us, *ds;
+    int64_t qstride, dqstride, sstride, dsstride;
+    int I;
+    const uint8_t *sgq, *suq, *sdq;
+    const float *sgs, *sus, *sds;
+    int Ish, sh_bits;
+    float *h, *shh, *y, *shp;
+    const uint16_t *res;
+    void *out;
+    int out_f32;
+    hipEvent_t ev0, ev1;  // nullable: recorded around the gate/up kernel
+};
+bool decode_supported(int T, int H, int E, int k, int I, int Ish, int sh_bits);
+hipError_t launch_decode(const DecLaunch &d, hipStream_t st);
+
 int router_ks(int T, int H, int E);
 int router_select_blocks(int T);
 int superblock_tokens(int k);

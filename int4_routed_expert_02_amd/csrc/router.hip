@@ -17,6 +17,7 @@
 // (lane l holds experts [l*EPL, (l+1)*EPL)); arg-max reductions across the wave
 // break ties toward the lower expert id.
 #include "moe_device.h"
+#include "moe_select.h"
 
 namespace moe {
 
@@ -125,32 +126,6 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restric
             }
 }
 
-struct ArgMax {
-    float v;
-    int i;
-};
-
-// larger value wins; equal values -> lower index; index < 0 means empty
-__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b)
-{
-    if (b.i < 0) return a;
-    if (a.i < 0) return b;
-    if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
-    return a;
-}
-
-__device__ __forceinline__ ArgMax wave_argmax(ArgMax a)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        ArgMax b;
-        b.v = __shfl_xor(a.v, o, WAVE);
-        b.i = __shfl_xor(a.i, o, WAVE);
-        a = better(a, b);
-    }
-    return a;
-}
-
 constexpr int SEL_TPW = 4;                 // tokens per wave
 constexpr int SEL_TOKENS = 4 * SEL_TPW;    // tokens per workgroup (4 waves)
 
@@ -190,86 +165,7 @@ __global__ __launch_bounds__(256) void k_router_select(const float *__restrict__
                 b[q] = s[q] + bias[e];
             }
         }
-        float ggap = INFINITY;
-        if (n_group > 1 && topk_group < n_group) {
-            const int Eg = E / n_group;
-            float my_g = -INFINITY;  // lane g holds group g's score
-            for (int g = 0; g < n_group; ++g) {
-                ArgMax m1{-INFINITY, -1};
-#pragma unroll
-                for (int q = 0; q < EPL; ++q) {
-                    int e = lane * EPL + q;
-                    if (ok[q] && e / Eg == g) m1 = better(m1, ArgMax{b[q], e});
-                }
-                m1 = wave_argmax(m1);
-                ArgMax m2{-INFINITY, -1};
-#pragma unroll
-                for (int q = 0; q < EPL; ++q) {
-                    int e = lane * EPL + q;
-                    if (ok[q] && e / Eg == g && e != m1.i) m2 = better(m2, ArgMax{b[q], e});
-                }
-                m2 = wave_argmax(m2);
-                if (lane == g) my_g = m1.v + m2.v;
-            }
-            bool kept = false;
-            float last_kept = 0.f;
-            for (int r = 0; r < topk_group; ++r) {
-                ArgMax m = (lane < n_group && !kept) ? ArgMax{my_g, lane} : ArgMax{-INFINITY, -1};
-                m = wave_argmax(m);
-                if (lane == m.i) kept = true;
-                last_kept = m.v;
-            }
-            ArgMax d = (lane < n_group && !kept) ? ArgMax{my_g, lane} : ArgMax{-INFINITY, -1};
-            d = wave_argmax(d);
-            ggap = last_kept - d.v;
-            const uint64_t kept_mask = __ballot(kept);
-#pragma unroll
-            for (int q = 0; q < EPL; ++q) {
-                int e = lane * EPL + q;
-                if (ok[q] && !((kept_mask >> (e / Eg)) & 1ull)) ok[q] = false;
-            }
-        }
-        // top-k by repeated arg-max over the allowed experts
-        float ssum = 0.f;
-        float sel_s = 0.f;  // lane j keeps the unbiased score of selection j
-        float bk = 0.f;
-        for (int j = 0; j < k; ++j) {
-            ArgMax m{-INFINITY, -1};
-#pragma unroll
-            for (int q = 0; q < EPL; ++q)
-                if (ok[q]) m = better(m, ArgMax{b[q], lane * EPL + q});
-            m = wave_argmax(m);
-            bk = m.v;
-            float own = 0.f;
-#pragma unroll
-            for (int q = 0; q < EPL; ++q)
-                if (lane * EPL + q == m.i) {
-                    ok[q] = false;
-                    own = s[q];
-                }
-            const float sj = __shfl(own, m.i / EPL, WAVE);
-            ssum += sj;
-            if (lane == j) sel_s = sj;
-            if (lane == 0) {
-                ids[(size_t)t * k + j] = m.i;
-                atomicAdd(&hist[m.i], 1);
-            }
-        }
-        // the best remaining allowed score, for the tie gap
-        ArgMax nx{-INFINITY, -1};
-#pragma unroll
-        for (int q = 0; q < EPL; ++q)
-            if (ok[q]) nx = better(nx, ArgMax{b[q], lane * EPL + q});
-        nx = wave_argmax(nx);
-        if (lane < k) {
-            const float wj = sel_s / ssum;
-            w[(size_t)t * k + lane] = wj;
-            if (pair_scale) pair_scale[(size_t)t * k + lane] = rsf * wj;
-        }
-        if (lane == 0 && gap) {
-            const float g1 = nx.i >= 0 ? bk - nx.v : INFINITY;
-            gap[t] = fminf(g1, ggap);
-        }
+        select_token<EPL>(s, b, ok, lane, t, E, k, n_group, topk_group, rsf, ids, w, gap, pair_scale, hist);
     }
     __syncthreads();
     if (sbcounts) {
