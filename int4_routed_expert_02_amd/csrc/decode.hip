@@ -116,9 +116,11 @@ __global__ __launch_bounds__(256) void k_dec_route(const uint16_t *__restrict__ 
 
 // ------------------------------------------------------------- pair lists
 
-// Pairs routed to expert e in ascending order -> list; returns the count.
+// Pairs routed to expert e in ascending order -> list (and their tokens ->
+// tok); returns the count.
 // Called by the whole workgroup; the result is in LDS after the barrier.
-__device__ __forceinline__ int gather_pairs(const int32_t *__restrict__ ids, int P, int e, int *list, int *cnt)
+__device__ __forceinline__ int gather_pairs(const int32_t *__restrict__ ids, int P, int k, int e, int *list,
+                                            int *tok, int *cnt)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     if (tid < WAVE) {
@@ -127,13 +129,48 @@ __device__ __forceinline__ int gather_pairs(const int32_t *__restrict__ ids, int
             const int p = p0 + lane;
             const bool hit = p < P && ids[p] == e;
             const uint64_t m = __ballot(hit);
-            if (hit) list[n + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = p;
+            if (hit) {
+                const int slot = n + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+                list[slot] = p;
+                tok[slot] = p / k;
+            }
             n += __popcll(m);
         }
         if (lane == 0) *cnt = n;
     }
     __syncthreads();
     return *cnt;
+}
+
+// The rank-th active expert (ascending id) of this batch, or -1 when fewer
+// experts are active: units of inactive experts never get a workgroup slot
+// ahead of active work.  `flags` is E <= 256 ints of LDS.  Whole workgroup.
+__device__ __forceinline__ int active_expert(const int32_t *__restrict__ ids, int P, int E, int rank, int *flags,
+                                             int *res)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < 256; e += 256) flags[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += 256) flags[ids[p]] = 1;  // every writer stores 1
+    __syncthreads();
+    if (wave == 0) {
+        int before = 0, found = -1;
+        for (int e0 = 0; e0 < E; e0 += WAVE) {
+            const bool on = (e0 + lane < E) && flags[e0 + lane];
+            const uint64_t m = __ballot(on);
+            const int cnt = __popcll(m);
+            if (found < 0 && rank < before + cnt) {
+                const int want = rank - before;
+                const bool me = on && __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)))) == want;
+                const uint64_t hit = __ballot(me);
+                found = e0 + (int)__builtin_ctzll(hit);
+            }
+            before += cnt;
+        }
+        if (lane == 0) *res = found;
+    }
+    __syncthreads();
+    return *res;
 }
 
 struct DecArgs {
@@ -171,54 +208,85 @@ __device__ __forceinline__ void load_rows(u32x4 (&dst)[CPL], const uint8_t *row)
 // the wave's whole weight slice, so the activations can be staged in LDS
 // (interleaved, row sums taken) while the weights are still streaming in.
 template <int WBITS, int NMB>
-__device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n, const int *plist, uint16_t *sA,
-                                            float *sRow, float *sPart, const uint8_t *grow, const uint8_t *urow,
-                                            float sg, float su, float *dst, int I, int row)
+__device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n, const int *plist, const int *tok,
+                                            uint16_t *sA,
+                                            float *sPart, const uint8_t *grow, const uint8_t *urow, float sg,
+                                            float su, float *dst, int I, int row)
 {
     constexpr int CPL = 8;                 // 16-byte weight chunks per lane per row per super-stage
     constexpr int SB = CPL * 64;           // weight bytes of a row per super-stage (512)
     constexpr int KS = SB * 8 / WBITS;     // columns per super-stage (1024 int4, 512 int8)
     constexpr int LDA = KS + 8;
     constexpr int CPR = KS / 8;            // 8-column activation chunks per row
-    constexpr int XPT = NMB * 16 * CPR / 256;
-    static_assert(CPR == 128 || CPR == 64, "a row is two waves or one wave of chunks");
+    constexpr int XPT = CPR / 16;          // chunks per thread: a 16-thread group owns one row
+    constexpr int NCH = 2;                 // independent accumulator chains per matrix
+    static_assert(CPR == 128 || CPR == 64, "a row is 128 or 64 chunks");
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
-    f32x4 acc[NMB][2];
+    f32x4 acc[NMB][2][NCH];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) acc[mb][0] = acc[mb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rsum[XPT];
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) rsum[i] = 0.f;
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) acc[mb][x][ch] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float rsum[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) rsum[mb] = 0.f;
     const int nss = a.H / KS;
     const uint16_t *ap = sA + (lane & 15) * LDA;
+    const int rsub = tid >> 4, csub = tid & 15;  // row within a 16-row block, chunk phase
+    const uint16_t *xrow[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+        const int r = mb * 16 + rsub;
+        xrow[mb] = (r < n) ? a.x + (size_t)(shared ? r : tok[r]) * a.H + csub * 8 : nullptr;
+    }
+    auto load_x = [&](u32x4 (&xr)[XPT], int mb, int ss) {
+        if (xrow[mb]) {
+#pragma unroll
+            for (int j = 0; j < XPT; ++j) xr[j] = *(const u32x4 *)(xrow[mb] + (size_t)ss * KS + j * 128);
+        } else {
+#pragma unroll
+            for (int j = 0; j < XPT; ++j) xr[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto stage_x = [&](u32x4 (&xr)[XPT], int mb) {
+        uint16_t *dstrow = sA + (mb * 16 + rsub) * LDA + csub * 8;
+#pragma unroll
+        for (int j = 0; j < XPT; ++j) {
+            u32x4 v = xr[j];
+            float s = 0.f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) s += bf16_lo(v[d]) + bf16_hi(v[d]);
+            rsum[mb] += s;
+            if (WBITS == 4) v = interleave_bf16x8(v);
+            *(u32x4 *)(dstrow + j * 128) = v;
+        }
+    };
     for (int ss = 0; ss < nss; ++ss) {
         u32x4 xr[XPT];
-#pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
-            xr[i] = u32x4{0u, 0u, 0u, 0u};
-            if (r < n) {
-                const int tok = shared ? r : plist[r] / a.k;
-                xr[i] = *(const u32x4 *)(a.x + (size_t)tok * a.H + (size_t)ss * KS + cc * 8);
-            }
-        }
+        load_x(xr, 0, ss);
         u32x4 wg[CPL], wu[CPL];
         load_rows<CPL>(wg, grow + (size_t)ss * SB);
         load_rows<CPL>(wu, urow + (size_t)ss * SB);
         if (ss > 0) __syncthreads();  // the previous super-stage's A reads are done
+        stage_x(xr, 0);
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
-            u32x4 v = xr[i];
-            float s = 0.f;
+        for (int mb = 1; mb < NMB; ++mb) {
+            load_x(xr, mb, ss);
+            stage_x(xr, mb);
+        }
+        if (ss == nss - 1) {
+            // row sums: the 16 threads of a row are 16 consecutive lanes
 #pragma unroll
-            for (int d = 0; d < 4; ++d) s += bf16_lo(v[d]) + bf16_hi(v[d]);
-            rsum[i] += s;
-            if (WBITS == 4) v = interleave_bf16x8(v);
-            *(u32x4 *)(sA + r * LDA + cc * 8) = v;
+            for (int mb = 0; mb < NMB; ++mb) {
+                float s = rsum[mb];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, WAVE);
+                if (csub == 0) sPart[mb * 16 + rsub] = s;
+            }
         }
         __syncthreads();
-        const uint16_t *apl = ap;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             if constexpr (WBITS == 4) {
@@ -228,9 +296,9 @@ __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n
                     const u32x4 bu = unpack_int4x8(wu[c][wd]);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
-                        const u32x4 af = *(const u32x4 *)(apl + mb * 16 * LDA + (4 * c + g) * 32 + 8 * wd);
-                        acc[mb][0] = mfma_bf16(af, bg, acc[mb][0]);
-                        acc[mb][1] = mfma_bf16(af, bu, acc[mb][1]);
+                        const u32x4 af = *(const u32x4 *)(ap + mb * 16 * LDA + (4 * c + g) * 32 + 8 * wd);
+                        acc[mb][0][wd % NCH] = mfma_bf16(af, bg, acc[mb][0][wd % NCH]);
+                        acc[mb][1][wd % NCH] = mfma_bf16(af, bu, acc[mb][1][wd % NCH]);
                     }
                 }
             } else {
@@ -240,26 +308,14 @@ __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n
                     const u32x4 bu = unpack_int8x8(u32x2{wu[c][2 * wd], wu[c][2 * wd + 1]});
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
-                        const u32x4 af = *(const u32x4 *)(apl + mb * 16 * LDA + (4 * c + g) * 16 + 8 * wd);
-                        acc[mb][0] = mfma_bf16(af, bg, acc[mb][0]);
-                        acc[mb][1] = mfma_bf16(af, bu, acc[mb][1]);
+                        const u32x4 af = *(const u32x4 *)(ap + mb * 16 * LDA + (4 * c + g) * 16 + 8 * wd);
+                        acc[mb][0][wd % NCH] = mfma_bf16(af, bg, acc[mb][0][wd % NCH]);
+                        acc[mb][1][wd % NCH] = mfma_bf16(af, bu, acc[mb][1][wd % NCH]);
                     }
                 }
             }
         }
     }
-    // row sums: the CPR chunks of a row sit in consecutive threads, 64 per wave
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-        float s = rsum[i];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, WAVE);
-        const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
-        if ((cc & 63) == 0) sPart[r * 2 + cc / 64] = s;
-    }
-    __syncthreads();
-    if (tid < NMB * 16) sRow[tid] = (CPR == 128) ? sPart[2 * tid] + sPart[2 * tid + 1] : sPart[2 * tid];
-    __syncthreads();
     const float bias = (WBITS == 4) ? INT4_BIAS : 0.f;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
@@ -267,9 +323,15 @@ __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n
         for (int r = 0; r < 4; ++r) {
             const int m = mb * 16 + g * 4 + r;
             if (m >= n) continue;
-            const float corr = bias * sRow[m];
-            const float gv = (acc[mb][0][r] - corr) * sg;
-            const float uv = (acc[mb][1][r] - corr) * su;
+            const float corr = bias * sPart[m];
+            float ga = acc[mb][0][0][r], ua = acc[mb][1][0][r];
+#pragma unroll
+            for (int ch = 1; ch < NCH; ++ch) {
+                ga += acc[mb][0][ch][r];
+                ua += acc[mb][1][ch][r];
+            }
+            const float gv = (ga - corr) * sg;
+            const float uv = (ua - corr) * su;
             const int orow = shared ? m : plist[m];
             dst[(size_t)orow * I + row] = fast_silu(gv) * uv;
         }
@@ -284,9 +346,10 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a)
     constexpr int KS = 512 * 8 / WBITS;
     constexpr int LDA = KS + 8;
     __shared__ __attribute__((aligned(16))) uint16_t sA[DEC_MAXT * LDA];
-    __shared__ float sRow[DEC_MAXT], sPart[2 * DEC_MAXT];
-    __shared__ int plist[DEC_MAXT];
-    __shared__ int pcnt;
+    __shared__ float sPart[DEC_MAXT];
+    __shared__ int plist[DEC_MAXT], tok[DEC_MAXT];
+    __shared__ int flags[256];
+    __shared__ int pcnt, ares;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nsh = a.sh_bits ? a.Ish / 64 : 0;
@@ -308,12 +371,12 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a)
         dst = a.shh;
     } else {
         const int v = u - nsh, per = a.I / 64;
-        const int e = v / per;
+        const int e = active_expert(a.ids, a.T * a.k, a.E, v / per, flags, &ares);
+        if (e < 0) return;
         i0 = (v % per) * 64;
         I = a.I;
         wb = 4;
-        n = gather_pairs(a.ids, a.T * a.k, e, plist, &pcnt);
-        if (n == 0) return;
+        n = gather_pairs(a.ids, a.T * a.k, a.k, e, plist, tok, &pcnt);
         gq = a.gq + (size_t)e * a.qstride;
         uq = a.uq + (size_t)e * a.qstride;
         gsc = a.gs + (size_t)e * a.sstride;
@@ -328,25 +391,29 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a)
     const uint8_t *urow = uq + (size_t)row * rbytes + g * 16;
     const float sg = gsc[row], su = usc[row];
     if (n <= 16)
-        gateup_body<WBITS, 1>(a, shared, n, plist, sA, sRow, sPart, grow, urow, sg, su, dst, I, row);
+        gateup_body<WBITS, 1>(a, shared, n, plist, tok, sA, sPart, grow, urow, sg, su, dst, I, row);
     else
-        gateup_body<WBITS, 2>(a, shared, n, plist, sA, sRow, sPart, grow, urow, sg, su, dst, I, row);
+        gateup_body<WBITS, 2>(a, shared, n, plist, tok, sA, sPart, grow, urow, sg, su, dst, I, row);
 }
 
 // ------------------------------------------------------------------- down
 
+constexpr int DN_ROWS = 128;  // output rows per down unit (32 per wave)
+
 // The body of k_dec_down: h rows (f32) are requested first, then the wave's
-// weight slice; h is split into exact hi + lo bf16 planes in LDS while the
-// weights stream in.  KC columns of the reduction per call (one super-stage).
+// weight slice (2 blocks of 16 output rows); h is split into exact hi + lo
+// bf16 planes in LDS while the weights stream in.  One 512-column chunk of the
+// reduction per unit.
 template <int WBITS, int NMB>
 __device__ __forceinline__ void down_body(const DecArgs &a, bool shared, int n, const int *plist, uint16_t *sHi,
-                                          uint16_t *sLo, float *sRow, float *sPart, const uint8_t *drow,
-                                          const float *hsrc, int hld, int kbeg, float sd, int row)
+                                          uint16_t *sLo, float *sPart, const uint8_t *drow0,
+                                          const uint8_t *drow1, const float *hsrc, int hld, int kbeg, float sd0,
+                                          float sd1, int row0, int row1)
 {
-    constexpr int KC = 512;                 // reduction columns per unit
+    constexpr int KC = 512;                   // reduction columns per unit
     constexpr int CPL = KC * WBITS / 8 / 64;  // weight chunks per lane per row (4 int4, 8 int8)
     constexpr int LDA = KC + 8;
-    constexpr int CPR = KC / 8;             // 64 chunks of 8 columns per row
+    constexpr int CPR = KC / 8;               // 64 chunks of 8 columns per row
     constexpr int XPT = NMB * 16 * CPR / 256;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
     f32x4 hv[XPT][2];
@@ -360,8 +427,9 @@ __device__ __forceinline__ void down_body(const DecArgs &a, bool shared, int n, 
             hv[i][1] = *(const f32x4 *)(hp + 4);
         }
     }
-    u32x4 wr[CPL];
-    load_rows<CPL>(wr, drow);
+    u32x4 w0[CPL], w1[CPL];
+    load_rows<CPL>(w0, drow0);
+    load_rows<CPL>(w1, drow1);
     float rsum[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
@@ -399,34 +467,45 @@ __device__ __forceinline__ void down_body(const DecArgs &a, bool shared, int n, 
         if ((c % CPR) == 0) sPart[r] = s;
     }
     __syncthreads();
-    if (tid < NMB * 16) sRow[tid] = sPart[tid];
-    __syncthreads();
-    f32x4 acc[NMB];
+    // chains: [row block 0/1][hi/lo plane]
+    f32x4 acc[NMB][2][2];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) acc[mb][x][0] = acc[mb][x][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint16_t *ah = sHi + (lane & 15) * LDA, *al = sLo + (lane & 15) * LDA;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         if constexpr (WBITS == 4) {
 #pragma unroll
             for (int wd = 0; wd < 4; ++wd) {
-                const u32x4 bf = unpack_int4x8(wr[c][wd]);
+                const u32x4 b0 = unpack_int4x8(w0[c][wd]);
+                const u32x4 b1 = unpack_int4x8(w1[c][wd]);
                 const int ko = (4 * c + g) * 32 + 8 * wd;
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb) {
-                    acc[mb] = mfma_bf16(*(const u32x4 *)(ah + mb * 16 * LDA + ko), bf, acc[mb]);
-                    acc[mb] = mfma_bf16(*(const u32x4 *)(al + mb * 16 * LDA + ko), bf, acc[mb]);
+                    const u32x4 fh = *(const u32x4 *)(ah + mb * 16 * LDA + ko);
+                    const u32x4 fl = *(const u32x4 *)(al + mb * 16 * LDA + ko);
+                    acc[mb][0][0] = mfma_bf16(fh, b0, acc[mb][0][0]);
+                    acc[mb][1][0] = mfma_bf16(fh, b1, acc[mb][1][0]);
+                    acc[mb][0][1] = mfma_bf16(fl, b0, acc[mb][0][1]);
+                    acc[mb][1][1] = mfma_bf16(fl, b1, acc[mb][1][1]);
                 }
             }
         } else {
 #pragma unroll
             for (int wd = 0; wd < 2; ++wd) {
-                const u32x4 bf = unpack_int8x8(u32x2{wr[c][2 * wd], wr[c][2 * wd + 1]});
+                const u32x4 b0 = unpack_int8x8(u32x2{w0[c][2 * wd], w0[c][2 * wd + 1]});
+                const u32x4 b1 = unpack_int8x8(u32x2{w1[c][2 * wd], w1[c][2 * wd + 1]});
                 const int ko = (4 * c + g) * 16 + 8 * wd;
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb) {
-                    acc[mb] = mfma_bf16(*(const u32x4 *)(ah + mb * 16 * LDA + ko), bf, acc[mb]);
-                    acc[mb] = mfma_bf16(*(const u32x4 *)(al + mb * 16 * LDA + ko), bf, acc[mb]);
+                    const u32x4 fh = *(const u32x4 *)(ah + mb * 16 * LDA + ko);
+                    const u32x4 fl = *(const u32x4 *)(al + mb * 16 * LDA + ko);
+                    acc[mb][0][0] = mfma_bf16(fh, b0, acc[mb][0][0]);
+                    acc[mb][1][0] = mfma_bf16(fh, b1, acc[mb][1][0]);
+                    acc[mb][0][1] = mfma_bf16(fl, b0, acc[mb][0][1]);
+                    acc[mb][1][1] = mfma_bf16(fl, b1, acc[mb][1][1]);
                 }
             }
         }
@@ -438,31 +517,39 @@ __device__ __forceinline__ void down_body(const DecArgs &a, bool shared, int n, 
         for (int r = 0; r < 4; ++r) {
             const int m = mb * 16 + g * 4 + r;
             if (m >= n) continue;
-            const float v = (acc[mb][r] - bias * sRow[m]) * sd;
+            const float corr = bias * sPart[m];
+            const float v0 = (acc[mb][0][0][r] + acc[mb][0][1][r] - corr) * sd0;
+            const float v1 = (acc[mb][1][0][r] + acc[mb][1][1][r] - corr) * sd1;
             if (shared) {
-                a.shp[((size_t)(kbeg / KC) * a.T + m) * a.H + row] = v;
+                float *o = a.shp + ((size_t)(kbeg / KC) * a.T + m) * a.H;
+                o[row0] = v0;
+                o[row1] = v1;
             } else {
                 const int p = plist[m];
-                a.y[((size_t)(kbeg / KC) * a.T * a.k + p) * a.H + row] = v * a.pscale[p];
+                const float ps = a.pscale[p];
+                float *o = a.y + ((size_t)(kbeg / KC) * a.T * a.k + p) * a.H;
+                o[row0] = v0 * ps;
+                o[row1] = v1 * ps;
             }
         }
     }
 }
 
-// units: [0, nsh) shared (64 output rows x one 512-column chunk of Ish), then
-// E * (H/64) * (I/512) routed (64 output rows x one 512-column chunk of I).
+// units: [0, nsh) shared (128 output rows x one 512-column chunk of Ish), then
+// routed (active expert rank, 128 output rows, one 512-column chunk of I).
 template <int WBITS>
 __global__ __launch_bounds__(256) void k_dec_down(DecArgs a)
 {
     constexpr int LDA = 512 + 8;
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][DEC_MAXT * LDA];  // hi, lo planes
-    __shared__ float sRow[DEC_MAXT], sPart[DEC_MAXT];
-    __shared__ int plist[DEC_MAXT];
-    __shared__ int pcnt;
+    __shared__ float sPart[DEC_MAXT];
+    __shared__ int plist[DEC_MAXT], tok[DEC_MAXT];
+    __shared__ int flags[256];
+    __shared__ int pcnt, ares;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nkc = a.sh_bits ? a.Ish / 512 : 0;
-    const int nsh = nkc * (a.H / 64);
+    const int nsh = nkc * (a.H / DN_ROWS);
     const int u = blockIdx.x;
     const bool shared = u < nsh;
     int n, K, kbeg, wbits, c0;
@@ -472,7 +559,7 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a)
     int hld;
     if (shared) {
         const int kc = u % nkc;
-        c0 = (u / nkc) * 64;
+        c0 = (u / nkc) * DN_ROWS;
         n = a.T;
         K = a.Ish;
         kbeg = kc * 512;
@@ -483,29 +570,32 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a)
         hld = a.Ish;
     } else {
         const int nkr = a.I / 512;
-        const int v = u - nsh, per = (a.H / 64) * nkr;
-        const int e = v / per;
-        c0 = ((v % per) / nkr) * 64;
+        const int v = u - nsh, per = (a.H / DN_ROWS) * nkr;
+        const int e = active_expert(a.ids, a.T * a.k, a.E, v / per, flags, &ares);
+        if (e < 0) return;
+        c0 = ((v % per) / nkr) * DN_ROWS;
         kbeg = ((v % per) % nkr) * 512;
         K = a.I;
         wbits = 4;
-        n = gather_pairs(a.ids, a.T * a.k, e, plist, &pcnt);
-        if (n == 0) return;
+        n = gather_pairs(a.ids, a.T * a.k, a.k, e, plist, tok, &pcnt);
         dq = a.dq + (size_t)e * a.dqstride;
         dsc = a.ds + (size_t)e * a.dsstride;
         hsrc = a.h;
         hld = a.I;
     }
     if (wbits != WBITS) return;
-    const int row = c0 + wave * 16 + (lane & 15);
+    const int row0 = c0 + wave * 32 + (lane & 15), row1 = row0 + 16;
     const int g = lane >> 4;
     const size_t rbytes = (size_t)K * WBITS / 8;
-    const uint8_t *drow = dq + (size_t)row * rbytes + (size_t)kbeg * WBITS / 8 + g * 16;
-    const float sd = dsc[row];
+    const uint8_t *drow0 = dq + (size_t)row0 * rbytes + (size_t)kbeg * WBITS / 8 + g * 16;
+    const uint8_t *drow1 = drow0 + 16 * rbytes;
+    const float sd0 = dsc[row0], sd1 = dsc[row1];
     if (n <= 16)
-        down_body<WBITS, 1>(a, shared, n, plist, sA[0], sA[1], sRow, sPart, drow, hsrc, hld, kbeg, sd, row);
+        down_body<WBITS, 1>(a, shared, n, plist, sA[0], sA[1], sPart, drow0, drow1, hsrc, hld, kbeg, sd0, sd1, row0,
+                            row1);
     else
-        down_body<WBITS, 2>(a, shared, n, plist, sA[0], sA[1], sRow, sPart, drow, hsrc, hld, kbeg, sd, row);
+        down_body<WBITS, 2>(a, shared, n, plist, sA[0], sA[1], sPart, drow0, drow1, hsrc, hld, kbeg, sd0, sd1, row0,
+                            row1);
 }
 
 // ---------------------------------------------------------------- combine
@@ -620,8 +710,8 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     if (e != hipSuccess) return e;
     const int nkc = d.sh_bits ? d.Ish / 512 : 0;
     const int nkr = d.I / 512;
-    const int nsh_d = nkc * (d.H / 64);
-    const int nd = nsh_d + d.E * (d.H / 64) * nkr;
+    const int nsh_d = nkc * (d.H / DN_ROWS);
+    const int nd = nsh_d + d.E * (d.H / DN_ROWS) * nkr;
     if (d.sh_bits == 8) {
         hipLaunchKernelGGL(k_dec_down<8>, dim3(nsh_d), dim3(256), 0, st, a);
         hipLaunchKernelGGL(k_dec_down<4>, dim3(nd), dim3(256), 0, st, a);

@@ -45,20 +45,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 // Eight packed int4 values -> eight bf16 holding q + 136, in k-slot order
 // (e0,e4),(e1,e5),(e2,e6),(e3,e7) where e_j is nibble j of w.
-// Flipping bit 3 of every nibble turns two's complement q into the offset
-// value n = q + 8 in [0, 15]; the bf16 with bit pattern 0x4300 | n is exactly
-// 128 + n.  One AND-OR per bf16 pair: the caller removes the constant 136 from
-// the dot product with 136 * (sum of the A row).
+// Flipping bit 3 of a nibble turns two's complement q into the offset value
+// n = q + 8 in [0, 15]; the bf16 with bit pattern 0x4300 | n is exactly
+// 128 + n.  Per pair of values: a shift and one 3-input bit operation
+// (keep the nibble bits of (w >> s) ^ 0x0008_0008, elsewhere 0x4300_4300).
+// The caller removes the constant 136 from the dot product with
+// 136 * (sum of the A row).
 constexpr float INT4_BIAS = 136.0f;
 
 __device__ __forceinline__ u32x4 unpack_int4x8(uint32_t w)
 {
-    w ^= 0x88888888u;
     u32x4 r;
-    r[0] = (w & 0x000F000Fu) | 0x43004300u;
-    r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-    r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-    r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+    r[0] = ((w ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
+    r[1] = (((w >> 4) ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
+    r[2] = (((w >> 8) ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
+    r[3] = (((w >> 12) ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
     return r;
 }
 
