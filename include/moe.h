@@ -212,7 +212,7 @@ const char *moe_status_string(int status);
  * routing it computed: moe_layer_routing(ws, shape, ...) returns device
  * pointers into ws (ids [T][k], w [T][k], offsets [E+1], sorted [T*k]).
  * Pointers stay valid until the workspace is reused.  In the small-batch
- * regime (T <= 32, H % 1024 == 0, I % 512 == 0, I_shared % 512 == 0) each
+ * regime (T <= 32, top_k <= 16, H % 1024 == 0, I % 512 == 0, I_shared % 512 == 0) each
  * expert kernel gathers its own pairs and no sorted list is materialised:
  * offsets and sorted_pairs are then returned as NULL. */
 int moe_layer_routing(const moe_shape *shape, void *ws, size_t ws_bytes, int32_t **topk_ids, float **topk_w,

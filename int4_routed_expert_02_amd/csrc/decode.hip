@@ -4,19 +4,23 @@
 // The engine chooses kernels per shape by measurement (colibri README, "What's
 // implemented", integer-dot kernels: the single-row int4 case takes a
 // different path from the batched one).  Here, for T <= 32 tokens:
-//   k_dec_route    one workgroup per token: logits (f32 FMA), sigmoid + bias,
-//                  top-k (moe_select.h), weights and rsf * w per pair;
-//   k_dec_gateup   one workgroup per (expert, 64 intermediate rows): gathers
+//   k_dec_logits   router logits z = x W^T in f32 FMA, one workgroup per four
+//                  experts (W is the largest read of the router);
+//   k_dec_gateup   routed workgroups first select the top-k experts of every
+//                  token from z (sigmoid + bias, moe_select.h; each workgroup
+//                  takes the same decision, the first publishes ids, weights
+//                  and rsf * w), then one workgroup per (active expert, 64
+//                  intermediate rows): gathers
 //                  the pairs routed to its expert (batch-union: the expert's
 //                  rows are read once for all of them), streams its gate and up
 //                  rows straight from HBM into registers, MFMA on 16-pair
 //                  blocks, SwiGLU epilogue -> h [pair][I] f32;  the shared
 //                  expert's rows form extra units over all T tokens;
-//   k_dec_down     one workgroup per (expert, 64 output rows, 512-column chunk
+//   k_dec_down     one workgroup per (expert, 128 output rows, 512-column chunk
 //                  of the reduction): h as an exact hi + lo bf16 pair, down rows
 //                  streamed to registers, epilogue scales by sd * rsf * w ->
 //                  partial y [chunk][pair][H];  the shared expert's units are
-//                  (64 output rows, 512-column chunk) over all T tokens;
+//                  (128 output rows, 512-column chunk) over all T tokens;
 //   k_dec_combine  out = sum_j sum_chunk y + sum_chunk shared partials (+ x),
 //                  in a fixed order.
 // Buffers are indexed by pair, so no permutation is materialised: each
@@ -38,79 +42,253 @@ constexpr int DEC_MAXT = 32;  // tokens per layer call in this regime
 
 // ------------------------------------------------------------------ router
 
-template <int EPL>
-__global__ __launch_bounds__(256) void k_dec_route(const uint16_t *__restrict__ x, const float *__restrict__ W,
-                                                   const float *__restrict__ bias, int T, int H, int E, int k,
-                                                   int n_group, int topk_group, float rsf, int32_t *__restrict__ ids,
-                                                   float *__restrict__ w, float *__restrict__ gap,
-                                                   float *__restrict__ pscale)
+constexpr int LG_KSPLIT = 16;  // K slices of the router logits, one per wave
+constexpr int LG_NP = DEC_LOGIT_PLANES;  // partial logit planes (one per workgroup of 4 waves)
+static_assert(LG_KSPLIT == 4 * LG_NP, "four K slices per plane");
+constexpr int DEC_MAXK = 16;   // top-k limit of this regime (LDS lists of T * k pairs)
+
+// Router logits on the matrix cores.  The f32 router row W_e is split exactly
+// into three bf16 terms (hi + mid + lo carries all 24 mantissa bits), so three
+// bf16 products against the bf16 hidden row give x . W_e to f32 accuracy.
+// Workgroup = (16-expert tile, 16-token tile, group of 4 K slices); wave w
+// takes slice 4 * group + w of H / 16 columns, the four wave tiles are added in
+// wave order and written as one partial plane: zp[group][t][e].  The consumer
+// adds the LG_NP planes in plane order.
+__device__ __forceinline__ void split3_bf16(const f32x4 &a, const f32x4 &b, u32x4 &hi, u32x4 &mid, u32x4 &lo)
 {
-    extern __shared__ float xs[];  // H floats
-    __shared__ float zs[256];
-    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid * 8; i < H; i += 256 * 8) {
-        const u32x4 v = *(const u32x4 *)(x + (size_t)t * H + i);
+    float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    uint16_t h[8], m[8], l[8];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            xs[i + 2 * d] = bf16_lo(v[d]);
-            xs[i + 2 * d + 1] = bf16_hi(v[d]);
+    for (int i = 0; i < 8; ++i) {
+        h[i] = f32_to_bf16(v[i]);
+        const float r1 = v[i] - bf16_to_f32(h[i]);
+        m[i] = f32_to_bf16(r1);
+        l[i] = f32_to_bf16(r1 - bf16_to_f32(m[i]));
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        hi[d] = (uint32_t)h[2 * d] | ((uint32_t)h[2 * d + 1] << 16);
+        mid[d] = (uint32_t)m[2 * d] | ((uint32_t)m[2 * d + 1] << 16);
+        lo[d] = (uint32_t)l[2 * d] | ((uint32_t)l[2 * d + 1] << 16);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_dec_logits(const uint16_t *__restrict__ x, const float *__restrict__ W,
+                                                    int T, int H, int E, float *__restrict__ zp)
+{
+    __shared__ f32x4 red[3][WAVE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int net = (E + 15) / 16, ntt = (T + 15) / 16;
+    const int et = blockIdx.x % net, tt = (blockIdx.x / net) % ntt, grp = blockIdx.x / (net * ntt);
+    const int ksl = H / LG_KSPLIT;
+    const int k0 = (grp * 4 + wave) * ksl;
+    const int e = et * 16 + n, t = tt * 16 + n;
+    const float *wrow = W + (size_t)(e < E ? e : 0) * H + k0 + g * 8;
+    const uint16_t *xrow = x + (size_t)(t < T ? t : 0) * H + k0 + g * 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < ksl; kk += 64) {  // two 32-column steps per round, loads first
+        f32x4 wa[2], wb[2];
+        u32x4 xv[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            wa[s] = *(const f32x4 *)(wrow + kk + 32 * s);
+            wb[s] = *(const f32x4 *)(wrow + kk + 32 * s + 4);
+            xv[s] = *(const u32x4 *)(xrow + kk + 32 * s);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (e >= E) wa[s] = wb[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (t >= T) xv[s] = u32x4{0u, 0u, 0u, 0u};
+            u32x4 hi, mid, lo;
+            split3_bf16(wa[s], wb[s], hi, mid, lo);
+            acc = mfma_bf16(hi, xv[s], acc);
+            acc = mfma_bf16(mid, xv[s], acc);
+            acc = mfma_bf16(lo, xv[s], acc);
         }
     }
-    __syncthreads();
-    // Q consecutive threads share one expert's dot product; thread q takes the
-    // float4 columns q, q + Q, q + 2Q, ...  Eight loads are kept in flight and
-    // four partial sums interleaved, then combined in a fixed order.
-    int Q = 64;
-    while (Q > 1 && Q * E > 256) Q >>= 1;
-    const int q = tid % Q;
-    const int nper = H / 4 / Q;  // float4 columns per thread
-    const f32x4 *x4 = (const f32x4 *)xs;
-    for (int e = tid / Q; e < E; e += 256 / Q) {
-        const f32x4 *w4 = (const f32x4 *)(W + (size_t)e * H) + q;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        int i = 0;
-        for (; i + 8 <= nper; i += 8) {
-            f32x4 wv[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) wv[u] = w4[(size_t)(i + u) * Q];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const f32x4 xv = x4[q + (i + u) * Q];
-                float &ac = acc[u & 3];
-                ac = fmaf(wv[u][0], xv[0], ac);
-                ac = fmaf(wv[u][1], xv[1], ac);
-                ac = fmaf(wv[u][2], xv[2], ac);
-                ac = fmaf(wv[u][3], xv[3], ac);
-            }
-        }
-        for (; i < nper; ++i) {
-            const f32x4 wv = w4[(size_t)i * Q];
-            const f32x4 xv = x4[q + i * Q];
-            acc[0] = fmaf(wv[0], xv[0], acc[0]);
-            acc[0] = fmaf(wv[1], xv[1], acc[0]);
-            acc[0] = fmaf(wv[2], xv[2], acc[0]);
-            acc[0] = fmaf(wv[3], xv[3], acc[0]);
-        }
-        float tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        for (int o = Q / 2; o > 0; o >>= 1) tot += __shfl_xor(tot, o, WAVE);
-        if (q == 0) zs[e] = tot;
-    }
+    if (wave > 0) red[wave - 1][lane] = acc;
     __syncthreads();
     if (wave == 0) {
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            const f32x4 o = red[w][lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] += o[r];
+        }
+        // acc[r] = z[token tt*16 + n][expert et*16 + 4g + r]
+        if (t < T) {
+            float *dst = zp + ((size_t)grp * T + t) * E + et * 16 + 4 * g;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (et * 16 + 4 * g + r < E) dst[r] = acc[r];
+        }
+    }
+}
+
+__device__ __forceinline__ float dec_logit(const float *__restrict__ zp, int T, int E, int t, int e)
+{
+    float z = zp[(size_t)t * E + e];
+#pragma unroll
+    for (int p = 1; p < LG_NP; ++p) z += zp[((size_t)p * T + t) * E + e];
+    return z;
+}
+
+// Selection for all T tokens of the batch, any E <= 256, k <= 16 and group
+// limit (moe_select.h, one wave per token): wave w takes tokens w, w + 4, ...
+// Results go to LDS (ids_l, w_l: [T][k]); with `pub` set the workgroup also
+// writes ids, w, rsf * w and the tie gap to global memory.
+template <int EPL>
+__device__ __noinline__ void dec_select_waves(const float *__restrict__ zp, const float *__restrict__ bias, int T,
+                                              int E, int k, int n_group, int topk_group, float rsf, int32_t *ids_l,
+                                              float *w_l, bool pub, float *__restrict__ gap_g)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int t = wave; t < T; t += 4) {
         float s[EPL], b[EPL];
         bool ok[EPL];
 #pragma unroll
-        for (int qq = 0; qq < EPL; ++qq) {
-            const int e = lane * EPL + qq;
-            ok[qq] = e < E;
-            s[qq] = 0.f;
-            b[qq] = -INFINITY;
-            if (ok[qq]) {
-                s[qq] = 1.0f / (1.0f + expf(-zs[e]));
-                b[qq] = s[qq] + bias[e];
-            }
+        for (int q = 0; q < EPL; ++q) {
+            const int e = lane * EPL + q;
+            ok[q] = e < E;
+            s[q] = ok[q] ? 1.0f / (1.0f + expf(-dec_logit(zp, T, E, t, e))) : 0.f;
+            b[q] = ok[q] ? s[q] + bias[e] : -INFINITY;
         }
-        select_token<EPL>(s, b, ok, lane, t, E, k, n_group, topk_group, rsf, ids, w, gap, pscale, nullptr);
+        select_token<EPL>(s, b, ok, lane, t, E, k, n_group, topk_group, rsf, ids_l, w_l, pub ? gap_g : nullptr,
+                          nullptr, nullptr);
+    }
+}
+
+// One selection candidate: selection score v (sigmoid + bias), unbiased score
+// s, expert id i.  Order: larger v first, equal v -> lower id first (the
+// order of moe_select.h); an empty slot (i = INT_MAX, v = -inf) loses to all.
+struct Cand {
+    float v, s;
+    int i;
+};
+__device__ __forceinline__ bool cand_before(const Cand &a, const Cand &b)
+{
+    return a.v > b.v || (a.v == b.v && a.i < b.i);
+}
+__device__ __forceinline__ void cand_sort2(Cand &a, Cand &b)
+{
+    if (cand_before(b, a)) {
+        const Cand t = a;
+        a = b;
+        b = t;
+    }
+}
+
+// Fast selection when no group limit applies, E <= 64, E % 8 == 0 and k < KL:
+// eight lanes per token (lane slice q scans experts 8q .. 8q + 7), each keeps
+// its best KL candidates sorted, then three butterfly merges over the slices
+// (bitonic: pair own entry j with the partner's entry KL - 1 - j, keep the
+// better, re-sort) leave the batch-wide best KL in every lane of the token.
+// The selected k are the first k, taken in that order; the weight of
+// selection j is s_j over the sum of the selected s (summed in selection
+// order); the tie gap is v_{k-1} - v_k.  Same results as moe_select.h.
+template <int KL, typename Pre>
+__device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, const float *__restrict__ bias, int T,
+                                                 int E, int k, int32_t *ids_l, float *w_l, bool pub,
+                                                 float *__restrict__ gap_g, Pre &&pre)
+{
+    const int tid = threadIdx.x, t = tid >> 3, q = tid & 7;
+    Cand c[KL];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) c[j] = Cand{-INFINITY, 0.f, 0x7fffffff};
+    const bool live = t < T && 8 * q < E;
+    // the logits are requested first, then the caller's own requests (pre), so
+    // that waiting for the logits never waits for those
+    f32x4 pa[LG_NP][2], b0, b1;
+    if (live) {
+#pragma unroll
+        for (int p = 0; p < LG_NP; ++p) {
+            const f32x4 *pp = (const f32x4 *)(zp + ((size_t)p * T + t) * E + 8 * q);
+            pa[p][0] = pp[0];
+            pa[p][1] = pp[1];
+        }
+        b0 = *(const f32x4 *)(bias + 8 * q);
+        b1 = *(const f32x4 *)(bias + 8 * q + 4);
+    }
+    pre();
+    if (live) {
+        float z[8];
+        const f32x4 a0 = pa[0][0], a1 = pa[0][1];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            z[r] = a0[r];
+            z[r + 4] = a1[r];
+        }
+#pragma unroll
+        for (int p = 1; p < LG_NP; ++p)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                z[r] += pa[p][0][r];
+                z[r + 4] += pa[p][1][r];
+            }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float sc = __builtin_amdgcn_rcpf(1.0f + __expf(-z[r]));
+            Cand x{sc + (r < 4 ? b0[r] : b1[r - 4]), sc, 8 * q + r};
+            // insert into the sorted list (drop the last)
+#pragma unroll
+            for (int j = 0; j < KL; ++j)
+                if (cand_before(x, c[j])) {
+                    const Cand tmp = c[j];
+                    c[j] = x;
+                    x = tmp;
+                }
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+        Cand o[KL];
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+            o[j].v = __shfl_xor(c[j].v, m, WAVE);
+            o[j].s = __shfl_xor(c[j].s, m, WAVE);
+            o[j].i = __shfl_xor(c[j].i, m, WAVE);
+        }
+#pragma unroll
+        for (int j = 0; j < KL; ++j)
+            if (cand_before(o[KL - 1 - j], c[j])) c[j] = o[KL - 1 - j];
+        // c is now bitonic; sort it (KL <= 4)
+        if (KL == 4) {
+            cand_sort2(c[0], c[2]);
+            cand_sort2(c[1], c[3]);
+        }
+        if (KL >= 3) {
+            cand_sort2(c[0], c[1]);
+            cand_sort2(c[KL - 2], c[KL - 1]);
+            if (KL == 3) cand_sort2(c[0], c[1]);
+        } else {
+            cand_sort2(c[0], c[1]);
+        }
+    }
+    if (t < T && q == 0) {
+        float ssum = 0.f;
+#pragma unroll
+        for (int j = 0; j < KL - 1; ++j)
+            if (j < k) ssum += c[j].s;
+#pragma unroll
+        for (int j = 0; j < KL - 1; ++j)
+            if (j < k) {
+                ids_l[t * k + j] = c[j].i;
+                w_l[t * k + j] = c[j].s / ssum;
+            }
+        if (pub) {
+            float nv = -INFINITY, kv = 0.f;
+            bool has = false;
+#pragma unroll
+            for (int j = 0; j < KL; ++j) {
+                if (j == k - 1) kv = c[j].v;
+                if (j == k) {
+                    nv = c[j].v;
+                    has = c[j].i != 0x7fffffff;
+                }
+            }
+            gap_g[t] = has ? kv - nv : INFINITY;
+        }
     }
 }
 
@@ -151,7 +329,10 @@ __device__ __forceinline__ int active_expert(const int32_t *__restrict__ ids, in
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int e = tid; e < 256; e += 256) flags[e] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += 256) flags[ids[p]] = 1;  // every writer stores 1
+    for (int p = tid; p < P; p += 256) {
+        const int e = ids[p];
+        if ((unsigned)e < (unsigned)E) flags[e] = 1;  // every writer stores 1
+    }
     __syncthreads();
     if (wave == 0) {
         int before = 0, found = -1;
@@ -176,7 +357,13 @@ __device__ __forceinline__ int active_expert(const int32_t *__restrict__ ids, in
 struct DecArgs {
     const uint16_t *x;  // [T][H] bf16
     int T, H, k, E;
-    const int32_t *ids;  // [T*k]
+    int32_t *ids;        // [T*k] selected experts (written by the first routed gate/up workgroup)
+    float *w, *gap;      // [T*k] combine weights, [T] tie gaps (same writer)
+    const float *zp;     // [LG_NP][T][E] partial router logits
+    const float *rb;     // [E] selection bias
+    int n_group, topk_group;
+    float rsf;
+    int spec;  // routed units map to experts by index and fetch before routing
     // routed experts
     const uint8_t *gq, *uq, *dq;
     const float *gs, *us, *ds;
@@ -189,10 +376,39 @@ struct DecArgs {
     // buffers
     float *h;      // [P][I]
     float *shh;    // [T][Ish]
-    const float *pscale;  // [P]
+    float *pscale;  // [P] rsf * w
     float *y;      // [P][H]
     float *shp;    // [Ish/512][T][H]
 };
+
+// The routing decision of the batch into LDS (every routed gate/up workgroup
+// takes it, from the same logits, so all agree); the publishing workgroup
+// also writes ids, w, rsf * w and the tie gaps to global memory.
+// `pre` runs once, after the logits are requested and before they are used.
+template <int EPL, typename Pre>
+__device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k, int32_t *ids_l, float *w_l,
+                                          bool pub, Pre &&pre)
+{
+    const bool grouped = r.n_group > 1 && r.topk_group < r.n_group;
+    if (!grouped && E <= 64 && E % 8 == 0 && k <= 3) {
+        if (k == 1)
+            dec_select_lanes<2>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, pre);
+        else if (k == 2)
+            dec_select_lanes<3>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, pre);
+        else
+            dec_select_lanes<4>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, pre);
+    } else {
+        pre();
+        dec_select_waves<EPL>(r.zp, r.rb, T, E, k, r.n_group, r.topk_group, r.rsf, ids_l, w_l, pub, r.gap);
+    }
+    __syncthreads();
+    if (pub)
+        for (int i = threadIdx.x; i < T * k; i += 256) {
+            r.ids[i] = ids_l[i];
+            r.w[i] = w_l[i];
+            r.pscale[i] = r.rsf * w_l[i];
+        }
+}
 
 // ------------------------------------------------------------------ gate/up
 
@@ -207,13 +423,15 @@ __device__ __forceinline__ void load_rows(u32x4 (&dst)[CPL], const uint8_t *row)
 // Per super-stage of KS columns: the activation rows are requested first, then
 // the wave's whole weight slice, so the activations can be staged in LDS
 // (interleaved, row sums taken) while the weights are still streaming in.
+constexpr int GU_CPL = 8;  // 16-byte gate/up weight chunks per lane per row per super-stage
+
 template <int WBITS, int NMB>
 __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n, const int *plist, const int *tok,
-                                            uint16_t *sA,
-                                            float *sPart, const uint8_t *grow, const uint8_t *urow, float sg,
+                                            uint16_t *sA, float *sPart, const uint8_t *grow, const uint8_t *urow,
+                                            const u32x4 (&wg0)[GU_CPL], const u32x4 (&wu0)[GU_CPL], float sg,
                                             float su, float *dst, int I, int row)
 {
-    constexpr int CPL = 8;                 // 16-byte weight chunks per lane per row per super-stage
+    constexpr int CPL = GU_CPL;
     constexpr int SB = CPL * 64;           // weight bytes of a row per super-stage (512)
     constexpr int KS = SB * 8 / WBITS;     // columns per super-stage (1024 int4, 512 int8)
     constexpr int LDA = KS + 8;
@@ -267,8 +485,16 @@ __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n
         u32x4 xr[XPT];
         load_x(xr, 0, ss);
         u32x4 wg[CPL], wu[CPL];
-        load_rows<CPL>(wg, grow + (size_t)ss * SB);
-        load_rows<CPL>(wu, urow + (size_t)ss * SB);
+        if (ss == 0) {  // the first super-stage's weights were requested by the caller
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                wg[c] = wg0[c];
+                wu[c] = wu0[c];
+            }
+        } else {
+            load_rows<CPL>(wg, grow + (size_t)ss * SB);
+            load_rows<CPL>(wu, urow + (size_t)ss * SB);
+        }
         if (ss > 0) __syncthreads();  // the previous super-stage's A reads are done
         stage_x(xr, 0);
 #pragma unroll
@@ -340,7 +566,14 @@ __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n
 
 // units: [0, nsh) shared (64 intermediate rows each), then E * (I/64) routed.
 // Each wave owns 16 intermediate rows i and streams both their gate and up rows.
-template <int WBITS>
+// Routed units first take the routing decision for the whole batch (every
+// routed workgroup computes the same one from the logits).  With a.spec set
+// (a batch expected to touch most experts) routed unit v belongs to expert
+// v / (I/64) and requests its first weight stage before routing, so the
+// selection overlaps the weight fetch; a unit whose expert nobody chose
+// exits.  Otherwise unit v belongs to the (v / (I/64))-th chosen expert in
+// ascending id order and fetches after routing (no wasted reads).
+template <int WBITS, int EPL>
 __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a)
 {
     constexpr int KS = 512 * 8 / WBITS;
@@ -349,56 +582,66 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a)
     __shared__ float sPart[DEC_MAXT];
     __shared__ int plist[DEC_MAXT], tok[DEC_MAXT];
     __shared__ int flags[256];
+    __shared__ int32_t sIds[DEC_MAXT * DEC_MAXK];
+    __shared__ float sW[DEC_MAXT * DEC_MAXK];
     __shared__ int pcnt, ares;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
     const int nsh = a.sh_bits ? a.Ish / 64 : 0;
     const int u = blockIdx.x;
     const bool shared = u < nsh;
-    int i0, n, I, wb;
-    const uint8_t *gq, *uq;
-    const float *gsc, *usc;
+    if ((shared ? a.sh_bits : 4) != WBITS) return;  // the launch instantiates one weight format
+    const size_t rbytes = (size_t)a.H * WBITS / 8;
+    u32x4 wg0[GU_CPL], wu0[GU_CPL];
+    const uint8_t *grow, *urow;
+    float sg, su;
+    int row;
+    auto fetch = [&](const uint8_t *gq, const uint8_t *uq, const float *gsc, const float *usc, int i0) {
+        row = i0 + wave * 16 + (lane & 15);
+        grow = gq + (size_t)row * rbytes + g * 16;
+        urow = uq + (size_t)row * rbytes + g * 16;
+        load_rows<GU_CPL>(wg0, grow);
+        load_rows<GU_CPL>(wu0, urow);
+        sg = gsc[row];
+        su = usc[row];
+    };
+    int n, I;
     float *dst;
     if (shared) {
-        i0 = u * 64;
+        fetch(a.sgq, a.suq, a.sgs, a.sus, u * 64);
         n = a.T;
         I = a.Ish;
-        wb = a.sh_bits;
-        gq = a.sgq;
-        uq = a.suq;
-        gsc = a.sgs;
-        usc = a.sus;
         dst = a.shh;
     } else {
         const int v = u - nsh, per = a.I / 64;
-        const int e = active_expert(a.ids, a.T * a.k, a.E, v / per, flags, &ares);
-        if (e < 0) return;
-        i0 = (v % per) * 64;
+        int e = v / per;
+        dec_route<EPL>(a, a.T, a.E, a.k, sIds, sW, v == 0, [&]() {
+            if (a.spec)
+                fetch(a.gq + (size_t)e * a.qstride, a.uq + (size_t)e * a.qstride, a.gs + (size_t)e * a.sstride,
+                      a.us + (size_t)e * a.sstride, (v % per) * 64);
+        });
+        if (!a.spec) {
+            e = active_expert(sIds, a.T * a.k, a.E, v / per, flags, &ares);
+            if (e < 0) return;
+            fetch(a.gq + (size_t)e * a.qstride, a.uq + (size_t)e * a.qstride, a.gs + (size_t)e * a.sstride,
+                  a.us + (size_t)e * a.sstride, (v % per) * 64);
+        }
+        n = gather_pairs(sIds, a.T * a.k, a.k, e, plist, tok, &pcnt);
+        if (n == 0) return;  // (speculative units only) nobody chose this expert
         I = a.I;
-        wb = 4;
-        n = gather_pairs(a.ids, a.T * a.k, a.k, e, plist, tok, &pcnt);
-        gq = a.gq + (size_t)e * a.qstride;
-        uq = a.uq + (size_t)e * a.qstride;
-        gsc = a.gs + (size_t)e * a.sstride;
-        usc = a.us + (size_t)e * a.sstride;
         dst = a.h;
     }
-    if (wb != WBITS) return;  // the launch instantiates one weight format
-    const int row = i0 + wave * 16 + (lane & 15);
-    const int g = lane >> 4;
-    const size_t rbytes = (size_t)a.H * WBITS / 8;
-    const uint8_t *grow = gq + (size_t)row * rbytes + g * 16;
-    const uint8_t *urow = uq + (size_t)row * rbytes + g * 16;
-    const float sg = gsc[row], su = usc[row];
     if (n <= 16)
-        gateup_body<WBITS, 1>(a, shared, n, plist, tok, sA, sPart, grow, urow, sg, su, dst, I, row);
+        gateup_body<WBITS, 1>(a, shared, n, plist, tok, sA, sPart, grow, urow, wg0, wu0, sg, su, dst, I, row);
     else
-        gateup_body<WBITS, 2>(a, shared, n, plist, tok, sA, sPart, grow, urow, sg, su, dst, I, row);
+        gateup_body<WBITS, 2>(a, shared, n, plist, tok, sA, sPart, grow, urow, wg0, wu0, sg, su, dst, I, row);
 }
 
 // ------------------------------------------------------------------- down
 
 constexpr int DN_ROWS = 128;  // output rows per down unit (32 per wave)
+// 16-byte weight chunks per lane per row of a 512-column unit (4 int4, 8 int8)
+constexpr int dn_cpl(int wbits) { return 512 * wbits / 8 / 64; }
 
 // The body of k_dec_down: h rows (f32) are requested first, then the wave's
 // weight slice (2 blocks of 16 output rows); h is split into exact hi + lo
@@ -406,12 +649,12 @@ constexpr int DN_ROWS = 128;  // output rows per down unit (32 per wave)
 // reduction per unit.
 template <int WBITS, int NMB>
 __device__ __forceinline__ void down_body(const DecArgs &a, bool shared, int n, const int *plist, uint16_t *sHi,
-                                          uint16_t *sLo, float *sPart, const uint8_t *drow0,
-                                          const uint8_t *drow1, const float *hsrc, int hld, int kbeg, float sd0,
-                                          float sd1, int row0, int row1)
+                                          uint16_t *sLo, float *sPart, const u32x4 (&w0)[dn_cpl(WBITS)],
+                                          const u32x4 (&w1)[dn_cpl(WBITS)], const float *hsrc, int hld, int kbeg,
+                                          float sd0, float sd1, int row0, int row1)
 {
     constexpr int KC = 512;                   // reduction columns per unit
-    constexpr int CPL = KC * WBITS / 8 / 64;  // weight chunks per lane per row (4 int4, 8 int8)
+    constexpr int CPL = dn_cpl(WBITS);
     constexpr int LDA = KC + 8;
     constexpr int CPR = KC / 8;               // 64 chunks of 8 columns per row
     constexpr int XPT = NMB * 16 * CPR / 256;
@@ -427,9 +670,6 @@ __device__ __forceinline__ void down_body(const DecArgs &a, bool shared, int n, 
             hv[i][1] = *(const f32x4 *)(hp + 4);
         }
     }
-    u32x4 w0[CPL], w1[CPL];
-    load_rows<CPL>(w0, drow0);
-    load_rows<CPL>(w1, drow1);
     float rsum[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
@@ -536,66 +776,71 @@ __device__ __forceinline__ void down_body(const DecArgs &a, bool shared, int n, 
 }
 
 // units: [0, nsh) shared (128 output rows x one 512-column chunk of Ish), then
-// routed (active expert rank, 128 output rows, one 512-column chunk of I).
+// routed (expert, 128 output rows, one 512-column chunk of I).  The expert of
+// a routed unit is its index / units-per-expert with a.spec set (weights are
+// requested before the routing is read; units of unchosen experts exit),
+// else the chosen expert of that rank in ascending id order.
 template <int WBITS>
 __global__ __launch_bounds__(256) void k_dec_down(DecArgs a)
 {
     constexpr int LDA = 512 + 8;
+    constexpr int CPL = dn_cpl(WBITS);
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][DEC_MAXT * LDA];  // hi, lo planes
     __shared__ float sPart[DEC_MAXT];
     __shared__ int plist[DEC_MAXT], tok[DEC_MAXT];
     __shared__ int flags[256];
     __shared__ int pcnt, ares;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
     const int nkc = a.sh_bits ? a.Ish / 512 : 0;
     const int nsh = nkc * (a.H / DN_ROWS);
     const int u = blockIdx.x;
     const bool shared = u < nsh;
-    int n, K, kbeg, wbits, c0;
-    const uint8_t *dq;
-    const float *dsc;
+    if ((shared ? a.sh_bits : 4) != WBITS) return;
+    u32x4 w0[CPL], w1[CPL];
+    float sd0, sd1;
+    int row0, row1;
+    auto fetch = [&](const uint8_t *dq, const float *dsc, int K, int c0, int kbeg) {
+        row0 = c0 + wave * 32 + (lane & 15);
+        row1 = row0 + 16;
+        const size_t rbytes = (size_t)K * WBITS / 8;
+        const uint8_t *drow0 = dq + (size_t)row0 * rbytes + (size_t)kbeg * WBITS / 8 + g * 16;
+        load_rows<CPL>(w0, drow0);
+        load_rows<CPL>(w1, drow0 + 16 * rbytes);
+        sd0 = dsc[row0];
+        sd1 = dsc[row1];
+    };
+    int n, kbeg, hld;
     const float *hsrc;
-    int hld;
     if (shared) {
         const int kc = u % nkc;
-        c0 = (u / nkc) * DN_ROWS;
-        n = a.T;
-        K = a.Ish;
         kbeg = kc * 512;
-        wbits = a.sh_bits;
-        dq = a.sdq;
-        dsc = a.sds;
+        fetch(a.sdq, a.sds, a.Ish, (u / nkc) * DN_ROWS, kbeg);
+        n = a.T;
         hsrc = a.shh;
         hld = a.Ish;
     } else {
         const int nkr = a.I / 512;
         const int v = u - nsh, per = (a.H / DN_ROWS) * nkr;
-        const int e = active_expert(a.ids, a.T * a.k, a.E, v / per, flags, &ares);
-        if (e < 0) return;
-        c0 = ((v % per) / nkr) * DN_ROWS;
+        const int c0 = ((v % per) / nkr) * DN_ROWS;
         kbeg = ((v % per) % nkr) * 512;
-        K = a.I;
-        wbits = 4;
+        int e = v / per;
+        if (a.spec) {
+            fetch(a.dq + (size_t)e * a.dqstride, a.ds + (size_t)e * a.dsstride, a.I, c0, kbeg);
+        } else {
+            e = active_expert(a.ids, a.T * a.k, a.E, v / per, flags, &ares);
+            if (e < 0) return;
+            fetch(a.dq + (size_t)e * a.dqstride, a.ds + (size_t)e * a.dsstride, a.I, c0, kbeg);
+        }
         n = gather_pairs(a.ids, a.T * a.k, a.k, e, plist, tok, &pcnt);
-        dq = a.dq + (size_t)e * a.dqstride;
-        dsc = a.ds + (size_t)e * a.dsstride;
+        if (n == 0) return;  // (speculative units only) nobody chose this expert
         hsrc = a.h;
         hld = a.I;
     }
-    if (wbits != WBITS) return;
-    const int row0 = c0 + wave * 32 + (lane & 15), row1 = row0 + 16;
-    const int g = lane >> 4;
-    const size_t rbytes = (size_t)K * WBITS / 8;
-    const uint8_t *drow0 = dq + (size_t)row0 * rbytes + (size_t)kbeg * WBITS / 8 + g * 16;
-    const uint8_t *drow1 = drow0 + 16 * rbytes;
-    const float sd0 = dsc[row0], sd1 = dsc[row1];
     if (n <= 16)
-        down_body<WBITS, 1>(a, shared, n, plist, sA[0], sA[1], sPart, drow0, drow1, hsrc, hld, kbeg, sd0, sd1, row0,
-                            row1);
+        down_body<WBITS, 1>(a, shared, n, plist, sA[0], sA[1], sPart, w0, w1, hsrc, hld, kbeg, sd0, sd1, row0, row1);
     else
-        down_body<WBITS, 2>(a, shared, n, plist, sA[0], sA[1], sPart, drow0, drow1, hsrc, hld, kbeg, sd0, sd1, row0,
-                            row1);
+        down_body<WBITS, 2>(a, shared, n, plist, sA[0], sA[1], sPart, w0, w1, hsrc, hld, kbeg, sd0, sd1, row0, row1);
 }
 
 // ---------------------------------------------------------------- combine
@@ -639,7 +884,7 @@ __global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ y
 
 bool decode_supported(int T, int H, int E, int k, int I, int Ish, int sh_bits)
 {
-    if (T > DEC_MAXT || E > 256) return false;
+    if (T > DEC_MAXT || E > 256 || k > DEC_MAXK) return false;
     if (H % 1024 || I % 512) return false;
     if (sh_bits && Ish % 512) return false;
     return true;
@@ -654,6 +899,14 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     a.k = d.k;
     a.E = d.E;
     a.ids = d.ids;
+    a.w = d.w;
+    a.gap = d.gap;
+    a.zp = d.z;
+    a.rb = d.rb;
+    a.n_group = d.n_group;
+    a.topk_group = d.topk_group;
+    a.rsf = d.rsf;
+    a.spec = 0;
     a.gq = d.gq;
     a.uq = d.uq;
     a.dq = d.dq;
@@ -679,16 +932,10 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     a.y = d.y;
     a.shp = d.shp;
 
-    const size_t lds_route = (size_t)d.H * sizeof(float);
-    if (d.E <= 64)
-        hipLaunchKernelGGL(k_dec_route<1>, dim3(d.T), dim3(256), lds_route, st, d.x, d.rw, d.rb, d.T, d.H, d.E, d.k,
-                           d.n_group, d.topk_group, d.rsf, d.ids, d.w, d.gap, d.pscale);
-    else if (d.E <= 128)
-        hipLaunchKernelGGL(k_dec_route<2>, dim3(d.T), dim3(256), lds_route, st, d.x, d.rw, d.rb, d.T, d.H, d.E, d.k,
-                           d.n_group, d.topk_group, d.rsf, d.ids, d.w, d.gap, d.pscale);
-    else
-        hipLaunchKernelGGL(k_dec_route<4>, dim3(d.T), dim3(256), lds_route, st, d.x, d.rw, d.rb, d.T, d.H, d.E, d.k,
-                           d.n_group, d.topk_group, d.rsf, d.ids, d.w, d.gap, d.pscale);
+    {
+        const int grid = ((d.E + 15) / 16) * ((d.T + 15) / 16) * LG_NP;
+        hipLaunchKernelGGL(k_dec_logits, dim3(grid), dim3(256), 0, st, d.x, d.rw, d.T, d.H, d.E, d.z);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -699,12 +946,13 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
         e = hipEventRecord(d.ev0, st);
         if (e != hipSuccess) return e;
     }
-    if (d.sh_bits == 8) {
-        hipLaunchKernelGGL(k_dec_gateup<8>, dim3(nsh_gu), dim3(256), 0, st, a);
-        hipLaunchKernelGGL(k_dec_gateup<4>, dim3(ngu), dim3(256), 0, st, a);
-    } else {
-        hipLaunchKernelGGL(k_dec_gateup<4>, dim3(ngu), dim3(256), 0, st, a);
-    }
+    if (d.sh_bits == 8) hipLaunchKernelGGL((k_dec_gateup<8, 1>), dim3(nsh_gu), dim3(256), 0, st, a);
+    if (d.E <= 64)
+        hipLaunchKernelGGL((k_dec_gateup<4, 1>), dim3(ngu), dim3(256), 0, st, a);
+    else if (d.E <= 128)
+        hipLaunchKernelGGL((k_dec_gateup<4, 2>), dim3(ngu), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_dec_gateup<4, 4>), dim3(ngu), dim3(256), 0, st, a);
     e = hipGetLastError();
     if (e == hipSuccess && d.ev1) e = hipEventRecord(d.ev1, st);
     if (e != hipSuccess) return e;

@@ -80,6 +80,7 @@ Layout layout(const moe_shape *s, int which)
         // pair-indexed buffers, no permutation; shy holds the shared expert's
         // partial sums over 512-column chunks of its intermediate dimension
         L.decode = true;
+        L.zpart = take(moe::DEC_LOGIT_PLANES * T * E * 4);
         L.ids = take(P * 4);
         L.w = take(P * 4);
         L.gap = take(T * 4);
@@ -352,6 +353,7 @@ int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const m
         d.w = at<float>(ws, L.w);
         d.gap = at<float>(ws, L.gap);
         d.pscale = at<float>(ws, L.pscale);
+        d.z = at<float>(ws, L.zpart);
         d.gq = (const uint8_t *)w->gate.q;
         d.uq = (const uint8_t *)w->up.q;
         d.dq = (const uint8_t *)w->down.q;

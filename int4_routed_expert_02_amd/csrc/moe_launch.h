@@ -36,6 +36,7 @@ struct DecLaunch {
     float rsf;
     int32_t *ids;
     float *w, *gap, *pscale;
+    float *z;  // [DEC_LOGIT_PLANES][T][E] partial router logits (scratch)
     const uint8_t *gq, *uq, *dq;
     const float *gs, *us, *ds;
     int64_t qstride, dqstride, sstride, dsstride;
@@ -49,6 +50,7 @@ struct DecLaunch {
     int out_f32;
     hipEvent_t ev0, ev1;  // nullable: recorded around the gate/up kernel
 };
+constexpr int DEC_LOGIT_PLANES = 4;  // partial-logit planes of the small-batch router
 bool decode_supported(int T, int H, int E, int k, int I, int Ish, int sh_bits);
 hipError_t launch_decode(const DecLaunch &d, hipStream_t st);
 
