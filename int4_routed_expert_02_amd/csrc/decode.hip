@@ -187,18 +187,16 @@ __device__ __forceinline__ void cand_sort2(Cand &a, Cand &b)
 // The selected k are the first k, taken in that order; the weight of
 // selection j is s_j over the sum of the selected s (summed in selection
 // order); the tie gap is v_{k-1} - v_k.  Same results as moe_select.h.
-template <int KL, typename Pre>
+template <int KL>
 __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, const float *__restrict__ bias, int T,
                                                  int E, int k, int32_t *ids_l, float *w_l, bool pub,
-                                                 float *__restrict__ gap_g, Pre &&pre)
+                                                 float *__restrict__ gap_g)
 {
     const int tid = threadIdx.x, t = tid >> 3, q = tid & 7;
     Cand c[KL];
 #pragma unroll
     for (int j = 0; j < KL; ++j) c[j] = Cand{-INFINITY, 0.f, 0x7fffffff};
     const bool live = t < T && 8 * q < E;
-    // the logits are requested first, then the caller's own requests (pre), so
-    // that waiting for the logits never waits for those
     f32x4 pa[LG_NP][2], b0, b1;
     if (live) {
 #pragma unroll
@@ -210,7 +208,6 @@ __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, c
         b0 = *(const f32x4 *)(bias + 8 * q);
         b1 = *(const f32x4 *)(bias + 8 * q + 4);
     }
-    pre();
     if (live) {
         float z[8];
         const f32x4 a0 = pa[0][0], a1 = pa[0][1];
@@ -357,13 +354,13 @@ __device__ __forceinline__ int active_expert(const int32_t *__restrict__ ids, in
 struct DecArgs {
     const uint16_t *x;  // [T][H] bf16
     int T, H, k, E;
-    int32_t *ids;        // [T*k] selected experts (written by the first routed gate/up workgroup)
+    int32_t *ids;        // [T*k] selected experts (written by the first routed workgroup)
     float *w, *gap;      // [T*k] combine weights, [T] tie gaps (same writer)
+    float *pscale;       // [T*k] rsf * w (same writer)
     const float *zp;     // [LG_NP][T][E] partial router logits
     const float *rb;     // [E] selection bias
     int n_group, topk_group;
     float rsf;
-    int spec;  // routed units map to experts by index and fetch before routing
     // routed experts
     const uint8_t *gq, *uq, *dq;
     const float *gs, *us, *ds;
@@ -373,32 +370,26 @@ struct DecArgs {
     const uint8_t *sgq, *suq, *sdq;
     const float *sgs, *sus, *sds;
     int Ish, sh_bits;
-    // buffers
-    float *h;      // [P][I]
-    float *shh;    // [T][Ish]
-    float *pscale;  // [P] rsf * w
-    float *y;      // [P][H]
-    float *shp;    // [Ish/512][T][H]
+    // partial expert outputs, one plane per 64-row chunk of the intermediate
+    float *yp;   // [I/64][T*k][H]   routed, scaled by rsf * w
+    float *ysp;  // [Ish/64][T][H]   shared
 };
 
-// The routing decision of the batch into LDS (every routed gate/up workgroup
-// takes it, from the same logits, so all agree); the publishing workgroup
-// also writes ids, w, rsf * w and the tie gaps to global memory.
-// `pre` runs once, after the logits are requested and before they are used.
-template <int EPL, typename Pre>
-__device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k, int32_t *ids_l, float *w_l,
-                                          bool pub, Pre &&pre)
+// The routing decision of the batch into LDS (every routed workgroup takes
+// it, from the same logits, so all agree); the publishing workgroup also
+// writes ids, w, rsf * w and the tie gaps to global memory.
+template <int EPL>
+__device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k, int32_t *ids_l, float *w_l, bool pub)
 {
     const bool grouped = r.n_group > 1 && r.topk_group < r.n_group;
     if (!grouped && E <= 64 && E % 8 == 0 && k <= 3) {
         if (k == 1)
-            dec_select_lanes<2>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, pre);
+            dec_select_lanes<2>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
         else if (k == 2)
-            dec_select_lanes<3>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, pre);
+            dec_select_lanes<3>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
         else
-            dec_select_lanes<4>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, pre);
+            dec_select_lanes<4>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
     } else {
-        pre();
         dec_select_waves<EPL>(r.zp, r.rb, T, E, k, r.n_group, r.topk_group, r.rsf, ids_l, w_l, pub, r.gap);
     }
     __syncthreads();
@@ -410,7 +401,14 @@ __device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k,
         }
 }
 
-// ------------------------------------------------------------------ gate/up
+// ------------------------------------------------------------- expert kernel
+
+constexpr int DX_ROWS = 64;                  // intermediate rows per unit (16 per wave)
+constexpr int DX_LDH = DX_ROWS + 8;          // padded row of the on-chip h chunk (bf16)
+constexpr int DX_TILES = 16;                 // down output tiles of 16 columns per wave per round
+constexpr int DX_RCOLS = 4 * DX_TILES * 16;  // output columns per round (1024)
+constexpr int GU_CPL = 8;                    // 16-byte gate/up chunks per lane per row per super-stage
+constexpr int DX_LDY = DX_TILES * 16 + 4;    // padded row of a wave's staged down tile (floats)
 
 template <int CPL>
 __device__ __forceinline__ void load_rows(u32x4 (&dst)[CPL], const uint8_t *row)
@@ -419,27 +417,110 @@ __device__ __forceinline__ void load_rows(u32x4 (&dst)[CPL], const uint8_t *row)
     for (int c = 0; c < CPL; ++c) dst[c] = *(const u32x4 *)(row + c * 64);
 }
 
-// The body of k_dec_gateup for a compile-time number of 16-row blocks (NMB).
-// Per super-stage of KS columns: the activation rows are requested first, then
-// the wave's whole weight slice, so the activations can be staged in LDS
-// (interleaved, row sums taken) while the weights are still streaming in.
-constexpr int GU_CPL = 8;  // 16-byte gate/up weight chunks per lane per row per super-stage
+// Down weights of one round: lane (n, g) holds, for each of its wave's 16
+// output tiles tt, the 16 values of intermediate [16g, 16g + 16) of the chunk
+// in output row 16 tt + n of the wave's 256: 8 bytes int4 (u32x2), 16 bytes
+// int8 (u32x4).
+template <int WBITS>
+struct DownW {
+    uint32_t d[DX_TILES][WBITS / 2];
+};
 
+// Buffer resource over `bytes` bytes at `base` (raw, byte-addressed; loads
+// beyond the range return zero).  `base` and `bytes` must be uniform over the
+// wave; they are taken from the first lane so that the compiler keeps the
+// descriptor in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t p = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    void *ub = (void *)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// The 16 rows of a lane are 16 * rstride bytes apart: one per-lane offset
+// plus a uniform per-tile offset, so the 16 loads share one address register.
+template <int WBITS>
+__device__ __forceinline__ void load_down(DownW<WBITS> &w, f32x4 &sd, const uint8_t *dq, const float *dsc,
+                                          int64_t rstride, int H, int col0, int i0)
+{
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    sd = *(const f32x4 *)(dsc + col0 + 4 * lane);  // the wave's 256 row scales, 4 per lane
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(dq, (uint32_t)(H * rstride));
+    const int voff = (int)((col0 + n) * rstride + (i0 + 16 * g) * WBITS / 8);
+#pragma unroll
+    for (int tt = 0; tt < DX_TILES; ++tt) {
+        const int soff = (int)(tt * 16 * rstride);
+        if constexpr (WBITS == 4) {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+            w.d[tt][0] = v[0];
+            w.d[tt][1] = v[1];
+        } else {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w.d[tt][q] = v[q];
+        }
+    }
+}
+
+// Position of intermediate j (0..63) in a row of the on-chip h chunk: with
+// int4 weights each 8-group is stored in the unpack's k-slot order
+// (j0, j4, j1, j5, j2, j6, j3, j7).
+template <int WBITS>
+__device__ __forceinline__ int h_pos(int j)
+{
+    return WBITS == 4 ? (j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1) : j;
+}
+
+// LDS of the expert kernel.  The routing lists are dead once the unit's pairs
+// are gathered and the staged activations once the gate/up MFMAs are done, so
+// routing lists, activations and down scales share one area.
+template <int WBITS>
+struct alignas(16) DxSmem {
+    static constexpr int KS = 512 * 8 / WBITS;  // columns per gate/up super-stage
+    static constexpr int LDA = KS + 8;
+    union {
+        uint16_t a[DEC_MAXT * LDA];  // bf16 activations of the super-stage
+        struct {
+            int32_t ids[DEC_MAXT * DEC_MAXK];
+            int flags[256];
+        } r;
+        float y[4][16 * DX_LDY];  // each wave's 16 x 256 down tile, raw (after the gate/up MFMAs)
+    } u;
+    float w[DEC_MAXT * DEC_MAXK];            // routing weights of the batch
+    uint16_t hh[DEC_MAXT * DX_LDH];          // h chunk, bf16 high part
+    uint16_t hl[DEC_MAXT * DX_LDH];          // h chunk, bf16 low part (h - high)
+    float xsum[DEC_MAXT];                    // activation row sums
+    float hs[4][DEC_MAXT];                   // per-wave h row sums
+    float psc[DEC_MAXT];                     // output scale of each row (rsf * w, or 1)
+    f32x4 rowinfo[DEC_MAXT];                 // per row: 136 * h row sum, output scale, output row
+    int plist[DEC_MAXT], tok[DEC_MAXT];
+    int pcnt, ares;
+};
+
+// One unit: gate/up of 64 intermediate rows for the n rows of its batch
+// (SwiGLU -> h chunk, on chip as an exact bf16 high + low pair), then
+// y_part = h_chunk . D[:, chunk]^T for every output column, scaled by the
+// down row scale and the row's output scale, stored to plane `chunk` of out.
+// Loads are issued in the order they are needed (activations, gate/up rows,
+// down slice): vector loads complete in issue order, so waiting for the
+// activations never waits for the weights.
 template <int WBITS, int NMB>
-__device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n, const int *plist, const int *tok,
-                                            uint16_t *sA, float *sPart, const uint8_t *grow, const uint8_t *urow,
-                                            const u32x4 (&wg0)[GU_CPL], const u32x4 (&wu0)[GU_CPL], float sg,
-                                            float su, float *dst, int I, int row)
+__device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm, int n,
+                                            const uint8_t *grow, const uint8_t *urow, float sg, float su,
+                                            const uint8_t *dq, const float *dsc, int64_t drstride, int i0,
+                                            float *out, int nrows)
 {
     constexpr int CPL = GU_CPL;
     constexpr int SB = CPL * 64;           // weight bytes of a row per super-stage (512)
-    constexpr int KS = SB * 8 / WBITS;     // columns per super-stage (1024 int4, 512 int8)
-    constexpr int LDA = KS + 8;
+    constexpr int KS = DxSmem<WBITS>::KS;  // columns per super-stage (1024 int4, 512 int8)
+    constexpr int LDA = DxSmem<WBITS>::LDA;
     constexpr int CPR = KS / 8;            // 8-column activation chunks per row
     constexpr int XPT = CPR / 16;          // chunks per thread: a 16-thread group owns one row
-    constexpr int NCH = 2;                 // independent accumulator chains per matrix
+    constexpr int NCH = NMB == 1 ? 2 : 1;  // independent accumulator chains per matrix (register budget)
     static_assert(CPR == 128 || CPR == 64, "a row is 128 or 64 chunks");
-    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, ln = lane & 15;
     f32x4 acc[NMB][2][NCH];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -451,13 +532,13 @@ __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) rsum[mb] = 0.f;
     const int nss = a.H / KS;
-    const uint16_t *ap = sA + (lane & 15) * LDA;
+    const uint16_t *ap = sm.u.a + ln * LDA;
     const int rsub = tid >> 4, csub = tid & 15;  // row within a 16-row block, chunk phase
     const uint16_t *xrow[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
         const int r = mb * 16 + rsub;
-        xrow[mb] = (r < n) ? a.x + (size_t)(shared ? r : tok[r]) * a.H + csub * 8 : nullptr;
+        xrow[mb] = (r < n) ? a.x + (size_t)sm.tok[r] * a.H + csub * 8 : nullptr;
     }
     auto load_x = [&](u32x4 (&xr)[XPT], int mb, int ss) {
         if (xrow[mb]) {
@@ -469,7 +550,7 @@ __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n
         }
     };
     auto stage_x = [&](u32x4 (&xr)[XPT], int mb) {
-        uint16_t *dstrow = sA + (mb * 16 + rsub) * LDA + csub * 8;
+        uint16_t *dstrow = sm.u.a + (mb * 16 + rsub) * LDA + csub * 8;
 #pragma unroll
         for (int j = 0; j < XPT; ++j) {
             u32x4 v = xr[j];
@@ -481,27 +562,20 @@ __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n
             *(u32x4 *)(dstrow + j * 128) = v;
         }
     };
+    DownW<WBITS> dw;
+    f32x4 sdv;
+    u32x4 wg[CPL], wu[CPL];
     for (int ss = 0; ss < nss; ++ss) {
-        u32x4 xr[XPT];
-        load_x(xr, 0, ss);
-        u32x4 wg[CPL], wu[CPL];
-        if (ss == 0) {  // the first super-stage's weights were requested by the caller
+        u32x4 xr[NMB][XPT];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                wg[c] = wg0[c];
-                wu[c] = wu0[c];
-            }
-        } else {
-            load_rows<CPL>(wg, grow + (size_t)ss * SB);
-            load_rows<CPL>(wu, urow + (size_t)ss * SB);
-        }
+        for (int mb = 0; mb < NMB; ++mb) load_x(xr[mb], mb, ss);
+        load_rows<CPL>(wg, grow + (size_t)ss * SB);
+        load_rows<CPL>(wu, urow + (size_t)ss * SB);
+        // the first round of down weights: in flight during the gate/up MFMAs
+        if (ss == nss - 1) load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, wave * (DX_TILES * 16), i0);
         if (ss > 0) __syncthreads();  // the previous super-stage's A reads are done
-        stage_x(xr, 0);
 #pragma unroll
-        for (int mb = 1; mb < NMB; ++mb) {
-            load_x(xr, mb, ss);
-            stage_x(xr, mb);
-        }
+        for (int mb = 0; mb < NMB; ++mb) stage_x(xr[mb], mb);
         if (ss == nss - 1) {
             // row sums: the 16 threads of a row are 16 consecutive lanes
 #pragma unroll
@@ -509,7 +583,7 @@ __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n
                 float s = rsum[mb];
 #pragma unroll
                 for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, WAVE);
-                if (csub == 0) sPart[mb * 16 + rsub] = s;
+                if (csub == 0) sm.xsum[mb * 16 + rsub] = s;
             }
         }
         __syncthreads();
@@ -542,330 +616,230 @@ __device__ __forceinline__ void gateup_body(const DecArgs &a, bool shared, int n
             }
         }
     }
+    // SwiGLU epilogue: h for (row m, intermediate wave * 16 + ln) -> on-chip
+    // chunk as bf16 high + low; per-wave row sums of (high + low) over the 16
+    // intermediates of the wave, added over lanes in a fixed tree order.
     const float bias = (WBITS == 4) ? INT4_BIAS : 0.f;
+    const int hp = h_pos<WBITS>(wave * 16 + ln);
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = mb * 16 + g * 4 + r;
-            if (m >= n) continue;
-            const float corr = bias * sPart[m];
+            const float corr = bias * sm.xsum[m];
             float ga = acc[mb][0][0][r], ua = acc[mb][1][0][r];
 #pragma unroll
             for (int ch = 1; ch < NCH; ++ch) {
                 ga += acc[mb][0][ch][r];
                 ua += acc[mb][1][ch][r];
             }
-            const float gv = (ga - corr) * sg;
-            const float uv = (ua - corr) * su;
-            const int orow = shared ? m : plist[m];
-            dst[(size_t)orow * I + row] = fast_silu(gv) * uv;
+            const float h = m < n ? fast_silu((ga - corr) * sg) * ((ua - corr) * su) : 0.f;
+            const uint16_t hb = f32_to_bf16(h);
+            const uint16_t lb = f32_to_bf16(h - bf16_to_f32(hb));
+            sm.hh[m * DX_LDH + hp] = hb;
+            sm.hl[m * DX_LDH + hp] = lb;
+            float s = bf16_to_f32(hb) + bf16_to_f32(lb);
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, WAVE);
+            if (ln == 0) sm.hs[wave][m] = s;
         }
-    }
-}
-
-// units: [0, nsh) shared (64 intermediate rows each), then E * (I/64) routed.
-// Each wave owns 16 intermediate rows i and streams both their gate and up rows.
-// Routed units first take the routing decision for the whole batch (every
-// routed workgroup computes the same one from the logits).  With a.spec set
-// (a batch expected to touch most experts) routed unit v belongs to expert
-// v / (I/64) and requests its first weight stage before routing, so the
-// selection overlaps the weight fetch; a unit whose expert nobody chose
-// exits.  Otherwise unit v belongs to the (v / (I/64))-th chosen expert in
-// ascending id order and fetches after routing (no wasted reads).
-template <int WBITS, int EPL>
-__global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a)
-{
-    constexpr int KS = 512 * 8 / WBITS;
-    constexpr int LDA = KS + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t sA[DEC_MAXT * LDA];
-    __shared__ float sPart[DEC_MAXT];
-    __shared__ int plist[DEC_MAXT], tok[DEC_MAXT];
-    __shared__ int flags[256];
-    __shared__ int32_t sIds[DEC_MAXT * DEC_MAXK];
-    __shared__ float sW[DEC_MAXT * DEC_MAXK];
-    __shared__ int pcnt, ares;
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
-    const int nsh = a.sh_bits ? a.Ish / 64 : 0;
-    const int u = blockIdx.x;
-    const bool shared = u < nsh;
-    if ((shared ? a.sh_bits : 4) != WBITS) return;  // the launch instantiates one weight format
-    const size_t rbytes = (size_t)a.H * WBITS / 8;
-    u32x4 wg0[GU_CPL], wu0[GU_CPL];
-    const uint8_t *grow, *urow;
-    float sg, su;
-    int row;
-    auto fetch = [&](const uint8_t *gq, const uint8_t *uq, const float *gsc, const float *usc, int i0) {
-        row = i0 + wave * 16 + (lane & 15);
-        grow = gq + (size_t)row * rbytes + g * 16;
-        urow = uq + (size_t)row * rbytes + g * 16;
-        load_rows<GU_CPL>(wg0, grow);
-        load_rows<GU_CPL>(wu0, urow);
-        sg = gsc[row];
-        su = usc[row];
-    };
-    int n, I;
-    float *dst;
-    if (shared) {
-        fetch(a.sgq, a.suq, a.sgs, a.sus, u * 64);
-        n = a.T;
-        I = a.Ish;
-        dst = a.shh;
-    } else {
-        const int v = u - nsh, per = a.I / 64;
-        int e = v / per;
-        dec_route<EPL>(a, a.T, a.E, a.k, sIds, sW, v == 0, [&]() {
-            if (a.spec)
-                fetch(a.gq + (size_t)e * a.qstride, a.uq + (size_t)e * a.qstride, a.gs + (size_t)e * a.sstride,
-                      a.us + (size_t)e * a.sstride, (v % per) * 64);
-        });
-        if (!a.spec) {
-            e = active_expert(sIds, a.T * a.k, a.E, v / per, flags, &ares);
-            if (e < 0) return;
-            fetch(a.gq + (size_t)e * a.qstride, a.uq + (size_t)e * a.qstride, a.gs + (size_t)e * a.sstride,
-                  a.us + (size_t)e * a.sstride, (v % per) * 64);
-        }
-        n = gather_pairs(sIds, a.T * a.k, a.k, e, plist, tok, &pcnt);
-        if (n == 0) return;  // (speculative units only) nobody chose this expert
-        I = a.I;
-        dst = a.h;
-    }
-    if (n <= 16)
-        gateup_body<WBITS, 1>(a, shared, n, plist, tok, sA, sPart, grow, urow, wg0, wu0, sg, su, dst, I, row);
-    else
-        gateup_body<WBITS, 2>(a, shared, n, plist, tok, sA, sPart, grow, urow, wg0, wu0, sg, su, dst, I, row);
-}
-
-// ------------------------------------------------------------------- down
-
-constexpr int DN_ROWS = 128;  // output rows per down unit (32 per wave)
-// 16-byte weight chunks per lane per row of a 512-column unit (4 int4, 8 int8)
-constexpr int dn_cpl(int wbits) { return 512 * wbits / 8 / 64; }
-
-// The body of k_dec_down: h rows (f32) are requested first, then the wave's
-// weight slice (2 blocks of 16 output rows); h is split into exact hi + lo
-// bf16 planes in LDS while the weights stream in.  One 512-column chunk of the
-// reduction per unit.
-template <int WBITS, int NMB>
-__device__ __forceinline__ void down_body(const DecArgs &a, bool shared, int n, const int *plist, uint16_t *sHi,
-                                          uint16_t *sLo, float *sPart, const u32x4 (&w0)[dn_cpl(WBITS)],
-                                          const u32x4 (&w1)[dn_cpl(WBITS)], const float *hsrc, int hld, int kbeg,
-                                          float sd0, float sd1, int row0, int row1)
-{
-    constexpr int KC = 512;                   // reduction columns per unit
-    constexpr int CPL = dn_cpl(WBITS);
-    constexpr int LDA = KC + 8;
-    constexpr int CPR = KC / 8;               // 64 chunks of 8 columns per row
-    constexpr int XPT = NMB * 16 * CPR / 256;
-    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
-    f32x4 hv[XPT][2];
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-        const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
-        hv[i][0] = hv[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (r < n) {
-            const float *hp = hsrc + (size_t)(shared ? r : plist[r]) * hld + kbeg + cc * 8;
-            hv[i][0] = *(const f32x4 *)hp;
-            hv[i][1] = *(const f32x4 *)(hp + 4);
-        }
-    }
-    float rsum[XPT];
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-        const int c = tid + 256 * i, r = c / CPR, cc = c % CPR;
-        u32x4 hi, lo;
-        float s = 0.f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            uint32_t hb[2], lb[2];
-#pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-                const float v = hv[i][d / 2][(d % 2) * 2 + e2];
-                hb[e2] = f32_to_bf16(v);
-                const float hf = __uint_as_float(hb[e2] << 16);
-                lb[e2] = f32_to_bf16(v - hf);
-                s += hf + __uint_as_float(lb[e2] << 16);
-            }
-            hi[d] = hb[0] | (hb[1] << 16);
-            lo[d] = lb[0] | (lb[1] << 16);
-        }
-        rsum[i] = s;
-        if (WBITS == 4) {
-            hi = interleave_bf16x8(hi);
-            lo = interleave_bf16x8(lo);
-        }
-        *(u32x4 *)(sHi + r * LDA + cc * 8) = hi;
-        *(u32x4 *)(sLo + r * LDA + cc * 8) = lo;
-    }
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-        float s = rsum[i];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, WAVE);
-        const int c = tid + 256 * i, r = c / CPR;
-        if ((c % CPR) == 0) sPart[r] = s;
     }
     __syncthreads();
-    // chains: [row block 0/1][hi/lo plane]
-    f32x4 acc[NMB][2][2];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int x = 0; x < 2; ++x) acc[mb][x][0] = acc[mb][x][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t *ah = sHi + (lane & 15) * LDA, *al = sLo + (lane & 15) * LDA;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        if constexpr (WBITS == 4) {
-#pragma unroll
-            for (int wd = 0; wd < 4; ++wd) {
-                const u32x4 b0 = unpack_int4x8(w0[c][wd]);
-                const u32x4 b1 = unpack_int4x8(w1[c][wd]);
-                const int ko = (4 * c + g) * 32 + 8 * wd;
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb) {
-                    const u32x4 fh = *(const u32x4 *)(ah + mb * 16 * LDA + ko);
-                    const u32x4 fl = *(const u32x4 *)(al + mb * 16 * LDA + ko);
-                    acc[mb][0][0] = mfma_bf16(fh, b0, acc[mb][0][0]);
-                    acc[mb][1][0] = mfma_bf16(fh, b1, acc[mb][1][0]);
-                    acc[mb][0][1] = mfma_bf16(fl, b0, acc[mb][0][1]);
-                    acc[mb][1][1] = mfma_bf16(fl, b1, acc[mb][1][1]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int wd = 0; wd < 2; ++wd) {
-                const u32x4 b0 = unpack_int8x8(u32x2{w0[c][2 * wd], w0[c][2 * wd + 1]});
-                const u32x4 b1 = unpack_int8x8(u32x2{w1[c][2 * wd], w1[c][2 * wd + 1]});
-                const int ko = (4 * c + g) * 16 + 8 * wd;
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb) {
-                    const u32x4 fh = *(const u32x4 *)(ah + mb * 16 * LDA + ko);
-                    const u32x4 fl = *(const u32x4 *)(al + mb * 16 * LDA + ko);
-                    acc[mb][0][0] = mfma_bf16(fh, b0, acc[mb][0][0]);
-                    acc[mb][1][0] = mfma_bf16(fh, b1, acc[mb][1][0]);
-                    acc[mb][0][1] = mfma_bf16(fl, b0, acc[mb][0][1]);
-                    acc[mb][1][1] = mfma_bf16(fl, b1, acc[mb][1][1]);
-                }
-            }
-        }
+    if (tid < NMB * 16) {
+        const int m = tid;
+        const float cor = bias * (((sm.hs[0][m] + sm.hs[1][m]) + sm.hs[2][m]) + sm.hs[3][m]);
+        const int orow = m < n ? sm.plist[m] : 0;
+        sm.rowinfo[m] = f32x4{cor, sm.psc[m], __int_as_float(orow), 0.f};
     }
-    const float bias = (WBITS == 4) ? INT4_BIAS : 0.f;
+    __syncthreads();
+    // down: A = h chunk (rows m, 64 k in two 32-steps, high and low planes),
+    // one 16-row block at a time (the weights are unpacked again per block).
+    // Each wave stages its raw 16 x 256 result in LDS and writes it out row
+    // by row as 16-byte stores, applying (d - 136 rowsum) * row scale * output
+    // scale on the way.
+    const int chunk = i0 / DX_ROWS;
+    float *yl = sm.u.y[wave];
+    for (int c0 = 0; c0 < a.H; c0 += DX_RCOLS) {
+        const int col0 = c0 + wave * (DX_TILES * 16);
+        if (c0 > 0) load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, col0, i0);
+#pragma unroll 1
+        for (int mb = 0; mb < NMB; ++mb) {
+            if (mb * 16 >= n) break;
+            u32x4 fh[2], fl[2];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
+            for (int s = 0; s < 2; ++s) {
+                fh[s] = *(const u32x4 *)(sm.hh + (mb * 16 + ln) * DX_LDH + 16 * g + 8 * s);
+                fl[s] = *(const u32x4 *)(sm.hl + (mb * 16 + ln) * DX_LDH + 16 * g + 8 * s);
+            }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = mb * 16 + g * 4 + r;
-            if (m >= n) continue;
-            const float corr = bias * sPart[m];
-            const float v0 = (acc[mb][0][0][r] + acc[mb][0][1][r] - corr) * sd0;
-            const float v1 = (acc[mb][1][0][r] + acc[mb][1][1][r] - corr) * sd1;
-            if (shared) {
-                float *o = a.shp + ((size_t)(kbeg / KC) * a.T + m) * a.H;
-                o[row0] = v0;
-                o[row1] = v1;
-            } else {
-                const int p = plist[m];
-                const float ps = a.pscale[p];
-                float *o = a.y + ((size_t)(kbeg / KC) * a.T * a.k + p) * a.H;
-                o[row0] = v0 * ps;
-                o[row1] = v1 * ps;
+            for (int tt = 0; tt < DX_TILES; ++tt) {
+                u32x4 b0, b1;
+                if constexpr (WBITS == 4) {
+                    b0 = unpack_int4x8(dw.d[tt][0]);
+                    b1 = unpack_int4x8(dw.d[tt][1]);
+                } else {
+                    b0 = unpack_int8x8(u32x2{dw.d[tt][0], dw.d[tt][1]});
+                    b1 = unpack_int8x8(u32x2{dw.d[tt][2], dw.d[tt][3]});
+                }
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                d = mfma_bf16(fh[0], b0, d);
+                d = mfma_bf16(fl[0], b0, d);
+                d = mfma_bf16(fh[1], b1, d);
+                d = mfma_bf16(fl[1], b1, d);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yl[(4 * g + r) * DX_LDY + tt * 16 + ln] = d[r];
+            }
+            // read back row-wise (own wave's data: LDS order within the wave suffices)
+            const int nr = n - mb * 16;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                if (rr < nr) {
+                    const f32x4 ri = sm.rowinfo[mb * 16 + rr];
+                    const f32x4 v = *(const f32x4 *)(yl + rr * DX_LDY + 4 * lane);
+                    f32x4 o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) o[q] = (v[q] - ri[0]) * sdv[q] * ri[1];
+                    *(f32x4 *)(out + ((size_t)chunk * nrows + __float_as_int(ri[2])) * a.H + col0 + 4 * lane) = o;
+                }
             }
         }
     }
 }
 
-// units: [0, nsh) shared (128 output rows x one 512-column chunk of Ish), then
-// routed (expert, 128 output rows, one 512-column chunk of I).  The expert of
-// a routed unit is its index / units-per-expert with a.spec set (weights are
-// requested before the routing is read; units of unchosen experts exit),
-// else the chosen expert of that rank in ascending id order.
-template <int WBITS>
-__global__ __launch_bounds__(256) void k_dec_down(DecArgs a)
+// Units (logical index L): [0, nsh) shared-expert units (64 intermediate rows
+// x up to 16 tokens: the two token halves of a chunk are adjacent units),
+// then routed units (rank of the chosen expert in ascending id order, chunk).
+// Routed units first take the routing decision of the whole batch (every
+// one computes the same from the logits), then gather the pairs routed to
+// their expert; units beyond the chosen experts exit.  A unit's loads are
+// its activation rows, its gate/up rows and its down slice (all output rows,
+// the chunk's 64 columns), all in flight before the first MFMA.
+//
+// XCD-aware placement: workgroup b runs on XCD b % 8; logical units 4q ..
+// 4q + 3 (chunks whose down slices share 128-byte lines, or the token
+// halves of one chunk) are given workgroups on the same XCD, so shared data
+// is fetched into one L2.
+__device__ __forceinline__ int dx_logical_unit(int b)
 {
-    constexpr int LDA = 512 + 8;
-    constexpr int CPL = dn_cpl(WBITS);
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][DEC_MAXT * LDA];  // hi, lo planes
-    __shared__ float sPart[DEC_MAXT];
-    __shared__ int plist[DEC_MAXT], tok[DEC_MAXT];
-    __shared__ int flags[256];
-    __shared__ int pcnt, ares;
+    const int x = b & 7, s = b >> 3;
+    return 4 * (x + 8 * (s >> 2)) + (s & 3);
+}
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
-    const int nkc = a.sh_bits ? a.Ish / 512 : 0;
-    const int nsh = nkc * (a.H / DN_ROWS);
-    const int u = blockIdx.x;
-    const bool shared = u < nsh;
-    if ((shared ? a.sh_bits : 4) != WBITS) return;
-    u32x4 w0[CPL], w1[CPL];
-    float sd0, sd1;
-    int row0, row1;
-    auto fetch = [&](const uint8_t *dq, const float *dsc, int K, int c0, int kbeg) {
-        row0 = c0 + wave * 32 + (lane & 15);
-        row1 = row0 + 16;
-        const size_t rbytes = (size_t)K * WBITS / 8;
-        const uint8_t *drow0 = dq + (size_t)row0 * rbytes + (size_t)kbeg * WBITS / 8 + g * 16;
-        load_rows<CPL>(w0, drow0);
-        load_rows<CPL>(w1, drow0 + 16 * rbytes);
-        sd0 = dsc[row0];
-        sd1 = dsc[row1];
+__host__ __device__ __forceinline__ int dx_token_halves(int T) { return (T + 15) / 16; }
+
+template <int WBITS, int EPL>
+__global__ __launch_bounds__(256, WBITS == 4 ? 2 : 1) void k_dec_expert(DecArgs a, int nunits)
+{
+    __shared__ DxSmem<WBITS> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+    const int nth = dx_token_halves(a.T);
+    const int nsh = a.sh_bits ? (a.Ish / DX_ROWS) * nth : 0;
+    const int L = dx_logical_unit(blockIdx.x);
+    if (L >= nunits) return;
+    const bool shared = L < nsh;
+    if ((shared ? a.sh_bits : 4) != WBITS) return;  // the launch instantiates one weight format
+    const size_t rbytes = (size_t)a.H * WBITS / 8;
+    const uint8_t *grow, *urow, *dq;
+    const float *dsc;
+    float sg, su;
+    int64_t drs;
+    int i0;
+    auto locate = [&](const uint8_t *gq, const uint8_t *uq, const uint8_t *dqq, const float *gsc, const float *usc,
+                      const float *dscc, int K, int chunk0) {
+        i0 = chunk0;
+        const int row = i0 + wave * 16 + (lane & 15);
+        grow = gq + (size_t)row * rbytes + g * 16;
+        urow = uq + (size_t)row * rbytes + g * 16;
+        sg = gsc[row];
+        su = usc[row];
+        dq = dqq;
+        dsc = dscc;
+        drs = (int64_t)K * WBITS / 8;
     };
-    int n, kbeg, hld;
-    const float *hsrc;
+    int n, nrows;
+    float *out;
     if (shared) {
-        const int kc = u % nkc;
-        kbeg = kc * 512;
-        fetch(a.sdq, a.sds, a.Ish, (u / nkc) * DN_ROWS, kbeg);
-        n = a.T;
-        hsrc = a.shh;
-        hld = a.Ish;
-    } else {
-        const int nkr = a.I / 512;
-        const int v = u - nsh, per = (a.H / DN_ROWS) * nkr;
-        const int c0 = ((v % per) / nkr) * DN_ROWS;
-        kbeg = ((v % per) % nkr) * 512;
-        int e = v / per;
-        if (a.spec) {
-            fetch(a.dq + (size_t)e * a.dqstride, a.ds + (size_t)e * a.dsstride, a.I, c0, kbeg);
-        } else {
-            e = active_expert(a.ids, a.T * a.k, a.E, v / per, flags, &ares);
-            if (e < 0) return;
-            fetch(a.dq + (size_t)e * a.dqstride, a.ds + (size_t)e * a.dsstride, a.I, c0, kbeg);
+        const int th = L % nth;
+        locate(a.sgq, a.suq, a.sdq, a.sgs, a.sus, a.sds, a.Ish, (L / nth) * DX_ROWS);
+        n = a.T - 16 * th < 16 ? a.T - 16 * th : 16;
+        nrows = a.T;
+        out = a.ysp;
+        if (tid < 16) {
+            sm.tok[tid] = 16 * th + tid;
+            sm.plist[tid] = 16 * th + tid;
+            sm.psc[tid] = 1.0f;
         }
-        n = gather_pairs(a.ids, a.T * a.k, a.k, e, plist, tok, &pcnt);
-        if (n == 0) return;  // (speculative units only) nobody chose this expert
-        hsrc = a.h;
-        hld = a.I;
+        __syncthreads();
+    } else {
+        const int v = L - nsh, per = a.I / DX_ROWS;
+        dec_route<EPL>(a, a.T, a.E, a.k, sm.u.r.ids, sm.w, v == 0);
+        const int e = __builtin_amdgcn_readfirstlane(
+            active_expert(sm.u.r.ids, a.T * a.k, a.E, v / per, sm.u.r.flags, &sm.ares));
+        if (e < 0) return;
+        locate(a.gq + (size_t)e * a.qstride, a.uq + (size_t)e * a.qstride, a.dq + (size_t)e * a.dqstride,
+               a.gs + (size_t)e * a.sstride, a.us + (size_t)e * a.sstride, a.ds + (size_t)e * a.dsstride, a.I,
+               (v % per) * DX_ROWS);
+        n = __builtin_amdgcn_readfirstlane(gather_pairs(sm.u.r.ids, a.T * a.k, a.k, e, sm.plist, sm.tok, &sm.pcnt));
+        nrows = a.T * a.k;
+        out = a.yp;
+        if (tid < n) sm.psc[tid] = a.rsf * sm.w[sm.plist[tid]];
     }
     if (n <= 16)
-        down_body<WBITS, 1>(a, shared, n, plist, sA[0], sA[1], sPart, w0, w1, hsrc, hld, kbeg, sd0, sd1, row0, row1);
+        expert_body<WBITS, 1>(a, sm, n, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
     else
-        down_body<WBITS, 2>(a, shared, n, plist, sA[0], sA[1], sPart, w0, w1, hsrc, hld, kbeg, sd0, sd1, row0, row1);
+        expert_body<WBITS, 2>(a, sm, n, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
 }
 
 // ---------------------------------------------------------------- combine
 
-__global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ y, int nkr, const float *__restrict__ shp,
-                                                     int nkc, const uint16_t *__restrict__ res, void *__restrict__ out,
-                                                     int T, int H, int k, int out_f32)
+constexpr int CB_SPLIT = 4;  // threads per output quad, each summing every 4th plane
+
+// out[t] = sum over partial planes (routed pairs of t in order j, their
+// chunks in order; then the shared expert's chunks) (+ x[t]).  Four
+// consecutive lanes own one 4-column quad: lane q sums planes q, q + 4, ...
+// with all its loads in flight together, then the four sums are added in
+// lane order.  Fixed order throughout.
+__global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ yp, int nkr,
+                                                     const float *__restrict__ ysp, int nks,
+                                                     const uint16_t *__restrict__ res, void *__restrict__ out, int T,
+                                                     int H, int k, int out_f32)
 {
+    constexpr int MAXL = 16;  // planes per lane per batch
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
     const int cpt = H / 4;
-    if (idx >= (long)T * cpt) return;
-    const int t = (int)(idx / cpt);
-    const int c = (int)(idx % cpt) * 4;
+    const bool live = idx < (long)T * cpt * CB_SPLIT;
+    const long quad = idx / CB_SPLIT;
+    const int q = (int)(idx % CB_SPLIT);
+    const int t = live ? (int)(quad / cpt) : 0;
+    const int c = live ? (int)(quad % cpt) * 4 : 0;
+    const size_t P = (size_t)T * k;
+    const int nrp = k * nkr, np = nrp + nks;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j)
-        for (int kr = 0; kr < nkr; ++kr) {
-            const f32x4 v = *(const f32x4 *)(y + (((size_t)kr * T + t) * k + j) * H + c);
+    for (int p0 = q; p0 < np; p0 += CB_SPLIT * MAXL) {
+        f32x4 v[MAXL];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] += v[i];
+        for (int i = 0; i < MAXL; ++i) {
+            const int p = p0 + CB_SPLIT * i;
+            v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (live && p < np) {
+                const float *src = p < nrp ? yp + ((size_t)(p % nkr) * P + (size_t)t * k + p / nkr) * H + c
+                                           : ysp + ((size_t)(p - nrp) * T + t) * H + c;
+                v[i] = *(const f32x4 *)src;
+            }
         }
-    for (int kc = 0; kc < nkc; ++kc) {
-        const f32x4 v = *(const f32x4 *)(shp + ((size_t)kc * T + t) * H + c);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += v[i];
+        for (int i = 0; i < MAXL; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += v[i][e];
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float s1 = __shfl_down(acc[e], 1, WAVE);
+        const float s2 = __shfl_down(acc[e], 2, WAVE);
+        const float s3 = __shfl_down(acc[e], 3, WAVE);
+        acc[e] = ((acc[e] + s1) + s2) + s3;
+    }
+    if (!live || q != 0) return;
     if (res) {
         const u32x2 v = *(const u32x2 *)(res + (size_t)t * H + c);
         acc[0] += bf16_lo(v[0]);
@@ -901,12 +875,12 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     a.ids = d.ids;
     a.w = d.w;
     a.gap = d.gap;
+    a.pscale = d.pscale;
     a.zp = d.z;
     a.rb = d.rb;
     a.n_group = d.n_group;
     a.topk_group = d.topk_group;
     a.rsf = d.rsf;
-    a.spec = 0;
     a.gq = d.gq;
     a.uq = d.uq;
     a.dq = d.dq;
@@ -926,11 +900,8 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     a.sds = d.sds;
     a.Ish = d.Ish;
     a.sh_bits = d.sh_bits;
-    a.h = d.h;
-    a.shh = d.shh;
-    a.pscale = d.pscale;
-    a.y = d.y;
-    a.shp = d.shp;
+    a.yp = d.y;
+    a.ysp = d.shp;
 
     {
         const int grid = ((d.E + 15) / 16) * ((d.T + 15) / 16) * LG_NP;
@@ -939,38 +910,29 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    // gate/up: the int8 shared expert needs its own instantiation
-    const int nsh_gu = d.sh_bits ? d.Ish / 64 : 0;
-    const int ngu = nsh_gu + d.E * (d.I / 64);
+    // expert units; the grid is padded to whole groups of 32 workgroups (the
+    // XCD-aware placement permutes within such groups)
+    const int nsh = d.sh_bits ? (d.Ish / DX_ROWS) * dx_token_halves(d.T) : 0;
+    const int nunits = nsh + d.E * (d.I / DX_ROWS);
+    const int grid = (nunits + 31) / 32 * 32;
     if (d.ev0) {
         e = hipEventRecord(d.ev0, st);
         if (e != hipSuccess) return e;
     }
-    if (d.sh_bits == 8) hipLaunchKernelGGL((k_dec_gateup<8, 1>), dim3(nsh_gu), dim3(256), 0, st, a);
+    if (d.sh_bits == 8) hipLaunchKernelGGL((k_dec_expert<8, 1>), dim3(grid), dim3(256), 0, st, a, nunits);
     if (d.E <= 64)
-        hipLaunchKernelGGL((k_dec_gateup<4, 1>), dim3(ngu), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_dec_expert<4, 1>), dim3(grid), dim3(256), 0, st, a, nunits);
     else if (d.E <= 128)
-        hipLaunchKernelGGL((k_dec_gateup<4, 2>), dim3(ngu), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_dec_expert<4, 2>), dim3(grid), dim3(256), 0, st, a, nunits);
     else
-        hipLaunchKernelGGL((k_dec_gateup<4, 4>), dim3(ngu), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_dec_expert<4, 4>), dim3(grid), dim3(256), 0, st, a, nunits);
     e = hipGetLastError();
     if (e == hipSuccess && d.ev1) e = hipEventRecord(d.ev1, st);
     if (e != hipSuccess) return e;
-    const int nkc = d.sh_bits ? d.Ish / 512 : 0;
-    const int nkr = d.I / 512;
-    const int nsh_d = nkc * (d.H / DN_ROWS);
-    const int nd = nsh_d + d.E * (d.H / DN_ROWS) * nkr;
-    if (d.sh_bits == 8) {
-        hipLaunchKernelGGL(k_dec_down<8>, dim3(nsh_d), dim3(256), 0, st, a);
-        hipLaunchKernelGGL(k_dec_down<4>, dim3(nd), dim3(256), 0, st, a);
-    } else {
-        hipLaunchKernelGGL(k_dec_down<4>, dim3(nd), dim3(256), 0, st, a);
-    }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long nthreads = (long)d.T * (d.H / 4);
-    hipLaunchKernelGGL(k_dec_combine, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, d.y, nkr, d.shp,
-                       nkc, d.res, d.out, d.T, d.H, d.k, d.out_f32);
+    const long nthreads = (long)d.T * (d.H / 4) * CB_SPLIT;
+    hipLaunchKernelGGL(k_dec_combine, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, d.y,
+                       d.I / DX_ROWS, d.shp, d.sh_bits ? d.Ish / DX_ROWS : 0, d.res, d.out, d.T, d.H, d.k,
+                       d.out_f32);
     return hipGetLastError();
 }
 

@@ -77,20 +77,16 @@ Layout layout(const moe_shape *s, int which)
     } else if (which == MOE_WS_EXPERT_FFN) {
         L.hbuf = take(P * (size_t)s->I * 4);
     } else if (use_decode(s)) {
-        // pair-indexed buffers, no permutation; shy holds the shared expert's
-        // partial sums over 512-column chunks of its intermediate dimension
+        // pair-indexed buffers, no permutation: partial logits, routing, and
+        // the experts' partial outputs (one plane per 64-row intermediate chunk)
         L.decode = true;
         L.zpart = take(moe::DEC_LOGIT_PLANES * T * E * 4);
         L.ids = take(P * 4);
         L.w = take(P * 4);
         L.gap = take(T * 4);
         L.pscale = take(P * 4);
-        L.hbuf = take(P * (size_t)s->I * 4);
-        L.ypair = take((size_t)(s->I / 512) * P * (size_t)s->H * 4);
-        if (s->shared_bits) {
-            L.shh = take(T * (size_t)s->I_shared * 4);
-            L.shy = take((size_t)(s->I_shared / 512) * T * (size_t)s->H * 4);
-        }
+        L.ypair = take((size_t)(s->I / 64) * P * (size_t)s->H * 4);
+        if (s->shared_bits) L.shy = take((size_t)(s->I_shared / 64) * T * (size_t)s->H * 4);
     } else {
         L.zpart = take((size_t)KS * T * E * 4);
         L.sbc = take(nsb * E * 4);
@@ -372,12 +368,10 @@ int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const m
             d.sgs = w->sh_gate.qs;
             d.sus = w->sh_up.qs;
             d.sds = w->sh_down.qs;
-            d.shh = at<float>(ws, L.shh);
             d.shp = at<float>(ws, L.shy);
         }
         d.Ish = s->I_shared;
         d.sh_bits = s->shared_bits;
-        d.h = at<float>(ws, L.hbuf);
         d.y = at<float>(ws, L.ypair);
         d.res = (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr;
         d.out = out;

@@ -44,11 +44,11 @@ struct DecLaunch {
     const uint8_t *sgq, *suq, *sdq;
     const float *sgs, *sus, *sds;
     int Ish, sh_bits;
-    float *h, *shh, *y, *shp;
+    float *y, *shp;  // partial outputs: [I/64][T*k][H] routed, [I_shared/64][T][H] shared
     const uint16_t *res;
     void *out;
     int out_f32;
-    hipEvent_t ev0, ev1;  // nullable: recorded around the gate/up kernel
+    hipEvent_t ev0, ev1;  // nullable: recorded around the expert kernel
 };
 constexpr int DEC_LOGIT_PLANES = 4;  // partial-logit planes of the small-batch router
 bool decode_supported(int T, int H, int E, int k, int I, int Ish, int sh_bits);
