@@ -10,10 +10,14 @@ more than the 256 MB last-level cache, so each step streams them from HBM).
 One step = one HIP-graph replay of the 23 moe_layer_forward calls.
 
 Prints one JSON line: tokens/s for the step, plus
-  roofline:     the routed gate/up grouped-GEMM kernel (the largest weight
-                stream of the step) against HBM peak, its duration measured with
-                HIP events around each launch on its own stream;
+  roofline:     the fused expert kernel (the step's weight stream: every chosen
+                routed expert and the shared expert) against HBM peak; its
+                average duration comes from HIP events on its stream around
+                back-to-back replays of the 23 layers' expert stages;
   cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+
+--copy-calibration MIB runs only a plain device-to-device copy of that size
+(the reference kernel for scaling hardware byte counters) and exits.
 """
 import argparse
 import json
@@ -27,6 +31,26 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 
 
+def sh_of(moe, cfg, T, flags):
+    return moe.shape_of(cfg, T, flags)
+
+
+def measured_traffic(root):
+    """HBM bytes per expert-kernel launch from the committed rocprofv3 counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(root, "profiles", "k_dec_expert_c1_traffic.json")
+    src = os.path.join(root, "int4_routed_expert_02_amd", "csrc", "decode.hip")
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_hip_sha256") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -35,7 +59,9 @@ def parse():
     ap.add_argument("--config", default="c1", help="workload key (c1 = the decode step this line reports)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
-    ap.add_argument("--roofline-reps", type=int, default=10)
+    ap.add_argument("--roofline-reps", type=int, default=20)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB, 5 times (counter calibration), and exit")
     return ap.parse_args()
 
 
@@ -47,6 +73,16 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel(), "launches": 5}), flush=True)
+        return
 
     import int4_routed_expert_02_amd as moe
     import synth
@@ -105,50 +141,59 @@ def main():
     ms_per_step = ms_total / args.steps
     tok_s = T / (ms_per_step / 1e3)
 
-    # ---- roofline of the dominant kernel: the expert gate/up weight stream
-    # (routed experts the batch selected + the shared expert, one launch per
-    # layer).  HIP events are recorded right before and after that kernel on
-    # its own stream inside real layer passes (moe_layer_forward_profiled);
-    # each pass is queued behind a short GPU-side delay so that host enqueue
-    # time never lands between the events.
+    # ---- roofline of the dominant kernel: the fused expert kernel (routing
+    # decision, gate/up + SwiGLU + down of every chosen routed expert and of the
+    # shared expert, one launch per layer).  Its duration is measured with HIP
+    # events on the kernel's own stream around a HIP graph of the 23 layers'
+    # expert stages alone (MOE_STAGE_EXPERTS_ONLY: the same launches as in the
+    # step above, reading the router logits the step left in each workspace),
+    # replayed back to back: average = elapsed / launches.
     P = T * cfg.k
-    sh_f = moe.shape_of(cfg, T, flags)
-    pairs = []
+    eflags = flags | moe.MOE_STAGE_EXPERTS_ONLY
     with torch.cuda.stream(stream):
-        for rep in range(args.roofline_reps):
-            evl = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-            for a, b in evl:  # materialise the events before handing their handles to the library
-                a.record(stream)
-                b.record(stream)
-            stream.synchronize()
-            if hasattr(torch.cuda, "_sleep"):
-                torch.cuda._sleep(2_000_000)
-            for l in range(L):
-                moe.moe_layer_forward_profiled(sh_f, layers[l].weights, xs[l], xs[l + 1], wss[l], evl[l][0],
-                                               evl[l][1], stream=stream)
-            pairs.append(evl)
+        step(stream)  # leave each layer's logits in its workspace
+        for l in range(L):
+            layers[l].forward(xs[l], xs[l + 1], wss[l], eflags, stream=stream)
     torch.cuda.synchronize()
+    egraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(egraph, stream=stream):
+        for l in range(L):
+            layers[l].forward(xs[l], xs[l + 1], wss[l], eflags, stream=stream)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        egraph.replay()
+    torch.cuda.synchronize()
+    ea = torch.cuda.Event(enable_timing=True)
+    eb = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ea.record(stream)
+        for _ in range(args.roofline_reps):
+            egraph.replay()
+        eb.record(stream)
+    torch.cuda.synchronize()
+    avg_ms = ea.elapsed_time(eb) / (args.roofline_reps * L)
+
     n_act = []
     for l in range(L):
-        pid, _, _, _ = moe.moe_layer_routing(sh_f, wss[l])
+        pid, _, _, _ = moe.moe_layer_routing(sh_of(moe, cfg, T, flags), wss[l])
         base = wss[l].data_ptr()
         ids = wss[l][pid - base:pid - base + 4 * P].view(torch.int32).cpu().numpy()
         n_act.append(int(np.unique(ids).size))
-    sh_bytes = (cfg.I_sh * H * cfg.shared_bits // 8 + 8 * cfg.I_sh) if cfg.shared_bits else 0
-    gu_bytes = [na * (cfg.I * H + 8 * cfg.I) + sh_bytes + 2 * T * H + 4 * P * cfg.I + 4 * T * cfg.I_sh + 4 * P
-                for na in n_act]
-    k_ms, k_b = [], []
-    for evl in pairs:
-        for l, (a, b) in enumerate(evl):
-            k_ms.append(a.elapsed_time(b))
-            k_b.append(gu_bytes[l])
-    avg_ms = float(np.mean(k_ms))
-    achieved = float(np.sum(k_b)) / (float(np.sum(k_ms)) / 1e3) / 1e9  # GB/s
+    # algorithmic bytes of one expert-kernel launch: the weights (int4 rows and
+    # f32 row scales) of every chosen routed expert and of the shared expert,
+    # the activations and routing logits read once, one f32 output row per
+    # (token, expert) pair and per token for the shared expert
+    sh_w = (3 * cfg.I_sh * H * cfg.shared_bits // 8 + 4 * (2 * cfg.I_sh + H)) if cfg.shared_bits else 0
+    ex_bytes = [na * (3 * cfg.I * H // 2 + 4 * (2 * cfg.I + H)) + sh_w + 2 * T * H + 4 * T * cfg.E
+                + 4 * P * H + (4 * T * H if cfg.shared_bits else 0) for na in n_act]
+    alg_per_launch = float(np.mean(ex_bytes))
+    achieved = alg_per_launch / (avg_ms / 1e3) / 1e9  # GB/s
+    traffic = measured_traffic(ROOT)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_dec_gateup<4> (expert gate/up + SwiGLU weight stream)",
-                "avg_launch_us": round(avg_ms * 1e3, 2), "alg_bytes_per_launch": int(np.mean(gu_bytes)),
-                "launches_timed": len(k_ms)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "k_dec_expert<4,1> (routing + fused gate/up/SwiGLU/down of the chosen and shared experts)",
+                "avg_launch_us": round(avg_ms * 1e3, 2), "alg_bytes_per_launch": int(alg_per_launch),
+                "launches_timed": args.roofline_reps * L, "active_experts_mean": round(float(np.mean(n_act)), 2)}
 
     # step-level HBM fraction: algorithmic bytes of the whole step / step time
     step_bytes = 0

@@ -75,6 +75,10 @@ extern "C" {
                                int8 dense stack); otherwise packed int4 */
 #define MOE_STAGE_GATEUP_ONLY 0x200u /* moe_expert_ffn, profiling: run only the gate/up + SwiGLU kernel
                                (h stays in the workspace; y_pairs is not written) */
+#define MOE_STAGE_EXPERTS_ONLY 0x400u /* moe_layer_forward(_profiled), profiling, small-batch regime only
+                               (else MOE_ERR_UNSUPPORTED): run only the expert kernel, from the router
+                               logits a previous full call with the same shape, weights, input and ws
+                               left in ws; out is not written */
 #define MOE_TEST_GATEUP_SUMS 0x100u /* moe_expert_ffn, testing only: write the raw integer-weight sums
                                sum_h x*q of gate into y_pairs[r][0:I] and of up into y_pairs[r][I:2I]
                                (no scale, no activation, no down projection); needs 2*I <= H, int4 */

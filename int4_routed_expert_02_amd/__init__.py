@@ -31,6 +31,7 @@ MOE_ADD_RESIDUAL = 2
 MOE_EXPERT_INT8 = 4
 MOE_TEST_GATEUP_SUMS = 0x100
 MOE_STAGE_GATEUP_ONLY = 0x200
+MOE_STAGE_EXPERTS_ONLY = 0x400
 
 MOE_WS_PERMUTE = 1
 MOE_WS_EXPERT_FFN = 2

@@ -903,12 +903,13 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     a.yp = d.y;
     a.ysp = d.shp;
 
-    {
+    hipError_t e;
+    if (!d.experts_only) {
         const int grid = ((d.E + 15) / 16) * ((d.T + 15) / 16) * LG_NP;
         hipLaunchKernelGGL(k_dec_logits, dim3(grid), dim3(256), 0, st, d.x, d.rw, d.T, d.H, d.E, d.z);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
 
     // expert units; the grid is padded to whole groups of 32 workgroups (the
     // XCD-aware placement permutes within such groups)
@@ -928,7 +929,7 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
         hipLaunchKernelGGL((k_dec_expert<4, 4>), dim3(grid), dim3(256), 0, st, a, nunits);
     e = hipGetLastError();
     if (e == hipSuccess && d.ev1) e = hipEventRecord(d.ev1, st);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || d.experts_only) return e;
     const long nthreads = (long)d.T * (d.H / 4) * CB_SPLIT;
     hipLaunchKernelGGL(k_dec_combine, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, d.y,
                        d.I / DX_ROWS, d.shp, d.sh_bits ? d.Ish / DX_ROWS : 0, d.res, d.out, d.T, d.H, d.k,

@@ -332,6 +332,7 @@ int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const m
         return MOE_ERR_UNSUPPORTED;
     const Layout L = layout(s, MOE_WS_LAYER);
     hipStream_t hs = (hipStream_t)stream;
+    if ((s->flags & MOE_STAGE_EXPERTS_ONLY) && !L.decode) return MOE_ERR_UNSUPPORTED;
     if (L.decode) {
         moe::DecLaunch d;
         memset(&d, 0, sizeof(d));
@@ -378,6 +379,7 @@ int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const m
         d.out_f32 = (s->flags & MOE_OUT_F32) ? 1 : 0;
         d.ev0 = (hipEvent_t)ev_start;
         d.ev1 = (hipEvent_t)ev_stop;
+        d.experts_only = (s->flags & MOE_STAGE_EXPERTS_ONLY) ? 1 : 0;
         return hip_status(moe::launch_decode(d, hs));
     }
     const int P = s->T * s->top_k;

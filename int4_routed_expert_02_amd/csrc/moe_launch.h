@@ -49,6 +49,7 @@ struct DecLaunch {
     void *out;
     int out_f32;
     hipEvent_t ev0, ev1;  // nullable: recorded around the expert kernel
+    int experts_only;     // launch only the expert kernel (router logits already in z)
 };
 constexpr int DEC_LOGIT_PLANES = 4;  // partial-logit planes of the small-batch router
 bool decode_supported(int T, int H, int E, int k, int I, int Ish, int sh_bits);

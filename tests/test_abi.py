@@ -114,6 +114,11 @@ def test_errors_before_any_enqueue(moe):
     w3.up = moe.MoeQMat(FAKE, FAKE, 16, 0)
     assert lib.moe_layer_forward(ctypes.byref(s), ctypes.byref(w3), vp(FAKE), vp(FAKE), vp(FAKE), need,
                                  None) == moe.MOE_ERR_UNSUPPORTED
+    # the experts-only profiling stage exists only in the small-batch regime (T <= 32, H % 1024 == 0)
+    big = good(moe, T=64, flags=moe.MOE_STAGE_EXPERTS_ONLY)
+    need_big = moe.moe_workspace_bytes(big, moe.MOE_WS_LAYER)
+    assert lib.moe_layer_forward(ctypes.byref(big), ctypes.byref(w), vp(FAKE), vp(FAKE), vp(FAKE), need_big,
+                                 None) == moe.MOE_ERR_UNSUPPORTED
     # T == 0 is a no-op
     assert lib.moe_layer_forward(ctypes.byref(good(moe, T=0)), ctypes.byref(w), None, None, None, 0, None) == 0
     assert lib.moe_router(ctypes.byref(good(moe, T=0)), None, None, None, None, None, None, None, 0, None) == 0
