@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 
 
 def sh_of(moe, cfg, T, flags):
@@ -94,6 +95,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = synth.CONFIGS[args.config]
+    if cfg.T > 32:
+        return bench_prefill(args, cfg, moe, synth, torch, np, dev)
     L, T, H = cfg.layers, cfg.T, cfg.H
     flags = moe.MOE_ADD_RESIDUAL  # bf16 out, residual added: the layer output is the next layer's input
 
@@ -240,6 +243,102 @@ def main():
         "step_hbm_GBs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_alg_bytes": int(step_bytes),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_prefill(args, cfg, moe, synth, torch, np, dev):
+    """One large-batch layer (the tiled grouped-GEMM regime): tokens/s of one
+    moe_layer_forward (bf16 out), and the routed gate/up grouped GEMM against
+    the bf16 matrix-core peak."""
+    T, H, P = cfg.T, cfg.H, cfg.T * cfg.k
+    d = synth.layer(cfg)
+    layer = moe.MoeLayer(cfg, d, dev)
+    x = torch.from_numpy(d["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    flags = 0
+    ws = layer.workspace(T, flags)
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        layer.forward(x, out, ws, flags, stream=stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        layer.forward(x, out, ws, flags, stream=stream)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # the routed gate/up grouped GEMM (+ SwiGLU), bracketed by HIP events inside
+    # real layer passes on the kernel's stream, each pass queued behind a
+    # GPU-side delay so host enqueue time never lands between the events
+    sh = moe.shape_of(cfg, T, flags)
+    kms = []
+    with torch.cuda.stream(stream):
+        for _ in range(args.roofline_reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            b.record(stream)
+            stream.synchronize()
+            torch.cuda._sleep(2_000_000)
+            moe.moe_layer_forward_profiled(sh, layer.weights, x, out, ws, a, b, stream=stream)
+            stream.synchronize()
+            kms.append(a.elapsed_time(b))
+    avg_ms = float(np.mean(kms))
+    gu_flops = 4.0 * P * cfg.I * H
+    achieved = gu_flops / (avg_ms / 1e3) / 1e12
+    layer_flops = 6.0 * P * H * cfg.I + (6.0 * T * H * cfg.I_sh if cfg.shared_bits else 0.0)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "k_ffn gate/up (routed grouped GEMM + SwiGLU, int4 weights on bf16 MFMA)",
+                "avg_launch_us": round(avg_ms * 1e3, 2), "alg_flops_per_launch": gu_flops,
+                "launches_timed": len(kms)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        lw = oracle.LayerWeights(cfg, d)
+        n, spent, done = 4, 0.0, 0
+        while spent < args.cpu_seconds and done < T:
+            take = min(n, T - done)
+            t0 = time.time()
+            oracle.layer_forward(cfg.with_(T=take), lw, d["hidden"][done:done + take])
+            spent += time.time() - t0
+            done += take
+            n *= 2
+        cpu = {"value": round(done / spent, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"the first {done} tokens of the batch as sub-batches (router, permutation, routed and "
+                         f"shared FFN, combine) in {spent:.1f} s, f64-accumulating C oracle"}
+    line = {
+        "metric": f"MoE-layer tokens/s (prefill layer, {cfg.name})",
+        "value": round(T / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 MFMA, int4 weights, f32 accumulate",
+        "data": "synthetic (seeded)",
+        "config": {"workload": cfg.name, "T": T, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
+                   "I_shared": cfg.I_sh, "shared_bits": cfg.shared_bits, "global_batch": T,
+                   "parallelism": "single GPU"},
+        "layer_TFLOPs": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1),
+        "layer_mfma_frac": round(layer_flops / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
