@@ -144,7 +144,8 @@ __device__ __noinline__ void dec_select_waves(const float *__restrict__ zp, cons
                                               float *w_l, bool pub, float *__restrict__ gap_g)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int t = wave; t < T; t += 4) {
+    const int nw = blockDim.x / WAVE;
+    for (int t = wave; t < T; t += nw) {
         float s[EPL], b[EPL];
         bool ok[EPL];
 #pragma unroll
@@ -324,9 +325,9 @@ __device__ __forceinline__ int active_expert(const int32_t *__restrict__ ids, in
                                              int *res)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int e = tid; e < 256; e += 256) flags[e] = 0;
+    for (int e = tid; e < 256; e += blockDim.x) flags[e] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += 256) {
+    for (int p = tid; p < P; p += blockDim.x) {
         const int e = ids[p];
         if ((unsigned)e < (unsigned)E) flags[e] = 1;  // every writer stores 1
     }
@@ -394,7 +395,7 @@ __device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k,
     }
     __syncthreads();
     if (pub)
-        for (int i = threadIdx.x; i < T * k; i += 256) {
+        for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
             r.ids[i] = ids_l[i];
             r.w[i] = w_l[i];
             r.pscale[i] = r.rsf * w_l[i];
@@ -403,27 +404,24 @@ __device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k,
 
 // ------------------------------------------------------------- expert kernel
 
-constexpr int DX_ROWS = 64;                  // intermediate rows per unit (16 per wave)
-constexpr int DX_LDH = DX_ROWS + 8;          // padded row of the on-chip h chunk (bf16)
-constexpr int DX_TILES = 16;                 // down output tiles of 16 columns per wave per round
-constexpr int DX_RCOLS = 4 * DX_TILES * 16;  // output columns per round (1024)
-constexpr int GU_CPL = 8;                    // 16-byte gate/up chunks per lane per row per super-stage
-constexpr int DX_LDY = DX_TILES * 16 + 4;    // padded row of a wave's staged down tile (floats)
+constexpr int DX_WAVES = 8;                         // waves per workgroup
+constexpr int DX_THREADS = DX_WAVES * WAVE;         // 512
+constexpr int DX_ROWS = DX_WAVES * 16;              // intermediate rows per unit (16 per wave)
+static_assert(DX_ROWS == DEC_CHUNK_ROWS, "the workspace holds one output plane per unit chunk");
+constexpr int DX_LDH = DX_ROWS + 8;                 // padded row of the on-chip h chunk (bf16)
+constexpr int DX_TILES = 8;                         // down output tiles of 16 columns per wave per round
+constexpr int DX_WCOLS = DX_TILES * 16;             // output columns per wave per round (128)
+constexpr int DX_RCOLS = DX_WAVES * DX_WCOLS;       // output columns per round (1024)
+constexpr int DX_LDY = DX_WCOLS + 4;                // padded row of a wave's staged down tile (floats)
+constexpr int GU_CPL = 8;                           // 16-byte gate/up chunks per lane per row per super-stage
 
-template <int CPL>
-__device__ __forceinline__ void load_rows(u32x4 (&dst)[CPL], const uint8_t *row)
-{
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) dst[c] = *(const u32x4 *)(row + c * 64);
-}
-
-// Down weights of one round: lane (n, g) holds, for each of its wave's 16
-// output tiles tt, the 16 values of intermediate [16g, 16g + 16) of the chunk
-// in output row 16 tt + n of the wave's 256: 8 bytes int4 (u32x2), 16 bytes
-// int8 (u32x4).
+// Down weights of one round: lane (n, g) holds, for each of its wave's 8
+// output tiles tt, the 32 values of intermediate [32g, 32g + 32) of the
+// unit's chunk in output row 16 tt + n of the wave's 128: 16 bytes int4,
+// 32 bytes int8.  Word s (int4) or words 2s, 2s + 1 (int8) feed k-step s.
 template <int WBITS>
 struct DownW {
-    uint32_t d[DX_TILES][WBITS / 2];
+    uint32_t d[DX_TILES][WBITS];
 };
 
 // Buffer resource over `bytes` bytes at `base` (raw, byte-addressed; loads
@@ -439,33 +437,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uin
     return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-// The 16 rows of a lane are 16 * rstride bytes apart: one per-lane offset
-// plus a uniform per-tile offset, so the 16 loads share one address register.
+// A lane's 8 rows are 16 * rstride bytes apart: one per-lane offset plus a
+// uniform per-tile offset, so the loads share one address register.  Also
+// the row scales of the wave's 128 columns, 4 per lane (lanes 32..63 repeat
+// lanes 0..31: the write-out covers a row with 32 lanes).
 template <int WBITS>
 __device__ __forceinline__ void load_down(DownW<WBITS> &w, f32x4 &sd, const uint8_t *dq, const float *dsc,
                                           int64_t rstride, int H, int col0, int i0)
 {
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-    sd = *(const f32x4 *)(dsc + col0 + 4 * lane);  // the wave's 256 row scales, 4 per lane
+    sd = *(const f32x4 *)(dsc + col0 + 4 * (lane & 31));
     const __amdgpu_buffer_rsrc_t rs = raw_rsrc(dq, (uint32_t)(H * rstride));
-    const int voff = (int)((col0 + n) * rstride + (i0 + 16 * g) * WBITS / 8);
+    const int voff = (int)((col0 + n) * rstride + (i0 + 32 * g) * WBITS / 8);
 #pragma unroll
     for (int tt = 0; tt < DX_TILES; ++tt) {
         const int soff = (int)(tt * 16 * rstride);
-        if constexpr (WBITS == 4) {
-            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
-            w.d[tt][0] = v[0];
-            w.d[tt][1] = v[1];
-        } else {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) w.d[tt][q] = v[q];
+        for (int h = 0; h < WBITS / 4; ++h) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * h, soff, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w.d[tt][4 * h + q] = v[q];
         }
     }
 }
 
-// Position of intermediate j (0..63) in a row of the on-chip h chunk: with
-// int4 weights each 8-group is stored in the unpack's k-slot order
+// Position of intermediate j in a row of the on-chip h chunk: with int4
+// weights each 8-group is stored in the unpack's k-slot order
 // (j0, j4, j1, j5, j2, j6, j3, j7).
 template <int WBITS>
 __device__ __forceinline__ int h_pos(int j)
@@ -475,7 +472,7 @@ __device__ __forceinline__ int h_pos(int j)
 
 // LDS of the expert kernel.  The routing lists are dead once the unit's pairs
 // are gathered and the staged activations once the gate/up MFMAs are done, so
-// routing lists, activations and down scales share one area.
+// routing lists, activations and the staged down tiles share one area.
 template <int WBITS>
 struct alignas(16) DxSmem {
     static constexpr int KS = 512 * 8 / WBITS;  // columns per gate/up super-stage
@@ -486,20 +483,20 @@ struct alignas(16) DxSmem {
             int32_t ids[DEC_MAXT * DEC_MAXK];
             int flags[256];
         } r;
-        float y[4][16 * DX_LDY];  // each wave's 16 x 256 down tile, raw (after the gate/up MFMAs)
+        float y[DX_WAVES][16 * DX_LDY];  // each wave's 16 x 128 down tile, raw (after the gate/up MFMAs)
     } u;
     float w[DEC_MAXT * DEC_MAXK];            // routing weights of the batch
     uint16_t hh[DEC_MAXT * DX_LDH];          // h chunk, bf16 high part
     uint16_t hl[DEC_MAXT * DX_LDH];          // h chunk, bf16 low part (h - high)
     float xsum[DEC_MAXT];                    // activation row sums
-    float hs[4][DEC_MAXT];                   // per-wave h row sums
+    float hs[DX_WAVES][DEC_MAXT];            // per-wave h row sums
     float psc[DEC_MAXT];                     // output scale of each row (rsf * w, or 1)
     f32x4 rowinfo[DEC_MAXT];                 // per row: 136 * h row sum, output scale, output row
     int plist[DEC_MAXT], tok[DEC_MAXT];
     int pcnt, ares;
 };
 
-// One unit: gate/up of 64 intermediate rows for the n rows of its batch
+// One unit: gate/up of 128 intermediate rows for the n rows of its batch
 // (SwiGLU -> h chunk, on chip as an exact bf16 high + low pair), then
 // y_part = h_chunk . D[:, chunk]^T for every output column, scaled by the
 // down row scale and the row's output scale, stored to plane `chunk` of out.
@@ -517,9 +514,10 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
     constexpr int KS = DxSmem<WBITS>::KS;  // columns per super-stage (1024 int4, 512 int8)
     constexpr int LDA = DxSmem<WBITS>::LDA;
     constexpr int CPR = KS / 8;            // 8-column activation chunks per row
-    constexpr int XPT = CPR / 16;          // chunks per thread: a 16-thread group owns one row
+    constexpr int TPR = DX_THREADS / (NMB * 16);  // threads staging one row (32 or 16)
+    constexpr int XPT = CPR / TPR;         // chunks per thread
     constexpr int NCH = NMB == 1 ? 2 : 1;  // independent accumulator chains per matrix (register budget)
-    static_assert(CPR == 128 || CPR == 64, "a row is 128 or 64 chunks");
+    static_assert(CPR % TPR == 0, "whole chunks per thread");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, ln = lane & 15;
     f32x4 acc[NMB][2][NCH];
 #pragma unroll
@@ -528,63 +526,48 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
         for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int ch = 0; ch < NCH; ++ch) acc[mb][x][ch] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rsum[NMB];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) rsum[mb] = 0.f;
+    float rsum = 0.f;
     const int nss = a.H / KS;
     const uint16_t *ap = sm.u.a + ln * LDA;
-    const int rsub = tid >> 4, csub = tid & 15;  // row within a 16-row block, chunk phase
-    const uint16_t *xrow[NMB];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-        const int r = mb * 16 + rsub;
-        xrow[mb] = (r < n) ? a.x + (size_t)sm.tok[r] * a.H + csub * 8 : nullptr;
-    }
-    auto load_x = [&](u32x4 (&xr)[XPT], int mb, int ss) {
-        if (xrow[mb]) {
-#pragma unroll
-            for (int j = 0; j < XPT; ++j) xr[j] = *(const u32x4 *)(xrow[mb] + (size_t)ss * KS + j * 128);
-        } else {
-#pragma unroll
-            for (int j = 0; j < XPT; ++j) xr[j] = u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto stage_x = [&](u32x4 (&xr)[XPT], int mb) {
-        uint16_t *dstrow = sm.u.a + (mb * 16 + rsub) * LDA + csub * 8;
-#pragma unroll
-        for (int j = 0; j < XPT; ++j) {
-            u32x4 v = xr[j];
-            float s = 0.f;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) s += bf16_lo(v[d]) + bf16_hi(v[d]);
-            rsum[mb] += s;
-            if (WBITS == 4) v = interleave_bf16x8(v);
-            *(u32x4 *)(dstrow + j * 128) = v;
-        }
-    };
+    const int srow = tid / TPR, csub = tid % TPR;  // staged row, chunk phase
+    const uint16_t *xrow = (srow < n) ? a.x + (size_t)sm.tok[srow] * a.H + csub * 8 : nullptr;
     DownW<WBITS> dw;
     f32x4 sdv;
     u32x4 wg[CPL], wu[CPL];
     for (int ss = 0; ss < nss; ++ss) {
-        u32x4 xr[NMB][XPT];
+        u32x4 xr[XPT];
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) load_x(xr[mb], mb, ss);
-        load_rows<CPL>(wg, grow + (size_t)ss * SB);
-        load_rows<CPL>(wu, urow + (size_t)ss * SB);
+        for (int j = 0; j < XPT; ++j)
+            xr[j] = xrow ? *(const u32x4 *)(xrow + (size_t)ss * KS + j * (8 * TPR)) : u32x4{0u, 0u, 0u, 0u};
+        // gate and up chunk c in adjacent requests: the MFMAs on chunk c can
+        // start once its pair has arrived
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            wg[c] = *(const u32x4 *)(grow + (size_t)ss * SB + c * 64);
+            wu[c] = *(const u32x4 *)(urow + (size_t)ss * SB + c * 64);
+        }
         // the first round of down weights: in flight during the gate/up MFMAs
-        if (ss == nss - 1) load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, wave * (DX_TILES * 16), i0);
+        if (ss == nss - 1) load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, wave * DX_WCOLS, i0);
         if (ss > 0) __syncthreads();  // the previous super-stage's A reads are done
+        {
+            uint16_t *dstrow = sm.u.a + srow * LDA + csub * 8;
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) stage_x(xr[mb], mb);
-        if (ss == nss - 1) {
-            // row sums: the 16 threads of a row are 16 consecutive lanes
+            for (int j = 0; j < XPT; ++j) {
+                u32x4 v = xr[j];
+                float s = 0.f;
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                float s = rsum[mb];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, WAVE);
-                if (csub == 0) sm.xsum[mb * 16 + rsub] = s;
+                for (int d = 0; d < 4; ++d) s += bf16_lo(v[d]) + bf16_hi(v[d]);
+                rsum += s;
+                if (WBITS == 4) v = interleave_bf16x8(v);
+                *(u32x4 *)(dstrow + j * (8 * TPR)) = v;
             }
+        }
+        if (ss == nss - 1) {
+            // row sums: the TPR threads of a row are consecutive lanes
+            float s = rsum;
+#pragma unroll
+            for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o, WAVE);
+            if (csub == 0) sm.xsum[srow] = s;
         }
         __syncthreads();
 #pragma unroll
@@ -647,73 +630,72 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
     __syncthreads();
     if (tid < NMB * 16) {
         const int m = tid;
-        const float cor = bias * (((sm.hs[0][m] + sm.hs[1][m]) + sm.hs[2][m]) + sm.hs[3][m]);
+        float hsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < DX_WAVES; ++w) hsum += sm.hs[w][m];
         const int orow = m < n ? sm.plist[m] : 0;
-        sm.rowinfo[m] = f32x4{cor, sm.psc[m], __int_as_float(orow), 0.f};
+        sm.rowinfo[m] = f32x4{bias * hsum, sm.psc[m], __int_as_float(orow), 0.f};
     }
     __syncthreads();
-    // down: A = h chunk (rows m, 64 k in two 32-steps, high and low planes),
+    // down: A = h chunk (rows m, 128 k in four 32-steps, high and low planes),
     // one 16-row block at a time (the weights are unpacked again per block).
-    // Each wave stages its raw 16 x 256 result in LDS and writes it out row
-    // by row as 16-byte stores, applying (d - 136 rowsum) * row scale * output
-    // scale on the way.
+    // Each wave stages its raw 16 x 128 result in LDS and writes it out two
+    // rows at a time as 16-byte stores, applying
+    // (d - 136 rowsum) * row scale * output scale on the way.
     const int chunk = i0 / DX_ROWS;
     float *yl = sm.u.y[wave];
     for (int c0 = 0; c0 < a.H; c0 += DX_RCOLS) {
-        const int col0 = c0 + wave * (DX_TILES * 16);
+        const int col0 = c0 + wave * DX_WCOLS;
         if (c0 > 0) load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, col0, i0);
 #pragma unroll 1
         for (int mb = 0; mb < NMB; ++mb) {
             if (mb * 16 >= n) break;
-            u32x4 fh[2], fl[2];
+            u32x4 fh[4], fl[4];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                fh[s] = *(const u32x4 *)(sm.hh + (mb * 16 + ln) * DX_LDH + 16 * g + 8 * s);
-                fl[s] = *(const u32x4 *)(sm.hl + (mb * 16 + ln) * DX_LDH + 16 * g + 8 * s);
+            for (int s = 0; s < 4; ++s) {
+                fh[s] = *(const u32x4 *)(sm.hh + (mb * 16 + ln) * DX_LDH + 32 * g + 8 * s);
+                fl[s] = *(const u32x4 *)(sm.hl + (mb * 16 + ln) * DX_LDH + 32 * g + 8 * s);
             }
 #pragma unroll
             for (int tt = 0; tt < DX_TILES; ++tt) {
-                u32x4 b0, b1;
-                if constexpr (WBITS == 4) {
-                    b0 = unpack_int4x8(dw.d[tt][0]);
-                    b1 = unpack_int4x8(dw.d[tt][1]);
-                } else {
-                    b0 = unpack_int8x8(u32x2{dw.d[tt][0], dw.d[tt][1]});
-                    b1 = unpack_int8x8(u32x2{dw.d[tt][2], dw.d[tt][3]});
-                }
                 f32x4 d = {0.f, 0.f, 0.f, 0.f};
-                d = mfma_bf16(fh[0], b0, d);
-                d = mfma_bf16(fl[0], b0, d);
-                d = mfma_bf16(fh[1], b1, d);
-                d = mfma_bf16(fl[1], b1, d);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const u32x4 b = WBITS == 4 ? unpack_int4x8(dw.d[tt][s])
+                                               : unpack_int8x8(u32x2{dw.d[tt][2 * s], dw.d[tt][2 * s + 1]});
+                    d = mfma_bf16(fh[s], b, d);
+                    d = mfma_bf16(fl[s], b, d);
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) yl[(4 * g + r) * DX_LDY + tt * 16 + ln] = d[r];
             }
-            // read back row-wise (own wave's data: LDS order within the wave suffices)
+            // read back two rows at a time (own wave's data: LDS order within the wave suffices)
             const int nr = n - mb * 16;
+            const int half = lane >> 5, q4 = 4 * (lane & 31);
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                if (rr < nr) {
-                    const f32x4 ri = sm.rowinfo[mb * 16 + rr];
-                    const f32x4 v = *(const f32x4 *)(yl + rr * DX_LDY + 4 * lane);
+            for (int rr = 0; rr < 16; rr += 2) {
+                const int row = rr + half;
+                if (row < nr) {
+                    const f32x4 ri = sm.rowinfo[mb * 16 + row];
+                    const f32x4 v = *(const f32x4 *)(yl + row * DX_LDY + q4);
                     f32x4 o;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) o[q] = (v[q] - ri[0]) * sdv[q] * ri[1];
-                    *(f32x4 *)(out + ((size_t)chunk * nrows + __float_as_int(ri[2])) * a.H + col0 + 4 * lane) = o;
+                    *(f32x4 *)(out + ((size_t)chunk * nrows + __float_as_int(ri[2])) * a.H + col0 + q4) = o;
                 }
             }
         }
     }
 }
 
-// Units (logical index L): [0, nsh) shared-expert units (64 intermediate rows
-// x up to 16 tokens: the two token halves of a chunk are adjacent units),
-// then routed units (rank of the chosen expert in ascending id order, chunk).
-// Routed units first take the routing decision of the whole batch (every
-// one computes the same from the logits), then gather the pairs routed to
-// their expert; units beyond the chosen experts exit.  A unit's loads are
-// its activation rows, its gate/up rows and its down slice (all output rows,
-// the chunk's 64 columns), all in flight before the first MFMA.
+// Units (logical index L): [0, nsh) shared-expert units (128 intermediate
+// rows x up to 16 tokens: the two token halves of a chunk are adjacent
+// units), then routed units (rank of the chosen expert in ascending id
+// order, chunk).  Routed units first take the routing decision of the whole
+// batch (every one computes the same from the logits), then gather the pairs
+// routed to their expert; units beyond the chosen experts exit.  A unit's
+// loads are its activation rows, its gate/up rows and its down slice (all
+// output rows, the chunk's 128 columns), all in flight before the first MFMA.
 //
 // XCD-aware placement: workgroup b runs on XCD b % 8; logical units 4q ..
 // 4q + 3 (chunks whose down slices share 128-byte lines, or the token
@@ -728,7 +710,7 @@ __device__ __forceinline__ int dx_logical_unit(int b)
 __host__ __device__ __forceinline__ int dx_token_halves(int T) { return (T + 15) / 16; }
 
 template <int WBITS, int EPL>
-__global__ __launch_bounds__(256, WBITS == 4 ? 2 : 1) void k_dec_expert(DecArgs a, int nunits)
+__global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nunits)
 {
     __shared__ DxSmem<WBITS> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
@@ -920,13 +902,13 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
         e = hipEventRecord(d.ev0, st);
         if (e != hipSuccess) return e;
     }
-    if (d.sh_bits == 8) hipLaunchKernelGGL((k_dec_expert<8, 1>), dim3(grid), dim3(256), 0, st, a, nunits);
+    if (d.sh_bits == 8) hipLaunchKernelGGL((k_dec_expert<8, 1>), dim3(grid), dim3(DX_THREADS), 0, st, a, nunits);
     if (d.E <= 64)
-        hipLaunchKernelGGL((k_dec_expert<4, 1>), dim3(grid), dim3(256), 0, st, a, nunits);
+        hipLaunchKernelGGL((k_dec_expert<4, 1>), dim3(grid), dim3(DX_THREADS), 0, st, a, nunits);
     else if (d.E <= 128)
-        hipLaunchKernelGGL((k_dec_expert<4, 2>), dim3(grid), dim3(256), 0, st, a, nunits);
+        hipLaunchKernelGGL((k_dec_expert<4, 2>), dim3(grid), dim3(DX_THREADS), 0, st, a, nunits);
     else
-        hipLaunchKernelGGL((k_dec_expert<4, 4>), dim3(grid), dim3(256), 0, st, a, nunits);
+        hipLaunchKernelGGL((k_dec_expert<4, 4>), dim3(grid), dim3(DX_THREADS), 0, st, a, nunits);
     e = hipGetLastError();
     if (e == hipSuccess && d.ev1) e = hipEventRecord(d.ev1, st);
     if (e != hipSuccess || d.experts_only) return e;

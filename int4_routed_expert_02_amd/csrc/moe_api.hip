@@ -78,15 +78,15 @@ Layout layout(const moe_shape *s, int which)
         L.hbuf = take(P * (size_t)s->I * 4);
     } else if (use_decode(s)) {
         // pair-indexed buffers, no permutation: partial logits, routing, and
-        // the experts' partial outputs (one plane per 64-row intermediate chunk)
+        // the experts' partial outputs (one plane per 128-row intermediate chunk)
         L.decode = true;
         L.zpart = take(moe::DEC_LOGIT_PLANES * T * E * 4);
         L.ids = take(P * 4);
         L.w = take(P * 4);
         L.gap = take(T * 4);
         L.pscale = take(P * 4);
-        L.ypair = take((size_t)(s->I / 64) * P * (size_t)s->H * 4);
-        if (s->shared_bits) L.shy = take((size_t)(s->I_shared / 64) * T * (size_t)s->H * 4);
+        L.ypair = take((size_t)(s->I / moe::DEC_CHUNK_ROWS) * P * (size_t)s->H * 4);
+        if (s->shared_bits) L.shy = take((size_t)(s->I_shared / moe::DEC_CHUNK_ROWS) * T * (size_t)s->H * 4);
     } else {
         L.zpart = take((size_t)KS * T * E * 4);
         L.sbc = take(nsb * E * 4);

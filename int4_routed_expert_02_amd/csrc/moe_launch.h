@@ -52,6 +52,7 @@ struct DecLaunch {
     int experts_only;     // launch only the expert kernel (router logits already in z)
 };
 constexpr int DEC_LOGIT_PLANES = 4;  // partial-logit planes of the small-batch router
+constexpr int DEC_CHUNK_ROWS = 128;  // intermediate rows per small-batch expert unit (one output plane each)
 bool decode_supported(int T, int H, int E, int k, int I, int Ish, int sh_bits);
 hipError_t launch_decode(const DecLaunch &d, hipStream_t st);
 
