@@ -188,10 +188,10 @@ __device__ __forceinline__ void cand_sort2(Cand &a, Cand &b)
 // The selected k are the first k, taken in that order; the weight of
 // selection j is s_j over the sum of the selected s (summed in selection
 // order); the tie gap is v_{k-1} - v_k.  Same results as moe_select.h.
-template <int KL>
+template <int KL, typename Mid>
 __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, const float *__restrict__ bias, int T,
                                                  int E, int k, int32_t *ids_l, float *w_l, bool pub,
-                                                 float *__restrict__ gap_g)
+                                                 float *__restrict__ gap_g, Mid &&mid)
 {
     const int tid = threadIdx.x, t = tid >> 3, q = tid & 7;
     Cand c[KL];
@@ -209,6 +209,7 @@ __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, c
         b0 = *(const f32x4 *)(bias + 8 * q);
         b1 = *(const f32x4 *)(bias + 8 * q + 4);
     }
+    mid();  // the caller's own work while the logits are in flight
     if (live) {
         float z[8];
         const f32x4 a0 = pa[0][0], a1 = pa[0][1];
@@ -292,47 +293,21 @@ __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, c
 
 // ------------------------------------------------------------- pair lists
 
-// Pairs routed to expert e in ascending order -> list (and their tokens ->
-// tok); returns the count.
-// Called by the whole workgroup; the result is in LDS after the barrier.
-__device__ __forceinline__ int gather_pairs(const int32_t *__restrict__ ids, int P, int k, int e, int *list,
-                                            int *tok, int *cnt)
+// Wave 0 alone: the rank-th chosen expert of the batch (ascending id) and the
+// pairs routed to it in ascending order -> list (their tokens -> tok).  A
+// single wave needs no barrier between its own LDS steps (a wave's LDS
+// operations complete in order); one barrier publishes the result.  Returns
+// the expert (or -1 when fewer experts are chosen) and its pair count.
+__device__ __forceinline__ int2 dec_locate_unit(const int32_t *ids, int P, int k, int E, int rank, int *flags,
+                                                int *list, int *tok, int *res)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     if (tid < WAVE) {
-        int n = 0;
-        for (int p0 = 0; p0 < P; p0 += WAVE) {
-            const int p = p0 + lane;
-            const bool hit = p < P && ids[p] == e;
-            const uint64_t m = __ballot(hit);
-            if (hit) {
-                const int slot = n + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-                list[slot] = p;
-                tok[slot] = p / k;
-            }
-            n += __popcll(m);
+        for (int e = lane; e < E; e += WAVE) flags[e] = 0;
+        for (int p = lane; p < P; p += WAVE) {
+            const int e = ids[p];
+            if ((unsigned)e < (unsigned)E) flags[e] = 1;
         }
-        if (lane == 0) *cnt = n;
-    }
-    __syncthreads();
-    return *cnt;
-}
-
-// The rank-th active expert (ascending id) of this batch, or -1 when fewer
-// experts are active: units of inactive experts never get a workgroup slot
-// ahead of active work.  `flags` is E <= 256 ints of LDS.  Whole workgroup.
-__device__ __forceinline__ int active_expert(const int32_t *__restrict__ ids, int P, int E, int rank, int *flags,
-                                             int *res)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int e = tid; e < 256; e += blockDim.x) flags[e] = 0;
-    __syncthreads();
-    for (int p = tid; p < P; p += blockDim.x) {
-        const int e = ids[p];
-        if ((unsigned)e < (unsigned)E) flags[e] = 1;  // every writer stores 1
-    }
-    __syncthreads();
-    if (wave == 0) {
         int before = 0, found = -1;
         for (int e0 = 0; e0 < E; e0 += WAVE) {
             const bool on = (e0 + lane < E) && flags[e0 + lane];
@@ -341,15 +316,31 @@ __device__ __forceinline__ int active_expert(const int32_t *__restrict__ ids, in
             if (found < 0 && rank < before + cnt) {
                 const int want = rank - before;
                 const bool me = on && __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)))) == want;
-                const uint64_t hit = __ballot(me);
-                found = e0 + (int)__builtin_ctzll(hit);
+                found = e0 + (int)__builtin_ctzll(__ballot(me));
             }
             before += cnt;
         }
-        if (lane == 0) *res = found;
+        int n = 0;
+        if (found >= 0) {
+            for (int p0 = 0; p0 < P; p0 += WAVE) {
+                const int p = p0 + lane;
+                const bool hit = p < P && ids[p] == found;
+                const uint64_t m = __ballot(hit);
+                if (hit) {
+                    const int slot = n + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+                    list[slot] = p;
+                    tok[slot] = p / k;
+                }
+                n += __popcll(m);
+            }
+        }
+        if (lane == 0) {
+            res[0] = found;
+            res[1] = n;
+        }
     }
     __syncthreads();
-    return *res;
+    return int2{res[0], res[1]};
 }
 
 struct DecArgs {
@@ -378,19 +369,22 @@ struct DecArgs {
 
 // The routing decision of the batch into LDS (every routed workgroup takes
 // it, from the same logits, so all agree); the publishing workgroup also
-// writes ids, w, rsf * w and the tie gaps to global memory.
-template <int EPL>
-__device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k, int32_t *ids_l, float *w_l, bool pub)
+// writes ids, w, rsf * w and the tie gaps to global memory.  `mid` runs once,
+// while the logits are in flight.
+template <int EPL, typename Mid>
+__device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k, int32_t *ids_l, float *w_l, bool pub,
+                                          Mid &&mid)
 {
     const bool grouped = r.n_group > 1 && r.topk_group < r.n_group;
     if (!grouped && E <= 64 && E % 8 == 0 && k <= 3) {
         if (k == 1)
-            dec_select_lanes<2>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
+            dec_select_lanes<2>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, mid);
         else if (k == 2)
-            dec_select_lanes<3>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
+            dec_select_lanes<3>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, mid);
         else
-            dec_select_lanes<4>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
+            dec_select_lanes<4>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, mid);
     } else {
+        mid();
         dec_select_waves<EPL>(r.zp, r.rb, T, E, k, r.n_group, r.topk_group, r.rsf, ids_l, w_l, pub, r.gap);
     }
     __syncthreads();
@@ -470,54 +464,88 @@ __device__ __forceinline__ int h_pos(int j)
     return WBITS == 4 ? (j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1) : j;
 }
 
-// LDS of the expert kernel.  The routing lists are dead once the unit's pairs
-// are gathered and the staged activations once the gate/up MFMAs are done, so
-// routing lists, activations and the staged down tiles share one area.
+// LDS of the expert kernel.  The staged activations are dead once the gate/up
+// MFMAs are done, so they share storage with the staged down tiles.
 template <int WBITS>
 struct alignas(16) DxSmem {
     static constexpr int KS = 512 * 8 / WBITS;  // columns per gate/up super-stage
     static constexpr int LDA = KS + 8;
     union {
-        uint16_t a[DEC_MAXT * LDA];  // bf16 activations of the super-stage
-        struct {
-            int32_t ids[DEC_MAXT * DEC_MAXK];
-            int flags[256];
-        } r;
-        float y[DX_WAVES][16 * DX_LDY];  // each wave's 16 x 128 down tile, raw (after the gate/up MFMAs)
+        uint16_t a[DEC_MAXT * LDA];      // bf16 activation rows of the super-stage
+        float y[DX_WAVES][16 * DX_LDY];  // each wave's 16 x 128 down tile (after the gate/up MFMAs)
     } u;
-    float w[DEC_MAXT * DEC_MAXK];            // routing weights of the batch
+    int32_t ids[DEC_MAXT * DEC_MAXK];        // routing of the batch
+    float w[DEC_MAXT * DEC_MAXK];
+    int flags[256];
     uint16_t hh[DEC_MAXT * DX_LDH];          // h chunk, bf16 high part
     uint16_t hl[DEC_MAXT * DX_LDH];          // h chunk, bf16 low part (h - high)
-    float xsum[DEC_MAXT];                    // activation row sums
-    float hs[DX_WAVES][DEC_MAXT];            // per-wave h row sums
-    float psc[DEC_MAXT];                     // output scale of each row (rsf * w, or 1)
-    f32x4 rowinfo[DEC_MAXT];                 // per row: 136 * h row sum, output scale, output row
+    float xsum[DEC_MAXT];                    // activation row sums (by staged row)
+    float psc[DEC_MAXT];                     // output scale of each pair row (rsf * w, or 1)
+    int arow[DEC_MAXT];                      // staged activation row of each pair row
     int plist[DEC_MAXT], tok[DEC_MAXT];
-    int pcnt, ares;
+    int res[2];
 };
 
-// One unit: gate/up of 128 intermediate rows for the n rows of its batch
+// Activation staging: 16 threads per row, 32 rows; row r of the staging
+// area holds token rtok(r).  Loads and stores are separate steps so that
+// other requests can be issued in between; each thread keeps its row's
+// running sum (over its chunks and all super-stages) in rsum.
+template <int WBITS>
+struct XStage {
+    static constexpr int TPR = 16;
+    static constexpr int XPT = DxSmem<WBITS>::KS / 8 / TPR;
+    u32x4 v[XPT];
+};
+
+template <int WBITS, typename RowTok>
+__device__ __forceinline__ void xstage_load(XStage<WBITS> &xs, const DecArgs &a, int nr, int ss, RowTok rtok)
+{
+    constexpr int TPR = XStage<WBITS>::TPR, KS = DxSmem<WBITS>::KS;
+    const int srow = threadIdx.x / TPR, csub = threadIdx.x % TPR;
+    const uint16_t *src = srow < nr ? a.x + (size_t)rtok(srow) * a.H + (size_t)ss * KS + csub * 8 : nullptr;
+#pragma unroll
+    for (int j = 0; j < XStage<WBITS>::XPT; ++j)
+        xs.v[j] = src ? *(const u32x4 *)(src + j * 8 * TPR) : u32x4{0u, 0u, 0u, 0u};
+}
+
+template <int WBITS>
+__device__ __forceinline__ void xstage_store(const XStage<WBITS> &xs, DxSmem<WBITS> &sm, int nr, float &rsum)
+{
+    constexpr int TPR = XStage<WBITS>::TPR, LDA = DxSmem<WBITS>::LDA;
+    const int srow = threadIdx.x / TPR, csub = threadIdx.x % TPR;
+    if (srow >= nr) return;
+    uint16_t *dst = sm.u.a + srow * LDA + csub * 8;
+#pragma unroll
+    for (int j = 0; j < XStage<WBITS>::XPT; ++j) {
+        u32x4 v = xs.v[j];
+        float s = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) s += bf16_lo(v[d]) + bf16_hi(v[d]);
+        rsum += s;
+        if (WBITS == 4) v = interleave_bf16x8(v);
+        *(u32x4 *)(dst + j * 8 * TPR) = v;
+    }
+}
+
+// One unit: gate/up of 128 intermediate rows for the n pair rows of its batch
 // (SwiGLU -> h chunk, on chip as an exact bf16 high + low pair), then
 // y_part = h_chunk . D[:, chunk]^T for every output column, scaled by the
 // down row scale and the row's output scale, stored to plane `chunk` of out.
-// Loads are issued in the order they are needed (activations, gate/up rows,
-// down slice): vector loads complete in issue order, so waiting for the
-// activations never waits for the weights.
-template <int WBITS, int NMB>
-__device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm, int n,
-                                            const uint8_t *grow, const uint8_t *urow, float sg, float su,
-                                            const uint8_t *dq, const float *dsc, int64_t drstride, int i0,
-                                            float *out, int nrows)
+// The first super-stage's activations are already staged (rows 0..nr-1);
+// later super-stages are staged here.  Weight loads are issued gate/up first,
+// then the down slice, all before the first MFMA.
+template <int WBITS, int NMB, typename RowTok>
+__device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm, int n, int nr, RowTok rtok,
+                                            float rsum, const uint8_t *grow, const uint8_t *urow, float sg,
+                                            float su, const uint8_t *dq, const float *dsc, int64_t drstride,
+                                            int i0, float *out, int nrows)
 {
     constexpr int CPL = GU_CPL;
     constexpr int SB = CPL * 64;           // weight bytes of a row per super-stage (512)
     constexpr int KS = DxSmem<WBITS>::KS;  // columns per super-stage (1024 int4, 512 int8)
     constexpr int LDA = DxSmem<WBITS>::LDA;
-    constexpr int CPR = KS / 8;            // 8-column activation chunks per row
-    constexpr int TPR = DX_THREADS / (NMB * 16);  // threads staging one row (32 or 16)
-    constexpr int XPT = CPR / TPR;         // chunks per thread
     constexpr int NCH = NMB == 1 ? 2 : 1;  // independent accumulator chains per matrix (register budget)
-    static_assert(CPR % TPR == 0, "whole chunks per thread");
+    constexpr int TPR = XStage<WBITS>::TPR;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, ln = lane & 15;
     f32x4 acc[NMB][2][NCH];
 #pragma unroll
@@ -526,19 +554,16 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
         for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int ch = 0; ch < NCH; ++ch) acc[mb][x][ch] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rsum = 0.f;
     const int nss = a.H / KS;
-    const uint16_t *ap = sm.u.a + ln * LDA;
-    const int srow = tid / TPR, csub = tid % TPR;  // staged row, chunk phase
-    const uint16_t *xrow = (srow < n) ? a.x + (size_t)sm.tok[srow] * a.H + csub * 8 : nullptr;
+    const uint16_t *ap[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) ap[mb] = sm.u.a + sm.arow[mb * 16 + ln] * LDA;
     DownW<WBITS> dw;
     f32x4 sdv;
     u32x4 wg[CPL], wu[CPL];
     for (int ss = 0; ss < nss; ++ss) {
-        u32x4 xr[XPT];
-#pragma unroll
-        for (int j = 0; j < XPT; ++j)
-            xr[j] = xrow ? *(const u32x4 *)(xrow + (size_t)ss * KS + j * (8 * TPR)) : u32x4{0u, 0u, 0u, 0u};
+        XStage<WBITS> xs;
+        if (ss > 0) xstage_load<WBITS>(xs, a, nr, ss, rtok);
         // gate and up chunk c in adjacent requests: the MFMAs on chunk c can
         // start once its pair has arrived
 #pragma unroll
@@ -548,26 +573,16 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
         }
         // the first round of down weights: in flight during the gate/up MFMAs
         if (ss == nss - 1) load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, wave * DX_WCOLS, i0);
-        if (ss > 0) __syncthreads();  // the previous super-stage's A reads are done
-        {
-            uint16_t *dstrow = sm.u.a + srow * LDA + csub * 8;
-#pragma unroll
-            for (int j = 0; j < XPT; ++j) {
-                u32x4 v = xr[j];
-                float s = 0.f;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) s += bf16_lo(v[d]) + bf16_hi(v[d]);
-                rsum += s;
-                if (WBITS == 4) v = interleave_bf16x8(v);
-                *(u32x4 *)(dstrow + j * (8 * TPR)) = v;
-            }
+        if (ss > 0) {
+            __syncthreads();  // the previous super-stage's A reads are done
+            xstage_store<WBITS>(xs, sm, nr, rsum);
         }
         if (ss == nss - 1) {
-            // row sums: the TPR threads of a row are consecutive lanes
+            // row sums: the TPR threads of a staged row are consecutive lanes
             float s = rsum;
 #pragma unroll
             for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o, WAVE);
-            if (csub == 0) sm.xsum[srow] = s;
+            if (tid % TPR == 0 && tid / TPR < nr) sm.xsum[tid / TPR] = s;
         }
         __syncthreads();
 #pragma unroll
@@ -579,7 +594,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
                     const u32x4 bu = unpack_int4x8(wu[c][wd]);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
-                        const u32x4 af = *(const u32x4 *)(ap + mb * 16 * LDA + (4 * c + g) * 32 + 8 * wd);
+                        const u32x4 af = *(const u32x4 *)(ap[mb] + (4 * c + g) * 32 + 8 * wd);
                         acc[mb][0][wd % NCH] = mfma_bf16(af, bg, acc[mb][0][wd % NCH]);
                         acc[mb][1][wd % NCH] = mfma_bf16(af, bu, acc[mb][1][wd % NCH]);
                     }
@@ -591,7 +606,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
                     const u32x4 bu = unpack_int8x8(u32x2{wu[c][2 * wd], wu[c][2 * wd + 1]});
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
-                        const u32x4 af = *(const u32x4 *)(ap + mb * 16 * LDA + (4 * c + g) * 16 + 8 * wd);
+                        const u32x4 af = *(const u32x4 *)(ap[mb] + (4 * c + g) * 16 + 8 * wd);
                         acc[mb][0][wd % NCH] = mfma_bf16(af, bg, acc[mb][0][wd % NCH]);
                         acc[mb][1][wd % NCH] = mfma_bf16(af, bu, acc[mb][1][wd % NCH]);
                     }
@@ -600,8 +615,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
         }
     }
     // SwiGLU epilogue: h for (row m, intermediate wave * 16 + ln) -> on-chip
-    // chunk as bf16 high + low; per-wave row sums of (high + low) over the 16
-    // intermediates of the wave, added over lanes in a fixed tree order.
+    // chunk as bf16 high + low.
     const float bias = (WBITS == 4) ? INT4_BIAS : 0.f;
     const int hp = h_pos<WBITS>(wave * 16 + ln);
 #pragma unroll
@@ -609,7 +623,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = mb * 16 + g * 4 + r;
-            const float corr = bias * sm.xsum[m];
+            const float corr = bias * sm.xsum[sm.arow[m]];
             float ga = acc[mb][0][0][r], ua = acc[mb][1][0][r];
 #pragma unroll
             for (int ch = 1; ch < NCH; ++ch) {
@@ -618,30 +632,18 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
             }
             const float h = m < n ? fast_silu((ga - corr) * sg) * ((ua - corr) * su) : 0.f;
             const uint16_t hb = f32_to_bf16(h);
-            const uint16_t lb = f32_to_bf16(h - bf16_to_f32(hb));
             sm.hh[m * DX_LDH + hp] = hb;
-            sm.hl[m * DX_LDH + hp] = lb;
-            float s = bf16_to_f32(hb) + bf16_to_f32(lb);
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, WAVE);
-            if (ln == 0) sm.hs[wave][m] = s;
+            sm.hl[m * DX_LDH + hp] = f32_to_bf16(h - bf16_to_f32(hb));
         }
-    }
-    __syncthreads();
-    if (tid < NMB * 16) {
-        const int m = tid;
-        float hsum = 0.f;
-#pragma unroll
-        for (int w = 0; w < DX_WAVES; ++w) hsum += sm.hs[w][m];
-        const int orow = m < n ? sm.plist[m] : 0;
-        sm.rowinfo[m] = f32x4{bias * hsum, sm.psc[m], __int_as_float(orow), 0.f};
     }
     __syncthreads();
     // down: A = h chunk (rows m, 128 k in four 32-steps, high and low planes),
     // one 16-row block at a time (the weights are unpacked again per block).
-    // Each wave stages its raw 16 x 128 result in LDS and writes it out two
-    // rows at a time as 16-byte stores, applying
-    // (d - 136 rowsum) * row scale * output scale on the way.
+    // With int4 weights the B fragments hold q + 136: each tile starts from
+    // -136 * (row sum of high + low), itself an MFMA against a constant
+    // fragment, so the accumulation yields the sum over q.  Each wave stages
+    // its 16 x 128 result in LDS and writes it out two rows at a time as
+    // 16-byte stores scaled by the down row scale and the row's output scale.
     const int chunk = i0 / DX_ROWS;
     float *yl = sm.u.y[wave];
     for (int c0 = 0; c0 < a.H; c0 += DX_RCOLS) {
@@ -656,9 +658,20 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
                 fh[s] = *(const u32x4 *)(sm.hh + (mb * 16 + ln) * DX_LDH + 32 * g + 8 * s);
                 fl[s] = *(const u32x4 *)(sm.hl + (mb * 16 + ln) * DX_LDH + 32 * g + 8 * s);
             }
+            f32x4 d0 = {0.f, 0.f, 0.f, 0.f};
+            if (WBITS == 4) {
+                const u32x4 c136 = u32x4{0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};  // bf16 136
+                f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    cs = mfma_bf16(fh[s], c136, cs);
+                    cs = mfma_bf16(fl[s], c136, cs);
+                }
+                d0 = -cs;
+            }
 #pragma unroll
             for (int tt = 0; tt < DX_TILES; ++tt) {
-                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                f32x4 d = d0;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const u32x4 b = WBITS == 4 ? unpack_int4x8(dw.d[tt][s])
@@ -670,18 +683,19 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
                 for (int r = 0; r < 4; ++r) yl[(4 * g + r) * DX_LDY + tt * 16 + ln] = d[r];
             }
             // read back two rows at a time (own wave's data: LDS order within the wave suffices)
-            const int nr = n - mb * 16;
+            const int nrw = n - mb * 16;
             const int half = lane >> 5, q4 = 4 * (lane & 31);
 #pragma unroll
             for (int rr = 0; rr < 16; rr += 2) {
                 const int row = rr + half;
-                if (row < nr) {
-                    const f32x4 ri = sm.rowinfo[mb * 16 + row];
+                if (row < nrw) {
+                    const int m = mb * 16 + row;
+                    const float osc = sm.psc[m];
                     const f32x4 v = *(const f32x4 *)(yl + row * DX_LDY + q4);
                     f32x4 o;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) o[q] = (v[q] - ri[0]) * sdv[q] * ri[1];
-                    *(f32x4 *)(out + ((size_t)chunk * nrows + __float_as_int(ri[2])) * a.H + col0 + q4) = o;
+                    for (int q = 0; q < 4; ++q) o[q] = v[q] * sdv[q] * osc;
+                    *(f32x4 *)(out + ((size_t)chunk * nrows + sm.plist[m]) * a.H + col0 + q4) = o;
                 }
             }
         }
@@ -738,38 +752,57 @@ __global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nun
         dsc = dscc;
         drs = (int64_t)K * WBITS / 8;
     };
-    int n, nrows;
+    int n, nrows, nr;
     float *out;
+    float rsum = 0.f;
+    XStage<WBITS> xs;
     if (shared) {
+        // 16 tokens of one half: staged rows r = pair rows r = token 16 th + r
         const int th = L % nth;
-        locate(a.sgq, a.suq, a.sdq, a.sgs, a.sus, a.sds, a.Ish, (L / nth) * DX_ROWS);
         n = a.T - 16 * th < 16 ? a.T - 16 * th : 16;
+        nr = n;
+        auto rtok = [th](int r) { return 16 * th + r; };
+        xstage_load<WBITS>(xs, a, nr, 0, rtok);
+        locate(a.sgq, a.suq, a.sdq, a.sgs, a.sus, a.sds, a.Ish, (L / nth) * DX_ROWS);
+        xstage_store<WBITS>(xs, sm, nr, rsum);
         nrows = a.T;
         out = a.ysp;
-        if (tid < 16) {
-            sm.tok[tid] = 16 * th + tid;
+        if (tid < DEC_MAXT) {
             sm.plist[tid] = 16 * th + tid;
+            sm.arow[tid] = tid < n ? tid : 0;
             sm.psc[tid] = 1.0f;
         }
         __syncthreads();
-    } else {
-        const int v = L - nsh, per = a.I / DX_ROWS;
-        dec_route<EPL>(a, a.T, a.E, a.k, sm.u.r.ids, sm.w, v == 0);
-        const int e = __builtin_amdgcn_readfirstlane(
-            active_expert(sm.u.r.ids, a.T * a.k, a.E, v / per, sm.u.r.flags, &sm.ares));
-        if (e < 0) return;
-        locate(a.gq + (size_t)e * a.qstride, a.uq + (size_t)e * a.qstride, a.dq + (size_t)e * a.dqstride,
-               a.gs + (size_t)e * a.sstride, a.us + (size_t)e * a.sstride, a.ds + (size_t)e * a.dsstride, a.I,
-               (v % per) * DX_ROWS);
-        n = __builtin_amdgcn_readfirstlane(gather_pairs(sm.u.r.ids, a.T * a.k, a.k, e, sm.plist, sm.tok, &sm.pcnt));
-        nrows = a.T * a.k;
-        out = a.yp;
-        if (tid < n) sm.psc[tid] = a.rsf * sm.w[sm.plist[tid]];
+        expert_body<WBITS, 1>(a, sm, n, nr, rtok, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
+        return;
     }
+    // routed: every token's activation row is staged (row t = token t) while
+    // the routing logits are in flight
+    const int v = L - nsh, per = a.I / DX_ROWS;
+    nr = a.T;
+    auto rtok = [](int r) { return r; };
+    dec_route<EPL>(a, a.T, a.E, a.k, sm.ids, sm.w, v == 0, [&]() {
+        xstage_load<WBITS>(xs, a, nr, 0, rtok);
+        xstage_store<WBITS>(xs, sm, nr, rsum);
+    });
+    const int2 un = dec_locate_unit(sm.ids, a.T * a.k, a.k, a.E, v / per, sm.flags, sm.plist, sm.tok, sm.res);
+    const int e = __builtin_amdgcn_readfirstlane(un.x);
+    if (e < 0) return;
+    n = __builtin_amdgcn_readfirstlane(un.y);
+    locate(a.gq + (size_t)e * a.qstride, a.uq + (size_t)e * a.qstride, a.dq + (size_t)e * a.dqstride,
+           a.gs + (size_t)e * a.sstride, a.us + (size_t)e * a.sstride, a.ds + (size_t)e * a.dsstride, a.I,
+           (v % per) * DX_ROWS);
+    nrows = a.T * a.k;
+    out = a.yp;
+    if (tid < DEC_MAXT) {
+        sm.psc[tid] = tid < n ? a.rsf * sm.w[sm.plist[tid]] : 0.f;
+        sm.arow[tid] = tid < n ? sm.tok[tid] : 0;
+    }
+    __syncthreads();
     if (n <= 16)
-        expert_body<WBITS, 1>(a, sm, n, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
+        expert_body<WBITS, 1>(a, sm, n, nr, rtok, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
     else
-        expert_body<WBITS, 2>(a, sm, n, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
+        expert_body<WBITS, 2>(a, sm, n, nr, rtok, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
 }
 
 // ---------------------------------------------------------------- combine
