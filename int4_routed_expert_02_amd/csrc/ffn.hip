@@ -7,20 +7,28 @@
 // expert's three matrices are gate [I][H], up [I][H], down [H][I].
 //
 // Both GEMMs run on bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with f32
-// accumulation.  A rows (activations) are staged through LDS; B rows (weights)
-// are staged through LDS as raw packed bytes and unpacked to bf16 in registers
-// right before the MFMA.  int4 values become q + 136 (one AND-OR per pair of
-// values, see unpack_int4x8); the constant is removed in the epilogue as
-// 136 * sum(A row), a sum taken from the same bf16 values the MFMA consumes.
-// int8 values are converted exactly.  The per-row weight scale, SiLU * up
-// (gate/up kernel) and the per-pair combine weight rsf * w (down kernel) are
-// applied in the epilogue.
+// accumulation.  A rows (activations) and B rows (raw packed weight bytes) are
+// staged through a double-buffered LDS tile, one barrier per 64-column stage;
+// the next stage's global loads are in flight while the current one feeds the
+// MFMAs.  Weights are unpacked to bf16 in registers right before the MFMA: int4
+// values become q + 136 (one 3-input bit operation per pair of values, see
+// unpack_int4x8); the constant is removed in the epilogue as 136 * sum(A row),
+// a sum taken from the same bf16 values the MFMA consumes.  int8 values are
+// converted exactly.  The per-row weight scale, SiLU * up (gate/up kernel) and
+// the per-pair combine weight rsf * w (down kernel) are applied in the
+// epilogue.
 //
-// The intermediate h = silu(g) * u is stored in f32.  The down kernel feeds it
-// to the bf16 matrix cores as an exact two-term split h = hi + lo (hi = bf16(h),
-// lo = bf16(h - hi)), two MFMAs per unpacked weight fragment: a single bf16
-// rounding of h would leave a 2^-9 relative error on every product, about 1e-2
-// of the output RMS at the tails of a large batch.
+// Tiles are 128 output columns wide (gate and up of the same 128 intermediate
+// rows in one workgroup) and 16, 64 or 128 rows tall by the mean rows per
+// expert; a wave holds up to 64 x 64 outputs per matrix, so each unpacked
+// weight fragment feeds up to four MFMAs.
+//
+// The intermediate h = silu(g) * u leaves the gate/up kernel as an exact
+// two-term bf16 split h = hi + lo (hi = bf16(h), lo = bf16(h - hi)), two bf16
+// planes [rows][N], already in the k-slot order the down kernel's int4 unpack
+// uses; the down kernel runs two MFMAs per unpacked weight fragment.  A single
+// bf16 rounding of h would leave a 2^-9 relative error on every product, about
+// 1e-2 of the output RMS at the tails of a large batch.
 //
 // Tiles.  A launch covers every (m-tile, n-tile) of every expert without
 // reading the histogram back to the host: the grid is an upper bound
@@ -31,9 +39,8 @@
 
 namespace moe {
 
-constexpr int FF_BK = 64;             // reduction columns per stage
-constexpr int FF_LDA = FF_BK + 8;     // LDS A row, bf16 elements (144 B)
-
+constexpr int FF_BK = 64;           // reduction columns per stage
+constexpr int FF_LDA = FF_BK + 8;   // LDS A row, bf16 elements (144 B: conflict-free fragment reads)
 
 // Find this workgroup's expert, first sorted row and row count for m-tile
 // slot `slot`; returns false when the slot is beyond the last tile.
@@ -88,35 +95,50 @@ __device__ __forceinline__ bool find_tile(const FfnArgs &a, int slot, int &e, in
     return e >= 0;
 }
 
-// MODE 0: gate/up + SwiGLU -> f32 h [rows][N];  MODE 1: down -> f32 y [rows][N] * pscale;
+// Position of column j of an h row in its stored order: with int4 down weights
+// each 8-group is stored as (j0, j4, j1, j5, j2, j6, j3, j7), the k-slot order
+// of unpack_int4x8.
+template <int WBITS>
+__device__ __forceinline__ int hpos(int j)
+{
+    return WBITS == 4 ? (j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1) : j;
+}
+
+// MODE 0: gate/up + SwiGLU -> h as bf16 hi/lo planes [M][N] (see hpos);
+// MODE 1: down -> f32 y [rows][N] * pscale, A = those two planes;
 // MODE 2: gate/up raw integer-weight sums (no scale, no activation) -> f32
 // [rows][0:N] (gate) and [rows][N:2N] (up), for the exactness test.
 template <int MODE, int WBITS, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void k_ffn(FfnArgs a)
+__global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
 {
     constexpr int NMAT = (MODE == 1) ? 1 : 2;
+    constexpr int NPLANE = (MODE == 1) ? 2 : 1;   // bf16 planes of A (hi, lo)
     constexpr int BKB = FF_BK * WBITS / 8;        // bytes of a B row per stage
     constexpr int LDB = BKB + 16;                 // LDS B row stride in bytes
     constexpr int BROWS = NMAT * BN;
-    constexpr int A_CHUNKS = BM * FF_BK / 8;      // 16-byte chunks of A per stage
+    constexpr int A_CHUNKS = NPLANE * BM * FF_BK / 8;  // 16-byte chunks of A per stage
     constexpr int B_CPR = BKB / 16;               // 16-byte chunks per B row per stage
     constexpr int B_CHUNKS = BROWS * B_CPR;
     constexpr int A_PT = (A_CHUNKS + 255) / 256;  // per thread
     constexpr int B_PT = (B_CHUNKS + 255) / 256;
     constexpr int MB = BM / WM / 16;
     constexpr int NB = BN / WN / 16;
-    constexpr int AW = (MODE == 1) ? 2 : 1;       // 16-byte loads per 8-element A chunk (f32 h: 2)
-    constexpr int NPLANE = (MODE == 1) ? 2 : 1;   // bf16 planes of A in LDS (hi, lo)
+    constexpr int ABUF = NPLANE * BM * FF_LDA;    // bf16 elements of one A buffer
+    constexpr int BBUF = BROWS * LDB;             // bytes of one B buffer
     static_assert(WM * WN == 4, "four waves");
     static_assert(MB >= 1 && NB >= 1, "wave tile");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sA[NPLANE * BM * FF_LDA];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[BROWS * LDB];
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2 * ABUF];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2 * BBUF];
     __shared__ float sRow[BM];
 
+    // XCD-aware placement: workgroup b runs on XCD b % 8; the NT n-tiles of
+    // m-tile slot s get workgroups on XCD s % 8, so the slot's activation rows
+    // are fetched into one L2 and re-read from there
     const int NT = a.N / BN;
-    const int slot = blockIdx.x / NT;
-    const int nt = blockIdx.x % NT;
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int nt = q % NT;
+    const int slot = (q / NT) * 8 + xcd;
     int e, row0, rows;
     if (!find_tile<BM>(a, slot, e, row0, rows)) return;
     const int n0 = nt * BN;
@@ -124,17 +146,18 @@ __global__ __launch_bounds__(256) void k_ffn(FfnArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
-    // A source rows for this thread's chunks (fixed across stages)
-    const uint8_t *asrc[A_PT];  // bytes; A elements are bf16 (gate/up) or f32 (down)
+    // A source of this thread's chunks (fixed across stages): chunk c is
+    // (plane, row m, 8-column group c % 8)
+    const uint16_t *asrc[A_PT];
 #pragma unroll
     for (int i = 0; i < A_PT; ++i) {
         const int c = tid + i * 256;
-        const int m = c / 8;
+        const int pl = c / (BM * 8), m = (c / 8) % BM;
         asrc[i] = nullptr;
         if (c < A_CHUNKS && m < rows) {
             const int r = row0 + m;
             const int src = a.gather ? a.gather[r] / a.kdiv : r;
-            asrc[i] = (const uint8_t *)a.A + ((size_t)src * a.lda + (c % 8) * 8) * (AW * 2);
+            asrc[i] = (const uint16_t *)a.A + (size_t)pl * a.M * a.lda + (size_t)src * a.lda + (c % 8) * 8;
         }
     }
     const uint8_t *bsrc[B_PT];
@@ -151,7 +174,7 @@ __global__ __launch_bounds__(256) void k_ffn(FfnArgs a)
         }
     }
 
-    u32x4 ra[A_PT][AW], rb[B_PT];
+    u32x4 ra[A_PT], rb[B_PT];
     float rsum[A_PT];
 #pragma unroll
     for (int i = 0; i < A_PT; ++i) rsum[i] = 0.f;
@@ -159,57 +182,33 @@ __global__ __launch_bounds__(256) void k_ffn(FfnArgs a)
     auto load_stage = [&](int kt) {
 #pragma unroll
         for (int i = 0; i < A_PT; ++i)
-#pragma unroll
-            for (int h = 0; h < AW; ++h)
-                ra[i][h] = asrc[i] ? *(const u32x4 *)(asrc[i] + (size_t)kt * FF_BK * AW * 2 + h * 16)
-                                   : u32x4{0u, 0u, 0u, 0u};
+            ra[i] = asrc[i] ? *(const u32x4 *)(asrc[i] + (size_t)kt * FF_BK) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < B_PT; ++i)
-            if (bsrc[i]) rb[i] = *(const u32x4 *)(bsrc[i] + kt * BKB);
+            if (bsrc[i]) rb[i] = *(const u32x4 *)(bsrc[i] + (size_t)kt * BKB);
     };
-    auto store_stage = [&]() {
+    auto store_stage = [&](int buf) {
+        uint16_t *dA = sA + buf * ABUF;
+        uint8_t *dB = sB + buf * BBUF;
 #pragma unroll
         for (int i = 0; i < A_PT; ++i) {
             const int c = tid + i * 256;
             if (c < A_CHUNKS) {
+                u32x4 v = ra[i];
                 float s = 0.f;
-                u32x4 v, vlo;
-                if constexpr (MODE == 1) {
-                    // eight f32 -> bf16 hi and bf16 lo planes
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        uint32_t pr[2], pl[2];
-#pragma unroll
-                        for (int e2 = 0; e2 < 2; ++e2) {
-                            const float f = __uint_as_float(ra[i][d / 2][(d % 2) * 2 + e2]);
-                            const uint32_t hb = f32_to_bf16(f);
-                            const float hf = __uint_as_float(hb << 16);
-                            const uint32_t lb = f32_to_bf16(f - hf);
-                            s += hf + __uint_as_float(lb << 16);
-                            pr[e2] = hb;
-                            pl[e2] = lb;
-                        }
-                        v[d] = pr[0] | (pr[1] << 16);
-                        vlo[d] = pl[0] | (pl[1] << 16);
-                    }
-                } else {
-                    v = ra[i][0];
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) s += bf16_lo(v[d]) + bf16_hi(v[d]);
-                }
+                for (int d = 0; d < 4; ++d) s += bf16_lo(v[d]) + bf16_hi(v[d]);
                 rsum[i] += s;
-                if constexpr (WBITS == 4) {
-                    v = interleave_bf16x8(v);
-                    if constexpr (MODE == 1) vlo = interleave_bf16x8(vlo);
-                }
-                *(u32x4 *)(sA + (c / 8) * FF_LDA + (c % 8) * 8) = v;
-                if constexpr (MODE == 1) *(u32x4 *)(sA + BM * FF_LDA + (c / 8) * FF_LDA + (c % 8) * 8) = vlo;
+                // gate/up: the activations take the int4 k-slot order here;
+                // down: h is stored in that order already
+                if (WBITS == 4 && MODE != 1) v = interleave_bf16x8(v);
+                *(u32x4 *)(dA + (c / 8) * FF_LDA + (c % 8) * 8) = v;
             }
         }
 #pragma unroll
         for (int i = 0; i < B_PT; ++i) {
             const int c = tid + i * 256;
-            if (c < B_CHUNKS) *(u32x4 *)(sB + (c / B_CPR) * LDB + (c % B_CPR) * 16) = rb[i];
+            if (c < B_CHUNKS) *(u32x4 *)(dB + (c / B_CPR) * LDB + (c % B_CPR) * 16) = rb[i];
         }
     };
 
@@ -223,10 +222,13 @@ __global__ __launch_bounds__(256) void k_ffn(FfnArgs a)
 
     const int KT = a.K / FF_BK;
     load_stage(0);
-    store_stage();
+    store_stage(0);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
         if (kt + 1 < KT) load_stage(kt + 1);
+        const uint16_t *cA = sA + buf * ABUF;
+        const uint8_t *cB = sB + buf * BBUF;
 #pragma unroll
         for (int ks = 0; ks < FF_BK / 32; ++ks) {
             u32x4 af[NPLANE][MB];
@@ -234,14 +236,14 @@ __global__ __launch_bounds__(256) void k_ffn(FfnArgs a)
             for (int pl = 0; pl < NPLANE; ++pl)
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
-                    af[pl][i] = *(const u32x4 *)(sA + pl * BM * FF_LDA +
+                    af[pl][i] = *(const u32x4 *)(cA + pl * BM * FF_LDA +
                                                  (wm * (BM / WM) + i * 16 + (lane & 15)) * FF_LDA + ks * 32 +
                                                  (lane >> 4) * 8);
 #pragma unroll
             for (int x = 0; x < NMAT; ++x)
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    const uint8_t *bp = sB + (x * BN + wn * (BN / WN) + j * 16 + (lane & 15)) * LDB;
+                    const uint8_t *bp = cB + (x * BN + wn * (BN / WN) + j * 16 + (lane & 15)) * LDB;
                     u32x4 bf;
                     if (WBITS == 4) {
                         bf = unpack_int4x8(*(const uint32_t *)(bp + ks * 16 + (lane >> 4) * 4));
@@ -254,22 +256,39 @@ __global__ __launch_bounds__(256) void k_ffn(FfnArgs a)
                         for (int i = 0; i < MB; ++i) acc[x][i][j] = mfma_bf16(af[pl][i], bf, acc[x][i][j]);
                 }
         }
+        if (kt + 1 < KT) store_stage(buf ^ 1);  // the other buffer: last read before the previous barrier
         __syncthreads();
-        if (kt + 1 < KT) {
-            store_stage();
-            __syncthreads();
-        }
     }
 
-    // row sums of A: the 8 threads of a row are 8 consecutive lanes
+    // row sums of A: the 8 threads of a row are 8 consecutive lanes; the down
+    // kernel adds the hi and lo planes' sums of a row
 #pragma unroll
     for (int i = 0; i < A_PT; ++i) {
         float s = rsum[i];
         s += __shfl_xor(s, 1, WAVE);
         s += __shfl_xor(s, 2, WAVE);
         s += __shfl_xor(s, 4, WAVE);
-        const int c = tid + i * 256;
-        if (c < A_CHUNKS && (c % 8) == 0) sRow[c / 8] = s;
+        rsum[i] = s;
+    }
+    if (NPLANE == 1) {
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i) {
+            const int c = tid + i * 256;
+            if (c < A_CHUNKS && (c % 8) == 0) sRow[c / 8] = rsum[i];
+        }
+    } else {
+        // plane 0 rows first, then plane 1 rows add (fixed order: hi + lo)
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i) {
+            const int c = tid + i * 256;
+            if (c < BM * 8 && (c % 8) == 0) sRow[c / 8] = rsum[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i) {
+            const int c = tid + i * 256;
+            if (c >= BM * 8 && c < A_CHUNKS && (c % 8) == 0) sRow[(c / 8) % BM] += rsum[i];
+        }
     }
     __syncthreads();
 
@@ -285,13 +304,17 @@ __global__ __launch_bounds__(256) void k_ffn(FfnArgs a)
             const float corr = bias * sRow[m];
             const int row = row0 + m;
             if constexpr (MODE == 0) {
-                float *o = (float *)a.out + (size_t)row * a.ldo;
+                uint16_t *ohi = (uint16_t *)a.out + (size_t)row * a.ldo;
+                uint16_t *olo = ohi + (size_t)a.M * a.ldo;
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int n = n0 + wn * (BN / WN) + j * 16 + (lane & 15);
                     const float g = (acc[0][i][j][r] - corr) * sc0[n];
                     const float u = (acc[1][i][j][r] - corr) * sc1[n];
-                    o[n] = silu(g) * u;
+                    const float h = silu(g) * u;
+                    const uint16_t hb = f32_to_bf16(h);
+                    ohi[hpos<WBITS>(n)] = hb;
+                    olo[hpos<WBITS>(n)] = f32_to_bf16(h - bf16_to_f32(hb));
                 }
             } else if constexpr (MODE == 2) {
                 float *o = (float *)a.out + (size_t)row * a.ldo;
@@ -313,6 +336,212 @@ __global__ __launch_bounds__(256) void k_ffn(FfnArgs a)
         }
 }
 
+// ------------------------------------------------------------------ pipelined tiles (64 and 128 rows)
+
+// Tiles of 64 or 128 rows run a deeper pipeline: global memory is copied
+// straight into a ring of FF3_STAGES LDS stages (global_load_lds, 16 bytes
+// per lane), so loads in flight hold no registers and staging costs no
+// vector instructions.  Each wave's copy fills 1 KB of LDS contiguously:
+//  - A (bf16 rows of 64 columns = 8 chunks of 16 bytes) is stored with the
+//    chunk slot XOR-swizzled by (row % 8), which makes the fragment reads
+//    conflict-free; the int4 k-slot order of the activations is applied
+//    after the fragment read (four byte permutes), h arrives in that order;
+//  - B rows are raw packed weight bytes.
+// The int4 bias is removed with one extra MFMA per 16-row block and k-step
+// against a constant -136 fragment, accumulated apart and added to every
+// output tile of the block in the epilogue.
+constexpr int FF3_STAGES = 3;
+
+template <int MODE, int WBITS, int BM>
+struct Ff3 {
+    static constexpr int NMAT = (MODE == 1) ? 1 : 2;
+    static constexpr int NPLANE = (MODE == 1) ? 2 : 1;
+    static constexpr int BN = 128;
+    static constexpr int BKB = FF_BK * WBITS / 8;               // B bytes per row per stage
+    static constexpr int A_BYTES = NPLANE * BM * FF_BK * 2;     // per stage
+    static constexpr int B_BYTES = NMAT * BN * BKB;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 1024;              // wave copies per stage
+    static constexpr int B_LOADS = B_BYTES / 1024;
+    static constexpr int LOADS = A_LOADS + B_LOADS;
+    static_assert(LOADS % 4 == 0, "copies split evenly over the four waves");
+    static constexpr int PER_WAVE = LOADS / 4;
+};
+
+__device__ __forceinline__ void lds_copy16(const void *g, void *l)
+{
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)g,
+                                     (void __attribute__((address_space(3))) *)l, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));  // gfx9 encoding
+}
+
+template <int MODE, int WBITS, int BM, int WM, int WN>
+__global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
+{
+    using C = Ff3<MODE, WBITS, BM>;
+    constexpr int NMAT = C::NMAT, NPLANE = C::NPLANE, BN = C::BN, BKB = C::BKB;
+    constexpr int MB = BM / WM / 16;
+    constexpr int NB = BN / WN / 16;
+    static_assert(WM * WN == 4 && MB >= 1 && NB >= 1, "wave tile");
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem3[];
+
+    const int NT = a.N / BN;
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int nt = q % NT;
+    const int slot = (q / NT) * 8 + xcd;
+    int e, row0, rows;
+    if (!find_tile<BM>(a, slot, e, row0, rows)) return;
+    const int n0 = nt * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // this lane's source for each of its wave's copies (fixed across stages)
+    const uint8_t *src[C::PER_WAVE];
+    int dst[C::PER_WAVE];  // byte offset of the wave's 1 KB block within a stage
+#pragma unroll
+    for (int j = 0; j < C::PER_WAVE; ++j) {
+        const int l = wave + 4 * j;  // copy index within the stage
+        dst[j] = l * 1024;
+        if (l < C::A_LOADS) {
+            const int pl = l / (BM / 8);
+            const int r = (l % (BM / 8)) * 8 + lane / 8;  // tile row
+            const int slotc = lane % 8;
+            const int chunk = slotc ^ (r & 7);
+            const int rr = r < rows ? r : 0;  // padded rows read row 0 (outputs discarded)
+            const int srow = a.gather ? a.gather[row0 + rr] / a.kdiv : row0 + rr;
+            src[j] = (const uint8_t *)a.A + ((size_t)pl * a.M * a.lda + (size_t)srow * a.lda + chunk * 8) * 2;
+        } else {
+            const int lb = l - C::A_LOADS;
+            const int cpr = BKB / 16;                  // 16-byte chunks per B row per stage
+            const int br = lb * (64 / cpr) + lane / cpr;  // B row within the stage
+            const int mat = br / BN, n = br % BN;
+            const uint8_t *qm = (mat == 0) ? a.q0 : a.q1;
+            src[j] = qm + (size_t)e * a.qstride + (size_t)(n0 + n) * (size_t)a.K * WBITS / 8 + (lane % cpr) * 16;
+        }
+    }
+    auto issue = [&](int kt) {
+        uint8_t *base = smem3 + (kt % FF3_STAGES) * C::STAGE;
+#pragma unroll
+        for (int j = 0; j < C::PER_WAVE; ++j) {
+            const int l = wave + 4 * j;
+            const size_t adv = l < C::A_LOADS ? (size_t)kt * FF_BK * 2 : (size_t)kt * BKB;
+            lds_copy16(src[j] + adv, base + dst[j]);
+        }
+    };
+
+    f32x4 acc[NMAT][MB][NB];
+    f32x4 cor[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        cor[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int x = 0; x < NMAT; ++x)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[x][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const u32x4 cneg = u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};  // bf16 -136
+
+    const int KT = a.K / FF_BK;
+#pragma unroll
+    for (int s0 = 0; s0 < FF3_STAGES - 1; ++s0)
+        if (s0 < KT) issue(s0);
+    for (int kt = 0; kt < KT; ++kt) {
+        // stage kt has landed once at most the later stages' copies are outstanding
+        if (kt + 1 < KT) wait_vm<C::PER_WAVE * (FF3_STAGES - 2)>();
+        else wait_vm<0>();
+        __syncthreads();  // every wave's copies of stage kt are in LDS; stage kt - 1 is free
+        if (kt + FF3_STAGES - 1 < KT) issue(kt + FF3_STAGES - 1);
+        const uint8_t *sa = smem3 + (kt % FF3_STAGES) * C::STAGE;
+        const uint8_t *sb = sa + C::A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < FF_BK / 32; ++ks) {
+            u32x4 af[NPLANE][MB];
+#pragma unroll
+            for (int pl = 0; pl < NPLANE; ++pl)
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const int r = wm * (BM / WM) + i * 16 + (lane & 15);
+                    const int chunk = ks * 4 + (lane >> 4);
+                    u32x4 v = *(const u32x4 *)(sa + pl * BM * FF_BK * 2 + r * 128 + ((chunk ^ (r & 7)) * 16));
+                    if (WBITS == 4 && MODE != 1) v = interleave_bf16x8(v);
+                    af[pl][i] = v;
+                }
+            if (WBITS == 4) {
+#pragma unroll
+                for (int pl = 0; pl < NPLANE; ++pl)
+#pragma unroll
+                    for (int i = 0; i < MB; ++i) cor[i] = mfma_bf16(af[pl][i], cneg, cor[i]);
+            }
+#pragma unroll
+            for (int x = 0; x < NMAT; ++x)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const uint8_t *bp = sb + (x * BN + wn * (BN / WN) + j * 16 + (lane & 15)) * BKB;
+                    u32x4 bf;
+                    if (WBITS == 4) {
+                        bf = unpack_int4x8(*(const uint32_t *)(bp + ks * 16 + (lane >> 4) * 4));
+                    } else {
+                        bf = unpack_int8x8(*(const u32x2 *)(bp + ks * 32 + (lane >> 4) * 8));
+                    }
+#pragma unroll
+                    for (int pl = 0; pl < NPLANE; ++pl)
+#pragma unroll
+                        for (int i = 0; i < MB; ++i) acc[x][i][j] = mfma_bf16(af[pl][i], bf, acc[x][i][j]);
+                }
+        }
+    }
+
+    // epilogue: the lane's column scales are loaded once
+    float s0v[NB], s1v[NB];
+    int ncol[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        ncol[j] = n0 + wn * (BN / WN) + j * 16 + (lane & 15);
+        s0v[j] = a.s0[(size_t)e * a.sstride + ncol[j]];
+        s1v[j] = (MODE == 0) ? a.s1[(size_t)e * a.sstride + ncol[j]] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
+            if (m >= rows) continue;
+            const float c = cor[i][r];  // -136 * (row sum), or 0
+            const int row = row0 + m;
+            if constexpr (MODE == 0) {
+                uint16_t *ohi = (uint16_t *)a.out + (size_t)row * a.ldo;
+                uint16_t *olo = ohi + (size_t)a.M * a.ldo;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const float g = (acc[0][i][j][r] + c) * s0v[j];
+                    const float u = (acc[1][i][j][r] + c) * s1v[j];
+                    const float h = fast_silu(g) * u;
+                    const uint16_t hb = f32_to_bf16(h);
+                    ohi[hpos<WBITS>(ncol[j])] = hb;
+                    olo[hpos<WBITS>(ncol[j])] = f32_to_bf16(h - bf16_to_f32(hb));
+                }
+            } else if constexpr (MODE == 2) {
+                float *o = (float *)a.out + (size_t)row * a.ldo;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    o[ncol[j]] = acc[0][i][j][r] + c;
+                    o[a.N + ncol[j]] = acc[1][i][j][r] + c;
+                }
+            } else {
+                float *o = (float *)a.out + (size_t)row * a.ldo;
+                const float ps = (a.pscale && a.pair_of_row) ? a.pscale[a.pair_of_row[row]] : 1.f;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) o[ncol[j]] = (acc[0][i][j][r] + c) * s0v[j] * ps;
+            }
+        }
+}
+
 // ------------------------------------------------------------------ launchers
 
 // m-tile row count for a regime: mean rows per group decides
@@ -328,28 +557,40 @@ template <int MODE, int WBITS, int BM, int BN, int WM, int WN>
 static hipError_t launch_one(const FfnArgs &a, int slots, hipStream_t st)
 {
     const int NT = a.N / BN;
-    const long grid = (long)slots * NT;
+    const long grid = (long)((slots + 7) / 8 * 8) * NT;  // whole groups of 8 slots (see the placement)
     if (grid <= 0) return hipSuccess;
     hipLaunchKernelGGL((k_ffn<MODE, WBITS, BM, BN, WM, WN>), dim3((unsigned)grid), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
-// slots = upper bound on m-tiles over all groups
+template <int MODE, int WBITS, int BM, int WM, int WN>
+static hipError_t launch_three(const FfnArgs &a, int slots, hipStream_t st)
+{
+    const int NT = a.N / 128;
+    const long grid = (long)((slots + 7) / 8 * 8) * NT;
+    if (grid <= 0) return hipSuccess;
+    const size_t lds = (size_t)FF3_STAGES * Ff3<MODE, WBITS, BM>::STAGE;
+    hipLaunchKernelGGL((k_ffn3<MODE, WBITS, BM, WM, WN>), dim3((unsigned)grid), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
+// slots = upper bound on m-tiles over all groups.  Output tiles are 128
+// columns wide when N allows (64 otherwise); rows per tile by the mean rows
+// per group.
 template <int MODE, int WBITS>
 static hipError_t launch_mode(const FfnArgs &a, int rows_total, int groups, hipStream_t st)
 {
     const int bm = ffn_bm(rows_total, groups);
     const int ng = a.offsets ? groups : 1;
     const int slots = (rows_total + bm - 1) / bm + (a.offsets ? min(ng, rows_total) : 0);
-    if constexpr (MODE != 1) {
-        if (bm == 16) return launch_one<MODE, WBITS, 16, 64, 1, 4>(a, slots, st);
-        if (bm == 64) return launch_one<MODE, WBITS, 64, 64, 2, 2>(a, slots, st);
-        return launch_one<MODE, WBITS, 128, 64, 2, 2>(a, slots, st);
-    } else {
-        if (bm == 16) return launch_one<MODE, WBITS, 16, 64, 1, 4>(a, slots, st);
-        if (bm == 64) return launch_one<MODE, WBITS, 64, 128, 2, 2>(a, slots, st);
-        return launch_one<MODE, WBITS, 128, 128, 2, 2>(a, slots, st);
+    if (a.N % 128 == 0) {
+        if (bm == 16) return launch_one<MODE, WBITS, 16, 128, 1, 4>(a, slots, st);
+        if (bm == 64) return launch_three<MODE, WBITS, 64, 2, 2>(a, slots, st);
+        return launch_three<MODE, WBITS, 128, 2, 2>(a, slots, st);
     }
+    if (bm == 16) return launch_one<MODE, WBITS, 16, 64, 1, 4>(a, slots, st);
+    if (bm == 64) return launch_one<MODE, WBITS, 64, 64, 2, 2>(a, slots, st);
+    return launch_one<MODE, WBITS, 128, 64, 4, 1>(a, slots, st);
 }
 
 hipError_t launch_ffn(int mode, int wbits, const FfnArgs &a, int rows_total, int groups, hipStream_t st)

@@ -169,7 +169,7 @@ int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, con
 {
     FfnArgs d;
     memset(&d, 0, sizeof(d));
-    d.A = hbuf;
+    d.A = hbuf;  // bf16 hi plane [rows][I], then the lo plane
     d.lda = I;
     d.gather = nullptr;
     d.kdiv = 1;

@@ -7,7 +7,7 @@
 namespace moe {
 
 struct FfnArgs {
-    const void *A;  // bf16 rows (gate/up) or f32 rows (down)
+    const void *A;  // bf16 rows: activations (gate/up) or the h hi plane followed by the lo plane (down)
     int lda;
     const int32_t *gather;
     int kdiv;
