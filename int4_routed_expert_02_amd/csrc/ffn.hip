@@ -435,6 +435,8 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
         }
     };
 
+    // The products run as W x A^T (weights are the MFMA's first operand), so
+    // a lane ends up holding four consecutive output columns of one row.
     f32x4 acc[NMAT][MB][NB];
     f32x4 cor[MB];
 #pragma unroll
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 #pragma unroll
                 for (int pl = 0; pl < NPLANE; ++pl)
 #pragma unroll
-                    for (int i = 0; i < MB; ++i) cor[i] = mfma_bf16(af[pl][i], cneg, cor[i]);
+                    for (int i = 0; i < MB; ++i) cor[i] = mfma_bf16(cneg, af[pl][i], cor[i]);
             }
 #pragma unroll
             for (int x = 0; x < NMAT; ++x)
@@ -492,54 +494,93 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 #pragma unroll
                     for (int pl = 0; pl < NPLANE; ++pl)
 #pragma unroll
-                        for (int i = 0; i < MB; ++i) acc[x][i][j] = mfma_bf16(af[pl][i], bf, acc[x][i][j]);
+                        for (int i = 0; i < MB; ++i) acc[x][i][j] = mfma_bf16(bf, af[pl][i], acc[x][i][j]);
                 }
         }
     }
 
-    // epilogue: the lane's column scales are loaded once
-    float s0v[NB], s1v[NB];
-    int ncol[NB];
+    // Epilogue.  Lane l holds, for block (i, j), row m = l % 16 of the block
+    // and its columns 4 (l / 16) .. 4 (l / 16) + 3; cor[i] carries -136 times
+    // the row sum in every element (0 for int8 weights).
+    const int mloc = wm * (BM / WM) + (lane & 15);
+    const int nloc = wn * (BN / WN) + 4 * (lane >> 4);
+    const size_t sbase = (size_t)e * a.sstride + n0 + nloc;
+    if constexpr (MODE == 0) {
+        // h = silu(g) * u as bf16 hi and lo planes, staged in LDS in natural
+        // column order (8-byte writes), then copied out as whole rows with
+        // the down kernel's k-slot order applied on the way
+        constexpr int HP = BN * 2 + 16;  // LDS row pitch in bytes
+        static_assert(2 * BM * HP <= FF3_STAGES * C::STAGE, "the h tile fits in the stage ring");
+        f32x4 sg[NB], su[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        ncol[j] = n0 + wn * (BN / WN) + j * 16 + (lane & 15);
-        s0v[j] = a.s0[(size_t)e * a.sstride + ncol[j]];
-        s1v[j] = (MODE == 0) ? a.s1[(size_t)e * a.sstride + ncol[j]] : 0.f;
-    }
+        for (int j = 0; j < NB; ++j) {
+            sg[j] = *(const f32x4 *)(a.s0 + sbase + j * 16);
+            su[j] = *(const f32x4 *)(a.s1 + sbase + j * 16);
+        }
+        __syncthreads();  // every wave is done reading the stage ring
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MB; ++i) {
+            const float c = cor[i][0];
+            uint8_t *hrow = smem3 + (mloc + i * 16) * HP + nloc * 2;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
-            if (m >= rows) continue;
-            const float c = cor[i][r];  // -136 * (row sum), or 0
-            const int row = row0 + m;
-            if constexpr (MODE == 0) {
-                uint16_t *ohi = (uint16_t *)a.out + (size_t)row * a.ldo;
-                uint16_t *olo = ohi + (size_t)a.M * a.ldo;
+            for (int j = 0; j < NB; ++j) {
+                uint32_t hi[2], lo[2];
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const float g = (acc[0][i][j][r] + c) * s0v[j];
-                    const float u = (acc[1][i][j][r] + c) * s1v[j];
-                    const float h = fast_silu(g) * u;
-                    const uint16_t hb = f32_to_bf16(h);
-                    ohi[hpos<WBITS>(ncol[j])] = hb;
-                    olo[hpos<WBITS>(ncol[j])] = f32_to_bf16(h - bf16_to_f32(hb));
+                for (int q = 0; q < 2; ++q) {
+                    uint32_t ph = 0, pq = 0;
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int r = 2 * q + h2;
+                        const float g = (acc[0][i][j][r] + c) * sg[j][r];
+                        const float u = (acc[1][i][j][r] + c) * su[j][r];
+                        const float h = fast_silu(g) * u;
+                        const uint16_t hb = f32_to_bf16(h);
+                        ph |= (uint32_t)hb << (16 * h2);
+                        pq |= (uint32_t)f32_to_bf16(h - bf16_to_f32(hb)) << (16 * h2);
+                    }
+                    hi[q] = ph;
+                    lo[q] = pq;
                 }
-            } else if constexpr (MODE == 2) {
-                float *o = (float *)a.out + (size_t)row * a.ldo;
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    o[ncol[j]] = acc[0][i][j][r] + c;
-                    o[a.N + ncol[j]] = acc[1][i][j][r] + c;
-                }
-            } else {
-                float *o = (float *)a.out + (size_t)row * a.ldo;
-                const float ps = (a.pscale && a.pair_of_row) ? a.pscale[a.pair_of_row[row]] : 1.f;
-#pragma unroll
-                for (int j = 0; j < NB; ++j) o[ncol[j]] = (acc[0][i][j][r] + c) * s0v[j] * ps;
+                *(u32x2 *)(hrow + j * 32) = u32x2{hi[0], hi[1]};
+                *(u32x2 *)(hrow + BM * HP + j * 32) = u32x2{lo[0], lo[1]};
             }
         }
+        __syncthreads();
+        constexpr int CPR = BN * 2 / 16;  // 16-byte chunks per row
+        for (int ci = tid; ci < 2 * BM * CPR; ci += 256) {
+            const int pl = ci / (BM * CPR), rem = ci % (BM * CPR);
+            const int m = rem / CPR, ch = rem % CPR;
+            if (m >= rows) continue;
+            u32x4 v = *(const u32x4 *)(smem3 + pl * BM * HP + m * HP + ch * 16);
+            if (WBITS == 4) v = interleave_bf16x8(v);
+            *(u32x4 *)((uint16_t *)a.out + (size_t)pl * a.M * a.ldo + (size_t)(row0 + m) * a.ldo + n0 + ch * 8) = v;
+        }
+    } else {
+        f32x4 sv[NB];
+        if constexpr (MODE == 1) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) sv[j] = *(const f32x4 *)(a.s0 + sbase + j * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const int m = mloc + i * 16;
+            if (m >= rows) continue;
+            const int row = row0 + m;
+            const float c = cor[i][0];
+            float *o = (float *)a.out + (size_t)row * a.ldo + n0 + nloc;
+            if constexpr (MODE == 2) {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    *(f32x4 *)(o + j * 16) = acc[0][i][j] + c;
+                    *(f32x4 *)(o + a.N + j * 16) = acc[1][i][j] + c;
+                }
+            } else {
+                const float ps = (a.pscale && a.pair_of_row) ? a.pscale[a.pair_of_row[row]] : 1.f;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) *(f32x4 *)(o + j * 16) = (acc[0][i][j] + c) * sv[j] * ps;
+            }
+        }
+    }
 }
 
 // ------------------------------------------------------------------ launchers
