@@ -6,29 +6,27 @@
 // per row (colibri-nano README, "Converting a checkpoint yourself"); an
 // expert's three matrices are gate [I][H], up [I][H], down [H][I].
 //
-// Both GEMMs run on bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with f32
-// accumulation.  A rows (activations) and B rows (raw packed weight bytes) are
-// staged through a double-buffered LDS tile, one barrier per 64-column stage;
-// the next stage's global loads are in flight while the current one feeds the
-// MFMAs.  Weights are unpacked to bf16 in registers right before the MFMA: int4
-// values become q + 136 (one 3-input bit operation per pair of values, see
-// unpack_int4x8); the constant is removed in the epilogue as 136 * sum(A row),
-// a sum taken from the same bf16 values the MFMA consumes.  int8 values are
-// converted exactly.  The per-row weight scale, SiLU * up (gate/up kernel) and
-// the per-pair combine weight rsf * w (down kernel) are applied in the
-// epilogue.
+// Gate/up runs on bf16 matrix cores (v_mfma_f32_16x16x32_bf16, the
+// activations' own format), down on f16 matrix cores (v_mfma_f32_16x16x32_f16)
+// with h = silu(g) * u carried in f16; both accumulate in f32.  Weights are
+// unpacked in registers right before the MFMA, with an OR of exponent bits:
+// int4 becomes q + 136 in bf16 or q + 1032 in f16, int8 becomes q + 1152 in
+// f16 (gate/up converts int8 exactly to bf16).  The constant times the A row
+// sum is taken out again, either by one more MFMA against a constant fragment
+// or from row sums of the same 16-bit values the MFMA consumes.  The per-row
+// weight scale, SiLU * up (gate/up) and the per-pair combine weight rsf * w
+// (down) are applied in the epilogue.
 //
-// Tiles are 128 output columns wide (gate and up of the same 128 intermediate
-// rows in one workgroup) and 16, 64 or 128 rows tall by the mean rows per
-// expert; a wave holds up to 64 x 64 outputs per matrix, so each unpacked
-// weight fragment feeds up to four MFMAs.
+// h in f16 rounds each value with a 2^-11 relative error, a quarter of one
+// bf16 rounding (which alone left about 1e-2 of the output RMS at the tails
+// of a large batch); f16 holds |h| up to 65504.  The gate/up kernel writes h
+// already in the k-slot order the down kernel's int4 unpack uses.
 //
-// The intermediate h = silu(g) * u leaves the gate/up kernel as an exact
-// two-term bf16 split h = hi + lo (hi = bf16(h), lo = bf16(h - hi)), two bf16
-// planes [rows][N], already in the k-slot order the down kernel's int4 unpack
-// uses; the down kernel runs two MFMAs per unpacked weight fragment.  A single
-// bf16 rounding of h would leave a 2^-9 relative error on every product, about
-// 1e-2 of the output RMS at the tails of a large batch.
+// Tiles of 64 and 128 rows (k_ffn3) are 128 output columns wide, gate and up
+// of the same 128 intermediate rows in one workgroup; a wave holds up to
+// 64 x 64 outputs per matrix, so each unpacked weight fragment feeds up to
+// four MFMAs.  Tiles of 16 rows, and widths that are not a multiple of 128,
+// use the register-staged k_ffn.
 //
 // Tiles.  A launch covers every (m-tile, n-tile) of every expert without
 // reading the histogram back to the host: the grid is an upper bound
@@ -104,15 +102,16 @@ __device__ __forceinline__ int hpos(int j)
     return WBITS == 4 ? (j & ~7) | ((j & 3) << 1) | ((j >> 2) & 1) : j;
 }
 
-// MODE 0: gate/up + SwiGLU -> h as bf16 hi/lo planes [M][N] (see hpos);
-// MODE 1: down -> f32 y [rows][N] * pscale, A = those two planes;
+// MODE 0: gate/up + SwiGLU -> h as f16 [M][N] (see hpos);
+// MODE 1: down -> f32 y [rows][N] * pscale, A = that f16 h, f16 matrix cores;
 // MODE 2: gate/up raw integer-weight sums (no scale, no activation) -> f32
 // [rows][0:N] (gate) and [rows][N:2N] (up), for the exactness test.
 template <int MODE, int WBITS, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
 {
     constexpr int NMAT = (MODE == 1) ? 1 : 2;
-    constexpr int NPLANE = (MODE == 1) ? 2 : 1;   // bf16 planes of A (hi, lo)
+    constexpr int NPLANE = 1;
+    constexpr bool F16 = (MODE == 1);             // A is f16 h, weights unpack to f16
     constexpr int BKB = FF_BK * WBITS / 8;        // bytes of a B row per stage
     constexpr int LDB = BKB + 16;                 // LDS B row stride in bytes
     constexpr int BROWS = NMAT * BN;
@@ -197,7 +196,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
                 u32x4 v = ra[i];
                 float s = 0.f;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) s += bf16_lo(v[d]) + bf16_hi(v[d]);
+                for (int d = 0; d < 4; ++d) s += F16 ? f16_lo(v[d]) + f16_hi(v[d]) : bf16_lo(v[d]) + bf16_hi(v[d]);
                 rsum[i] += s;
                 // gate/up: the activations take the int4 k-slot order here;
                 // down: h is stored in that order already
@@ -246,22 +245,25 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
                     const uint8_t *bp = cB + (x * BN + wn * (BN / WN) + j * 16 + (lane & 15)) * LDB;
                     u32x4 bf;
                     if (WBITS == 4) {
-                        bf = unpack_int4x8(*(const uint32_t *)(bp + ks * 16 + (lane >> 4) * 4));
+                        const uint32_t w = *(const uint32_t *)(bp + ks * 16 + (lane >> 4) * 4);
+                        bf = F16 ? unpack_int4x8_f16(w) : unpack_int4x8(w);
                     } else {
-                        bf = unpack_int8x8(*(const u32x2 *)(bp + ks * 32 + (lane >> 4) * 8));
+                        const u32x2 w = *(const u32x2 *)(bp + ks * 32 + (lane >> 4) * 8);
+                        bf = F16 ? unpack_int8x8_f16(w) : unpack_int8x8(w);
                     }
 #pragma unroll
                     for (int pl = 0; pl < NPLANE; ++pl)
 #pragma unroll
-                        for (int i = 0; i < MB; ++i) acc[x][i][j] = mfma_bf16(af[pl][i], bf, acc[x][i][j]);
+                        for (int i = 0; i < MB; ++i)
+                            acc[x][i][j] = F16 ? mfma_f16(af[pl][i], bf, acc[x][i][j])
+                                               : mfma_bf16(af[pl][i], bf, acc[x][i][j]);
                 }
         }
         if (kt + 1 < KT) store_stage(buf ^ 1);  // the other buffer: last read before the previous barrier
         __syncthreads();
     }
 
-    // row sums of A: the 8 threads of a row are 8 consecutive lanes; the down
-    // kernel adds the hi and lo planes' sums of a row
+    // row sums of A: the 8 threads of a row are 8 consecutive lanes
 #pragma unroll
     for (int i = 0; i < A_PT; ++i) {
         float s = rsum[i];
@@ -270,29 +272,14 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
         s += __shfl_xor(s, 4, WAVE);
         rsum[i] = s;
     }
-    if (NPLANE == 1) {
 #pragma unroll
-        for (int i = 0; i < A_PT; ++i) {
-            const int c = tid + i * 256;
-            if (c < A_CHUNKS && (c % 8) == 0) sRow[c / 8] = rsum[i];
-        }
-    } else {
-        // plane 0 rows first, then plane 1 rows add (fixed order: hi + lo)
-#pragma unroll
-        for (int i = 0; i < A_PT; ++i) {
-            const int c = tid + i * 256;
-            if (c < BM * 8 && (c % 8) == 0) sRow[c / 8] = rsum[i];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < A_PT; ++i) {
-            const int c = tid + i * 256;
-            if (c >= BM * 8 && c < A_CHUNKS && (c % 8) == 0) sRow[(c / 8) % BM] += rsum[i];
-        }
+    for (int i = 0; i < A_PT; ++i) {
+        const int c = tid + i * 256;
+        if (c < A_CHUNKS && (c % 8) == 0) sRow[c / 8] = rsum[i];
     }
     __syncthreads();
 
-    const float bias = (WBITS == 4) ? INT4_BIAS : 0.f;
+    const float bias = F16 ? (WBITS == 4 ? INT4_F16_BIAS : INT8_F16_BIAS) : (WBITS == 4 ? INT4_BIAS : 0.f);
     const float *sc0 = a.s0 + (size_t)e * a.sstride;
     const float *sc1 = (MODE != 1) ? a.s1 + (size_t)e * a.sstride : nullptr;
 #pragma unroll
@@ -304,17 +291,13 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
             const float corr = bias * sRow[m];
             const int row = row0 + m;
             if constexpr (MODE == 0) {
-                uint16_t *ohi = (uint16_t *)a.out + (size_t)row * a.ldo;
-                uint16_t *olo = ohi + (size_t)a.M * a.ldo;
+                _Float16 *oh = (_Float16 *)a.out + (size_t)row * a.ldo;
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int n = n0 + wn * (BN / WN) + j * 16 + (lane & 15);
                     const float g = (acc[0][i][j][r] - corr) * sc0[n];
                     const float u = (acc[1][i][j][r] - corr) * sc1[n];
-                    const float h = silu(g) * u;
-                    const uint16_t hb = f32_to_bf16(h);
-                    ohi[hpos<WBITS>(n)] = hb;
-                    olo[hpos<WBITS>(n)] = f32_to_bf16(h - bf16_to_f32(hb));
+                    oh[hpos<WBITS>(n)] = (_Float16)(silu(g) * u);
                 }
             } else if constexpr (MODE == 2) {
                 float *o = (float *)a.out + (size_t)row * a.ldo;
@@ -347,15 +330,15 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
 //    conflict-free; the int4 k-slot order of the activations is applied
 //    after the fragment read (four byte permutes), h arrives in that order;
 //  - B rows are raw packed weight bytes.
-// The int4 bias is removed with one extra MFMA per 16-row block and k-step
-// against a constant -136 fragment, accumulated apart and added to every
-// output tile of the block in the epilogue.
+// The unpack offset is removed with one extra MFMA per 16-row block and
+// k-step against a constant fragment holding minus the offset, accumulated
+// apart and added to every output tile of the block in the epilogue.
 constexpr int FF3_STAGES = 3;
 
 template <int MODE, int WBITS, int BM>
 struct Ff3 {
     static constexpr int NMAT = (MODE == 1) ? 1 : 2;
-    static constexpr int NPLANE = (MODE == 1) ? 2 : 1;
+    static constexpr int NPLANE = 1;
     static constexpr int BN = 128;
     static constexpr int BKB = FF_BK * WBITS / 8;               // B bytes per row per stage
     static constexpr int A_BYTES = NPLANE * BM * FF_BK * 2;     // per stage
@@ -386,6 +369,8 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 {
     using C = Ff3<MODE, WBITS, BM>;
     constexpr int NMAT = C::NMAT, NPLANE = C::NPLANE, BN = C::BN, BKB = C::BKB;
+    constexpr bool F16 = (MODE == 1);           // down: A is f16 h, weights unpack to f16
+    constexpr bool COR = F16 || WBITS == 4;     // the unpacked weights carry a constant offset
     constexpr int MB = BM / WM / 16;
     constexpr int NB = BN / WN / 16;
     static_assert(WM * WN == 4 && MB >= 1 && NB >= 1, "wave tile");
@@ -447,7 +432,9 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 #pragma unroll
             for (int j = 0; j < NB; ++j) acc[x][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const u32x4 cneg = u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};  // bf16 -136
+    // minus the unpack offset, as a constant operand: bf16 -136, f16 -1032 or f16 -1152
+    constexpr uint32_t CW = F16 ? (WBITS == 4 ? 0xE408E408u : 0xE480E480u) : 0xC308C308u;
+    const u32x4 cneg = u32x4{CW, CW, CW, CW};
 
     const int KT = a.K / FF_BK;
 #pragma unroll
@@ -474,11 +461,12 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
                     if (WBITS == 4 && MODE != 1) v = interleave_bf16x8(v);
                     af[pl][i] = v;
                 }
-            if (WBITS == 4) {
+            if (COR) {
 #pragma unroll
                 for (int pl = 0; pl < NPLANE; ++pl)
 #pragma unroll
-                    for (int i = 0; i < MB; ++i) cor[i] = mfma_bf16(cneg, af[pl][i], cor[i]);
+                    for (int i = 0; i < MB; ++i)
+                        cor[i] = F16 ? mfma_f16(cneg, af[pl][i], cor[i]) : mfma_bf16(cneg, af[pl][i], cor[i]);
             }
 #pragma unroll
             for (int x = 0; x < NMAT; ++x)
@@ -487,30 +475,34 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
                     const uint8_t *bp = sb + (x * BN + wn * (BN / WN) + j * 16 + (lane & 15)) * BKB;
                     u32x4 bf;
                     if (WBITS == 4) {
-                        bf = unpack_int4x8(*(const uint32_t *)(bp + ks * 16 + (lane >> 4) * 4));
+                        const uint32_t w = *(const uint32_t *)(bp + ks * 16 + (lane >> 4) * 4);
+                        bf = F16 ? unpack_int4x8_f16(w) : unpack_int4x8(w);
                     } else {
-                        bf = unpack_int8x8(*(const u32x2 *)(bp + ks * 32 + (lane >> 4) * 8));
+                        const u32x2 w = *(const u32x2 *)(bp + ks * 32 + (lane >> 4) * 8);
+                        bf = F16 ? unpack_int8x8_f16(w) : unpack_int8x8(w);
                     }
 #pragma unroll
                     for (int pl = 0; pl < NPLANE; ++pl)
 #pragma unroll
-                        for (int i = 0; i < MB; ++i) acc[x][i][j] = mfma_bf16(bf, af[pl][i], acc[x][i][j]);
+                        for (int i = 0; i < MB; ++i)
+                            acc[x][i][j] = F16 ? mfma_f16(bf, af[pl][i], acc[x][i][j])
+                                               : mfma_bf16(bf, af[pl][i], acc[x][i][j]);
                 }
         }
     }
 
     // Epilogue.  Lane l holds, for block (i, j), row m = l % 16 of the block
-    // and its columns 4 (l / 16) .. 4 (l / 16) + 3; cor[i] carries -136 times
-    // the row sum in every element (0 for int8 weights).
+    // and its columns 4 (l / 16) .. 4 (l / 16) + 3; cor[i] carries minus the
+    // unpack offset times the row sum in every element (0 for int8 gate/up).
     const int mloc = wm * (BM / WM) + (lane & 15);
     const int nloc = wn * (BN / WN) + 4 * (lane >> 4);
     const size_t sbase = (size_t)e * a.sstride + n0 + nloc;
     if constexpr (MODE == 0) {
-        // h = silu(g) * u as bf16 hi and lo planes, staged in LDS in natural
-        // column order (8-byte writes), then copied out as whole rows with
-        // the down kernel's k-slot order applied on the way
+        // h = silu(g) * u in f16, staged in LDS in natural column order
+        // (8-byte writes), then copied out as whole rows with the down
+        // kernel's k-slot order applied on the way
         constexpr int HP = BN * 2 + 16;  // LDS row pitch in bytes
-        static_assert(2 * BM * HP <= FF3_STAGES * C::STAGE, "the h tile fits in the stage ring");
+        static_assert(BM * HP <= FF3_STAGES * C::STAGE, "the h tile fits in the stage ring");
         f32x4 sg[NB], su[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -524,36 +516,24 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
             uint8_t *hrow = smem3 + (mloc + i * 16) * HP + nloc * 2;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                uint32_t hi[2], lo[2];
+                float h[4];
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    uint32_t ph = 0, pq = 0;
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const int r = 2 * q + h2;
-                        const float g = (acc[0][i][j][r] + c) * sg[j][r];
-                        const float u = (acc[1][i][j][r] + c) * su[j][r];
-                        const float h = fast_silu(g) * u;
-                        const uint16_t hb = f32_to_bf16(h);
-                        ph |= (uint32_t)hb << (16 * h2);
-                        pq |= (uint32_t)f32_to_bf16(h - bf16_to_f32(hb)) << (16 * h2);
-                    }
-                    hi[q] = ph;
-                    lo[q] = pq;
+                for (int r = 0; r < 4; ++r) {
+                    const float g = (acc[0][i][j][r] + c) * sg[j][r];
+                    const float u = (acc[1][i][j][r] + c) * su[j][r];
+                    h[r] = fast_silu(g) * u;
                 }
-                *(u32x2 *)(hrow + j * 32) = u32x2{hi[0], hi[1]};
-                *(u32x2 *)(hrow + BM * HP + j * 32) = u32x2{lo[0], lo[1]};
+                *(u32x2 *)(hrow + j * 32) = u32x2{pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3])};
             }
         }
         __syncthreads();
         constexpr int CPR = BN * 2 / 16;  // 16-byte chunks per row
-        for (int ci = tid; ci < 2 * BM * CPR; ci += 256) {
-            const int pl = ci / (BM * CPR), rem = ci % (BM * CPR);
-            const int m = rem / CPR, ch = rem % CPR;
+        for (int ci = tid; ci < BM * CPR; ci += 256) {
+            const int m = ci / CPR, ch = ci % CPR;
             if (m >= rows) continue;
-            u32x4 v = *(const u32x4 *)(smem3 + pl * BM * HP + m * HP + ch * 16);
+            u32x4 v = *(const u32x4 *)(smem3 + m * HP + ch * 16);
             if (WBITS == 4) v = interleave_bf16x8(v);
-            *(u32x4 *)((uint16_t *)a.out + (size_t)pl * a.M * a.ldo + (size_t)(row0 + m) * a.ldo + n0 + ch * 8) = v;
+            *(u32x4 *)((uint16_t *)a.out + (size_t)(row0 + m) * a.ldo + n0 + ch * 8) = v;
         }
     } else {
         f32x4 sv[NB];

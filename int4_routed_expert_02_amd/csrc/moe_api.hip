@@ -75,7 +75,7 @@ Layout layout(const moe_shape *s, int which)
         const size_t a = (size_t)KS * T * E * 4, b = nsb * E * 4;
         L.zpart = L.sbc = take(a > b ? a : b);
     } else if (which == MOE_WS_EXPERT_FFN) {
-        L.hbuf = take(P * (size_t)s->I * 4);
+        L.hbuf = take(P * (size_t)s->I * 2);  // h, f16
     } else if (use_decode(s)) {
         // pair-indexed buffers, no permutation: partial logits, routing, and
         // the experts' partial outputs (one plane per 128-row intermediate chunk)
@@ -98,10 +98,10 @@ Layout layout(const moe_shape *s, int which)
         L.offsets = take((E + 1) * 4);
         L.sorted = take(P * 4);
         L.inv = take(P * 4);
-        L.hbuf = take(P * (size_t)s->I * 4);
+        L.hbuf = take(P * (size_t)s->I * 2);  // h, f16
         L.ypair = take(P * (size_t)s->H * 4);
         if (s->shared_bits) {
-            L.shh = take(T * (size_t)s->I_shared * 4);
+            L.shh = take(T * (size_t)s->I_shared * 2);
             L.shy = take(T * (size_t)s->H * 4);
         }
     }
@@ -127,13 +127,13 @@ int check_ws(const moe_shape *s, int which, void *ws, size_t ws_bytes)
 }
 
 int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
-                 const int32_t *sorted, int E, int rows, const float *pscale, const float *hbuf, float *y,
+                 const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, float *y,
                  hipStream_t st);
 
 // The two grouped GEMMs of one expert family on sorted rows.
 int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qmat &gate, const moe_qmat &up,
             const moe_qmat &down, int I, const int32_t *offsets, const int32_t *sorted, int E, int kdiv, int rows,
-            const float *pscale, float *hbuf, float *y, hipStream_t st, bool gateup_only = false)
+            const float *pscale, uint16_t *hbuf, float *y, hipStream_t st, bool gateup_only = false)
 {
     if (gate.q_stride_bytes != up.q_stride_bytes || gate.qs_stride_floats != up.qs_stride_floats)
         return MOE_ERR_UNSUPPORTED;
@@ -164,12 +164,12 @@ int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qma
 
 // The down GEMM on h (f32) of sorted rows.
 int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
-                 const int32_t *sorted, int E, int rows, const float *pscale, const float *hbuf, float *y,
+                 const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, float *y,
                  hipStream_t st)
 {
     FfnArgs d;
     memset(&d, 0, sizeof(d));
-    d.A = hbuf;  // bf16 hi plane [rows][I], then the lo plane
+    d.A = hbuf;  // h in f16 [rows][I], k-slot order of the down weights
     d.lda = I;
     d.gather = nullptr;
     d.kdiv = 1;
@@ -290,7 +290,7 @@ int moe_expert_ffn(const moe_shape *s, const moe_bf16 *hidden, const moe_weights
         return hip_status(moe::launch_ffn(2, 4, g, s->T * s->top_k, s->E, (hipStream_t)stream));
     }
     return run_ffn(s, wbits, hidden, w->gate, w->up, w->down, s->I, offsets, sorted_pairs, s->E, s->top_k,
-                   s->T * s->top_k, pair_scale, at<float>(ws, L.hbuf), y_pairs, (hipStream_t)stream,
+                   s->T * s->top_k, pair_scale, at<uint16_t>(ws, L.hbuf), y_pairs, (hipStream_t)stream,
                    (s->flags & MOE_STAGE_GATEUP_ONLY) != 0);
 }
 
@@ -399,18 +399,18 @@ int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const m
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (ev_start && hipEventRecord((hipEvent_t)ev_start, hs) != hipSuccess) return MOE_ERR_HIP;
     st = run_ffn(s, 4, hidden, w->gate, w->up, w->down, s->I, offsets, sorted, s->E, s->top_k, P, pscale,
-                 at<float>(ws, L.hbuf), ypair, hs, ev_stop != nullptr);
+                 at<uint16_t>(ws, L.hbuf), ypair, hs, ev_stop != nullptr);
     if (st) return st;
     if (ev_stop) {
         // profiled: the routed gate/up kernel ran alone between the events; now the down GEMM
         if (hipEventRecord((hipEvent_t)ev_stop, hs) != hipSuccess) return MOE_ERR_HIP;
-        st = run_ffn_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, at<float>(ws, L.hbuf), ypair, hs);
+        st = run_ffn_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, at<uint16_t>(ws, L.hbuf), ypair, hs);
         if (st) return st;
     }
     const float *shy = nullptr;
     if (s->shared_bits) {
         st = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr, 1,
-                     1, s->T, nullptr, at<float>(ws, L.shh), at<float>(ws, L.shy), hs);
+                     1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<float>(ws, L.shy), hs);
         if (st) return st;
         shy = at<float>(ws, L.shy);
     }

@@ -14,6 +14,7 @@
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -24,6 +25,23 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                    c, 0, 0, 0);
+}
+
+// the same shape with f16 operands (v_mfma_f32_16x16x32_f16)
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); }
+__device__ __forceinline__ float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
+
+// two f32 -> packed f16 pair, each rounded to nearest even
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -60,6 +78,37 @@ __device__ __forceinline__ u32x4 unpack_int4x8(uint32_t w)
     r[1] = (((w >> 4) ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
     r[2] = (((w >> 8) ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
     r[3] = (((w >> 12) ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
+    return r;
+}
+
+// f16 forms of the same unpacks, for the down GEMM, whose activations h are
+// f16.  The f16 with bit pattern 0x6400 | m is exactly 1024 + m for m < 1024:
+//  - int4: nibble n = q + 8 gives q + 1032, k-slot order as unpack_int4x8;
+//  - int8: byte b = q + 128 (bit 7 flipped) gives q + 1152, natural order,
+//    one byte permute per pair (the 0x64 bytes come from a constant).
+// The caller removes the constant with (its bias) * (sum of the A row).
+constexpr float INT4_F16_BIAS = 1032.0f;
+constexpr float INT8_F16_BIAS = 1152.0f;
+
+__device__ __forceinline__ u32x4 unpack_int4x8_f16(uint32_t w)
+{
+    u32x4 r;
+    r[0] = ((w ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+    r[1] = (((w >> 4) ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+    r[2] = (((w >> 8) ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+    r[3] = (((w >> 12) ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+    return r;
+}
+
+__device__ __forceinline__ u32x4 unpack_int8x8_f16(u32x2 w)
+{
+    const uint32_t f0 = w[0] ^ 0x80808080u, f1 = w[1] ^ 0x80808080u;
+    u32x4 r;
+    // selector bytes: 0..3 pick bytes of the second operand, 4..7 of the first
+    r[0] = __builtin_amdgcn_perm(0x64646464u, f0, 0x04010400u);
+    r[1] = __builtin_amdgcn_perm(0x64646464u, f0, 0x04030402u);
+    r[2] = __builtin_amdgcn_perm(0x64646464u, f1, 0x04010400u);
+    r[3] = __builtin_amdgcn_perm(0x64646464u, f1, 0x04030402u);
     return r;
 }
 

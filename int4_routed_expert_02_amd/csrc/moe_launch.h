@@ -7,7 +7,7 @@
 namespace moe {
 
 struct FfnArgs {
-    const void *A;  // bf16 rows: activations (gate/up) or the h hi plane followed by the lo plane (down)
+    const void *A;  // rows: bf16 activations (gate/up) or f16 h (down)
     int lda;
     const int32_t *gather;
     int kdiv;
