@@ -364,6 +364,17 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));  // gfx9 encoding
 }
 
+// Workgroup barrier of the stage ring.  It waits for this wave's LDS reads
+// (lgkmcnt 0) but not for its global-to-LDS copies in flight, which the
+// counted wait_vm before it has already settled for the stage about to be
+// read; the memory clobber keeps the compiler from moving memory accesses
+// across it.  (__syncthreads would also drain every copy in flight, leaving
+// the ring only one stage ahead.)
+__device__ __forceinline__ void ring_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int MODE, int WBITS, int BM, int WM, int WN>
 __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 {
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
         // stage kt has landed once at most the later stages' copies are outstanding
         if (kt + 1 < KT) wait_vm<C::PER_WAVE * (FF3_STAGES - 2)>();
         else wait_vm<0>();
-        __syncthreads();  // every wave's copies of stage kt are in LDS; stage kt - 1 is free
+        ring_barrier();  // every wave's copies of stage kt are in LDS; stage kt - 1 is free
         if (kt + FF3_STAGES - 1 < KT) issue(kt + FF3_STAGES - 1);
         const uint8_t *sa = smem3 + (kt % FF3_STAGES) * C::STAGE;
         const uint8_t *sb = sa + C::A_BYTES;

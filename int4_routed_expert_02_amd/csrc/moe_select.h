@@ -29,6 +29,12 @@ __device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b)
     return a;
 }
 
+// c ranks strictly before d (an empty d ranks last)
+__device__ __forceinline__ bool beats(ArgMax c, ArgMax d)
+{
+    return c.i >= 0 && (d.i < 0 || c.v > d.v || (c.v == d.v && c.i < d.i));
+}
+
 __device__ __forceinline__ ArgMax wave_argmax(ArgMax a)
 {
 #pragma unroll
@@ -55,6 +61,39 @@ __device__ __forceinline__ void select_token(float (&s)[EPL], float (&b)[EPL], b
     if (n_group > 1 && topk_group < n_group) {
         const int Eg = E / n_group;
         float my_g = -INFINITY;  // lane g holds group g's score
+        const int lpg = Eg / EPL;  // lanes per group when groups cover whole lanes
+        if (Eg % EPL == 0 && (lpg & (lpg - 1)) == 0) {
+            // each lane's own top two, then a top-two merge across the lpg
+            // lanes of its group (xor partners stay inside the group)
+            ArgMax m1{-INFINITY, -1}, m2{-INFINITY, -1};
+#pragma unroll
+            for (int q = 0; q < EPL; ++q) {
+                const ArgMax c{b[q], lane * EPL + q};
+                if (!ok[q]) continue;
+                if (beats(c, m1)) {
+                    m2 = m1;
+                    m1 = c;
+                } else if (beats(c, m2)) {
+                    m2 = c;
+                }
+            }
+            for (int o = 1; o < lpg; o <<= 1) {
+                ArgMax o1, o2;
+                o1.v = __shfl_xor(m1.v, o, WAVE);
+                o1.i = __shfl_xor(m1.i, o, WAVE);
+                o2.v = __shfl_xor(m2.v, o, WAVE);
+                o2.i = __shfl_xor(m2.i, o, WAVE);
+                if (beats(o1, m1)) {
+                    m2 = beats(m1, o2) ? m1 : o2;
+                    m1 = o1;
+                } else {
+                    m2 = beats(o1, m2) ? o1 : m2;
+                }
+            }
+            const float gsc = m1.v + m2.v;
+            const float gv = __shfl(gsc, (lane < n_group ? lane : 0) * lpg, WAVE);
+            if (lane < n_group) my_g = gv;
+        } else
         for (int g = 0; g < n_group; ++g) {
             ArgMax m1{-INFINITY, -1};
 #pragma unroll

@@ -15,7 +15,8 @@
 //
 // Selection.  One wavefront per token.  A lane holds up to four experts' scores
 // (lane l holds experts [l*EPL, (l+1)*EPL)); arg-max reductions across the wave
-// break ties toward the lower expert id.
+// break ties toward the lower expert id.  The K-split partial logits are added
+// in split order, so results do not depend on timing.
 #include "moe_device.h"
 #include "moe_select.h"
 
@@ -39,7 +40,9 @@ __device__ __forceinline__ void split3(float w, uint32_t &hi, uint32_t &mid, uin
     lo = __float_as_uint(r2) >> 16;  // r2 has at most 8 significant bits: exact
 }
 
-// grid: (ceil(T/RT_TB) * ceil(E/RT_EB), KS).  zpart[ks][t][e] f32.
+// grid: (ceil(T/RT_TB) * ceil(E/RT_EB), KS).  zpart[ks][t][e] f32.  Global
+// loads run two k-steps ahead of the matrix cores (two register sets, used in
+// turn), so a workgroup waits for memory once rather than once per k-step.
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restrict__ x, const float *__restrict__ W,
                                                        float *__restrict__ zpart, int T, int H, int E, int ksteps_per_split,
                                                        int32_t *__restrict__ clear, int clear_n)
@@ -63,55 +66,79 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restric
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int kbeg = ks * ksteps_per_split;
-    for (int kt = kbeg; kt < kbeg + ksteps_per_split; ++kt) {
+    // x: 64 rows x 64 bf16 = 512 chunks of 16 B, 2 per thread;
+    // W: 64 experts x 64 f32 = 1024 chunks of 4 floats, 4 per thread
+    struct Regs {
+        u32x4 x[2];
+        f32x4 w[4];
+    };
+    auto gload = [&](Regs &r, int kt) {
         const int k0 = kt * RT_BK;
-        // stage x: 64 rows x 64 bf16 = 512 chunks of 16 B, 2 per thread
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            int chunk = tid + c * 256;
-            int r = chunk >> 3, cc = chunk & 7;
-            int t = t0 + r;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (t < T) v = *(const u32x4 *)(x + (size_t)t * H + k0 + cc * 8);
-            *(u32x4 *)(sA + r * RT_LDA + cc * 8) = v;
+            const int chunk = tid + c * 256;
+            const int t = t0 + (chunk >> 3);
+            r.x[c] = t < T ? *(const u32x4 *)(x + (size_t)t * H + k0 + (chunk & 7) * 8) : u32x4{0u, 0u, 0u, 0u};
         }
-        // stage W: 64 experts x 64 f32 = 1024 chunks of 4 floats, 4 per thread, split into 3 parts
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            int chunk = tid + c * 256;
-            int r = chunk >> 4, cc = chunk & 15;
-            int e = e0 + r;
-            f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (e < E) v = *(const f32x4 *)(W + (size_t)e * H + k0 + cc * 4);
+            const int chunk = tid + c * 256;
+            const int e = e0 + (chunk >> 4);
+            r.w[c] = e < E ? *(const f32x4 *)(W + (size_t)e * H + k0 + (chunk & 15) * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    auto lstore = [&](const Regs &r) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int chunk = tid + c * 256;
+            *(u32x4 *)(sA + (chunk >> 3) * RT_LDA + (chunk & 7) * 8) = r.x[c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int chunk = tid + c * 256;
+            const int row = chunk >> 4, cc = chunk & 15;
             uint32_t h[4], m[4], l[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) split3(v[i], h[i], m[i], l[i]);
-            u32x2 ph = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-            u32x2 pm = u32x2{m[0] | (m[1] << 16), m[2] | (m[3] << 16)};
-            u32x2 pl = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-            *(u32x2 *)(sB[0] + r * RT_LDA + cc * 4) = ph;
-            *(u32x2 *)(sB[1] + r * RT_LDA + cc * 4) = pm;
-            *(u32x2 *)(sB[2] + r * RT_LDA + cc * 4) = pl;
+            for (int i = 0; i < 4; ++i) split3(r.w[c][i], h[i], m[i], l[i]);
+            *(u32x2 *)(sB[0] + row * RT_LDA + cc * 4) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            *(u32x2 *)(sB[1] + row * RT_LDA + cc * 4) = u32x2{m[0] | (m[1] << 16), m[2] | (m[3] << 16)};
+            *(u32x2 *)(sB[2] + row * RT_LDA + cc * 4) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
         }
-        __syncthreads();
+    };
+    auto compute = [&]() {
 #pragma unroll
         for (int kk = 0; kk < RT_BK; kk += 32) {
             const int ko = kk + (lane >> 4) * 8;
-            u32x4 a[2];
+            u32x4 av[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = *(const u32x4 *)(sA + (wm * 32 + i * 16 + (lane & 15)) * RT_LDA + ko);
+            for (int i = 0; i < 2; ++i) av[i] = *(const u32x4 *)(sA + (wm * 32 + i * 16 + (lane & 15)) * RT_LDA + ko);
 #pragma unroll
             for (int p = 0; p < 3; ++p) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    u32x4 b = *(const u32x4 *)(sB[p] + (wn * 32 + j * 16 + (lane & 15)) * RT_LDA + ko);
+                    const u32x4 bv = *(const u32x4 *)(sB[p] + (wn * 32 + j * 16 + (lane & 15)) * RT_LDA + ko);
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) acc[i][j] = mfma_bf16(a[i], b, acc[i][j]);
+                    for (int i = 0; i < 2; ++i) acc[i][j] = mfma_bf16(av[i], bv, acc[i][j]);
                 }
             }
         }
+    };
+    // one k-step from register set r, which then fetches k-step kt + 2
+    auto step = [&](Regs &r, int kt, int kend) {
+        lstore(r);
         __syncthreads();
+        if (kt + 2 < kend) gload(r, kt + 2);
+        compute();
+        __syncthreads();
+    };
+
+    const int kbeg = ks * ksteps_per_split, kend = kbeg + ksteps_per_split;
+    Regs ra, rb;
+    gload(ra, kbeg);
+    if (kbeg + 1 < kend) gload(rb, kbeg + 1);
+    for (int kt = kbeg; kt < kend; kt += 2) {
+        step(ra, kt, kend);
+        if (kt + 1 < kend) step(rb, kt + 1, kend);
     }
     float *zp = zpart + (size_t)ks * T * E;
 #pragma unroll
@@ -126,8 +153,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restric
             }
 }
 
-constexpr int SEL_TPW = 4;                 // tokens per wave
-constexpr int SEL_TOKENS = 4 * SEL_TPW;    // tokens per workgroup (4 waves)
+constexpr int SEL_TOKENS = 4;  // tokens per workgroup: one wave per token
 
 // One wave per token.  Writes ids, w, gap and optionally pair_scale (rsf * w
 // per pair).  When sbcounts is given, each workgroup adds the expert histogram
@@ -147,23 +173,34 @@ __global__ __launch_bounds__(256) void k_router_select(const float *__restrict__
     for (int e = tid; e < E; e += 256) hist[e] = 0;
     __syncthreads();
 
-    for (int it = 0; it < SEL_TPW; ++it) {
-        const int t = blockIdx.x * SEL_TOKENS + wave * SEL_TPW + it;
-        if (t >= T) break;
-        float s[EPL], b[EPL];
+    const int t = blockIdx.x * SEL_TOKENS + wave;
+    if (t < T) {
+        float s[EPL], b[EPL], z[EPL];
         bool ok[EPL];
 #pragma unroll
         for (int q = 0; q < EPL; ++q) {
-            int e = lane * EPL + q;
-            ok[q] = e < E;
-            s[q] = 0.f;
-            b[q] = -INFINITY;
-            if (ok[q]) {
-                float z = 0.f;
-                for (int p = 0; p < KS; ++p) z += zpart[((size_t)p * T + t) * E + e];
-                s[q] = 1.0f / (1.0f + expf(-z));
-                b[q] = s[q] + bias[e];
-            }
+            ok[q] = lane * EPL + q < E;
+            z[q] = 0.f;
+        }
+        // partial logits added in plane order; eight planes' loads in flight at once
+        constexpr int PB = 8;
+        for (int p0 = 0; p0 < KS; p0 += PB) {
+            float v[PB][EPL];
+#pragma unroll
+            for (int i = 0; i < PB; ++i)
+#pragma unroll
+                for (int q = 0; q < EPL; ++q)
+                    v[i][q] = (p0 + i < KS && ok[q]) ? zpart[((size_t)(p0 + i) * T + t) * E + lane * EPL + q] : 0.f;
+#pragma unroll
+            for (int i = 0; i < PB; ++i)
+#pragma unroll
+                for (int q = 0; q < EPL; ++q)
+                    if (p0 + i < KS) z[q] += v[i][q];
+        }
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) {
+            s[q] = ok[q] ? 1.0f / (1.0f + expf(-z[q])) : 0.f;
+            b[q] = ok[q] ? s[q] + bias[lane * EPL + q] : -INFINITY;
         }
         select_token<EPL>(s, b, ok, lane, t, E, k, n_group, topk_group, rsf, ids, w, gap, pair_scale, hist);
     }
@@ -177,6 +214,8 @@ __global__ __launch_bounds__(256) void k_router_select(const float *__restrict__
 
 // ------------------------------------------------------------------ launchers
 
+// K splits of the logits: the smallest divisor of the k-step count that gives
+// at least 512 workgroups (two per compute unit), else one k-step each
 int router_ks(int T, int H, int E)
 {
     const int ksteps = H / RT_BK;
@@ -185,7 +224,7 @@ int router_ks(int T, int H, int E)
     for (int c = 1; c <= ksteps; ++c) {
         if (ksteps % c) continue;
         ks = c;
-        if (tiles * c >= 256 || ksteps / c <= 2) break;
+        if (tiles * c >= 512) break;
     }
     return ks;
 }
