@@ -325,26 +325,28 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
 // straight into a ring of FF3_STAGES LDS stages (global_load_lds, 16 bytes
 // per lane), so loads in flight hold no registers and staging costs no
 // vector instructions.  Each wave's copy fills 1 KB of LDS contiguously:
-//  - A (bf16 rows of 64 columns = 8 chunks of 16 bytes) is stored with the
+//  - A (16-bit rows of 64 columns = 8 chunks of 16 bytes) is stored with the
 //    chunk slot XOR-swizzled by (row % 8), which makes the fragment reads
-//    conflict-free; the int4 k-slot order of the activations is applied
-//    after the fragment read (four byte permutes), h arrives in that order;
+//    conflict-free;
 //  - B rows are raw packed weight bytes.
-// The unpack offset is removed with one extra MFMA per 16-row block and
-// k-step against a constant fragment holding minus the offset, accumulated
-// apart and added to every output tile of the block in the epilogue.
+// The four waves share the tile's rows and split its 128 columns (32 each),
+// so one unpacked weight fragment feeds BM / 16 MFMAs.  Gate/up unpacks its
+// weights in natural k order (the activations are used as they are); down
+// uses the k-slot order h is written in.  The unpack offset is removed with
+// one extra MFMA per 16-row block and k-step against a constant fragment
+// holding minus the offset: wave w takes the row blocks i = w (mod 4) and the
+// results are shared through LDS in the epilogue.
 constexpr int FF3_STAGES = 3;
 
 template <int MODE, int WBITS, int BM>
 struct Ff3 {
     static constexpr int NMAT = (MODE == 1) ? 1 : 2;
-    static constexpr int NPLANE = 1;
     static constexpr int BN = 128;
-    static constexpr int BKB = FF_BK * WBITS / 8;               // B bytes per row per stage
-    static constexpr int A_BYTES = NPLANE * BM * FF_BK * 2;     // per stage
+    static constexpr int BKB = FF_BK * WBITS / 8;      // B bytes per row per stage
+    static constexpr int A_BYTES = BM * FF_BK * 2;     // per stage
     static constexpr int B_BYTES = NMAT * BN * BKB;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int A_LOADS = A_BYTES / 1024;              // wave copies per stage
+    static constexpr int A_LOADS = A_BYTES / 1024;     // wave copies per stage
     static constexpr int B_LOADS = B_BYTES / 1024;
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static_assert(LOADS % 4 == 0, "copies split evenly over the four waves");
@@ -375,17 +377,31 @@ __device__ __forceinline__ void ring_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int MODE, int WBITS, int BM, int WM, int WN>
+// one weight fragment (8 k values of one output column) from its LDS bytes
+template <int MODE, int WBITS>
+__device__ __forceinline__ u32x4 weight_fragment(const uint8_t *bp)
+{
+    if constexpr (WBITS == 4) {
+        const uint32_t w = *(const uint32_t *)bp;
+        return MODE == 1 ? unpack_int4x8_f16(w) : unpack_int4x8_nat(w);
+    } else {
+        const u32x2 w = *(const u32x2 *)bp;
+        return MODE == 1 ? unpack_int8x8_f16(w) : unpack_int8x8_bf16o(w);
+    }
+}
+
+template <int MODE, int WBITS, int BM>
 __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 {
     using C = Ff3<MODE, WBITS, BM>;
-    constexpr int NMAT = C::NMAT, NPLANE = C::NPLANE, BN = C::BN, BKB = C::BKB;
-    constexpr bool F16 = (MODE == 1);           // down: A is f16 h, weights unpack to f16
-    constexpr bool COR = F16 || WBITS == 4;     // the unpacked weights carry a constant offset
-    constexpr int MB = BM / WM / 16;
-    constexpr int NB = BN / WN / 16;
-    static_assert(WM * WN == 4 && MB >= 1 && NB >= 1, "wave tile");
+    constexpr int NMAT = C::NMAT, BN = C::BN, BKB = C::BKB;
+    constexpr bool F16 = (MODE == 1);   // down: A is f16 h, weights unpack to f16
+    constexpr int MB = BM / 16;         // 16-row blocks, all in every wave
+    constexpr int NB = BN / 4 / 16;     // 16-column blocks per wave and matrix
+    constexpr int CB = MB / 4;          // offset-correction blocks per wave
+    static_assert(MB % 4 == 0, "row blocks split evenly over the waves");
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem3[];
+    __shared__ float sCor[BM];
 
     const int NT = a.N / BN;
     const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
@@ -394,27 +410,24 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
     int e, row0, rows;
     if (!find_tile<BM>(a, slot, e, row0, rows)) return;
     const int n0 = nt * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
 
     // this lane's source for each of its wave's copies (fixed across stages)
     const uint8_t *src[C::PER_WAVE];
     int dst[C::PER_WAVE];  // byte offset of the wave's 1 KB block within a stage
 #pragma unroll
     for (int j = 0; j < C::PER_WAVE; ++j) {
-        const int l = wave + 4 * j;  // copy index within the stage
+        const int l = wn + 4 * j;  // copy index within the stage
         dst[j] = l * 1024;
         if (l < C::A_LOADS) {
-            const int pl = l / (BM / 8);
-            const int r = (l % (BM / 8)) * 8 + lane / 8;  // tile row
-            const int slotc = lane % 8;
-            const int chunk = slotc ^ (r & 7);
+            const int r = l * 8 + lane / 8;  // tile row
+            const int chunk = (lane % 8) ^ (r & 7);
             const int rr = r < rows ? r : 0;  // padded rows read row 0 (outputs discarded)
             const int srow = a.gather ? a.gather[row0 + rr] / a.kdiv : row0 + rr;
-            src[j] = (const uint8_t *)a.A + ((size_t)pl * a.M * a.lda + (size_t)srow * a.lda + chunk * 8) * 2;
+            src[j] = (const uint8_t *)a.A + ((size_t)srow * a.lda + chunk * 8) * 2;
         } else {
             const int lb = l - C::A_LOADS;
-            const int cpr = BKB / 16;                  // 16-byte chunks per B row per stage
+            const int cpr = BKB / 16;                     // 16-byte chunks per B row per stage
             const int br = lb * (64 / cpr) + lane / cpr;  // B row within the stage
             const int mat = br / BN, n = br % BN;
             const uint8_t *qm = (mat == 0) ? a.q0 : a.q1;
@@ -425,7 +438,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
         uint8_t *base = smem3 + (kt % FF3_STAGES) * C::STAGE;
 #pragma unroll
         for (int j = 0; j < C::PER_WAVE; ++j) {
-            const int l = wave + 4 * j;
+            const int l = wn + 4 * j;
             const size_t adv = l < C::A_LOADS ? (size_t)kt * FF_BK * 2 : (size_t)kt * BKB;
             lds_copy16(src[j] + adv, base + dst[j]);
         }
@@ -434,18 +447,19 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
     // The products run as W x A^T (weights are the MFMA's first operand), so
     // a lane ends up holding four consecutive output columns of one row.
     f32x4 acc[NMAT][MB][NB];
-    f32x4 cor[MB];
+    f32x4 cor[CB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        cor[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CB; ++c) cor[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int x = 0; x < NMAT; ++x)
+    for (int x = 0; x < NMAT; ++x)
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
             for (int j = 0; j < NB; ++j) acc[x][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // minus the unpack offset, as a constant operand: bf16 -136, f16 -1032 or f16 -1152
-    constexpr uint32_t CW = F16 ? (WBITS == 4 ? 0xE408E408u : 0xE480E480u) : 0xC308C308u;
+    // minus the unpack offset as a constant operand: bf16 -136 / -128, f16 -1032 / -1152
+    constexpr uint32_t CW = F16 ? (WBITS == 4 ? 0xE408E408u : 0xE480E480u) : (WBITS == 4 ? 0xC308C308u : 0xC300C300u);
     const u32x4 cneg = u32x4{CW, CW, CW, CW};
+    auto mma = [](u32x4 x, u32x4 y, f32x4 c) { return F16 ? mfma_f16(x, y, c) : mfma_bf16(x, y, c); };
 
     const int KT = a.K / FF_BK;
 #pragma unroll
@@ -461,52 +475,41 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
         const uint8_t *sb = sa + C::A_BYTES;
 #pragma unroll
         for (int ks = 0; ks < FF_BK / 32; ++ks) {
-            u32x4 af[NPLANE][MB];
+            u32x4 af[MB];
 #pragma unroll
-            for (int pl = 0; pl < NPLANE; ++pl)
+            for (int i = 0; i < MB; ++i) {
+                const int r = i * 16 + (lane & 15);
+                const int chunk = ks * 4 + (lane >> 4);
+                af[i] = *(const u32x4 *)(sa + r * 128 + ((chunk ^ (r & 7)) * 16));
+            }
+            // (the correction blocks depend on the wave, so their fragments
+            // are read again rather than picked from af by a run-time index)
 #pragma unroll
-                for (int i = 0; i < MB; ++i) {
-                    const int r = wm * (BM / WM) + i * 16 + (lane & 15);
-                    const int chunk = ks * 4 + (lane >> 4);
-                    u32x4 v = *(const u32x4 *)(sa + pl * BM * FF_BK * 2 + r * 128 + ((chunk ^ (r & 7)) * 16));
-                    if (WBITS == 4 && MODE != 1) v = interleave_bf16x8(v);
-                    af[pl][i] = v;
-                }
-            if (COR) {
-#pragma unroll
-                for (int pl = 0; pl < NPLANE; ++pl)
-#pragma unroll
-                    for (int i = 0; i < MB; ++i)
-                        cor[i] = F16 ? mfma_f16(cneg, af[pl][i], cor[i]) : mfma_bf16(cneg, af[pl][i], cor[i]);
+            for (int c = 0; c < CB; ++c) {
+                const int r = (wn + 4 * c) * 16 + (lane & 15);
+                const int chunk = ks * 4 + (lane >> 4);
+                cor[c] = mma(cneg, *(const u32x4 *)(sa + r * 128 + ((chunk ^ (r & 7)) * 16)), cor[c]);
             }
 #pragma unroll
             for (int x = 0; x < NMAT; ++x)
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    const uint8_t *bp = sb + (x * BN + wn * (BN / WN) + j * 16 + (lane & 15)) * BKB;
-                    u32x4 bf;
-                    if (WBITS == 4) {
-                        const uint32_t w = *(const uint32_t *)(bp + ks * 16 + (lane >> 4) * 4);
-                        bf = F16 ? unpack_int4x8_f16(w) : unpack_int4x8(w);
-                    } else {
-                        const u32x2 w = *(const u32x2 *)(bp + ks * 32 + (lane >> 4) * 8);
-                        bf = F16 ? unpack_int8x8_f16(w) : unpack_int8x8(w);
-                    }
+                    const uint8_t *bp = sb + (x * BN + wn * (BN / 4) + j * 16 + (lane & 15)) * BKB;
+                    const u32x4 bf = weight_fragment<MODE, WBITS>(bp + ks * (BKB / 2) + (lane >> 4) * (WBITS / 2) * 2);
 #pragma unroll
-                    for (int pl = 0; pl < NPLANE; ++pl)
-#pragma unroll
-                        for (int i = 0; i < MB; ++i)
-                            acc[x][i][j] = F16 ? mfma_f16(bf, af[pl][i], acc[x][i][j])
-                                               : mfma_bf16(bf, af[pl][i], acc[x][i][j]);
+                    for (int i = 0; i < MB; ++i) acc[x][i][j] = mma(bf, af[i], acc[x][i][j]);
                 }
         }
     }
 
-    // Epilogue.  Lane l holds, for block (i, j), row m = l % 16 of the block
-    // and its columns 4 (l / 16) .. 4 (l / 16) + 3; cor[i] carries minus the
-    // unpack offset times the row sum in every element (0 for int8 gate/up).
-    const int mloc = wm * (BM / WM) + (lane & 15);
-    const int nloc = wn * (BN / WN) + 4 * (lane >> 4);
+    // Epilogue.  Lane l holds, for block (i, j), row m = 16 i + l % 16 and the
+    // columns 4 (l / 16) .. 4 (l / 16) + 3 of its 16 x 16 block; the offset
+    // correction of every row comes back from sCor.
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+        if (lane < 16) sCor[(wn + 4 * c) * 16 + lane] = cor[c][0];
+    const int mloc = lane & 15;
+    const int nloc = wn * (BN / 4) + 4 * (lane >> 4);
     const size_t sbase = (size_t)e * a.sstride + n0 + nloc;
     if constexpr (MODE == 0) {
         // h = silu(g) * u in f16, staged in LDS in natural column order
@@ -520,11 +523,11 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
             sg[j] = *(const f32x4 *)(a.s0 + sbase + j * 16);
             su[j] = *(const f32x4 *)(a.s1 + sbase + j * 16);
         }
-        __syncthreads();  // every wave is done reading the stage ring
+        __syncthreads();  // every wave is done reading the stage ring; sCor is complete
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-            const float c = cor[i][0];
-            uint8_t *hrow = smem3 + (mloc + i * 16) * HP + nloc * 2;
+            const float c = sCor[i * 16 + mloc];
+            uint8_t *hrow = smem3 + (i * 16 + mloc) * HP + nloc * 2;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 float h[4];
@@ -552,12 +555,13 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 #pragma unroll
             for (int j = 0; j < NB; ++j) sv[j] = *(const f32x4 *)(a.s0 + sbase + j * 16);
         }
+        __syncthreads();  // sCor is complete
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-            const int m = mloc + i * 16;
+            const int m = i * 16 + mloc;
             if (m >= rows) continue;
             const int row = row0 + m;
-            const float c = cor[i][0];
+            const float c = sCor[m];
             float *o = (float *)a.out + (size_t)row * a.ldo + n0 + nloc;
             if constexpr (MODE == 2) {
 #pragma unroll
@@ -595,14 +599,14 @@ static hipError_t launch_one(const FfnArgs &a, int slots, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int MODE, int WBITS, int BM, int WM, int WN>
+template <int MODE, int WBITS, int BM>
 static hipError_t launch_three(const FfnArgs &a, int slots, hipStream_t st)
 {
     const int NT = a.N / 128;
     const long grid = (long)((slots + 7) / 8 * 8) * NT;
     if (grid <= 0) return hipSuccess;
     const size_t lds = (size_t)FF3_STAGES * Ff3<MODE, WBITS, BM>::STAGE;
-    hipLaunchKernelGGL((k_ffn3<MODE, WBITS, BM, WM, WN>), dim3((unsigned)grid), dim3(256), lds, st, a);
+    hipLaunchKernelGGL((k_ffn3<MODE, WBITS, BM>), dim3((unsigned)grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
@@ -617,8 +621,8 @@ static hipError_t launch_mode(const FfnArgs &a, int rows_total, int groups, hipS
     const int slots = (rows_total + bm - 1) / bm + (a.offsets ? min(ng, rows_total) : 0);
     if (a.N % 128 == 0) {
         if (bm == 16) return launch_one<MODE, WBITS, 16, 128, 1, 4>(a, slots, st);
-        if (bm == 64) return launch_three<MODE, WBITS, 64, 2, 2>(a, slots, st);
-        return launch_three<MODE, WBITS, 128, 2, 2>(a, slots, st);
+        if (bm == 64) return launch_three<MODE, WBITS, 64>(a, slots, st);
+        return launch_three<MODE, WBITS, 128>(a, slots, st);
     }
     if (bm == 16) return launch_one<MODE, WBITS, 16, 64, 1, 4>(a, slots, st);
     if (bm == 64) return launch_one<MODE, WBITS, 64, 64, 2, 2>(a, slots, st);

@@ -81,6 +81,42 @@ __device__ __forceinline__ u32x4 unpack_int4x8(uint32_t w)
     return r;
 }
 
+// Natural k order forms for bf16 operands whose activations are not
+// reordered (k-slot pairs (e0,e1),(e2,e3),(e4,e5),(e6,e7)):
+//  - int4: byte j of w and of w >> 4 hold nibbles 2j and 2j+1 in their low
+//    bits; a byte permute places them in the two halves, then the same bit
+//    operation as unpack_int4x8 gives q + 136;
+//  - int8: b = q + 128 (bit 7 flipped) converted byte-wise to f32 is exact,
+//    and so are its upper halves as bf16; the caller removes 128 * (row sum).
+constexpr float INT8_BF16_BIAS = 128.0f;
+
+__device__ __forceinline__ u32x4 unpack_int4x8_nat(uint32_t w)
+{
+    const uint32_t u = w >> 4;
+    u32x4 r;
+    // selector: byte 0 <- byte j of w, byte 2 <- byte j of u, bytes 1 and 3 <- 0
+    r[0] = ((__builtin_amdgcn_perm(u, w, 0x0C040C00u) ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
+    r[1] = ((__builtin_amdgcn_perm(u, w, 0x0C050C01u) ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
+    r[2] = ((__builtin_amdgcn_perm(u, w, 0x0C060C02u) ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
+    r[3] = ((__builtin_amdgcn_perm(u, w, 0x0C070C03u) ^ 0x00080008u) & 0x000F000Fu) | 0x43004300u;
+    return r;
+}
+
+__device__ __forceinline__ u32x4 unpack_int8x8_bf16o(u32x2 w)
+{
+    u32x4 r;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const uint32_t t = w[d] ^ 0x80808080u;
+        const float f0 = (float)(t & 0xFFu), f1 = (float)((t >> 8) & 0xFFu);
+        const float f2 = (float)((t >> 16) & 0xFFu), f3 = (float)(t >> 24);
+        // the upper halves of (f0, f1) and of (f2, f3)
+        r[2 * d] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+        r[2 * d + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+    }
+    return r;
+}
+
 // f16 forms of the same unpacks, for the down GEMM, whose activations h are
 // f16.  The f16 with bit pattern 0x6400 | m is exactly 1024 + m for m < 1024:
 //  - int4: nibble n = q + 8 gives q + 1032, k-slot order as unpack_int4x8;
