@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--roofline-reps", type=int, default=20)
+    ap.add_argument("--quantize", action="store_true",
+                    help="time the per-row int4 quantiser on the GLM-class routed gate/up weights instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB, 5 times (counter calibration), and exit")
     return ap.parse_args()
@@ -94,6 +96,8 @@ def main():
     moe.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.quantize:
+        return bench_quantize(args, moe, torch, np)
     cfg = synth.CONFIGS[args.config]
     if cfg.T > 32:
         return bench_prefill(args, cfg, moe, synth, torch, np, dev)
@@ -246,6 +250,61 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    print(json.dumps(line), flush=True)
+
+
+def bench_quantize(args, moe, torch, np):
+    """The step before the path: per-row symmetric int4 quantisation of the
+    GLM-class layer's routed gate and up weights (256 experts x 2 x 2048 rows
+    of 6144) from bf16, N(0, s^2) rows with s ~ U(0.005, 0.05), seeded on the
+    device.  One step = the whole family."""
+    rows, cols = 256 * 2 * 2048, 6144
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1300)
+    src = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, 65536):
+        sd = torch.empty(65536, 1, device="cuda").uniform_(0.005, 0.05, generator=g)
+        src[r0:r0 + 65536] = (torch.randn(65536, cols, device="cuda", generator=g) * sd).to(torch.bfloat16)
+    q = torch.empty(rows, cols // 2, dtype=torch.uint8, device="cuda")
+    qs = torch.empty(rows, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        moe.moe_quantize_rows(src, 4, q, qs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        moe.moe_quantize_rows(src, 4, q, qs)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    alg = rows * cols * 2 + rows * cols // 2 + rows * 4
+    gbs = alg / (ms * 1e-3) / 1e9
+    line = {"metric": "per-row int4 quantiser throughput (bf16 source -> packed int4 + f32 scales)",
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32 arithmetic on bf16 input", "data": "synthetic (seeded on the device)",
+            "config": {"workload": "GLM-class routed gate+up family: 1048576 rows x 6144, bf16", "rows": rows,
+                       "cols": cols, "bits": 4},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "k_quantize_rows<bf16,4>", "avg_launch_us": round(ms * 1e3, 2),
+                         "alg_bytes_per_launch": alg}}
+    if not args.no_cpu_baseline:
+        import oracle
+        n = 2048
+        sample = src[:n].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            oracle.quantize_rows(sample, 4)
+            done += n
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(done * (cols * 2 + cols // 2 + 4) / dt / 1e9, 3), "unit": "GB/s",
+                                "cores": oracle.num_threads(), "kind": "oracle",
+                                "sample": f"the first {n} rows, {done // n} passes in {dt:.1f} s, C oracle, OpenMP over rows"}
     print(json.dumps(line), flush=True)
 
 

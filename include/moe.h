@@ -222,6 +222,34 @@ const char *moe_status_string(int status);
 int moe_layer_routing(const moe_shape *shape, void *ws, size_t ws_bytes, int32_t **topk_ids, float **topk_w,
                       int32_t **offsets, int32_t **sorted_pairs);
 
+/* ---- the step before the path: the per-row symmetric quantiser and packer ----
+ *
+ * moe_quantize_rows turns `rows` rows of `cols` values into the container
+ * format the layer reads: per-row symmetric codes with one f32 scale per row
+ * in a sibling .qs array (colibri-nano README, "Converting a checkpoint
+ * yourself"; colibri README, "What's implemented": int8 and packed int4
+ * quantisation kernels with per-row scales).  The pages give no formula; per
+ * row, with qmax = 7 (bits 4) or 127 (bits 8):
+ *   scale = max|w| / qmax                 (f32, correctly rounded)
+ *   code  = clamp(nearest integer to w / scale, ties to even, -qmax, qmax)
+ * and an all-zero row gets scale 0 and codes 0.  Inputs must be finite.
+ *
+ *   src         device, [rows][cols], f32 (src_format MOE_SRC_F32) or bf16
+ *               bits (MOE_SRC_BF16), row-major, no padding
+ *   q           device, [rows][cols/2] bytes for bits 4 (element 2c in the low
+ *               nibble of byte c, two's complement; cols must be even) or
+ *               [rows][cols] int8 for bits 8
+ *   qs          device, [rows] f32 scales
+ * The caller owns every buffer; the call only enqueues on `stream`.
+ * Returns MOE_OK (rows == 0 is a no-op), MOE_ERR_SHAPE (rows < 0, cols <= 0,
+ * bits not 4 or 8, odd cols for bits 4, unknown src_format), MOE_ERR_NULL,
+ * MOE_ERR_ALIGN (src or qs not aligned to its element size) or MOE_ERR_HIP.
+ * 16-byte aligned rows with cols % 8 == 0 take the vector path. */
+#define MOE_SRC_F32 0
+#define MOE_SRC_BF16 1
+int moe_quantize_rows(const void *src, int32_t src_format, int64_t rows, int32_t cols, int32_t bits, void *q,
+                      float *qs, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

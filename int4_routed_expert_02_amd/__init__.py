@@ -6,7 +6,8 @@ library is missing, every call raises -- there is no CPU fallback.
 
 The functions mirror the C ABI names:
   moe_router, moe_permute, moe_expert_ffn, moe_combine, moe_layer_forward,
-  moe_workspace_bytes, moe_validate_shape, moe_status_string, moe_layer_routing
+  moe_workspace_bytes, moe_validate_shape, moe_status_string, moe_layer_routing,
+  moe_quantize_rows
 and ``MoeLayer`` keeps one layer's device weights and workspace.
 """
 from __future__ import annotations
@@ -33,13 +34,16 @@ MOE_TEST_GATEUP_SUMS = 0x100
 MOE_STAGE_GATEUP_ONLY = 0x200
 MOE_STAGE_EXPERTS_ONLY = 0x400
 
+MOE_SRC_F32 = 0
+MOE_SRC_BF16 = 1
+
 MOE_WS_PERMUTE = 1
 MOE_WS_EXPERT_FFN = 2
 MOE_WS_LAYER = 3
 
 EXPORTS = ["moe_router", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_profiled", "moe_workspace_bytes", "moe_validate_shape", "moe_status_string",
-           "moe_layer_routing"]
+           "moe_layer_routing", "moe_quantize_rows"]
 
 
 class MoeShape(ctypes.Structure):
@@ -89,6 +93,7 @@ def load() -> ctypes.CDLL:
             "moe_layer_forward_profiled": [S, W, vp, vp, vp, sz, vp, vp, vp],
             "moe_validate_shape": [S],
             "moe_layer_routing": [S, vp, sz, vp, vp, vp, vp],
+            "moe_quantize_rows": [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -190,6 +195,26 @@ def moe_layer_routing(sh: MoeShape, ws):
     _check(load().moe_layer_routing(ctypes.byref(sh), _ptr(ws), ws.numel(), *[ctypes.byref(x) for x in p]),
            "moe_layer_routing")
     return [x.value for x in p]
+
+
+def moe_quantize_rows(src, bits: int, q=None, qs=None, stream=None):
+    """Per-row symmetric quantiser (include/moe.h): src a 2-D float32 or
+    bfloat16 GPU tensor.  Allocates the outputs when not given and returns
+    (q, qs): q uint8 [rows][cols/2] (packed int4) or int8 [rows][cols], qs
+    float32 [rows]."""
+    import torch
+    if src.dim() != 2 or src.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("src must be a 2-D float32 or bfloat16 tensor")
+    rows, cols = src.shape
+    if q is None:
+        q = torch.empty((rows, cols // 2) if bits == 4 else (rows, cols),
+                        dtype=torch.uint8 if bits == 4 else torch.int8, device=src.device)
+    if qs is None:
+        qs = torch.empty(rows, dtype=torch.float32, device=src.device)
+    fmt = MOE_SRC_BF16 if src.dtype == torch.bfloat16 else MOE_SRC_F32
+    _check(load().moe_quantize_rows(_ptr(src), fmt, rows, cols, bits, _ptr(q), _ptr(qs), _stream(stream)),
+           "moe_quantize_rows")
+    return q, qs
 
 
 def qmat(q, qs, q_stride_bytes: int = 0, qs_stride_floats: int = 0, q_offset: int = 0, qs_offset: int = 0) -> MoeQMat:

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_hip.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["moe_api.hip", "router.hip", "permute.hip", "ffn.hip", "combine.hip", "decode.hip"]
+SOURCES = ["moe_api.hip", "router.hip", "permute.hip", "ffn.hip", "combine.hip", "decode.hip", "quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC,

@@ -419,6 +419,19 @@ int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const m
                                           s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, hs));
 }
 
+int moe_quantize_rows(const void *src, int32_t src_format, int64_t rows, int32_t cols, int32_t bits, void *q,
+                      float *qs, void *stream)
+{
+    if (rows < 0 || cols <= 0 || (bits != 4 && bits != 8) || (bits == 4 && cols % 2) ||
+        (src_format != MOE_SRC_F32 && src_format != MOE_SRC_BF16))
+        return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!src || !q || !qs) return MOE_ERR_NULL;
+    if (!aligned(src, src_format == MOE_SRC_BF16 ? 2 : 4) || !aligned(qs, 4)) return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_quantize(src, src_format == MOE_SRC_BF16, (long)rows, cols, bits, q, qs,
+                                           (hipStream_t)stream));
+}
+
 int moe_layer_routing(const moe_shape *s, void *ws, size_t ws_bytes, int32_t **topk_ids, float **topk_w,
                       int32_t **offsets, int32_t **sorted_pairs)
 {

@@ -82,6 +82,7 @@ def lib():
             "oracle_layer_forward_dense": ([S, W, vp, vp], ctypes.c_int),
             "oracle_gateup_int_sums": ([S, vp, W, vp, vp, vp, vp], ctypes.c_int),
             "oracle_num_threads": ([], ctypes.c_int),
+            "oracle_quantize_rows": ([vp, i32, ctypes.c_int64, i32, i32, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -268,6 +269,21 @@ def bf16_to_f32(bits: int) -> float:
 
 def f32_to_bf16(f: float) -> int:
     return int(lib().oracle_f32_to_bf16(f))
+
+
+def quantize_rows(src: np.ndarray, bits: int):
+    """Per-row symmetric quantiser: src [rows][cols] f32, or uint16 holding bf16
+    bits.  Returns (codes, scales): codes uint8 [rows][cols/2] packed int4 or
+    int8 [rows][cols]; scales f32 [rows]."""
+    src = np.ascontiguousarray(src)
+    if src.ndim != 2 or src.dtype not in (np.float32, np.uint16):
+        raise ValueError("src must be a 2-D float32 or uint16 (bf16 bits) array")
+    rows, cols = src.shape
+    q = np.zeros((rows, cols // 2) if bits == 4 else (rows, cols), dtype=np.uint8 if bits == 4 else np.int8)
+    qs = np.zeros(rows, dtype=np.float32)
+    _chk(lib().oracle_quantize_rows(_p(src), 1 if src.dtype == np.uint16 else 0, rows, cols, bits, _p(q), _p(qs)),
+         "oracle_quantize_rows")
+    return q, qs
 
 
 def num_threads() -> int:

@@ -89,6 +89,63 @@ void oracle_dequant_row(const void *q, int32_t bits, const float *scale, int32_t
     }
 }
 
+/* ---------------------------------------------------------------- quantiser */
+
+/* See oracle_moe.h for the reading.  Rows are independent, so they are split
+ * across threads; each row is done in column order. */
+int oracle_quantize_rows(const void *src, int32_t src_bf16, int64_t rows, int32_t cols, int32_t bits, void *q,
+                         float *qs)
+{
+    if (rows < 0 || cols <= 0 || (bits != 4 && bits != 8) || (bits == 4 && cols % 2)) return O_ERR_SHAPE;
+    if (rows == 0) return O_OK;
+    if (!src || !q || !qs) return O_ERR_NULL;
+    const float qmax = (bits == 4) ? 7.0f : 127.0f;
+    const int64_t row_bytes = (bits == 4) ? cols / 2 : cols;
+    int failed = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float *w = (float *)malloc((size_t)cols * sizeof(float));
+        int32_t *code = (int32_t *)malloc((size_t)cols * sizeof(int32_t));
+        if (!w || !code) {
+            free(w);
+            free(code);
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        /* the row in f32 */
+        for (int32_t c = 0; c < cols; ++c)
+            w[c] = src_bf16 ? oracle_bf16_to_f32(((const uint16_t *)src)[r * cols + c])
+                            : ((const float *)src)[r * cols + c];
+        /* its largest magnitude and the scale */
+        float amax = 0.0f;
+        for (int32_t c = 0; c < cols; ++c)
+            if (fabsf(w[c]) > amax) amax = fabsf(w[c]);
+        const float scale = amax / qmax;
+        /* the codes: nearest integer, ties to even, inside [-qmax, qmax] */
+        for (int32_t c = 0; c < cols; ++c) {
+            if (amax == 0.0f) {
+                code[c] = 0;
+                continue;
+            }
+            float v = nearbyintf(w[c] / scale);
+            if (v > qmax) v = qmax;
+            if (v < -qmax) v = -qmax;
+            code[c] = (int32_t)v;
+        }
+        qs[r] = scale;
+        if (bits == 4) {
+            oracle_pack_int4_row(code, cols, (uint8_t *)q + r * row_bytes);
+        } else {
+            int8_t *out = (int8_t *)q + r * row_bytes;
+            for (int32_t c = 0; c < cols; ++c) out[c] = (int8_t)code[c];
+        }
+        free(w);
+        free(code);
+    }
+    return failed ? O_ERR_NOMEM : O_OK;
+}
+
 /* row r of expert e of a matrix family with `cols` columns */
 static const void *qrow(const oracle_qmat *m, int32_t bits, int32_t e, int64_t r, int32_t cols)
 {

@@ -119,6 +119,24 @@ int oracle_layer_forward_dense(const oracle_shape *sh, const oracle_weights *wt,
 int oracle_gateup_int_sums(const oracle_shape *sh, const uint16_t *hidden, const oracle_weights *wt,
                            const int32_t *offsets, const int32_t *sorted, double *g, double *u);
 
+/* Per-row symmetric quantiser (colibri-nano README, "Converting a checkpoint
+ * yourself": per-row symmetric quantisation with f32 scales in a sibling .qs
+ * tensor; colibri README, "What's implemented": int8 and packed int4
+ * quantisation kernels with per-row scales).  The pages give no formula; the
+ * plain reading taken here, per row of `cols` values w (f32, or bf16 widened
+ * exactly when src_bf16 != 0):
+ *   amax  = max |w|                        (exact)
+ *   scale = amax / qmax                    (f32 division, round to nearest
+ *                                           even; qmax = 7 for int4, 127 for
+ *                                           int8)
+ *   q     = clamp(rint(w / scale), -qmax, qmax)   (f32 division, then round
+ *                                           half to even, as numpy does)
+ * An all-zero row gets scale 0 and codes 0.  Codes are stored in the packed
+ * layout of oracle_pack_int4_row (int4, cols even, rows of cols/2 bytes) or as
+ * int8 rows.  Inputs must be finite.  Returns 0, or -2 for a bad shape. */
+int oracle_quantize_rows(const void *src, int32_t src_bf16, int64_t rows, int32_t cols, int32_t bits, void *q,
+                         float *qs);
+
 int oracle_num_threads(void);
 
 #ifdef __cplusplus

@@ -143,3 +143,23 @@ def test_product_path_has_no_fallback(moe, tmp_path, monkeypatch):
     src = open(os.path.join(ROOT, "int4_routed_expert_02_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("oracle_", "")
     assert "import oracle" not in src
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(rows=-1), -2),
+    (dict(cols=0), -2),
+    (dict(bits=5), -2),
+    (dict(bits=4, cols=7), -2),
+    (dict(fmt=2), -2),
+    (dict(rows=0), 0),
+    (dict(src=None), -1),
+    (dict(qs=None), -1),
+    (dict(src=FAKE + 2, fmt=0), -5),
+    (dict(src=FAKE + 1, fmt=1), -5),
+    (dict(qs=FAKE + 2), -5),
+])
+def test_quantize_rows_validation(moe, args, code):
+    a = dict(src=FAKE, fmt=0, rows=4, cols=16, bits=4, q=FAKE, qs=FAKE)
+    a.update(args)
+    assert moe.load().moe_quantize_rows(a["src"], a["fmt"], a["rows"], a["cols"], a["bits"], a["q"], a["qs"],
+                                        None) == code

@@ -340,6 +340,106 @@ def test_integer_sums_exact(synth_mod, oracle_mod):
         assert np.array_equal(u[r], (qu @ xi[t]).astype(np.float64))
 
 
+# ------------------------------------------------------------------ quantiser (NEXT-2)
+# Per-row symmetric quantisation with one f32 scale per row (colibri-nano
+# README, "Converting a checkpoint yourself"); the codes are the nearest
+# integer multiples of the scale, ties to even (numpy's rounding, which the
+# pages' converter uses), and the scale maps the row's largest magnitude to
+# the largest code.
+
+QMAX = {4: 7, 8: 127}
+
+
+def _codes(oracle_mod, q, bits, cols):
+    if bits == 4:
+        return np.stack([oracle_mod.unpack_int4_row(r, cols) for r in q])
+    return q.astype(np.int32)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantizer_zero_rows(oracle_mod, bits):
+    src = np.zeros((3, 10), np.float32)
+    src[1, 3] = -0.0
+    q, s = oracle_mod.quantize_rows(src, bits)
+    assert np.all(s == 0) and np.all(_codes(oracle_mod, q, bits, 10) == 0)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantizer_exact_round_trip(oracle_mod, bits):
+    # codes with one +-qmax per row and scales m * 2^e (m odd, 5 bits): every
+    # product q * s, and amax / qmax = s, is exact in f32, so quantising the
+    # dequantised row must return the same codes and the same scale bits
+    rng = np.random.default_rng(11)
+    qm = QMAX[bits]
+    rows, cols = 40, 34
+    codes = rng.integers(-qm, qm + 1, size=(rows, cols))
+    codes[np.arange(rows), rng.integers(0, cols, rows)] = qm * rng.choice([-1, 1], rows)
+    scales = (rng.integers(0, 16, rows) * 2 + 1) * np.exp2(rng.integers(-14, 2, rows))
+    src = (codes * scales[:, None]).astype(np.float32)
+    assert np.array_equal(src.astype(np.float64), codes * scales[:, None])  # exact
+    q, s = oracle_mod.quantize_rows(src, bits)
+    assert np.array_equal(s, scales.astype(np.float32))
+    assert np.array_equal(_codes(oracle_mod, q, bits, cols), codes)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantizer_ties_go_to_even(oracle_mod, bits):
+    qm = QMAX[bits]
+    halves = np.arange(-qm, qm) + 0.5  # every half-way point inside the range
+    want = np.where(np.floor(halves) % 2 == 0, np.floor(halves), np.ceil(halves))
+    row = np.concatenate([[qm], halves]) * 0.125  # a power-of-two scale keeps them exact
+    if len(row) % 2:
+        row = np.concatenate([row, [0.0]])
+        want = np.concatenate([want, [0.0]])
+    q, s = oracle_mod.quantize_rows(row[None, :].astype(np.float32), bits)
+    assert s[0] == np.float32(0.125)
+    got = _codes(oracle_mod, q, bits, len(row))[0]
+    assert got[0] == qm and np.array_equal(got[1:], want)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantizer_nearest_code_brute_force(oracle_mod, bits):
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    qm = QMAX[bits]
+    src = (rng.standard_normal((6, 64)) * rng.uniform(0.01, 3.0, (6, 1))).astype(np.float32)
+    q, s = oracle_mod.quantize_rows(src, bits)
+    codes = _codes(oracle_mod, q, bits, 64)
+    for r in range(src.shape[0]):
+        amax = np.max(np.abs(src[r]))
+        assert s[r] == np.float32(amax) / np.float32(qm)  # the scale's definition, one f32 division
+        S = Fraction(float(s[r]))
+        for c in range(64):
+            w = Fraction(float(src[r, c]))
+            dist = sorted((abs(w - k * S), k) for k in range(-qm, qm + 1))
+            if dist[1][0] - dist[0][0] < Fraction(1, 10**6) * S:
+                continue  # (an exact tie or a near one; the tie rule has its own pin)
+            assert codes[r, c] == dist[0][1], (r, c)
+        assert np.max(np.abs(codes[r])) == qm
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quantizer_sign_and_power_of_two_scaling(oracle_mod, bits):
+    rng = np.random.default_rng(9)
+    src = rng.standard_normal((5, 48)).astype(np.float32)
+    q, s = oracle_mod.quantize_rows(src, bits)
+    qn, sn = oracle_mod.quantize_rows(-src, bits)
+    q4, s4 = oracle_mod.quantize_rows(src * np.float32(4.0), bits)
+    c, cn, c4 = (_codes(oracle_mod, a, bits, 48) for a in (q, qn, q4))
+    assert np.array_equal(sn, s) and np.array_equal(cn, -c)
+    assert np.array_equal(s4, s * 4) and np.array_equal(c4, c)
+
+
+def test_quantizer_bf16_input_is_its_widened_value(oracle_mod):
+    rng = np.random.default_rng(3)
+    bits16 = (rng.standard_normal((4, 40)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    widened = (bits16.astype(np.uint32) << 16).view(np.float32)
+    for b in (4, 8):
+        qa, sa = oracle_mod.quantize_rows(bits16, b)
+        qb, sb = oracle_mod.quantize_rows(widened, b)
+        assert np.array_equal(qa, qb) and np.array_equal(sa, sb)
+
+
 def test_thread_count_does_not_change_bits(synth_mod, oracle_mod, tmp_path):
     code = ("import sys, numpy as np; sys.path.insert(0, %r); import synth, oracle;"
             "cfg = synth.CONFIGS['c0'];"
