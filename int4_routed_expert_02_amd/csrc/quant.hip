@@ -7,20 +7,37 @@
 // quantisation kernels with per-row scales).  The pages give no formula; the
 // reading used here: scale = max|w| / qmax (qmax = 7 for int4, 127 for int8),
 // code = the nearest integer to w / scale with ties to even, clamped to
-// [-qmax, qmax]; an all-zero row gets scale 0 and codes 0.  Both divisions
-// are correctly rounded f32 (__fdiv_rn) and the rounding is v_rndne, so each
-// code is decided exactly as a plain f32 implementation decides it.  Int4
+// [-qmax, qmax]; an all-zero row gets scale 0 and codes 0.  The scale is a
+// correctly rounded f32 division and every code equals the nearest integer
+// (v_rndne, ties to even) of the correctly rounded quotient, so each code is
+// decided exactly as a plain f32 implementation decides it (see qz_code).  Int4
 // packing: element 2c in the low nibble of byte c, two's complement.
 //
-// One wave per row, four rows per workgroup.  The row is read twice (its
-// maximum, then its codes; the second pass mostly hits the cache) and its
-// codes written once: HBM-bound.
+// One wave per row, four rows per workgroup, HBM-bound.  Rows of up to
+// 64 x QZ_RG groups of eight values are read once: each lane keeps its groups
+// in registers while the row maximum is reduced.  Longer or unaligned rows
+// are read twice (maximum, then codes).
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace moe {
 
 constexpr int QZ_ROWS = 4;  // rows (waves) per workgroup
+constexpr int QZ_RG = 16;   // register-held groups of eight values per lane (rows up to 8192)
+
+// The code of w: the nearest integer to the correctly rounded quotient w /
+// scale (ties to even), clamped to [-qmax, qmax].  t = w * inv (inv the
+// correctly rounded 1 / scale) is within 1.5 * 2^-23 * |t| <= 2.3e-5 of that
+// quotient for |t| <= 127.5, so rint(t) is the same integer unless t lies
+// within that distance of a half-integer; there (about one value in 8000)
+// the correctly rounded division decides.
+__device__ __forceinline__ uint32_t qz_code(float w, float scale, float inv, float qmax)
+{
+    const float t = w * inv;
+    float k = rintf(t);
+    if (fabsf(fabsf(t - k) - 0.5f) < 0x1p-14f) k = rintf(__fdiv_rn(w, scale));
+    return (uint32_t)(int)fminf(fmaxf(k, -qmax), qmax);
+}
 
 template <bool BF16>
 __device__ __forceinline__ float qz_load1(const void *src, size_t i)
@@ -64,6 +81,84 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const void *__restrict__ 
     const size_t base = (size_t)r * cols;
     const int ng = vec ? cols / 8 : 0;  // groups of eight on the vector path
     const int tail0 = ng * 8;
+    uint8_t *qrow = q + (size_t)r * (BITS == 4 ? cols / 2 : cols);
+
+    if (vec && ng <= WAVE * QZ_RG) {
+        // one pass: group g = lane + 64 j stays in registers (raw bits)
+        constexpr int RW = BF16 ? 4 : 8;  // 32-bit words per group
+        uint32_t raw[QZ_RG][RW];
+#pragma unroll
+        for (int j = 0; j < QZ_RG; ++j) {
+            const int g = lane + WAVE * j;
+            if (g < ng) {
+                if constexpr (BF16) {
+                    const u32x4 d = *(const u32x4 *)((const uint16_t *)src + base + (size_t)g * 8);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) raw[j][w] = d[w];
+                } else {
+                    const u32x4 a = *(const u32x4 *)((const float *)src + base + (size_t)g * 8);
+                    const u32x4 b = *(const u32x4 *)((const float *)src + base + (size_t)g * 8 + 4);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        raw[j][w] = a[w];
+                        raw[j][4 + w] = b[w];
+                    }
+                }
+            }
+        }
+        auto values = [&](int j, float (&v)[8]) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                if constexpr (BF16) {
+                    v[2 * w] = bf16_lo(raw[j][w]);
+                    v[2 * w + 1] = bf16_hi(raw[j][w]);
+                } else {
+                    v[w] = __uint_as_float(raw[j][w]);
+                    v[4 + w] = __uint_as_float(raw[j][4 + w]);
+                }
+            }
+        };
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < QZ_RG; ++j) {
+            if (lane + WAVE * j < ng) {
+                float v[8];
+                values(j, v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
+        const float scale = __fdiv_rn(amax, QMAX);
+        const float inv = __frcp_rn(scale);
+        if (lane == 0) qs[r] = scale;
+#pragma unroll
+        for (int j = 0; j < QZ_RG; ++j) {
+            const int g = lane + WAVE * j;
+            if (g >= ng) continue;
+            float v[8];
+            values(j, v);
+            uint32_t c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = amax == 0.0f ? 0u : qz_code(v[i], scale, inv, QMAX);
+            if constexpr (BITS == 4) {
+                uint32_t p = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) p |= (c[i] & 0xFu) << (4 * i);
+                *(uint32_t *)(qrow + (size_t)g * 4) = p;
+            } else {
+                uint32_t p0 = 0, p1 = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p0 |= (c[i] & 0xFFu) << (8 * i);
+                    p1 |= (c[4 + i] & 0xFFu) << (8 * i);
+                }
+                *(u32x2 *)(qrow + (size_t)g * 8) = u32x2{p0, p1};
+            }
+        }
+        return;
+    }
 
     float amax = 0.0f;
     for (int g = lane; g < ng; g += WAVE) {
@@ -77,14 +172,10 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const void *__restrict__ 
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
 
     const float scale = __fdiv_rn(amax, QMAX);
+    const float inv = __frcp_rn(scale);
     if (lane == 0) qs[r] = scale;
-    auto code = [&](float w) -> uint32_t {
-        if (amax == 0.0f) return 0u;
-        const float v = fminf(fmaxf(rintf(__fdiv_rn(w, scale)), -QMAX), QMAX);
-        return (uint32_t)(int)v;
-    };
+    auto code = [&](float w) -> uint32_t { return amax == 0.0f ? 0u : qz_code(w, scale, inv, QMAX); };
 
-    uint8_t *qrow = q + (size_t)r * (BITS == 4 ? cols / 2 : cols);
     for (int g = lane; g < ng; g += WAVE) {
         float v[8];
         qz_load8<BF16>(src, base + (size_t)g * 8, v);
