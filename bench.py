@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--quantize", action="store_true",
                     help="time the per-row int4 quantiser on the GLM-class routed gate/up weights instead")
+    ap.add_argument("--bias-update", action="store_true",
+                    help="time the aux-loss-free bias update (E = 256) instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB, 5 times (counter calibration), and exit")
     return ap.parse_args()
@@ -98,6 +100,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.quantize:
         return bench_quantize(args, moe, torch, np)
+    if args.bias_update:
+        return bench_bias_update(args, moe, torch, np)
     cfg = synth.CONFIGS[args.config]
     if cfg.T > 32:
         return bench_prefill(args, cfg, moe, synth, torch, np, dev)
@@ -305,6 +309,47 @@ def bench_quantize(args, moe, torch, np):
         line["cpu_baseline"] = {"value": round(done * (cols * 2 + cols // 2 + 4) / dt / 1e9, 3), "unit": "GB/s",
                                 "cores": oracle.num_threads(), "kind": "oracle",
                                 "sample": f"the first {n} rows, {done // n} passes in {dt:.1f} s, C oracle, OpenMP over rows"}
+    print(json.dumps(line), flush=True)
+
+
+def bench_bias_update(args, moe, torch, np):
+    """The training-side step after the histogram: one aux-loss-free bias
+    update for E = 256 experts (the GLM-class layer), counts of a 16384-pair
+    step.  Latency-bound: 12 bytes per expert."""
+    E = 256
+    rng = np.random.default_rng(1300)
+    counts = torch.from_numpy(rng.multinomial(16384, np.full(E, 1.0 / E)).astype(np.int32)).cuda()
+    bias = torch.from_numpy((rng.standard_normal(E) * 0.01).astype(np.float32)).cuda()
+    st = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        moe.moe_bias_update(counts, bias, 1e-3)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        moe.moe_bias_update(counts, bias, 1e-3)
+    e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    alg = 12 * E
+    line = {"metric": "aux-loss-free bias updates per second (E = 256)", "value": round(1e6 / us, 1),
+            "unit": "updates/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic (seeded multinomial counts)",
+            "config": {"workload": "one bias update, E = 256, counts of 16384 pairs", "E": E},
+            "roofline": {"bound": "hbm", "achieved": round(alg / (us * 1e-6) / 1e9, 3), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 7), "traffic": None,
+                         "kernel": "k_bias_update", "avg_launch_us": round(us, 2), "alg_bytes_per_launch": alg}}
+    if not args.no_cpu_baseline:
+        import oracle
+        c, b = counts.cpu().numpy(), bias.cpu().numpy()
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 2.0):
+            b = oracle.bias_update(c, b, 1e-3)
+            n += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(n / dt, 1), "unit": "updates/s", "cores": 1, "kind": "oracle",
+                                "sample": f"{n} updates in {dt:.1f} s, C oracle through ctypes"}
     print(json.dumps(line), flush=True)
 
 

@@ -250,6 +250,25 @@ int moe_layer_routing(const moe_shape *shape, void *ws, size_t ws_bytes, int32_t
 int moe_quantize_rows(const void *src, int32_t src_format, int64_t rows, int32_t cols, int32_t bits, void *q,
                       float *qs, void *stream);
 
+/* ---- the training-side step after the histogram: aux-loss-free balancing ----
+ *
+ * moe_bias_update moves each expert's router bias (the bias that only decides
+ * selection) by gamma toward balance, from the expert counts of a step
+ * (Colibri-Nano model card, "Architecture": sigmoid+bias router with
+ * DeepSeek-V3-style aux-loss-free balancing).  The pages give no rule; the
+ * reading is the published DeepSeek-V3 one:
+ *   router_bias[e] += gamma * sign(mean - counts[e]),  mean = sum(counts) / E,
+ * the comparison taken exactly in integers (E * counts[e] against the sum),
+ * no change for an expert exactly at the mean, one f32 addition each.
+ *
+ *   counts       device, [E] int32, e.g. the counts output of moe_permute
+ *                (or a sum of several steps' counts)
+ *   router_bias  device, [E] f32, updated in place
+ * Enqueues one small kernel on `stream`.  Returns MOE_OK, MOE_ERR_SHAPE
+ * (E < 1), MOE_ERR_NULL, MOE_ERR_ALIGN (pointers not 4-byte aligned) or
+ * MOE_ERR_HIP. */
+int moe_bias_update(int32_t E, const int32_t *counts, float *router_bias, float gamma, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,7 @@ library is missing, every call raises -- there is no CPU fallback.
 The functions mirror the C ABI names:
   moe_router, moe_permute, moe_expert_ffn, moe_combine, moe_layer_forward,
   moe_workspace_bytes, moe_validate_shape, moe_status_string, moe_layer_routing,
-  moe_quantize_rows
+  moe_quantize_rows, moe_bias_update
 and ``MoeLayer`` keeps one layer's device weights and workspace.
 """
 from __future__ import annotations
@@ -43,7 +43,7 @@ MOE_WS_LAYER = 3
 
 EXPORTS = ["moe_router", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_profiled", "moe_workspace_bytes", "moe_validate_shape", "moe_status_string",
-           "moe_layer_routing", "moe_quantize_rows"]
+           "moe_layer_routing", "moe_quantize_rows", "moe_bias_update"]
 
 
 class MoeShape(ctypes.Structure):
@@ -94,6 +94,7 @@ def load() -> ctypes.CDLL:
             "moe_validate_shape": [S],
             "moe_layer_routing": [S, vp, sz, vp, vp, vp, vp],
             "moe_quantize_rows": [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp],
+            "moe_bias_update": [ctypes.c_int32, vp, vp, ctypes.c_float, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -215,6 +216,15 @@ def moe_quantize_rows(src, bits: int, q=None, qs=None, stream=None):
     _check(load().moe_quantize_rows(_ptr(src), fmt, rows, cols, bits, _ptr(q), _ptr(qs), _stream(stream)),
            "moe_quantize_rows")
     return q, qs
+
+
+def moe_bias_update(counts, router_bias, gamma: float, stream=None):
+    """Aux-loss-free balancing step (include/moe.h): router_bias (f32 [E], GPU)
+    is updated in place from counts (int32 [E], GPU)."""
+    if counts.numel() != router_bias.numel():
+        raise ValueError("counts and router_bias must both have E elements")
+    _check(load().moe_bias_update(router_bias.numel(), _ptr(counts), _ptr(router_bias), gamma, _stream(stream)),
+           "moe_bias_update")
 
 
 def qmat(q, qs, q_stride_bytes: int = 0, qs_stride_floats: int = 0, q_offset: int = 0, qs_offset: int = 0) -> MoeQMat:

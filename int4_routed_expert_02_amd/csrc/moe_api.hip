@@ -419,6 +419,14 @@ int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const m
                                           s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, hs));
 }
 
+int moe_bias_update(int32_t E, const int32_t *counts, float *router_bias, float gamma, void *stream)
+{
+    if (E < 1) return MOE_ERR_SHAPE;
+    if (!counts || !router_bias) return MOE_ERR_NULL;
+    if (!aligned(counts, 4) || !aligned(router_bias, 4)) return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_bias_update(E, counts, router_bias, gamma, (hipStream_t)stream));
+}
+
 int moe_quantize_rows(const void *src, int32_t src_format, int64_t rows, int32_t cols, int32_t bits, void *q,
                       float *qs, void *stream)
 {

@@ -67,6 +67,7 @@ hipError_t launch_pair_hist(const int32_t *ids, int P, int E, int chunk, int nbl
 hipError_t launch_scatter(const int32_t *ids, const int32_t *bcounts, int nblocks, int P, int E, int chunk,
                           int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *inv, hipStream_t st);
 hipError_t launch_ffn(int mode, int wbits, const FfnArgs &a, int rows_total, int groups, hipStream_t st);
+hipError_t launch_bias_update(int E, const int32_t *counts, float *bias, float gamma, hipStream_t st);
 hipError_t launch_quantize(const void *src, int src_bf16, long rows, int cols, int bits, void *q, float *qs,
                            hipStream_t st);
 hipError_t launch_combine(const float *y, const int32_t *inv, const float *topk_w, float rsf, const float *sh,

@@ -212,6 +212,40 @@ __global__ __launch_bounds__(256) void k_router_select(const float *__restrict__
     }
 }
 
+// ------------------------------------------------------------------ bias update
+
+// Aux-loss-free balancing after a step (Colibri-Nano model card,
+// "Architecture": sigmoid+bias router with DeepSeek-V3-style aux-loss-free
+// balancing).  Reading (the pages give no rule): bias[e] += gamma *
+// sign(mean - counts[e]) with mean = sum(counts) / E, compared exactly as
+// E * counts[e] against the sum; an expert exactly at the mean keeps its
+// bias.  One workgroup: the sum in int64, then one f32 addition per expert.
+__global__ __launch_bounds__(256) void k_bias_update(int E, const int32_t *__restrict__ counts,
+                                                     float *__restrict__ bias, float gamma)
+{
+    __shared__ long long part[256];
+    long long s = 0;
+    for (int e = threadIdx.x; e < E; e += 256) s += counts[e];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+        __syncthreads();
+    }
+    const long long total = part[0];
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const long long load = (long long)E * counts[e];
+        if (load < total) bias[e] = bias[e] + gamma;
+        else if (load > total) bias[e] = bias[e] - gamma;
+    }
+}
+
+hipError_t launch_bias_update(int E, const int32_t *counts, float *bias, float gamma, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_bias_update, dim3(1), dim3(256), 0, st, E, counts, bias, gamma);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ launchers
 
 // K splits of the logits: the smallest divisor of the k-step count that gives

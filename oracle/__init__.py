@@ -83,6 +83,7 @@ def lib():
             "oracle_gateup_int_sums": ([S, vp, W, vp, vp, vp, vp], ctypes.c_int),
             "oracle_num_threads": ([], ctypes.c_int),
             "oracle_quantize_rows": ([vp, i32, ctypes.c_int64, i32, i32, vp, vp], ctypes.c_int),
+            "oracle_bias_update": ([i32, vp, vp, ctypes.c_float, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -284,6 +285,15 @@ def quantize_rows(src: np.ndarray, bits: int):
     _chk(lib().oracle_quantize_rows(_p(src), 1 if src.dtype == np.uint16 else 0, rows, cols, bits, _p(q), _p(qs)),
          "oracle_quantize_rows")
     return q, qs
+
+
+def bias_update(counts: np.ndarray, bias: np.ndarray, gamma: float) -> np.ndarray:
+    """One aux-loss-free balancing step: the updated f32 bias for these expert counts."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    bias = np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty_like(bias)
+    _chk(lib().oracle_bias_update(len(bias), _p(counts), _p(bias), gamma, _p(out)), "oracle_bias_update")
+    return out
 
 
 def num_threads() -> int:

@@ -146,6 +146,26 @@ int oracle_quantize_rows(const void *src, int32_t src_bf16, int64_t rows, int32_
     return failed ? O_ERR_NOMEM : O_OK;
 }
 
+/* ---------------------------------------------------------------- bias update */
+
+int oracle_bias_update(int32_t E, const int32_t *counts, const float *bias_in, float gamma, float *bias_out)
+{
+    if (E <= 0) return O_ERR_SHAPE;
+    if (!counts || !bias_in || !bias_out) return O_ERR_NULL;
+    int64_t total = 0;
+    for (int32_t e = 0; e < E; ++e) total += counts[e];
+    for (int32_t e = 0; e < E; ++e) {
+        const int64_t load = (int64_t)E * counts[e];  /* E times this expert's load, against E times the mean */
+        if (load < total)
+            bias_out[e] = bias_in[e] + gamma;  /* under-loaded: more likely to be selected */
+        else if (load > total)
+            bias_out[e] = bias_in[e] - gamma;  /* over-loaded: less likely */
+        else
+            bias_out[e] = bias_in[e];
+    }
+    return O_OK;
+}
+
 /* row r of expert e of a matrix family with `cols` columns */
 static const void *qrow(const oracle_qmat *m, int32_t bits, int32_t e, int64_t r, int32_t cols)
 {

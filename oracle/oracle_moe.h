@@ -137,6 +137,18 @@ int oracle_gateup_int_sums(const oracle_shape *sh, const uint16_t *hidden, const
 int oracle_quantize_rows(const void *src, int32_t src_bf16, int64_t rows, int32_t cols, int32_t bits, void *q,
                          float *qs);
 
+/* Aux-loss-free load balancing, the training-side step after the histogram
+ * (Colibri-Nano model card, "Architecture": sigmoid+bias router with
+ * DeepSeek-V3-style aux-loss-free balancing; the README's repository layout
+ * lists aux-loss-free balancing under train/).  The pages give no rule; the
+ * reading is the published DeepSeek-V3 one: after a step, every expert's bias
+ * moves by gamma toward balance,
+ *   bias[e] += gamma * sign(mean - counts[e]),  mean = sum(counts) / E,
+ * with the comparison taken exactly in integers (E * counts[e] against the
+ * sum) and no change for an expert exactly at the mean.  Each update is one
+ * f32 addition.  bias_out may equal bias_in.  Returns 0, -1 or -2. */
+int oracle_bias_update(int32_t E, const int32_t *counts, const float *bias_in, float gamma, float *bias_out);
+
 int oracle_num_threads(void);
 
 #ifdef __cplusplus

@@ -163,3 +163,16 @@ def test_quantize_rows_validation(moe, args, code):
     a.update(args)
     assert moe.load().moe_quantize_rows(a["src"], a["fmt"], a["rows"], a["cols"], a["bits"], a["q"], a["qs"],
                                         None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(E=0), -2),
+    (dict(counts=None), -1),
+    (dict(bias=None), -1),
+    (dict(counts=FAKE + 2), -5),
+    (dict(bias=FAKE + 1), -5),
+])
+def test_bias_update_validation(moe, args, code):
+    a = dict(E=64, counts=FAKE, bias=FAKE)
+    a.update(args)
+    assert moe.load().moe_bias_update(a["E"], a["counts"], a["bias"], 0.001, None) == code

@@ -28,6 +28,9 @@ MUTANTS = {
                              "for (int64_t p = P - 1; p >= 0; --p) {\n        int32_t pos = fill[ids[p]]++;"),
     "quantiser ties away from zero": ("float v = nearbyintf(w[c] / scale);", "float v = roundf(w[c] / scale);"),
     "quantiser scale one level short": ("const float scale = amax / qmax;", "const float scale = amax / (qmax + 1.0f);"),
+    "bias update sign flipped": ("if (load < total)\n            bias_out[e] = bias_in[e] + gamma;",
+                                 "if (load < total)\n            bias_out[e] = bias_in[e] - gamma;"),
+    "bias update moves at the mean": ("else if (load > total)", "else if (load >= total)"),
     "down transposed": ("oracle_dequant_row(qrow(down, bits, e, c, I), bits, qscale(down, e, c), I, wrow);",
                         "for (int32_t i2 = 0; i2 < I; ++i2) oracle_dequant_row(qrow(down, bits, e, i2 % H, I), bits, qscale(down, e, c), 1, wrow + i2);"),
 }

@@ -440,6 +440,49 @@ def test_quantizer_bf16_input_is_its_widened_value(oracle_mod):
         assert np.array_equal(qa, qb) and np.array_equal(sa, sb)
 
 
+# ------------------------------------------------------------------ bias update (NEXT-3)
+# Aux-loss-free balancing (Colibri-Nano model card, "Architecture": sigmoid +
+# bias router with DeepSeek-V3-style aux-loss-free balancing): after a step
+# each expert's bias moves by gamma toward balance.
+
+def test_bias_update_worked_example(oracle_mod):
+    # loads 3, 1, 2, 2 against a mean of 2; power-of-two values keep the sums exact
+    bias = np.array([0.5, -0.25, 0.125, 0.0], np.float32)
+    out = oracle_mod.bias_update(np.array([3, 1, 2, 2]), bias, 0.0625)
+    assert out.tolist() == [0.4375, -0.1875, 0.125, 0.0]
+
+
+def test_bias_update_no_op_cases(oracle_mod):
+    rng = np.random.default_rng(4)
+    bias = (rng.standard_normal(16) * 0.01).astype(np.float32)
+    assert np.array_equal(oracle_mod.bias_update(np.full(16, 5), bias, 0.01), bias)  # balanced
+    assert np.array_equal(oracle_mod.bias_update(rng.integers(0, 9, 16), bias, 0.0), bias)  # gamma 0
+    # a fractional mean (sum 7 over 4): nobody is exactly at it, everyone moves
+    out = oracle_mod.bias_update(np.array([2, 2, 2, 1]), np.zeros(4, np.float32), 0.5)
+    assert out.tolist() == [-0.5, -0.5, -0.5, 0.5]
+
+
+def test_bias_update_drives_loads_toward_balance(synth_mod, oracle_mod):
+    # the method's purpose: repeated router -> histogram -> update steps on a
+    # batch skewed toward two experts bring the loads back toward the mean
+    cfg = tiny_cfg(synth_mod, T=256, E=8, k=2, H=64, seed=91)
+    d = synth_mod.layer(cfg)
+    bias = d["router_bias"].copy()
+    bias[:2] += np.float32(0.3)
+
+    def loads(b):
+        ids = oracle_mod.router(cfg, d["hidden"], d["router_w"], b)[0]
+        return np.bincount(ids.reshape(-1), minlength=cfg.E)
+
+    start = loads(bias)
+    for _ in range(80):
+        bias = oracle_mod.bias_update(loads(bias), bias, 0.005)
+    end = loads(bias)
+    mean = cfg.T * cfg.k / cfg.E
+    assert start.max() / mean > 3.0
+    assert end.max() / mean < 1.5 and end.min() / mean > 0.5
+
+
 def test_thread_count_does_not_change_bits(synth_mod, oracle_mod, tmp_path):
     code = ("import sys, numpy as np; sys.path.insert(0, %r); import synth, oracle;"
             "cfg = synth.CONFIGS['c0'];"
