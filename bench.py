@@ -123,9 +123,17 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
+    # the chained step: each layer's combine also takes the next layer's router
+    # logits of the output row just written, so layers 2..L run no logits
+    # kernel (MOE_LOGITS_GIVEN)
+    def lflags(l):
+        return flags | (moe.MOE_LOGITS_GIVEN if l else 0)
+
     def step(s):
         for l in range(L):
-            layers[l].forward(xs[l], xs[l + 1], wss[l], flags, stream=s)
+            nxt = layers[l + 1] if l + 1 < L else None
+            layers[l].forward_chain(xs[l], xs[l + 1], wss[l], lflags(l), nxt, wss[l + 1] if nxt is not None else None,
+                                    stream=s)
 
     # eager once (validates arguments), then capture the step in a HIP graph
     with torch.cuda.stream(stream):
@@ -152,24 +160,28 @@ def main():
     ms_per_step = ms_total / args.steps
     tok_s = T / (ms_per_step / 1e3)
 
-    # ---- roofline of the dominant kernel: the fused expert kernel (routing
-    # decision, gate/up + SwiGLU + down of every chosen routed expert and of the
-    # shared expert, one launch per layer).  Its duration is measured with HIP
-    # events on the kernel's own stream around a HIP graph of the 23 layers'
-    # expert stages alone (MOE_STAGE_EXPERTS_ONLY: the same launches as in the
-    # step above, reading the router logits the step left in each workspace),
+    # ---- roofline of the dominant kernel: the fused expert kernel (gate/up +
+    # SwiGLU + down of every chosen routed expert and of the shared expert, one
+    # launch per layer, each taking its routing decision from the router
+    # logits in its workspace).  Its duration is measured with
+    # HIP events on the kernel's own stream around a HIP graph of the 23
+    # layers' expert stages alone (MOE_STAGE_EXPERTS_ONLY: the same launches as
+    # in the step above, reading the routing the step left in each workspace),
     # replayed back to back: average = elapsed / launches.
     P = T * cfg.k
-    eflags = flags | moe.MOE_STAGE_EXPERTS_ONLY
+
+    def eflags(l):
+        return lflags(l) | moe.MOE_STAGE_EXPERTS_ONLY
+
     with torch.cuda.stream(stream):
-        step(stream)  # leave each layer's logits in its workspace
+        step(stream)  # leave each layer's routing in its workspace
         for l in range(L):
-            layers[l].forward(xs[l], xs[l + 1], wss[l], eflags, stream=stream)
+            layers[l].forward(xs[l], xs[l + 1], wss[l], eflags(l), stream=stream)
     torch.cuda.synchronize()
     egraph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(egraph, stream=stream):
         for l in range(L):
-            layers[l].forward(xs[l], xs[l + 1], wss[l], eflags, stream=stream)
+            layers[l].forward(xs[l], xs[l + 1], wss[l], eflags(l), stream=stream)
     torch.cuda.synchronize()
     for _ in range(2):
         egraph.replay()
@@ -247,7 +259,8 @@ def main():
         "dtype": "bf16 MFMA, int4 weights, f32 accumulate",
         "data": "synthetic (seeded, random-init weights of the Colibri-Nano MoE layer shape)",
         "config": {"workload": cfg.name, "T": T, "layers": L, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
-                   "I_shared": cfg.I_sh, "global_batch": T, "parallelism": "single GPU"},
+                   "I_shared": cfg.I_sh, "global_batch": T, "parallelism": "single GPU",
+                   "chained": "each layer's combine takes the next layer's router logits"},
         "step_hbm_GBs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_alg_bytes": int(step_bytes),

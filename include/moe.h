@@ -79,6 +79,10 @@ extern "C" {
                                (else MOE_ERR_UNSUPPORTED): run only the expert kernel, from the router
                                logits a previous full call with the same shape, weights, input and ws
                                left in ws; out is not written */
+#define MOE_LOGITS_GIVEN 0x800u /* moe_layer_forward(_chain), small-batch regime only (else
+                               MOE_ERR_UNSUPPORTED): this call's router logits are already in ws, written
+                               there by the previous layer's moe_layer_forward_chain; the logits kernel
+                               is not run (the selection is, from those logits) */
 #define MOE_TEST_GATEUP_SUMS 0x100u /* moe_expert_ffn, testing only: write the raw integer-weight sums
                                sum_h x*q of gate into y_pairs[r][0:I] and of up into y_pairs[r][I:2I]
                                (no scale, no activation, no down projection); needs 2*I <= H, int4 */
@@ -193,6 +197,31 @@ int moe_combine(const moe_shape *shape, const float *y_pairs, const int32_t *inv
  */
 int moe_layer_forward(const moe_shape *shape, const moe_weights *weights, const moe_bf16 *hidden, void *out,
                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_layer_forward_chain -- one layer of a stacked small-batch decode step
+ * whose output is the next layer's input (the layers of a model run one after
+ * another, each on the previous one's output: colibri README, "What's
+ * implemented", the faithful model forward).  It runs the layer as
+ * moe_layer_forward does; when next_weights is given, the layer's combine also
+ * computes the next layer's router logits of the output row it has just
+ * written, into next_ws, so the next call passes MOE_LOGITS_GIVEN and skips
+ * its logits kernel.  Results equal the unchained calls (same output bits;
+ * the next layer's logits are summed in another order, within f32 rounding,
+ * so only a near-tie selection can differ).
+ *   shape, weights, hidden, out, ws  as for moe_layer_forward; out must be bf16
+ *               (no MOE_OUT_F32): it is what the next layer reads
+ *   next_shape  the next layer's shape: same T and H, small-batch regime
+ *   next_weights  nullable: the next layer's weights (only router_w is read);
+ *               NULL runs this layer unchained (the last layer of a step)
+ *   next_ws     the next layer's MOE_WS_LAYER workspace (next_ws_bytes bytes)
+ * Errors: as moe_layer_forward; MOE_ERR_UNSUPPORTED if either layer is not in
+ * the small-batch regime, out is f32 or MOE_STAGE_EXPERTS_ONLY is set with a
+ * next layer; MOE_ERR_SHAPE if T or H differ.
+ */
+int moe_layer_forward_chain(const moe_shape *shape, const moe_weights *weights, const moe_bf16 *hidden, void *out,
+                            void *ws, size_t ws_bytes, const moe_shape *next_shape, const moe_weights *next_weights,
+                            void *next_ws, size_t next_ws_bytes, void *stream);
 
 /* moe_layer_forward with two HIP events (hipEvent_t as void*, nullable) recorded
  * on `stream` immediately before and after the expert gate/up kernel: the

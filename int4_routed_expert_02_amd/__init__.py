@@ -7,7 +7,7 @@ library is missing, every call raises -- there is no CPU fallback.
 The functions mirror the C ABI names:
   moe_router, moe_permute, moe_expert_ffn, moe_combine, moe_layer_forward,
   moe_workspace_bytes, moe_validate_shape, moe_status_string, moe_layer_routing,
-  moe_quantize_rows, moe_bias_update
+  moe_quantize_rows, moe_bias_update, moe_layer_forward_chain
 and ``MoeLayer`` keeps one layer's device weights and workspace.
 """
 from __future__ import annotations
@@ -33,6 +33,7 @@ MOE_EXPERT_INT8 = 4
 MOE_TEST_GATEUP_SUMS = 0x100
 MOE_STAGE_GATEUP_ONLY = 0x200
 MOE_STAGE_EXPERTS_ONLY = 0x400
+MOE_LOGITS_GIVEN = 0x800
 
 MOE_SRC_F32 = 0
 MOE_SRC_BF16 = 1
@@ -43,7 +44,7 @@ MOE_WS_LAYER = 3
 
 EXPORTS = ["moe_router", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_profiled", "moe_workspace_bytes", "moe_validate_shape", "moe_status_string",
-           "moe_layer_routing", "moe_quantize_rows", "moe_bias_update"]
+           "moe_layer_routing", "moe_quantize_rows", "moe_bias_update", "moe_layer_forward_chain"]
 
 
 class MoeShape(ctypes.Structure):
@@ -91,6 +92,7 @@ def load() -> ctypes.CDLL:
             "moe_combine": [S, vp, vp, vp, vp, vp, vp, vp],
             "moe_layer_forward": [S, W, vp, vp, vp, sz, vp],
             "moe_layer_forward_profiled": [S, W, vp, vp, vp, sz, vp, vp, vp],
+            "moe_layer_forward_chain": [S, W, vp, vp, vp, sz, S, W, vp, sz, vp],
             "moe_validate_shape": [S],
             "moe_layer_routing": [S, vp, sz, vp, vp, vp, vp],
             "moe_quantize_rows": [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp],
@@ -190,6 +192,16 @@ def moe_layer_forward_profiled(sh: MoeShape, weights: MoeWeights, hidden, out, w
                                              ev_start.cuda_event, ev_stop.cuda_event), "moe_layer_forward_profiled")
 
 
+def moe_layer_forward_chain(sh: MoeShape, weights: MoeWeights, hidden, out, ws, next_sh: Optional[MoeShape] = None,
+                            next_weights: Optional[MoeWeights] = None, next_ws=None, stream=None):
+    """One layer of a chained small-batch decode step (include/moe.h)."""
+    _check(load().moe_layer_forward_chain(ctypes.byref(sh), ctypes.byref(weights), _ptr(hidden), _ptr(out), _ptr(ws),
+                                          ws.numel(), ctypes.byref(next_sh) if next_sh is not None else None,
+                                          ctypes.byref(next_weights) if next_weights is not None else None,
+                                          _ptr(next_ws), next_ws.numel() if next_ws is not None else 0,
+                                          _stream(stream)), "moe_layer_forward_chain")
+
+
 def moe_layer_routing(sh: MoeShape, ws):
     """Device pointers (ints) of ids, w, offsets, sorted inside a layer workspace."""
     p = [ctypes.c_void_p() for _ in range(4)]
@@ -274,4 +286,15 @@ class MoeLayer:
 
     def forward(self, hidden, out, ws, flags: int = 0, stream=None):
         moe_layer_forward(shape_of(self.cfg, hidden.shape[0], flags), self.weights, hidden, out, ws, stream)
+        return out
+
+    def forward_chain(self, hidden, out, ws, flags: int = 0, nxt: Optional["MoeLayer"] = None, next_ws=None,
+                      stream=None):
+        """moe_layer_forward_chain: this layer, and the router logits of `nxt`
+        (if given) from `out` into next_ws.  Pass MOE_LOGITS_GIVEN in flags
+        when the previous layer's chained call wrote this one's logits."""
+        T = hidden.shape[0]
+        moe_layer_forward_chain(shape_of(self.cfg, T, flags), self.weights, hidden, out, ws,
+                                shape_of(nxt.cfg, T) if nxt is not None else None,
+                                nxt.weights if nxt is not None else None, next_ws, stream)
         return out

@@ -362,9 +362,9 @@ struct DecArgs {
     const uint8_t *sgq, *suq, *sdq;
     const float *sgs, *sus, *sds;
     int Ish, sh_bits;
-    // partial expert outputs, one plane per 64-row chunk of the intermediate
-    float *yp;   // [I/64][T*k][H]   routed, scaled by rsf * w
-    float *ysp;  // [Ish/64][T][H]   shared
+    // partial expert outputs, one plane per 128-row unit of the intermediate
+    float *yp;   // [I/128][T*k][H]   routed, scaled by rsf * w
+    float *ysp;  // [Ish/128][T][H]   shared
 };
 
 // The routing decision of the batch into LDS (every routed workgroup takes
@@ -869,6 +869,116 @@ __global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ y
     }
 }
 
+// Chained decode: k_dec_combine (same grid, lanes and plane order, so the
+// bf16 output is the same bits) that also takes the next layer's router
+// logits of its output, in the 4-plane form k_dec_expert reads.  Workgroup
+// (token t, quarter g) covers columns [g H/4, (g+1) H/4): once the quarter of
+// the output row is in LDS (as the next layer reads it, bf16), four
+// consecutive threads take one expert, thread j of the four the j-th quarter
+// of those columns (contiguous, 16-byte W loads; for H = 1024 the W values
+// are loaded before the combine, while the planes are in flight); fused
+// multiply-adds in column order, then the four partial sums in a fixed
+// two-step tree; the sum goes to plane g.  The next layer adds the 4 planes
+// as it does its own logits kernel's.
+constexpr int CL_VEC = 16;  // 16-byte W loads per thread held across the combine (64 columns)
+
+__global__ __launch_bounds__(256) void k_dec_combine_logits(const float *__restrict__ yp, int nkr,
+                                                            const float *__restrict__ ysp, int nks,
+                                                            const uint16_t *__restrict__ res,
+                                                            uint16_t *__restrict__ out, int T, int H, int k,
+                                                            const float *__restrict__ nrw, int nE,
+                                                            float *__restrict__ nzp)
+{
+    static_assert(DEC_LOGIT_PLANES == 4, "one plane per quarter of the row");
+    extern __shared__ float xq[];  // [H / 4] this quarter of the output row
+    constexpr int MAXL = 16;
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x / 4, g = blockIdx.x % 4;
+    const int H4 = H / 4, c0 = g * H4;
+    const int ncs = H4 / 4;  // columns per thread (one expert per four threads)
+    const int sub = tid & 3;
+    const bool pre = ncs == 4 * CL_VEC;
+    f32x4 wv[CL_VEC];
+    if (pre) {
+        const float *wr = nrw + (size_t)min(tid >> 2, nE - 1) * H + c0 + sub * ncs;
+#pragma unroll
+        for (int i = 0; i < CL_VEC; ++i) wv[i] = *(const f32x4 *)(wr + 4 * i);
+    }
+    const size_t P = (size_t)T * k;
+    const int nrp = k * nkr, np = nrp + nks;
+    for (int qd0 = 0; qd0 < H4 / 4; qd0 += 256 / CB_SPLIT) {
+        const int quad = qd0 + tid / CB_SPLIT, q = tid % CB_SPLIT;
+        const int c = c0 + quad * 4;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int p0 = q; p0 < np; p0 += CB_SPLIT * MAXL) {
+            f32x4 v[MAXL];
+#pragma unroll
+            for (int i = 0; i < MAXL; ++i) {
+                const int p = p0 + CB_SPLIT * i;
+                v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (p < np) {
+                    const float *src = p < nrp ? yp + ((size_t)(p % nkr) * P + (size_t)t * k + p / nkr) * H + c
+                                               : ysp + ((size_t)(p - nrp) * T + t) * H + c;
+                    v[i] = *(const f32x4 *)src;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < MAXL; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] += v[i][e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float s1 = __shfl_down(acc[e], 1, WAVE);
+            const float s2 = __shfl_down(acc[e], 2, WAVE);
+            const float s3 = __shfl_down(acc[e], 3, WAVE);
+            acc[e] = ((acc[e] + s1) + s2) + s3;
+        }
+        if (q == 0) {
+            if (res) {
+                const u32x2 r = *(const u32x2 *)(res + (size_t)t * H + c);
+                acc[0] += bf16_lo(r[0]);
+                acc[1] += bf16_hi(r[0]);
+                acc[2] += bf16_lo(r[1]);
+                acc[3] += bf16_hi(r[1]);
+            }
+            const u32x2 o = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            *(u32x2 *)(out + (size_t)t * H + c) = o;
+            float *x = xq + quad * 4;
+            x[0] = bf16_lo(o[0]);
+            x[1] = bf16_hi(o[0]);
+            x[2] = bf16_lo(o[1]);
+            x[3] = bf16_hi(o[1]);
+        }
+    }
+    __syncthreads();
+    float *zp = nzp + ((size_t)g * T + t) * nE;
+    const float *xs = xq + sub * ncs;
+    for (int e0 = 0; e0 < nE; e0 += 64) {
+        const int e = e0 + (tid >> 2);
+        float z = 0.f;
+        if (pre && e0 == 0) {
+#pragma unroll
+            for (int i = 0; i < CL_VEC; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) z = fmaf(xs[4 * i + r], wv[i][r], z);
+        } else {
+            const float *wr = nrw + (size_t)min(e, nE - 1) * H + c0 + sub * ncs;
+            for (int i = 0; i < ncs; i += 4) {
+                const f32x4 w4 = *(const f32x4 *)(wr + i);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) z = fmaf(xs[i + r], w4[r], z);
+            }
+        }
+        const float z1 = __shfl_xor(z, 1, WAVE);
+        const float z2 = __shfl_xor(z, 2, WAVE);
+        const float z3 = __shfl_xor(z, 3, WAVE);
+        // the four partials added in the order of their column ranges
+        const float zt = sub == 0 ? ((z + z1) + z2) + z3 : 0.f;
+        if (sub == 0 && e < nE) zp[e] = zt;
+    }
+}
+
 // ---------------------------------------------------------------- launcher
 
 bool decode_supported(int T, int H, int E, int k, int I, int Ish, int sh_bits)
@@ -919,7 +1029,7 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     a.ysp = d.shp;
 
     hipError_t e;
-    if (!d.experts_only) {
+    if (!d.experts_only && !d.logits_given) {
         const int grid = ((d.E + 15) / 16) * ((d.T + 15) / 16) * LG_NP;
         hipLaunchKernelGGL(k_dec_logits, dim3(grid), dim3(256), 0, st, d.x, d.rw, d.T, d.H, d.E, d.z);
         e = hipGetLastError();
@@ -945,6 +1055,12 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     e = hipGetLastError();
     if (e == hipSuccess && d.ev1) e = hipEventRecord(d.ev1, st);
     if (e != hipSuccess || d.experts_only) return e;
+    if (d.nrw) {
+        hipLaunchKernelGGL(k_dec_combine_logits, dim3(d.T * 4), dim3(256), (size_t)(d.H / 4) * sizeof(float), st, d.y,
+                           d.I / DX_ROWS, d.shp, d.sh_bits ? d.Ish / DX_ROWS : 0, d.res, (uint16_t *)d.out, d.T, d.H,
+                           d.k, d.nrw, d.nE, d.nz);
+        return hipGetLastError();
+    }
     const long nthreads = (long)d.T * (d.H / 4) * CB_SPLIT;
     hipLaunchKernelGGL(k_dec_combine, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, d.y,
                        d.I / DX_ROWS, d.shp, d.sh_bits ? d.Ish / DX_ROWS : 0, d.res, d.out, d.T, d.H, d.k,

@@ -309,14 +309,15 @@ int moe_combine(const moe_shape *s, const float *y_pairs, const int32_t *inv_pos
                                           (hipStream_t)stream));
 }
 
-int moe_layer_forward(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out, void *ws,
-                      size_t ws_bytes, void *stream)
-{
-    return moe_layer_forward_profiled(s, w, hidden, out, ws, ws_bytes, stream, nullptr, nullptr);
-}
+}  // extern "C"
 
-int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out,
-                               void *ws, size_t ws_bytes, void *stream, void *ev_start, void *ev_stop)
+namespace {
+
+// The layer forward behind moe_layer_forward(_profiled, _chain).  ns/nw/nws:
+// the next layer of a chained small-batch step (nw null: not chained).
+int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out, void *ws,
+                 size_t ws_bytes, void *stream, void *ev_start, void *ev_stop, const moe_shape *ns,
+                 const moe_weights *nw, void *nws, size_t nws_bytes)
 {
     int st = validate(s);
     if (st) return st;
@@ -332,7 +333,18 @@ int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const m
         return MOE_ERR_UNSUPPORTED;
     const Layout L = layout(s, MOE_WS_LAYER);
     hipStream_t hs = (hipStream_t)stream;
-    if ((s->flags & MOE_STAGE_EXPERTS_ONLY) && !L.decode) return MOE_ERR_UNSUPPORTED;
+    if ((s->flags & (MOE_STAGE_EXPERTS_ONLY | MOE_LOGITS_GIVEN)) && !L.decode) return MOE_ERR_UNSUPPORTED;
+    Layout NL;
+    if (nw) {
+        // chained: the next layer's router logits from this layer's bf16 output
+        if (!ns || !nws || !nw->router_w || !nw->router_bias) return MOE_ERR_NULL;
+        if ((st = validate(ns))) return st;
+        if (ns->T != s->T || ns->H != s->H) return MOE_ERR_SHAPE;
+        NL = layout(ns, MOE_WS_LAYER);
+        if (!L.decode || !NL.decode || (s->flags & (MOE_OUT_F32 | MOE_STAGE_EXPERTS_ONLY))) return MOE_ERR_UNSUPPORTED;
+        if (!aligned(nw->router_w, 16)) return MOE_ERR_ALIGN;
+        if ((st = check_ws(ns, MOE_WS_LAYER, nws, nws_bytes))) return st;
+    }
     if (L.decode) {
         moe::DecLaunch d;
         memset(&d, 0, sizeof(d));
@@ -380,6 +392,12 @@ int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const m
         d.ev0 = (hipEvent_t)ev_start;
         d.ev1 = (hipEvent_t)ev_stop;
         d.experts_only = (s->flags & MOE_STAGE_EXPERTS_ONLY) ? 1 : 0;
+        d.logits_given = (s->flags & MOE_LOGITS_GIVEN) ? 1 : 0;
+        if (nw) {
+            d.nrw = nw->router_w;
+            d.nE = ns->E;
+            d.nz = at<float>(nws, NL.zpart);
+        }
         return hip_status(moe::launch_decode(d, hs));
     }
     const int P = s->T * s->top_k;
@@ -417,6 +435,30 @@ int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const m
     return hip_status(moe::launch_combine(ypair, inv, nullptr, 1.f, shy,
                                           (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr, out, s->T, s->H,
                                           s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, hs));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out, void *ws,
+                      size_t ws_bytes, void *stream)
+{
+    return forward_impl(s, w, hidden, out, ws, ws_bytes, stream, nullptr, nullptr, nullptr, nullptr, nullptr, 0);
+}
+
+int moe_layer_forward_profiled(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out,
+                               void *ws, size_t ws_bytes, void *stream, void *ev_start, void *ev_stop)
+{
+    return forward_impl(s, w, hidden, out, ws, ws_bytes, stream, ev_start, ev_stop, nullptr, nullptr, nullptr, 0);
+}
+
+int moe_layer_forward_chain(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out, void *ws,
+                            size_t ws_bytes, const moe_shape *next_shape, const moe_weights *next_weights,
+                            void *next_ws, size_t next_ws_bytes, void *stream)
+{
+    return forward_impl(s, w, hidden, out, ws, ws_bytes, stream, nullptr, nullptr, next_shape, next_weights, next_ws,
+                        next_ws_bytes);
 }
 
 int moe_bias_update(int32_t E, const int32_t *counts, float *router_bias, float gamma, void *stream)

@@ -50,6 +50,12 @@ struct DecLaunch {
     int out_f32;
     hipEvent_t ev0, ev1;  // nullable: recorded around the expert kernel
     int experts_only;     // launch only the expert kernel (router logits already in z)
+    int logits_given;     // z already holds this step's router logits (written by the previous layer's combine)
+    // chained next layer (used when nrw is set): its router logits, taken from
+    // this layer's bf16 output, into its workspace's planes nz
+    const float *nrw;
+    int nE;
+    float *nz;
 };
 constexpr int DEC_LOGIT_PLANES = 4;  // partial-logit planes of the small-batch router
 constexpr int DEC_CHUNK_ROWS = 128;  // intermediate rows per small-batch expert unit (one output plane each)

@@ -176,3 +176,36 @@ def test_bias_update_validation(moe, args, code):
     a = dict(E=64, counts=FAKE, bias=FAKE)
     a.update(args)
     assert moe.load().moe_bias_update(a["E"], a["counts"], a["bias"], 0.001, None) == code
+
+
+def _fake_weights(moe):
+    w = moe.MoeWeights()
+    w.router_w, w.router_bias = FAKE, FAKE
+    for m in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+        setattr(w, m, moe.MoeQMat(FAKE, FAKE, 0, 0))
+    return w
+
+
+@pytest.mark.parametrize("case,code", [
+    ("next ws missing", -1),
+    ("T differs", -2),
+    ("f32 out", -3),
+    ("tiled regime", -3),
+    ("logits given, tiled", -3),
+])
+def test_chain_validation(moe, case, code):
+    T = 64 if "tiled" in case else 32
+    flags = moe.MOE_OUT_F32 if case == "f32 out" else 0
+    if case == "logits given, tiled":
+        flags |= moe.MOE_LOGITS_GIVEN
+    s = good(moe, T=T, flags=flags)
+    ns = good(moe, T=16 if case == "T differs" else T)
+    w = _fake_weights(moe)
+    nbytes = moe.moe_workspace_bytes(s, moe.MOE_WS_LAYER)
+    nnbytes = moe.moe_workspace_bytes(ns, moe.MOE_WS_LAYER)
+    nxt = None if case == "logits given, tiled" else w
+    nws = None if case == "next ws missing" else FAKE
+    st = moe.load().moe_layer_forward_chain(ctypes.byref(s), ctypes.byref(w), FAKE, FAKE, FAKE, nbytes,
+                                            ctypes.byref(ns), ctypes.byref(nxt) if nxt is not None else None, nws,
+                                            nnbytes, None)
+    assert st == code

@@ -228,3 +228,47 @@ def test_decode_stack_on_oracle_trajectory():
         got, ids, w, offsets, srt = run_layer(cfg, d, flags=moe.MOE_ADD_RESIDUAL, hidden=x)
         ex = check_routing(cfg, d, x, ids, w, offsets, srt, tag=f"c1 layer {l}")
         check_output(cfg, d, x, got, ex, residual=True, bf16_out=True, tag=f"c1 layer {l}")
+
+
+def test_decode_chain_matches_unchained():
+    """The chained decode step (moe_layer_forward_chain: each combine takes the
+    next layer's router logits) over the 23-layer stack, on its own
+    trajectory.  At every layer the chained call is compared with the
+    unchained moe_layer_forward on the same input -- the path
+    test_decode_stack_on_oracle_trajectory checks against the oracle: the
+    routing (ids bit-exact outside near ties, w within 1e-5) and the output."""
+    import torch
+    cfg = synth.CONFIGS["c1"]
+    T, k, H = cfg.T, cfg.k, cfg.H
+    flags = moe.MOE_ADD_RESIDUAL
+    layers = [moe.MoeLayer(cfg, synth.layer(cfg, l, with_hidden=False)) for l in range(cfg.layers)]
+    wss = [ly.workspace(T, flags) for ly in layers]
+    ws_ref = layers[0].workspace(T, flags)
+    sh = moe.shape_of(cfg, T, flags)
+    x = dev_bf16(synth.hidden(cfg, 0))
+    for l, ly in enumerate(layers):
+        out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        nxt = layers[l + 1] if l + 1 < len(layers) else None
+        ly.forward_chain(x, out, wss[l], flags | (moe.MOE_LOGITS_GIVEN if l else 0), nxt,
+                         wss[l + 1] if nxt is not None else None)
+        ref = torch.empty_like(out)
+        ly.forward(x, ref, ws_ref, flags)
+        torch.cuda.synchronize()
+        pid, pw, _, _ = moe.moe_layer_routing(sh, wss[l])
+        rid, rw, _, _ = moe.moe_layer_routing(sh, ws_ref)
+        ids = ws_view(wss[l], pid, T * k, torch.int32).cpu().numpy().reshape(T, k)
+        w = ws_view(wss[l], pw, T * k, torch.float32).cpu().numpy().reshape(T, k)
+        r_ids = ws_view(ws_ref, rid, T * k, torch.int32).cpu().numpy().reshape(T, k)
+        r_w = ws_view(ws_ref, rw, T * k, torch.float32).cpu().numpy().reshape(T, k)
+        same = np.all(ids == r_ids, axis=1)
+        # (two f32 summation orders of the same logits can only part at a near tie)
+        assert (~same).sum() <= 1, f"layer {l}: {int((~same).sum())} tokens routed differently"
+        werr = float(np.max(np.abs(w[same] - r_w[same]))) if same.any() else 0.0
+        assert werr <= 1e-5, f"layer {l}: chained weights differ by {werr}"
+        a, b = out.float().cpu().numpy()[same], ref.float().cpu().numpy()[same]
+        rms = float(np.sqrt(np.mean(b.astype(np.float64) ** 2)))
+        err = float(np.max(np.abs(a - b))) / rms
+        say(f"chain layer {l}: max|chained-unchained|/rms = {err:.3e}, weights {werr:.1e}, "
+            f"{int((~same).sum())} tokens routed differently")
+        assert err <= 1e-2
+        x = out
