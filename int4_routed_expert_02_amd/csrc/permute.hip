@@ -53,13 +53,21 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t *__restrict__ ids
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x;
 
-    // totals and this block's prefix over earlier blocks, one expert per thread
+    // totals and this block's prefix over earlier blocks, one expert per
+    // thread; sixteen blocks' counts in flight at a time (integer sums, so the
+    // grouping does not change them)
     int total = 0, before = 0;
     if (tid < E) {
-        for (int q = 0; q < nblocks; ++q) {
-            const int c = bcounts[(size_t)q * E + tid];
-            total += c;
-            if (q < b) before += c;
+        constexpr int QB = 16;
+        for (int q0 = 0; q0 < nblocks; q0 += QB) {
+            int c[QB];
+#pragma unroll
+            for (int i = 0; i < QB; ++i) c[i] = q0 + i < nblocks ? bcounts[(size_t)(q0 + i) * E + tid] : 0;
+#pragma unroll
+            for (int i = 0; i < QB; ++i) {
+                total += c[i];
+                if (q0 + i < b) before += c[i];
+            }
         }
     }
     // exclusive scan of totals over experts (E <= 256): Hillis-Steele in LDS
