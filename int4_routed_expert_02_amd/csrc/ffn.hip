@@ -322,9 +322,10 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
 // ------------------------------------------------------------------ pipelined tiles (64 and 128 rows)
 
 // Tiles of 64 or 128 rows run a deeper pipeline: global memory is copied
-// straight into a ring of FF3_STAGES LDS stages (global_load_lds, 16 bytes
-// per lane), so loads in flight hold no registers and staging costs no
-// vector instructions.  Each wave's copy fills 1 KB of LDS contiguously:
+// straight into a ring of LDS stages (global_load_lds, 16 bytes per lane), so
+// loads in flight hold no registers and staging costs no vector instructions.
+// Three stages, or two when a stage exceeds 24 KB (int8 gate/up at 128
+// rows), so that two workgroups fit in a compute unit's 160 KB.  Each wave's copy fills 1 KB of LDS contiguously:
 //  - A (16-bit rows of 64 columns = 8 chunks of 16 bytes) is stored with the
 //    chunk slot XOR-swizzled by (row % 8), which makes the fragment reads
 //    conflict-free;
@@ -336,7 +337,6 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
 // one extra MFMA per 16-row block and k-step against a constant fragment
 // holding minus the offset: wave w takes the row blocks i = w (mod 4) and the
 // results are shared through LDS in the epilogue.
-constexpr int FF3_STAGES = 3;
 
 template <int MODE, int WBITS, int BM>
 struct Ff3 {
@@ -351,6 +351,7 @@ struct Ff3 {
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static_assert(LOADS % 4 == 0, "copies split evenly over the four waves");
     static constexpr int PER_WAVE = LOADS / 4;
+    static constexpr int NST = STAGE <= 24 * 1024 ? 3 : 2;  // ring stages
 };
 
 __device__ __forceinline__ void lds_copy16(const void *g, void *l)
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
         }
     }
     auto issue = [&](int kt) {
-        uint8_t *base = smem3 + (kt % FF3_STAGES) * C::STAGE;
+        uint8_t *base = smem3 + (kt % C::NST) * C::STAGE;
 #pragma unroll
         for (int j = 0; j < C::PER_WAVE; ++j) {
             const int l = wn + 4 * j;
@@ -463,15 +464,15 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 
     const int KT = a.K / FF_BK;
 #pragma unroll
-    for (int s0 = 0; s0 < FF3_STAGES - 1; ++s0)
+    for (int s0 = 0; s0 < C::NST - 1; ++s0)
         if (s0 < KT) issue(s0);
     for (int kt = 0; kt < KT; ++kt) {
         // stage kt has landed once at most the later stages' copies are outstanding
-        if (kt + 1 < KT) wait_vm<C::PER_WAVE * (FF3_STAGES - 2)>();
+        if (kt + 1 < KT) wait_vm<C::PER_WAVE * (C::NST - 2)>();
         else wait_vm<0>();
         ring_barrier();  // every wave's copies of stage kt are in LDS; stage kt - 1 is free
-        if (kt + FF3_STAGES - 1 < KT) issue(kt + FF3_STAGES - 1);
-        const uint8_t *sa = smem3 + (kt % FF3_STAGES) * C::STAGE;
+        if (kt + C::NST - 1 < KT) issue(kt + C::NST - 1);
+        const uint8_t *sa = smem3 + (kt % C::NST) * C::STAGE;
         const uint8_t *sb = sa + C::A_BYTES;
 #pragma unroll
         for (int ks = 0; ks < FF_BK / 32; ++ks) {
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
         // (8-byte writes), then copied out as whole rows with the down
         // kernel's k-slot order applied on the way
         constexpr int HP = BN * 2 + 16;  // LDS row pitch in bytes
-        static_assert(BM * HP <= FF3_STAGES * C::STAGE, "the h tile fits in the stage ring");
+        static_assert(BM * HP <= C::NST * C::STAGE, "the h tile fits in the stage ring");
         f32x4 sg[NB], su[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -580,12 +581,22 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 
 // ------------------------------------------------------------------ launchers
 
-// m-tile row count for a regime: mean rows per group decides
-int ffn_bm(int rows, int groups)
+// m-tile row count.  Few rows per group: 16-row tiles.  Otherwise 64-row
+// tiles, which on the measured shapes were never slower for the int4 down
+// GEMM and were faster elsewhere whenever 128-row tiles would leave the
+// chip's 512 workgroup slots (two per compute unit) partly idle: 128-row
+// tiles are kept when their estimated count (a group adds half a tile on
+// average) fills at least 90% of a round and no round is less than half full.
+int ffn_bm(int mode, int wbits, int rows, int groups, int nt)
 {
     const int mean = groups > 0 ? rows / groups : rows;
     if (mean < 24) return 16;
-    if (mean < 96) return 64;
+    if ((mode == 1 && wbits == 4) || mean < 96) return 64;
+    const long t128 = ((long)rows / 128 + (groups > 1 ? groups / 2 : 0)) * nt;
+    const long slots = 512;
+    if (t128 < slots * 9 / 10) return 64;
+    const long rem = t128 % slots;
+    if (rem != 0 && rem < slots / 2 && t128 < 4 * slots) return 64;
     return 128;
 }
 
@@ -605,7 +616,7 @@ static hipError_t launch_three(const FfnArgs &a, int slots, hipStream_t st)
     const int NT = a.N / 128;
     const long grid = (long)((slots + 7) / 8 * 8) * NT;
     if (grid <= 0) return hipSuccess;
-    const size_t lds = (size_t)FF3_STAGES * Ff3<MODE, WBITS, BM>::STAGE;
+    const size_t lds = (size_t)Ff3<MODE, WBITS, BM>::NST * Ff3<MODE, WBITS, BM>::STAGE;
     hipLaunchKernelGGL((k_ffn3<MODE, WBITS, BM>), dim3((unsigned)grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
@@ -616,7 +627,7 @@ static hipError_t launch_three(const FfnArgs &a, int slots, hipStream_t st)
 template <int MODE, int WBITS>
 static hipError_t launch_mode(const FfnArgs &a, int rows_total, int groups, hipStream_t st)
 {
-    const int bm = ffn_bm(rows_total, groups);
+    const int bm = ffn_bm(MODE, WBITS, rows_total, groups, a.N % 128 == 0 ? a.N / 128 : a.N / 64);
     const int ng = a.offsets ? groups : 1;
     const int slots = (rows_total + bm - 1) / bm + (a.offsets ? min(ng, rows_total) : 0);
     if (a.N % 128 == 0) {
