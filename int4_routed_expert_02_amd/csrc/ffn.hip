@@ -338,6 +338,11 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
 // holding minus the offset: wave w takes the row blocks i = w (mod 4) and the
 // results are shared through LDS in the epilogue.
 
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
 template <int MODE, int WBITS, int BM>
 struct Ff3 {
     static constexpr int NMAT = (MODE == 1) ? 1 : 2;
@@ -351,7 +356,10 @@ struct Ff3 {
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static_assert(LOADS % 4 == 0, "copies split evenly over the four waves");
     static constexpr int PER_WAVE = LOADS / 4;
-    static constexpr int NST = STAGE <= 24 * 1024 ? 3 : 2;  // ring stages
+    // ring stages: three, or two where three would not leave room for two
+    // workgroups per compute unit (deeper rings measured slower)
+    static constexpr int NST = STAGE <= 24 * 1024 ? 3 : 2;
+    static_assert(PER_WAVE * (NST - 2) < 64, "vmcnt range");
 };
 
 __device__ __forceinline__ void lds_copy16(const void *g, void *l)
@@ -365,6 +373,20 @@ __device__ __forceinline__ void wait_vm()
 {
     static_assert(N >= 0 && N < 64, "vmcnt field");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));  // gfx9 encoding
+}
+
+// Wait until at most min(later, L) stages of PW copies each are outstanding:
+// the stages after the one about to be read that were issued (fewer than L
+// near the end of the k loop).
+template <int PW, int L>
+__device__ __forceinline__ void wait_stages(int later)
+{
+    if constexpr (L == 0) {
+        wait_vm<0>();
+    } else {
+        if (later >= L) wait_vm<PW * L>();
+        else wait_stages<PW, L - 1>(later);
+    }
 }
 
 // Workgroup barrier of the stage ring.  It waits for this wave's LDS reads
@@ -412,6 +434,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
     if (!find_tile<BM>(a, slot, e, row0, rows)) return;
     const int n0 = nt * BN;
     const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(wn);  // the same, known wave-uniform
 
     // this lane's source for each of its wave's copies (fixed across stages)
     const uint8_t *src[C::PER_WAVE];
@@ -435,12 +458,15 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
             src[j] = qm + (size_t)e * a.qstride + (size_t)(n0 + n) * (size_t)a.K * WBITS / 8 + (lane % cpr) * 16;
         }
     }
-    auto issue = [&](int kt) {
+    // Copy j < A_LOADS / 4 of every wave is an A copy (8 rows).  Only the
+    // first AJ of them are issued: rows past 32 AJ are never read.
+    auto issue = [&](int kt, auto ajc) {
+        constexpr int AJ = decltype(ajc)::value;
         uint8_t *base = smem3 + (kt % C::NST) * C::STAGE;
 #pragma unroll
         for (int j = 0; j < C::PER_WAVE; ++j) {
-            const int l = wn + 4 * j;
-            const size_t adv = l < C::A_LOADS ? (size_t)kt * FF_BK * 2 : (size_t)kt * BKB;
+            if (j >= AJ && j < C::A_LOADS / 4) continue;
+            const size_t adv = j < C::A_LOADS / 4 ? (size_t)kt * FF_BK * 2 : (size_t)kt * BKB;
             lds_copy16(src[j] + adv, base + dst[j]);
         }
     };
@@ -463,43 +489,76 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
     auto mma = [](u32x4 x, u32x4 y, f32x4 c) { return F16 ? mfma_f16(x, y, c) : mfma_bf16(x, y, c); };
 
     const int KT = a.K / FF_BK;
+    // The k loop, specialised on MV, the number of 16-row blocks holding valid
+    // rows: rows past the tile's last 32-row group are not copied, and blocks
+    // past its last row take no fragment reads and no MFMAs (a group's last
+    // tile is often mostly padding).
+    auto kloop = [&](auto mvc) {
+        constexpr int MV = decltype(mvc)::value;
+        constexpr int AJ = (MV + 1) / 2;                       // A copies per wave and stage
+        constexpr int PW = C::PER_WAVE - (C::A_LOADS / 4 - AJ);  // copies per wave and stage
+        const IntC<AJ> ajc;
 #pragma unroll
-    for (int s0 = 0; s0 < C::NST - 1; ++s0)
-        if (s0 < KT) issue(s0);
-    for (int kt = 0; kt < KT; ++kt) {
-        // stage kt has landed once at most the later stages' copies are outstanding
-        if (kt + 1 < KT) wait_vm<C::PER_WAVE * (C::NST - 2)>();
-        else wait_vm<0>();
-        ring_barrier();  // every wave's copies of stage kt are in LDS; stage kt - 1 is free
-        if (kt + C::NST - 1 < KT) issue(kt + C::NST - 1);
-        const uint8_t *sa = smem3 + (kt % C::NST) * C::STAGE;
-        const uint8_t *sb = sa + C::A_BYTES;
+        for (int s0 = 0; s0 < C::NST - 1; ++s0)
+            if (s0 < KT) issue(s0, ajc);
+        for (int kt = 0; kt < KT; ++kt) {
+            // stage kt has landed once at most the later stages' copies are outstanding
+            wait_stages<PW, C::NST - 2>(KT - 1 - kt);
+            ring_barrier();  // every wave's copies of stage kt are in LDS; stage kt - 1 is free
+            if (kt + C::NST - 1 < KT) issue(kt + C::NST - 1, ajc);
+            const uint8_t *sa = smem3 + (kt % C::NST) * C::STAGE;
+            const uint8_t *sb = sa + C::A_BYTES;
 #pragma unroll
-        for (int ks = 0; ks < FF_BK / 32; ++ks) {
-            u32x4 af[MB];
+            for (int ks = 0; ks < FF_BK / 32; ++ks) {
+                u32x4 af[MV];
 #pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                const int r = i * 16 + (lane & 15);
-                const int chunk = ks * 4 + (lane >> 4);
-                af[i] = *(const u32x4 *)(sa + r * 128 + ((chunk ^ (r & 7)) * 16));
-            }
-            // (the correction blocks depend on the wave, so their fragments
-            // are read again rather than picked from af by a run-time index)
-#pragma unroll
-            for (int c = 0; c < CB; ++c) {
-                const int r = (wn + 4 * c) * 16 + (lane & 15);
-                const int chunk = ks * 4 + (lane >> 4);
-                cor[c] = mma(cneg, *(const u32x4 *)(sa + r * 128 + ((chunk ^ (r & 7)) * 16)), cor[c]);
-            }
-#pragma unroll
-            for (int x = 0; x < NMAT; ++x)
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const uint8_t *bp = sb + (x * BN + wn * (BN / 4) + j * 16 + (lane & 15)) * BKB;
-                    const u32x4 bf = weight_fragment<MODE, WBITS>(bp + ks * (BKB / 2) + (lane >> 4) * (WBITS / 2) * 2);
-#pragma unroll
-                    for (int i = 0; i < MB; ++i) acc[x][i][j] = mma(bf, af[i], acc[x][i][j]);
+                for (int i = 0; i < MV; ++i) {
+                    const int r = i * 16 + (lane & 15);
+                    const int chunk = ks * 4 + (lane >> 4);
+                    af[i] = *(const u32x4 *)(sa + r * 128 + ((chunk ^ (r & 7)) * 16));
                 }
+                // (the correction blocks depend on the wave, so their fragments
+                // are read again rather than picked from af by a run-time index;
+                // a block past the valid ones is skipped, by a wave-uniform test)
+#pragma unroll
+                for (int c = 0; c < CB; ++c) {
+                    if (4 * c >= MV) break;
+                    if (4 * c + 3 >= MV && wu + 4 * c >= MV) continue;
+                    const int r = (wn + 4 * c) * 16 + (lane & 15);
+                    const int chunk = ks * 4 + (lane >> 4);
+                    cor[c] = mma(cneg, *(const u32x4 *)(sa + r * 128 + ((chunk ^ (r & 7)) * 16)), cor[c]);
+                }
+#pragma unroll
+                for (int x = 0; x < NMAT; ++x)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        const uint8_t *bp = sb + (x * BN + wn * (BN / 4) + j * 16 + (lane & 15)) * BKB;
+                        const u32x4 bf = weight_fragment<MODE, WBITS>(bp + ks * (BKB / 2) + (lane >> 4) * (WBITS / 2) * 2);
+#pragma unroll
+                        for (int i = 0; i < MV; ++i) acc[x][i][j] = mma(bf, af[i], acc[x][i][j]);
+                    }
+            }
+        }
+    };
+    const int mv = (rows + 15) / 16;  // 1 .. MB
+    if constexpr (MB == 4) {
+        switch (mv) {
+        case 1: kloop(IntC<1>{}); break;
+        case 2: kloop(IntC<2>{}); break;
+        case 3: kloop(IntC<3>{}); break;
+        default: kloop(IntC<4>{}); break;
+        }
+    } else {
+        static_assert(MB == 8, "64- or 128-row tiles");
+        switch (mv) {
+        case 1: kloop(IntC<1>{}); break;
+        case 2: kloop(IntC<2>{}); break;
+        case 3: kloop(IntC<3>{}); break;
+        case 4: kloop(IntC<4>{}); break;
+        case 5: kloop(IntC<5>{}); break;
+        case 6: kloop(IntC<6>{}); break;
+        case 7: kloop(IntC<7>{}); break;
+        default: kloop(IntC<8>{}); break;
         }
     }
 
@@ -581,17 +640,18 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 
 // ------------------------------------------------------------------ launchers
 
-// m-tile row count.  Few rows per group: 16-row tiles.  Otherwise 64-row
-// tiles, which on the measured shapes were never slower for the int4 down
-// GEMM and were faster elsewhere whenever 128-row tiles would leave the
-// chip's 512 workgroup slots (two per compute unit) partly idle: 128-row
-// tiles are kept when their estimated count (a group adds half a tile on
-// average) fills at least 90% of a round and no round is less than half full.
+// m-tile row count.  Few rows per group: 16-row tiles.  Otherwise 128-row
+// tiles where they fill the chip's 512 workgroup slots (two per compute
+// unit): their estimated count (a group adds half a tile on average) fills at
+// least 90% of a round and no round is less than half full; else 64.  Padded
+// row blocks cost no MFMAs, so larger tiles mostly save weight re-reads.  The
+// int4 down GEMM always takes 64-row tiles (measured never slower: its stage
+// is small and the extra workgroups hide its short k loop's prologue).
 int ffn_bm(int mode, int wbits, int rows, int groups, int nt)
 {
     const int mean = groups > 0 ? rows / groups : rows;
     if (mean < 24) return 16;
-    if ((mode == 1 && wbits == 4) || mean < 96) return 64;
+    if (mode == 1 && wbits == 4) return 64;
     const long t128 = ((long)rows / 128 + (groups > 1 ? groups / 2 : 0)) * nt;
     const long slots = 512;
     if (t128 < slots * 9 / 10) return 64;
