@@ -4,34 +4,32 @@
 // The engine chooses kernels per shape by measurement (colibri README, "What's
 // implemented", integer-dot kernels: the single-row int4 case takes a
 // different path from the batched one).  Here, for T <= 32 tokens:
-//   k_dec_logits   router logits z = x W^T in f32 FMA, one workgroup per four
-//                  experts (W is the largest read of the router);
-//   k_dec_gateup   routed workgroups first select the top-k experts of every
-//                  token from z (sigmoid + bias, moe_select.h; each workgroup
-//                  takes the same decision, the first publishes ids, weights
-//                  and rsf * w), then one workgroup per (active expert, 64
-//                  intermediate rows): gathers
-//                  the pairs routed to its expert (batch-union: the expert's
-//                  rows are read once for all of them), streams its gate and up
-//                  rows straight from HBM into registers, MFMA on 16-pair
-//                  blocks, SwiGLU epilogue -> h [pair][I] f32;  the shared
-//                  expert's rows form extra units over all T tokens;
-//   k_dec_down     one workgroup per (expert, 128 output rows, 512-column chunk
-//                  of the reduction): h as an exact hi + lo bf16 pair, down rows
-//                  streamed to registers, epilogue scales by sd * rsf * w ->
-//                  partial y [chunk][pair][H];  the shared expert's units are
-//                  (128 output rows, 512-column chunk) over all T tokens;
-//   k_dec_combine  out = sum_j sum_chunk y + sum_chunk shared partials (+ x),
-//                  in a fixed order.
+//   k_dec_logits          router logits z = x W^T (exact split-bf16 MFMA) as 4
+//                         partial planes;
+//   k_dec_expert          one workgroup per unit of 128 intermediate rows of a
+//                         chosen expert (or of the shared expert): routed units
+//                         first take the routing decision of the batch from
+//                         the logits (every unit computes the same; the first
+//                         publishes ids, weights and rsf * w), find their
+//                         expert (the rank-th chosen one) and its pairs, then
+//                         stream gate/up rows into registers a few chunks
+//                         ahead of the MFMAs (16-pair blocks), SwiGLU -> h on
+//                         chip in f16, and the down slice (all output rows x
+//                         the unit's 128 columns) on f16 MFMA -> one f32
+//                         partial output plane per unit, scaled by the down
+//                         row scale and rsf * w;
+//   k_dec_combine         out = the partial planes summed in a fixed order
+//                         (+ x);
+//   k_dec_combine_logits  the same, plus the next layer's router logits of
+//                         the row it writes (stacked layers).
 // Buffers are indexed by pair, so no permutation is materialised: each
 // workgroup finds its expert's pairs by scanning the ids in ascending order.
 //
 // Weight loads: a wave owns 16 weight rows; lane (n = lane % 16, g = lane / 16)
 // loads 16-byte chunks (4c + g) of row n, c = 0..CPL-1, so the four lane
-// groups read 64 contiguous bytes of each row per instruction and the whole
-// stage is in flight before the first MFMA.  The k-slots of chunk c, word w
-// for lane group g are k = (4c + g) * 32 + 8w + [0, 8) (int4), and the A
-// fragments are read from LDS at the same k.
+// groups read 64 contiguous bytes of each row per instruction.  The k-slots
+// of chunk c, word w for lane group g are k = (4c + g) * 32 + 8w + [0, 8)
+// (int4), and the A fragments are read from LDS at the same k.
 #include "moe_device.h"
 #include "moe_launch.h"
 #include "moe_select.h"
@@ -188,10 +186,10 @@ __device__ __forceinline__ void cand_sort2(Cand &a, Cand &b)
 // The selected k are the first k, taken in that order; the weight of
 // selection j is s_j over the sum of the selected s (summed in selection
 // order); the tie gap is v_{k-1} - v_k.  Same results as moe_select.h.
-template <int KL, typename Mid>
+template <int KL>
 __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, const float *__restrict__ bias, int T,
                                                  int E, int k, int32_t *ids_l, float *w_l, bool pub,
-                                                 float *__restrict__ gap_g, Mid &&mid)
+                                                 float *__restrict__ gap_g)
 {
     const int tid = threadIdx.x, t = tid >> 3, q = tid & 7;
     Cand c[KL];
@@ -209,7 +207,6 @@ __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, c
         b0 = *(const f32x4 *)(bias + 8 * q);
         b1 = *(const f32x4 *)(bias + 8 * q + 4);
     }
-    mid();  // the caller's own work while the logits are in flight
     if (live) {
         float z[8];
         const f32x4 a0 = pa[0][0], a1 = pa[0][1];
@@ -369,22 +366,19 @@ struct DecArgs {
 
 // The routing decision of the batch into LDS (every routed workgroup takes
 // it, from the same logits, so all agree); the publishing workgroup also
-// writes ids, w, rsf * w and the tie gaps to global memory.  `mid` runs once,
-// while the logits are in flight.
-template <int EPL, typename Mid>
-__device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k, int32_t *ids_l, float *w_l, bool pub,
-                                          Mid &&mid)
+// writes ids, w, rsf * w and the tie gaps to global memory.
+template <int EPL>
+__device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k, int32_t *ids_l, float *w_l, bool pub)
 {
     const bool grouped = r.n_group > 1 && r.topk_group < r.n_group;
     if (!grouped && E <= 64 && E % 8 == 0 && k <= 3) {
         if (k == 1)
-            dec_select_lanes<2>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, mid);
+            dec_select_lanes<2>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
         else if (k == 2)
-            dec_select_lanes<3>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, mid);
+            dec_select_lanes<3>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
         else
-            dec_select_lanes<4>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap, mid);
+            dec_select_lanes<4>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
     } else {
-        mid();
         dec_select_waves<EPL>(r.zp, r.rb, T, E, k, r.n_group, r.topk_group, r.rsf, ids_l, w_l, pub, r.gap);
     }
     __syncthreads();
@@ -408,6 +402,7 @@ constexpr int DX_WCOLS = DX_TILES * 16;             // output columns per wave p
 constexpr int DX_RCOLS = DX_WAVES * DX_WCOLS;       // output columns per round (1024)
 constexpr int DX_LDY = DX_WCOLS + 4;                // padded row of a wave's staged down tile (floats)
 constexpr int GU_CPL = 8;                           // 16-byte gate/up chunks per lane per row per super-stage
+constexpr int GU_AHEAD = 4;                         // gate/up chunks in flight ahead of the MFMAs
 
 // Down weights of one round: lane (n, g) holds, for each of its wave's 8
 // output tiles tt, the 32 values of intermediate [32g, 32g + 32) of the
@@ -477,8 +472,7 @@ struct alignas(16) DxSmem {
     int32_t ids[DEC_MAXT * DEC_MAXK];        // routing of the batch
     float w[DEC_MAXT * DEC_MAXK];
     int flags[256];
-    uint16_t hh[DEC_MAXT * DX_LDH];          // h chunk, bf16 high part
-    uint16_t hl[DEC_MAXT * DX_LDH];          // h chunk, bf16 low part (h - high)
+    uint16_t hh[DEC_MAXT * DX_LDH];          // h chunk, f16
     float xsum[DEC_MAXT];                    // activation row sums (by staged row)
     float psc[DEC_MAXT];                     // output scale of each pair row (rsf * w, or 1)
     int arow[DEC_MAXT];                      // staged activation row of each pair row
@@ -528,12 +522,14 @@ __device__ __forceinline__ void xstage_store(const XStage<WBITS> &xs, DxSmem<WBI
 }
 
 // One unit: gate/up of 128 intermediate rows for the n pair rows of its batch
-// (SwiGLU -> h chunk, on chip as an exact bf16 high + low pair), then
+// (SwiGLU -> h chunk, on chip in f16), then
 // y_part = h_chunk . D[:, chunk]^T for every output column, scaled by the
 // down row scale and the row's output scale, stored to plane `chunk` of out.
-// The first super-stage's activations are already staged (rows 0..nr-1);
-// later super-stages are staged here.  Weight loads are issued gate/up first,
-// then the down slice, all before the first MFMA.
+// Each super-stage's activation rows (row r = token rtok(r), r < nr) are
+// loaded here just before its weight rows, so they land first (vector loads
+// complete in issue order) while the weights stream behind them.  Weight
+// loads are issued gate/up first, then the down slice, a few chunks ahead of
+// the MFMAs that consume them.
 template <int WBITS, int NMB, typename RowTok>
 __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm, int n, int nr, RowTok rtok,
                                             float rsum, const uint8_t *grow, const uint8_t *urow, float sg,
@@ -562,21 +558,22 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
     f32x4 sdv;
     u32x4 wg[CPL], wu[CPL];
     for (int ss = 0; ss < nss; ++ss) {
-        XStage<WBITS> xs;
-        if (ss > 0) xstage_load<WBITS>(xs, a, nr, ss, rtok);
         // gate and up chunk c in adjacent requests: the MFMAs on chunk c can
         // start once its pair has arrived
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
+        auto issue_gu = [&](int c) {
             wg[c] = *(const u32x4 *)(grow + (size_t)ss * SB + c * 64);
             wu[c] = *(const u32x4 *)(urow + (size_t)ss * SB + c * 64);
-        }
-        // the first round of down weights: in flight during the gate/up MFMAs
-        if (ss == nss - 1) load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, wave * DX_WCOLS, i0);
-        if (ss > 0) {
-            __syncthreads();  // the previous super-stage's A reads are done
-            xstage_store<WBITS>(xs, sm, nr, rsum);
-        }
+        };
+        XStage<WBITS> xs;
+        xstage_load<WBITS>(xs, a, nr, ss, rtok);
+        // The first GU_AHEAD chunks now, each later one as an earlier chunk is
+        // consumed (so a wave is not held at issue while the memory system is
+        // saturated, and its MFMAs overlap the stream); the down slice after
+        // the last gate/up chunk.
+#pragma unroll
+        for (int c = 0; c < GU_AHEAD; ++c) issue_gu(c);
+        if (ss > 0) __syncthreads();  // the previous super-stage's A reads are done
+        xstage_store<WBITS>(xs, sm, nr, rsum);
         if (ss == nss - 1) {
             // row sums: the TPR threads of a staged row are consecutive lanes
             float s = rsum;
@@ -587,6 +584,11 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
+            if (c + GU_AHEAD < CPL) issue_gu(c + GU_AHEAD);
+            else if (ss == nss - 1 && c + GU_AHEAD == CPL) {
+                load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, wave * DX_WCOLS, i0);
+                asm volatile("" ::: "memory");  // keeps the compiler from sinking these loads to their use
+            }
             if constexpr (WBITS == 4) {
 #pragma unroll
                 for (int wd = 0; wd < 4; ++wd) {
@@ -615,7 +617,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
         }
     }
     // SwiGLU epilogue: h for (row m, intermediate wave * 16 + ln) -> on-chip
-    // chunk as bf16 high + low.
+    // chunk in f16 (round to nearest even).
     const float bias = (WBITS == 4) ? INT4_BIAS : 0.f;
     const int hp = h_pos<WBITS>(wave * 16 + ln);
 #pragma unroll
@@ -631,17 +633,15 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
                 ua += acc[mb][1][ch][r];
             }
             const float h = m < n ? fast_silu((ga - corr) * sg) * ((ua - corr) * su) : 0.f;
-            const uint16_t hb = f32_to_bf16(h);
-            sm.hh[m * DX_LDH + hp] = hb;
-            sm.hl[m * DX_LDH + hp] = f32_to_bf16(h - bf16_to_f32(hb));
+            sm.hh[m * DX_LDH + hp] = __builtin_bit_cast(uint16_t, (_Float16)h);
         }
     }
     __syncthreads();
-    // down: A = h chunk (rows m, 128 k in four 32-steps, high and low planes),
+    // down on f16 matrix cores: A = h chunk (rows m, 128 k in four 32-steps),
     // one 16-row block at a time (the weights are unpacked again per block).
-    // With int4 weights the B fragments hold q + 136: each tile starts from
-    // -136 * (row sum of high + low), itself an MFMA against a constant
-    // fragment, so the accumulation yields the sum over q.  Each wave stages
+    // The B fragments hold q + 1032 (int4) or q + 1152 (int8): each tile
+    // starts from minus that constant times the row sum of h, itself an MFMA
+    // against a constant fragment, so the accumulation yields the sum over q.  Each wave stages
     // its 16 x 128 result in LDS and writes it out two rows at a time as
     // 16-byte stores scaled by the down row scale and the row's output scale.
     const int chunk = i0 / DX_ROWS;
@@ -652,32 +652,24 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
 #pragma unroll 1
         for (int mb = 0; mb < NMB; ++mb) {
             if (mb * 16 >= n) break;
-            u32x4 fh[4], fl[4];
+            u32x4 fh[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                fh[s] = *(const u32x4 *)(sm.hh + (mb * 16 + ln) * DX_LDH + 32 * g + 8 * s);
-                fl[s] = *(const u32x4 *)(sm.hl + (mb * 16 + ln) * DX_LDH + 32 * g + 8 * s);
-            }
-            f32x4 d0 = {0.f, 0.f, 0.f, 0.f};
-            if (WBITS == 4) {
-                const u32x4 c136 = u32x4{0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u};  // bf16 136
-                f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 4; ++s) fh[s] = *(const u32x4 *)(sm.hh + (mb * 16 + ln) * DX_LDH + 32 * g + 8 * s);
+            // f16 1032 / 1152
+            constexpr uint32_t CB16 = WBITS == 4 ? 0x64086408u : 0x64806480u;
+            const u32x4 cb = u32x4{CB16, CB16, CB16, CB16};
+            f32x4 cs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    cs = mfma_bf16(fh[s], c136, cs);
-                    cs = mfma_bf16(fl[s], c136, cs);
-                }
-                d0 = -cs;
-            }
+            for (int s = 0; s < 4; ++s) cs = mfma_f16(fh[s], cb, cs);
+            const f32x4 d0 = -cs;
 #pragma unroll
             for (int tt = 0; tt < DX_TILES; ++tt) {
                 f32x4 d = d0;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const u32x4 b = WBITS == 4 ? unpack_int4x8(dw.d[tt][s])
-                                               : unpack_int8x8(u32x2{dw.d[tt][2 * s], dw.d[tt][2 * s + 1]});
-                    d = mfma_bf16(fh[s], b, d);
-                    d = mfma_bf16(fl[s], b, d);
+                    const u32x4 b = WBITS == 4 ? unpack_int4x8_f16(dw.d[tt][s])
+                                               : unpack_int8x8_f16(u32x2{dw.d[tt][2 * s], dw.d[tt][2 * s + 1]});
+                    d = mfma_f16(fh[s], b, d);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) yl[(4 * g + r) * DX_LDY + tt * 16 + ln] = d[r];
@@ -709,7 +701,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
 // batch (every one computes the same from the logits), then gather the pairs
 // routed to their expert; units beyond the chosen experts exit.  A unit's
 // loads are its activation rows, its gate/up rows and its down slice (all
-// output rows, the chunk's 128 columns), all in flight before the first MFMA.
+// output rows, the chunk's 128 columns), issued a few chunks ahead of the MFMAs.
 //
 // XCD-aware placement: workgroup b runs on XCD b % 8; logical units 4q ..
 // 4q + 3 (chunks whose down slices share 128-byte lines, or the token
@@ -754,17 +746,14 @@ __global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nun
     };
     int n, nrows, nr;
     float *out;
-    float rsum = 0.f;
-    XStage<WBITS> xs;
+    const float rsum = 0.f;
     if (shared) {
         // 16 tokens of one half: staged rows r = pair rows r = token 16 th + r
         const int th = L % nth;
         n = a.T - 16 * th < 16 ? a.T - 16 * th : 16;
         nr = n;
         auto rtok = [th](int r) { return 16 * th + r; };
-        xstage_load<WBITS>(xs, a, nr, 0, rtok);
         locate(a.sgq, a.suq, a.sdq, a.sgs, a.sus, a.sds, a.Ish, (L / nth) * DX_ROWS);
-        xstage_store<WBITS>(xs, sm, nr, rsum);
         nrows = a.T;
         out = a.ysp;
         if (tid < DEC_MAXT) {
@@ -776,19 +765,16 @@ __global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nun
         expert_body<WBITS, 1>(a, sm, n, nr, rtok, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
         return;
     }
-    // routed: every token's activation row is staged (row t = token t) while
-    // the routing logits are in flight
+    // routed: the routing decision, then the unit's expert and pairs; only
+    // the rows of those pairs are staged (row r = token of pair r)
     const int v = L - nsh, per = a.I / DX_ROWS;
-    nr = a.T;
-    auto rtok = [](int r) { return r; };
-    dec_route<EPL>(a, a.T, a.E, a.k, sm.ids, sm.w, v == 0, [&]() {
-        xstage_load<WBITS>(xs, a, nr, 0, rtok);
-        xstage_store<WBITS>(xs, sm, nr, rsum);
-    });
+    dec_route<EPL>(a, a.T, a.E, a.k, sm.ids, sm.w, v == 0);
     const int2 un = dec_locate_unit(sm.ids, a.T * a.k, a.k, a.E, v / per, sm.flags, sm.plist, sm.tok, sm.res);
     const int e = __builtin_amdgcn_readfirstlane(un.x);
     if (e < 0) return;
     n = __builtin_amdgcn_readfirstlane(un.y);
+    nr = n;
+    auto rtok = [&](int r) { return sm.tok[r]; };
     locate(a.gq + (size_t)e * a.qstride, a.uq + (size_t)e * a.qstride, a.dq + (size_t)e * a.dqstride,
            a.gs + (size_t)e * a.sstride, a.us + (size_t)e * a.sstride, a.ds + (size_t)e * a.dsstride, a.I,
            (v % per) * DX_ROWS);
@@ -796,7 +782,7 @@ __global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nun
     out = a.yp;
     if (tid < DEC_MAXT) {
         sm.psc[tid] = tid < n ? a.rsf * sm.w[sm.plist[tid]] : 0.f;
-        sm.arow[tid] = tid < n ? sm.tok[tid] : 0;
+        sm.arow[tid] = tid < n ? tid : 0;
     }
     __syncthreads();
     if (n <= 16)
