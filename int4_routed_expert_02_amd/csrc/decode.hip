@@ -158,130 +158,137 @@ __device__ __noinline__ void dec_select_waves(const float *__restrict__ zp, cons
     }
 }
 
-// One selection candidate: selection score v (sigmoid + bias), unbiased score
-// s, expert id i.  Order: larger v first, equal v -> lower id first (the
-// order of moe_select.h); an empty slot (i = INT_MAX, v = -inf) loses to all.
-struct Cand {
-    float v, s;
-    int i;
-};
-__device__ __forceinline__ bool cand_before(const Cand &a, const Cand &b)
+// Selection order as one 64-bit key: the score's bits made monotone in the
+// float order (-0 taken as +0, NaN below everything), then the complement of
+// the id, so a larger key is a larger score or, at equal scores, a lower id.
+// Key 0 marks an empty or taken slot.
+__device__ __forceinline__ uint64_t sel_key(float v, int id)
 {
-    return a.v > b.v || (a.v == b.v && a.i < b.i);
-}
-__device__ __forceinline__ void cand_sort2(Cand &a, Cand &b)
-{
-    if (cand_before(b, a)) {
-        const Cand t = a;
-        a = b;
-        b = t;
-    }
+    uint32_t b = __float_as_uint(v);
+    if (b == 0x80000000u) b = 0;
+    uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    if (v != v) o = 0;
+    return ((uint64_t)o << 32) | (0xFFFFFFFFu - (uint32_t)id);
 }
 
-// Fast selection when no group limit applies, E <= 64, E % 8 == 0 and k < KL:
-// eight lanes per token (lane slice q scans experts 8q .. 8q + 7), each keeps
-// its best KL candidates sorted, then three butterfly merges over the slices
-// (bitonic: pair own entry j with the partner's entry KL - 1 - j, keep the
-// better, re-sort) leave the batch-wide best KL in every lane of the token.
-// The selected k are the first k, taken in that order; the weight of
-// selection j is s_j over the sum of the selected s (summed in selection
-// order); the tie gap is v_{k-1} - v_k.  Same results as moe_select.h.
+// Data-parallel-primitive lane moves (no LDS round trip): DPP_X1 and DPP_X2
+// swap lanes within each group of four (xor 1, xor 2), DPP_HM mirrors each
+// half-row of eight (lane i <-> 7 - i), DPP_RM each row of sixteen.
+constexpr int DPP_X1 = 0xB1, DPP_X2 = 0x4E, DPP_HM = 0x141, DPP_RM = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x)
+{
+    return ((uint64_t)dpp_u32<CTRL>((uint32_t)(x >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)x);
+}
+
+// maximum / bitwise or over each group of eight lanes, in every lane of it
+__device__ __forceinline__ uint64_t max8_u64(uint64_t b)
+{
+    uint64_t x = dpp_u64<DPP_X1>(b);
+    b = x > b ? x : b;
+    x = dpp_u64<DPP_X2>(b);
+    b = x > b ? x : b;
+    x = dpp_u64<DPP_HM>(b);
+    return x > b ? x : b;
+}
+
+__device__ __forceinline__ uint32_t or8_u32(uint32_t b)
+{
+    b |= dpp_u32<DPP_X1>(b);
+    b |= dpp_u32<DPP_X2>(b);
+    return b | dpp_u32<DPP_HM>(b);
+}
+
+// Fast selection when no group limit applies, E <= 64, E % 8 == 0 and
+// k < KL: eight lanes per token (lane slice q holds experts 8q .. 8q + 7).
+// KL rounds, each taking the best remaining key of the token: a lane's best
+// of its eight, the maximum over the token's eight lanes, and the owner lane
+// retires the winner.  Rounds 0 .. k-1 are the selection in order; round k
+// gives the tie gap v_{k-1} - v_k.  The weight of selection j is s_j over the
+// sum of the selected s (summed in selection order).  Same results as
+// moe_select.h.  Waves holding no token skip the work.
 template <int KL>
 __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, const float *__restrict__ bias, int T,
                                                  int E, int k, int32_t *ids_l, float *w_l, bool pub,
                                                  float *__restrict__ gap_g)
 {
     const int tid = threadIdx.x, t = tid >> 3, q = tid & 7;
-    Cand c[KL];
-#pragma unroll
-    for (int j = 0; j < KL; ++j) c[j] = Cand{-INFINITY, 0.f, 0x7fffffff};
+    if (__builtin_amdgcn_readfirstlane(tid >> 6) * 8 >= T) return;  // (wave-uniform)
     const bool live = t < T && 8 * q < E;
-    f32x4 pa[LG_NP][2], b0, b1;
+    uint64_t key[8];
+    float sv[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        key[r] = 0;
+        sv[r] = 0.f;
+    }
     if (live) {
+        f32x4 pa[LG_NP][2];
 #pragma unroll
         for (int p = 0; p < LG_NP; ++p) {
             const f32x4 *pp = (const f32x4 *)(zp + ((size_t)p * T + t) * E + 8 * q);
             pa[p][0] = pp[0];
             pa[p][1] = pp[1];
         }
-        b0 = *(const f32x4 *)(bias + 8 * q);
-        b1 = *(const f32x4 *)(bias + 8 * q + 4);
-    }
-    if (live) {
-        float z[8];
-        const f32x4 a0 = pa[0][0], a1 = pa[0][1];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            z[r] = a0[r];
-            z[r + 4] = a1[r];
-        }
-#pragma unroll
-        for (int p = 1; p < LG_NP; ++p)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                z[r] += pa[p][0][r];
-                z[r + 4] += pa[p][1][r];
-            }
+        const f32x4 b0 = *(const f32x4 *)(bias + 8 * q), b1 = *(const f32x4 *)(bias + 8 * q + 4);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const float sc = __builtin_amdgcn_rcpf(1.0f + __expf(-z[r]));
-            Cand x{sc + (r < 4 ? b0[r] : b1[r - 4]), sc, 8 * q + r};
-            // insert into the sorted list (drop the last)
+            float z = r < 4 ? pa[0][0][r] : pa[0][1][r - 4];
 #pragma unroll
-            for (int j = 0; j < KL; ++j)
-                if (cand_before(x, c[j])) {
-                    const Cand tmp = c[j];
-                    c[j] = x;
-                    x = tmp;
-                }
+            for (int p = 1; p < LG_NP; ++p) z += r < 4 ? pa[p][0][r] : pa[p][1][r - 4];
+            const float sc = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+            sv[r] = sc;
+            key[r] = sel_key(sc + (r < 4 ? b0[r] : b1[r - 4]), 8 * q + r);
         }
     }
+    int sid[KL];
+    float ss[KL], vv[KL];
+    bool has = true;
 #pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {
-        Cand o[KL];
+    for (int j = 0; j < KL; ++j) {
+        uint64_t b = key[0];
 #pragma unroll
-        for (int j = 0; j < KL; ++j) {
-            o[j].v = __shfl_xor(c[j].v, m, WAVE);
-            o[j].s = __shfl_xor(c[j].s, m, WAVE);
-            o[j].i = __shfl_xor(c[j].i, m, WAVE);
-        }
+        for (int r = 1; r < 8; ++r) b = key[r] > b ? key[r] : b;
+        b = max8_u64(b);
+        const int id = (int)(0xFFFFFFFFu - (uint32_t)b);
+        uint32_t mine = 0;  // the winner's s from its owner lane (the others give 0 bits)
 #pragma unroll
-        for (int j = 0; j < KL; ++j)
-            if (cand_before(o[KL - 1 - j], c[j])) c[j] = o[KL - 1 - j];
-        // c is now bitonic; sort it (KL <= 4)
-        if (KL == 4) {
-            cand_sort2(c[0], c[2]);
-            cand_sort2(c[1], c[3]);
-        }
-        if (KL >= 3) {
-            cand_sort2(c[0], c[1]);
-            cand_sort2(c[KL - 2], c[KL - 1]);
-            if (KL == 3) cand_sort2(c[0], c[1]);
-        } else {
-            cand_sort2(c[0], c[1]);
-        }
+        for (int r = 0; r < 8; ++r)
+            if (b != 0 && 8 * q + r == id) {
+                mine = __float_as_uint(sv[r]);
+                key[r] = 0;
+            }
+        ss[j] = __uint_as_float(or8_u32(mine));
+        sid[j] = id;
+        // the score of the key: invert the monotone map
+        const uint32_t o = (uint32_t)(b >> 32);
+        vv[j] = __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+        if (j == k) has = b != 0;
     }
     if (t < T && q == 0) {
         float ssum = 0.f;
 #pragma unroll
         for (int j = 0; j < KL - 1; ++j)
-            if (j < k) ssum += c[j].s;
+            if (j < k) ssum += ss[j];
 #pragma unroll
         for (int j = 0; j < KL - 1; ++j)
             if (j < k) {
-                ids_l[t * k + j] = c[j].i;
-                w_l[t * k + j] = c[j].s / ssum;
+                ids_l[t * k + j] = sid[j];
+                w_l[t * k + j] = ss[j] / ssum;
             }
         if (pub) {
             float nv = -INFINITY, kv = 0.f;
-            bool has = false;
 #pragma unroll
             for (int j = 0; j < KL; ++j) {
-                if (j == k - 1) kv = c[j].v;
-                if (j == k) {
-                    nv = c[j].v;
-                    has = c[j].i != 0x7fffffff;
-                }
+                if (j == k - 1) kv = vv[j];
+                if (j == k) nv = vv[j];
             }
             gap_g[t] = has ? kv - nv : INFINITY;
         }
@@ -290,54 +297,73 @@ __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, c
 
 // ------------------------------------------------------------- pair lists
 
-// Wave 0 alone: the rank-th chosen expert of the batch (ascending id) and the
-// pairs routed to it in ascending order -> list (their tokens -> tok).  A
-// single wave needs no barrier between its own LDS steps (a wave's LDS
-// operations complete in order); one barrier publishes the result.  Returns
-// the expert (or -1 when fewer experts are chosen) and its pair count.
-__device__ __forceinline__ int2 dec_locate_unit(const int32_t *ids, int P, int k, int E, int rank, int *flags,
-                                                int *list, int *tok, int *res)
+// A unit's pair rows, one per lane: lane s < n holds pair row s (its pair
+// index, token and output scale); other lanes hold pair 0, token 0, scale 0.
+struct PairRows {
+    int pair, tok;
+    float psc;
+};
+
+// Every wave on its own (no LDS table, no barrier): the rank-th chosen
+// expert of the batch (ascending id) from the ids in LDS, and the pairs
+// routed to it in ascending order, compacted into lanes.  The chosen set is
+// an or over the pairs of one-hot words (EW words of 64 experts), reduced
+// within rows of sixteen lanes by lane moves and across the four rows in
+// scalar registers.  Returns the expert (-1 when fewer experts are chosen)
+// and the pair count, both wave-uniform.
+template <int EW>
+__device__ __forceinline__ int2 dec_locate_wave(const int32_t *ids, int P, int k, int E, int rank, PairRows &pr)
 {
-    const int tid = threadIdx.x, lane = tid & 63;
-    if (tid < WAVE) {
-        for (int e = lane; e < E; e += WAVE) flags[e] = 0;
-        for (int p = lane; p < P; p += WAVE) {
-            const int e = ids[p];
-            if ((unsigned)e < (unsigned)E) flags[e] = 1;
-        }
-        int before = 0, found = -1;
-        for (int e0 = 0; e0 < E; e0 += WAVE) {
-            const bool on = (e0 + lane < E) && flags[e0 + lane];
-            const uint64_t m = __ballot(on);
-            const int cnt = __popcll(m);
-            if (found < 0 && rank < before + cnt) {
-                const int want = rank - before;
-                const bool me = on && __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)))) == want;
-                found = e0 + (int)__builtin_ctzll(__ballot(me));
-            }
-            before += cnt;
-        }
-        int n = 0;
-        if (found >= 0) {
-            for (int p0 = 0; p0 < P; p0 += WAVE) {
-                const int p = p0 + lane;
-                const bool hit = p < P && ids[p] == found;
-                const uint64_t m = __ballot(hit);
-                if (hit) {
-                    const int slot = n + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-                    list[slot] = p;
-                    tok[slot] = p / k;
-                }
-                n += __popcll(m);
-            }
-        }
-        if (lane == 0) {
-            res[0] = found;
-            res[1] = n;
-        }
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes below this one
+    uint32_t m[2 * EW];
+#pragma unroll
+    for (int w = 0; w < 2 * EW; ++w) m[w] = 0;
+    for (int p0 = 0; p0 < P; p0 += WAVE) {
+        const int p = p0 + lane;
+        const int e = p < P ? ids[p] : -1;
+#pragma unroll
+        for (int w = 0; w < 2 * EW; ++w)
+            if ((unsigned)(e - 32 * w) < 32u && e < E) m[w] |= 1u << (e - 32 * w);
     }
-    __syncthreads();
-    return int2{res[0], res[1]};
+    int found = -1, before = 0;
+#pragma unroll
+    for (int w = 0; w < EW; ++w) {
+        uint64_t mw = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t x = or8_u32(m[2 * w + h]);
+            x |= dpp_u32<DPP_RM>(x);
+            const uint32_t r = __builtin_amdgcn_readlane(x, 0) | __builtin_amdgcn_readlane(x, 16) |
+                               __builtin_amdgcn_readlane(x, 32) | __builtin_amdgcn_readlane(x, 48);
+            mw |= (uint64_t)r << (32 * h);
+        }
+        const int cnt = __popcll(mw);
+        if (found < 0 && rank < before + cnt) {
+            const bool me = ((mw >> lane) & 1ull) && __popcll(mw & lt) == rank - before;
+            found = 64 * w + (int)__builtin_ctzll(__ballot(me));
+        }
+        before += cnt;
+    }
+    found = __builtin_amdgcn_readfirstlane(found);
+    int n = 0;
+    pr = PairRows{0, 0, 0.f};
+    if (found >= 0) {
+        for (int p0 = 0; p0 < P; p0 += WAVE) {
+            const int p = p0 + lane;
+            const bool hit = p < P && ids[p] == found;
+            const uint64_t bm = __ballot(hit);
+            // forward permute: a hit lane sends its pair to lane n + (hits below it);
+            // the others to lane 63, which no pair row reaches (n <= T <= 32)
+            const int dst = hit ? n + __popcll(bm & lt) : 63;
+            const int got = __builtin_amdgcn_ds_permute(dst * 4, p);
+            const int c = __popcll(bm);
+            if (lane >= n && lane < n + c) pr.pair = got;
+            n += c;
+        }
+        if (lane < n) pr.tok = pr.pair / k;
+    }
+    return int2{found, n};
 }
 
 struct DecArgs {
@@ -471,13 +497,8 @@ struct alignas(16) DxSmem {
     } u;
     int32_t ids[DEC_MAXT * DEC_MAXK];        // routing of the batch
     float w[DEC_MAXT * DEC_MAXK];
-    int flags[256];
     uint16_t hh[DEC_MAXT * DX_LDH];          // h chunk, f16
-    float xsum[DEC_MAXT];                    // activation row sums (by staged row)
-    float psc[DEC_MAXT];                     // output scale of each pair row (rsf * w, or 1)
-    int arow[DEC_MAXT];                      // staged activation row of each pair row
-    int plist[DEC_MAXT], tok[DEC_MAXT];
-    int res[2];
+    float xsum[DEC_MAXT];                    // activation row sums (by staged row = pair row)
 };
 
 // Activation staging: 16 threads per row, 32 rows; row r of the staging
@@ -491,12 +512,13 @@ struct XStage {
     u32x4 v[XPT];
 };
 
-template <int WBITS, typename RowTok>
-__device__ __forceinline__ void xstage_load(XStage<WBITS> &xs, const DecArgs &a, int nr, int ss, RowTok rtok)
+template <int WBITS>
+__device__ __forceinline__ void xstage_load(XStage<WBITS> &xs, const DecArgs &a, int nr, int ss, const PairRows &pr)
 {
     constexpr int TPR = XStage<WBITS>::TPR, KS = DxSmem<WBITS>::KS;
     const int srow = threadIdx.x / TPR, csub = threadIdx.x % TPR;
-    const uint16_t *src = srow < nr ? a.x + (size_t)rtok(srow) * a.H + (size_t)ss * KS + csub * 8 : nullptr;
+    const int tk = __shfl(pr.tok, srow, WAVE);  // staged row srow holds pair row srow (srow < 32)
+    const uint16_t *src = srow < nr ? a.x + (size_t)tk * a.H + (size_t)ss * KS + csub * 8 : nullptr;
 #pragma unroll
     for (int j = 0; j < XStage<WBITS>::XPT; ++j)
         xs.v[j] = src ? *(const u32x4 *)(src + j * 8 * TPR) : u32x4{0u, 0u, 0u, 0u};
@@ -525,13 +547,13 @@ __device__ __forceinline__ void xstage_store(const XStage<WBITS> &xs, DxSmem<WBI
 // (SwiGLU -> h chunk, on chip in f16), then
 // y_part = h_chunk . D[:, chunk]^T for every output column, scaled by the
 // down row scale and the row's output scale, stored to plane `chunk` of out.
-// Each super-stage's activation rows (row r = token rtok(r), r < nr) are
+// Each super-stage's activation rows (staged row r = pair row r, r < nr) are
 // loaded here just before its weight rows, so they land first (vector loads
 // complete in issue order) while the weights stream behind them.  Weight
 // loads are issued gate/up first, then the down slice, a few chunks ahead of
 // the MFMAs that consume them.
-template <int WBITS, int NMB, typename RowTok>
-__device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm, int n, int nr, RowTok rtok,
+template <int WBITS, int NMB>
+__device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm, int n, int nr, const PairRows &pr,
                                             float rsum, const uint8_t *grow, const uint8_t *urow, float sg,
                                             float su, const uint8_t *dq, const float *dsc, int64_t drstride,
                                             int i0, float *out, int nrows)
@@ -553,7 +575,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
     const int nss = a.H / KS;
     const uint16_t *ap[NMB];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) ap[mb] = sm.u.a + sm.arow[mb * 16 + ln] * LDA;
+    for (int mb = 0; mb < NMB; ++mb) ap[mb] = sm.u.a + (mb * 16 + ln < n ? mb * 16 + ln : 0) * LDA;
     DownW<WBITS> dw;
     f32x4 sdv;
     u32x4 wg[CPL], wu[CPL];
@@ -565,7 +587,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
             wu[c] = *(const u32x4 *)(urow + (size_t)ss * SB + c * 64);
         };
         XStage<WBITS> xs;
-        xstage_load<WBITS>(xs, a, nr, ss, rtok);
+        xstage_load<WBITS>(xs, a, nr, ss, pr);
         // The first GU_AHEAD chunks now, each later one as an earlier chunk is
         // consumed (so a wave is not held at issue while the memory system is
         // saturated, and its MFMAs overlap the stream); the down slice after
@@ -625,7 +647,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = mb * 16 + g * 4 + r;
-            const float corr = bias * sm.xsum[sm.arow[m]];
+            const float corr = bias * sm.xsum[m < n ? m : 0];
             float ga = acc[mb][0][0][r], ua = acc[mb][1][0][r];
 #pragma unroll
             for (int ch = 1; ch < NCH; ++ch) {
@@ -680,14 +702,15 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
 #pragma unroll
             for (int rr = 0; rr < 16; rr += 2) {
                 const int row = rr + half;
+                const int m = mb * 16 + row;
+                const float osc = __shfl(pr.psc, m, WAVE);  // pair row m's scale and pair (m < 32)
+                const int prow = __shfl(pr.pair, m, WAVE);
                 if (row < nrw) {
-                    const int m = mb * 16 + row;
-                    const float osc = sm.psc[m];
                     const f32x4 v = *(const f32x4 *)(yl + row * DX_LDY + q4);
                     f32x4 o;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) o[q] = v[q] * sdv[q] * osc;
-                    *(f32x4 *)(out + ((size_t)chunk * nrows + sm.plist[m]) * a.H + col0 + q4) = o;
+                    *(f32x4 *)(out + ((size_t)chunk * nrows + prow) * a.H + col0 + q4) = o;
                 }
             }
         }
@@ -752,43 +775,33 @@ __global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nun
         const int th = L % nth;
         n = a.T - 16 * th < 16 ? a.T - 16 * th : 16;
         nr = n;
-        auto rtok = [th](int r) { return 16 * th + r; };
+        const PairRows pr{16 * th + lane, 16 * th + lane, 1.0f};
         locate(a.sgq, a.suq, a.sdq, a.sgs, a.sus, a.sds, a.Ish, (L / nth) * DX_ROWS);
         nrows = a.T;
         out = a.ysp;
-        if (tid < DEC_MAXT) {
-            sm.plist[tid] = 16 * th + tid;
-            sm.arow[tid] = tid < n ? tid : 0;
-            sm.psc[tid] = 1.0f;
-        }
-        __syncthreads();
-        expert_body<WBITS, 1>(a, sm, n, nr, rtok, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
+        expert_body<WBITS, 1>(a, sm, n, nr, pr, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
         return;
     }
     // routed: the routing decision, then the unit's expert and pairs; only
     // the rows of those pairs are staged (row r = token of pair r)
     const int v = L - nsh, per = a.I / DX_ROWS;
     dec_route<EPL>(a, a.T, a.E, a.k, sm.ids, sm.w, v == 0);
-    const int2 un = dec_locate_unit(sm.ids, a.T * a.k, a.k, a.E, v / per, sm.flags, sm.plist, sm.tok, sm.res);
+    PairRows pr;
+    const int2 un = dec_locate_wave<EPL>(sm.ids, a.T * a.k, a.k, a.E, v / per, pr);
     const int e = __builtin_amdgcn_readfirstlane(un.x);
     if (e < 0) return;
     n = __builtin_amdgcn_readfirstlane(un.y);
     nr = n;
-    auto rtok = [&](int r) { return sm.tok[r]; };
+    pr.psc = lane < n ? a.rsf * sm.w[pr.pair] : 0.f;
     locate(a.gq + (size_t)e * a.qstride, a.uq + (size_t)e * a.qstride, a.dq + (size_t)e * a.dqstride,
            a.gs + (size_t)e * a.sstride, a.us + (size_t)e * a.sstride, a.ds + (size_t)e * a.dsstride, a.I,
            (v % per) * DX_ROWS);
     nrows = a.T * a.k;
     out = a.yp;
-    if (tid < DEC_MAXT) {
-        sm.psc[tid] = tid < n ? a.rsf * sm.w[sm.plist[tid]] : 0.f;
-        sm.arow[tid] = tid < n ? tid : 0;
-    }
-    __syncthreads();
     if (n <= 16)
-        expert_body<WBITS, 1>(a, sm, n, nr, rtok, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
+        expert_body<WBITS, 1>(a, sm, n, nr, pr, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
     else
-        expert_body<WBITS, 2>(a, sm, n, nr, rtok, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
+        expert_body<WBITS, 2>(a, sm, n, nr, pr, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
 }
 
 // ---------------------------------------------------------------- combine
