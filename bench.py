@@ -256,7 +256,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 MFMA, int4 weights, f32 accumulate",
+        "dtype": "bf16 MFMA gate/up, f16 MFMA down, int4 weights, f32 accumulate",
         "data": "synthetic (seeded, random-init weights of the Colibri-Nano MoE layer shape)",
         "config": {"workload": cfg.name, "T": T, "layers": L, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
                    "I_shared": cfg.I_sh, "global_batch": T, "parallelism": "single GPU",
@@ -449,7 +449,7 @@ def bench_prefill(args, cfg, moe, synth, torch, np, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 MFMA, int4 weights, f32 accumulate",
+        "dtype": "bf16 MFMA gate/up, f16 MFMA down, int4 weights, f32 accumulate",
         "data": "synthetic (seeded)",
         "config": {"workload": cfg.name, "T": T, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
                    "I_shared": cfg.I_sh, "shared_bits": cfg.shared_bits, "global_batch": T,
