@@ -37,7 +37,7 @@ class Shape(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
                 ("shared_bits", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("top_p", ctypes.c_float)]
 
 
 class QMat(ctypes.Structure):
@@ -104,7 +104,8 @@ def _chk(st: int, what: str):
 
 def shape_of(cfg, T: Optional[int] = None, residual: bool = False) -> Shape:
     return Shape(cfg.T if T is None else T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_sh, cfg.shared_bits,
-                 cfg.n_group, cfg.topk_group, cfg.rsf, ADD_RESIDUAL if residual else 0)
+                 cfg.n_group, cfg.topk_group, cfg.rsf, ADD_RESIDUAL if residual else 0,
+                 float(getattr(cfg, "top_p", 0.0)))
 
 
 class LayerWeights:

@@ -202,6 +202,7 @@ static int check_shape(const oracle_shape *sh)
     if (sh->topk_group <= 0 || sh->topk_group > sh->n_group) return O_ERR_SHAPE;
     if (sh->n_group > 1 && sh->E / sh->n_group < 2) return O_ERR_SHAPE;
     if (sh->top_k > sh->topk_group * (sh->E / sh->n_group)) return O_ERR_SHAPE;
+    if (sh->top_p != sh->top_p || (sh->top_p > 0.f && sh->top_p < 1.f && sh->top_k > 256)) return O_ERR_SHAPE;
     return O_OK;
 }
 
@@ -232,6 +233,45 @@ static void token_scores(const oracle_shape *sh, const float *xf, const float *W
  * listed in descending b.  Weights are the unbiased scores of the chosen
  * experts divided by their sum (normalised sigmoid scores); the routed scaling
  * factor is applied later, in the combine. */
+/* Adaptive expert top-p (colibri README, "Got a better machine", the
+ * `--topp 0.7` knob: adaptive expert top-p, less expert traffic).  The pages
+ * give no formula; the reading here is nucleus selection over the routing
+ * weights: rank the k selections by weight (descending; equal weights, the
+ * lower id first), keep the shortest prefix of that ranking whose weights
+ * add up to at least p (the running sum in f32, in rank order, as the kernel
+ * decides it), drop the rest (id -1, weight 0) and renormalise the kept
+ * weights: w_j = s_j / (sum of the kept s). */
+static void apply_top_p(float p, int32_t k, const float *s, int32_t *ids, float *w)
+{
+    int32_t ord[256];
+    for (int32_t j = 0; j < k; ++j) ord[j] = j;
+    for (int32_t a = 0; a < k; ++a) /* selection sort by (w desc, id asc) */
+        for (int32_t c = a + 1; c < k; ++c) {
+            const int32_t x = ord[a], y = ord[c];
+            if (w[y] > w[x] || (w[y] == w[x] && ids[y] < ids[x])) {
+                ord[a] = y;
+                ord[c] = x;
+            }
+        }
+    float mass = 0.f;
+    int32_t keep = 0;
+    while (keep < k && mass < p) mass += w[ord[keep++]];
+    unsigned char kept[256] = {0};
+    double ks = 0.0;
+    for (int32_t r = 0; r < keep; ++r) {
+        kept[ord[r]] = 1;
+        ks += (double)s[ids[ord[r]]];
+    }
+    for (int32_t j = 0; j < k; ++j) {
+        if (kept[j]) {
+            w[j] = (float)((double)s[ids[j]] / ks);
+        } else {
+            ids[j] = -1;
+            w[j] = 0.f;
+        }
+    }
+}
+
 static void token_select(const oracle_shape *sh, const float *s, const float *b, int32_t *ids, float *w,
                          float *gap, float *ggap, unsigned char *allowed, float *gscore, unsigned char *gkept)
 {
@@ -287,6 +327,7 @@ static void token_select(const oracle_shape *sh, const float *s, const float *b,
     double sum = 0.0;
     for (int32_t j = 0; j < k; ++j) sum += (double)s[ids[j]];
     for (int32_t j = 0; j < k; ++j) w[j] = (float)((double)s[ids[j]] / sum);
+    if (sh->top_p > 0.f && sh->top_p < 1.f) apply_top_p(sh->top_p, k, s, ids, w);
 }
 
 int oracle_router_scores(const oracle_shape *sh, const uint16_t *hidden, const float *W, const float *bias,
@@ -379,6 +420,7 @@ int oracle_permute(const oracle_shape *sh, const int32_t *ids, int32_t *counts, 
     const int64_t P = (int64_t)sh->T * sh->top_k;
     for (int32_t e = 0; e < sh->E; ++e) counts[e] = 0;
     for (int64_t p = 0; p < P; ++p) {
+        if (ids[p] == -1) continue; /* dropped by adaptive top-p */
         if (ids[p] < 0 || ids[p] >= sh->E) return O_ERR_SHAPE;
         counts[ids[p]] += 1;
     }
@@ -388,6 +430,10 @@ int oracle_permute(const oracle_shape *sh, const int32_t *ids, int32_t *counts, 
     if (!fill) return O_ERR_NOMEM;
     for (int32_t e = 0; e < sh->E; ++e) fill[e] = offsets[e];
     for (int64_t p = 0; p < P; ++p) {
+        if (ids[p] == -1) {
+            inv[p] = -1;
+            continue;
+        }
         int32_t pos = fill[ids[p]]++;
         sorted[pos] = (int32_t)p;
         inv[p] = pos;
@@ -531,6 +577,7 @@ int oracle_combine(const oracle_shape *sh, const float *y_pairs, const int32_t *
             double acc = 0.0;
             for (int32_t j = 0; j < k; ++j) {
                 int64_t p = (int64_t)t * k + j;
+                if (inv[p] < 0) continue; /* a pair dropped by adaptive top-p */
                 double coef = topk_w ? rsf * (double)topk_w[p] : 1.0;
                 acc += coef * (double)y_pairs[(int64_t)inv[p] * H + c];
             }
@@ -633,12 +680,14 @@ int oracle_layer_tokens(const oracle_shape *sh, const oracle_weights *wt, const 
                     int32_t t = tokens[i];
                     widen_row(hidden + (int64_t)t * H, H, xf);
                     for (int32_t j = 0; j < k; ++j)
-                        ffn_one(xf, H, I, 4, &wt->gate, &wt->up, &wt->down, ids[(int64_t)i * k + j], h, wrow,
-                                y + (int64_t)j * H);
+                        if (ids[(int64_t)i * k + j] >= 0) /* (-1: dropped by adaptive top-p) */
+                            ffn_one(xf, H, I, 4, &wt->gate, &wt->up, &wt->down, ids[(int64_t)i * k + j], h, wrow,
+                                    y + (int64_t)j * H);
                     for (int32_t c = 0; c < H; ++c) {
                         double acc = 0.0;
                         for (int32_t j = 0; j < k; ++j)
-                            acc += rsf * (double)w[(int64_t)i * k + j] * (double)y[(int64_t)j * H + c];
+                            if (ids[(int64_t)i * k + j] >= 0)
+                                acc += rsf * (double)w[(int64_t)i * k + j] * (double)y[(int64_t)j * H + c];
                         if (sh->shared_bits) acc += (double)shout[(int64_t)i * H + c];
                         if (sh->flags & ORACLE_ADD_RESIDUAL) acc += (double)xf[c];
                         out[(int64_t)i * H + c] = (float)acc;
@@ -681,8 +730,9 @@ int oracle_layer_forward_dense(const oracle_shape *sh, const oracle_weights *wt,
     if (st) goto done;
     for (int32_t t = 0; t < T; ++t)
         for (int32_t j = 0; j < k; ++j)
-            mask[(int64_t)t * E + ids[(int64_t)t * k + j]] =
-                (double)sh->routed_scaling_factor * (double)w[(int64_t)t * k + j];
+            if (ids[(int64_t)t * k + j] >= 0) /* (-1: dropped by adaptive top-p) */
+                mask[(int64_t)t * E + ids[(int64_t)t * k + j]] =
+                    (double)sh->routed_scaling_factor * (double)w[(int64_t)t * k + j];
     st = oracle_shared_ffn(sh, hidden, wt, shout);
     if (st) goto done;
     {

@@ -57,6 +57,7 @@ typedef struct {
     int32_t topk_group;   /* groups kept */
     float routed_scaling_factor;
     uint32_t flags;       /* ORACLE_ADD_RESIDUAL: the combine adds the layer input */
+    float top_p;          /* adaptive expert top-p, 0 < top_p < 1; any other value keeps all top_k */
 } oracle_shape;
 
 /* One quantised matrix family: expert e's rows start at q + e*q_stride_bytes

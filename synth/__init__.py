@@ -108,6 +108,7 @@ class LayerConfig:
     layers: int = 1
     seed: int = 1000
     skew: Optional[str] = None    # None | "hot8x3" | "zipf1.2"
+    top_p: float = 0.0            # adaptive expert top-p (0 = keep all top_k)
     # value distributions
     x_std: float = 1.0
     w_std: float = 0.02

@@ -24,8 +24,11 @@ MUTANTS = {
     "up reads gate rows": ("oracle_dequant_row(qrow(up, bits, e, i, H), bits, qscale(up, e, i), H, wrow);",
                            "oracle_dequant_row(qrow(gate, bits, e, i, H), bits, qscale(up, e, i), H, wrow);"),
     "scale of row 0": ("qscale(down, e, c)", "qscale(down, e, 0)"),
-    "unstable permutation": ("for (int64_t p = 0; p < P; ++p) {\n        int32_t pos = fill[ids[p]]++;",
-                             "for (int64_t p = P - 1; p >= 0; --p) {\n        int32_t pos = fill[ids[p]]++;"),
+    "unstable permutation": ("for (int64_t p = 0; p < P; ++p) {\n        if (ids[p] == -1) {",
+                             "for (int64_t p = P - 1; p >= 0; --p) {\n        if (ids[p] == -1) {"),
+    "top-p keeps the pair that reaches p exactly": ("while (keep < k && mass < p)", "while (keep < k && mass <= p)"),
+    "top-p not renormalised": ("w[j] = (float)((double)s[ids[j]] / ks);", "w[j] = w[j];"),
+    "top-p in selection order": ("if (w[y] > w[x] || (w[y] == w[x] && ids[y] < ids[x])) {", "if (0) {"),
     "quantiser ties away from zero": ("float v = nearbyintf(w[c] / scale);", "float v = roundf(w[c] / scale);"),
     "quantiser scale one level short": ("const float scale = amax / qmax;", "const float scale = amax / (qmax + 1.0f);"),
     "bias update sign flipped": ("if (load < total)\n            bias_out[e] = bias_in[e] + gamma;",

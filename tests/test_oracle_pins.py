@@ -496,3 +496,134 @@ def test_thread_count_does_not_change_bits(synth_mod, oracle_mod, tmp_path):
         subprocess.run([sys.executable, "-c", code, p], check=True, env=env)
         outs.append(np.load(p))
     assert np.array_equal(outs[0], outs[1])
+
+
+# ------------------------------------------------------- adaptive expert top-p
+
+def _controlled_router(cfg, z_row):
+    """H = 2, hidden [1, 0] (exact in bf16), W[e] = [z_e, 0]: every token's
+    logits are exactly the f32 values z_row."""
+    x = np.zeros((cfg.T, 2), np.uint16)
+    x[:, 0] = 0x3F80  # bf16 1.0
+    W = np.zeros((cfg.E, 2), np.float32)
+    W[:, 0] = np.asarray(z_row, np.float32)
+    return x, W
+
+
+def test_top_p_worked_example(synth_mod, oracle_mod):
+    """Scores 1/2, 3/10, 1/5 (weights the same, their sum is 1); p = 0.7 keeps
+    the two largest (running mass 0.5 < 0.7, then 0.8 >= 0.7), renormalised to
+    0.5/0.8 = 0.625 and 0.3/0.8 = 0.375; the third is dropped (id -1, w 0)."""
+    s_tgt = np.array([0.5, 0.3, 0.2])
+    cfg = tiny_cfg(synth_mod, T=3, H=2, E=3, k=3, top_p=0.7)
+    x, W = _controlled_router(cfg, np.log(s_tgt / (1 - s_tgt)))
+    ids, w, _, _ = oracle_mod.router(cfg, x, W, np.zeros(3, np.float32))
+    for t in range(cfg.T):
+        assert list(ids[t]) == [0, 1, -1]
+        assert np.allclose(w[t], [0.625, 0.375, 0.0], rtol=0, atol=1e-6) and w[t][2] == 0.0
+
+
+def test_top_p_ties_keep_lower_id(synth_mod, oracle_mod):
+    """Scores 1/2, 1/2, 1/4 -> weights 0.4, 0.4, 0.2; p = 0.3 is reached by the
+    first ranked alone, and of the two equal weights the lower id ranks first
+    (the selection order itself is b = s + bias, here the bias puts id 1 first)."""
+    cfg = tiny_cfg(synth_mod, T=2, H=2, E=3, k=3, top_p=0.3)
+    x, W = _controlled_router(cfg, [0.0, 0.0, np.log(1 / 3)])
+    bias = np.array([0.0, 0.01, 0.0], np.float32)
+    ids, w, _, _ = oracle_mod.router(cfg, x, W, bias)
+    for t in range(cfg.T):
+        # selection order [1, 0, 2]; the tie of ids 1 and 0 ranks id 0 first
+        assert list(ids[t]) == [-1, 0, -1]
+        assert list(w[t]) == [0.0, 1.0, 0.0]
+
+
+def test_top_p_mass_reaching_p_exactly_stops(synth_mod, oracle_mod):
+    """Two equal scores: weights exactly 1/2 each; p = 1/2 is reached by the
+    first ranked (the lower id), so the second is dropped."""
+    cfg = tiny_cfg(synth_mod, T=2, H=2, E=2, k=2, top_p=0.5)
+    x, W = _controlled_router(cfg, [0.3, 0.3])
+    ids, w, _, _ = oracle_mod.router(cfg, x, W, np.zeros(2, np.float32))
+    for t in range(cfg.T):
+        assert list(ids[t]) == [0, -1] and list(w[t]) == [1.0, 0.0]
+
+
+def test_top_p_off_values_keep_everything(synth_mod, oracle_mod):
+    cfg = tiny_cfg(synth_mod, T=20, E=16, k=4, seed=91)
+    x = synth_mod.hidden(cfg)
+    W, bias = synth_mod.router(cfg)
+    ref = oracle_mod.router(cfg, x, W, bias)
+    for p in (0.0, 1.0, 1.5, -0.2):
+        got = oracle_mod.router(cfg.with_(top_p=p), x, W, bias)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def test_top_p_tiny_keeps_the_heaviest(synth_mod, oracle_mod):
+    """p -> 0: one expert per token, the one of largest weight (= largest
+    unbiased score among the selected), with weight exactly 1."""
+    cfg = tiny_cfg(synth_mod, T=30, E=16, k=4, seed=92)
+    x = synth_mod.hidden(cfg)
+    W, bias = synth_mod.router(cfg)
+    W *= 8
+    ids0, w0, _, _ = oracle_mod.router(cfg, x, W, bias)
+    ids, w, _, _ = oracle_mod.router(cfg.with_(top_p=1e-6), x, W, bias)
+    for t in range(cfg.T):
+        kept = [j for j in range(cfg.k) if ids[t][j] >= 0]
+        assert len(kept) == 1 and w[t][kept[0]] == 1.0
+        best = max(range(cfg.k), key=lambda j: (w0[t][j], -ids0[t][j]))
+        assert kept == [best] and ids[t][best] == ids0[t][best]
+
+
+@pytest.mark.parametrize("p", [0.35, 0.7, 0.9])
+def test_top_p_definition_invariants(synth_mod, oracle_mod, p):
+    """The kept set is the shortest prefix of the weight ranking whose f32
+    running mass reaches p; kept weights are the unbiased scores renormalised
+    over the kept set; positions and ids of the kept selections are unchanged."""
+    cfg = tiny_cfg(synth_mod, T=64, E=16, k=6, n_group=4, topk_group=3, seed=93)
+    x = synth_mod.hidden(cfg)
+    W, bias = synth_mod.router(cfg)
+    W *= 6
+    _, s, _ = oracle_mod.router_scores(cfg, x, W, bias)
+    ids0, w0, _, _ = oracle_mod.router(cfg, x, W, bias)
+    ids, w, _, _ = oracle_mod.router(cfg.with_(top_p=p), x, W, bias)
+    for t in range(cfg.T):
+        rank = sorted(range(cfg.k), key=lambda j: (-w0[t][j], ids0[t][j]))
+        mass, keep = np.float32(0), 0
+        while keep < cfg.k and mass < np.float32(p):
+            mass = np.float32(mass + w0[t][rank[keep]])
+            keep += 1
+        kept = set(rank[:keep])
+        ssum = sum(float(s[t][ids0[t][j]]) for j in kept)
+        for j in range(cfg.k):
+            if j in kept:
+                assert ids[t][j] == ids0[t][j]
+                assert abs(w[t][j] - s[t][ids0[t][j]] / ssum) <= 1e-7
+            else:
+                assert ids[t][j] == -1 and w[t][j] == 0.0
+        assert abs(float(w[t][list(kept)].sum()) - 1.0) < 1e-6
+
+
+@pytest.mark.parametrize("kw", [dict(top_p=0.6, w_std=0.2), dict(E=8, k=3, n_group=4, topk_group=2, rsf=2.5, top_p=0.5, w_std=0.2)])
+def test_top_p_sparse_equals_dense_mask(synth_mod, oracle_mod, kw):
+    """With dropped pairs the sorted grouped path (permutation skips them, the
+    combine skips them) equals the dense all-experts-times-mask path."""
+    cfg = tiny_cfg(synth_mod, **kw)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    sparse, ids, *_ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    assert (ids == -1).any()
+    dense = oracle_mod.layer_forward_dense(cfg, lw, d["hidden"])
+    assert np.allclose(sparse, dense, rtol=2e-7, atol=1e-9)
+
+
+def test_top_p_permutation_skips_dropped(synth_mod, oracle_mod):
+    cfg = tiny_cfg(synth_mod, T=40, E=8, k=3, top_p=0.6, seed=95)
+    x = synth_mod.hidden(cfg)
+    W, bias = synth_mod.router(cfg)
+    ids, _, _, _ = oracle_mod.router(cfg, x, W, bias)
+    counts, offsets, srt, inv = oracle_mod.permute(cfg, ids)
+    flat = ids.reshape(-1)
+    live = np.nonzero(flat >= 0)[0]
+    assert counts.sum() == len(live) and offsets[-1] == len(live)
+    assert np.all(inv[flat < 0] == -1)
+    order = live[np.argsort(flat[live], kind="stable")]
+    assert np.array_equal(srt[:len(live)], order)
+    assert np.array_equal(inv[order], np.arange(len(live)))
