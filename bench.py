@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c1", help="workload key (c1 = the decode step this line reports)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--top-p", type=float, default=0.0,
+                    help="adaptive expert top-p of the workload's router (0 = off, the workloads' own setting)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--quantize", action="store_true",
@@ -103,6 +105,8 @@ def main():
     if args.bias_update:
         return bench_bias_update(args, moe, torch, np)
     cfg = synth.CONFIGS[args.config]
+    if args.top_p:
+        cfg = cfg.with_(top_p=args.top_p)
     if cfg.T > 32:
         return bench_prefill(args, cfg, moe, synth, torch, np, dev)
     L, T, H = cfg.layers, cfg.T, cfg.H
@@ -196,19 +200,20 @@ def main():
     torch.cuda.synchronize()
     avg_ms = ea.elapsed_time(eb) / (args.roofline_reps * L)
 
-    n_act = []
+    n_act, p_kept = [], []
     for l in range(L):
         pid, _, _, _ = moe.moe_layer_routing(sh_of(moe, cfg, T, flags), wss[l])
         base = wss[l].data_ptr()
         ids = wss[l][pid - base:pid - base + 4 * P].view(torch.int32).cpu().numpy()
-        n_act.append(int(np.unique(ids).size))
+        n_act.append(int(np.unique(ids[ids >= 0]).size))  # (-1: a pair dropped by adaptive top-p)
+        p_kept.append(int((ids >= 0).sum()))
     # algorithmic bytes of one expert-kernel launch: the weights (int4 rows and
     # f32 row scales) of every chosen routed expert and of the shared expert,
     # the activations and routing logits read once, one f32 output row per
     # (token, expert) pair and per token for the shared expert
     sh_w = (3 * cfg.I_sh * H * cfg.shared_bits // 8 + 4 * (2 * cfg.I_sh + H)) if cfg.shared_bits else 0
     ex_bytes = [na * (3 * cfg.I * H // 2 + 4 * (2 * cfg.I + H)) + sh_w + 2 * T * H + 4 * T * cfg.E
-                + 4 * P * H + (4 * T * H if cfg.shared_bits else 0) for na in n_act]
+                + 4 * pk * H + (4 * T * H if cfg.shared_bits else 0) for na, pk in zip(n_act, p_kept)]
     alg_per_launch = float(np.mean(ex_bytes))
     achieved = alg_per_launch / (avg_ms / 1e3) / 1e9  # GB/s
     traffic = measured_traffic(ROOT)
@@ -260,7 +265,7 @@ def main():
         "data": "synthetic (seeded, random-init weights of the Colibri-Nano MoE layer shape)",
         "config": {"workload": cfg.name, "T": T, "layers": L, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
                    "I_shared": cfg.I_sh, "global_batch": T, "parallelism": "single GPU",
-                   "chained": "each layer's combine takes the next layer's router logits"},
+                   "chained": "each layer's combine takes the next layer's router logits", "top_p": cfg.top_p},
         "step_hbm_GBs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_alg_bytes": int(step_bytes),
@@ -415,6 +420,9 @@ def bench_prefill(args, cfg, moe, synth, torch, np, dev):
             stream.synchronize()
             kms.append(a.elapsed_time(b))
     avg_ms = float(np.mean(kms))
+    # the routed rows the pass computed (fewer than T*k when adaptive top-p drops pairs)
+    _, _, poff, _ = moe.moe_layer_routing(sh, ws)
+    P = int(ws[poff - ws.data_ptr() + 4 * cfg.E:poff - ws.data_ptr() + 4 * cfg.E + 4].view(torch.int32).item())
     gu_flops = 4.0 * P * cfg.I * H
     achieved = gu_flops / (avg_ms / 1e3) / 1e12
     layer_flops = 6.0 * P * H * cfg.I + (6.0 * T * H * cfg.I_sh if cfg.shared_bits else 0.0)
@@ -453,7 +461,7 @@ def bench_prefill(args, cfg, moe, synth, torch, np, dev):
         "data": "synthetic (seeded)",
         "config": {"workload": cfg.name, "T": T, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
                    "I_shared": cfg.I_sh, "shared_bits": cfg.shared_bits, "global_batch": T,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "top_p": cfg.top_p, "routed_pairs": P},
         "layer_TFLOPs": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1),
         "layer_mfma_frac": round(layer_flops / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "roofline": roofline,

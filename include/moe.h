@@ -106,6 +106,12 @@ typedef struct {
     int32_t topk_group; /* groups kept, 1 <= topk_group <= n_group */
     float routed_scaling_factor; /* multiplies the routed terms (not the shared expert) */
     uint32_t flags;     /* MOE_OUT_F32 | MOE_ADD_RESIDUAL */
+    float top_p;        /* adaptive expert top-p (colibri README, the --topp knob): with 0 < top_p < 1
+                           each token keeps only the shortest prefix of its top_k selections ranked by
+                           combine weight (descending; equal weights, the lower id first) whose f32
+                           running weight reaches top_p, renormalised over the kept ones; dropped slots
+                           read id -1, weight 0 and cost no expert work.  Any other value keeps all
+                           top_k (0 is the plain router); NaN is MOE_ERR_SHAPE */
 } moe_shape;
 
 typedef struct {

@@ -52,7 +52,7 @@ class MoeShape(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
                 ("shared_bits", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("top_p", ctypes.c_float)]
 
 
 class MoeQMat(ctypes.Structure):
@@ -122,14 +122,15 @@ def _check(status: int, what: str):
         raise MoeError(status, what)
 
 
-def shape(T, H, E, top_k, I, I_shared=0, shared_bits=0, n_group=1, topk_group=1, rsf=1.0, flags=0) -> MoeShape:
-    return MoeShape(T, H, E, top_k, I, I_shared, shared_bits, n_group, topk_group, rsf, flags)
+def shape(T, H, E, top_k, I, I_shared=0, shared_bits=0, n_group=1, topk_group=1, rsf=1.0, flags=0,
+          top_p=0.0) -> MoeShape:
+    return MoeShape(T, H, E, top_k, I, I_shared, shared_bits, n_group, topk_group, rsf, flags, top_p)
 
 
 def shape_of(cfg, T: Optional[int] = None, flags: int = 0) -> MoeShape:
     """MoeShape of a synth.LayerConfig-like object (fields T,H,E,k,I,I_sh,...)."""
     return shape(cfg.T if T is None else T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_sh, cfg.shared_bits, cfg.n_group,
-                 cfg.topk_group, cfg.rsf, flags)
+                 cfg.topk_group, cfg.rsf, flags, float(getattr(cfg, "top_p", 0.0)))
 
 
 def _ptr(t) -> Optional[int]:

@@ -25,6 +25,7 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ y, co
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
         const int p = t * k + j;
+        if (inv[p] < 0) continue;  // a pair dropped by adaptive top-p
         const float coef = topk_w ? rsf * topk_w[p] : 1.f;
         const f32x4 v = *(const f32x4 *)(y + (size_t)inv[p] * H + c);
 #pragma unroll

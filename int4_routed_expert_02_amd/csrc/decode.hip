@@ -138,8 +138,8 @@ __device__ __forceinline__ float dec_logit(const float *__restrict__ zp, int T, 
 // writes ids, w, rsf * w and the tie gap to global memory.
 template <int EPL>
 __device__ __noinline__ void dec_select_waves(const float *__restrict__ zp, const float *__restrict__ bias, int T,
-                                              int E, int k, int n_group, int topk_group, float rsf, int32_t *ids_l,
-                                              float *w_l, bool pub, float *__restrict__ gap_g)
+                                              int E, int k, int n_group, int topk_group, float rsf, float top_p,
+                                              int32_t *ids_l, float *w_l, bool pub, float *__restrict__ gap_g)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nw = blockDim.x / WAVE;
@@ -154,7 +154,7 @@ __device__ __noinline__ void dec_select_waves(const float *__restrict__ zp, cons
             b[q] = ok[q] ? s[q] + bias[e] : -INFINITY;
         }
         select_token<EPL>(s, b, ok, lane, t, E, k, n_group, topk_group, rsf, ids_l, w_l, pub ? gap_g : nullptr,
-                          nullptr, nullptr);
+                          nullptr, nullptr, top_p);
     }
 }
 
@@ -216,7 +216,7 @@ __device__ __forceinline__ uint32_t or8_u32(uint32_t b)
 // moe_select.h.  Waves holding no token skip the work.
 template <int KL>
 __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, const float *__restrict__ bias, int T,
-                                                 int E, int k, int32_t *ids_l, float *w_l, bool pub,
+                                                 int E, int k, float top_p, int32_t *ids_l, float *w_l, bool pub,
                                                  float *__restrict__ gap_g)
 {
     const int tid = threadIdx.x, t = tid >> 3, q = tid & 7;
@@ -277,11 +277,44 @@ __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, c
 #pragma unroll
         for (int j = 0; j < KL - 1; ++j)
             if (j < k) ssum += ss[j];
+        float wj[KL - 1];
+        bool keep[KL - 1];
+#pragma unroll
+        for (int j = 0; j < KL - 1; ++j) {
+            wj[j] = j < k ? ss[j] / ssum : 0.f;
+            keep[j] = j < k;
+        }
+        if (top_p > 0.f && top_p < 1.f) {
+            // adaptive expert top-p, as in moe_select.h: rank by weight (equal
+            // weights, lower id first), keep while the f32 running mass in rank
+            // order is below p, renormalise over the kept scores
+            int rank[KL - 1];
+#pragma unroll
+            for (int j = 0; j < KL - 1; ++j) {
+                rank[j] = 0;
+#pragma unroll
+                for (int i = 0; i < KL - 1; ++i)
+                    if (i < k && j < k && i != j && (wj[i] > wj[j] || (wj[i] == wj[j] && sid[i] < sid[j])))
+                        ++rank[j];
+            }
+            float mass = 0.f, ks = 0.f;
+#pragma unroll
+            for (int r = 0; r < KL - 1; ++r)
+#pragma unroll
+                for (int j = 0; j < KL - 1; ++j)
+                    if (j < k && rank[j] == r) {
+                        keep[j] = mass < top_p;
+                        mass += wj[j];
+                        if (keep[j]) ks += ss[j];
+                    }
+#pragma unroll
+            for (int j = 0; j < KL - 1; ++j) wj[j] = keep[j] ? ss[j] / ks : 0.f;
+        }
 #pragma unroll
         for (int j = 0; j < KL - 1; ++j)
             if (j < k) {
-                ids_l[t * k + j] = sid[j];
-                w_l[t * k + j] = ss[j] / ssum;
+                ids_l[t * k + j] = keep[j] ? sid[j] : -1;
+                w_l[t * k + j] = wj[j];
             }
         if (pub) {
             float nv = -INFINITY, kv = 0.f;
@@ -375,7 +408,7 @@ struct DecArgs {
     const float *zp;     // [LG_NP][T][E] partial router logits
     const float *rb;     // [E] selection bias
     int n_group, topk_group;
-    float rsf;
+    float rsf, top_p;  // top_p: adaptive expert top-p (0 < top_p < 1), else all top_k kept
     // routed experts
     const uint8_t *gq, *uq, *dq;
     const float *gs, *us, *ds;
@@ -399,13 +432,13 @@ __device__ __forceinline__ void dec_route(const DecArgs &r, int T, int E, int k,
     const bool grouped = r.n_group > 1 && r.topk_group < r.n_group;
     if (!grouped && E <= 64 && E % 8 == 0 && k <= 3) {
         if (k == 1)
-            dec_select_lanes<2>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
+            dec_select_lanes<2>(r.zp, r.rb, T, E, k, r.top_p, ids_l, w_l, pub, r.gap);
         else if (k == 2)
-            dec_select_lanes<3>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
+            dec_select_lanes<3>(r.zp, r.rb, T, E, k, r.top_p, ids_l, w_l, pub, r.gap);
         else
-            dec_select_lanes<4>(r.zp, r.rb, T, E, k, ids_l, w_l, pub, r.gap);
+            dec_select_lanes<4>(r.zp, r.rb, T, E, k, r.top_p, ids_l, w_l, pub, r.gap);
     } else {
-        dec_select_waves<EPL>(r.zp, r.rb, T, E, k, r.n_group, r.topk_group, r.rsf, ids_l, w_l, pub, r.gap);
+        dec_select_waves<EPL>(r.zp, r.rb, T, E, k, r.n_group, r.topk_group, r.rsf, r.top_p, ids_l, w_l, pub, r.gap);
     }
     __syncthreads();
     if (pub)
@@ -808,6 +841,17 @@ __global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nun
 
 constexpr int CB_SPLIT = 4;  // threads per output quad, each summing every 4th plane
 
+// Bit j set: token t's selection slot j was dropped by adaptive top-p (id -1;
+// its partial planes were never written).  ids is null when top-p is off.
+__device__ __forceinline__ uint32_t dec_dropped_slots(const int32_t *ids, int t, int k)
+{
+    uint32_t m = 0;
+    if (ids)
+        for (int j = 0; j < k; ++j)
+            if (ids[(size_t)t * k + j] < 0) m |= 1u << j;
+    return m;
+}
+
 // out[t] = sum over partial planes (routed pairs of t in order j, their
 // chunks in order; then the shared expert's chunks) (+ x[t]).  Four
 // consecutive lanes own one 4-column quad: lane q sums planes q, q + 4, ...
@@ -816,7 +860,7 @@ constexpr int CB_SPLIT = 4;  // threads per output quad, each summing every 4th 
 __global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ yp, int nkr,
                                                      const float *__restrict__ ysp, int nks,
                                                      const uint16_t *__restrict__ res, void *__restrict__ out, int T,
-                                                     int H, int k, int out_f32)
+                                                     int H, int k, int out_f32, const int32_t *__restrict__ ids)
 {
     constexpr int MAXL = 16;  // planes per lane per batch
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
@@ -828,6 +872,7 @@ __global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ y
     const int c = live ? (int)(quad % cpt) * 4 : 0;
     const size_t P = (size_t)T * k;
     const int nrp = k * nkr, np = nrp + nks;
+    const uint32_t dropped = dec_dropped_slots(ids, live ? t : 0, k);
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int p0 = q; p0 < np; p0 += CB_SPLIT * MAXL) {
         f32x4 v[MAXL];
@@ -835,7 +880,7 @@ __global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ y
         for (int i = 0; i < MAXL; ++i) {
             const int p = p0 + CB_SPLIT * i;
             v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (live && p < np) {
+            if (live && p < np && !(p < nrp && ((dropped >> (p / nkr)) & 1u))) {
                 const float *src = p < nrp ? yp + ((size_t)(p % nkr) * P + (size_t)t * k + p / nkr) * H + c
                                            : ysp + ((size_t)(p - nrp) * T + t) * H + c;
                 v[i] = *(const f32x4 *)src;
@@ -886,7 +931,7 @@ __global__ __launch_bounds__(256) void k_dec_combine_logits(const float *__restr
                                                             const uint16_t *__restrict__ res,
                                                             uint16_t *__restrict__ out, int T, int H, int k,
                                                             const float *__restrict__ nrw, int nE,
-                                                            float *__restrict__ nzp)
+                                                            float *__restrict__ nzp, const int32_t *__restrict__ ids)
 {
     static_assert(DEC_LOGIT_PLANES == 4, "one plane per quarter of the row");
     extern __shared__ float xq[];  // [H / 4] this quarter of the output row
@@ -905,6 +950,7 @@ __global__ __launch_bounds__(256) void k_dec_combine_logits(const float *__restr
     }
     const size_t P = (size_t)T * k;
     const int nrp = k * nkr, np = nrp + nks;
+    const uint32_t dropped = dec_dropped_slots(ids, t, k);
     for (int qd0 = 0; qd0 < H4 / 4; qd0 += 256 / CB_SPLIT) {
         const int quad = qd0 + tid / CB_SPLIT, q = tid % CB_SPLIT;
         const int c = c0 + quad * 4;
@@ -915,7 +961,7 @@ __global__ __launch_bounds__(256) void k_dec_combine_logits(const float *__restr
             for (int i = 0; i < MAXL; ++i) {
                 const int p = p0 + CB_SPLIT * i;
                 v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (p < np) {
+                if (p < np && !(p < nrp && ((dropped >> (p / nkr)) & 1u))) {
                     const float *src = p < nrp ? yp + ((size_t)(p % nkr) * P + (size_t)t * k + p / nkr) * H + c
                                                : ysp + ((size_t)(p - nrp) * T + t) * H + c;
                     v[i] = *(const f32x4 *)src;
@@ -980,6 +1026,8 @@ __global__ __launch_bounds__(256) void k_dec_combine_logits(const float *__restr
 
 // ---------------------------------------------------------------- launcher
 
+static bool dec_topp_on(float p) { return p > 0.f && p < 1.f; }
+
 bool decode_supported(int T, int H, int E, int k, int I, int Ish, int sh_bits)
 {
     if (T > DEC_MAXT || E > 256 || k > DEC_MAXK) return false;
@@ -1005,6 +1053,7 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     a.n_group = d.n_group;
     a.topk_group = d.topk_group;
     a.rsf = d.rsf;
+    a.top_p = d.top_p;
     a.gq = d.gq;
     a.uq = d.uq;
     a.dq = d.dq;
@@ -1057,13 +1106,13 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     if (d.nrw) {
         hipLaunchKernelGGL(k_dec_combine_logits, dim3(d.T * 4), dim3(256), (size_t)(d.H / 4) * sizeof(float), st, d.y,
                            d.I / DX_ROWS, d.shp, d.sh_bits ? d.Ish / DX_ROWS : 0, d.res, (uint16_t *)d.out, d.T, d.H,
-                           d.k, d.nrw, d.nE, d.nz);
+                           d.k, d.nrw, d.nE, d.nz, dec_topp_on(d.top_p) ? d.ids : nullptr);
         return hipGetLastError();
     }
     const long nthreads = (long)d.T * (d.H / 4) * CB_SPLIT;
     hipLaunchKernelGGL(k_dec_combine, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, d.y,
                        d.I / DX_ROWS, d.shp, d.sh_bits ? d.Ish / DX_ROWS : 0, d.res, d.out, d.T, d.H, d.k,
-                       d.out_f32);
+                       d.out_f32, dec_topp_on(d.top_p) ? d.ids : nullptr);
     return hipGetLastError();
 }
 

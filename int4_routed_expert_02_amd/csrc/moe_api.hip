@@ -29,6 +29,7 @@ int validate(const moe_shape *s)
     if (s->n_group > 1 && s->E / s->n_group < 2) return MOE_ERR_SHAPE;
     if (s->top_k > s->topk_group * (s->E / s->n_group)) return MOE_ERR_SHAPE;
     if ((int64_t)s->T * s->top_k > INT32_MAX / 2) return MOE_ERR_SHAPE;
+    if (s->top_p != s->top_p) return MOE_ERR_SHAPE;  // NaN
     // what the gfx950 kernels cover
     if (s->H % 128 || s->I % 64) return MOE_ERR_UNSUPPORTED;
     if (s->shared_bits && s->I_shared % 64) return MOE_ERR_UNSUPPORTED;
@@ -228,7 +229,7 @@ int moe_router(const moe_shape *s, const moe_bf16 *hidden, const float *router_w
     const Layout L = layout(s, MOE_WS_PERMUTE);
     const int KS = moe::router_ks(s->T, s->H, s->E);
     return hip_status(moe::launch_router(hidden, router_w, router_bias, s->T, s->H, s->E, s->top_k, s->n_group,
-                                         s->topk_group, s->routed_scaling_factor, at<float>(ws, L.zpart), KS,
+                                         s->topk_group, s->routed_scaling_factor, s->top_p, at<float>(ws, L.zpart), KS,
                                          topk_ids, topk_w, sel_gap, nullptr, nullptr, (hipStream_t)stream));
 }
 
@@ -358,6 +359,7 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         d.n_group = s->n_group;
         d.topk_group = s->topk_group;
         d.rsf = s->routed_scaling_factor;
+        d.top_p = s->top_p;
         d.ids = at<int32_t>(ws, L.ids);
         d.w = at<float>(ws, L.w);
         d.gap = at<float>(ws, L.gap);
@@ -410,7 +412,7 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     float *pscale = at<float>(ws, L.pscale), *ypair = at<float>(ws, L.ypair);
 
     hipError_t e = moe::launch_router(hidden, w->router_w, w->router_bias, s->T, s->H, s->E, s->top_k, s->n_group,
-                                      s->topk_group, s->routed_scaling_factor, at<float>(ws, L.zpart), KS, ids,
+                                      s->topk_group, s->routed_scaling_factor, s->top_p, at<float>(ws, L.zpart), KS, ids,
                                       at<float>(ws, L.w), at<float>(ws, L.gap), pscale, sbc, hs);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = moe::launch_scatter(ids, sbc, nsb, P, s->E, sbt * s->top_k, counts, offsets, sorted, inv, hs);

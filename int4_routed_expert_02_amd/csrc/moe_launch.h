@@ -33,7 +33,7 @@ struct DecLaunch {
     const uint16_t *x;
     const float *rw, *rb;
     int T, H, E, k, n_group, topk_group;
-    float rsf;
+    float rsf, top_p;
     int32_t *ids;
     float *w, *gap, *pscale;
     float *z;  // [DEC_LOGIT_PLANES][T][E] partial router logits (scratch)
@@ -44,7 +44,7 @@ struct DecLaunch {
     const uint8_t *sgq, *suq, *sdq;
     const float *sgs, *sus, *sds;
     int Ish, sh_bits;
-    float *y, *shp;  // partial outputs: [I/64][T*k][H] routed, [I_shared/64][T][H] shared
+    float *y, *shp;  // partial outputs: [I/128][T*k][H] routed, [I_shared/128][T][H] shared
     const uint16_t *res;
     void *out;
     int out_f32;
@@ -66,8 +66,8 @@ int router_ks(int T, int H, int E);
 int router_select_blocks(int T);
 int superblock_tokens(int k);
 hipError_t launch_router(const uint16_t *x, const float *W, const float *bias, int T, int H, int E, int k,
-                         int n_group, int topk_group, float rsf, float *zpart, int KS, int32_t *ids, float *w,
-                         float *gap, float *pair_scale, int32_t *sbcounts, hipStream_t st);
+                         int n_group, int topk_group, float rsf, float top_p, float *zpart, int KS, int32_t *ids,
+                         float *w, float *gap, float *pair_scale, int32_t *sbcounts, hipStream_t st);
 hipError_t launch_pair_hist(const int32_t *ids, int P, int E, int chunk, int nblocks, int32_t *bcounts,
                             hipStream_t st);
 hipError_t launch_scatter(const int32_t *ids, const int32_t *bcounts, int nblocks, int P, int E, int chunk,

@@ -55,7 +55,7 @@ __device__ __forceinline__ void select_token(float (&s)[EPL], float (&b)[EPL], b
                                              int E, int k, int n_group, int topk_group, float rsf,
                                              int32_t *__restrict__ ids, float *__restrict__ w,
                                              float *__restrict__ gap, float *__restrict__ pair_scale,
-                                             int32_t *hist)
+                                             int32_t *hist, float top_p)
 {
     float ggap = INFINITY;
     if (n_group > 1 && topk_group < n_group) {
@@ -131,7 +131,8 @@ __device__ __forceinline__ void select_token(float (&s)[EPL], float (&b)[EPL], b
     }
     // top-k by repeated arg-max over the allowed experts
     float ssum = 0.f;
-    float sel_s = 0.f;  // lane j keeps the unbiased score of selection j
+    float sel_s = 0.f;  // lane j keeps the unbiased score and the id of selection j
+    int sel_id = -1;
     float bk = 0.f;
     for (int j = 0; j < k; ++j) {
         ArgMax m{-INFINITY, -1};
@@ -149,10 +150,9 @@ __device__ __forceinline__ void select_token(float (&s)[EPL], float (&b)[EPL], b
             }
         const float sj = __shfl(own, m.i / EPL, WAVE);
         ssum += sj;
-        if (lane == j) sel_s = sj;
-        if (lane == 0) {
-            ids[(size_t)t * k + j] = m.i;
-            if (hist) atomicAdd(&hist[m.i], 1);
+        if (lane == j) {
+            sel_s = sj;
+            sel_id = m.i;
         }
     }
     // the best remaining allowed score, for the tie gap
@@ -161,10 +161,36 @@ __device__ __forceinline__ void select_token(float (&s)[EPL], float (&b)[EPL], b
     for (int q = 0; q < EPL; ++q)
         if (ok[q]) nx = better(nx, ArgMax{b[q], lane * EPL + q});
     nx = wave_argmax(nx);
+    float wj = lane < k ? sel_s / ssum : 0.f;
+    bool keep = lane < k;
+    if (top_p > 0.f && top_p < 1.f) {
+        // adaptive expert top-p: rank the k selections by weight (descending,
+        // equal weights the lower id first), keep those whose running mass
+        // before them (f32, summed in rank order) is below p, renormalise
+        int rank = 0;
+        for (int i = 0; i < k; ++i) {
+            const float wi = __shfl(wj, i, WAVE);
+            const int ii = __shfl(sel_id, i, WAVE);
+            if (lane < k && i != lane && (wi > wj || (wi == wj && ii < sel_id))) ++rank;
+        }
+        float mass = 0.f, before = 0.f;
+        for (int r = 0; r < k; ++r) {
+            const uint64_t at = __ballot(lane < k && rank == r);
+            const float wr = __shfl(wj, (int)__builtin_ctzll(at), WAVE);
+            if (lane < k && rank == r) before = mass;
+            mass += wr;
+        }
+        keep = lane < k && before < top_p;
+        float ks = keep ? sel_s : 0.f;  // the kept scores' sum (a wave sum; order immaterial at 1e-7)
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ks += __shfl_xor(ks, o, WAVE);
+        wj = keep ? sel_s / ks : 0.f;
+    }
     if (lane < k) {
-        const float wj = sel_s / ssum;
+        ids[(size_t)t * k + lane] = keep ? sel_id : -1;
         w[(size_t)t * k + lane] = wj;
         if (pair_scale) pair_scale[(size_t)t * k + lane] = rsf * wj;
+        if (hist && keep) atomicAdd(&hist[sel_id], 1);
     }
     if (lane == 0 && gap) {
         const float g1 = nx.i >= 0 ? bk - nx.v : INFINITY;

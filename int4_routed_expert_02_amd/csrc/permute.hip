@@ -23,7 +23,8 @@ __global__ __launch_bounds__(256) void k_pair_hist(const int32_t *__restrict__ i
     __syncthreads();
     const int p0 = blockIdx.x * chunk;
     const int p1 = min(P, p0 + chunk);
-    for (int p = p0 + threadIdx.x; p < p1; p += 256) atomicAdd(&hist[ids[p]], 1);
+    for (int p = p0 + threadIdx.x; p < p1; p += 256)
+        if (ids[p] >= 0) atomicAdd(&hist[ids[p]], 1);  // (-1: a pair dropped by adaptive top-p)
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256) bcounts[(size_t)blockIdx.x * E + e] = hist[e];
 }
@@ -94,8 +95,10 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t *__restrict__ ids
     const int p1 = min(P, p0 + chunk);
     for (int s0 = p0; s0 < p1; s0 += 256) {
         const int p = s0 + tid;
-        const bool act = p < p1;
-        const int id = act ? ids[p] : 0;
+        const int idr = p < p1 ? ids[p] : 0;
+        const bool act = p < p1 && idr >= 0;  // (-1: a pair dropped by adaptive top-p, no row)
+        const int id = act ? idr : 0;
+        if (p < p1 && idr < 0) inv[p] = -1;
         const uint64_t same = match_key(id, act);
         const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         const int rank_w = __popcll(same & lt);

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void k_router_select(const float *__restrict__
                                                        int n_group, int topk_group, float rsf,
                                                        int32_t *__restrict__ ids, float *__restrict__ w,
                                                        float *__restrict__ gap, float *__restrict__ pair_scale,
-                                                       int32_t *__restrict__ sbcounts, int sb_tokens)
+                                                       int32_t *__restrict__ sbcounts, int sb_tokens, float top_p)
 {
     __shared__ int32_t hist[256];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void k_router_select(const float *__restrict__
             s[q] = ok[q] ? 1.0f / (1.0f + expf(-z[q])) : 0.f;
             b[q] = ok[q] ? s[q] + bias[lane * EPL + q] : -INFINITY;
         }
-        select_token<EPL>(s, b, ok, lane, t, E, k, n_group, topk_group, rsf, ids, w, gap, pair_scale, hist);
+        select_token<EPL>(s, b, ok, lane, t, E, k, n_group, topk_group, rsf, ids, w, gap, pair_scale, hist, top_p);
     }
     __syncthreads();
     if (sbcounts) {
@@ -273,8 +273,8 @@ int superblock_tokens(int k)
 }
 
 hipError_t launch_router(const uint16_t *x, const float *W, const float *bias, int T, int H, int E, int k,
-                         int n_group, int topk_group, float rsf, float *zpart, int KS, int32_t *ids, float *w,
-                         float *gap, float *pair_scale, int32_t *sbcounts, hipStream_t st)
+                         int n_group, int topk_group, float rsf, float top_p, float *zpart, int KS, int32_t *ids,
+                         float *w, float *gap, float *pair_scale, int32_t *sbcounts, hipStream_t st)
 {
     const int ksteps = H / RT_BK;
     const int sbt = superblock_tokens(k);
@@ -285,13 +285,13 @@ hipError_t launch_router(const uint16_t *x, const float *W, const float *bias, i
     const int nb = router_select_blocks(T);
     if (E <= 64)
         hipLaunchKernelGGL(k_router_select<1>, dim3(nb), dim3(256), 0, st, zpart, KS, bias, T, E, k, n_group,
-                           topk_group, rsf, ids, w, gap, pair_scale, sbcounts, sbt);
+                           topk_group, rsf, ids, w, gap, pair_scale, sbcounts, sbt, top_p);
     else if (E <= 128)
         hipLaunchKernelGGL(k_router_select<2>, dim3(nb), dim3(256), 0, st, zpart, KS, bias, T, E, k, n_group,
-                           topk_group, rsf, ids, w, gap, pair_scale, sbcounts, sbt);
+                           topk_group, rsf, ids, w, gap, pair_scale, sbcounts, sbt, top_p);
     else
         hipLaunchKernelGGL(k_router_select<4>, dim3(nb), dim3(256), 0, st, zpart, KS, bias, T, E, k, n_group,
-                           topk_group, rsf, ids, w, gap, pair_scale, sbcounts, sbt);
+                           topk_group, rsf, ids, w, gap, pair_scale, sbcounts, sbt, top_p);
     return hipGetLastError();
 }
 
