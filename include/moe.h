@@ -198,7 +198,12 @@ int moe_combine(const moe_shape *shape, const float *y_pairs, const int32_t *inv
  * moe_layer_forward -- the whole layer: router, permutation, routed experts,
  * shared expert, combine (and the input added back when MOE_ADD_RESIDUAL).
  * out: [T][H] f32 or bf16 per MOE_OUT_F32.  The regime (small-batch weight
- * streaming or tiled grouped GEMM) is chosen from the shape.
+ * streaming or tiled grouped GEMM) is chosen from the shape.  In the tiled
+ * regime the shared expert runs on a second stream of the current device
+ * (created on first use, default priority), forked from and joined back to
+ * `stream` with events, so the call stays ordered on `stream` and a captured
+ * graph gets two branches.  Calls from several host threads are serialised
+ * around that fork and join.
  * Workspace: moe_workspace_bytes(shape, MOE_WS_LAYER).
  */
 int moe_layer_forward(const moe_shape *shape, const moe_weights *weights, const moe_bf16 *hidden, void *out,

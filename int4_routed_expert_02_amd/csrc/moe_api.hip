@@ -3,12 +3,44 @@
 // or synchronises; every error is detected before the first enqueue.
 #include <string.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "moe_launch.h"
 
 namespace {
 
 using moe::FfnArgs;
+
+// A second stream per device (default priority, non-blocking) for work that
+// does not depend on the routing: the tiled regime runs the shared expert on it
+// while the router, the permutation and the routed GEMMs run on the caller's
+// stream, forked and joined with events (a captured graph gets two branches).
+// The mutex keeps one call's fork/join pair from interleaving with another's.
+struct SideStream {
+    hipStream_t st = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int MAX_DEVICES = 64;
+SideStream g_side[MAX_DEVICES];
+std::mutex g_side_mu;
+
+SideStream *side_stream(hipStream_t caller)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    SideStream &s = g_side[dev];
+    if (!s.st) {
+        // not created under graph capture: the caller's stream then runs everything
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+        if (hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess)
+            return nullptr;
+    }
+    return &s;
+}
 
 constexpr size_t WS_ALIGN = 256;
 
@@ -411,6 +443,23 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     int32_t *sorted = at<int32_t>(ws, L.sorted), *inv = at<int32_t>(ws, L.inv);
     float *pscale = at<float>(ws, L.pscale), *ypair = at<float>(ws, L.ypair);
 
+    // the shared expert (no dependence on the routing) on the side stream,
+    // except in the profiled call, whose events time the routed gate/up alone
+    SideStream *side = nullptr;
+    std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+    if (s->shared_bits && !ev_start && !ev_stop) {
+        side_lock.lock();
+        side = side_stream(hs);
+        if (side) {
+            if (hipEventRecord(side->fork, hs) != hipSuccess || hipStreamWaitEvent(side->st, side->fork, 0) != hipSuccess)
+                return MOE_ERR_HIP;
+            st = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr,
+                         1, 1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<float>(ws, L.shy), side->st);
+            if (st) return st;
+        } else {
+            side_lock.unlock();
+        }
+    }
     hipError_t e = moe::launch_router(hidden, w->router_w, w->router_bias, s->T, s->H, s->E, s->top_k, s->n_group,
                                       s->topk_group, s->routed_scaling_factor, s->top_p, at<float>(ws, L.zpart), KS, ids,
                                       at<float>(ws, L.w), at<float>(ws, L.gap), pscale, sbc, hs);
@@ -427,13 +476,16 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         st = run_ffn_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, at<uint16_t>(ws, L.hbuf), ypair, hs);
         if (st) return st;
     }
-    const float *shy = nullptr;
-    if (s->shared_bits) {
+    if (side) {
+        if (hipEventRecord(side->join, side->st) != hipSuccess || hipStreamWaitEvent(hs, side->join, 0) != hipSuccess)
+            return MOE_ERR_HIP;
+        side_lock.unlock();
+    } else if (s->shared_bits) {
         st = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr, 1,
                      1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<float>(ws, L.shy), hs);
         if (st) return st;
-        shy = at<float>(ws, L.shy);
     }
+    const float *shy = s->shared_bits ? at<float>(ws, L.shy) : nullptr;
     return hip_status(moe::launch_combine(ypair, inv, nullptr, 1.f, shy,
                                           (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr, out, s->T, s->H,
                                           s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, hs));
