@@ -21,6 +21,7 @@ _SRC = os.path.join(_HERE, "oracle_moe.c")
 _LIB = os.path.join(_HERE, "liboracle_moe.so")
 
 ADD_RESIDUAL = 2
+ACT_Q8 = 4         # Q8_0-style int8 activations (ORACLE_ACT_Q8)
 
 
 def build() -> str:
@@ -83,6 +84,7 @@ def lib():
             "oracle_gateup_int_sums": ([S, vp, W, vp, vp, vp, vp], ctypes.c_int),
             "oracle_num_threads": ([], ctypes.c_int),
             "oracle_quantize_rows": ([vp, i32, ctypes.c_int64, i32, i32, vp, vp], ctypes.c_int),
+            "oracle_quantize_act_q8": ([vp, i32, ctypes.c_int64, i32, vp, vp], ctypes.c_int),
             "oracle_bias_update": ([i32, vp, vp, ctypes.c_float, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
@@ -103,9 +105,9 @@ def _chk(st: int, what: str):
 
 
 def shape_of(cfg, T: Optional[int] = None, residual: bool = False) -> Shape:
+    flags = (ADD_RESIDUAL if residual else 0) | (ACT_Q8 if getattr(cfg, "act_q8", False) else 0)
     return Shape(cfg.T if T is None else T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_sh, cfg.shared_bits,
-                 cfg.n_group, cfg.topk_group, cfg.rsf, ADD_RESIDUAL if residual else 0,
-                 float(getattr(cfg, "top_p", 0.0)))
+                 cfg.n_group, cfg.topk_group, cfg.rsf, flags, float(getattr(cfg, "top_p", 0.0)))
 
 
 class LayerWeights:
@@ -286,6 +288,20 @@ def quantize_rows(src: np.ndarray, bits: int):
     _chk(lib().oracle_quantize_rows(_p(src), 1 if src.dtype == np.uint16 else 0, rows, cols, bits, _p(q), _p(qs)),
          "oracle_quantize_rows")
     return q, qs
+
+
+def quantize_act_q8(src: np.ndarray):
+    """Q8_0-style activation codes: src [rows][cols] f32, or uint16 holding bf16
+    bits (cols % 32 == 0).  Returns (codes int8 [rows][cols], d f32 [rows][cols/32])."""
+    src = np.ascontiguousarray(src)
+    if src.ndim != 2 or src.dtype not in (np.float32, np.uint16):
+        raise ValueError("src must be a 2-D float32 or uint16 (bf16 bits) array")
+    rows, cols = src.shape
+    q = np.zeros((rows, cols), dtype=np.int8)
+    d = np.zeros((rows, max(cols // 32, 1)), dtype=np.float32)
+    _chk(lib().oracle_quantize_act_q8(_p(src), 1 if src.dtype == np.uint16 else 0, rows, cols, _p(q), _p(d)),
+         "oracle_quantize_act_q8")
+    return q, d
 
 
 def bias_update(counts: np.ndarray, bias: np.ndarray, gamma: float) -> np.ndarray:

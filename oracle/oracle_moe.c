@@ -146,6 +146,58 @@ int oracle_quantize_rows(const void *src, int32_t src_bf16, int64_t rows, int32_
     return failed ? O_ERR_NOMEM : O_OK;
 }
 
+/* One block of Q8_0-style activation codes: the rule above with qmax 127 over
+ * the n values of v (see ORACLE_ACT_Q8 in oracle_moe.h). */
+static float q8_block(const float *v, int32_t n, int8_t *q)
+{
+    float amax = 0.0f;
+    for (int32_t c = 0; c < n; ++c)
+        if (fabsf(v[c]) > amax) amax = fabsf(v[c]);
+    const float d = amax / 127.0f;
+    for (int32_t c = 0; c < n; ++c) {
+        if (amax == 0.0f) {
+            q[c] = 0;
+            continue;
+        }
+        float t = nearbyintf(v[c] / d);
+        if (t > 127.0f) t = 127.0f;
+        if (t < -127.0f) t = -127.0f;
+        q[c] = (int8_t)t;
+    }
+    return d;
+}
+
+static void q8_row(const float *v, int32_t n, int8_t *q, float *d)
+{
+    for (int32_t b = 0; b < n / 32; ++b) d[b] = q8_block(v + 32 * b, 32, q + 32 * b);
+}
+
+int oracle_quantize_act_q8(const void *src, int32_t src_bf16, int64_t rows, int32_t cols, int8_t *q, float *d)
+{
+    if (rows < 0 || cols <= 0 || cols % 32) return O_ERR_SHAPE;
+    if (rows == 0) return O_OK;
+    if (!src || !q || !d) return O_ERR_NULL;
+    int failed = 0;
+#pragma omp parallel
+    {
+        float *v = (float *)malloc((size_t)cols * sizeof(float));
+        if (!v) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < rows; ++r) {
+                for (int32_t c = 0; c < cols; ++c)
+                    v[c] = src_bf16 ? oracle_bf16_to_f32(((const uint16_t *)src)[r * cols + c])
+                                    : ((const float *)src)[r * cols + c];
+                q8_row(v, cols, q + r * cols, d + r * (cols / 32));
+            }
+        }
+        free(v);
+    }
+    return failed ? O_ERR_NOMEM : O_OK;
+}
+
 /* ---------------------------------------------------------------- bias update */
 
 int oracle_bias_update(int32_t E, const int32_t *counts, const float *bias_in, float gamma, float *bias_out)
@@ -203,6 +255,8 @@ static int check_shape(const oracle_shape *sh)
     if (sh->n_group > 1 && sh->E / sh->n_group < 2) return O_ERR_SHAPE;
     if (sh->top_k > sh->topk_group * (sh->E / sh->n_group)) return O_ERR_SHAPE;
     if (sh->top_p != sh->top_p || (sh->top_p > 0.f && sh->top_p < 1.f && sh->top_k > 256)) return O_ERR_SHAPE;
+    if ((sh->flags & ORACLE_ACT_Q8) && (sh->H % 32 || sh->I % 32 || (sh->shared_bits && sh->I_shared % 32)))
+        return O_ERR_SHAPE;
     return O_OK;
 }
 
@@ -447,9 +501,56 @@ int oracle_permute(const oracle_shape *sh, const int32_t *ids, int32_t *counts, 
 /* SwiGLU expert (activation from the benchmark spec; the pages say only
  * that an expert has three matrices): g = x.Wg_i, u = x.Wu_i,
  * h_i = silu(g)*u with silu(z) = z/(1+exp(-z)), y_c = h.Wd_c. */
-static void ffn_one(const float *xf, int32_t H, int32_t I, int32_t bits, const oracle_qmat *gate,
-                    const oracle_qmat *up, const oracle_qmat *down, int32_t e, float *h, float *wrow, float *y)
+/* Q8_0-style dot of a quantised activation row with weight row r of expert
+ * e: s_w * sum_b d_b * (sum over block b of q * code), block sums in integers. */
+static double q8_dot(const int8_t *q, const float *d, const oracle_qmat *m, int32_t bits, int32_t e, int64_t r,
+                     int32_t n, int32_t *codes)
 {
+    const void *row = qrow(m, bits, e, r, n);
+    if (bits == 4) {
+        oracle_unpack_int4_row((const uint8_t *)row, n, codes);
+    } else {
+        for (int32_t c = 0; c < n; ++c) codes[c] = ((const int8_t *)row)[c];
+    }
+    double acc = 0.0;
+    for (int32_t b = 0; b < n / 32; ++b) {
+        int64_t isum = 0;
+        for (int32_t c = 32 * b; c < 32 * b + 32; ++c) isum += (int64_t)q[c] * codes[c];
+        acc += (double)d[b] * (double)isum;
+    }
+    return (double)*qscale(m, e, r) * acc;
+}
+
+/* The expert with Q8_0-style activations: x and then h (as f32) quantised per
+ * 32-block, every dot as q8_dot; the SwiGLU as in ffn_one. */
+static void ffn_one_q8(const float *xf, int32_t H, int32_t I, int32_t bits, const oracle_qmat *gate,
+                       const oracle_qmat *up, const oracle_qmat *down, int32_t e, float *h, float *y)
+{
+    const int32_t n = H > I ? H : I;
+    int8_t *q = malloc((size_t)n);
+    float *d = malloc(sizeof(float) * (size_t)(n / 32));
+    int32_t *codes = malloc(sizeof(int32_t) * (size_t)n);
+    q8_row(xf, H, q, d);
+    for (int32_t i = 0; i < I; ++i) {
+        float g = (float)q8_dot(q, d, gate, bits, e, i, H, codes);
+        float u = (float)q8_dot(q, d, up, bits, e, i, H, codes);
+        h[i] = (float)((double)g / (1.0 + exp(-(double)g)) * (double)u);
+    }
+    q8_row(h, I, q, d);
+    for (int32_t c = 0; c < H; ++c) y[c] = (float)q8_dot(q, d, down, bits, e, c, I, codes);
+    free(q);
+    free(d);
+    free(codes);
+}
+
+static void ffn_one(const float *xf, int32_t H, int32_t I, int32_t bits, const oracle_qmat *gate,
+                    const oracle_qmat *up, const oracle_qmat *down, int32_t e, float *h, float *wrow, float *y,
+                    int q8)
+{
+    if (q8) {
+        ffn_one_q8(xf, H, I, bits, gate, up, down, e, h, y);
+        return;
+    }
     for (int32_t i = 0; i < I; ++i) {
         oracle_dequant_row(qrow(gate, bits, e, i, H), bits, qscale(gate, e, i), H, wrow);
         float g = (float)dot_f64(xf, wrow, H);
@@ -501,7 +602,7 @@ int oracle_expert_ffn(const oracle_shape *sh, const uint16_t *hidden, const orac
                 int32_t t = p / k;
                 float *y = y_pairs + (int64_t)r * H;
                 widen_row(hidden + (int64_t)t * H, H, xf);
-                ffn_one(xf, H, I, 4, &wt->gate, &wt->up, &wt->down, e, h, wrow, y);
+                ffn_one(xf, H, I, 4, &wt->gate, &wt->up, &wt->down, e, h, wrow, y, (sh->flags & ORACLE_ACT_Q8) != 0);
                 if (pair_scale) {
                     const double c = (double)pair_scale[p];
                     for (int32_t j = 0; j < H; ++j) y[j] = (float)((double)y[j] * c);
@@ -540,7 +641,7 @@ static int shared_tokens(const oracle_shape *sh, const uint16_t *hidden, const o
                 int32_t t = tokens ? tokens[i] : i;
                 widen_row(hidden + (int64_t)t * H, H, xf);
                 ffn_one(xf, H, I, sh->shared_bits, &wt->sh_gate, &wt->sh_up, &wt->sh_down, 0, h, wrow,
-                        out + (int64_t)i * H);
+                        out + (int64_t)i * H, (sh->flags & ORACLE_ACT_Q8) != 0);
             }
         }
         free(xf);
@@ -682,7 +783,7 @@ int oracle_layer_tokens(const oracle_shape *sh, const oracle_weights *wt, const 
                     for (int32_t j = 0; j < k; ++j)
                         if (ids[(int64_t)i * k + j] >= 0) /* (-1: dropped by adaptive top-p) */
                             ffn_one(xf, H, I, 4, &wt->gate, &wt->up, &wt->down, ids[(int64_t)i * k + j], h, wrow,
-                                    y + (int64_t)j * H);
+                                    y + (int64_t)j * H, (sh->flags & ORACLE_ACT_Q8) != 0);
                     for (int32_t c = 0; c < H; ++c) {
                         double acc = 0.0;
                         for (int32_t j = 0; j < k; ++j)
@@ -752,7 +853,8 @@ int oracle_layer_forward_dense(const oracle_shape *sh, const oracle_weights *wt,
                 for (int32_t t = 0; t < T; ++t) {
                     widen_row(hidden + (int64_t)t * H, H, xf);
                     for (int32_t e = 0; e < E; ++e)
-                        ffn_one(xf, H, I, 4, &wt->gate, &wt->up, &wt->down, e, h, wrow, y + (int64_t)e * H);
+                        ffn_one(xf, H, I, 4, &wt->gate, &wt->up, &wt->down, e, h, wrow, y + (int64_t)e * H,
+                                (sh->flags & ORACLE_ACT_Q8) != 0);
                     for (int32_t c = 0; c < H; ++c) {
                         double acc = 0.0;
                         for (int32_t e = 0; e < E; ++e)

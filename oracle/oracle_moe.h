@@ -44,6 +44,16 @@ extern "C" {
 #endif
 
 #define ORACLE_ADD_RESIDUAL 2u
+/* Q8_0-style int8 activations (colibri README, "What's implemented": the
+ * integer-dot kernels take int8 activations).  Reading: the input row of
+ * every expert matmul (x for gate and up, h for down) is cut into blocks of 32
+ * consecutive elements along the contraction axis; each block gets
+ * d = max|v| / 127 (f32 division) and codes q = the nearest integer to v / d
+ * (f32 division, ties to even, inside [-127, 127]; an all-zero block has
+ * d = 0 and codes 0), the rule of oracle_quantize_rows per block.  A dot is
+ * s_w * sum over blocks of d * (sum of q * weight code), the inner sums in
+ * integers.  h enters as f32.  H, I and I_shared must be multiples of 32. */
+#define ORACLE_ACT_Q8 4u
 
 typedef struct {
     int32_t T;            /* tokens */
@@ -56,7 +66,7 @@ typedef struct {
     int32_t n_group;      /* expert groups for group-limited selection (1 = off) */
     int32_t topk_group;   /* groups kept */
     float routed_scaling_factor;
-    uint32_t flags;       /* ORACLE_ADD_RESIDUAL: the combine adds the layer input */
+    uint32_t flags;       /* ORACLE_ADD_RESIDUAL: the combine adds the layer input; ORACLE_ACT_Q8 */
     float top_p;          /* adaptive expert top-p, 0 < top_p < 1; any other value keeps all top_k */
 } oracle_shape;
 
@@ -135,6 +145,11 @@ int oracle_gateup_int_sums(const oracle_shape *sh, const uint16_t *hidden, const
  * An all-zero row gets scale 0 and codes 0.  Codes are stored in the packed
  * layout of oracle_pack_int4_row (int4, cols even, rows of cols/2 bytes) or as
  * int8 rows.  Inputs must be finite.  Returns 0, or -2 for a bad shape. */
+/* Q8_0-style activation codes (see ORACLE_ACT_Q8): rows x cols (cols % 32 ==
+ * 0) f32 or bf16 (src_bf16) values -> q [rows][cols] int8 and d
+ * [rows][cols/32] f32. */
+int oracle_quantize_act_q8(const void *src, int32_t src_bf16, int64_t rows, int32_t cols, int8_t *q, float *d);
+
 int oracle_quantize_rows(const void *src, int32_t src_bf16, int64_t rows, int32_t cols, int32_t bits, void *q,
                          float *qs);
 

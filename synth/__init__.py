@@ -109,6 +109,7 @@ class LayerConfig:
     seed: int = 1000
     skew: Optional[str] = None    # None | "hot8x3" | "zipf1.2"
     top_p: float = 0.0            # adaptive expert top-p (0 = keep all top_k)
+    act_q8: bool = False          # Q8_0-style int8 activations for the expert matmuls
     # value distributions
     x_std: float = 1.0
     w_std: float = 0.02

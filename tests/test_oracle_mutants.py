@@ -34,6 +34,13 @@ MUTANTS = {
     "bias update sign flipped": ("if (load < total)\n            bias_out[e] = bias_in[e] + gamma;",
                                  "if (load < total)\n            bias_out[e] = bias_in[e] - gamma;"),
     "bias update moves at the mean": ("else if (load > total)", "else if (load >= total)"),
+    "q8 ties away from zero": ("float t = nearbyintf(v[c] / d);", "float t = roundf(v[c] / d);"),
+    "q8 scale of the next block": ("acc += (double)d[b] * (double)isum;",
+                                   "acc += (double)d[(b + 1) % (n / 32)] * (double)isum;"),
+    "q8 weight scale dropped": ("return (double)*qscale(m, e, r) * acc;", "return acc;"),
+    "q8 blocks of 16": ("for (int32_t b = 0; b < n / 32; ++b) d[b] = q8_block(v + 32 * b, 32, q + 32 * b);",
+                        "for (int32_t b = 0; b < n / 32; ++b) { d[b] = q8_block(v + 32 * b, 16, q + 32 * b); "
+                        "q8_block(v + 32 * b + 16, 16, q + 32 * b + 16); }"),
     "down transposed": ("oracle_dequant_row(qrow(down, bits, e, c, I), bits, qscale(down, e, c), I, wrow);",
                         "for (int32_t i2 = 0; i2 < I; ++i2) oracle_dequant_row(qrow(down, bits, e, i2 % H, I), bits, qscale(down, e, c), 1, wrow + i2);"),
 }

@@ -627,3 +627,121 @@ def test_top_p_permutation_skips_dropped(synth_mod, oracle_mod):
     order = live[np.argsort(flat[live], kind="stable")]
     assert np.array_equal(srt[:len(live)], order)
     assert np.array_equal(inv[order], np.arange(len(live)))
+
+
+# --------------------------------------------- Q8_0-style int8 activations
+
+def test_q8_worked_example(oracle_mod):
+    """One block with max |v| = 63.5, so d = 0.5 exactly: 0.25 / d = 0.5 and
+    1.25 / d = 2.5 are ties (to even: 0 and 2), 0.75 / d = 1.5 goes to 2;
+    then an all-zero block (d = 0, codes 0).  bf16 input gives the same."""
+    blk = np.zeros(32, dtype=np.float32)
+    blk[:8] = [63.5, 0.25, 0.75, -0.75, 1.25, 0.26, -63.5, 10.0]
+    v = np.concatenate([blk, np.zeros(32, dtype=np.float32)])[None, :]
+    q, d = oracle_mod.quantize_act_q8(v)
+    assert d.tolist() == [[0.5, 0.0]]
+    assert q[0, :8].tolist() == [127, 0, 2, -2, 2, 1, -127, 20]
+    assert not q[0, 8:].any()
+    qb, db = oracle_mod.quantize_act_q8(U.f32_to_bf16_rne(v))
+    assert np.array_equal(qb, q) and np.array_equal(db, d)
+
+
+def test_q8_nearest_code_and_bounds(oracle_mod):
+    """Random blocks over many magnitudes: every code is the nearest integer to
+    v / d (checked in f64 against all 255 codes, near-ties left out), |q| <=
+    127 with 127 reached in every non-zero block, and d * 127 is max |v| to
+    f32 rounding."""
+    rng = np.random.default_rng(5)
+    rows = []
+    for e in (-30, -8, 0, 3, 30):
+        rows.append((rng.standard_normal(256) * 10.0 ** e).astype(np.float32))
+    rows.append(np.where(rng.random(256) < 0.7, 0.0, rng.standard_normal(256)).astype(np.float32))
+    v = np.stack(rows)
+    q, d = oracle_mod.quantize_act_q8(v)
+    codes = np.arange(-127, 128, dtype=np.float64)
+    checked = 0
+    for r in range(v.shape[0]):
+        for b in range(v.shape[1] // 32):
+            vb = v[r, 32 * b:32 * b + 32].astype(np.float64)
+            db = float(d[r, b])
+            qb = q[r, 32 * b:32 * b + 32].astype(np.int64)
+            amax = np.abs(vb).max()
+            if amax == 0:
+                assert db == 0 and not qb.any()
+                continue
+            assert abs(db * 127 - amax) <= 2e-7 * amax
+            assert np.abs(qb).max() == 127
+            t = vb / db
+            near_tie = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-4
+            best = codes[np.argmin(np.abs(t[:, None] - codes[None, :]), axis=1)]
+            assert np.array_equal(best[~near_tie].astype(np.int64), qb[~near_tie])
+            checked += int((~near_tie).sum())
+    assert checked > 1000
+
+
+def test_q8_sign_power_of_two_and_block_independence(oracle_mod):
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((3, 128)).astype(np.float32)
+    q, d = oracle_mod.quantize_act_q8(v)
+    q2, d2 = oracle_mod.quantize_act_q8(-v * np.float32(2.0 ** -9))
+    assert np.array_equal(q2, -q) and np.array_equal(d2, d * np.float32(2.0 ** -9))
+    w = v.copy()
+    w[:, 32:64] *= 1000.0  # another block's values leave the rest alone
+    q3, d3 = oracle_mod.quantize_act_q8(w)
+    keep = np.r_[0:32, 64:128]
+    assert np.array_equal(q3[:, keep], q[:, keep])
+    assert np.array_equal(d3[:, [0, 2, 3]], d[:, [0, 2, 3]])
+
+
+def _q8_dequant(oracle_mod, v32):
+    q, d = oracle_mod.quantize_act_q8(np.ascontiguousarray(v32, dtype=np.float32))
+    return q.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+
+
+def _q8_mlp(oracle_mod, x, g, u, dn):
+    """The Q8 expert through dequantised activations, in f64 matmuls (a route
+    independent of the oracle's integer block sums): x' = d * q, g and u
+    rounded to f32, h in f32, h' = d * q of h."""
+    xq = _q8_dequant(oracle_mod, x)
+    gg = (xq @ g.T).astype(np.float32).astype(np.float64)
+    uu = (xq @ u.T).astype(np.float32).astype(np.float64)
+    h = (gg * expit(gg) * uu).astype(np.float32)
+    return _q8_dequant(oracle_mod, h) @ dn.T
+
+
+@pytest.mark.parametrize("shared_bits", [4, 8])
+def test_q8_layer_against_numpy_dequantised(synth_mod, oracle_mod, shared_bits):
+    """The whole layer in Q8 mode against sum_j rsf*w_j*FFN'_{id_j}(x) +
+    shared'(x) where FFN' runs the dequantised activations through f64
+    matmuls of the dequantised weights (the routing is the plain one: the
+    router does not see the mode)."""
+    cfg = tiny_cfg(synth_mod, T=16, E=8, k=3, rsf=1.5, n_group=4, topk_group=2, shared_bits=shared_bits,
+                   I_sh=64, act_q8=True)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    out, ids, w, _, _ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    plain = cfg.with_(act_q8=False)
+    _, ids0, w0, _, _ = oracle_mod.layer_forward(plain, oracle_mod.LayerWeights(plain, d), d["hidden"])
+    assert np.array_equal(ids, ids0) and np.array_equal(w, w0)
+    x = U.bf16_to_f32(d["hidden"])
+    ref = np.zeros((cfg.T, cfg.H))
+    for t in range(cfg.T):
+        ref[t] = _q8_mlp(oracle_mod, x[t:t + 1], *U.shared_mats(cfg, d))[0]
+        for j in range(cfg.k):
+            ref[t] += 1.5 * float(w[t, j]) * _q8_mlp(oracle_mod, x[t:t + 1], *U.expert_mats(cfg, d, ids[t, j]))[0]
+    assert U.rel_max_err(out, ref) < 2e-6
+
+
+def test_q8_sparse_equals_dense_mask(synth_mod, oracle_mod):
+    cfg = tiny_cfg(synth_mod, I_sh=64, act_q8=True)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    sparse, *_ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    dense = oracle_mod.layer_forward_dense(cfg, lw, d["hidden"])
+    assert np.allclose(sparse, dense, rtol=2e-7, atol=1e-9)
+
+
+def test_q8_shape_rule(synth_mod, oracle_mod):
+    """Q8 mode needs the contraction sizes in whole 32-blocks."""
+    cfg = tiny_cfg(synth_mod, I=48, I_sh=64, act_q8=True)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    with pytest.raises(RuntimeError):
+        oracle_mod.layer_forward(cfg, lw, d["hidden"])
