@@ -83,6 +83,14 @@ extern "C" {
                                MOE_ERR_UNSUPPORTED): this call's router logits are already in ws, written
                                there by the previous layer's moe_layer_forward_chain; the logits kernel
                                is not run (the selection is, from those logits) */
+#define MOE_ACT_Q8 0x1000u /* moe_layer_forward(_profiled): Q8_0-style int8 activations for the expert
+                               matmuls (colibri README, "What's implemented": the integer-dot kernels take
+                               int8 activations).  The input row of every expert matmul (x for gate and up,
+                               h for down, h taken in f32) is cut into blocks of 32 along the contraction
+                               axis; each block gets d = max|v| / 127 and codes as moe_quantize_act_q8
+                               gives; a dot is s_w * sum over blocks of d * (integer sum of code products).
+                               Always the tiled kernels (v_mfma_i32_16x16x32_i8); the router is unchanged.
+                               moe_expert_ffn and moe_layer_forward_chain return MOE_ERR_UNSUPPORTED */
 #define MOE_TEST_GATEUP_SUMS 0x100u /* moe_expert_ffn, testing only: write the raw integer-weight sums
                                sum_h x*q of gate into y_pairs[r][0:I] and of up into y_pairs[r][I:2I]
                                (no scale, no activation, no down projection); needs 2*I <= H, int4 */
@@ -289,6 +297,26 @@ int moe_layer_routing(const moe_shape *shape, void *ws, size_t ws_bytes, int32_t
 #define MOE_SRC_BF16 1
 int moe_quantize_rows(const void *src, int32_t src_format, int64_t rows, int32_t cols, int32_t bits, void *q,
                       float *qs, void *stream);
+
+/* ---- Q8_0-style activation codes (the MOE_ACT_Q8 mode's quantiser) ----
+ *
+ * moe_quantize_act_q8 cuts each of `rows` rows of `cols` values into blocks of
+ * 32 and writes, per block (colibri README, "What's implemented": Q8_0-style
+ * int8 activations; the pages give no formula, the reading is the weight
+ * quantiser's rule per block):
+ *   d    = max|v| / 127                    (f32, correctly rounded)
+ *   code = clamp(nearest integer to v / d, ties to even, -127, 127)
+ * and an all-zero block gets d = 0 and codes 0.  Inputs must be finite.
+ *   src   device, [rows][cols] f32 (MOE_SRC_F32) or bf16 bits (MOE_SRC_BF16),
+ *         16-byte aligned, row-major, no padding
+ *   q     device, [rows][cols] int8 codes, 16-byte aligned
+ *   d     device, [rows][cols/32] f32 block scales
+ * The caller owns every buffer; the call only enqueues on `stream`.
+ * Returns MOE_OK (rows == 0 is a no-op), MOE_ERR_SHAPE (rows < 0, cols <= 0,
+ * cols % 32 != 0, unknown src_format), MOE_ERR_NULL, MOE_ERR_ALIGN or
+ * MOE_ERR_HIP. */
+int moe_quantize_act_q8(const void *src, int32_t src_format, int64_t rows, int32_t cols, int8_t *q, float *d,
+                        void *stream);
 
 /* ---- the training-side step after the histogram: aux-loss-free balancing ----
  *

@@ -7,7 +7,7 @@ library is missing, every call raises -- there is no CPU fallback.
 The functions mirror the C ABI names:
   moe_router, moe_permute, moe_expert_ffn, moe_combine, moe_layer_forward,
   moe_workspace_bytes, moe_validate_shape, moe_status_string, moe_layer_routing,
-  moe_quantize_rows, moe_bias_update, moe_layer_forward_chain
+  moe_quantize_rows, moe_bias_update, moe_layer_forward_chain, moe_quantize_act_q8
 and ``MoeLayer`` keeps one layer's device weights and workspace.
 """
 from __future__ import annotations
@@ -34,6 +34,7 @@ MOE_TEST_GATEUP_SUMS = 0x100
 MOE_STAGE_GATEUP_ONLY = 0x200
 MOE_STAGE_EXPERTS_ONLY = 0x400
 MOE_LOGITS_GIVEN = 0x800
+MOE_ACT_Q8 = 0x1000
 
 MOE_SRC_F32 = 0
 MOE_SRC_BF16 = 1
@@ -44,7 +45,8 @@ MOE_WS_LAYER = 3
 
 EXPORTS = ["moe_router", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_profiled", "moe_workspace_bytes", "moe_validate_shape", "moe_status_string",
-           "moe_layer_routing", "moe_quantize_rows", "moe_bias_update", "moe_layer_forward_chain"]
+           "moe_layer_routing", "moe_quantize_rows", "moe_bias_update", "moe_layer_forward_chain",
+           "moe_quantize_act_q8"]
 
 
 class MoeShape(ctypes.Structure):
@@ -96,6 +98,7 @@ def load() -> ctypes.CDLL:
             "moe_validate_shape": [S],
             "moe_layer_routing": [S, vp, sz, vp, vp, vp, vp],
             "moe_quantize_rows": [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp],
+            "moe_quantize_act_q8": [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp],
             "moe_bias_update": [ctypes.c_int32, vp, vp, ctypes.c_float, vp],
         }
         for name, args in sig.items():
@@ -129,6 +132,8 @@ def shape(T, H, E, top_k, I, I_shared=0, shared_bits=0, n_group=1, topk_group=1,
 
 def shape_of(cfg, T: Optional[int] = None, flags: int = 0) -> MoeShape:
     """MoeShape of a synth.LayerConfig-like object (fields T,H,E,k,I,I_sh,...)."""
+    if getattr(cfg, "act_q8", False):
+        flags |= MOE_ACT_Q8
     return shape(cfg.T if T is None else T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_sh, cfg.shared_bits, cfg.n_group,
                  cfg.topk_group, cfg.rsf, flags, float(getattr(cfg, "top_p", 0.0)))
 
@@ -229,6 +234,24 @@ def moe_quantize_rows(src, bits: int, q=None, qs=None, stream=None):
     _check(load().moe_quantize_rows(_ptr(src), fmt, rows, cols, bits, _ptr(q), _ptr(qs), _stream(stream)),
            "moe_quantize_rows")
     return q, qs
+
+
+def moe_quantize_act_q8(src, q=None, d=None, stream=None):
+    """Q8_0-style activation codes (include/moe.h): src a 2-D float32 or
+    bfloat16 GPU tensor with cols % 32 == 0.  Returns (q int8 [rows][cols],
+    d float32 [rows][cols/32]), allocated when not given."""
+    import torch
+    if src.dim() != 2 or src.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("src must be a 2-D float32 or bfloat16 tensor")
+    rows, cols = src.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=src.device)
+    if d is None:
+        d = torch.empty((rows, max(cols // 32, 1)), dtype=torch.float32, device=src.device)
+    fmt = MOE_SRC_BF16 if src.dtype == torch.bfloat16 else MOE_SRC_F32
+    _check(load().moe_quantize_act_q8(_ptr(src), fmt, rows, cols, _ptr(q), _ptr(d), _stream(stream)),
+           "moe_quantize_act_q8")
+    return q, d
 
 
 def moe_bias_update(counts, router_bias, gamma: float, stream=None):

@@ -700,6 +700,238 @@ static hipError_t launch_mode(const FfnArgs &a, int rows_total, int groups, hipS
     return launch_one<MODE, WBITS, 128, 64, 4, 1>(a, slots, st);
 }
 
+// ------------------------------------------------- int8 activations (Q8_0-style)
+//
+// The integer-dot form of the expert matmuls (colibri README, "What's
+// implemented": int8 activations against int8 or int4 weights): rows hold
+// int8 activation codes with one f32 scale per 32 codes along k, weights int4
+// or int8 codes with one f32 scale per row.  Each 32-wide k block is one
+// v_mfma_i32_16x16x32_i8 (an exact integer sum), converted and added into f32
+// with the row's block scale; the weight row scale comes in the epilogue.
+// Int4 weights enter the MFMA as code << 4, sixteen times the code, exact in
+// int8 and in the i32 sums; the 1/16 joins the weight scale.  Operands as in
+// k_ffn: activations first (a lane ends with four rows of one column).
+// MODE 0: gate/up + SwiGLU -> h as f32 [rows][N]; MODE 1: down -> f32
+// [rows][N] * pscale.  Staging: registers to a double-buffered LDS tile, the
+// rows' two block scales of a stage beside it.
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int FQ_BK = 64;           // k per stage (two blocks)
+constexpr int FQ_LDA = FQ_BK + 16;  // LDS A row in bytes (80: the 8-byte fragment reads spread over the banks)
+
+// eight int4 codes (element 2c in the low nibble of byte c) -> eight bytes,
+// byte j = code j << 4
+__device__ __forceinline__ u32x2 unpack_int4x8_i8(uint32_t w)
+{
+    const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
+    return u32x2{__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u)};
+}
+
+__device__ __forceinline__ i32x4 mfma_i8(u32x2 a, u32x2 b)
+{
+    return __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b),
+                                                 i32x4{0, 0, 0, 0}, 0, 0, 0);
+}
+
+template <int MODE, int WBITS, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256, 2) void k_ffn_q8(FfnArgs a)
+{
+    constexpr int NMAT = (MODE == 0) ? 2 : 1;
+    constexpr int BKB = FQ_BK * WBITS / 8;  // bytes of a B row per stage
+    constexpr int LDB = BKB + 16;
+    constexpr int BROWS = NMAT * BN;
+    constexpr int A_CHUNKS = BM * FQ_BK / 16;  // 16-byte chunks of A per stage (four per row)
+    constexpr int B_CPR = BKB / 16;
+    constexpr int B_CHUNKS = BROWS * B_CPR;
+    constexpr int A_PT = (A_CHUNKS + 255) / 256;
+    constexpr int B_PT = (B_CHUNKS + 255) / 256;
+    constexpr int MB = BM / WM / 16;
+    constexpr int NB = BN / WN / 16;
+    static_assert(WM * WN == 4, "four waves");
+    static_assert(MB >= 1 && NB >= 1 && BM <= 256, "wave tile");
+
+    __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * FQ_LDA];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BROWS * LDB];
+    __shared__ __attribute__((aligned(16))) float sD[2][2][BM];  // [buffer][block of the stage][row]
+
+    // XCD-aware placement as in k_ffn
+    const int NT = a.N / BN;
+    const int xcd = blockIdx.x & 7, qq = blockIdx.x >> 3;
+    const int nt = qq % NT;
+    const int slot = (qq / NT) * 8 + xcd;
+    int e, row0, rows;
+    if (!find_tile<BM>(a, slot, e, row0, rows)) return;
+    const int n0 = nt * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int KB = a.K / 32;  // scale blocks per row
+
+    const int8_t *asrc[A_PT];
+#pragma unroll
+    for (int i = 0; i < A_PT; ++i) {
+        const int c = tid + i * 256, m = c / 4;
+        asrc[i] = nullptr;
+        if (c < A_CHUNKS && m < rows) {
+            const int r = row0 + m;
+            const int src = a.gather ? a.gather[r] / a.kdiv : r;
+            asrc[i] = (const int8_t *)a.A + (size_t)src * a.lda + (c % 4) * 16;
+        }
+    }
+    const float *dsrc = nullptr;
+    if (tid < rows) {
+        const int r = row0 + tid;
+        const int src = a.gather ? a.gather[r] / a.kdiv : r;
+        dsrc = a.ad + (size_t)src * KB;
+    }
+    const uint8_t *bsrc[B_PT];
+    const size_t brow_bytes = (size_t)a.K * WBITS / 8;
+#pragma unroll
+    for (int i = 0; i < B_PT; ++i) {
+        const int c = tid + i * 256;
+        bsrc[i] = nullptr;
+        if (c < B_CHUNKS) {
+            const int rr = c / B_CPR, cc = c % B_CPR;
+            const int mat = rr / BN, n = rr % BN;
+            const uint8_t *q = (mat == 0) ? a.q0 : a.q1;
+            bsrc[i] = q + (size_t)e * a.qstride + (size_t)(n0 + n) * brow_bytes + cc * 16;
+        }
+    }
+
+    u32x4 ra[A_PT], rb[B_PT];
+    u32x2 rd = u32x2{0u, 0u};
+    auto load_stage = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i)
+            ra[i] = asrc[i] ? *(const u32x4 *)(asrc[i] + (size_t)kt * FQ_BK) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < B_PT; ++i)
+            if (bsrc[i]) rb[i] = *(const u32x4 *)(bsrc[i] + (size_t)kt * BKB);
+        if (tid < BM) rd = dsrc ? *(const u32x2 *)(dsrc + 2 * kt) : u32x2{0u, 0u};
+    };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i) {
+            const int c = tid + i * 256;
+            if (c < A_CHUNKS) *(u32x4 *)(sA[buf] + (c / 4) * FQ_LDA + (c % 4) * 16) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_PT; ++i) {
+            const int c = tid + i * 256;
+            if (c < B_CHUNKS) *(u32x4 *)(sB[buf] + (c / B_CPR) * LDB + (c % B_CPR) * 16) = rb[i];
+        }
+        if (tid < BM) {
+            sD[buf][0][tid] = __uint_as_float(rd[0]);
+            sD[buf][1][tid] = __uint_as_float(rd[1]);
+        }
+    };
+
+    f32x4 acc[NMAT][MB][NB];
+#pragma unroll
+    for (int x = 0; x < NMAT; ++x)
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[x][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = a.K / FQ_BK;
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) load_stage(kt + 1);
+        const uint8_t *cA = sA[buf];
+        const uint8_t *cB = sB[buf];
+#pragma unroll
+        for (int ks = 0; ks < FQ_BK / 32; ++ks) {
+            u32x2 af[MB];
+            f32x4 dsc[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const int mr = wm * (BM / WM) + i * 16;
+                af[i] = *(const u32x2 *)(cA + (mr + (lane & 15)) * FQ_LDA + ks * 32 + (lane >> 4) * 8);
+                dsc[i] = *(const f32x4 *)(&sD[buf][ks][mr + (lane >> 4) * 4]);
+            }
+#pragma unroll
+            for (int x = 0; x < NMAT; ++x)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const uint8_t *bp = cB + (x * BN + wn * (BN / WN) + j * 16 + (lane & 15)) * LDB;
+                    const u32x2 bf = WBITS == 4 ? unpack_int4x8_i8(*(const uint32_t *)(bp + ks * 16 + (lane >> 4) * 4))
+                                                : *(const u32x2 *)(bp + ks * 32 + (lane >> 4) * 8);
+#pragma unroll
+                    for (int i = 0; i < MB; ++i) {
+                        const i32x4 p = mfma_i8(af[i], bf);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[x][i][j][r] = fmaf((float)p[r], dsc[i][r], acc[x][i][j][r]);
+                    }
+                }
+        }
+        if (kt + 1 < KT) store_stage(buf ^ 1);  // the other buffer: last read before the previous barrier
+        __syncthreads();
+    }
+
+    const float wq = WBITS == 4 ? 0.0625f : 1.f;  // int4 codes entered as code << 4
+    const float *sc0 = a.s0 + (size_t)e * a.sstride;
+    const float *sc1 = (MODE == 0) ? a.s1 + (size_t)e * a.sstride : nullptr;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
+            if (m >= rows) continue;
+            const int row = row0 + m;
+            float *o = (float *)a.out + (size_t)row * a.ldo;
+            if constexpr (MODE == 0) {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int n = n0 + wn * (BN / WN) + j * 16 + (lane & 15);
+                    const float g = acc[0][i][j][r] * (sc0[n] * wq);
+                    const float u = acc[1][i][j][r] * (sc1[n] * wq);
+                    o[n] = silu(g) * u;
+                }
+            } else {
+                const float ps = (a.pscale && a.pair_of_row) ? a.pscale[a.pair_of_row[row]] : 1.f;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int n = n0 + wn * (BN / WN) + j * 16 + (lane & 15);
+                    o[n] = acc[0][i][j][r] * (sc0[n] * wq) * ps;
+                }
+            }
+        }
+}
+
+template <int MODE, int WBITS, int BM, int BN, int WM, int WN>
+static hipError_t launch_q8(const FfnArgs &a, int slots, hipStream_t st)
+{
+    const int NT = a.N / BN;
+    const long grid = (long)((slots + 7) / 8 * 8) * NT;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((k_ffn_q8<MODE, WBITS, BM, BN, WM, WN>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// 64-row tiles once the groups average 24 rows, else 16; 64 output columns.
+template <int MODE, int WBITS>
+static hipError_t launch_q8_mode(const FfnArgs &a, int rows_total, int groups, hipStream_t st)
+{
+    const int ng = a.offsets ? groups : 1;
+    const bool big = rows_total >= 24 * ng;
+    const int bm = big ? 64 : 16;
+    const int slots = (rows_total + bm - 1) / bm + (a.offsets ? min(ng, rows_total) : 0);
+    if (big) return launch_q8<MODE, WBITS, 64, 64, 2, 2>(a, slots, st);
+    return launch_q8<MODE, WBITS, 16, 64, 1, 4>(a, slots, st);
+}
+
+hipError_t launch_ffn_q8(int mode, int wbits, const FfnArgs &a, int rows_total, int groups, hipStream_t st)
+{
+    if (mode == 0) return wbits == 4 ? launch_q8_mode<0, 4>(a, rows_total, groups, st)
+                                     : launch_q8_mode<0, 8>(a, rows_total, groups, st);
+    return wbits == 4 ? launch_q8_mode<1, 4>(a, rows_total, groups, st) : launch_q8_mode<1, 8>(a, rows_total, groups, st);
+}
+
 hipError_t launch_ffn(int mode, int wbits, const FfnArgs &a, int rows_total, int groups, hipStream_t st)
 {
     if (mode == 2) return launch_mode<2, 4>(a, rows_total, groups, st);

@@ -81,11 +81,14 @@ int check_qmat(const moe_qmat &m)
 // Workspace sections, in bytes, each 256-aligned.
 struct Layout {
     size_t zpart, sbc, ids, w, gap, pscale, counts, offsets, sorted, inv, hbuf, shh, ypair, shy, total;
+    // Q8_0-style activations: x codes and block scales, h (f32), its codes and scales (routed, shared)
+    size_t xq, xd, hf, hq, hd, shf, shq, shd;
     bool decode;  // the small-batch path serves this shape (MOE_WS_LAYER)
 };
 
 bool use_decode(const moe_shape *s)
 {
+    if (s->flags & MOE_ACT_Q8) return false;  // the int8-activation mode runs the tiled kernels
     return moe::decode_supported(s->T, s->H, s->E, s->top_k, s->I, s->I_shared, s->shared_bits);
 }
 
@@ -136,6 +139,19 @@ Layout layout(const moe_shape *s, int which)
         if (s->shared_bits) {
             L.shh = take(T * (size_t)s->I_shared * 2);
             L.shy = take(T * (size_t)s->H * 4);
+        }
+        if (s->flags & MOE_ACT_Q8) {
+            const size_t H = (size_t)s->H, I = (size_t)s->I, Is = (size_t)s->I_shared;
+            L.xq = take(T * H);
+            L.xd = take(T * (H / 32) * 4);
+            L.hf = take(P * I * 4);
+            L.hq = take(P * I);
+            L.hd = take(P * (I / 32) * 4);
+            if (s->shared_bits) {
+                L.shf = take(T * Is * 4);
+                L.shq = take(T * Is);
+                L.shd = take(T * (Is / 32) * 4);
+            }
         }
     }
     L.total = off;
@@ -222,6 +238,78 @@ int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, con
     return hip_status(moe::launch_ffn(1, wbits, d, rows, offsets ? E : 1, st));
 }
 
+// Buffers of one expert family in the Q8_0-style activation mode.
+struct Q8Bufs {
+    const int8_t *xq;  // [T][H] codes of the layer input
+    const float *xd;   // [T][H/32]
+    float *hf;         // [rows][I] h
+    int8_t *hq;        // [rows][I] its codes
+    float *hd;         // [rows][I/32]
+};
+
+// The down GEMM of the Q8 mode: h quantised per 32-block, then int8 x int4/int8.
+int run_ffn_q8_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
+                    const int32_t *sorted, int E, int rows, const float *pscale, const Q8Bufs &b, float *y,
+                    hipStream_t st)
+{
+    hipError_t e = moe::launch_quant_act_q8(b.hf, 0, rows, I, b.hq, b.hd, st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    FfnArgs d;
+    memset(&d, 0, sizeof(d));
+    d.A = b.hq;
+    d.ad = b.hd;
+    d.lda = I;
+    d.kdiv = 1;
+    d.pair_of_row = sorted;
+    d.offsets = offsets;
+    d.E = E;
+    d.M = rows;
+    d.q0 = (const uint8_t *)down.q;
+    d.s0 = down.qs;
+    d.qstride = down.q_stride_bytes;
+    d.sstride = down.qs_stride_floats;
+    d.K = I;
+    d.N = s->H;
+    d.out = y;
+    d.ldo = s->H;
+    d.pscale = pscale;
+    return hip_status(moe::launch_ffn_q8(1, wbits, d, rows, offsets ? E : 1, st));
+}
+
+// The two grouped GEMMs of one expert family on sorted rows, int8 activations
+// (x codes gathered by token when `sorted` is given).
+int run_ffn_q8(const moe_shape *s, int wbits, const moe_qmat &gate, const moe_qmat &up, const moe_qmat &down, int I,
+               const int32_t *offsets, const int32_t *sorted, int E, int kdiv, int rows, const float *pscale,
+               const Q8Bufs &b, float *y, hipStream_t st, bool gateup_only = false)
+{
+    if (gate.q_stride_bytes != up.q_stride_bytes || gate.qs_stride_floats != up.qs_stride_floats)
+        return MOE_ERR_UNSUPPORTED;
+    FfnArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A = b.xq;
+    g.ad = b.xd;
+    g.lda = s->H;
+    g.gather = sorted;
+    g.kdiv = kdiv;
+    g.offsets = offsets;
+    g.E = E;
+    g.M = rows;
+    g.q0 = (const uint8_t *)gate.q;
+    g.s0 = gate.qs;
+    g.q1 = (const uint8_t *)up.q;
+    g.s1 = up.qs;
+    g.qstride = gate.q_stride_bytes;
+    g.sstride = gate.qs_stride_floats;
+    g.K = s->H;
+    g.N = I;
+    g.out = b.hf;
+    g.ldo = I;
+    hipError_t e = moe::launch_ffn_q8(0, wbits, g, rows, offsets ? E : 1, st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (gateup_only) return MOE_OK;
+    return run_ffn_q8_down(s, wbits, down, I, offsets, sorted, E, rows, pscale, b, y, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -296,6 +384,7 @@ int moe_expert_ffn(const moe_shape *s, const moe_bf16 *hidden, const moe_weights
     if (!aligned(hidden, 16) || !aligned(y_pairs, 16)) return MOE_ERR_ALIGN;
     if ((st = check_qmat(w->gate)) || (st = check_qmat(w->up)) || (st = check_qmat(w->down))) return st;
     if ((st = check_ws(s, MOE_WS_EXPERT_FFN, ws, ws_bytes))) return st;
+    if (s->flags & MOE_ACT_Q8) return MOE_ERR_UNSUPPORTED;  // the int8-activation mode: moe_layer_forward
     const Layout L = layout(s, MOE_WS_EXPERT_FFN);
     const int wbits = (s->flags & MOE_EXPERT_INT8) ? 8 : 4;
     if (s->flags & MOE_TEST_GATEUP_SUMS) {
@@ -443,6 +532,42 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     int32_t *sorted = at<int32_t>(ws, L.sorted), *inv = at<int32_t>(ws, L.inv);
     float *pscale = at<float>(ws, L.pscale), *ypair = at<float>(ws, L.ypair);
 
+    if (s->flags & MOE_ACT_Q8) {
+        // Q8_0-style int8 activations: x quantised once (routed and shared
+        // experts read the same codes), each h before its down GEMM
+        hipError_t e = moe::launch_router(hidden, w->router_w, w->router_bias, s->T, s->H, s->E, s->top_k,
+                                          s->n_group, s->topk_group, s->routed_scaling_factor, s->top_p,
+                                          at<float>(ws, L.zpart), KS, ids, at<float>(ws, L.w), at<float>(ws, L.gap),
+                                          pscale, sbc, hs);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = moe::launch_scatter(ids, sbc, nsb, P, s->E, sbt * s->top_k, counts, offsets, sorted, inv, hs);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = moe::launch_quant_act_q8(hidden, 1, s->T, s->H, at<int8_t>(ws, L.xq), at<float>(ws, L.xd), hs);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        const Q8Bufs rb{at<int8_t>(ws, L.xq), at<float>(ws, L.xd), at<float>(ws, L.hf), at<int8_t>(ws, L.hq),
+                        at<float>(ws, L.hd)};
+        if (ev_start && hipEventRecord((hipEvent_t)ev_start, hs) != hipSuccess) return MOE_ERR_HIP;
+        st = run_ffn_q8(s, 4, w->gate, w->up, w->down, s->I, offsets, sorted, s->E, s->top_k, P, pscale, rb, ypair,
+                        hs, ev_stop != nullptr);
+        if (st) return st;
+        if (ev_stop) {
+            if (hipEventRecord((hipEvent_t)ev_stop, hs) != hipSuccess) return MOE_ERR_HIP;
+            st = run_ffn_q8_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, rb, ypair, hs);
+            if (st) return st;
+        }
+        if (s->shared_bits) {
+            const Q8Bufs sb{at<int8_t>(ws, L.xq), at<float>(ws, L.xd), at<float>(ws, L.shf), at<int8_t>(ws, L.shq),
+                            at<float>(ws, L.shd)};
+            st = run_ffn_q8(s, s->shared_bits, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr, 1, 1,
+                            s->T, nullptr, sb, at<float>(ws, L.shy), hs);
+            if (st) return st;
+        }
+        return hip_status(moe::launch_combine(ypair, inv, nullptr, 1.f,
+                                              s->shared_bits ? at<float>(ws, L.shy) : nullptr,
+                                              (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr, out, s->T, s->H,
+                                              s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, hs));
+    }
+
     // the shared expert (no dependence on the routing) on the side stream,
     // except in the profiled call, whose events time the routed gate/up alone
     SideStream *side = nullptr;
@@ -534,6 +659,18 @@ int moe_quantize_rows(const void *src, int32_t src_format, int64_t rows, int32_t
     if (!aligned(src, src_format == MOE_SRC_BF16 ? 2 : 4) || !aligned(qs, 4)) return MOE_ERR_ALIGN;
     return hip_status(moe::launch_quantize(src, src_format == MOE_SRC_BF16, (long)rows, cols, bits, q, qs,
                                            (hipStream_t)stream));
+}
+
+int moe_quantize_act_q8(const void *src, int32_t src_format, int64_t rows, int32_t cols, int8_t *q, float *d,
+                        void *stream)
+{
+    if (rows < 0 || cols <= 0 || cols % 32 || (src_format != MOE_SRC_F32 && src_format != MOE_SRC_BF16))
+        return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!src || !q || !d) return MOE_ERR_NULL;
+    if (!aligned(src, 16) || !aligned(q, 16) || !aligned(d, 4)) return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_quant_act_q8(src, src_format == MOE_SRC_BF16, (long)rows, cols, q, d,
+                                               (hipStream_t)stream));
 }
 
 int moe_layer_routing(const moe_shape *s, void *ws, size_t ws_bytes, int32_t **topk_ids, float **topk_w,

@@ -26,6 +26,7 @@ struct FfnArgs {
     void *out;
     int ldo;
     const float *pscale;
+    const float *ad;  // Q8 mode: f32 scale of every 32 activation codes, [rows of A][K/32]
 };
 
 // small-batch regime (decode.hip)
@@ -73,6 +74,11 @@ hipError_t launch_pair_hist(const int32_t *ids, int P, int E, int chunk, int nbl
 hipError_t launch_scatter(const int32_t *ids, const int32_t *bcounts, int nblocks, int P, int E, int chunk,
                           int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *inv, hipStream_t st);
 hipError_t launch_ffn(int mode, int wbits, const FfnArgs &a, int rows_total, int groups, hipStream_t st);
+// Q8_0-style int8 activations (A = int8 codes, ad = their block scales);
+// mode 0 writes h as f32, mode 1 the down rows
+hipError_t launch_ffn_q8(int mode, int wbits, const FfnArgs &a, int rows_total, int groups, hipStream_t st);
+hipError_t launch_quant_act_q8(const void *src, int src_bf16, long rows, int cols, int8_t *q, float *d,
+                               hipStream_t st);
 hipError_t launch_bias_update(int E, const int32_t *counts, float *bias, float gamma, hipStream_t st);
 hipError_t launch_quantize(const void *src, int src_bf16, long rows, int cols, int bits, void *q, float *qs,
                            hipStream_t st);

@@ -224,3 +224,78 @@ hipError_t launch_quantize(const void *src, int src_bf16, long rows, int cols, i
 }
 
 }  // namespace moe
+
+// ------------------------------------------------- Q8_0-style activation codes
+//
+// Int8 activations for the integer-dot expert matmuls (colibri README, "What's
+// implemented": Q8_0-style int8 activations).  Reading: blocks of 32
+// consecutive values along a row; d = max|v| / 127 and each code the nearest
+// integer to v / d (ties to even) inside [-127, 127], both divisions correctly
+// rounded f32; an all-zero block has d = 0 and codes 0.  One thread per
+// block: its 32 values are read as 16-byte vectors, the codes written as two.
+
+namespace moe {
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_quant_act_q8(const void *__restrict__ src, long nblocks,
+                                                      int8_t *__restrict__ q, float *__restrict__ d)
+{
+    const long b = (long)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblocks) return;
+    float v[32];
+    if (BF16) {
+        const u32x4 *s = (const u32x4 *)((const uint16_t *)src + b * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 w = s[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+                v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+            }
+        }
+    } else {
+        const f32x4 *s = (const f32x4 *)((const float *)src + b * 32);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 w = s[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * i + j] = w[j];
+        }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float dd = __fdiv_rn(amax, 127.f);
+    u32x4 out[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float c = 0.f;
+            if (amax != 0.f) c = fminf(fmaxf(rintf(__fdiv_rn(v[4 * i + j], dd)), -127.f), 127.f);
+            word |= ((uint32_t)(int)c & 0xFFu) << (8 * j);
+        }
+        out[i / 4][i % 4] = word;
+    }
+    u32x4 *o = (u32x4 *)(q + b * 32);
+    o[0] = out[0];
+    o[1] = out[1];
+    d[b] = dd;
+}
+
+hipError_t launch_quant_act_q8(const void *src, int src_bf16, long rows, int cols, int8_t *q, float *d,
+                               hipStream_t st)
+{
+    const long nblocks = rows * (cols / 32);
+    if (nblocks <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)((nblocks + 255) / 256);
+    if (src_bf16)
+        hipLaunchKernelGGL(k_quant_act_q8<true>, dim3(grid), dim3(256), 0, st, src, nblocks, q, d);
+    else
+        hipLaunchKernelGGL(k_quant_act_q8<false>, dim3(grid), dim3(256), 0, st, src, nblocks, q, d);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -22,7 +22,7 @@ def moe():
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(moe):
