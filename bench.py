@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 matrix-core peak
 
 
 def sh_of(moe, cfg, T, flags):
@@ -61,6 +62,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="adaptive expert top-p of the workload's router (0 = off, the workloads' own setting)")
+    ap.add_argument("--act-q8", action="store_true",
+                    help="Q8_0-style int8 activations for the expert matmuls (tiled configurations)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--quantize", action="store_true",
@@ -107,6 +110,10 @@ def main():
     cfg = synth.CONFIGS[args.config]
     if args.top_p:
         cfg = cfg.with_(top_p=args.top_p)
+    if args.act_q8:
+        if cfg.T <= 32:
+            sys.exit("--act-q8 is a mode of the tiled configurations (c2, c3, c4)")
+        cfg = cfg.with_(act_q8=True)
     if cfg.T > 32:
         return bench_prefill(args, cfg, moe, synth, torch, np, dev)
     L, T, H = cfg.layers, cfg.T, cfg.H
@@ -426,9 +433,13 @@ def bench_prefill(args, cfg, moe, synth, torch, np, dev):
     gu_flops = 4.0 * P * cfg.I * H
     achieved = gu_flops / (avg_ms / 1e3) / 1e12
     layer_flops = 6.0 * P * H * cfg.I + (6.0 * T * H * cfg.I_sh if cfg.shared_bits else 0.0)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "k_ffn gate/up (routed grouped GEMM + SwiGLU, int4 weights on bf16 MFMA)",
+    q8 = bool(cfg.act_q8)
+    peak = INT8_PEAK_TOPS if q8 else BF16_PEAK_TFLOPS  # a contraction takes the peak of its own type
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TOP/s" if q8 else "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": ("k_ffn_q8 gate/up (routed grouped GEMM + SwiGLU, int8 activations x int4 weights on "
+                           "i8 MFMA)" if q8 else
+                           "k_ffn gate/up (routed grouped GEMM + SwiGLU, int4 weights on bf16 MFMA)"),
                 "avg_launch_us": round(avg_ms * 1e3, 2), "alg_flops_per_launch": gu_flops,
                 "launches_timed": len(kms)}
     cpu = None
@@ -457,13 +468,14 @@ def bench_prefill(args, cfg, moe, synth, torch, np, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 MFMA gate/up, f16 MFMA down, int4 weights, f32 accumulate",
+        "dtype": ("i8 MFMA (Q8_0-style activations x int4/int8 weights), i32 block sums, f32 accumulate" if q8 else
+                  "bf16 MFMA gate/up, f16 MFMA down, int4 weights, f32 accumulate"),
         "data": "synthetic (seeded)",
         "config": {"workload": cfg.name, "T": T, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
                    "I_shared": cfg.I_sh, "shared_bits": cfg.shared_bits, "global_batch": T,
-                   "parallelism": "single GPU", "top_p": cfg.top_p, "routed_pairs": P},
+                   "parallelism": "single GPU", "top_p": cfg.top_p, "routed_pairs": P, "act_q8": q8},
         "layer_TFLOPs": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1),
-        "layer_mfma_frac": round(layer_flops / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "layer_mfma_frac": round(layer_flops / (ms_per_step / 1e3) / 1e12 / peak, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -95,3 +95,18 @@ def test_int8_forms_random_words():
 def test_offset_constants():
     assert bf16(0xC308) == -136.0 and bf16(0xC300) == -128.0
     assert f16(0xE408) == -1032.0 and f16(0xE480) == -1152.0
+
+
+def test_int4_into_int8_code_shifted():
+    """The Q8 GEMM's int4 form (unpack_int4x8_i8): two masks and two byte
+    permutes give byte j = code j << 4 as a signed byte, i.e. sixteen times the
+    two's-complement code, for every nibble value in every position."""
+    rng = np.random.default_rng(3)
+    words = [0x76543210, 0xFEDCBA98, 0x0F0F0F0F, 0xF0F0F0F0] + [int(x) for x in rng.integers(0, 2**32, 2000)]
+    for w in words:
+        lo = (w << 4) & 0xF0F0F0F0
+        hi = w & 0xF0F0F0F0
+        r = [perm(hi, lo, 0x05010400), perm(hi, lo, 0x07030602)]
+        got = [((r[j // 4] >> (8 * (j % 4))) & 0xFF) for j in range(8)]
+        got = [b - 256 if b >= 128 else b for b in got]
+        assert got == [16 * q for q in nibbles(w)], hex(w)
