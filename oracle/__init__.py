@@ -49,7 +49,7 @@ class QMat(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
                 ("gate", QMat), ("up", QMat), ("down", QMat),
-                ("sh_gate", QMat), ("sh_up", QMat), ("sh_down", QMat)]
+                ("sh_gate", QMat), ("sh_up", QMat), ("sh_down", QMat), ("expert_bits", ctypes.c_void_p)]
 
 
 _lib = None
@@ -70,6 +70,7 @@ def lib():
             "oracle_bf16_to_f32": ([ctypes.c_uint16], ctypes.c_float),
             "oracle_f32_to_bf16": ([ctypes.c_float], ctypes.c_uint16),
             "oracle_unpack_int4_row": ([vp, i32, vp], None),
+            "oracle_unpack_int2_row": ([vp, i32, vp], None),
             "oracle_pack_int4_row": ([vp, i32, vp], None),
             "oracle_dequant_row": ([vp, i32, vp, i32, vp], None),
             "oracle_router_scores": ([S, vp, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -133,6 +134,8 @@ class LayerWeights:
             w.sh_gate = QMat(sq.ctypes.data, sqs.ctypes.data, 0, 0)
             w.sh_up = QMat(sq.ctypes.data + smat, sqs.ctypes.data + 4 * Ish, 0, 0)
             w.sh_down = QMat(sq.ctypes.data + 2 * smat, sqs.ctypes.data + 8 * Ish, 0, 0)
+        eb = d.get("expert_bits")
+        w.expert_bits = eb.ctypes.data if eb is not None else None
         self.w = w
 
     def ref(self):

@@ -61,6 +61,16 @@ void oracle_unpack_int4_row(const uint8_t *row, int32_t cols, int32_t *vals)
     }
 }
 
+/* Packed int2 (see oracle_weights.expert_bits): element 4c + j in bits
+ * 2j..2j+1 of byte c, two's complement. */
+void oracle_unpack_int2_row(const uint8_t *row, int32_t cols, int32_t *vals)
+{
+    for (int32_t c = 0; c < cols; ++c) {
+        uint32_t f = ((uint32_t)row[c / 4] >> (2 * (c % 4))) & 3u;
+        vals[c] = (f >= 2u) ? (int32_t)f - 4 : (int32_t)f;
+    }
+}
+
 void oracle_pack_int4_row(const int32_t *vals, int32_t cols, uint8_t *row)
 {
     for (int32_t c = 0; c < cols; c += 2) {
@@ -75,7 +85,13 @@ void oracle_pack_int4_row(const int32_t *vals, int32_t cols, uint8_t *row)
 void oracle_dequant_row(const void *q, int32_t bits, const float *scale, int32_t cols, float *out)
 {
     const float s = scale[0];
-    if (bits == 4) {
+    if (bits == 2) {
+        for (int32_t c = 0; c < cols; ++c) {
+            uint32_t f = ((uint32_t)((const uint8_t *)q)[c / 4] >> (2 * (c % 4))) & 3u;
+            int32_t v = (f >= 2u) ? (int32_t)f - 4 : (int32_t)f;
+            out[c] = (float)v * s;
+        }
+    } else if (bits == 4) {
         const uint8_t *row = (const uint8_t *)q;
         for (int32_t c = 0; c < cols; ++c) {
             uint32_t byte = row[c / 2];
@@ -221,9 +237,12 @@ int oracle_bias_update(int32_t E, const int32_t *counts, const float *bias_in, f
 /* row r of expert e of a matrix family with `cols` columns */
 static const void *qrow(const oracle_qmat *m, int32_t bits, int32_t e, int64_t r, int32_t cols)
 {
-    int64_t row_bytes = (bits == 4) ? cols / 2 : cols;
+    int64_t row_bytes = (bits == 4) ? cols / 2 : (bits == 2) ? cols / 4 : cols;
     return (const uint8_t *)m->q + (int64_t)e * m->q_stride_bytes + r * row_bytes;
 }
+
+/* the weight format of routed expert e */
+static int32_t rbits(const oracle_weights *wt, int32_t e) { return wt->expert_bits ? wt->expert_bits[e] : 4; }
 
 static const float *qscale(const oracle_qmat *m, int32_t e, int64_t r)
 {
@@ -509,6 +528,8 @@ static double q8_dot(const int8_t *q, const float *d, const oracle_qmat *m, int3
     const void *row = qrow(m, bits, e, r, n);
     if (bits == 4) {
         oracle_unpack_int4_row((const uint8_t *)row, n, codes);
+    } else if (bits == 2) {
+        oracle_unpack_int2_row((const uint8_t *)row, n, codes);
     } else {
         for (int32_t c = 0; c < n; ++c) codes[c] = ((const int8_t *)row)[c];
     }
@@ -602,7 +623,8 @@ int oracle_expert_ffn(const oracle_shape *sh, const uint16_t *hidden, const orac
                 int32_t t = p / k;
                 float *y = y_pairs + (int64_t)r * H;
                 widen_row(hidden + (int64_t)t * H, H, xf);
-                ffn_one(xf, H, I, 4, &wt->gate, &wt->up, &wt->down, e, h, wrow, y, (sh->flags & ORACLE_ACT_Q8) != 0);
+                ffn_one(xf, H, I, rbits(wt, e), &wt->gate, &wt->up, &wt->down, e, h, wrow, y,
+                        (sh->flags & ORACLE_ACT_Q8) != 0);
                 if (pair_scale) {
                     const double c = (double)pair_scale[p];
                     for (int32_t j = 0; j < H; ++j) y[j] = (float)((double)y[j] * c);
@@ -782,7 +804,8 @@ int oracle_layer_tokens(const oracle_shape *sh, const oracle_weights *wt, const 
                     widen_row(hidden + (int64_t)t * H, H, xf);
                     for (int32_t j = 0; j < k; ++j)
                         if (ids[(int64_t)i * k + j] >= 0) /* (-1: dropped by adaptive top-p) */
-                            ffn_one(xf, H, I, 4, &wt->gate, &wt->up, &wt->down, ids[(int64_t)i * k + j], h, wrow,
+                            ffn_one(xf, H, I, rbits(wt, ids[(int64_t)i * k + j]), &wt->gate, &wt->up, &wt->down,
+                                    ids[(int64_t)i * k + j], h, wrow,
                                     y + (int64_t)j * H, (sh->flags & ORACLE_ACT_Q8) != 0);
                     for (int32_t c = 0; c < H; ++c) {
                         double acc = 0.0;
@@ -853,7 +876,7 @@ int oracle_layer_forward_dense(const oracle_shape *sh, const oracle_weights *wt,
                 for (int32_t t = 0; t < T; ++t) {
                     widen_row(hidden + (int64_t)t * H, H, xf);
                     for (int32_t e = 0; e < E; ++e)
-                        ffn_one(xf, H, I, 4, &wt->gate, &wt->up, &wt->down, e, h, wrow, y + (int64_t)e * H,
+                        ffn_one(xf, H, I, rbits(wt, e), &wt->gate, &wt->up, &wt->down, e, h, wrow, y + (int64_t)e * H,
                                 (sh->flags & ORACLE_ACT_Q8) != 0);
                     for (int32_t c = 0; c < H; ++c) {
                         double acc = 0.0;

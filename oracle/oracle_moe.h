@@ -86,12 +86,22 @@ typedef struct {
     oracle_qmat gate, up;      /* int4 [E][I][H/2], scales [E][I] */
     oracle_qmat down;          /* int4 [E][H][I/2], scales [E][H] */
     oracle_qmat sh_gate, sh_up, sh_down; /* shared expert, E = 1, int4 or int8 */
+    /* [E] per routed expert: 4 (packed int4) or 2 (packed int2, the cold-tail
+     * experts: colibri-nano README, "the checkpoint surgery tooling ... int2
+     * cold tails"; colibri README, "What's implemented": packed int2 with
+     * per-row scales, dequant-on-use).  Reading: element 4c + j of a row in
+     * bits 2j..2j+1 of byte c, two's complement (-2..1), one f32 scale per
+     * row, the row cols/4 bytes; an int2 expert's matrices sit where an int4
+     * expert's would (same expert stride, the first half of each).  NULL: all
+     * int4. */
+    const uint8_t *expert_bits;
 } oracle_weights;
 
 /* format helpers (the pins of the packed layout) */
 float oracle_bf16_to_f32(uint16_t bits);
 uint16_t oracle_f32_to_bf16(float f);
 void oracle_unpack_int4_row(const uint8_t *row, int32_t cols, int32_t *vals);
+void oracle_unpack_int2_row(const uint8_t *row, int32_t cols, int32_t *vals);
 void oracle_pack_int4_row(const int32_t *vals, int32_t cols, uint8_t *row);
 void oracle_dequant_row(const void *q, int32_t bits, const float *scale, int32_t cols, float *out);
 

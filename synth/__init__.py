@@ -110,6 +110,7 @@ class LayerConfig:
     skew: Optional[str] = None    # None | "hot8x3" | "zipf1.2"
     top_p: float = 0.0            # adaptive expert top-p (0 = keep all top_k)
     act_q8: bool = False          # Q8_0-style int8 activations for the expert matmuls
+    int2_frac: float = 0.0        # fraction of routed experts stored as packed int2 (cold-tail experts)
     # value distributions
     x_std: float = 1.0
     w_std: float = 0.02
@@ -267,12 +268,50 @@ def shared(cfg: LayerConfig, layer: int = 0):
     return q, qs
 
 
+def expert_bits(cfg: LayerConfig, layer: int = 0) -> np.ndarray:
+    """uint8 [E]: 2 for the cold-tail experts (a seeded choice of round(int2_frac * E)), 4 for the rest."""
+    bits = np.full(cfg.E, 4, np.uint8)
+    n2 = int(round(cfg.int2_frac * cfg.E))
+    if n2:
+        rng = np.random.default_rng([cfg.seed, layer, 0x1D2])
+        bits[rng.choice(cfg.E, n2, replace=False)] = 2
+    return bits
+
+
+def _int2_rows(rng, rows: int, cols: int) -> np.ndarray:
+    """rows x cols codes uniform over {-1, 0, 1}, packed four per byte (element
+    4c + j in bits 2j..2j+1 of byte c, two's complement)."""
+    c = (rng.integers(-1, 2, size=(rows, cols)).astype(np.int32) & 3).astype(np.uint8).reshape(rows, cols // 4, 4)
+    return (c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)).astype(np.uint8)
+
+
+def make_int2_experts(cfg: LayerConfig, layer: int, q: np.ndarray, qs: np.ndarray, bits: np.ndarray):
+    """Re-draw the cold-tail experts in place as packed int2: each matrix in
+    the first half of its int4-sized region (the rest zero), its scales times
+    qmax4 so the weights keep their magnitude."""
+    E, H, I = cfg.E, cfg.H, cfg.I
+    mat = I * H // 2
+    for e in np.nonzero(bits == 2)[0]:
+        rng = np.random.default_rng([cfg.seed, layer, 0x1D2, int(e)])
+        q[e] = 0
+        q[e, 0:mat // 2] = _int2_rows(rng, I, H).ravel()
+        q[e, mat:mat + mat // 2] = _int2_rows(rng, I, H).ravel()
+        q[e, 2 * mat:2 * mat + mat // 2] = _int2_rows(rng, H, I).ravel()
+        qs[e] *= np.float32(cfg.qmax4)
+
+
 def layer(cfg: LayerConfig, layer_idx: int = 0, with_hidden: bool = True, table: Optional[dict] = None) -> dict:
     """All inputs of one layer as a dict of host arrays (see module docstring)."""
     W, b = router(cfg, layer_idx, table=table)
     q, qs = experts(cfg, layer_idx)
+    eb = None
+    if cfg.int2_frac > 0:
+        eb = expert_bits(cfg, layer_idx)
+        make_int2_experts(cfg, layer_idx, q, qs, eb)
     sq, sqs = shared(cfg, layer_idx)
     d = dict(router_w=W, router_bias=b, experts_q=q, experts_qs=qs, shared_q=sq, shared_qs=sqs)
+    if eb is not None:
+        d["expert_bits"] = eb
     if with_hidden:
         d["hidden"] = hidden(cfg, layer_idx)
     return d

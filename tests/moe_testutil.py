@@ -32,6 +32,16 @@ def unpack_int4(packed: np.ndarray, cols: int) -> np.ndarray:
     return out
 
 
+def unpack_int2(packed: np.ndarray, cols: int) -> np.ndarray:
+    """[..., cols/4] uint8 -> [..., cols] int8; field j of byte c is element 4c + j, two's complement."""
+    b = np.asarray(packed, np.uint8)
+    out = np.empty(b.shape[:-1] + (cols,), np.int8)
+    for j in range(4):
+        f = ((b >> (2 * j)) & 3).astype(np.int16)
+        out[..., j::4] = np.where(f >= 2, f - 4, f)
+    return out
+
+
 def pack_int4(q: np.ndarray) -> np.ndarray:
     q = np.asarray(q, np.int16)
     lo = (q[..., 0::2] & 0xF).astype(np.uint8)
@@ -45,6 +55,12 @@ def expert_mats(cfg, d: dict, e: int):
     mat = I * H // 2
     q = d["experts_q"][e]
     qs = d["experts_qs"][e]
+    if "expert_bits" in d and d["expert_bits"][e] == 2:
+        q2 = mat // 2
+        g = unpack_int2(q[:q2].reshape(I, H // 4), H).astype(np.float64) * qs[:I, None].astype(np.float64)
+        u = unpack_int2(q[mat:mat + q2].reshape(I, H // 4), H).astype(np.float64) * qs[I:2 * I, None].astype(np.float64)
+        dn = unpack_int2(q[2 * mat:2 * mat + q2].reshape(H, I // 4), I).astype(np.float64) * qs[2 * I:, None].astype(np.float64)
+        return g, u, dn
     g = unpack_int4(q[:mat].reshape(I, H // 2), H).astype(np.float64) * qs[:I, None].astype(np.float64)
     u = unpack_int4(q[mat:2 * mat].reshape(I, H // 2), H).astype(np.float64) * qs[I:2 * I, None].astype(np.float64)
     dn = unpack_int4(q[2 * mat:].reshape(H, I // 2), I).astype(np.float64) * qs[2 * I:, None].astype(np.float64)

@@ -41,6 +41,11 @@ MUTANTS = {
     "q8 blocks of 16": ("for (int32_t b = 0; b < n / 32; ++b) d[b] = q8_block(v + 32 * b, 32, q + 32 * b);",
                         "for (int32_t b = 0; b < n / 32; ++b) { d[b] = q8_block(v + 32 * b, 16, q + 32 * b); "
                         "q8_block(v + 32 * b + 16, 16, q + 32 * b + 16); }"),
+    "int2 fields from the high bits": ("uint32_t f = ((uint32_t)row[c / 4] >> (2 * (c % 4))) & 3u;",
+                                       "uint32_t f = ((uint32_t)row[c / 4] >> (6 - 2 * (c % 4))) & 3u;"),
+    "int2 without sign": ("vals[c] = (f >= 2u) ? (int32_t)f - 4 : (int32_t)f;", "vals[c] = (int32_t)f;"),
+    "int2 row length of int4": ("int64_t row_bytes = (bits == 4) ? cols / 2 : (bits == 2) ? cols / 4 : cols;",
+                                "int64_t row_bytes = (bits == 4 || bits == 2) ? cols / 2 : cols;"),
     "down transposed": ("oracle_dequant_row(qrow(down, bits, e, c, I), bits, qscale(down, e, c), I, wrow);",
                         "for (int32_t i2 = 0; i2 < I; ++i2) oracle_dequant_row(qrow(down, bits, e, i2 % H, I), bits, qscale(down, e, c), 1, wrow + i2);"),
 }

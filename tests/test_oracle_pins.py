@@ -745,3 +745,71 @@ def test_q8_shape_rule(synth_mod, oracle_mod):
     d, lw = make(synth_mod, oracle_mod, cfg)
     with pytest.raises(RuntimeError):
         oracle_mod.layer_forward(cfg, lw, d["hidden"])
+
+
+# ------------------------------------------------ int2 cold-tail experts
+
+def test_int2_byte_decode_golden_and_exhaustive(oracle_mod):
+    """0xE4 = fields 00, 01, 10, 11 from the low bits: elements 0, 1, -2, -1;
+    and every byte value against a direct reading of its four fields."""
+    import ctypes
+    def decode(row, cols):
+        vals = np.zeros(cols, np.int32)
+        oracle_mod.lib().oracle_unpack_int2_row(row.ctypes.data, cols, vals.ctypes.data)
+        return vals
+    assert decode(np.array([0xE4], np.uint8), 4).tolist() == [0, 1, -2, -1]
+    allb = np.arange(256, dtype=np.uint8)
+    got = decode(allb, 1024).reshape(256, 4)
+    for b in range(256):
+        want = [((b >> (2 * j)) & 3) - (4 if (b >> (2 * j)) & 2 else 0) for j in range(4)]
+        assert got[b].tolist() == want
+    s = np.array([0.75], np.float32)
+    out = np.zeros(1024, np.float32)
+    oracle_mod.lib().oracle_dequant_row(allb.ctypes.data, 2, s.ctypes.data, 1024, out.ctypes.data)
+    assert np.array_equal(out, got.ravel().astype(np.float32) * np.float32(0.75))
+
+
+def test_int2_layer_against_numpy_sparse_sum(synth_mod, oracle_mod):
+    """A layer with half its routed experts in int2 against the numpy sum over
+    the routing, each expert decoded by numpy in its own format."""
+    cfg = tiny_cfg(synth_mod, T=16, E=8, k=3, rsf=1.5, int2_frac=0.5)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    assert (d["expert_bits"] == 2).sum() == 4
+    out, ids, w, _, _ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    assert np.isin(ids, np.nonzero(d["expert_bits"] == 2)[0]).any()
+    x = U.bf16_to_f32(d["hidden"]).astype(np.float64)
+    ref = U.swiglu_mlp(x, *U.shared_mats(cfg, d))
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            ref[t] += 1.5 * float(w[t, j]) * U.swiglu_mlp(x[t:t + 1], *U.expert_mats(cfg, d, ids[t, j]))[0]
+    assert U.rel_max_err(out, ref) < 2e-6
+
+
+@pytest.mark.parametrize("q8", [False, True])
+def test_int2_expert_equals_its_int4_encoding(synth_mod, oracle_mod, q8):
+    """Codes -1..1 fit int4: the same experts re-encoded as int4 (same scales)
+    give the same bits, in the plain and in the Q8 mode."""
+    cfg = tiny_cfg(synth_mod, T=16, E=8, k=2, I_sh=64, int2_frac=0.5, act_q8=q8)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    out2, *_ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    H, I = cfg.H, cfg.I
+    mat = I * H // 2
+    d4 = dict(d)
+    q4 = d["experts_q"].copy()
+    for e in np.nonzero(d["expert_bits"] == 2)[0]:
+        q = d["experts_q"][e]
+        for off, rows, cols in ((0, I, H), (mat, I, H), (2 * mat, H, I)):
+            codes = U.unpack_int2(q[off:off + rows * cols // 4].reshape(rows, cols // 4), cols)
+            q4[e, off:off + rows * cols // 2] = U.pack_int4(codes).ravel()
+    d4["experts_q"] = q4
+    d4["expert_bits"] = np.full(cfg.E, 4, np.uint8)
+    out4, *_ = oracle_mod.layer_forward(cfg, oracle_mod.LayerWeights(cfg, d4), d["hidden"])
+    assert np.array_equal(out2, out4)
+
+
+def test_int2_sparse_equals_dense_mask(synth_mod, oracle_mod):
+    cfg = tiny_cfg(synth_mod, int2_frac=0.4)
+    d, lw = make(synth_mod, oracle_mod, cfg)
+    sparse, *_ = oracle_mod.layer_forward(cfg, lw, d["hidden"])
+    dense = oracle_mod.layer_forward_dense(cfg, lw, d["hidden"])
+    assert np.allclose(sparse, dense, rtol=2e-7, atol=1e-9)
