@@ -64,6 +64,8 @@ def parse():
                     help="adaptive expert top-p of the workload's router (0 = off, the workloads' own setting)")
     ap.add_argument("--act-q8", action="store_true",
                     help="Q8_0-style int8 activations for the expert matmuls (tiled configurations)")
+    ap.add_argument("--int2-frac", type=float, default=0.0,
+                    help="fraction of routed experts stored as packed int2 (cold-tail experts; tiled configurations)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--quantize", action="store_true",
@@ -114,6 +116,10 @@ def main():
         if cfg.T <= 32:
             sys.exit("--act-q8 is a mode of the tiled configurations (c2, c3, c4)")
         cfg = cfg.with_(act_q8=True)
+    if args.int2_frac:
+        if cfg.T <= 32:
+            sys.exit("--int2-frac is a mode of the tiled configurations (c2, c3, c4)")
+        cfg = cfg.with_(int2_frac=args.int2_frac)
     if cfg.T > 32:
         return bench_prefill(args, cfg, moe, synth, torch, np, dev)
     L, T, H = cfg.layers, cfg.T, cfg.H
@@ -473,7 +479,8 @@ def bench_prefill(args, cfg, moe, synth, torch, np, dev):
         "data": "synthetic (seeded)",
         "config": {"workload": cfg.name, "T": T, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
                    "I_shared": cfg.I_sh, "shared_bits": cfg.shared_bits, "global_batch": T,
-                   "parallelism": "single GPU", "top_p": cfg.top_p, "routed_pairs": P, "act_q8": q8},
+                   "parallelism": "single GPU", "top_p": cfg.top_p, "routed_pairs": P, "act_q8": q8,
+                   "int2_frac": cfg.int2_frac},
         "layer_TFLOPs": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1),
         "layer_mfma_frac": round(layer_flops / (ms_per_step / 1e3) / 1e12 / peak, 4),
         "roofline": roofline,

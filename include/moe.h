@@ -91,6 +91,9 @@ extern "C" {
                                gives; a dot is s_w * sum over blocks of d * (integer sum of code products).
                                Always the tiled kernels (v_mfma_i32_16x16x32_i8); the router is unchanged.
                                moe_expert_ffn and moe_layer_forward_chain return MOE_ERR_UNSUPPORTED */
+#define MOE_EXPERT_MIXED 0x2000u /* routed experts in int4 or int2 per weights->expert_bits (the tiled kernels at
+                               any T; with MOE_ACT_Q8, MOE_TEST_GATEUP_SUMS or in a chained call:
+                               MOE_ERR_UNSUPPORTED) */
 #define MOE_TEST_GATEUP_SUMS 0x100u /* moe_expert_ffn, testing only: write the raw integer-weight sums
                                sum_h x*q of gate into y_pairs[r][0:I] and of up into y_pairs[r][I:2I]
                                (no scale, no activation, no down projection); needs 2*I <= H, int4 */
@@ -134,6 +137,13 @@ typedef struct {
     const float *router_bias; /* [E] f32; selection only */
     moe_qmat gate, up, down;  /* routed experts, int4 */
     moe_qmat sh_gate, sh_up, sh_down; /* shared expert (E = 1), int4 or int8 per shared_bits */
+    /* with MOE_EXPERT_MIXED: device [E] u8, each routed expert's format, 4 (packed int4) or 2
+     * (packed int2, the cold-tail experts of the colibri-nano README, "int2 cold tails"; colibri
+     * README, "What's implemented": packed int2 with per-row scales).  Int2: element 4c + j of a row
+     * in bits 2j..2j+1 of byte c, two's complement, rows of cols/4 bytes, one f32 scale per row; an
+     * int2 expert's gate, up and down start where an int4 expert's would (same strides), so its
+     * matrices take the first half of each region.  Ignored without the flag. */
+    const uint8_t *expert_bits;
 } moe_weights;
 
 /*

@@ -35,6 +35,7 @@ MOE_STAGE_GATEUP_ONLY = 0x200
 MOE_STAGE_EXPERTS_ONLY = 0x400
 MOE_LOGITS_GIVEN = 0x800
 MOE_ACT_Q8 = 0x1000
+MOE_EXPERT_MIXED = 0x2000
 
 MOE_SRC_F32 = 0
 MOE_SRC_BF16 = 1
@@ -65,7 +66,7 @@ class MoeQMat(ctypes.Structure):
 class MoeWeights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
                 ("gate", MoeQMat), ("up", MoeQMat), ("down", MoeQMat),
-                ("sh_gate", MoeQMat), ("sh_up", MoeQMat), ("sh_down", MoeQMat)]
+                ("sh_gate", MoeQMat), ("sh_up", MoeQMat), ("sh_down", MoeQMat), ("expert_bits", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -134,6 +135,8 @@ def shape_of(cfg, T: Optional[int] = None, flags: int = 0) -> MoeShape:
     """MoeShape of a synth.LayerConfig-like object (fields T,H,E,k,I,I_sh,...)."""
     if getattr(cfg, "act_q8", False):
         flags |= MOE_ACT_Q8
+    if getattr(cfg, "int2_frac", 0.0) > 0:
+        flags |= MOE_EXPERT_MIXED
     return shape(cfg.T if T is None else T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_sh, cfg.shared_bits, cfg.n_group,
                  cfg.topk_group, cfg.rsf, flags, float(getattr(cfg, "top_p", 0.0)))
 
@@ -287,6 +290,7 @@ class MoeLayer:
         self.experts_qs = up(arrays["experts_qs"])
         self.shared_q = up(arrays.get("shared_q"))
         self.shared_qs = up(arrays.get("shared_qs"))
+        self.expert_bits = up(arrays.get("expert_bits"))
         H, I, Ish = cfg.H, cfg.I, cfg.I_sh
         mat = I * H // 2
         blk, sblk = 3 * mat, 2 * I + H
@@ -301,6 +305,8 @@ class MoeLayer:
             w.sh_gate = qmat(self.shared_q, self.shared_qs, 0, 0, 0, 0)
             w.sh_up = qmat(self.shared_q, self.shared_qs, 0, 0, smat, Ish)
             w.sh_down = qmat(self.shared_q, self.shared_qs, 0, 0, 2 * smat, 2 * Ish)
+        if self.expert_bits is not None:
+            w.expert_bits = _ptr(self.expert_bits)
         self.weights = w
 
     def workspace(self, T: int, flags: int = 0):

@@ -107,7 +107,19 @@ __device__ __forceinline__ int hpos(int j)
 // MODE 2: gate/up raw integer-weight sums (no scale, no activation) -> f32
 // [rows][0:N] (gate) and [rows][N:2N] (up), for the exactness test.
 template <int MODE, int WBITS, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
+struct FfShape {
+    static constexpr int NMAT = (MODE == 1) ? 1 : 2;
+    static constexpr int BKB = FF_BK * WBITS / 8;  // bytes of a B row per stage
+    static constexpr int LDB = BKB + 16;           // LDS B row stride in bytes
+    static constexpr int ABUF = BM * FF_LDA;       // bf16 elements of one A buffer
+    static constexpr int BBUF = NMAT * BN * LDB;   // bytes of one B buffer
+};
+
+// One (m-tile, n-tile) of expert e: rows [row0, row0 + rows), columns
+// [n0, n0 + BN), weights in the WBITS format; sA / sB / sRow: the kernel's LDS.
+template <int MODE, int WBITS, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void ffn_tile(const FfnArgs &a, int e, int row0, int rows, int n0, uint16_t *sA,
+                                         uint8_t *sB, float *sRow)
 {
     constexpr int NMAT = (MODE == 1) ? 1 : 2;
     constexpr int NPLANE = 1;
@@ -126,21 +138,6 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
     constexpr int BBUF = BROWS * LDB;             // bytes of one B buffer
     static_assert(WM * WN == 4, "four waves");
     static_assert(MB >= 1 && NB >= 1, "wave tile");
-
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2 * ABUF];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2 * BBUF];
-    __shared__ float sRow[BM];
-
-    // XCD-aware placement: workgroup b runs on XCD b % 8; the NT n-tiles of
-    // m-tile slot s get workgroups on XCD s % 8, so the slot's activation rows
-    // are fetched into one L2 and re-read from there
-    const int NT = a.N / BN;
-    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-    const int nt = q % NT;
-    const int slot = (q / NT) * 8 + xcd;
-    int e, row0, rows;
-    if (!find_tile<BM>(a, slot, e, row0, rows)) return;
-    const int n0 = nt * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -247,6 +244,9 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
                     if (WBITS == 4) {
                         const uint32_t w = *(const uint32_t *)(bp + ks * 16 + (lane >> 4) * 4);
                         bf = F16 ? unpack_int4x8_f16(w) : unpack_int4x8(w);
+                    } else if (WBITS == 2) {
+                        const uint32_t w = *(const uint16_t *)(bp + ks * 8 + (lane >> 4) * 2);
+                        bf = F16 ? unpack_int2x8<0x6400u>(w) : unpack_int2x8<0x4300u>(w);
                     } else {
                         const u32x2 w = *(const u32x2 *)(bp + ks * 32 + (lane >> 4) * 8);
                         bf = F16 ? unpack_int8x8_f16(w) : unpack_int8x8(w);
@@ -279,7 +279,8 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
     }
     __syncthreads();
 
-    const float bias = F16 ? (WBITS == 4 ? INT4_F16_BIAS : INT8_F16_BIAS) : (WBITS == 4 ? INT4_BIAS : 0.f);
+    const float bias = F16 ? (WBITS == 4 ? INT4_F16_BIAS : WBITS == 2 ? INT2_F16_BIAS : INT8_F16_BIAS)
+                           : (WBITS == 4 ? INT4_BIAS : WBITS == 2 ? INT2_BIAS : 0.f);
     const float *sc0 = a.s0 + (size_t)e * a.sstride;
     const float *sc1 = (MODE != 1) ? a.s1 + (size_t)e * a.sstride : nullptr;
 #pragma unroll
@@ -317,6 +318,47 @@ __global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
                 }
             }
         }
+}
+
+template <int MODE, int WBITS, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256, 2) void k_ffn(FfnArgs a)
+{
+    using S = FfShape<MODE, WBITS, BM, BN, WM, WN>;
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2 * S::ABUF];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2 * S::BBUF];
+    __shared__ float sRow[BM];
+    // XCD-aware placement: workgroup b runs on XCD b % 8; the NT n-tiles of
+    // m-tile slot s get workgroups on XCD s % 8, so the slot's activation rows
+    // are fetched into one L2 and re-read from there
+    const int NT = a.N / BN;
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int nt = q % NT;
+    const int slot = (q / NT) * 8 + xcd;
+    int e, row0, rows;
+    if (!find_tile<BM>(a, slot, e, row0, rows)) return;
+    ffn_tile<MODE, WBITS, BM, BN, WM, WN>(a, e, row0, rows, nt * BN, sA, sB, sRow);
+}
+
+// A family whose experts are int4 or int2 each (a.ebits): the tile's expert
+// decides which body runs; the LDS is sized for int4, the larger stage.
+template <int MODE, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256, 2) void k_ffn_mix(FfnArgs a)
+{
+    using S = FfShape<MODE, 4, BM, BN, WM, WN>;
+    static_assert(FfShape<MODE, 2, BM, BN, WM, WN>::BBUF <= S::BBUF, "int2 stage fits the int4 one");
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2 * S::ABUF];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2 * S::BBUF];
+    __shared__ float sRow[BM];
+    const int NT = a.N / BN;
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int nt = q % NT;
+    const int slot = (q / NT) * 8 + xcd;
+    int e, row0, rows;
+    if (!find_tile<BM>(a, slot, e, row0, rows)) return;
+    if (a.ebits[e] == 2)
+        ffn_tile<MODE, 2, BM, BN, WM, WN>(a, e, row0, rows, nt * BN, sA, sB, sRow);
+    else
+        ffn_tile<MODE, 4, BM, BN, WM, WN>(a, e, row0, rows, nt * BN, sA, sB, sRow);
 }
 
 // ------------------------------------------------------------------ pipelined tiles (64 and 128 rows)
@@ -932,8 +974,34 @@ hipError_t launch_ffn_q8(int mode, int wbits, const FfnArgs &a, int rows_total, 
     return wbits == 4 ? launch_q8_mode<1, 4>(a, rows_total, groups, st) : launch_q8_mode<1, 8>(a, rows_total, groups, st);
 }
 
+template <int MODE, int BM, int BN, int WM, int WN>
+static hipError_t launch_mix(const FfnArgs &a, int slots, hipStream_t st)
+{
+    const int NT = a.N / BN;
+    const long grid = (long)((slots + 7) / 8 * 8) * NT;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((k_ffn_mix<MODE, BM, BN, WM, WN>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+// int4/int2 families: the register-staged tiles, 16 or 64 rows by the mean
+// rows per expert, 64 columns.
+template <int MODE>
+static hipError_t launch_mix_mode(const FfnArgs &a, int rows_total, int groups, hipStream_t st)
+{
+    const bool big = rows_total >= 24 * groups;
+    const int bm = big ? 64 : 16;
+    const int slots = (rows_total + bm - 1) / bm + min(groups, rows_total);
+    if (big) return launch_mix<MODE, 64, 64, 2, 2>(a, slots, st);
+    return launch_mix<MODE, 16, 64, 1, 4>(a, slots, st);
+}
+
 hipError_t launch_ffn(int mode, int wbits, const FfnArgs &a, int rows_total, int groups, hipStream_t st)
 {
+    if (a.ebits) {
+        if (!a.offsets || mode == 2) return hipErrorInvalidValue;
+        return mode == 0 ? launch_mix_mode<0>(a, rows_total, groups, st) : launch_mix_mode<1>(a, rows_total, groups, st);
+    }
     if (mode == 2) return launch_mode<2, 4>(a, rows_total, groups, st);
     if (mode == 0) return wbits == 4 ? launch_mode<0, 4>(a, rows_total, groups, st)
                                      : launch_mode<0, 8>(a, rows_total, groups, st);

@@ -66,6 +66,8 @@ int validate(const moe_shape *s)
     if (s->H % 128 || s->I % 64) return MOE_ERR_UNSUPPORTED;
     if (s->shared_bits && s->I_shared % 64) return MOE_ERR_UNSUPPORTED;
     if (s->E > 256 || s->top_k > 64 || s->n_group > 64) return MOE_ERR_UNSUPPORTED;
+    if ((s->flags & MOE_EXPERT_MIXED) && (s->flags & (MOE_ACT_Q8 | MOE_TEST_GATEUP_SUMS | MOE_EXPERT_INT8)))
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -88,7 +90,7 @@ struct Layout {
 
 bool use_decode(const moe_shape *s)
 {
-    if (s->flags & MOE_ACT_Q8) return false;  // the int8-activation mode runs the tiled kernels
+    if (s->flags & (MOE_ACT_Q8 | MOE_EXPERT_MIXED)) return false;  // these modes run the tiled kernels
     return moe::decode_supported(s->T, s->H, s->E, s->top_k, s->I, s->I_shared, s->shared_bits);
 }
 
@@ -177,12 +179,13 @@ int check_ws(const moe_shape *s, int which, void *ws, size_t ws_bytes)
 
 int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
                  const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, float *y,
-                 hipStream_t st);
+                 hipStream_t st, const uint8_t *ebits = nullptr);
 
 // The two grouped GEMMs of one expert family on sorted rows.
 int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qmat &gate, const moe_qmat &up,
             const moe_qmat &down, int I, const int32_t *offsets, const int32_t *sorted, int E, int kdiv, int rows,
-            const float *pscale, uint16_t *hbuf, float *y, hipStream_t st, bool gateup_only = false)
+            const float *pscale, uint16_t *hbuf, float *y, hipStream_t st, bool gateup_only = false,
+            const uint8_t *ebits = nullptr)
 {
     if (gate.q_stride_bytes != up.q_stride_bytes || gate.qs_stride_floats != up.qs_stride_floats)
         return MOE_ERR_UNSUPPORTED;
@@ -205,16 +208,17 @@ int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qma
     g.N = I;
     g.out = hbuf;
     g.ldo = I;
+    g.ebits = ebits;
     hipError_t e = moe::launch_ffn(0, wbits, g, rows, offsets ? E : 1, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (gateup_only) return MOE_OK;
-    return run_ffn_down(s, wbits, down, I, offsets, sorted, E, rows, pscale, hbuf, y, st);
+    return run_ffn_down(s, wbits, down, I, offsets, sorted, E, rows, pscale, hbuf, y, st, ebits);
 }
 
 // The down GEMM on h (f32) of sorted rows.
 int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
                  const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, float *y,
-                 hipStream_t st)
+                 hipStream_t st, const uint8_t *ebits)
 {
     FfnArgs d;
     memset(&d, 0, sizeof(d));
@@ -235,6 +239,7 @@ int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, con
     d.out = y;
     d.ldo = s->H;
     d.pscale = pscale;
+    d.ebits = ebits;
     return hip_status(moe::launch_ffn(1, wbits, d, rows, offsets ? E : 1, st));
 }
 
@@ -411,9 +416,11 @@ int moe_expert_ffn(const moe_shape *s, const moe_bf16 *hidden, const moe_weights
         g.ldo = s->H;
         return hip_status(moe::launch_ffn(2, 4, g, s->T * s->top_k, s->E, (hipStream_t)stream));
     }
+    if ((s->flags & MOE_EXPERT_MIXED) && !w->expert_bits) return MOE_ERR_NULL;
     return run_ffn(s, wbits, hidden, w->gate, w->up, w->down, s->I, offsets, sorted_pairs, s->E, s->top_k,
                    s->T * s->top_k, pair_scale, at<uint16_t>(ws, L.hbuf), y_pairs, (hipStream_t)stream,
-                   (s->flags & MOE_STAGE_GATEUP_ONLY) != 0);
+                   (s->flags & MOE_STAGE_GATEUP_ONLY) != 0,
+                   (s->flags & MOE_EXPERT_MIXED) ? w->expert_bits : nullptr);
 }
 
 int moe_combine(const moe_shape *s, const float *y_pairs, const int32_t *inv_pos, const float *topk_w,
@@ -453,6 +460,8 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     if ((st = check_ws(s, MOE_WS_LAYER, ws, ws_bytes))) return st;
     if (w->gate.q_stride_bytes != w->up.q_stride_bytes || w->gate.qs_stride_floats != w->up.qs_stride_floats)
         return MOE_ERR_UNSUPPORTED;
+    if ((s->flags & MOE_EXPERT_MIXED) && !w->expert_bits) return MOE_ERR_NULL;
+    const uint8_t *ebits = (s->flags & MOE_EXPERT_MIXED) ? w->expert_bits : nullptr;
     const Layout L = layout(s, MOE_WS_LAYER);
     hipStream_t hs = (hipStream_t)stream;
     if ((s->flags & (MOE_STAGE_EXPERTS_ONLY | MOE_LOGITS_GIVEN)) && !L.decode) return MOE_ERR_UNSUPPORTED;
@@ -593,12 +602,13 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (ev_start && hipEventRecord((hipEvent_t)ev_start, hs) != hipSuccess) return MOE_ERR_HIP;
     st = run_ffn(s, 4, hidden, w->gate, w->up, w->down, s->I, offsets, sorted, s->E, s->top_k, P, pscale,
-                 at<uint16_t>(ws, L.hbuf), ypair, hs, ev_stop != nullptr);
+                 at<uint16_t>(ws, L.hbuf), ypair, hs, ev_stop != nullptr, ebits);
     if (st) return st;
     if (ev_stop) {
         // profiled: the routed gate/up kernel ran alone between the events; now the down GEMM
         if (hipEventRecord((hipEvent_t)ev_stop, hs) != hipSuccess) return MOE_ERR_HIP;
-        st = run_ffn_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, at<uint16_t>(ws, L.hbuf), ypair, hs);
+        st = run_ffn_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, at<uint16_t>(ws, L.hbuf), ypair, hs,
+                          ebits);
         if (st) return st;
     }
     if (side) {

@@ -124,6 +124,23 @@ __device__ __forceinline__ u32x4 unpack_int8x8_bf16o(u32x2 w)
 //    one byte permute per pair (the 0x64 bytes come from a constant).
 // The caller removes the constant with (its bias) * (sum of the A row).
 constexpr float INT4_F16_BIAS = 1032.0f;
+constexpr float INT2_BIAS = 130.0f;       // int2 code + 130 in bf16
+constexpr float INT2_F16_BIAS = 1026.0f;  // int2 code + 1026 in f16
+
+// Eight packed int2 codes (element j in bits 2j..2j+1 of w, two's complement)
+// -> four pairs of 16-bit values 2^e + (code + 2) in natural order: the field
+// XOR 2 is code + 2 (0..3), ORed into the mantissa of 128 (bf16, hi =
+// 0x4300) or 1024 (f16, hi = 0x6400).  Pair i holds elements 2i (low half)
+// and 2i + 1: t = w | w << 14 puts element 2i + 1 sixteen bits above 2i.
+template <uint32_t HI>
+__device__ __forceinline__ u32x4 unpack_int2x8(uint32_t w)
+{
+    const uint32_t t = (w & 0xFFFFu) | ((w & 0xFFFFu) << 14);
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (((t >> (4 * i)) & 0x00030003u) ^ 0x00020002u) | (HI | (HI << 16));
+    return r;
+}
 constexpr float INT8_F16_BIAS = 1152.0f;
 
 __device__ __forceinline__ u32x4 unpack_int4x8_f16(uint32_t w)

@@ -27,6 +27,7 @@ struct FfnArgs {
     int ldo;
     const float *pscale;
     const float *ad;  // Q8 mode: f32 scale of every 32 activation codes, [rows of A][K/32]
+    const uint8_t *ebits;  // per-expert format (4 or 2) of a mixed family, or null (all WBITS)
 };
 
 // small-batch regime (decode.hip)

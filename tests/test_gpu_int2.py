@@ -1,0 +1,70 @@
+"""GPU: routed experts in int4 or int2 each (MOE_EXPERT_MIXED, the cold-tail
+experts) against the oracle.
+
+Bars as in test_gpu_parity.py: routing bit-exact outside near ties (the
+router does not see the formats), outputs within 1e-2 * RMS of the oracle's
+layer with each expert dequantised in its own format.
+"""
+import numpy as np
+import pytest
+
+import int4_routed_expert_02_amd as moe
+import synth
+from gpu_util import check_output, check_routing, run_layer, say, small_cfg
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.load()
+
+
+CASES = {
+    "c0_T16_quarter": synth.CONFIGS["c0"].with_(T=16, int2_frac=0.25),
+    "c0_T100_ragged_half": synth.CONFIGS["c0"].with_(T=100, seed=11, int2_frac=0.5),
+    "c2_shape_T700_quarter": synth.CONFIGS["c2"].with_(T=700, seed=21, int2_frac=0.25),
+    "c4_int8_shared_T300": synth.CONFIGS["c4"].with_(T=300, seed=23, int2_frac=0.3),
+    "grouped_E64_k8_all_int2": small_cfg(E=64, k=8, n_group=8, topk_group=4, rsf=2.5, T=40, I=64, I_sh=128,
+                                         int2_frac=1.0),
+    "no_shared_E8": small_cfg(E=8, T=50, shared_bits=0, int2_frac=0.5),
+    "c3_shape_T256": synth.CONFIGS["c3"].with_(T=256, seed=24, int2_frac=0.25),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_mixed_int2_layer_parity(name):
+    cfg = CASES[name]
+    d = synth.layer(cfg)
+    got, ids, w, offsets, srt = run_layer(cfg, d)
+    ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag=f"int2 {name}")
+    cold = np.isin(ids, np.nonzero(d["expert_bits"] == 2)[0])
+    say(f"int2 {name}: {int(cold.sum())} of {ids.size} pairs on int2 experts")
+    assert cold.any()
+    toks = None
+    if cfg.T * cfg.H > 200 * 1024:
+        rng = np.random.default_rng(9)
+        toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 48, replace=False)]))
+    check_output(cfg, d, d["hidden"], got, ex, tokens=toks, tag=f"int2 {name}")
+
+
+def test_mixed_residual_bf16():
+    cfg = synth.CONFIGS["c0"].with_(T=64, seed=41, int2_frac=0.5)
+    d = synth.layer(cfg)
+    got, ids, w, offsets, srt = run_layer(cfg, d, flags=moe.MOE_ADD_RESIDUAL)
+    ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag="int2 residual")
+    check_output(cfg, d, d["hidden"], got, ex, residual=True, bf16_out=True, tag="int2 residual bf16")
+
+
+def test_mixed_needs_the_bits_array():
+    import torch
+    cfg = synth.CONFIGS["c0"].with_(T=8, int2_frac=0.5)
+    d = synth.layer(cfg)
+    ly = moe.MoeLayer(cfg, d)
+    ly.weights.expert_bits = None
+    x = torch.zeros((8, cfg.H), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((8, cfg.H), dtype=torch.float32, device="cuda")
+    with pytest.raises(moe.MoeError):
+        ly.forward(x, out, ly.workspace(8, moe.MOE_OUT_F32), moe.MOE_OUT_F32)

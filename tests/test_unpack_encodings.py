@@ -110,3 +110,19 @@ def test_int4_into_int8_code_shifted():
         got = [((r[j // 4] >> (8 * (j % 4))) & 0xFF) for j in range(8)]
         got = [b - 256 if b >= 128 else b for b in got]
         assert got == [16 * q for q in nibbles(w)], hex(w)
+
+
+def test_int2_forms_every_word():
+    """unpack_int2x8: pair i holds elements 2i (low half) and 2i + 1, each
+    2^e + code + 2 with 2^e = 128 (bf16 0x4300) or 1024 (f16 0x6400): the int2
+    encodings are code + 130 in bf16 and code + 1026 in f16, for all 65536
+    eight-code words."""
+    for w in range(1 << 16):
+        t = (w & 0xFFFF) | ((w & 0xFFFF) << 14)
+        codes = [((w >> (2 * j)) & 3) - (4 if (w >> (2 * j)) & 2 else 0) for j in range(8)]
+        for hi, fn, off in ((0x4300, bf16, 130), (0x6400, f16, 1026)):
+            vals = []
+            for i in range(4):
+                r = (((t >> (4 * i)) & 0x00030003) ^ 0x00020002) | (hi | (hi << 16))
+                vals += [fn(r & 0xFFFF), fn(r >> 16)]
+            assert vals == [float(c + off) for c in codes], hex(w)
