@@ -62,6 +62,10 @@ def good(moe, **kw):
     (dict(E=512, top_k=2), -3),
     (dict(shared_bits=0, I_shared=0), 0),
     (dict(E=256, top_k=8, n_group=8, topk_group=4, H=6144, I=2048, rsf=2.5), 0),
+    (dict(flags=0x1000), 0),            # MOE_ACT_Q8
+    (dict(flags=0x2000), 0),            # MOE_EXPERT_MIXED
+    (dict(flags=0x3000), -3),           # both: the Q8 kernels have no int2 form
+    (dict(flags=0x2000 | 4), -3),       # mixed with MOE_EXPERT_INT8
 ])
 def test_validation(moe, kw, code):
     assert moe.moe_validate_shape(good(moe, **kw)) == code
@@ -69,6 +73,12 @@ def test_validation(moe, kw, code):
 
 def test_workspace_sizes(moe):
     s = good(moe)
+    # the int8-activation and mixed-format modes take the tiled layout (the
+    # Q8 one adds code and scale buffers)
+    dec = moe.moe_workspace_bytes(s, moe.MOE_WS_LAYER)
+    q8 = moe.moe_workspace_bytes(good(moe, flags=moe.MOE_ACT_Q8), moe.MOE_WS_LAYER)
+    mixed = moe.moe_workspace_bytes(good(moe, flags=moe.MOE_EXPERT_MIXED), moe.MOE_WS_LAYER)
+    assert q8 > mixed > 0 and dec > 0 and mixed != dec
     assert moe.moe_workspace_bytes(s, moe.MOE_WS_LAYER) > 16 * 2 * 1024 * 4
     assert moe.moe_workspace_bytes(s, moe.MOE_WS_PERMUTE) > 0
     assert moe.moe_workspace_bytes(s, moe.MOE_WS_EXPERT_FFN) >= 32 * 512 * 2
