@@ -392,10 +392,13 @@ struct Ff3 {
     static constexpr int BKB = FF_BK * WBITS / 8;      // B bytes per row per stage
     static constexpr int A_BYTES = BM * FF_BK * 2;     // per stage
     static constexpr int B_BYTES = NMAT * BN * BKB;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int A_LOADS = A_BYTES / 1024;     // wave copies per stage
     static constexpr int B_LOADS = B_BYTES / 1024;
-    static constexpr int LOADS = A_LOADS + B_LOADS;
+    // padding copies (a B copy repeated into a spare 1 KB) so that every wave
+    // issues the same number: int2 down has 8 + 2
+    static constexpr int PAD_LOADS = (4 - (A_LOADS + B_LOADS) % 4) % 4;
+    static constexpr int LOADS = A_LOADS + B_LOADS + PAD_LOADS;
+    static constexpr int STAGE = LOADS * 1024;
     static_assert(LOADS % 4 == 0, "copies split evenly over the four waves");
     static constexpr int PER_WAVE = LOADS / 4;
     // ring stages: three, or two where three would not leave room for two
@@ -449,14 +452,20 @@ __device__ __forceinline__ u32x4 weight_fragment(const uint8_t *bp)
     if constexpr (WBITS == 4) {
         const uint32_t w = *(const uint32_t *)bp;
         return MODE == 1 ? unpack_int4x8_f16(w) : unpack_int4x8_nat(w);
+    } else if constexpr (WBITS == 2) {
+        const uint32_t w = *(const uint16_t *)bp;
+        return MODE == 1 ? unpack_int2x8<0x6400u>(w) : unpack_int2x8<0x4300u>(w);
     } else {
         const u32x2 w = *(const u32x2 *)bp;
         return MODE == 1 ? unpack_int8x8_f16(w) : unpack_int8x8_bf16o(w);
     }
 }
 
+// One (m-tile, n-tile) of expert e in the WBITS format; smem3 / sCor: the
+// kernel's LDS (the stage ring, dynamic, and the row corrections).
 template <int MODE, int WBITS, int BM>
-__global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
+__device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int rows, int n0, uint8_t *smem3,
+                                          float *sCor)
 {
     using C = Ff3<MODE, WBITS, BM>;
     constexpr int NMAT = C::NMAT, BN = C::BN, BKB = C::BKB;
@@ -465,16 +474,6 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
     constexpr int NB = BN / 4 / 16;     // 16-column blocks per wave and matrix
     constexpr int CB = MB / 4;          // offset-correction blocks per wave
     static_assert(MB % 4 == 0, "row blocks split evenly over the waves");
-    extern __shared__ __attribute__((aligned(1024))) uint8_t smem3[];
-    __shared__ float sCor[BM];
-
-    const int NT = a.N / BN;
-    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-    const int nt = q % NT;
-    const int slot = (q / NT) * 8 + xcd;
-    int e, row0, rows;
-    if (!find_tile<BM>(a, slot, e, row0, rows)) return;
-    const int n0 = nt * BN;
     const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(wn);  // the same, known wave-uniform
 
@@ -492,7 +491,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
             const int srow = a.gather ? a.gather[row0 + rr] / a.kdiv : row0 + rr;
             src[j] = (const uint8_t *)a.A + ((size_t)srow * a.lda + chunk * 8) * 2;
         } else {
-            const int lb = l - C::A_LOADS;
+            const int lb = l < C::A_LOADS + C::B_LOADS ? l - C::A_LOADS : 0;  // a padding copy repeats B copy 0
             const int cpr = BKB / 16;                     // 16-byte chunks per B row per stage
             const int br = lb * (64 / cpr) + lane / cpr;  // B row within the stage
             const int mat = br / BN, n = br % BN;
@@ -525,8 +524,9 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
         for (int i = 0; i < MB; ++i)
 #pragma unroll
             for (int j = 0; j < NB; ++j) acc[x][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // minus the unpack offset as a constant operand: bf16 -136 / -128, f16 -1032 / -1152
-    constexpr uint32_t CW = F16 ? (WBITS == 4 ? 0xE408E408u : 0xE480E480u) : (WBITS == 4 ? 0xC308C308u : 0xC300C300u);
+    // minus the unpack offset as a constant operand: bf16 -136 / -130 / -128, f16 -1032 / -1026 / -1152
+    constexpr uint32_t CW = F16 ? (WBITS == 4 ? 0xE408E408u : WBITS == 2 ? 0xE402E402u : 0xE480E480u)
+                                : (WBITS == 4 ? 0xC308C308u : WBITS == 2 ? 0xC302C302u : 0xC300C300u);
     const u32x4 cneg = u32x4{CW, CW, CW, CW};
     auto mma = [](u32x4 x, u32x4 y, f32x4 c) { return F16 ? mfma_f16(x, y, c) : mfma_bf16(x, y, c); };
 
@@ -678,6 +678,52 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
             }
         }
     }
+}
+
+template <int MODE, int WBITS, int BM>
+__global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
+{
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem3[];
+    __shared__ float sCor[BM];
+    const int NT = a.N / Ff3<MODE, WBITS, BM>::BN;
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int nt = q % NT;
+    const int slot = (q / NT) * 8 + xcd;
+    int e, row0, rows;
+    if (!find_tile<BM>(a, slot, e, row0, rows)) return;
+    ffn3_tile<MODE, WBITS, BM>(a, e, row0, rows, nt * Ff3<MODE, WBITS, BM>::BN, smem3, sCor);
+}
+
+// A family whose experts are int4 or int2 each (a.ebits): the tile's expert
+// picks the body; the dynamic LDS holds the larger ring.
+template <int MODE, int BM>
+__global__ __launch_bounds__(256, 2) void k_ffn3_mix(FfnArgs a)
+{
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem3[];
+    __shared__ float sCor[BM];
+    const int NT = a.N / Ff3<MODE, 4, BM>::BN;
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int nt = q % NT;
+    const int slot = (q / NT) * 8 + xcd;
+    int e, row0, rows;
+    if (!find_tile<BM>(a, slot, e, row0, rows)) return;
+    if (a.ebits[e] == 2)
+        ffn3_tile<MODE, 2, BM>(a, e, row0, rows, nt * Ff3<MODE, 2, BM>::BN, smem3, sCor);
+    else
+        ffn3_tile<MODE, 4, BM>(a, e, row0, rows, nt * Ff3<MODE, 4, BM>::BN, smem3, sCor);
+}
+
+template <int MODE, int BM>
+static hipError_t launch_three_mix(const FfnArgs &a, int slots, hipStream_t st)
+{
+    const int NT = a.N / 128;
+    const long grid = (long)((slots + 7) / 8 * 8) * NT;
+    if (grid <= 0) return hipSuccess;
+    using C4 = Ff3<MODE, 4, BM>;
+    using C2 = Ff3<MODE, 2, BM>;
+    const size_t l4 = (size_t)C4::NST * C4::STAGE, l2 = (size_t)C2::NST * C2::STAGE;
+    hipLaunchKernelGGL((k_ffn3_mix<MODE, BM>), dim3((unsigned)grid), dim3(256), l4 > l2 ? l4 : l2, st, a);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ launchers
@@ -986,9 +1032,18 @@ static hipError_t launch_mix(const FfnArgs &a, int slots, hipStream_t st)
 
 // int4/int2 families: the register-staged tiles, 16 or 64 rows by the mean
 // rows per expert, 64 columns.
+int ffn_bm(int mode, int wbits, int rows, int groups, int nt);
+
 template <int MODE>
 static hipError_t launch_mix_mode(const FfnArgs &a, int rows_total, int groups, hipStream_t st)
 {
+    if (a.N % 128 == 0) {
+        // the pipelined tiles where the int4 path would take them
+        const int bm = ffn_bm(MODE, 4, rows_total, groups, a.N / 128);
+        const int slots = (rows_total + bm - 1) / bm + min(groups, rows_total);
+        if (bm == 64) return launch_three_mix<MODE, 64>(a, slots, st);
+        if (MODE == 0 && bm == 128) return launch_three_mix<0, 128>(a, slots, st);
+    }
     const bool big = rows_total >= 24 * groups;
     const int bm = big ? 64 : 16;
     const int slots = (rows_total + bm - 1) / bm + min(groups, rows_total);
