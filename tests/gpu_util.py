@@ -123,3 +123,47 @@ def small_cfg(**kw):
     base = dict(name="small", T=64, H=256, E=16, k=2, I=128, I_sh=256, seed=4242)
     base.update(kw)
     return synth.LayerConfig(**base)
+
+
+def _cut_margin(w0, ids0, p):
+    """Per token: the distance of p to the nearest f32 running mass of the
+    weight ranking (where the kept set would change under a tiny perturbation)."""
+    out = np.empty(w0.shape[0])
+    for t in range(w0.shape[0]):
+        rank = sorted(range(w0.shape[1]), key=lambda j: (-w0[t][j], ids0[t][j]))
+        mass, best = np.float32(0), np.inf
+        for j in rank:
+            mass = np.float32(mass + w0[t][j])
+            best = min(best, abs(float(mass) - p))
+        out[t] = best
+    return out
+
+
+def check_routing_top_p(cfg, d, hidden, ids, w, offsets, srt, tag=""):
+    """check_routing for adaptive expert top-p: the oracle's truncated routing
+    outside near ties and near cut points, dropped slots -1 / weight 0, kept
+    weights summing to 1, the permutation over the kept pairs only."""
+    o_ids0, o_w0, gap, ggap = oracle.router(cfg.with_(top_p=0.0), hidden, d["router_w"], d["router_bias"])
+    o_ids, o_w, _, _ = oracle.router(cfg, hidden, d["router_w"], d["router_bias"])
+    exempt = (gap < GAP_EXEMPT) | (ggap < GAP_EXEMPT) | (_cut_margin(o_w0, o_ids0, cfg.top_p) < GAP_EXEMPT)
+    keep = ~exempt
+    say(f"{tag}: {int((o_ids == -1).sum())} of {o_ids.size} pairs dropped by the oracle, {int(exempt.sum())} exempt tokens")
+    assert (o_ids == -1).any(), "the case drops no pair"
+    bad = np.nonzero(np.any(ids[keep] != o_ids[keep], axis=1))[0]
+    assert bad.size == 0, f"{tag}: ids differ on {bad.size} non-exempt tokens"
+    werr = float(np.max(np.abs(w[keep] - o_w[keep]))) if keep.any() else 0.0
+    assert werr <= W_TOL, f"{tag}: weight error {werr}"
+    # every token: kept ids distinct and in range, dropped slots -1 / weight 0, kept weights sum to 1
+    for t in range(ids.shape[0]):
+        live = ids[t] >= 0
+        assert live.any() and np.all(ids[t][live] < cfg.E) and len(set(ids[t][live])) == live.sum()
+        assert np.all(ids[t][~live] == -1) and np.all(w[t][~live] == 0.0)
+        assert abs(float(w[t][live].sum()) - 1.0) < 1e-5
+    if offsets is not None:
+        flat = ids.reshape(-1).astype(np.int64)
+        live = np.nonzero(flat >= 0)[0]
+        order = live[np.argsort(flat[live], kind="stable")]
+        counts = np.bincount(flat[live], minlength=cfg.E)
+        assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)])), f"{tag}: offsets"
+        assert np.array_equal(srt[:len(live)], order), f"{tag}: sorted pairs"
+    return exempt

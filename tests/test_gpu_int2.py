@@ -10,7 +10,7 @@ import pytest
 
 import int4_routed_expert_02_amd as moe
 import synth
-from gpu_util import check_output, check_routing, run_layer, say, small_cfg
+from gpu_util import check_output, check_routing, check_routing_top_p, run_layer, say, small_cfg
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +31,7 @@ CASES = {
                                          int2_frac=1.0),
     "no_shared_E8": small_cfg(E=8, T=50, shared_bits=0, int2_frac=0.5),
     "c3_shape_T256": synth.CONFIGS["c3"].with_(T=256, seed=24, int2_frac=0.25),
+    "grouped_top_p": synth.CONFIGS["c3"].with_(T=64, H=1024, I=512, I_sh=1024, seed=26, top_p=0.6, int2_frac=0.5),
 }
 
 
@@ -39,7 +40,8 @@ def test_mixed_int2_layer_parity(name):
     cfg = CASES[name]
     d = synth.layer(cfg)
     got, ids, w, offsets, srt = run_layer(cfg, d)
-    ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag=f"int2 {name}")
+    chk = check_routing_top_p if cfg.top_p else check_routing
+    ex = chk(cfg, d, d["hidden"], ids, w, offsets, srt, tag=f"int2 {name}")
     cold = np.isin(ids, np.nonzero(d["expert_bits"] == 2)[0])
     say(f"int2 {name}: {int(cold.sum())} of {ids.size} pairs on int2 experts")
     assert cold.any()

@@ -14,7 +14,7 @@ import pytest
 import int4_routed_expert_02_amd as moe
 import oracle
 import synth
-from gpu_util import check_output, check_routing, run_layer, say, small_cfg
+from gpu_util import check_output, check_routing, check_routing_top_p, run_layer, say, small_cfg
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,7 @@ CASES = {
     "grouped_E64_k8": small_cfg(E=64, k=8, n_group=8, topk_group=4, rsf=2.5, T=40, I=64, I_sh=128, act_q8=True),
     "no_shared_E8": small_cfg(E=8, T=50, shared_bits=0, act_q8=True),
     "c3_shape_T64": synth.CONFIGS["c3"].with_(T=64, seed=24, act_q8=True),
+    "grouped_top_p": synth.CONFIGS["c3"].with_(T=64, H=1024, I=512, I_sh=1024, seed=25, top_p=0.6, act_q8=True),
 }
 
 
@@ -71,7 +72,8 @@ def test_q8_layer_parity(name):
     cfg = CASES[name]
     d = synth.layer(cfg)
     got, ids, w, offsets, srt = run_layer(cfg, d)
-    ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag=f"q8 {name}")
+    chk = check_routing_top_p if cfg.top_p else check_routing
+    ex = chk(cfg, d, d["hidden"], ids, w, offsets, srt, tag=f"q8 {name}")
     toks = None
     if cfg.T * cfg.H > 200 * 1024:
         rng = np.random.default_rng(9)
