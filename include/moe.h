@@ -138,7 +138,7 @@ typedef struct {
     moe_qmat gate, up, down;  /* routed experts, int4 */
     moe_qmat sh_gate, sh_up, sh_down; /* shared expert (E = 1), int4 or int8 per shared_bits */
     /* with MOE_EXPERT_MIXED: device [E] u8, each routed expert's format, 4 (packed int4) or 2
-     * (packed int2, the cold-tail experts of the colibri-nano README, "int2 cold tails"; colibri
+     * (packed int2: the rarely routed experts, which the colibri-nano README's checkpoint tools store in int2; colibri
      * README, "What's implemented": packed int2 with per-row scales).  Int2: element 4c + j of a row
      * in bits 2j..2j+1 of byte c, two's complement, rows of cols/4 bytes, one f32 scale per row; an
      * int2 expert's gate, up and down start where an int4 expert's would (same strides), so its

@@ -87,9 +87,10 @@ typedef struct {
     oracle_qmat down;          /* int4 [E][H][I/2], scales [E][H] */
     oracle_qmat sh_gate, sh_up, sh_down; /* shared expert, E = 1, int4 or int8 */
     /* [E] per routed expert: 4 (packed int4) or 2 (packed int2, the cold-tail
-     * experts: colibri-nano README, "the checkpoint surgery tooling ... int2
-     * cold tails"; colibri README, "What's implemented": packed int2 with
-     * per-row scales, dequant-on-use).  Reading: element 4c + j of a row in
+     * experts: the colibri-nano README lists, among the checkpoint tools it
+     * leaves out, one that stores the rarely routed experts in int2; the
+     * colibri README, "What's implemented", has packed int2 with per-row
+     * scales, dequantised on use).  Reading: element 4c + j of a row in
      * bits 2j..2j+1 of byte c, two's complement (-2..1), one f32 scale per
      * row, the row cols/4 bytes; an int2 expert's matrices sit where an int4
      * expert's would (same expert stride, the first half of each).  NULL: all
