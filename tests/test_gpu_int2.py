@@ -70,3 +70,33 @@ def test_mixed_needs_the_bits_array():
     out = torch.empty((8, cfg.H), dtype=torch.float32, device="cuda")
     with pytest.raises(moe.MoeError):
         ly.forward(x, out, ly.workspace(8, moe.MOE_OUT_F32), moe.MOE_OUT_F32)
+
+
+@pytest.mark.parametrize("T", [40, 1000])
+def test_split_expert_ffn_mixed(T):
+    """moe_expert_ffn with MOE_EXPERT_MIXED (16-row and pipelined tiles) on
+    the oracle's own routing and permutation, against oracle_expert_ffn: every
+    sorted row of every expert, int4 and int2 alike."""
+    import torch
+    import oracle
+    cfg = synth.CONFIGS["c0"].with_(T=T, seed=81 + T, int2_frac=0.5)
+    d = synth.layer(cfg)
+    ly = moe.MoeLayer(cfg, d)
+    o_ids, o_w, _, _ = oracle.router(cfg, d["hidden"], d["router_w"], d["router_bias"])
+    _, offsets, srt, _ = oracle.permute(cfg, o_ids)
+    pscale = (o_w.reshape(-1) * np.float32(cfg.rsf)).astype(np.float32)
+    ref = oracle.expert_ffn(cfg, d["hidden"], oracle.LayerWeights(cfg, d), offsets, srt, pscale)
+    sh = moe.shape_of(cfg)
+    dv = dict(device="cuda")
+    x = torch.from_numpy(d["hidden"].view(np.int16)).cuda().view(torch.bfloat16)
+    y = torch.empty((T * cfg.k, cfg.H), dtype=torch.float32, **dv)
+    ws = torch.empty(moe.moe_workspace_bytes(sh, moe.MOE_WS_EXPERT_FFN), dtype=torch.uint8, **dv)
+    moe.moe_expert_ffn(sh, x, ly.weights, torch.from_numpy(offsets).cuda(), torch.from_numpy(srt).cuda(),
+                       torch.from_numpy(pscale).cuda(), y, ws)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    rows = int(offsets[-1])
+    rms = float(np.sqrt(np.mean(ref[:rows].astype(np.float64) ** 2)))
+    err = float(np.abs(got[:rows] - ref[:rows]).max()) / rms
+    say(f"split mixed T={T}: max|gpu-oracle|/rms = {err:.3e} over {rows} rows")
+    assert err <= 1e-2
