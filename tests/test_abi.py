@@ -219,3 +219,22 @@ def test_chain_validation(moe, case, code):
                                             ctypes.byref(ns), ctypes.byref(nxt) if nxt is not None else None, nws,
                                             nnbytes, None)
     assert st == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(rows=-1), -2),
+    (dict(cols=0), -2),
+    (dict(cols=48), -2),          # not whole 32-blocks
+    (dict(fmt=2), -2),
+    (dict(rows=0), 0),
+    (dict(src=None), -1),
+    (dict(q=None), -1),
+    (dict(d=None), -1),
+    (dict(src=FAKE + 4), -5),     # the block loads are 16-byte vectors
+    (dict(q=FAKE + 8), -5),
+    (dict(d=FAKE + 2), -5),
+])
+def test_quantize_act_q8_validation(moe, args, code):
+    a = dict(src=FAKE, fmt=1, rows=4, cols=64, q=FAKE, d=FAKE)
+    a.update(args)
+    assert moe.load().moe_quantize_act_q8(a["src"], a["fmt"], a["rows"], a["cols"], a["q"], a["d"], None) == code
