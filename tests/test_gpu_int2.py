@@ -23,6 +23,7 @@ def _gpu():
 
 
 CASES = {
+    "T1_all_int2": synth.CONFIGS["c0"].with_(T=1, seed=12, int2_frac=1.0),
     "c0_T16_quarter": synth.CONFIGS["c0"].with_(T=16, int2_frac=0.25),
     "c0_T100_ragged_half": synth.CONFIGS["c0"].with_(T=100, seed=11, int2_frac=0.5),
     "c2_shape_T700_quarter": synth.CONFIGS["c2"].with_(T=700, seed=21, int2_frac=0.25),

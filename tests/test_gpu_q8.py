@@ -56,6 +56,7 @@ def test_quantize_act_q8_bit_exact(name):
 
 
 CASES = {
+    "T1": synth.CONFIGS["c0"].with_(T=1, seed=12, act_q8=True),
     "c0_T16": synth.CONFIGS["c0"].with_(T=16, act_q8=True),
     "c0_T100_ragged": synth.CONFIGS["c0"].with_(T=100, seed=11, act_q8=True),
     "c2_shape_T700": synth.CONFIGS["c2"].with_(T=700, seed=21, act_q8=True),
@@ -103,3 +104,17 @@ def test_q8_full_size_c3_sampled():
     rng = np.random.default_rng(7)
     toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 24, replace=False)]))
     check_output(cfg, d, d["hidden"], got, ex, tokens=toks, tag="q8 c3 full size")
+
+
+def test_q8_empty_batch_is_a_no_op():
+    """T = 0 in the Q8 mode: the call succeeds and writes nothing."""
+    import torch
+    cfg = synth.CONFIGS["c0"].with_(T=4, act_q8=True)
+    d = synth.layer(cfg)
+    ly = moe.MoeLayer(cfg, d)
+    x = torch.zeros((0, cfg.H), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((1, cfg.H), 7.0, dtype=torch.float32, device="cuda")
+    ws = ly.workspace(4, moe.MOE_OUT_F32)
+    moe.moe_layer_forward(moe.shape_of(cfg, 0, moe.MOE_OUT_F32), ly.weights, x, out, ws)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
