@@ -34,10 +34,16 @@ SideStream *side_stream(hipStream_t caller)
         // not created under graph capture: the caller's stream then runs everything
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-        if (hipStreamCreateWithFlags(&s.st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        if (hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess)
+        // all three or none: a partial set is released and the next call tries again
+        SideStream n;
+        if (hipStreamCreateWithFlags(&n.st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+            if (n.fork) (void)hipEventDestroy(n.fork);
+            (void)hipStreamDestroy(n.st);
             return nullptr;
+        }
+        s = n;
     }
     return &s;
 }
