@@ -584,47 +584,59 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     }
 
     // the shared expert (no dependence on the routing) on the side stream,
-    // except in the profiled call, whose events time the routed gate/up alone
+    // except in the profiled call, whose events time the routed gate/up alone.
+    // Once forked, the side stream is joined back on every path, errors too,
+    // so a failing call leaves no open fork (nor a broken graph capture).
     SideStream *side = nullptr;
     std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
     if (s->shared_bits && !ev_start && !ev_stop) {
         side_lock.lock();
         side = side_stream(hs);
+        if (!side) side_lock.unlock();
+    }
+    auto routed = [&]() -> int {
         if (side) {
-            if (hipEventRecord(side->fork, hs) != hipSuccess || hipStreamWaitEvent(side->st, side->fork, 0) != hipSuccess)
-                return MOE_ERR_HIP;
-            st = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr,
-                         1, 1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<float>(ws, L.shy), side->st);
-            if (st) return st;
-        } else {
-            side_lock.unlock();
+            int r = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr,
+                            nullptr, 1, 1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<float>(ws, L.shy), side->st);
+            if (r) return r;
         }
-    }
-    hipError_t e = moe::launch_router(hidden, w->router_w, w->router_bias, s->T, s->H, s->E, s->top_k, s->n_group,
-                                      s->topk_group, s->routed_scaling_factor, s->top_p, at<float>(ws, L.zpart), KS, ids,
-                                      at<float>(ws, L.w), at<float>(ws, L.gap), pscale, sbc, hs);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    e = moe::launch_scatter(ids, sbc, nsb, P, s->E, sbt * s->top_k, counts, offsets, sorted, inv, hs);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    if (ev_start && hipEventRecord((hipEvent_t)ev_start, hs) != hipSuccess) return MOE_ERR_HIP;
-    st = run_ffn(s, 4, hidden, w->gate, w->up, w->down, s->I, offsets, sorted, s->E, s->top_k, P, pscale,
-                 at<uint16_t>(ws, L.hbuf), ypair, hs, ev_stop != nullptr, ebits);
-    if (st) return st;
-    if (ev_stop) {
-        // profiled: the routed gate/up kernel ran alone between the events; now the down GEMM
-        if (hipEventRecord((hipEvent_t)ev_stop, hs) != hipSuccess) return MOE_ERR_HIP;
-        st = run_ffn_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, at<uint16_t>(ws, L.hbuf), ypair, hs,
-                          ebits);
-        if (st) return st;
-    }
+        hipError_t e = moe::launch_router(hidden, w->router_w, w->router_bias, s->T, s->H, s->E, s->top_k,
+                                          s->n_group, s->topk_group, s->routed_scaling_factor, s->top_p,
+                                          at<float>(ws, L.zpart), KS, ids, at<float>(ws, L.w), at<float>(ws, L.gap),
+                                          pscale, sbc, hs);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = moe::launch_scatter(ids, sbc, nsb, P, s->E, sbt * s->top_k, counts, offsets, sorted, inv, hs);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        if (ev_start && hipEventRecord((hipEvent_t)ev_start, hs) != hipSuccess) return MOE_ERR_HIP;
+        int r = run_ffn(s, 4, hidden, w->gate, w->up, w->down, s->I, offsets, sorted, s->E, s->top_k, P, pscale,
+                        at<uint16_t>(ws, L.hbuf), ypair, hs, ev_stop != nullptr, ebits);
+        if (r) return r;
+        if (ev_stop) {
+            // profiled: the routed gate/up kernel ran alone between the events; now the down GEMM
+            if (hipEventRecord((hipEvent_t)ev_stop, hs) != hipSuccess) return MOE_ERR_HIP;
+            r = run_ffn_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, at<uint16_t>(ws, L.hbuf),
+                             ypair, hs, ebits);
+            if (r) return r;
+        }
+        return MOE_OK;
+    };
     if (side) {
-        if (hipEventRecord(side->join, side->st) != hipSuccess || hipStreamWaitEvent(hs, side->join, 0) != hipSuccess)
-            return MOE_ERR_HIP;
+        if (hipEventRecord(side->fork, hs) != hipSuccess || hipStreamWaitEvent(side->st, side->fork, 0) != hipSuccess)
+            return MOE_ERR_HIP;  // nothing forked yet
+        st = routed();
+        const bool joined =
+            hipEventRecord(side->join, side->st) == hipSuccess && hipStreamWaitEvent(hs, side->join, 0) == hipSuccess;
         side_lock.unlock();
-    } else if (s->shared_bits) {
-        st = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr, 1,
-                     1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<float>(ws, L.shy), hs);
         if (st) return st;
+        if (!joined) return MOE_ERR_HIP;
+    } else {
+        st = routed();
+        if (st) return st;
+        if (s->shared_bits) {
+            st = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr,
+                         1, 1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<float>(ws, L.shy), hs);
+            if (st) return st;
+        }
     }
     const float *shy = s->shared_bits ? at<float>(ws, L.shy) : nullptr;
     return hip_status(moe::launch_combine(ypair, inv, nullptr, 1.f, shy,
