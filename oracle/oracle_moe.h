@@ -22,8 +22,13 @@
  *     README, "Converting a checkpoint yourself");
  *   - a shared expert applied to every token (NanoColibri README, model
  *     table: top-2 of 64 plus a 2048-wide shared expert).
+ * Modes beside it: adaptive expert top-p (oracle_shape.top_p), Q8_0-style
+ * int8 activations with integer block sums (ORACLE_ACT_Q8: the integer-dot
+ * kernels of the same README), and int2 cold-tail experts
+ * (oracle_weights.expert_bits).
  * The readings taken where the pages are silent (activation, tie order,
- * group score, normalisation, nibble order) are stated at each function.
+ * group score, normalisation, nibble order, top-p rule, activation blocks,
+ * int2 layout) are stated at each function or field.
  *
  * Precision: x is widened from bf16 exactly; weights are dequantised as the
  * f32 product q * qs; every dot product is accumulated in double and rounded
