@@ -101,3 +101,16 @@ def test_split_expert_ffn_mixed(T):
     err = float(np.abs(got[:rows] - ref[:rows]).max()) / rms
     say(f"split mixed T={T}: max|gpu-oracle|/rms = {err:.3e} over {rows} rows")
     assert err <= 1e-2
+
+
+def test_int2_full_size_c3_sampled():
+    """The GLM-class 2048-token layer with a quarter of its experts in int2,
+    in the launch configuration bench.py --int2-frac times: routing on every
+    token, outputs on a seeded sample the oracle computes one by one."""
+    cfg = synth.CONFIGS["c3"].with_(int2_frac=0.25)
+    d = synth.layer(cfg)
+    got, ids, w, offsets, srt = run_layer(cfg, d)
+    ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag="int2 c3")
+    rng = np.random.default_rng(7)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 24, replace=False)]))
+    check_output(cfg, d, d["hidden"], got, ex, tokens=toks, tag="int2 c3 full size")
