@@ -1,21 +1,30 @@
 #!/usr/bin/env python3
-"""Benchmark: MoE-layer decode step on one MI355X.
+"""Benchmark: MoE-layer tokens/s on one MI355X, with the roofline of each
+workload's dominant kernel and the CPU oracle beside it.
 
-Workload: a decode step through 23 stacked Nano-shape MoE layers (hidden 1024,
-64 routed SwiGLU experts of intermediate 512 in packed int4 with per-row f32
-scales, top-2 sigmoid+bias routing, a 2048-wide int4 shared expert), T = 32
-tokens, bf16 hidden state, the residual added in each layer's combine.  Every
-layer has its own seeded weights (828 MB of layer weights per step in total,
-more than the 256 MB last-level cache, so each step streams them from HBM).
-One step = one HIP-graph replay of the 23 moe_layer_forward calls.
+The line's headline (`value`, `config`, `roofline`, `cpu_baseline`) is the
+largest workload: one GLM-class MoE layer (hidden 6144, 256 routed SwiGLU
+experts of intermediate 2048 in packed int4 with per-row f32 scales, top-8
+sigmoid+bias routing with 8 groups / 4 kept, routed scaling 2.5, a 2048-wide
+int4 shared expert), T = 2048 tokens, bf16 in and out.  One step = one
+HIP-graph replay of moe_layer_forward.  Its dominant kernel, the routed
+gate/up grouped GEMM, is HBM-bound (its weight stream), so its roofline is
+against the 8 TB/s HBM peak, with its matrix-core fraction beside it.
 
-Prints one JSON line: tokens/s for the step, plus
-  roofline:     the fused expert kernel (the step's weight stream: every chosen
-                routed expert and the shared expert) against HBM peak; its
-                average duration comes from HIP events on its stream around
-                back-to-back replays of the 23 layers' expert stages;
-  cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+The other workloads ride along under their own keys, each with its own
+roofline and CPU baseline:
+  c1  a decode step through 23 stacked Nano-shape layers, T = 32 (HIP graph of
+      23 chained moe_layer_forward_chain calls); expert kernel against HBM;
+  c2  a Nano-shape prefill layer, T = 4096 (8 hot experts); gate/up GEMM
+      against the bf16 matrix-core peak;
+  c4  a Nano-shape layer, T = 16384 (Zipf experts, int8 shared expert); same;
+  c0  one Nano-shape layer, T = 16: cold (24 copies of the layer's weights
+      rotated so that no weight is in the 256 MB last-level cache when it is
+      read) and warm (one copy, repeated).
+The CPU oracle is timed on each on a bounded sample, on all host threads, and
+on one thread for c0-c2.
 
+--config cN prints only that workload's line (its fields at the top level).
 --copy-calibration MIB runs only a plain device-to-device copy of that size
 (the reference kernel for scaling hardware byte counters) and exits.
 """
@@ -33,22 +42,34 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 matrix-core peak
 
 
-def sh_of(moe, cfg, T, flags):
-    return moe.shape_of(cfg, T, flags)
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def measured_traffic(root):
-    """HBM bytes per expert-kernel launch from the committed rocprofv3 counter
-    summary, or None when the kernel source changed since it was taken."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def measured_traffic(name, sources):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 counter
+    summary (profiles/<name>.json), or None when any of its kernel sources
+    changed since the counters were taken."""
     import hashlib
-    path = os.path.join(root, "profiles", "k_dec_expert_c1_traffic.json")
-    src = os.path.join(root, "int4_routed_expert_02_amd", "csrc", "decode.hip")
+    path = os.path.join(ROOT, "profiles", name + ".json")
     try:
         rec = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    except (OSError, ValueError):
-        return None
-    if rec.get("decode_hip_sha256") != digest:
+        for src in sources:
+            digest = hashlib.sha256(open(os.path.join(ROOT, "int4_routed_expert_02_amd", "csrc", src),
+                                         "rb").read()).hexdigest()
+            if rec.get("sources", {}).get(src) != digest:
+                return None
+    except (OSError, ValueError, AttributeError):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -56,9 +77,11 @@ def measured_traffic(root):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c1", help="workload key (c1 = the decode step this line reports)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=None,
+                    help="only this workload's line (c0..c4); default: c3 headline with c1, c2, c4, c0 beside it")
+    ap.add_argument("--no-extras", action="store_true", help="the c3 headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="adaptive expert top-p of the workload's router (0 = off, the workloads' own setting)")
@@ -66,8 +89,11 @@ def parse():
                     help="Q8_0-style int8 activations for the expert matmuls (tiled configurations)")
     ap.add_argument("--int2-frac", type=float, default=0.0,
                     help="fraction of routed experts stored as packed int2 (cold-tail experts; tiled configurations)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the headline's CPU-oracle sample")
+    ap.add_argument("--cpu-seconds-extra", type=float, default=4.0,
+                    help="budget of each other CPU-oracle sample (the extras and the one-thread runs)")
     ap.add_argument("--roofline-reps", type=int, default=20)
+    ap.add_argument("--cold-copies", type=int, default=24, help="rotated weight copies of the cold c0 layer")
     ap.add_argument("--quantize", action="store_true",
                     help="time the per-row int4 quantiser on the GLM-class routed gate/up weights instead")
     ap.add_argument("--bias-update", action="store_true",
@@ -109,40 +135,90 @@ def main():
         return bench_quantize(args, moe, torch, np)
     if args.bias_update:
         return bench_bias_update(args, moe, torch, np)
-    cfg = synth.CONFIGS[args.config]
-    if args.top_p:
-        cfg = cfg.with_(top_p=args.top_p)
-    if args.act_q8:
-        if cfg.T <= 32:
-            sys.exit("--act-q8 is a mode of the tiled configurations (c2, c3, c4)")
-        cfg = cfg.with_(act_q8=True)
-    if args.int2_frac:
-        if cfg.T <= 32:
-            sys.exit("--int2-frac is a mode of the tiled configurations (c2, c3, c4)")
-        cfg = cfg.with_(int2_frac=args.int2_frac)
-    if cfg.T > 32:
-        return bench_prefill(args, cfg, moe, synth, torch, np, dev)
+
+    def variant(cfg):
+        if args.top_p:
+            cfg = cfg.with_(top_p=args.top_p)
+        if args.act_q8:
+            if cfg.T <= 32:
+                sys.exit("--act-q8 is a mode of the tiled configurations (c2, c3, c4)")
+            cfg = cfg.with_(act_q8=True)
+        if args.int2_frac:
+            if cfg.T <= 32:
+                sys.exit("--int2-frac is a mode of the tiled configurations (c2, c3, c4)")
+            cfg = cfg.with_(int2_frac=args.int2_frac)
+        return cfg
+
+    def run(name, cpu_s, one_thread):
+        cfg = variant(synth.CONFIGS[name])
+        progress(f"{name}: {cfg.name}")
+        if name == "c0":
+            return bench_c0(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread)
+        if cfg.T > 32:
+            return bench_prefill(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread)
+        return bench_decode(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread)
+
+    if args.config:
+        line = run(args.config, args.cpu_seconds, args.config in ("c0", "c1", "c2"))
+        print(json.dumps(line), flush=True)
+        return
+    line = run("c3", args.cpu_seconds, False)
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        extras = {}
+        for name in ("c1", "c2", "c4", "c0"):
+            r = run(name, args.cpu_seconds_extra, name in ("c0", "c1", "c2"))
+            for key in ("n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline", "data"):
+                r.pop(key, None)
+            extras[name] = r
+            torch.cuda.empty_cache()
+        line["other_workloads"] = extras
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(oracle, work, cpu_s, unit_name, sample_fmt, threads=None):
+    """Time work(n) -> units done (growing n) until cpu_s seconds are spent;
+    returns the cpu_baseline object (units per second)."""
+    prev = oracle.num_threads()
+    if threads:
+        oracle.set_num_threads(threads)
+    try:
+        used = oracle.num_threads()
+        done, spent, n = 0, 0.0, 1
+        while spent < cpu_s:
+            t0 = time.perf_counter()
+            got = work(n)
+            spent += time.perf_counter() - t0
+            if got is None:
+                break
+            done += got
+            # grow the sample so that the next call fits in what is left of the budget
+            rate = done / spent
+            n = max(1, min(2 * n, int((cpu_s - spent) * rate / max(got / n, 1e-9)) or 1))
+    finally:
+        oracle.set_num_threads(prev)
+    return {"value": round(done / spent, 3), "unit": unit_name, "cores": used, "kind": "oracle",
+            "cpu_model": cpu_model(), "sample": sample_fmt(done, spent)}
+
+
+def bench_decode(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread):
+    """The decode step: 23 stacked Nano-shape layers, T = 32, each layer's
+    combine taking the next layer's router logits (HIP graph per step)."""
     L, T, H = cfg.layers, cfg.T, cfg.H
     flags = moe.MOE_ADD_RESIDUAL  # bf16 out, residual added: the layer output is the next layer's input
 
-    # ---- inputs resident in HBM before timing
-    t0 = time.time()
     layers, arrays = [], []
     for l in range(L):
         d = synth.layer(cfg, l, with_hidden=False)
         layers.append(moe.MoeLayer(cfg, d, dev))
         arrays.append(d)
     x0_np = synth.hidden(cfg, 0)
-    gen_s = time.time() - t0
     xs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(L + 1)]
     xs[0].copy_(torch.from_numpy(x0_np.view(np.int16)).view(torch.bfloat16))
     wss = [layers[l].workspace(T, flags) for l in range(L)]
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
-    # the chained step: each layer's combine also takes the next layer's router
-    # logits of the output row just written, so layers 2..L run no logits
-    # kernel (MOE_LOGITS_GIVEN)
     def lflags(l):
         return flags | (moe.MOE_LOGITS_GIVEN if l else 0)
 
@@ -152,7 +228,6 @@ def main():
             layers[l].forward_chain(xs[l], xs[l + 1], wss[l], lflags(l), nxt, wss[l + 1] if nxt is not None else None,
                                     stream=s)
 
-    # eager once (validates arguments), then capture the step in a HIP graph
     with torch.cuda.stream(stream):
         step(stream)
     torch.cuda.synchronize()
@@ -160,7 +235,6 @@ def main():
     with torch.cuda.graph(graph, stream=stream):
         step(stream)
     torch.cuda.synchronize()
-
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -172,26 +246,20 @@ def main():
             graph.replay()
         ev1.record(stream)
     torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    t_wall0 = time.time()
-    ms_per_step = ms_total / args.steps
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
     tok_s = T / (ms_per_step / 1e3)
 
-    # ---- roofline of the dominant kernel: the fused expert kernel (gate/up +
-    # SwiGLU + down of every chosen routed expert and of the shared expert, one
-    # launch per layer, each taking its routing decision from the router
-    # logits in its workspace).  Its duration is measured with
-    # HIP events on the kernel's own stream around a HIP graph of the 23
-    # layers' expert stages alone (MOE_STAGE_EXPERTS_ONLY: the same launches as
-    # in the step above, reading the routing the step left in each workspace),
-    # replayed back to back: average = elapsed / launches.
+    # the dominant kernel: the fused expert kernel, timed by HIP events on its
+    # own stream around a graph of the 23 layers' expert stages alone
+    # (MOE_STAGE_EXPERTS_ONLY: the same launches, reading the routing the step
+    # left in each workspace), replayed back to back
     P = T * cfg.k
 
     def eflags(l):
         return lflags(l) | moe.MOE_STAGE_EXPERTS_ONLY
 
     with torch.cuda.stream(stream):
-        step(stream)  # leave each layer's routing in its workspace
+        step(stream)
         for l in range(L):
             layers[l].forward(xs[l], xs[l + 1], wss[l], eflags(l), stream=stream)
     torch.cuda.synchronize()
@@ -215,24 +283,24 @@ def main():
 
     n_act, p_kept = [], []
     for l in range(L):
-        pid, _, _, _ = moe.moe_layer_routing(sh_of(moe, cfg, T, flags), wss[l])
+        pid, _, _, _ = moe.moe_layer_routing(moe.shape_of(cfg, T, flags), wss[l])
         base = wss[l].data_ptr()
         ids = wss[l][pid - base:pid - base + 4 * P].view(torch.int32).cpu().numpy()
         n_act.append(int(np.unique(ids[ids >= 0]).size))  # (-1: a pair dropped by adaptive top-p)
         p_kept.append(int((ids >= 0).sum()))
     # algorithmic bytes of one expert-kernel launch: the weights (int4 rows and
     # f32 row scales) of every chosen routed expert and of the shared expert,
-    # the activations and routing logits read once, one f32 output row per
-    # (token, expert) pair and per token for the shared expert
+    # the activations and router logits read once, the layer output written
+    # once (bf16)
     sh_w = (3 * cfg.I_sh * H * cfg.shared_bits // 8 + 4 * (2 * cfg.I_sh + H)) if cfg.shared_bits else 0
-    ex_bytes = [na * (3 * cfg.I * H // 2 + 4 * (2 * cfg.I + H)) + sh_w + 2 * T * H + 4 * T * cfg.E
-                + 4 * pk * H + (4 * T * H if cfg.shared_bits else 0) for na, pk in zip(n_act, p_kept)]
+    ex_bytes = [na * (3 * cfg.I * H // 2 + 4 * (2 * cfg.I + H)) + sh_w + 2 * T * H + 4 * T * cfg.E + 2 * T * H
+                for na in n_act]
     alg_per_launch = float(np.mean(ex_bytes))
     achieved = alg_per_launch / (avg_ms / 1e3) / 1e9  # GB/s
-    traffic = measured_traffic(ROOT)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_dec_expert<4,1> (routing + fused gate/up/SwiGLU/down of the chosen and shared experts)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("k_dec_expert_c1_traffic", ["decode.hip"]),
+                "kernel": "k_dec_expert (fused gate/up/SwiGLU/down of the chosen and shared experts)",
                 "avg_launch_us": round(avg_ms * 1e3, 2), "alg_bytes_per_launch": int(alg_per_launch),
                 "launches_timed": args.roofline_reps * L, "active_experts_mean": round(float(np.mean(n_act)), 2)}
 
@@ -244,24 +312,26 @@ def main():
             step_bytes += 3 * cfg.I_sh * H * cfg.shared_bits // 8 + 4 * (2 * cfg.I_sh + H)
         step_bytes += 4 * cfg.E * H + 4 * cfg.E + 2 * T * H * 2 + 8 * T * cfg.k
 
-    # ---- CPU baseline: the oracle on a bounded sample of the same workload
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         import oracle
         lws = [oracle.LayerWeights(cfg, arrays[l]) for l in range(L)]
-        x = x0_np
-        n_layers_done, t_cpu0 = 0, time.time()
-        while time.time() - t_cpu0 < args.cpu_seconds or n_layers_done < L:
-            l = n_layers_done % L
-            out = oracle.layer_forward(cfg, lws[l], x, residual=True)[0]
-            x = torch.from_numpy(out).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-            n_layers_done += 1
-        cpu_s = time.time() - t_cpu0
-        steps_done = n_layers_done / L
-        cpu = {"value": round(T * steps_done / cpu_s, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
-               "kind": "oracle",
-               "sample": f"{n_layers_done} layer passes ({steps_done:.2f} decode steps of 23 layers, T={T}) "
-                         f"in {cpu_s:.1f} s, f64-accumulating C oracle, OpenMP over tokens/rows"}
+        state = {"x": x0_np, "l": 0}
+
+        def work(n):
+            for _ in range(n):
+                l = state["l"] % L
+                out = oracle.layer_forward(cfg, lws[l], state["x"], residual=True)[0]
+                state["x"] = torch.from_numpy(out).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                state["l"] += 1
+            return n * T / L  # decode-step tokens: T per 23 layer passes
+
+        fmt = (lambda done, spent: f"{done * L / T:.0f} layer passes ({done / T:.2f} decode steps of {L} layers, "
+                                   f"T={T}) in {spent:.1f} s, f64-accumulating C oracle, OpenMP over tokens/rows")
+        cpu = cpu_baseline(oracle, work, cpu_s, "tokens/s", fmt)
+        if one_thread:
+            state.update(x=x0_np, l=0)
+            cpu1 = cpu_baseline(oracle, work, cpu_s, "tokens/s", fmt, threads=1)
 
     line = {
         "metric": "MoE-layer tokens/s (decode step, 23 stacked int4 MoE layers)",
@@ -285,7 +355,93 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    if cpu1 is not None:
+        line["cpu_baseline_1thread"] = cpu1
+    return line
+
+
+def bench_c0(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread):
+    """One Nano-shape layer, T = 16 (the small-batch regime): cold, with the
+    weights of `cold_copies` identical layer copies rotated so that each call
+    reads weights no recent call has touched (24 x 54 MB > the 256 MB
+    last-level cache), and warm, one copy repeated.  Each is a HIP graph of
+    `cold_copies` moe_layer_forward calls; the time per layer is the graph's
+    time divided by the calls."""
+    T, H, n = cfg.T, cfg.H, args.cold_copies
+    d = synth.layer(cfg)
+    copies = [moe.MoeLayer(cfg, d, dev) for _ in range(n)]
+    x = torch.from_numpy(d["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
+    flags = 0
+    outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    wss = [c.workspace(T, flags) for c in copies]
+    stream = torch.cuda.Stream(device=dev)
+
+    def timed(order):
+        with torch.cuda.stream(stream):
+            for i, c in enumerate(order):
+                copies[c].forward(x, outs[i], wss[i], flags, stream=stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i, c in enumerate(order):
+                copies[c].forward(x, outs[i], wss[i], flags, stream=stream)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (args.steps * n)
+
+    ms_cold = timed(list(range(n)))
+    ms_warm = timed([0] * n)
+    # algorithmic bytes of the layer: chosen routed experts, shared expert,
+    # router, x in, out, ids and weights
+    sh = moe.shape_of(cfg, T, flags)
+    pid, _, _, _ = moe.moe_layer_routing(sh, wss[0])
+    ids = wss[0][pid - wss[0].data_ptr():pid - wss[0].data_ptr() + 4 * T * cfg.k].view(torch.int32).cpu().numpy()
+    n_act = int(np.unique(ids).size)
+    alg = (n_act * (3 * cfg.I * H // 2 + 4 * (2 * cfg.I + H)) + 3 * cfg.I_sh * H // 2 + 4 * (2 * cfg.I_sh + H)
+           + 4 * cfg.E * H + 4 * cfg.E + 2 * T * H * 2 + 8 * T * cfg.k)
+    gbs_cold = alg / (ms_cold / 1e3) / 1e9
+    gbs_warm = alg / (ms_warm / 1e3) / 1e9
+    cpu = cpu1 = None
+    if not args.no_cpu_baseline:
+        import oracle
+        lw = oracle.LayerWeights(cfg, d)
+
+        def work(k):
+            for _ in range(k):
+                oracle.layer_forward(cfg, lw, d["hidden"])
+            return k * T
+
+        fmt = lambda done, spent: f"{done // T} passes of the T={T} layer in {spent:.1f} s, C oracle"
+        cpu = cpu_baseline(oracle, work, cpu_s, "tokens/s", fmt)
+        if one_thread:
+            cpu1 = cpu_baseline(oracle, work, cpu_s, "tokens/s", fmt, threads=1)
+    line = {
+        "metric": "MoE-layer tokens/s (one Nano-shape layer, T=16, weights cold in HBM)",
+        "value": round(T / (ms_cold / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms_cold, 5),
+        "config": {"workload": cfg.name, "T": T, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
+                   "I_shared": cfg.I_sh, "rotated_weight_copies": n},
+        "warm": {"value": round(T / (ms_warm / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms_warm, 5),
+                 "hbm_GBs": round(gbs_warm, 1),
+                 "note": "one weight copy repeated: the weights stay in the last-level cache"},
+        "layer_alg_bytes": int(alg), "active_experts": n_act,
+        "roofline": {"bound": "hbm", "achieved": round(gbs_cold, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs_cold / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "the whole layer (logits, fused expert kernel, combine), cold weights",
+                     "avg_launch_us": round(ms_cold * 1e3, 2), "alg_bytes_per_launch": int(alg)},
+        "cpu_baseline": cpu,
+    }
+    if cpu1 is not None:
+        line["cpu_baseline_1thread"] = cpu1
+    return line
 
 
 def bench_quantize(args, moe, torch, np):
@@ -384,13 +540,17 @@ def bench_bias_update(args, moe, torch, np):
     print(json.dumps(line), flush=True)
 
 
-def bench_prefill(args, cfg, moe, synth, torch, np, dev):
+def bench_prefill(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread):
     """One large-batch layer (the tiled grouped-GEMM regime): tokens/s of one
-    moe_layer_forward (bf16 out), and the routed gate/up grouped GEMM against
-    the bf16 matrix-core peak."""
-    T, H, P = cfg.T, cfg.H, cfg.T * cfg.k
+    moe_layer_forward (bf16 out), the layer against both roofs, and the
+    routed gate/up grouped GEMM (the dominant kernel) against its binding
+    roof: HBM when its algorithmic bytes take longer at 8 TB/s than its flops
+    at the matrix-core peak (the GLM-class layer), else the matrix cores."""
+    T, H = cfg.T, cfg.H
+    t0 = time.time()
     d = synth.layer(cfg)
     layer = moe.MoeLayer(cfg, d, dev)
+    progress(f"{cfg.name.split(':')[0]}: inputs generated and uploaded in {time.time() - t0:.1f} s")
     x = torch.from_numpy(d["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     flags = 0
@@ -435,37 +595,69 @@ def bench_prefill(args, cfg, moe, synth, torch, np, dev):
     avg_ms = float(np.mean(kms))
     # the routed rows the pass computed (fewer than T*k when adaptive top-p drops pairs)
     _, _, poff, _ = moe.moe_layer_routing(sh, ws)
-    P = int(ws[poff - ws.data_ptr() + 4 * cfg.E:poff - ws.data_ptr() + 4 * cfg.E + 4].view(torch.int32).item())
-    gu_flops = 4.0 * P * cfg.I * H
-    achieved = gu_flops / (avg_ms / 1e3) / 1e12
-    layer_flops = 6.0 * P * H * cfg.I + (6.0 * T * H * cfg.I_sh if cfg.shared_bits else 0.0)
+    off = ws[poff - ws.data_ptr():poff - ws.data_ptr() + 4 * (cfg.E + 1)].view(torch.int32).cpu().numpy()
+    P = int(off[-1])
+    counts = np.diff(off)
+    touched = int(np.count_nonzero(counts))
     q8 = bool(cfg.act_q8)
+    ebits = d.get("expert_bits")
+    wb = (lambda e: int(ebits[e])) if ebits is not None else (lambda e: 4)
+    # gate/up kernel: the touched experts' gate and up rows (int4 or int2) and
+    # their f32 scales, x read once (bf16), h written once (f16; f32 + int8
+    # codes in the Q8 mode are intermediates past this)
+    gu_w = sum(2 * cfg.I * H * wb(e) // 8 + 8 * cfg.I for e in range(cfg.E) if counts[e])
+    gu_bytes = gu_w + 2 * T * H + 2 * P * cfg.I
+    gu_flops = 4.0 * P * cfg.I * H
     peak = INT8_PEAK_TOPS if q8 else BF16_PEAK_TFLOPS  # a contraction takes the peak of its own type
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TOP/s" if q8 else "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                "kernel": ("k_ffn_q8 gate/up (routed grouped GEMM + SwiGLU, int8 activations x int4 weights on "
-                           "i8 MFMA)" if q8 else
-                           "k_ffn gate/up (routed grouped GEMM + SwiGLU, int4 weights on bf16 MFMA)"),
-                "avg_launch_us": round(avg_ms * 1e3, 2), "alg_flops_per_launch": gu_flops,
-                "launches_timed": len(kms)}
-    cpu = None
+    t_hbm, t_mma = gu_bytes / (HBM_PEAK_GBS * 1e9), gu_flops / (peak * 1e12)
+    gu_gbs = gu_bytes / (avg_ms / 1e3) / 1e9
+    gu_tf = gu_flops / (avg_ms / 1e3) / 1e12
+    kname = ("k_ffn_q8 gate/up (routed grouped GEMM + SwiGLU, int8 activations x int4 weights on i8 MFMA)" if q8 else
+             "routed gate/up grouped GEMM + SwiGLU (int4 weights on bf16 MFMA)")
+    traffic = None
+    if cfg.name.startswith("c3") and not q8 and not cfg.int2_frac and not cfg.top_p:
+        traffic = measured_traffic("k_ffn_gateup_c3_traffic", ["ffn.hip"])
+    if t_hbm >= t_mma:
+        roofline = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(gu_tf, 1), "peak": peak, "unit": "TOP/s" if q8 else "TFLOP/s",
+                    "frac": round(gu_tf / peak, 4), "traffic": traffic}
+    roofline.update({"kernel": kname, "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "alg_bytes_per_launch": int(gu_bytes), "alg_flops_per_launch": gu_flops,
+                     "hbm_frac": round(gu_gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(gu_tf / peak, 4),
+                     "launches_timed": len(kms)})
+    # the layer: algorithmic bytes (touched experts' three matrices and scales,
+    # the shared expert, the router, x in, out, ids and weights) and flops
+    sh_bytes = (3 * cfg.I_sh * H * cfg.shared_bits // 8 + 4 * (2 * cfg.I_sh + H)) if cfg.shared_bits else 0
+    layer_bytes = (sum(3 * cfg.I * H * wb(e) // 8 + 4 * (2 * cfg.I + H) for e in range(cfg.E) if counts[e])
+                   + sh_bytes + 4 * cfg.E * H + 4 * cfg.E + 2 * T * H * 2 + 8 * T * cfg.k)
+    layer_flops = 6.0 * P * H * cfg.I + (6.0 * T * H * cfg.I_sh if cfg.shared_bits else 0.0)
+    t_s = ms_per_step / 1e3
+    lt_hbm, lt_mma = layer_bytes / (HBM_PEAK_GBS * 1e9), layer_flops / (peak * 1e12)
+
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         import oracle
         lw = oracle.LayerWeights(cfg, d)
-        n, spent, done = 4, 0.0, 0
-        while spent < args.cpu_seconds and done < T:
-            take = min(n, T - done)
-            t0 = time.time()
-            oracle.layer_forward(cfg.with_(T=take), lw, d["hidden"][done:done + take])
-            spent += time.time() - t0
-            done += take
-            n *= 2
-        cpu = {"value": round(done / spent, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"the first {done} tokens of the batch as sub-batches (router, permutation, routed and "
-                         f"shared FFN, combine) in {spent:.1f} s, f64-accumulating C oracle"}
+        state = {"off": 0}
+
+        def work(n):
+            o = state["off"] % T
+            take = min(n, T - o)
+            oracle.layer_forward(cfg.with_(T=take), lw, d["hidden"][o:o + take])
+            state["off"] += take
+            return take
+
+        fmt = (lambda done, spent: f"{done} tokens of the batch as sub-batches (router, permutation, routed and "
+                                   f"shared FFN, combine) in {spent:.1f} s, f64-accumulating C oracle")
+        cpu = cpu_baseline(oracle, work, cpu_s, "tokens/s", fmt)
+        if one_thread:
+            state["off"] = 0
+            cpu1 = cpu_baseline(oracle, work, cpu_s, "tokens/s", fmt, threads=1)
     line = {
-        "metric": f"MoE-layer tokens/s (prefill layer, {cfg.name})",
-        "value": round(T / (ms_per_step / 1e3), 1),
+        "metric": f"MoE-layer tokens/s (prefill layer, {cfg.name.split(':')[0]})",
+        "value": round(T / t_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -478,15 +670,24 @@ def bench_prefill(args, cfg, moe, synth, torch, np, dev):
                   "bf16 MFMA gate/up, f16 MFMA down, int4 weights, f32 accumulate"),
         "data": "synthetic (seeded)",
         "config": {"workload": cfg.name, "T": T, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
-                   "I_shared": cfg.I_sh, "shared_bits": cfg.shared_bits, "global_batch": T,
+                   "I_shared": cfg.I_sh, "shared_bits": cfg.shared_bits, "n_group": cfg.n_group,
+                   "topk_group": cfg.topk_group, "rsf": cfg.rsf, "global_batch": T,
                    "parallelism": "single GPU", "top_p": cfg.top_p, "routed_pairs": P, "act_q8": q8,
                    "int2_frac": cfg.int2_frac},
-        "layer_TFLOPs": round(layer_flops / (ms_per_step / 1e3) / 1e12, 1),
-        "layer_mfma_frac": round(layer_flops / (ms_per_step / 1e3) / 1e12 / peak, 4),
+        "layer": {"alg_bytes": int(layer_bytes), "alg_flops": layer_flops, "experts_touched": touched,
+                  "hbm_GBs": round(layer_bytes / t_s / 1e9, 1), "hbm_frac": round(layer_bytes / t_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "TFLOPs": round(layer_flops / t_s / 1e12, 1),
+                  "mfma_frac": round(layer_flops / t_s / 1e12 / peak, 4),
+                  "bound": "hbm" if lt_hbm >= lt_mma else "mfma",
+                  "roofline_frac": round(max(lt_hbm, lt_mma) / t_s, 4),
+                  "ideal_us": round(max(lt_hbm, lt_mma) * 1e6, 1),
+                  "rows_per_expert_max": int(counts.max()), "rows_per_expert_min": int(counts.min())},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    if cpu1 is not None:
+        line["cpu_baseline_1thread"] = cpu1
+    return line
 
 
 if __name__ == "__main__":

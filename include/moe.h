@@ -162,7 +162,10 @@ typedef struct {
  *   G_(keep) - G_(keep+1); it measures how close the token's selection is to a tie.
  * The GPU kernels need H % 128 == 0, I % 64 == 0, I_shared % 64 == 0, E <= 256,
  * top_k <= 64 and n_group <= 64 (else MOE_ERR_UNSUPPORTED; every call checks).
- * Workspace: the partial logits; moe_workspace_bytes(shape, MOE_WS_PERMUTE) covers it.
+ * Workspace: the K-split partial logits (the router splits the H-long dot
+ * products over workgroups and adds the slices in a fixed order, so it needs
+ * scratch that the caller owns like every other buffer);
+ * moe_workspace_bytes(shape, MOE_WS_PERMUTE) covers it.
  */
 int moe_router(const moe_shape *shape, const moe_bf16 *hidden, const float *router_w, const float *router_bias,
                int32_t *topk_ids, float *topk_w, float *sel_gap, void *ws, size_t ws_bytes, void *stream);
@@ -183,14 +186,21 @@ int moe_permute(const moe_shape *shape, const int32_t *topk_ids, int32_t *counts
 
 /*
  * moe_expert_ffn -- the routed experts on their sorted rows.
+ * Defined by: colibri README at 0d2fb6f, "Never wait for the disk twice" (an
+ * expert is three matrices, stored adjacent, read once per step for every
+ * position routed to it) and colibri README (older revision), "What's
+ * implemented" (batch-union MoE; per-row int4 weights dequantised on use);
+ * the activation between the matrices is SwiGLU (the pages name only the
+ * three matrices; gate, up and down is the plainest reading).
  * For sorted row r of expert e (offsets[e] <= r < offsets[e+1]), pair
  * p = sorted_pairs[r], token t = p / top_k:
  *   g_i = sg_i * sum_h x[t,h] q_gate[e,i,h],  u_i likewise with up,
  *   h_i = silu(g_i) * u_i with silu(z) = z / (1 + exp(-z))  (SwiGLU),
  *   y_pairs[r, c] = pair_scale[p] * sd_c * sum_i h_i q_down[e,c,i].
- * pair_scale is indexed by pair and nullable (then 1).  Computed with bf16
- * matrix cores: x and the int4 values are exact in bf16, products accumulate in
- * f32, h is rounded to bf16 before the down projection.
+ * pair_scale is indexed by pair and nullable (then 1).  Computed on matrix
+ * cores: x and the int4 values are exact in bf16, products accumulate in f32,
+ * h is rounded to f16 (nearest even) before the down projection, which runs
+ * on f16 matrix cores.
  * The shared expert runs through this call as E = 1, top_k = 1 with
  * offsets = {0, T}, sorted_pairs = identity and gate/up/down = the shared
  * matrices (shape.I = I_shared; set MOE_EXPERT_INT8 for int8 rows).  gate and
@@ -203,8 +213,13 @@ int moe_expert_ffn(const moe_shape *shape, const moe_bf16 *hidden, const moe_wei
                    float *y_pairs, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * moe_combine -- out[t,c] = sum over j ascending of coef(t,j) * y_pairs[inv_pos[t*top_k+j], c]
- *                           + shared_out[t,c] + residual[t,c]
+ * moe_combine -- the weighted sum of a token's expert outputs plus the shared
+ * expert (colibri README (older revision), "What's implemented": the router's
+ * weights scaled by routed_scaling_factor, and the shared expert; Colibri-Nano
+ * model card, "Architecture": an always-resident shared expert beside the
+ * routed ones):
+ *   out[t,c] = sum over j ascending of coef(t,j) * y_pairs[inv_pos[t*top_k+j], c]
+ *              + shared_out[t,c] + residual[t,c]
  * with coef = routed_scaling_factor * topk_w[t,j] when topk_w is given, else 1
  * (pairs already scaled).  shared_out [T][H] f32 and residual [T][H] bf16 are
  * nullable.  out is f32 or bf16 per MOE_OUT_F32.
@@ -215,6 +230,12 @@ int moe_combine(const moe_shape *shape, const float *y_pairs, const int32_t *inv
 /*
  * moe_layer_forward -- the whole layer: router, permutation, routed experts,
  * shared expert, combine (and the input added back when MOE_ADD_RESIDUAL).
+ * Defined by the calls above together: Colibri-Nano model card, "Architecture"
+ * (a sigmoid-routed MoE layer with a shared expert), colibri README (older
+ * revision), "What's implemented" (router, batch-union, shared expert, scaled
+ * combine) and colibri README at 0d2fb6f, "Never wait for the disk twice"
+ * (the per-token expert path).  Routed experts must be packed int4 (or int4
+ * and int2 with MOE_EXPERT_MIXED); MOE_EXPERT_INT8 is MOE_ERR_UNSUPPORTED here.
  * out: [T][H] f32 or bf16 per MOE_OUT_F32.  The regime (small-batch weight
  * streaming or tiled grouped GEMM) is chosen from the shape.  In the tiled
  * regime the shared expert runs on a second stream of the current device
@@ -235,9 +256,12 @@ int moe_layer_forward(const moe_shape *shape, const moe_weights *weights, const 
  * moe_layer_forward does; when next_weights is given, the layer's combine also
  * computes the next layer's router logits of the output row it has just
  * written, into next_ws, so the next call passes MOE_LOGITS_GIVEN and skips
- * its logits kernel.  Results equal the unchained calls (same output bits;
- * the next layer's logits are summed in another order, within f32 rounding,
- * so only a near-tie selection can differ).
+ * its logits kernel.  The call's own output equals the unchained call's bit
+ * for bit when its router logits are the same (always for the first layer of
+ * a step, which computes them itself).  The logits it leaves for the next
+ * layer are the same f32 sums added in another order, so the next layer's
+ * combine weights can differ from the unchained call's by f32 rounding
+ * (about 1e-7) and its selection only at a near tie.
  *   shape, weights, hidden, out, ws  as for moe_layer_forward; out must be bf16
  *               (no MOE_OUT_F32): it is what the next layer reads
  *   next_shape  the next layer's shape: same T and H, small-batch regime
@@ -290,7 +314,9 @@ int moe_layer_routing(const moe_shape *shape, void *ws, size_t ws_bytes, int32_t
  * row, with qmax = 7 (bits 4) or 127 (bits 8):
  *   scale = max|w| / qmax                 (f32, correctly rounded)
  *   code  = clamp(nearest integer to w / scale, ties to even, -qmax, qmax)
- * and an all-zero row gets scale 0 and codes 0.  Inputs must be finite.
+ * and an all-zero row gets scale 0 and codes 0.  Inputs must be finite, and
+ * a nonzero row's scale must not underflow to 0 (max|w| >= qmax * 2^-149);
+ * subnormal scales are fine.
  *
  *   src         device, [rows][cols], f32 (src_format MOE_SRC_F32) or bf16
  *               bits (MOE_SRC_BF16), row-major, no padding

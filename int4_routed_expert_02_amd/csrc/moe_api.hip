@@ -187,14 +187,20 @@ int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, con
                  const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, float *y,
                  hipStream_t st, const uint8_t *ebits = nullptr);
 
-// The two grouped GEMMs of one expert family on sorted rows.
+// gate and up of a family with more than one expert share one expert stride
+// (the kernels step both by it); a single expert's strides are never used.
+bool strides_ok(const moe_qmat &gate, const moe_qmat &up, int E)
+{
+    return E == 1 || (gate.q_stride_bytes == up.q_stride_bytes && gate.qs_stride_floats == up.qs_stride_floats);
+}
+
+// The two grouped GEMMs of one expert family on sorted rows (the caller has
+// checked strides_ok before its first enqueue).
 int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qmat &gate, const moe_qmat &up,
             const moe_qmat &down, int I, const int32_t *offsets, const int32_t *sorted, int E, int kdiv, int rows,
             const float *pscale, uint16_t *hbuf, float *y, hipStream_t st, bool gateup_only = false,
             const uint8_t *ebits = nullptr)
 {
-    if (gate.q_stride_bytes != up.q_stride_bytes || gate.qs_stride_floats != up.qs_stride_floats)
-        return MOE_ERR_UNSUPPORTED;
     FfnArgs g;
     memset(&g, 0, sizeof(g));
     g.A = hidden;
@@ -293,8 +299,6 @@ int run_ffn_q8(const moe_shape *s, int wbits, const moe_qmat &gate, const moe_qm
                const int32_t *offsets, const int32_t *sorted, int E, int kdiv, int rows, const float *pscale,
                const Q8Bufs &b, float *y, hipStream_t st, bool gateup_only = false)
 {
-    if (gate.q_stride_bytes != up.q_stride_bytes || gate.qs_stride_floats != up.qs_stride_floats)
-        return MOE_ERR_UNSUPPORTED;
     FfnArgs g;
     memset(&g, 0, sizeof(g));
     g.A = b.xq;
@@ -396,12 +400,11 @@ int moe_expert_ffn(const moe_shape *s, const moe_bf16 *hidden, const moe_weights
     if ((st = check_qmat(w->gate)) || (st = check_qmat(w->up)) || (st = check_qmat(w->down))) return st;
     if ((st = check_ws(s, MOE_WS_EXPERT_FFN, ws, ws_bytes))) return st;
     if (s->flags & MOE_ACT_Q8) return MOE_ERR_UNSUPPORTED;  // the int8-activation mode: moe_layer_forward
+    if (!strides_ok(w->gate, w->up, s->E)) return MOE_ERR_UNSUPPORTED;
     const Layout L = layout(s, MOE_WS_EXPERT_FFN);
     const int wbits = (s->flags & MOE_EXPERT_INT8) ? 8 : 4;
     if (s->flags & MOE_TEST_GATEUP_SUMS) {
         if (wbits != 4 || 2 * s->I > s->H) return MOE_ERR_UNSUPPORTED;
-        if (w->gate.q_stride_bytes != w->up.q_stride_bytes || w->gate.qs_stride_floats != w->up.qs_stride_floats)
-            return MOE_ERR_UNSUPPORTED;
         FfnArgs g;
         memset(&g, 0, sizeof(g));
         g.A = hidden;
@@ -464,8 +467,9 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         ((st = check_qmat(w->sh_gate)) || (st = check_qmat(w->sh_up)) || (st = check_qmat(w->sh_down))))
         return st;
     if ((st = check_ws(s, MOE_WS_LAYER, ws, ws_bytes))) return st;
-    if (w->gate.q_stride_bytes != w->up.q_stride_bytes || w->gate.qs_stride_floats != w->up.qs_stride_floats)
-        return MOE_ERR_UNSUPPORTED;
+    // routed experts are packed int4 (int8 rows are a moe_expert_ffn format, for a shared expert)
+    if (s->flags & MOE_EXPERT_INT8) return MOE_ERR_UNSUPPORTED;
+    if (!strides_ok(w->gate, w->up, s->E)) return MOE_ERR_UNSUPPORTED;
     if ((s->flags & MOE_EXPERT_MIXED) && !w->expert_bits) return MOE_ERR_NULL;
     const uint8_t *ebits = (s->flags & MOE_EXPERT_MIXED) ? w->expert_bits : nullptr;
     const Layout L = layout(s, MOE_WS_LAYER);

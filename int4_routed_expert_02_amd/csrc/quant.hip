@@ -30,12 +30,20 @@ constexpr int QZ_RG = 16;   // register-held groups of eight values per lane (ro
 // correctly rounded 1 / scale) is within 1.5 * 2^-23 * |t| <= 2.3e-5 of that
 // quotient for |t| <= 127.5, so rint(t) is the same integer unless t lies
 // within that distance of a half-integer; there (about one value in 8000)
-// the correctly rounded division decides.
+// the correctly rounded division decides.  That bound needs a normal scale:
+// below 2^-126 (rows whose max|w| is under qmax * 2^-126) 1 / scale loses
+// precision and below 2^-128 it overflows to infinity, so such rows (a
+// wave-uniform case) take the division for every value.
 __device__ __forceinline__ uint32_t qz_code(float w, float scale, float inv, float qmax)
 {
-    const float t = w * inv;
-    float k = rintf(t);
-    if (fabsf(fabsf(t - k) - 0.5f) < 0x1p-14f) k = rintf(__fdiv_rn(w, scale));
+    float k;
+    if (scale < 0x1p-126f) {
+        k = rintf(__fdiv_rn(w, scale));
+    } else {
+        const float t = w * inv;
+        k = rintf(t);
+        if (fabsf(fabsf(t - k) - 0.5f) < 0x1p-14f) k = rintf(__fdiv_rn(w, scale));
+    }
     return (uint32_t)(int)fminf(fmaxf(k, -qmax), qmax);
 }
 

@@ -84,6 +84,7 @@ def lib():
             "oracle_layer_forward_dense": ([S, W, vp, vp], ctypes.c_int),
             "oracle_gateup_int_sums": ([S, vp, W, vp, vp, vp, vp], ctypes.c_int),
             "oracle_num_threads": ([], ctypes.c_int),
+            "oracle_set_num_threads": ([ctypes.c_int], None),
             "oracle_quantize_rows": ([vp, i32, ctypes.c_int64, i32, i32, vp, vp], ctypes.c_int),
             "oracle_quantize_act_q8": ([vp, i32, ctypes.c_int64, i32, vp, vp], ctypes.c_int),
             "oracle_bias_update": ([i32, vp, vp, ctypes.c_float, vp], ctypes.c_int),
@@ -318,3 +319,8 @@ def bias_update(counts: np.ndarray, bias: np.ndarray, gamma: float) -> np.ndarra
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the oracle's later calls from this thread (results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))

@@ -29,6 +29,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads of the following oracle calls from this thread (n >= 1); the
+ * results do not depend on it (no reduction is split across threads). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---------------------------------------------------------------- formats */
 
 float oracle_bf16_to_f32(uint16_t bits)

@@ -182,6 +182,7 @@ int oracle_quantize_rows(const void *src, int32_t src_bf16, int64_t rows, int32_
 int oracle_bias_update(int32_t E, const int32_t *counts, const float *bias_in, float gamma, float *bias_out);
 
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

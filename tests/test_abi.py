@@ -124,6 +124,13 @@ def test_errors_before_any_enqueue(moe):
     w3.up = moe.MoeQMat(FAKE, FAKE, 16, 0)
     assert lib.moe_layer_forward(ctypes.byref(s), ctypes.byref(w3), vp(FAKE), vp(FAKE), vp(FAKE), need,
                                  None) == moe.MOE_ERR_UNSUPPORTED
+    # the layer's routed experts are int4: the int8 row format is moe_expert_ffn's (shared expert)
+    s8 = good(moe, flags=moe.MOE_EXPERT_INT8)
+    assert lib.moe_layer_forward(ctypes.byref(s8), ctypes.byref(w), vp(FAKE), vp(FAKE), vp(FAKE),
+                                 moe.moe_workspace_bytes(s8, moe.MOE_WS_LAYER), None) == moe.MOE_ERR_UNSUPPORTED
+    # moe_expert_ffn with gate/up of different expert strides: rejected before any enqueue
+    assert lib.moe_expert_ffn(ctypes.byref(s), vp(FAKE), ctypes.byref(w3), vp(FAKE), vp(FAKE), None, vp(FAKE),
+                              vp(FAKE), 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
     # the experts-only profiling stage exists only in the small-batch regime (T <= 32, H % 1024 == 0)
     big = good(moe, T=64, flags=moe.MOE_STAGE_EXPERTS_ONLY)
     need_big = moe.moe_workspace_bytes(big, moe.MOE_WS_LAYER)

@@ -178,19 +178,22 @@ FULL = ["c0", "c2", "c4", "c3"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
+def test_full_size(name):
     """The full workload in the benchmark's launch configuration (moe_layer_forward,
-    f32 output); routing and permutation checked on every token, outputs on a
-    seeded sample of tokens the oracle computes one by one."""
+    f32 output); routing and permutation checked on every token, outputs on
+    every token (c0, c2, c4) or, for the GLM-class layer, whose oracle runs
+    about 40 tokens/s, on 514 tokens: the first, the last and a seeded sample
+    of 512."""
     cfg = synth.CONFIGS[name]
     say(f"[full] {name}: generating T={cfg.T} E={cfg.E} H={cfg.H}")
     d = synth.layer(cfg)
     got, ids, w, offsets, srt = run_layer(cfg, d)
     ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag=name)
-    rng = np.random.default_rng(7)
-    n = min(cfg.T, 24 if cfg.H > 2048 else 64)
-    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n, replace=False)]))
-    check_output(cfg, d, d["hidden"], got, ex, tokens=toks, tag=f"{name} (exempt {int(ex.sum())})")
+    toks = None
+    if cfg.H > 2048:
+        rng = np.random.default_rng(7)
+        toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(np.arange(1, cfg.T - 1), 512, replace=False)]))
+    check_output(cfg, d, d["hidden"], got, ex, tokens=toks, tag=f"{name} (skipped {int(ex.sum())})")
     counts = np.bincount(ids.ravel(), minlength=cfg.E)
     say(f"{name}: rows per expert max {counts.max()} min {counts.min()} active {np.count_nonzero(counts)}")
 
@@ -228,6 +231,74 @@ def test_decode_stack_on_oracle_trajectory():
         got, ids, w, offsets, srt = run_layer(cfg, d, flags=moe.MOE_ADD_RESIDUAL, hidden=x)
         ex = check_routing(cfg, d, x, ids, w, offsets, srt, tag=f"c1 layer {l}")
         check_output(cfg, d, x, got, ex, residual=True, bf16_out=True, tag=f"c1 layer {l}")
+
+
+def _identity_layer(cfg):
+    """The c1 shape with every expert weight scale zero: routed and shared
+    experts add exactly 0, so with the residual the layer's bf16 output is its
+    input, bit for bit."""
+    d = synth.layer(cfg, 0, with_hidden=False)
+    d["experts_qs"][:] = 0.0
+    d["shared_qs"][:] = 0.0
+    return moe.MoeLayer(cfg, d)
+
+
+def test_decode_chain_against_oracle():
+    """The benchmark's chained decode step, layer by layer, against the oracle
+    on the oracle's own 23-layer trajectory.  Layer 0 runs as in the step
+    (chained, computing its own logits).  Every later layer runs as in the
+    step too (MOE_LOGITS_GIVEN, chained to the next layer), on the oracle's
+    input to it, with its router logits written by the chained combine of the
+    identity layer (zero weight scales) run on that same input -- the kernel
+    that writes them in the step.  Checked: routing of every token, all
+    outputs; layer 0 gives the unchained call's bits exactly, the later
+    layers' outputs lie within 1e-4 of the RMS of the unchained call's (their
+    logits are the same sums in another order)."""
+    import torch
+    cfg = synth.CONFIGS["c1"]
+    T, k, H, L = cfg.T, cfg.k, cfg.H, cfg.layers
+    flags = moe.MOE_ADD_RESIDUAL
+    stack = oracle_stack(cfg)
+    layers = [moe.MoeLayer(cfg, synth.layer(cfg, l, with_hidden=False)) for l in range(L)]
+    wss = [ly.workspace(T, flags) for ly in layers]
+    ident = _identity_layer(cfg)
+    ws_id = ident.workspace(T, flags)
+    ws_ref = layers[0].workspace(T, flags)
+    sh = moe.shape_of(cfg, T, flags)
+    for l in range(L):
+        x_np = stack[l][0]
+        x = dev_bf16(x_np)
+        if l:
+            back = torch.empty_like(x)
+            ident.forward_chain(x, back, ws_id, flags, layers[l], wss[l])
+            torch.cuda.synchronize()
+            assert torch.equal(back, x), f"layer {l}: the identity layer changed its input"
+        out = torch.empty_like(x)
+        nxt = layers[l + 1] if l + 1 < L else None
+        layers[l].forward_chain(x, out, wss[l], flags | (moe.MOE_LOGITS_GIVEN if l else 0), nxt,
+                                wss[l + 1] if nxt is not None else None)
+        ref = torch.empty_like(x)
+        layers[l].forward(x, ref, ws_ref, flags)
+        torch.cuda.synchronize()
+        d = synth.layer(cfg, l, with_hidden=False)
+        pid, pw, _, _ = moe.moe_layer_routing(sh, wss[l])
+        ids = ws_view(wss[l], pid, T * k, torch.int32).cpu().numpy().reshape(T, k)
+        w = ws_view(wss[l], pw, T * k, torch.float32).cpu().numpy().reshape(T, k)
+        ex = check_routing(cfg, d, x_np, ids, w, None, None, tag=f"chained layer {l}")
+        got = out.float().cpu().numpy()
+        check_output(cfg, d, x_np, got, ex, residual=True, bf16_out=True, tag=f"chained layer {l}")
+        rid, _, _, _ = moe.moe_layer_routing(sh, ws_ref)
+        r_ids = ws_view(ws_ref, rid, T * k, torch.int32).cpu().numpy().reshape(T, k)
+        if l == 0:
+            assert torch.equal(out, ref), "layer 0: chained and unchained outputs differ"
+        else:
+            same = np.all(ids == r_ids, axis=1)
+            a, b = got[same].astype(np.float64), ref.float().cpu().numpy()[same].astype(np.float64)
+            rms = float(np.sqrt(np.mean(b * b)))
+            diff = float(np.max(np.abs(a - b))) / rms if same.any() else 0.0
+            # (a weight that moved by f32 rounding can flip one bf16 rounding: an ulp of the value)
+            ulp = np.abs(b) * 2.0 ** -7
+            assert np.all(np.abs(a - b) <= np.maximum(ulp, 1e-4 * rms)), f"layer {l}: {diff}"
 
 
 def test_decode_chain_matches_unchained():
@@ -270,7 +341,13 @@ def test_decode_chain_matches_unchained():
         err = float(np.max(np.abs(a - b))) / rms
         say(f"chain layer {l}: max|chained-unchained|/rms = {err:.3e}, weights {werr:.1e}, "
             f"{int((~same).sum())} tokens routed differently")
-        assert err <= 1e-2
+        if l == 0:
+            # the same logits kernel: the same bits
+            assert torch.equal(out, ref), "layer 0: chained and unchained outputs differ"
+        else:
+            # weights that moved by f32 rounding can flip a bf16 rounding (an ulp of the value)
+            ulp = np.abs(b.astype(np.float64)) * 2.0 ** -7
+            assert np.all(np.abs(a - b) <= np.maximum(ulp, 1e-4 * rms)), f"layer {l}: {err}"
         x = out
 
 

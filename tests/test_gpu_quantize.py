@@ -72,6 +72,33 @@ def test_quantize_matches_oracle(bits, fmt, rows, cols):
     same(f"{fmt} int{bits} {rows}x{cols}", gpu_quantize(src, bits), oracle.quantize_rows(src, bits))
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+@pytest.mark.parametrize("cols", [1024, 130])
+def test_quantize_tiny_rows(bits, fmt, cols):
+    """Rows whose scale max|w| / qmax is subnormal (max|w| around 1e-38 for
+    int4, 1e-37 for int8, and smaller still, down to a row of denormals), where
+    1 / scale overflows or loses precision: codes and scales still equal the
+    oracle's plain f32 division, zeros stay 0."""
+    rng = np.random.default_rng(31 + bits + cols)
+    rows = 24
+    amax = np.float32(1e-38 if bits == 4 else 1e-37) * np.logspace(0, -4, rows).astype(np.float32)
+    src = (rng.uniform(-1.0, 1.0, (rows, cols)) * amax[:, None]).astype(np.float32)
+    src[:, 0] = amax                # the row maximum itself
+    src[:, 1] = amax / 2            # a half of it
+    src[:, 2] = 0.0                 # zeros must stay 0
+    src[:, 3] = -amax
+    src[-1] = 0.0
+    src[-1, 5] = np.float32(1e-40)   # a row of denormals
+    src[-1, 6] = np.float32(-3e-41)
+    if fmt == "bf16":
+        src = to_bf16_bits(src)
+    got = gpu_quantize(src, bits)
+    want = oracle.quantize_rows(src, bits)
+    same(f"tiny {fmt} int{bits} {rows}x{cols}", got, want)
+    assert np.all(want[1] < np.float32(2.0 ** -126))
+
+
 @pytest.mark.parametrize("bits,cols", [(4, 130), (8, 131), (4, 2), (8, 1)])
 def test_quantize_ragged_widths(bits, cols):
     src = host_rows(7 + cols, 33, cols, bits)

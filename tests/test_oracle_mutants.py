@@ -16,6 +16,8 @@ MUTANTS = {
     "bias enters weights": ("sum += (double)s[ids[j]]", "sum += (double)b[ids[j]]"),
     "ties to higher id": ("(best < 0 || b[e] > b[best])", "(best < 0 || b[e] >= b[best])"),
     "group score top-1": ("gscore[g] = b1 + b2;", "gscore[g] = b1;"),
+    "group gap sign": ("group_gap = last_kept - first_dropped;", "group_gap = first_dropped - last_kept;"),
+    "group gap from the best kept group": ("last_kept = gscore[best];", "if (r == 0) last_kept = gscore[best];"),
     "gate and up swapped": ("h[i] = (float)((double)g / (1.0 + exp(-(double)g)) * (double)u);",
                             "h[i] = (float)((double)u / (1.0 + exp(-(double)u)) * (double)g);"),
     "rsf on shared": ("if (shared_out) acc += (double)shared_out[(int64_t)t * H + c];",

@@ -197,6 +197,74 @@ def test_router_gap_definition(synth_mod, oracle_mod):
     assert np.all(np.isinf(ggap))
 
 
+def _brute_gaps(b_row, k, n_group, topk_group):
+    """Tie gaps of group-limited selection by enumeration: ggap = the f32
+    difference between the kept group of lowest score and the best dropped
+    group, where the kept set is the best-scoring subset of topk_group groups
+    (group score: the largest f32 sum of two distinct members); gap = the f32
+    difference between the k-th and (k+1)-th largest b among the experts of
+    the kept groups (inf when no allowed expert is left over)."""
+    E = len(b_row)
+    Eg = E // n_group
+    G = [max(np.float32(b_row[a]) + np.float32(b_row[c])
+             for a, c in itertools.combinations(range(g * Eg, (g + 1) * Eg), 2)) for g in range(n_group)]
+    best = None
+    for sub in itertools.combinations(range(n_group), topk_group):
+        key = (sum(float(G[g]) for g in sub), [-g for g in sub])
+        if best is None or key > best[0]:
+            best = (key, sub)
+    kept = set(best[1])
+    worst_kept = min(G[g] for g in kept)
+    best_dropped = max(G[g] for g in range(n_group) if g not in kept)
+    ggap = np.float32(worst_kept - best_dropped)
+    allowed = sorted((float(b_row[e]) for e in range(E) if e // Eg in kept), reverse=True)
+    gap = np.float32(np.float32(allowed[k - 1]) - np.float32(allowed[k])) if len(allowed) > k else np.float32(np.inf)
+    return gap, ggap
+
+
+@pytest.mark.parametrize("E,k,ng,kg", [(16, 4, 4, 2), (12, 2, 3, 1), (16, 8, 8, 4), (32, 8, 8, 4), (16, 4, 4, 1)])
+def test_router_group_gaps_brute_force(synth_mod, oracle_mod, E, k, ng, kg):
+    """Group-limited routing: both tie gaps (the quantities the GPU tests use to
+    exempt near-tie tokens) against enumeration of the group subsets.  The
+    (16, 4, 4, 1) case keeps one group of four experts for k = 4, so nothing
+    is left over and gap is infinite."""
+    cfg = tiny_cfg(synth_mod, T=64, H=64, E=E, k=k, n_group=ng, topk_group=kg, seed=900 + E + k + kg)
+    x = synth_mod.hidden(cfg)
+    W, bias = synth_mod.router(cfg)
+    W *= 8
+    _, s, b = oracle_mod.router_scores(cfg, x, W, bias)
+    _, _, gap, ggap = oracle_mod.router(cfg, x, W, bias)
+    for t in range(cfg.T):
+        bg, bgg = _brute_gaps(b[t], k, ng, kg)
+        assert ggap[t] == bgg, (t, ggap[t], bgg)
+        assert gap[t] == bg, (t, gap[t], bg)
+        assert ggap[t] >= 0 and gap[t] >= 0
+    if (E, k, ng, kg) == (16, 4, 4, 1):
+        assert np.all(np.isinf(gap))
+
+
+def test_router_group_gap_worked_example(synth_mod, oracle_mod):
+    """A hand-computed token (W = 0, so s = 1/2 and b = 1/2 + bias): four
+    groups of four; group scores (top-two sums of b) 1.9, 1.5, 1.2, 1.45 ->
+    keep groups 0 and 1, ggap = 1.5 - 1.45; top-3 of the kept experts are
+    1.0, 0.9, 0.8 with 0.7 next -> gap = 0.8 - 0.7."""
+    cfg = tiny_cfg(synth_mod, T=1, E=16, k=3, n_group=4, topk_group=2)
+    x = synth_mod.hidden(cfg)
+    W = np.zeros((cfg.E, cfg.H), np.float32)
+    b_target = np.array([1.0, 0.9, 0.1, 0.2,   0.8, 0.7, 0.3, 0.0,
+                         0.6, 0.6, 0.5, 0.4,   0.75, 0.7, 0.2, 0.1], np.float32)
+    bias = (b_target - np.float32(0.5)).astype(np.float32)
+    _, _, b = oracle_mod.router_scores(cfg, x, W, bias)
+    ids, _, gap, ggap = oracle_mod.router(cfg, x, W, bias)
+    assert list(ids[0]) == [0, 1, 4]
+    G = [np.float32(b[0][0] + b[0][1]), np.float32(b[0][4] + b[0][5]), np.float32(b[0][8] + b[0][9]),
+         np.float32(b[0][12] + b[0][13])]
+    assert ggap[0] == np.float32(G[1] - G[3])
+    assert abs(float(ggap[0]) - 0.05) < 1e-6
+    assert gap[0] == np.float32(b[0][4] - b[0][5])
+    assert abs(float(gap[0]) - 0.1) < 1e-6
+
+
 # -------------------------------------------------------------- permutation
 
 def test_permute_is_stable_argsort_and_invariants(synth_mod, oracle_mod):
