@@ -276,6 +276,31 @@ int moe_layer_forward_chain(const moe_shape *shape, const moe_weights *weights, 
                             void *ws, size_t ws_bytes, const moe_shape *next_shape, const moe_weights *next_weights,
                             void *next_ws, size_t next_ws_bytes, void *stream);
 
+/*
+ * moe_layer_forward_noalloc -- moe_layer_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Instead of a caller workspace it uses the
+ * library's own scratch, a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that each GPU the library runs on holds until the process ends;
+ * the call allocates nothing (no hipMalloc, no stream or event creation: in
+ * the tiled regime the shared expert runs on `stream` too).  Results are
+ * those of moe_layer_forward, bit for bit.
+ *   shape, weights, hidden, out, stream  as for moe_layer_forward
+ * Errors: as moe_layer_forward; MOE_ERR_WORKSPACE when the shape's layer
+ * workspace, moe_workspace_bytes(shape, MOE_WS_LAYER), exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (checked before anything is enqueued);
+ * MOE_ERR_UNSUPPORTED with MOE_STAGE_EXPERTS_ONLY or MOE_LOGITS_GIVEN (they
+ * read a previous call's workspace); MOE_ERR_HIP if the scratch's device
+ * address cannot be had.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (every kernel of the layer writes what it later reads, so
+ * no clearing is needed): calls that overlap on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_forward_noalloc(const moe_shape *shape, const moe_weights *weights, const moe_bf16 *hidden, void *out,
+                              void *stream);
+
 /* moe_layer_forward with two HIP events (hipEvent_t as void*, nullable) recorded
  * on `stream` immediately before and after the expert gate/up kernel: the
  * grouped gate/up + SwiGLU GEMM of the routed experts (tiled regime) or the

@@ -47,7 +47,9 @@ MOE_WS_LAYER = 3
 EXPORTS = ["moe_router", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_profiled", "moe_workspace_bytes", "moe_validate_shape", "moe_status_string",
            "moe_layer_routing", "moe_quantize_rows", "moe_bias_update", "moe_layer_forward_chain",
-           "moe_quantize_act_q8"]
+           "moe_quantize_act_q8", "moe_layer_forward_noalloc"]
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeShape(ctypes.Structure):
@@ -95,6 +97,7 @@ def load() -> ctypes.CDLL:
             "moe_combine": [S, vp, vp, vp, vp, vp, vp, vp],
             "moe_layer_forward": [S, W, vp, vp, vp, sz, vp],
             "moe_layer_forward_profiled": [S, W, vp, vp, vp, sz, vp, vp, vp],
+            "moe_layer_forward_noalloc": [S, W, vp, vp, vp],
             "moe_layer_forward_chain": [S, W, vp, vp, vp, sz, S, W, vp, sz, vp],
             "moe_validate_shape": [S],
             "moe_layer_routing": [S, vp, sz, vp, vp, vp, vp],
@@ -199,6 +202,12 @@ def moe_layer_forward_profiled(sh: MoeShape, weights: MoeWeights, hidden, out, w
     _check(load().moe_layer_forward_profiled(ctypes.byref(sh), ctypes.byref(weights), _ptr(hidden), _ptr(out),
                                              _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream),
                                              ev_start.cuda_event, ev_stop.cuda_event), "moe_layer_forward_profiled")
+
+
+def moe_layer_forward_noalloc(sh: MoeShape, weights: MoeWeights, hidden, out, stream=None):
+    """moe_layer_forward on the library's static scratch: no workspace, no allocation (include/moe.h)."""
+    _check(load().moe_layer_forward_noalloc(ctypes.byref(sh), ctypes.byref(weights), _ptr(hidden), _ptr(out),
+                                            _stream(stream)), "moe_layer_forward_noalloc")
 
 
 def moe_layer_forward_chain(sh: MoeShape, weights: MoeWeights, hidden, out, ws, next_sh: Optional[MoeShape] = None,

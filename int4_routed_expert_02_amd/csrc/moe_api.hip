@@ -50,6 +50,30 @@ SideStream *side_stream(hipStream_t caller)
 
 constexpr size_t WS_ALIGN = 256;
 
+// The workspace of moe_layer_forward_noalloc: a file-scope device array, one
+// copy per GPU, kept until the process ends.  Host code never passes its name
+// to a kernel or a copy (on the host the name is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is kept in g_scratch.
+constexpr size_t NOALLOC_BYTES = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
+void *g_scratch[MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+// This device's copy of `scratch` (nullptr on failure).
+void *scratch_ptr()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch[dev] = p;
+    }
+    return g_scratch[dev];
+}
+
 size_t align_up(size_t v) { return (v + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -455,7 +479,7 @@ namespace {
 // the next layer of a chained small-batch step (nw null: not chained).
 int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out, void *ws,
                  size_t ws_bytes, void *stream, void *ev_start, void *ev_stop, const moe_shape *ns,
-                 const moe_weights *nw, void *nws, size_t nws_bytes)
+                 const moe_weights *nw, void *nws, size_t nws_bytes, bool allow_side = true)
 {
     int st = validate(s);
     if (st) return st;
@@ -593,7 +617,7 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     // so a failing call leaves no open fork (nor a broken graph capture).
     SideStream *side = nullptr;
     std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
-    if (s->shared_bits && !ev_start && !ev_stop) {
+    if (s->shared_bits && !ev_start && !ev_stop && allow_side) {
         side_lock.lock();
         side = side_stream(hs);
         if (!side) side_lock.unlock();
@@ -670,6 +694,22 @@ int moe_layer_forward_chain(const moe_shape *s, const moe_weights *w, const moe_
 {
     return forward_impl(s, w, hidden, out, ws, ws_bytes, stream, nullptr, nullptr, next_shape, next_weights, next_ws,
                         next_ws_bytes);
+}
+
+int moe_layer_forward_noalloc(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidden, void *out,
+                              void *stream)
+{
+    int st = validate(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;
+    const size_t need = layout(s, MOE_WS_LAYER).total;
+    if (need > NOALLOC_BYTES) return MOE_ERR_WORKSPACE;
+    if (s->flags & (MOE_STAGE_EXPERTS_ONLY | MOE_LOGITS_GIVEN)) return MOE_ERR_UNSUPPORTED;
+    void *ws = scratch_ptr();
+    if (!ws) return MOE_ERR_HIP;
+    // the shared expert stays on `stream` (no second stream is created here)
+    return forward_impl(s, w, hidden, out, ws, NOALLOC_BYTES, stream, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                        false);
 }
 
 int moe_bias_update(int32_t E, const int32_t *counts, float *router_bias, float gamma, void *stream)

@@ -131,6 +131,13 @@ def test_errors_before_any_enqueue(moe):
     # moe_expert_ffn with gate/up of different expert strides: rejected before any enqueue
     assert lib.moe_expert_ffn(ctypes.byref(s), vp(FAKE), ctypes.byref(w3), vp(FAKE), vp(FAKE), None, vp(FAKE),
                               vp(FAKE), 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
+    # the no-allocation entry point: a shape whose layer workspace exceeds its scratch is refused
+    huge = good(moe, T=4096)
+    assert moe.moe_workspace_bytes(huge, moe.MOE_WS_LAYER) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(huge), ctypes.byref(w), vp(FAKE), vp(FAKE),
+                                         None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(good(moe, H=1023)), ctypes.byref(w), vp(FAKE), vp(FAKE),
+                                         None) == moe.MOE_ERR_SHAPE
     # the experts-only profiling stage exists only in the small-batch regime (T <= 32, H % 1024 == 0)
     big = good(moe, T=64, flags=moe.MOE_STAGE_EXPERTS_ONLY)
     need_big = moe.moe_workspace_bytes(big, moe.MOE_WS_LAYER)
