@@ -14,7 +14,7 @@ BUILD = os.path.join(PKG, "_build")
 SOURCES = ["moe_api.hip", "router.hip", "permute.hip", "ffn.hip", "combine.hip", "decode.hip", "quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC,
+FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++20", "-I", INCLUDE, "-I", CSRC,
          # packed fp32 instructions stay off on this hardware
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-result"]
