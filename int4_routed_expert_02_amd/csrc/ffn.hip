@@ -369,15 +369,21 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
         }
     }
     // Copy j < A_LOADS / 4 of every wave is an A copy (8 rows).  Only the
-    // first AJ of them are issued: rows past 32 AJ are never read.
-    auto issue = [&](int kt, auto ajc) {
-        constexpr int AJ = decltype(ajc)::value;
-        uint8_t *base = smem3 + (kt % C::NST) * C::STAGE;
+    // first AJ of them are issued: rows past 32 AJ are never read.  The ring
+    // is laid out for the tile's valid rows: a stage holds 4 AJ KB of A, then
+    // the B copies, and the ring takes as many such stages as the space
+    // reserved for NST full-height stages holds (more weight bytes in flight
+    // when a group has fewer rows than the tile height).
+    auto issue = [&](int kt, auto ajc, auto nsc) {
+        constexpr int AJ = decltype(ajc)::value, NS = decltype(nsc)::value;
+        constexpr int ABY = 4 * AJ * 1024, SBY = ABY + (C::LOADS - C::A_LOADS) * 1024;
+        uint8_t *base = smem3 + (kt % NS) * SBY;
 #pragma unroll
         for (int j = 0; j < C::PER_WAVE; ++j) {
             if (j >= AJ && j < C::A_LOADS / 4) continue;
-            const size_t adv = j < C::A_LOADS / 4 ? (size_t)kt * FF_BK * 2 : (size_t)kt * BKB;
-            lds_copy16(src[j] + adv, base + dst[j]);
+            const bool isa = j < C::A_LOADS / 4;
+            const size_t adv = isa ? (size_t)kt * FF_BK * 2 : (size_t)kt * BKB;
+            lds_copy16(src[j] + adv, base + (isa ? dst[j] : ABY + dst[j] - C::A_BYTES));
         }
     };
 
@@ -408,17 +414,22 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
         constexpr int MV = decltype(mvc)::value;
         constexpr int AJ = (MV + 1) / 2;                       // A copies per wave and stage
         constexpr int PW = C::PER_WAVE - (C::A_LOADS / 4 - AJ);  // copies per wave and stage
+        constexpr int ABY = 4 * AJ * 1024, SBY = ABY + (C::LOADS - C::A_LOADS) * 1024;  // compact stage
+        constexpr int NS_FIT = C::RING / SBY, NS_CNT = 2 + 63 / PW;
+        constexpr int NS = NS_FIT < NS_CNT ? (NS_FIT < 8 ? NS_FIT : 8) : (NS_CNT < 8 ? NS_CNT : 8);
+        static_assert(NS >= C::NST && PW * (NS - 2) < 64, "ring");
         const IntC<AJ> ajc;
+        const IntC<NS> nsc;
 #pragma unroll
-        for (int s0 = 0; s0 < C::NST - 1; ++s0)
-            if (s0 < KT) issue(s0, ajc);
+        for (int s0 = 0; s0 < NS - 1; ++s0)
+            if (s0 < KT) issue(s0, ajc, nsc);
         for (int kt = 0; kt < KT; ++kt) {
             // stage kt has landed once at most the later stages' copies are outstanding
-            wait_stages<PW, C::NST - 2>(KT - 1 - kt);
+            wait_stages<PW, NS - 2>(KT - 1 - kt);
             ring_barrier();  // every wave's copies of stage kt are in LDS; stage kt - 1 is free
-            if (kt + C::NST - 1 < KT) issue(kt + C::NST - 1, ajc);
-            const uint8_t *sa = smem3 + (kt % C::NST) * C::STAGE;
-            const uint8_t *sb = sa + C::A_BYTES;
+            if (kt + NS - 1 < KT) issue(kt + NS - 1, ajc, nsc);
+            const uint8_t *sa = smem3 + (kt % NS) * SBY;
+            const uint8_t *sb = sa + ABY;
 #pragma unroll
             for (int ks = 0; ks < FF_BK / 32; ++ks) {
                 u32x4 af[MV];
@@ -451,7 +462,107 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
             }
         }
     };
+    // Tiles of few valid rows with int4 weights take 128-k stages instead
+    // (kloop128): a weight copy is then 16 rows x 64 bytes, half the
+    // requests per weight byte of the 32-byte rows above (the request rate,
+    // not the bytes, limits the copies of a weight-bound tile), and the
+    // compact stage of the valid rows still leaves two stages in the ring.
+    // Lane l of a copy of block b loads row l % 16 of the block, bytes
+    // 16 (l / 16) .. + 16 of the stage's 64; global_load_lds puts it at 16 l,
+    // so the wave that multiplies block b reads its own 16 bytes back with
+    // one conflict-free LDS read.  k-slots: lane group g holds k = 32 g + v of
+    // the stage, MFMA j takes v = 8 j .. 8 j + 7; the A fragment of lane
+    // (row, g) for j is the 16-byte chunk 4 g + j of the row (256-byte rows,
+    // chunk slots XOR-swizzled by the row's low four bits).
+    auto kloop128 = [&](auto mvc) {
+        constexpr int MV = decltype(mvc)::value;
+        constexpr int NBLK = NMAT * BN / 16;               // 16-row weight blocks of the tile
+        constexpr int BJ = NBLK / 4;                        // weight copies per wave and stage
+        constexpr int PW = MV + BJ;                         // copies per wave and stage (MV of A)
+        constexpr int ABY = MV * 4 * 1024, SBY = ABY + NBLK * 1024;
+        constexpr int NS_FIT = C::RING / SBY, NS_CNT = 2 + 63 / PW;
+        constexpr int NS = NS_FIT < NS_CNT ? (NS_FIT < 8 ? NS_FIT : 8) : (NS_CNT < 8 ? NS_CNT : 8);
+        static_assert(NS >= 2 && PW * (NS - 2) < 64, "ring");
+        const int KT2 = a.K / 128;
+        const uint8_t *as[MV];
+#pragma unroll
+        for (int j = 0; j < MV; ++j) {
+            const int c = wn + 4 * j;  // copy c: rows 4c .. 4c + 3
+            const int r = 4 * c + lane / 16;
+            const int rr = r < rows ? r : 0;
+            const int srow = a.gather ? a.gather[row0 + rr] / a.kdiv : row0 + rr;
+            as[j] = (const uint8_t *)a.A + ((size_t)srow * a.lda + (((lane & 15) ^ (r & 15)) * 8)) * 2;
+        }
+        const uint8_t *bs[BJ];
+#pragma unroll
+        for (int j = 0; j < BJ; ++j) {
+            const int b = wn + 4 * j;  // block b: matrix b / (BN / 16), rows 16 (b % (BN / 16)) ..
+            const uint8_t *qm = (b / (BN / 16) == 0) ? a.q0 : a.q1;
+            const int n = (b % (BN / 16)) * 16 + (lane & 15);
+            bs[j] = qm + (size_t)e * a.qstride + (size_t)(n0 + n) * (size_t)(a.K / 2) + (lane >> 4) * 16;
+        }
+        auto issue2 = [&](int kt) {
+            uint8_t *base = smem3 + (kt % NS) * SBY;
+#pragma unroll
+            for (int j = 0; j < MV; ++j) lds_copy16(as[j] + (size_t)kt * 256, base + (wn + 4 * j) * 1024);
+#pragma unroll
+            for (int j = 0; j < BJ; ++j) lds_copy16(bs[j] + (size_t)kt * 64, base + ABY + (wn + 4 * j) * 1024);
+        };
+#pragma unroll
+        for (int s0 = 0; s0 < NS - 1; ++s0)
+            if (s0 < KT2) issue2(s0);
+        for (int kt = 0; kt < KT2; ++kt) {
+            wait_stages<PW, NS - 2>(KT2 - 1 - kt);
+            ring_barrier();
+            if (kt + NS - 1 < KT2) issue2(kt + NS - 1);
+            const uint8_t *sa = smem3 + (kt % NS) * SBY;
+            // this wave's weight blocks: matrix x, column block wn * NB + j
+            u32x4 bw[NMAT][NB];
+#pragma unroll
+            for (int x = 0; x < NMAT; ++x)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    bw[x][j] = *(const u32x4 *)(sa + ABY + (x * (BN / 16) + wn * NB + j) * 1024 + lane * 16);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int chunk = 4 * (lane >> 4) + jj;
+                u32x4 af[MV];
+#pragma unroll
+                for (int i = 0; i < MV; ++i) {
+                    const int r = i * 16 + (lane & 15);
+                    af[i] = *(const u32x4 *)(sa + r * 256 + ((chunk ^ (r & 15)) * 16));
+                }
+#pragma unroll
+                for (int c = 0; c < CB; ++c) {
+                    if (4 * c >= MV) break;
+                    if (4 * c + 3 >= MV && wu + 4 * c >= MV) continue;
+                    const int r = (wn + 4 * c) * 16 + (lane & 15);
+                    cor[c] = mma(cneg, *(const u32x4 *)(sa + r * 256 + ((chunk ^ (r & 15)) * 16)), cor[c]);
+                }
+#pragma unroll
+                for (int x = 0; x < NMAT; ++x)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        const u32x4 bf = F16 ? unpack_int4x8_f16(bw[x][j][jj]) : unpack_int4x8_nat(bw[x][j][jj]);
+#pragma unroll
+                        for (int i = 0; i < MV; ++i) acc[x][i][j] = mma(bf, af[i], acc[x][i][j]);
+                    }
+            }
+        }
+    };
     const int mv = (rows + 15) / 16;  // 1 .. MB
+    if constexpr (WBITS == 4 && MB == 8) {
+        if (a.K % 128 == 0 && mv <= 5) {
+            switch (mv) {
+            case 1: kloop128(IntC<1>{}); break;
+            case 2: kloop128(IntC<2>{}); break;
+            case 3: kloop128(IntC<3>{}); break;
+            case 4: kloop128(IntC<4>{}); break;
+            default: kloop128(IntC<5>{}); break;
+            }
+            goto epilogue;
+        }
+    }
     if constexpr (MB == 4) {
         switch (mv) {
         case 1: kloop(IntC<1>{}); break;
@@ -473,6 +584,7 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
         }
     }
 
+epilogue:
     // Epilogue.  Lane l holds, for block (i, j), row m = 16 i + l % 16 and the
     // columns 4 (l / 16) .. 4 (l / 16) + 3 of its 16 x 16 block; the offset
     // correction of every row comes back from sCor.
@@ -633,7 +745,7 @@ static hipError_t launch_three(const FfnArgs &a, int slots, hipStream_t st)
     const int NT = a.N / 128;
     const long grid = (long)((slots + 7) / 8 * 8) * NT;
     if (grid <= 0) return hipSuccess;
-    const size_t lds = (size_t)Ff3<MODE, WBITS, BM>::NST * Ff3<MODE, WBITS, BM>::STAGE;
+    const size_t lds = (size_t)Ff3<MODE, WBITS, BM>::RING;
     hipLaunchKernelGGL((k_ffn3<MODE, WBITS, BM>), dim3((unsigned)grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }

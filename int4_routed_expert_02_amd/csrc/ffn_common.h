@@ -98,6 +98,9 @@ struct Ff3 {
     // workgroups per compute unit (deeper rings measured slower)
     static constexpr int NST = STAGE <= 24 * 1024 ? 3 : 2;
     static_assert(PER_WAVE * (NST - 2) < 64, "vmcnt range");
+    // LDS of the ring (the launch's dynamic LDS); tiles of fewer valid rows
+    // lay out more, smaller stages in it
+    static constexpr int RING = NST * STAGE;
 };
 
 __device__ __forceinline__ void lds_copy16(const void *g, void *l)
