@@ -98,6 +98,9 @@ def parse():
                     help="time the per-row int4 quantiser on the GLM-class routed gate/up weights instead")
     ap.add_argument("--bias-update", action="store_true",
                     help="time the aux-loss-free bias update (E = 256) instead")
+    ap.add_argument("--regime-sweep", action="store_true",
+                    help="time the small-batch and the tiled regime at the Nano layer shape over T (cold weights) "
+                         "instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB, 5 times (counter calibration), and exit")
     return ap.parse_args()
@@ -135,6 +138,8 @@ def main():
         return bench_quantize(args, moe, torch, np)
     if args.bias_update:
         return bench_bias_update(args, moe, torch, np)
+    if args.regime_sweep:
+        return bench_regime_sweep(args, moe, synth, torch, np, dev)
 
     def variant(cfg):
         if args.top_p:
@@ -442,6 +447,62 @@ def bench_c0(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread):
     if cpu1 is not None:
         line["cpu_baseline_1thread"] = cpu1
     return line
+
+
+def bench_regime_sweep(args, moe, synth, torch, np, dev):
+    """Where the small-batch regime stops paying: one Nano-shape layer
+    (moe_layer_forward, bf16 out) over T, with the weights of `cold_copies`
+    identical layer copies rotated (no weight in the last-level cache when it
+    is read), in the small-batch regime (T <= 32, the default there) and in
+    the tiled regime (MOE_REGIME_TILED).  Each point is a HIP graph of one
+    call per copy; time per layer = graph time / copies."""
+    base = synth.CONFIGS["c0"]
+    n = args.cold_copies
+    Tmax = 256
+    d = synth.layer(base.with_(T=Tmax))
+    copies = [moe.MoeLayer(base, d, dev) for _ in range(n)]
+    xall = torch.from_numpy(d["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
+    stream = torch.cuda.Stream(device=dev)
+    rows = []
+    for T in (1, 2, 4, 8, 16, 24, 32, 40, 48, 64, 96, 128, 192, 256):
+        x = xall[:T].contiguous()
+        point = {"T": T}
+        for name, fl in (("small_batch", 0), ("tiled", moe.MOE_REGIME_TILED)):
+            sh = moe.shape_of(base, T, fl)
+            if name == "small_batch" and moe.moe_layer_routing(sh, copies[0].workspace(T, fl))[2] is not None:
+                continue  # the small-batch regime does not serve this T
+            outs = [torch.empty((T, base.H), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+            wss = [c.workspace(T, fl) for c in copies]
+            with torch.cuda.stream(stream):
+                for i, c in enumerate(copies):
+                    c.forward(x, outs[i], wss[i], fl, stream=stream)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i, c in enumerate(copies):
+                    c.forward(x, outs[i], wss[i], fl, stream=stream)
+            torch.cuda.synchronize()
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                for _ in range(args.steps):
+                    g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (args.steps * n)
+            point[name + "_us"] = round(us, 2)
+            point[name + "_tok_s"] = round(T / (us * 1e-6), 1)
+            del g, outs, wss
+        rows.append(point)
+        progress(f"regime sweep {point}")
+    line = {"metric": "MoE-layer time per call by regime (Nano shape, cold weights)", "unit": "us",
+            "config": {"workload": "one Nano-shape layer (H=1024, E=64 top-2, I=512, int4 shared I=2048) over T",
+                       "rotated_weight_copies": n},
+            "points": rows}
+    print(json.dumps(line), flush=True)
 
 
 def bench_quantize(args, moe, torch, np):

@@ -94,6 +94,11 @@ extern "C" {
 #define MOE_EXPERT_MIXED 0x2000u /* routed experts in int4 or int2 per weights->expert_bits (the tiled kernels at
                                any T; with MOE_ACT_Q8, MOE_TEST_GATEUP_SUMS or in a chained call:
                                MOE_ERR_UNSUPPORTED) */
+#define MOE_REGIME_TILED 0x4000u /* moe_layer_forward(_profiled, _noalloc): take the tiled grouped-GEMM kernels at
+                               any T (the small-batch weight-streaming kernels are otherwise chosen for
+                               the shapes moe_layer_routing names); for measuring the two regimes side by
+                               side.  With MOE_STAGE_EXPERTS_ONLY, MOE_LOGITS_GIVEN or in a chained call:
+                               MOE_ERR_UNSUPPORTED */
 #define MOE_TEST_GATEUP_SUMS 0x100u /* moe_expert_ffn, testing only: write the raw integer-weight sums
                                sum_h x*q of gate into y_pairs[r][0:I] and of up into y_pairs[r][I:2I]
                                (no scale, no activation, no down projection); needs 2*I <= H, int4 */

@@ -563,6 +563,19 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
             goto epilogue;
         }
     }
+    if constexpr (WBITS == 4 && MB == 4 && MODE == 1) {
+        // the down GEMM's 64-row tiles: 128-k stages throughout (its 64-k
+        // stages carry too few MFMAs per barrier and per LDS round trip)
+        if (a.K % 128 == 0) {
+            switch (mv) {
+            case 1: kloop128(IntC<1>{}); break;
+            case 2: kloop128(IntC<2>{}); break;
+            case 3: kloop128(IntC<3>{}); break;
+            default: kloop128(IntC<4>{}); break;
+            }
+            goto epilogue;
+        }
+    }
     if constexpr (MB == 4) {
         switch (mv) {
         case 1: kloop(IntC<1>{}); break;

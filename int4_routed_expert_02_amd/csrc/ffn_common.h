@@ -99,8 +99,10 @@ struct Ff3 {
     static constexpr int NST = STAGE <= 24 * 1024 ? 3 : 2;
     static_assert(PER_WAVE * (NST - 2) < 64, "vmcnt range");
     // LDS of the ring (the launch's dynamic LDS); tiles of fewer valid rows
-    // lay out more, smaller stages in it
-    static constexpr int RING = NST * STAGE;
+    // lay out more, smaller stages in it.  The int4 down GEMM of 64-row tiles
+    // gets 48 KB, room for two of its 128-k stages (three workgroups still fit
+    // a compute unit, as many as its registers allow)
+    static constexpr int RING = (MODE == 1 && BM == 64 && WBITS == 4) ? 48 * 1024 : NST * STAGE;
 };
 
 __device__ __forceinline__ void lds_copy16(const void *g, void *l)

@@ -120,7 +120,7 @@ struct Layout {
 
 bool use_decode(const moe_shape *s)
 {
-    if (s->flags & (MOE_ACT_Q8 | MOE_EXPERT_MIXED)) return false;  // these modes run the tiled kernels
+    if (s->flags & (MOE_ACT_Q8 | MOE_EXPERT_MIXED | MOE_REGIME_TILED)) return false;  // the tiled kernels
     return moe::decode_supported(s->T, s->H, s->E, s->top_k, s->I, s->I_shared, s->shared_bits);
 }
 

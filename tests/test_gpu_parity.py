@@ -58,6 +58,19 @@ def test_layer_parity_small(name):
     check_output(cfg, d, d["hidden"], got, ex, tag=f"{name} (exempt {int(ex.sum())})")
 
 
+@pytest.mark.parametrize("T", [1, 16, 32])
+def test_regime_tiled_flag_at_small_T(T):
+    """MOE_REGIME_TILED runs the tiled kernels where the small-batch regime
+    would serve the shape: the same bar against the oracle, and the
+    permutation is materialised."""
+    cfg = synth.CONFIGS["c0"].with_(T=T, seed=90 + T)
+    d = synth.layer(cfg)
+    got, ids, w, offsets, srt = run_layer(cfg, d, flags=moe.MOE_OUT_F32 | moe.MOE_REGIME_TILED)
+    assert offsets is not None and srt is not None
+    ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag=f"tiled T={T}")
+    check_output(cfg, d, d["hidden"], got, ex, tag=f"tiled T={T}")
+
+
 @pytest.mark.parametrize("cfg", [small_cfg(T=300, E=16), synth.CONFIGS["c0"].with_(T=32, E=16, seed=33)],
                          ids=["generic_T300", "decode_T32"])
 def test_many_rows_per_expert_and_empty_experts(cfg):
