@@ -715,7 +715,7 @@ static hipError_t launch_three_mix(const FfnArgs &a, int slots, hipStream_t st)
     if (grid <= 0) return hipSuccess;
     using C4 = Ff3<MODE, 4, BM>;
     using C2 = Ff3<MODE, 2, BM>;
-    const size_t l4 = (size_t)C4::NST * C4::STAGE, l2 = (size_t)C2::NST * C2::STAGE;
+    const size_t l4 = (size_t)C4::RING, l2 = (size_t)C2::RING;  // the larger ring of the two formats
     hipLaunchKernelGGL((k_ffn3_mix<MODE, BM>), dim3((unsigned)grid), dim3(256), l4 > l2 ? l4 : l2, st, a);
     return hipGetLastError();
 }
