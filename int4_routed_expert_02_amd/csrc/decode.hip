@@ -30,6 +30,8 @@
 // groups read 64 contiguous bytes of each row per instruction.  The k-slots
 // of chunk c, word w for lane group g are k = (4c + g) * 32 + 8w + [0, 8)
 // (int4), and the A fragments are read from LDS at the same k.
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_launch.h"
 #include "moe_select.h"
@@ -233,9 +235,9 @@ __device__ __forceinline__ void dec_select_lanes(const float *__restrict__ zp, c
         f32x4 pa[LG_NP][2];
 #pragma unroll
         for (int p = 0; p < LG_NP; ++p) {
-            const f32x4 *pp = (const f32x4 *)(zp + ((size_t)p * T + t) * E + 8 * q);
-            pa[p][0] = pp[0];
-            pa[p][1] = pp[1];
+            const float *pz = zp + ((size_t)p * T + t) * E + 8 * q;
+            pa[p][0] = *(const f32x4 *)pz;
+            pa[p][1] = *(const f32x4 *)(pz + 4);
         }
         const f32x4 b0 = *(const f32x4 *)(bias + 8 * q), b1 = *(const f32x4 *)(bias + 8 * q + 4);
 #pragma unroll
@@ -347,18 +349,24 @@ struct PairRows {
 template <int EW>
 __device__ __forceinline__ int2 dec_locate_wave(const int32_t *ids, int P, int k, int E, int rank, PairRows &pr)
 {
+    constexpr int MAXC = DEC_MAXT * DEC_MAXK / WAVE;  // 64-pair chunks of the batch
     const int lane = threadIdx.x & 63;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes below this one
+    // every chunk's ids read once, kept in registers
+    int ev[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int p = c * WAVE + lane;
+        ev[c] = c * WAVE < P && p < P ? ids[p] : -1;
+    }
     uint32_t m[2 * EW];
 #pragma unroll
     for (int w = 0; w < 2 * EW; ++w) m[w] = 0;
-    for (int p0 = 0; p0 < P; p0 += WAVE) {
-        const int p = p0 + lane;
-        const int e = p < P ? ids[p] : -1;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
 #pragma unroll
         for (int w = 0; w < 2 * EW; ++w)
-            if ((unsigned)(e - 32 * w) < 32u && e < E) m[w] |= 1u << (e - 32 * w);
-    }
+            if ((unsigned)(ev[c] - 32 * w) < 32u && ev[c] < E) m[w] |= 1u << (ev[c] - 32 * w);
     int found = -1, before = 0;
 #pragma unroll
     for (int w = 0; w < EW; ++w) {
@@ -382,17 +390,19 @@ __device__ __forceinline__ int2 dec_locate_wave(const int32_t *ids, int P, int k
     int n = 0;
     pr = PairRows{0, 0, 0.f};
     if (found >= 0) {
-        for (int p0 = 0; p0 < P; p0 += WAVE) {
-            const int p = p0 + lane;
-            const bool hit = p < P && ids[p] == found;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            if (c * WAVE >= P) break;
+            const int p = c * WAVE + lane;
+            const bool hit = ev[c] == found;
             const uint64_t bm = __ballot(hit);
             // forward permute: a hit lane sends its pair to lane n + (hits below it);
             // the others to lane 63, which no pair row reaches (n <= T <= 32)
             const int dst = hit ? n + __popcll(bm & lt) : 63;
             const int got = __builtin_amdgcn_ds_permute(dst * 4, p);
-            const int c = __popcll(bm);
-            if (lane >= n && lane < n + c) pr.pair = got;
-            n += c;
+            const int cn = __popcll(bm);
+            if (lane >= n && lane < n + cn) pr.pair = got;
+            n += cn;
         }
         if (lane < n) pr.tok = pr.pair / k;
     }
@@ -418,9 +428,10 @@ struct DecArgs {
     const uint8_t *sgq, *suq, *sdq;
     const float *sgs, *sus, *sds;
     int Ish, sh_bits;
-    // partial expert outputs, one plane per 128-row unit of the intermediate
-    float *yp;   // [I/128][T*k][H]   routed, scaled by rsf * w
-    float *ysp;  // [Ish/128][T][H]   shared
+    // partial expert outputs, one plane per 128-row unit of the intermediate,
+    // f16 (each partial rounded once to nearest even)
+    uint16_t *yp;   // [I/128][T*k][H]   routed, scaled by rsf * w
+    uint16_t *ysp;  // [Ish/128][T][H]   shared
 };
 
 // The routing decision of the batch into LDS (every routed workgroup takes
@@ -462,6 +473,15 @@ constexpr int DX_RCOLS = DX_WAVES * DX_WCOLS;       // output columns per round 
 constexpr int DX_LDY = DX_WCOLS + 4;                // padded row of a wave's staged down tile (floats)
 constexpr int GU_CPL = 8;                           // 16-byte gate/up chunks per lane per row per super-stage
 constexpr int GU_AHEAD = 4;                         // gate/up chunks in flight ahead of the MFMAs
+
+// s_waitcnt for at most N outstanding vector-memory operations of the wave
+// (gfx9 encoding; expcnt and lgkmcnt not waited for)
+template <int N>
+__device__ __forceinline__ void dx_wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 // Down weights of one round: lane (n, g) holds, for each of its wave's 8
 // output tiles tt, the 32 values of intermediate [32g, 32g + 32) of the
@@ -589,7 +609,7 @@ template <int WBITS, int NMB>
 __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm, int n, int nr, const PairRows &pr,
                                             float rsum, const uint8_t *grow, const uint8_t *urow, float sg,
                                             float su, const uint8_t *dq, const float *dsc, int64_t drstride,
-                                            int i0, float *out, int nrows)
+                                            int i0, uint16_t *out, int nrows)
 {
     constexpr int CPL = GU_CPL;
     constexpr int SB = CPL * 64;           // weight bytes of a row per super-stage (512)
@@ -612,7 +632,11 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
     DownW<WBITS> dw;
     f32x4 sdv;
     u32x4 wg[CPL], wu[CPL];
-    for (int ss = 0; ss < nss; ++ss) {
+    // One super-stage; the last one (a separate instance, LAST set) also
+    // issues the down slice, so its loads stay where they are written
+    // instead of moving to the loop's exit, behind the gate/up MFMAs.
+    auto super_stage = [&](int ss, auto lastc) {
+        constexpr bool LAST = decltype(lastc)::value;
         // gate and up chunk c in adjacent requests: the MFMAs on chunk c can
         // start once its pair has arrived
         auto issue_gu = [&](int c) {
@@ -629,7 +653,11 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
         for (int c = 0; c < GU_AHEAD; ++c) issue_gu(c);
         if (ss > 0) __syncthreads();  // the previous super-stage's A reads are done
         xstage_store<WBITS>(xs, sm, nr, rsum);
-        if (ss == nss - 1) {
+        // every load older than these gate/up chunks (the activation rows, the
+        // row scales) has landed: waited for here by every wave, so the
+        // epilogue does not wait on the counter for the down slice
+        dx_wait_vm<2 * GU_AHEAD>();
+        if (LAST) {
             // row sums: the TPR threads of a staged row are consecutive lanes
             float s = rsum;
 #pragma unroll
@@ -640,7 +668,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             if (c + GU_AHEAD < CPL) issue_gu(c + GU_AHEAD);
-            else if (ss == nss - 1 && c + GU_AHEAD == CPL) {
+            else if (LAST && c + GU_AHEAD == CPL) {
                 load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, wave * DX_WCOLS, i0);
                 asm volatile("" ::: "memory");  // keeps the compiler from sinking these loads to their use
             }
@@ -670,7 +698,9 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
                 }
             }
         }
-    }
+    };
+    for (int ss = 0; ss < nss - 1; ++ss) super_stage(ss, std::false_type{});
+    super_stage(nss - 1, std::true_type{});
     // SwiGLU epilogue: h for (row m, intermediate wave * 16 + ln) -> on-chip
     // chunk in f16 (round to nearest even).
     const float bias = (WBITS == 4) ? INT4_BIAS : 0.f;
@@ -743,7 +773,8 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
                     f32x4 o;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) o[q] = v[q] * sdv[q] * osc;
-                    *(f32x4 *)(out + ((size_t)chunk * nrows + prow) * a.H + col0 + q4) = o;
+                    *(u32x2 *)(out + ((size_t)chunk * nrows + prow) * a.H + col0 + q4) =
+                        u32x2{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])};
                 }
             }
         }
@@ -801,7 +832,7 @@ __global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nun
         drs = (int64_t)K * WBITS / 8;
     };
     int n, nrows, nr;
-    float *out;
+    uint16_t *out;
     const float rsum = 0.f;
     if (shared) {
         // 16 tokens of one half: staged rows r = pair rows r = token 16 th + r
@@ -852,13 +883,46 @@ __device__ __forceinline__ uint32_t dec_dropped_slots(const int32_t *ids, int t,
     return m;
 }
 
+// The four f16 columns at c of this lane's planes p0, p0 + CB_SPLIT, ...
+// (MAXL of them): every load is issued, unconditionally, before any result
+// is used (a plane that is absent, past the last or dropped by top-p reads
+// a valid address and is marked unused), so the MAXL requests are in flight
+// together instead of one after another.
+template <int MAXL>
+__device__ __forceinline__ void dec_plane_loads(u32x2 (&hv)[MAXL], bool (&use)[MAXL], const uint16_t *yp,
+                                                const uint16_t *ysp, bool live, int p0, int np, int nrp, int nkr,
+                                                uint32_t dropped, size_t P, int T, int t, int k, int H, int c)
+{
+    // routed plane p is chunk p % nkr of the pair in slot p / nkr; the lane's
+    // planes step by CB_SPLIT <= nkr, so chunk and slot advance without a
+    // division.  Offsets are in elements (32 bits: the planes of this regime
+    // hold well under 2^31 of them).
+    int ch = p0 % nkr, j = p0 / nkr;
+    const uint32_t rbase = (uint32_t)((size_t)t * k * H + c), sbase = (uint32_t)((size_t)t * H + c);
+    const uint32_t rstep = (uint32_t)(P * H), sstep = (uint32_t)T * H;
+#pragma unroll
+    for (int i = 0; i < MAXL; ++i) {
+        const int p = p0 + CB_SPLIT * i;
+        use[i] = live && p < np && !(p < nrp && ((dropped >> j) & 1u));
+        const uint16_t *src = !use[i] ? yp
+                              : p < nrp ? yp + (rbase + (uint32_t)ch * rstep + (uint32_t)j * H)
+                                        : ysp + (sbase + (uint32_t)(p - nrp) * sstep);
+        hv[i] = *(const u32x2 *)src;
+        ch += CB_SPLIT;
+        if (ch >= nkr) {
+            ch -= nkr;
+            ++j;
+        }
+    }
+}
+
 // out[t] = sum over partial planes (routed pairs of t in order j, their
 // chunks in order; then the shared expert's chunks) (+ x[t]).  Four
 // consecutive lanes own one 4-column quad: lane q sums planes q, q + 4, ...
 // with all its loads in flight together, then the four sums are added in
 // lane order.  Fixed order throughout.
-__global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ yp, int nkr,
-                                                     const float *__restrict__ ysp, int nks,
+__global__ __launch_bounds__(256) void k_dec_combine(const uint16_t *__restrict__ yp, int nkr,
+                                                     const uint16_t *__restrict__ ysp, int nks,
                                                      const uint16_t *__restrict__ res, void *__restrict__ out, int T,
                                                      int H, int k, int out_f32, const int32_t *__restrict__ ids)
 {
@@ -874,22 +938,32 @@ __global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ y
     const int nrp = k * nkr, np = nrp + nks;
     const uint32_t dropped = dec_dropped_slots(ids, live ? t : 0, k);
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int p0 = q; p0 < np; p0 += CB_SPLIT * MAXL) {
-        f32x4 v[MAXL];
+    auto add_planes = [&](const u32x2 (&hv)[MAXL], const bool (&use)[MAXL]) {
 #pragma unroll
         for (int i = 0; i < MAXL; ++i) {
-            const int p = p0 + CB_SPLIT * i;
-            v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (live && p < np && !(p < nrp && ((dropped >> (p / nkr)) & 1u))) {
-                const float *src = p < nrp ? yp + ((size_t)(p % nkr) * P + (size_t)t * k + p / nkr) * H + c
-                                           : ysp + ((size_t)(p - nrp) * T + t) * H + c;
-                v[i] = *(const f32x4 *)src;
-            }
+            const f32x4 v = use[i] ? f32x4{f16_lo(hv[i][0]), f16_hi(hv[i][0]), f16_lo(hv[i][1]), f16_hi(hv[i][1])}
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += v[e];
         }
-#pragma unroll
-        for (int i = 0; i < MAXL; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += v[i][e];
+    };
+    u32x2 rv = u32x2{0u, 0u};
+    if (np <= CB_SPLIT * MAXL) {
+        // one batch (up to 64 planes): straight-line, the residual in flight
+        // with the planes
+        u32x2 hv[MAXL];
+        bool use[MAXL];
+        dec_plane_loads<MAXL>(hv, use, yp, ysp, live, q, np, nrp, nkr, dropped, P, T, t, k, H, c);
+        rv = *(const u32x2 *)(res ? res + (size_t)t * H + c : yp);  // (used only with res)
+        add_planes(hv, use);
+    } else {
+        for (int p0 = q; p0 < np; p0 += CB_SPLIT * MAXL) {
+            u32x2 hv[MAXL];
+            bool use[MAXL];
+            dec_plane_loads<MAXL>(hv, use, yp, ysp, live, p0, np, nrp, nkr, dropped, P, T, t, k, H, c);
+            add_planes(hv, use);
+        }
+        if (res) rv = *(const u32x2 *)(res + (size_t)t * H + c);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -900,7 +974,7 @@ __global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ y
     }
     if (!live || q != 0) return;
     if (res) {
-        const u32x2 v = *(const u32x2 *)(res + (size_t)t * H + c);
+        const u32x2 v = rv;
         acc[0] += bf16_lo(v[0]);
         acc[1] += bf16_hi(v[0]);
         acc[2] += bf16_lo(v[1]);
@@ -913,65 +987,54 @@ __global__ __launch_bounds__(256) void k_dec_combine(const float *__restrict__ y
     }
 }
 
-// Chained decode: k_dec_combine (same grid, lanes and plane order, so the
-// bf16 output is the same bits) that also takes the next layer's router
-// logits of its output, in the 4-plane form k_dec_expert reads.  Workgroup
-// (token t, quarter g) covers columns [g H/4, (g+1) H/4): once the quarter of
-// the output row is in LDS (as the next layer reads it, bf16), four
-// consecutive threads take one expert, thread j of the four the j-th quarter
-// of those columns (contiguous, 16-byte W loads; for H = 1024 the W values
-// are loaded before the combine, while the planes are in flight); fused
-// multiply-adds in column order, then the four partial sums in a fixed
-// two-step tree; the sum goes to plane g.  The next layer adds the 4 planes
-// as it does its own logits kernel's.
-constexpr int CL_VEC = 16;  // 16-byte W loads per thread held across the combine (64 columns)
+// Chained decode: k_dec_combine (same lanes and plane order per output
+// quad, so the bf16 output is the same bits) that also takes the next
+// layer's router logits of the row it writes, in the 4-plane form
+// k_dec_expert reads.  Workgroup (token t, quarter g) covers columns
+// [g H/4, (g+1) H/4): once that quarter of the output row is in LDS (as the
+// next layer reads it, bf16), sixteen consecutive threads take an expert,
+// thread j the 4-column groups j, j + 16, ... of the quarter (16-byte W
+// loads, sixteen threads on 256 contiguous bytes), four experts per thread
+// per round of 64; fused multiply-adds in that order, then the sixteen
+// partial sums in a fixed butterfly; the sum goes to plane g.  The next
+// layer adds the 4 planes as it does its own logits kernel's.  For H = 1024
+// the first round's W values are loaded with the planes, before the combine.
+constexpr int CL_SUBS = 16;  // threads per expert in the logits
+constexpr int CL_EPT = 4;    // experts per thread per round (64 per round)
+constexpr int CL_GPT = 4;    // 4-column groups per thread per expert (H = 1024: a quarter is 64 groups)
 
-__global__ __launch_bounds__(256) void k_dec_combine_logits(const float *__restrict__ yp, int nkr,
-                                                            const float *__restrict__ ysp, int nks,
-                                                            const uint16_t *__restrict__ res,
+__global__ __launch_bounds__(256) void k_dec_combine_logits(const uint16_t *__restrict__ yp, int nkr,
+                                                            const uint16_t *__restrict__ ysp, int nks,
+                                                            const uint16_t *res,  // (not restrict: its load
+                                                                                  // stays before the W loads)
                                                             uint16_t *__restrict__ out, int T, int H, int k,
                                                             const float *__restrict__ nrw, int nE,
                                                             float *__restrict__ nzp, const int32_t *__restrict__ ids)
 {
     static_assert(DEC_LOGIT_PLANES == 4, "one plane per quarter of the row");
     extern __shared__ float xq[];  // [H / 4] this quarter of the output row
-    constexpr int MAXL = 16;
+    constexpr int MAXL = 16, MAXF = 8;  // planes per lane per batch (generic path, straight-line path)
     const int tid = threadIdx.x;
     const int t = blockIdx.x / 4, g = blockIdx.x % 4;
     const int H4 = H / 4, c0 = g * H4;
-    const int ncs = H4 / 4;  // columns per thread (one expert per four threads)
-    const int sub = tid & 3;
-    const bool pre = ncs == 4 * CL_VEC;
-    f32x4 wv[CL_VEC];
-    if (pre) {
-        const float *wr = nrw + (size_t)min(tid >> 2, nE - 1) * H + c0 + sub * ncs;
-#pragma unroll
-        for (int i = 0; i < CL_VEC; ++i) wv[i] = *(const f32x4 *)(wr + 4 * i);
-    }
+    const int sub = tid % CL_SUBS, ex = tid / CL_SUBS;  // logits: experts ex + 16 i of the round, thread sub
+    bool pre = false;                                   // wv holds the first round's W values
+    f32x4 wv[CL_EPT][CL_GPT];
     const size_t P = (size_t)T * k;
     const int nrp = k * nkr, np = nrp + nks;
     const uint32_t dropped = dec_dropped_slots(ids, t, k);
-    for (int qd0 = 0; qd0 < H4 / 4; qd0 += 256 / CB_SPLIT) {
-        const int quad = qd0 + tid / CB_SPLIT, q = tid % CB_SPLIT;
-        const int c = c0 + quad * 4;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int p0 = q; p0 < np; p0 += CB_SPLIT * MAXL) {
-            f32x4 v[MAXL];
+    auto add_planes = [&](f32x4 &acc, const auto &hv, const auto &use) {
 #pragma unroll
-            for (int i = 0; i < MAXL; ++i) {
-                const int p = p0 + CB_SPLIT * i;
-                v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (p < np && !(p < nrp && ((dropped >> (p / nkr)) & 1u))) {
-                    const float *src = p < nrp ? yp + ((size_t)(p % nkr) * P + (size_t)t * k + p / nkr) * H + c
-                                               : ysp + ((size_t)(p - nrp) * T + t) * H + c;
-                    v[i] = *(const f32x4 *)src;
-                }
-            }
+        for (int i = 0; i < (int)(sizeof(use) / sizeof(use[0])); ++i) {
+            const f32x4 v = use[i] ? f32x4{f16_lo(hv[i][0]), f16_hi(hv[i][0]), f16_lo(hv[i][1]), f16_hi(hv[i][1])}
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < MAXL; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] += v[i][e];
+            for (int e = 0; e < 4; ++e) acc[e] += v[e];
         }
+    };
+    // the four lanes' sums in lane order, + the residual, out in bf16 and
+    // into LDS as the next layer reads it
+    auto finish = [&](f32x4 acc, int quad, int q, int c, u32x2 r) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float s1 = __shfl_down(acc[e], 1, WAVE);
@@ -981,7 +1044,6 @@ __global__ __launch_bounds__(256) void k_dec_combine_logits(const float *__restr
         }
         if (q == 0) {
             if (res) {
-                const u32x2 r = *(const u32x2 *)(res + (size_t)t * H + c);
                 acc[0] += bf16_lo(r[0]);
                 acc[1] += bf16_hi(r[0]);
                 acc[2] += bf16_lo(r[1]);
@@ -989,38 +1051,89 @@ __global__ __launch_bounds__(256) void k_dec_combine_logits(const float *__restr
             }
             const u32x2 o = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
             *(u32x2 *)(out + (size_t)t * H + c) = o;
-            float *x = xq + quad * 4;
+            float *x = xq + (c - c0);
             x[0] = bf16_lo(o[0]);
             x[1] = bf16_hi(o[0]);
             x[2] = bf16_lo(o[1]);
             x[3] = bf16_hi(o[1]);
         }
+    };
+    const int nquad = H4 / 4;
+    if (nquad == 256 / CB_SPLIT && np <= CB_SPLIT * MAXF) {
+        // H = 1024 (one quad per four threads), one batch of up to 32
+        // planes: straight-line code, the planes and the residual first, then
+        // the W values of the first 64 experts, all in flight together (no
+        // load is conditional, so waiting for the planes does not wait for W)
+        const int quad = tid / CB_SPLIT, q = tid % CB_SPLIT;
+        const int c = c0 + quad * 4;
+        u32x2 hv[MAXF];
+        bool use[MAXF];
+        dec_plane_loads<MAXF>(hv, use, yp, ysp, true, q, np, nrp, nkr, dropped, P, T, t, k, H, c);
+        const u32x2 r = *(const u32x2 *)(res ? res + (size_t)t * H + c : yp);  // (used only with res)
+        asm volatile("" ::: "memory");  // the W loads after the planes (they complete in issue order)
+        static_assert(CL_GPT * 4 * CL_SUBS == 256, "a quarter of a 1024-column row");
+#pragma unroll
+        for (int i = 0; i < CL_EPT; ++i) {
+            const float *wr = nrw + (size_t)min(ex + 16 * i, nE - 1) * H + c0 + 4 * sub;
+#pragma unroll
+            for (int j = 0; j < CL_GPT; ++j) wv[i][j] = *(const f32x4 *)(wr + 4 * CL_SUBS * j);
+        }
+        pre = true;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        add_planes(acc, hv, use);
+        finish(acc, quad, q, c, r);
+    } else {
+        for (int qd0 = 0; qd0 < nquad; qd0 += 256 / CB_SPLIT) {
+            const int quad = qd0 + tid / CB_SPLIT, q = tid % CB_SPLIT;
+            const bool lq = quad < nquad;
+            const int c = c0 + (lq ? quad : 0) * 4;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int p0 = q; p0 < np; p0 += CB_SPLIT * MAXL) {
+                u32x2 hv[MAXL];
+                bool use[MAXL];
+                dec_plane_loads<MAXL>(hv, use, yp, ysp, lq, p0, np, nrp, nkr, dropped, P, T, t, k, H, c);
+                add_planes(acc, hv, use);
+            }
+            const u32x2 r = *(const u32x2 *)(res ? res + (size_t)t * H + c : yp);
+            if (lq) finish(acc, quad, q, c, r);
+        }
     }
     __syncthreads();
     float *zp = nzp + ((size_t)g * T + t) * nE;
-    const float *xs = xq + sub * ncs;
-    for (int e0 = 0; e0 < nE; e0 += 64) {
-        const int e = e0 + (tid >> 2);
-        float z = 0.f;
+    const float *xs = xq + 4 * sub;
+    for (int e0 = 0; e0 < nE; e0 += CL_EPT * 16) {
+        float z[CL_EPT];
+#pragma unroll
+        for (int i = 0; i < CL_EPT; ++i) z[i] = 0.f;
         if (pre && e0 == 0) {
 #pragma unroll
-            for (int i = 0; i < CL_VEC; ++i)
+            for (int j = 0; j < CL_GPT; ++j) {
+                const f32x4 xv = *(const f32x4 *)(xs + 4 * CL_SUBS * j);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) z = fmaf(xs[4 * i + r], wv[i][r], z);
+                for (int i = 0; i < CL_EPT; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) z[i] = fmaf(xv[r], wv[i][j][r], z[i]);
+            }
         } else {
-            const float *wr = nrw + (size_t)min(e, nE - 1) * H + c0 + sub * ncs;
-            for (int i = 0; i < ncs; i += 4) {
-                const f32x4 w4 = *(const f32x4 *)(wr + i);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) z = fmaf(xs[i + r], w4[r], z);
+            for (int i = 0; i < CL_EPT; ++i) {
+                const float *wr = nrw + (size_t)min(e0 + ex + 16 * i, nE - 1) * H + c0 + 4 * sub;
+                for (int cc = 0; cc < H4; cc += 4 * CL_SUBS) {
+                    const f32x4 w4 = *(const f32x4 *)(wr + cc);
+                    const f32x4 xv = *(const f32x4 *)(xs + cc);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) z[i] = fmaf(xv[r], w4[r], z[i]);
+                }
             }
         }
-        const float z1 = __shfl_xor(z, 1, WAVE);
-        const float z2 = __shfl_xor(z, 2, WAVE);
-        const float z3 = __shfl_xor(z, 3, WAVE);
-        // the four partials added in the order of their column ranges
-        const float zt = sub == 0 ? ((z + z1) + z2) + z3 : 0.f;
-        if (sub == 0 && e < nE) zp[e] = zt;
+        // the sixteen partials in a fixed butterfly (the same sum in every lane)
+#pragma unroll
+        for (int i = 0; i < CL_EPT; ++i) {
+#pragma unroll
+            for (int o = 1; o < CL_SUBS; o <<= 1) z[i] += __shfl_xor(z[i], o, WAVE);
+            const int e = e0 + ex + 16 * i;
+            if (sub == 0 && e < nE) zp[e] = z[i];
+        }
     }
 }
 

@@ -153,8 +153,8 @@ Layout layout(const moe_shape *s, int which)
         L.w = take(P * 4);
         L.gap = take(T * 4);
         L.pscale = take(P * 4);
-        L.ypair = take((size_t)(s->I / moe::DEC_CHUNK_ROWS) * P * (size_t)s->H * 4);
-        if (s->shared_bits) L.shy = take((size_t)(s->I_shared / moe::DEC_CHUNK_ROWS) * T * (size_t)s->H * 4);
+        L.ypair = take((size_t)(s->I / moe::DEC_CHUNK_ROWS) * P * (size_t)s->H * 2);  // f16
+        if (s->shared_bits) L.shy = take((size_t)(s->I_shared / moe::DEC_CHUNK_ROWS) * T * (size_t)s->H * 2);
     } else {
         L.zpart = take((size_t)KS * T * E * 4);
         L.sbc = take(nsb * E * 4);
@@ -547,11 +547,11 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
             d.sgs = w->sh_gate.qs;
             d.sus = w->sh_up.qs;
             d.sds = w->sh_down.qs;
-            d.shp = at<float>(ws, L.shy);
+            d.shp = at<uint16_t>(ws, L.shy);
         }
         d.Ish = s->I_shared;
         d.sh_bits = s->shared_bits;
-        d.y = at<float>(ws, L.ypair);
+        d.y = at<uint16_t>(ws, L.ypair);
         d.res = (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr;
         d.out = out;
         d.out_f32 = (s->flags & MOE_OUT_F32) ? 1 : 0;

@@ -46,7 +46,7 @@ struct DecLaunch {
     const uint8_t *sgq, *suq, *sdq;
     const float *sgs, *sus, *sds;
     int Ish, sh_bits;
-    float *y, *shp;  // partial outputs: [I/128][T*k][H] routed, [I_shared/128][T][H] shared
+    uint16_t *y, *shp;  // f16 partial outputs: [I/128][T*k][H] routed, [I_shared/128][T][H] shared
     const uint16_t *res;
     void *out;
     int out_f32;
