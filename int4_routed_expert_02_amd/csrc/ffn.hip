@@ -332,12 +332,12 @@ __device__ __forceinline__ u32x4 weight_fragment(const uint8_t *bp)
 
 // One (m-tile, n-tile) of expert e in the WBITS format; smem3 / sCor: the
 // kernel's LDS (the stage ring, dynamic, and the row corrections).
-template <int MODE, int WBITS, int BM>
+template <int MODE, int WBITS, int BM, int BN = 128>
 __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int rows, int n0, uint8_t *smem3,
                                           float *sCor)
 {
-    using C = Ff3<MODE, WBITS, BM>;
-    constexpr int NMAT = C::NMAT, BN = C::BN, BKB = C::BKB;
+    using C = Ff3<MODE, WBITS, BM, BN>;
+    constexpr int NMAT = C::NMAT, BKB = C::BKB;
     constexpr bool F16 = (MODE == 1);   // down: A is f16 h, weights unpack to f16
     constexpr int MB = BM / 16;         // 16-row blocks, all in every wave
     constexpr int NB = BN / 4 / 16;     // 16-column blocks per wave and matrix
@@ -674,18 +674,18 @@ epilogue:
     }
 }
 
-template <int MODE, int WBITS, int BM>
+template <int MODE, int WBITS, int BM, int BN = 128>
 __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem3[];
     __shared__ float sCor[BM];
-    const int NT = a.N / Ff3<MODE, WBITS, BM>::BN;
+    const int NT = a.N / BN;
     const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
     const int nt = q % NT;
     const int slot = (q / NT) * 8 + xcd;
     int e, row0, rows;
     if (!find_tile<BM>(a, slot, e, row0, rows)) return;
-    ffn3_tile<MODE, WBITS, BM>(a, e, row0, rows, nt * Ff3<MODE, WBITS, BM>::BN, smem3, sCor);
+    ffn3_tile<MODE, WBITS, BM, BN>(a, e, row0, rows, nt * BN, smem3, sCor);
 }
 
 // A family whose experts are int4 or int2 each (a.ebits): the tile's expert
@@ -752,14 +752,14 @@ static hipError_t launch_one(const FfnArgs &a, int slots, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int MODE, int WBITS, int BM>
+template <int MODE, int WBITS, int BM, int BN = 128>
 static hipError_t launch_three(const FfnArgs &a, int slots, hipStream_t st)
 {
-    const int NT = a.N / 128;
+    const int NT = a.N / BN;
     const long grid = (long)((slots + 7) / 8 * 8) * NT;
     if (grid <= 0) return hipSuccess;
-    const size_t lds = (size_t)Ff3<MODE, WBITS, BM>::RING;
-    hipLaunchKernelGGL((k_ffn3<MODE, WBITS, BM>), dim3((unsigned)grid), dim3(256), lds, st, a);
+    const size_t lds = (size_t)Ff3<MODE, WBITS, BM, BN>::RING;
+    hipLaunchKernelGGL((k_ffn3<MODE, WBITS, BM, BN>), dim3((unsigned)grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
@@ -774,7 +774,15 @@ static hipError_t launch_mode(const FfnArgs &a, int rows_total, int groups, hipS
     const int slots = (rows_total + bm - 1) / bm + (a.offsets ? min(ng, rows_total) : 0);
     if (a.N % 128 == 0) {
         if (bm == 16) return launch_one<MODE, WBITS, 16, 128, 1, 4>(a, slots, st);
-        if (bm == 64) return launch_three<MODE, WBITS, 64>(a, slots, st);
+        if (bm == 64) {
+            // the int4 down GEMM of a wide output: 256-column tiles halve the
+            // re-reads of its activation rows (per tile as many bytes as its
+            // weights); measured faster at H = 6144, slower at H = 1024 (half
+            // the workgroups, two instead of three per compute unit)
+            if (MODE == 1 && WBITS == 4 && a.N % 256 == 0 && a.N >= 4096)
+                return launch_three<MODE, WBITS, 64, 256>(a, slots, st);
+            return launch_three<MODE, WBITS, 64>(a, slots, st);
+        }
         return launch_three<MODE, WBITS, 128>(a, slots, st);
     }
     if (bm == 16) return launch_one<MODE, WBITS, 16, 64, 1, 4>(a, slots, st);

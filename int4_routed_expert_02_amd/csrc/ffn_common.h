@@ -78,10 +78,10 @@ struct IntC {
     static constexpr int value = N;
 };
 
-template <int MODE, int WBITS, int BM>
+template <int MODE, int WBITS, int BM, int BN_ = 128>
 struct Ff3 {
     static constexpr int NMAT = (MODE == 1) ? 1 : 2;
-    static constexpr int BN = 128;
+    static constexpr int BN = BN_;  // output columns per matrix
     static constexpr int BKB = FF_BK * WBITS / 8;      // B bytes per row per stage
     static constexpr int A_BYTES = BM * FF_BK * 2;     // per stage
     static constexpr int B_BYTES = NMAT * BN * BKB;
@@ -100,9 +100,10 @@ struct Ff3 {
     static_assert(PER_WAVE * (NST - 2) < 64, "vmcnt range");
     // LDS of the ring (the launch's dynamic LDS); tiles of fewer valid rows
     // lay out more, smaller stages in it.  The int4 down GEMM of 64-row tiles
-    // gets 48 KB, room for two of its 128-k stages (three workgroups still fit
-    // a compute unit, as many as its registers allow)
-    static constexpr int RING = (MODE == 1 && BM == 64 && WBITS == 4) ? 48 * 1024 : NST * STAGE;
+    // gets room for two of its 128-k stages: 48 KB for 128 columns (three
+    // workgroups still fit a compute unit, as many as its registers allow),
+    // 64 KB for 256
+    static constexpr int RING = (MODE == 1 && BM == 64 && WBITS == 4) ? (BN == 256 ? 64 : 48) * 1024 : NST * STAGE;
 };
 
 __device__ __forceinline__ void lds_copy16(const void *g, void *l)

@@ -39,6 +39,9 @@ SMALL = {
     "c2_shape_T2000": synth.CONFIGS["c2"].with_(T=2000, seed=22),
     "c4_shape_T1500": synth.CONFIGS["c4"].with_(T=1500, seed=23),
     "c3_shape_T6": synth.CONFIGS["c3"].with_(T=6, seed=24),
+    # H = 6144 in the tiled regime with enough rows per expert for the
+    # 64-row down tiles of 256 columns (ragged groups, 300 tokens)
+    "c3_H6144_E32_T300": synth.CONFIGS["c3"].with_(T=300, E=32, k=4, n_group=4, topk_group=2, seed=30),
     # small-batch regime (T <= 32, H % 1024 == 0)
     "dec_c2_skew_T32": synth.CONFIGS["c2"].with_(T=32, seed=25),
     "dec_c4_int8_T24": synth.CONFIGS["c4"].with_(T=24, seed=26),
