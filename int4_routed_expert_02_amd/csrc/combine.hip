@@ -6,15 +6,26 @@
 // expert is always applied with weight 1 (NanoColibri README: a fat
 // always-resident shared expert).  The k routed terms are added in ascending j
 // order, then the shared term, then the residual: a fixed order, so the result
-// does not depend on scheduling.
+// does not depend on scheduling.  The layer's own routed and shared output
+// rows are f16 (each rounded once); those of the split API f32.
 #include "moe_device.h"
 
 namespace moe {
 
-// one thread per 4 consecutive columns of one token
-__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ y, const int32_t *__restrict__ inv,
+// Four consecutive values of a routed or shared output row: f32, or f16.
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *(const f32x4 *)p; }
+__device__ __forceinline__ f32x4 ld4(const uint16_t *p)
+{
+    const u32x2 h = *(const u32x2 *)p;
+    return f32x4{f16_lo(h[0]), f16_hi(h[0]), f16_lo(h[1]), f16_hi(h[1])};
+}
+
+// one thread per 4 consecutive columns of one token; YT: the element type of
+// the routed and shared output rows
+template <typename YT>
+__global__ __launch_bounds__(256) void k_combine(const YT *__restrict__ y, const int32_t *__restrict__ inv,
                                                  const float *__restrict__ topk_w, float rsf,
-                                                 const float *__restrict__ sh, const uint16_t *__restrict__ res,
+                                                 const YT *__restrict__ sh, const uint16_t *__restrict__ res,
                                                  void *__restrict__ out, int T, int H, int k, int out_f32)
 {
     const long idx = (long)blockIdx.x * 256 + threadIdx.x;
@@ -27,12 +38,12 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ y, co
         const int p = t * k + j;
         if (inv[p] < 0) continue;  // a pair dropped by adaptive top-p
         const float coef = topk_w ? rsf * topk_w[p] : 1.f;
-        const f32x4 v = *(const f32x4 *)(y + (size_t)inv[p] * H + c);
+        const f32x4 v = ld4(y + (size_t)inv[p] * H + c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] += coef * v[i];
     }
     if (sh) {
-        const f32x4 v = *(const f32x4 *)(sh + (size_t)t * H + c);
+        const f32x4 v = ld4(sh + (size_t)t * H + c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] += v[i];
     }
@@ -51,13 +62,18 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ y, co
     }
 }
 
-hipError_t launch_combine(const float *y, const int32_t *inv, const float *topk_w, float rsf, const float *sh,
-                          const uint16_t *res, void *out, int T, int H, int k, int out_f32, hipStream_t st)
+hipError_t launch_combine(const void *y, const int32_t *inv, const float *topk_w, float rsf, const void *sh,
+                          const uint16_t *res, void *out, int T, int H, int k, int out_f32, int y_f16, hipStream_t st)
 {
     const long n = (long)T * (H / 4);
     const unsigned grid = (unsigned)((n + 255) / 256);
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, st, y, inv, topk_w, rsf, sh, res, out, T, H, k, out_f32);
+    if (y_f16)
+        hipLaunchKernelGGL(k_combine<uint16_t>, dim3(grid), dim3(256), 0, st, (const uint16_t *)y, inv, topk_w, rsf,
+                           (const uint16_t *)sh, res, out, T, H, k, out_f32);
+    else
+        hipLaunchKernelGGL(k_combine<float>, dim3(grid), dim3(256), 0, st, (const float *)y, inv, topk_w, rsf,
+                           (const float *)sh, res, out, T, H, k, out_f32);
     return hipGetLastError();
 }
 

@@ -243,12 +243,15 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs &a, int e, int row0, int 
                     o[a.N + n] = acc[1][i][j][r] - corr;
                 }
             } else {
-                float *o = (float *)a.out + (size_t)row * a.ldo;
                 const float ps = (a.pscale && a.pair_of_row) ? a.pscale[a.pair_of_row[row]] : 1.f;
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int n = n0 + wn * (BN / WN) + j * 16 + (lane & 15);
-                    o[n] = (acc[0][i][j][r] - corr) * sc0[n] * ps;
+                    const float v = (acc[0][i][j][r] - corr) * sc0[n] * ps;
+                    if (a.out_f16)
+                        ((uint16_t *)a.out)[(size_t)row * a.ldo + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                    else
+                        ((float *)a.out)[(size_t)row * a.ldo + n] = v;
                 }
             }
         }
@@ -658,17 +661,25 @@ epilogue:
             if (m >= rows) continue;
             const int row = row0 + m;
             const float c = sCor[m];
-            float *o = (float *)a.out + (size_t)row * a.ldo + n0 + nloc;
+            const size_t o = (size_t)row * a.ldo + n0 + nloc;
             if constexpr (MODE == 2) {
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    *(f32x4 *)(o + j * 16) = acc[0][i][j] + c;
-                    *(f32x4 *)(o + a.N + j * 16) = acc[1][i][j] + c;
+                    *(f32x4 *)((float *)a.out + o + j * 16) = acc[0][i][j] + c;
+                    *(f32x4 *)((float *)a.out + o + a.N + j * 16) = acc[1][i][j] + c;
                 }
             } else {
                 const float ps = (a.pscale && a.pair_of_row) ? a.pscale[a.pair_of_row[row]] : 1.f;
 #pragma unroll
-                for (int j = 0; j < NB; ++j) *(f32x4 *)(o + j * 16) = (acc[0][i][j] + c) * sv[j] * ps;
+                for (int j = 0; j < NB; ++j) {
+                    f32x4 v;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = (acc[0][i][j][q] + c) * sv[j][q] * ps;
+                    if (a.out_f16)
+                        *(u32x2 *)((uint16_t *)a.out + o + j * 16) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+                    else
+                        *(f32x4 *)((float *)a.out + o + j * 16) = v;
+                }
             }
         }
     }

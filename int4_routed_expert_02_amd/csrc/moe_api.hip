@@ -167,10 +167,12 @@ Layout layout(const moe_shape *s, int which)
         L.sorted = take(P * 4);
         L.inv = take(P * 4);
         L.hbuf = take(P * (size_t)s->I * 2);  // h, f16
-        L.ypair = take(P * (size_t)s->H * 4);
+        // the routed and shared output rows: f16, f32 in the Q8 mode
+        const size_t yb = (s->flags & MOE_ACT_Q8) ? 4 : 2;
+        L.ypair = take(P * (size_t)s->H * yb);
         if (s->shared_bits) {
             L.shh = take(T * (size_t)s->I_shared * 2);
-            L.shy = take(T * (size_t)s->H * 4);
+            L.shy = take(T * (size_t)s->H * yb);
         }
         if (s->flags & MOE_ACT_Q8) {
             const size_t H = (size_t)s->H, I = (size_t)s->I, Is = (size_t)s->I_shared;
@@ -208,8 +210,8 @@ int check_ws(const moe_shape *s, int which, void *ws, size_t ws_bytes)
 }
 
 int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
-                 const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, float *y,
-                 hipStream_t st, const uint8_t *ebits = nullptr);
+                 const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, void *y,
+                 hipStream_t st, const uint8_t *ebits = nullptr, bool y_f16 = false);
 
 // gate and up of a family with more than one expert share one expert stride
 // (the kernels step both by it); a single expert's strides are never used.
@@ -222,8 +224,8 @@ bool strides_ok(const moe_qmat &gate, const moe_qmat &up, int E)
 // checked strides_ok before its first enqueue).
 int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qmat &gate, const moe_qmat &up,
             const moe_qmat &down, int I, const int32_t *offsets, const int32_t *sorted, int E, int kdiv, int rows,
-            const float *pscale, uint16_t *hbuf, float *y, hipStream_t st, bool gateup_only = false,
-            const uint8_t *ebits = nullptr)
+            const float *pscale, uint16_t *hbuf, void *y, hipStream_t st, bool gateup_only = false,
+            const uint8_t *ebits = nullptr, bool y_f16 = false)
 {
     FfnArgs g;
     memset(&g, 0, sizeof(g));
@@ -248,13 +250,13 @@ int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qma
     hipError_t e = moe::launch_ffn(0, wbits, g, rows, offsets ? E : 1, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (gateup_only) return MOE_OK;
-    return run_ffn_down(s, wbits, down, I, offsets, sorted, E, rows, pscale, hbuf, y, st, ebits);
+    return run_ffn_down(s, wbits, down, I, offsets, sorted, E, rows, pscale, hbuf, y, st, ebits, y_f16);
 }
 
-// The down GEMM on h (f32) of sorted rows.
+// The down GEMM on h (f16) of sorted rows; y in f32, or (y_f16) f16.
 int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
-                 const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, float *y,
-                 hipStream_t st, const uint8_t *ebits)
+                 const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, void *y,
+                 hipStream_t st, const uint8_t *ebits, bool y_f16)
 {
     FfnArgs d;
     memset(&d, 0, sizeof(d));
@@ -276,6 +278,7 @@ int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, con
     d.ldo = s->H;
     d.pscale = pscale;
     d.ebits = ebits;
+    d.out_f16 = y_f16 ? 1 : 0;
     return hip_status(moe::launch_ffn(1, wbits, d, rows, offsets ? E : 1, st));
 }
 
@@ -467,7 +470,7 @@ int moe_combine(const moe_shape *s, const float *y_pairs, const int32_t *inv_pos
         (residual && !aligned(residual, 8)))
         return MOE_ERR_ALIGN;
     return hip_status(moe::launch_combine(y_pairs, inv_pos, topk_w, s->routed_scaling_factor, shared_out, residual,
-                                          out, s->T, s->H, s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0,
+                                          out, s->T, s->H, s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, 0,
                                           (hipStream_t)stream));
 }
 
@@ -573,7 +576,8 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     int32_t *ids = at<int32_t>(ws, L.ids), *sbc = at<int32_t>(ws, L.sbc);
     int32_t *counts = at<int32_t>(ws, L.counts), *offsets = at<int32_t>(ws, L.offsets);
     int32_t *sorted = at<int32_t>(ws, L.sorted), *inv = at<int32_t>(ws, L.inv);
-    float *pscale = at<float>(ws, L.pscale), *ypair = at<float>(ws, L.ypair);
+    float *pscale = at<float>(ws, L.pscale);
+    float *ypair = at<float>(ws, L.ypair);  // f32 in the Q8 mode, else f16 (uint16_t)
 
     if (s->flags & MOE_ACT_Q8) {
         // Q8_0-style int8 activations: x quantised once (routed and shared
@@ -608,7 +612,7 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         return hip_status(moe::launch_combine(ypair, inv, nullptr, 1.f,
                                               s->shared_bits ? at<float>(ws, L.shy) : nullptr,
                                               (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr, out, s->T, s->H,
-                                              s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, hs));
+                                              s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, 0, hs));
     }
 
     // the shared expert (no dependence on the routing) on the side stream,
@@ -625,7 +629,8 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     auto routed = [&]() -> int {
         if (side) {
             int r = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr,
-                            nullptr, 1, 1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<float>(ws, L.shy), side->st);
+                            nullptr, 1, 1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<uint16_t>(ws, L.shy), side->st,
+                            false, nullptr, true);
             if (r) return r;
         }
         hipError_t e = moe::launch_router(hidden, w->router_w, w->router_bias, s->T, s->H, s->E, s->top_k,
@@ -637,13 +642,13 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         if (e != hipSuccess) return MOE_ERR_HIP;
         if (ev_start && hipEventRecord((hipEvent_t)ev_start, hs) != hipSuccess) return MOE_ERR_HIP;
         int r = run_ffn(s, 4, hidden, w->gate, w->up, w->down, s->I, offsets, sorted, s->E, s->top_k, P, pscale,
-                        at<uint16_t>(ws, L.hbuf), ypair, hs, ev_stop != nullptr, ebits);
+                        at<uint16_t>(ws, L.hbuf), ypair, hs, ev_stop != nullptr, ebits, true);
         if (r) return r;
         if (ev_stop) {
             // profiled: the routed gate/up kernel ran alone between the events; now the down GEMM
             if (hipEventRecord((hipEvent_t)ev_stop, hs) != hipSuccess) return MOE_ERR_HIP;
             r = run_ffn_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, at<uint16_t>(ws, L.hbuf),
-                             ypair, hs, ebits);
+                             ypair, hs, ebits, true);
             if (r) return r;
         }
         return MOE_OK;
@@ -662,14 +667,15 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         if (st) return st;
         if (s->shared_bits) {
             st = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr,
-                         1, 1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<float>(ws, L.shy), hs);
+                         1, 1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<uint16_t>(ws, L.shy), hs, false, nullptr,
+                         true);
             if (st) return st;
         }
     }
-    const float *shy = s->shared_bits ? at<float>(ws, L.shy) : nullptr;
+    const uint16_t *shy = s->shared_bits ? at<uint16_t>(ws, L.shy) : nullptr;
     return hip_status(moe::launch_combine(ypair, inv, nullptr, 1.f, shy,
                                           (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr, out, s->T, s->H,
-                                          s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, hs));
+                                          s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, 1, hs));
 }
 
 }  // namespace

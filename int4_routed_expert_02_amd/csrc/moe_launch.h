@@ -28,6 +28,7 @@ struct FfnArgs {
     const float *pscale;
     const float *ad;  // Q8 mode: f32 scale of every 32 activation codes, [rows of A][K/32]
     const uint8_t *ebits;  // per-expert format (4 or 2) of a mixed family, or null (all WBITS)
+    int out_f16;           // MODE 1: output rows in f16 (rounded to nearest even) instead of f32
 };
 
 // small-batch regime (decode.hip)
@@ -83,7 +84,8 @@ hipError_t launch_quant_act_q8(const void *src, int src_bf16, long rows, int col
 hipError_t launch_bias_update(int E, const int32_t *counts, float *bias, float gamma, hipStream_t st);
 hipError_t launch_quantize(const void *src, int src_bf16, long rows, int cols, int bits, void *q, float *qs,
                            hipStream_t st);
-hipError_t launch_combine(const float *y, const int32_t *inv, const float *topk_w, float rsf, const float *sh,
-                          const uint16_t *res, void *out, int T, int H, int k, int out_f32, hipStream_t st);
+// y and sh in f32, or (y_f16) both in f16
+hipError_t launch_combine(const void *y, const int32_t *inv, const float *topk_w, float rsf, const void *sh,
+                          const uint16_t *res, void *out, int T, int H, int k, int out_f32, int y_f16, hipStream_t st);
 
 }  // namespace moe

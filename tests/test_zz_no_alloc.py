@@ -53,8 +53,8 @@ def test_noalloc_matches_layer_forward(name, flags):
 
 
 def test_noalloc_rejects_oversized_shape():
-    """The full Nano-shape prefill layer needs more workspace than the scratch holds."""
-    cfg = synth.CONFIGS["c2"]
+    """The 16384-token Nano-shape layer needs more workspace than the scratch holds."""
+    cfg = synth.CONFIGS["c4"]
     sh = moe.shape_of(cfg, cfg.T, moe.MOE_OUT_F32)
     assert moe.moe_workspace_bytes(sh, moe.MOE_WS_LAYER) > moe.MOE_NOALLOC_SCRATCH_BYTES
     lib = moe.load()
