@@ -132,7 +132,7 @@ def test_errors_before_any_enqueue(moe):
     assert lib.moe_expert_ffn(ctypes.byref(s), vp(FAKE), ctypes.byref(w3), vp(FAKE), vp(FAKE), None, vp(FAKE),
                               vp(FAKE), 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
     # the no-allocation entry point: a shape whose layer workspace exceeds its scratch is refused
-    huge = good(moe, T=4096)
+    huge = good(moe, T=16384)
     assert moe.moe_workspace_bytes(huge, moe.MOE_WS_LAYER) > moe.MOE_NOALLOC_SCRATCH_BYTES
     assert lib.moe_layer_forward_noalloc(ctypes.byref(huge), ctypes.byref(w), vp(FAKE), vp(FAKE),
                                          None) == moe.MOE_ERR_WORKSPACE
