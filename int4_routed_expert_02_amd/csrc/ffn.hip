@@ -349,6 +349,13 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
     const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(wn);  // the same, known wave-uniform
 
+    // LDS swizzles of the 64-k stages, so that the fragment reads of 16
+    // consecutive lanes hit distinct banks: A rows (128 bytes, 16 rows per
+    // read) hold 16-byte chunk c at slot c ^ ((row >> 1) & 7); int4 B rows (32
+    // bytes) swap their two chunks when (row >> 3) & 1, int8 B rows (64 bytes)
+    // XOR the chunk with (row >> 2) & 3; int2 rows are one chunk.
+    auto aswz = [](int r) { return (r >> 1) & 7; };
+    auto bswz = [](int r) { return BKB == 32 ? (r >> 3) & 1 : BKB == 64 ? (r >> 2) & 3 : 0; };
     // this lane's source for each of its wave's copies (fixed across stages)
     const uint8_t *src[C::PER_WAVE];
     int dst[C::PER_WAVE];  // byte offset of the wave's 1 KB block within a stage
@@ -358,7 +365,7 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
         dst[j] = l * 1024;
         if (l < C::A_LOADS) {
             const int r = l * 8 + lane / 8;  // tile row
-            const int chunk = (lane % 8) ^ (r & 7);
+            const int chunk = (lane % 8) ^ aswz(r);
             const int rr = r < rows ? r : 0;  // padded rows read row 0 (outputs discarded)
             const int srow = a.gather ? a.gather[row0 + rr] / a.kdiv : row0 + rr;
             src[j] = (const uint8_t *)a.A + ((size_t)srow * a.lda + chunk * 8) * 2;
@@ -368,7 +375,8 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
             const int br = lb * (64 / cpr) + lane / cpr;  // B row within the stage
             const int mat = br / BN, n = br % BN;
             const uint8_t *qm = (mat == 0) ? a.q0 : a.q1;
-            src[j] = qm + (size_t)e * a.qstride + (size_t)(n0 + n) * (size_t)a.K * WBITS / 8 + (lane % cpr) * 16;
+            src[j] = qm + (size_t)e * a.qstride + (size_t)(n0 + n) * (size_t)a.K * WBITS / 8 +
+                     ((lane % cpr) ^ bswz(br)) * 16;
         }
     }
     // Copy j < A_LOADS / 4 of every wave is an A copy (8 rows).  Only the
@@ -440,7 +448,7 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
                 for (int i = 0; i < MV; ++i) {
                     const int r = i * 16 + (lane & 15);
                     const int chunk = ks * 4 + (lane >> 4);
-                    af[i] = *(const u32x4 *)(sa + r * 128 + ((chunk ^ (r & 7)) * 16));
+                    af[i] = *(const u32x4 *)(sa + r * 128 + ((chunk ^ aswz(r)) * 16));
                 }
                 // (the correction blocks depend on the wave, so their fragments
                 // are read again rather than picked from af by a run-time index;
@@ -451,14 +459,16 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
                     if (4 * c + 3 >= MV && wu + 4 * c >= MV) continue;
                     const int r = (wn + 4 * c) * 16 + (lane & 15);
                     const int chunk = ks * 4 + (lane >> 4);
-                    cor[c] = mma(cneg, *(const u32x4 *)(sa + r * 128 + ((chunk ^ (r & 7)) * 16)), cor[c]);
+                    cor[c] = mma(cneg, *(const u32x4 *)(sa + r * 128 + ((chunk ^ aswz(r)) * 16)), cor[c]);
                 }
 #pragma unroll
                 for (int x = 0; x < NMAT; ++x)
 #pragma unroll
                     for (int j = 0; j < NB; ++j) {
-                        const uint8_t *bp = sb + (x * BN + wn * (BN / 4) + j * 16 + (lane & 15)) * BKB;
-                        const u32x4 bf = weight_fragment<MODE, WBITS>(bp + ks * (BKB / 2) + (lane >> 4) * (WBITS / 2) * 2);
+                        const int br = x * BN + wn * (BN / 4) + j * 16 + (lane & 15);
+                        const int bo = ks * (BKB / 2) + (lane >> 4) * (WBITS / 2) * 2;  // byte in the row
+                        const u32x4 bf = weight_fragment<MODE, WBITS>(sb + br * BKB +
+                                                                      (((bo >> 4) ^ bswz(br)) << 4) + (bo & 15));
 #pragma unroll
                         for (int i = 0; i < MV; ++i) acc[x][i][j] = mma(bf, af[i], acc[x][i][j]);
                     }
