@@ -677,7 +677,7 @@ def bench_prefill(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread):
              "routed gate/up grouped GEMM + SwiGLU (int4 weights on bf16 MFMA)")
     traffic = None
     if cfg.name.startswith("c3") and not q8 and not cfg.int2_frac and not cfg.top_p:
-        traffic = measured_traffic("k_ffn_gateup_c3_traffic", ["ffn.hip"])
+        traffic = measured_traffic("k_ffn_gateup_c3_traffic", ["ffn.hip", "ffn_common.h"])
     if t_hbm >= t_mma:
         roofline = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
