@@ -453,9 +453,10 @@ def bench_regime_sweep(args, moe, synth, torch, np, dev):
     """Where the small-batch regime stops paying: one Nano-shape layer
     (moe_layer_forward, bf16 out) over T, with the weights of `cold_copies`
     identical layer copies rotated (no weight in the last-level cache when it
-    is read), in the small-batch regime (T <= 32, the default there) and in
-    the tiled regime (MOE_REGIME_TILED).  Each point is a HIP graph of one
-    call per copy; time per layer = graph time / copies."""
+    is read), in the small-batch regime (MOE_REGIME_SMALL: chunks of 32
+    tokens) and in the tiled regime (MOE_REGIME_TILED), whatever the default
+    for that T.  Each point is a HIP graph of one call per copy; time per
+    layer = graph time / copies."""
     base = synth.CONFIGS["c0"]
     n = args.cold_copies
     Tmax = 256
@@ -464,13 +465,12 @@ def bench_regime_sweep(args, moe, synth, torch, np, dev):
     xall = torch.from_numpy(d["hidden"].view(np.int16)).to(dev).view(torch.bfloat16)
     stream = torch.cuda.Stream(device=dev)
     rows = []
-    for T in (1, 2, 4, 8, 16, 24, 32, 40, 48, 64, 96, 128, 192, 256):
+    for T in (1, 2, 4, 8, 16, 24, 32, 40, 48, 64, 80, 96, 128, 192, 256):
         x = xall[:T].contiguous()
         point = {"T": T}
-        for name, fl in (("small_batch", 0), ("tiled", moe.MOE_REGIME_TILED)):
-            sh = moe.shape_of(base, T, fl)
-            if name == "small_batch" and moe.moe_layer_routing(sh, copies[0].workspace(T, fl))[2] is not None:
-                continue  # the small-batch regime does not serve this T
+        default_small = moe.moe_layer_routing(moe.shape_of(base, T, 0), copies[0].workspace(T, 0))[2] is None
+        point["default"] = "small_batch" if default_small else "tiled"
+        for name, fl in (("small_batch", moe.MOE_REGIME_SMALL), ("tiled", moe.MOE_REGIME_TILED)):
             outs = [torch.empty((T, base.H), dtype=torch.bfloat16, device=dev) for _ in range(n)]
             wss = [c.workspace(T, fl) for c in copies]
             with torch.cuda.stream(stream):

@@ -99,6 +99,12 @@ extern "C" {
                                the shapes moe_layer_routing names); for measuring the two regimes side by
                                side.  With MOE_STAGE_EXPERTS_ONLY, MOE_LOGITS_GIVEN or in a chained call:
                                MOE_ERR_UNSUPPORTED */
+#define MOE_REGIME_SMALL 0x8000u /* moe_layer_forward(_profiled, _noalloc): take the small-batch kernels at any T,
+                               in chunks of 32 tokens (each chunk streams its experts' weights again), for a
+                               shape they serve (top_k <= 16, H % 1024 == 0, I and I_shared % 512 == 0),
+                               else MOE_ERR_UNSUPPORTED; with MOE_REGIME_TILED, MOE_ACT_Q8 or
+                               MOE_EXPERT_MIXED: MOE_ERR_UNSUPPORTED.  For measuring the two regimes side
+                               by side */
 #define MOE_TEST_GATEUP_SUMS 0x100u /* moe_expert_ffn, testing only: write the raw integer-weight sums
                                sum_h x*q of gate into y_pairs[r][0:I] and of up into y_pairs[r][I:2I]
                                (no scale, no activation, no down projection); needs 2*I <= H, int4 */
@@ -328,9 +334,15 @@ const char *moe_status_string(int status);
  * routing it computed: moe_layer_routing(ws, shape, ...) returns device
  * pointers into ws (ids [T][k], w [T][k], offsets [E+1], sorted [T*k]).
  * Pointers stay valid until the workspace is reused.  In the small-batch
- * regime (T <= 32, top_k <= 16, H % 1024 == 0, I % 512 == 0, I_shared % 512 == 0) each
- * expert kernel gathers its own pairs and no sorted list is materialised:
- * offsets and sorted_pairs are then returned as NULL. */
+ * regime each expert kernel gathers its own pairs and no sorted list is
+ * materialised: offsets and sorted_pairs are then returned as NULL.  That
+ * regime serves T <= 64 (at most two chunks of 32 tokens: the measured
+ * crossover with the tiled kernels lies between 64 and 96 tokens at the Nano
+ * shape), top_k <= 16, H % 1024 == 0, I % 512 == 0 and I_shared % 512 == 0,
+ * unless MOE_REGIME_TILED or MOE_REGIME_SMALL decides; MOE_ACT_Q8 and
+ * MOE_EXPERT_MIXED always take the tiled kernels.  Chained calls
+ * (moe_layer_forward_chain), MOE_LOGITS_GIVEN and MOE_STAGE_EXPERTS_ONLY need
+ * T <= 32 (one chunk), else MOE_ERR_UNSUPPORTED. */
 int moe_layer_routing(const moe_shape *shape, void *ws, size_t ws_bytes, int32_t **topk_ids, float **topk_w,
                       int32_t **offsets, int32_t **sorted_pairs);
 

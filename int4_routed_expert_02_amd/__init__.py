@@ -37,6 +37,7 @@ MOE_LOGITS_GIVEN = 0x800
 MOE_ACT_Q8 = 0x1000
 MOE_EXPERT_MIXED = 0x2000
 MOE_REGIME_TILED = 0x4000
+MOE_REGIME_SMALL = 0x8000
 
 MOE_SRC_F32 = 0
 MOE_SRC_BF16 = 1

@@ -1141,9 +1141,10 @@ __global__ __launch_bounds__(256) void k_dec_combine_logits(const uint16_t *__re
 
 static bool dec_topp_on(float p) { return p > 0.f && p < 1.f; }
 
-bool decode_supported(int T, int H, int E, int k, int I, int Ish, int sh_bits)
+bool decode_supported(int H, int E, int k, int I, int Ish, int sh_bits)
 {
-    if (T > DEC_MAXT || E > 256 || k > DEC_MAXK) return false;
+    static_assert(DEC_MAXT == DEC_CHUNK_TOKENS, "one launch takes one chunk of the batch");
+    if (E > 256 || k > DEC_MAXK) return false;
     if (H % 1024 || I % 512) return false;
     if (sh_bits && Ish % 512) return false;
     return true;

@@ -98,6 +98,10 @@ int validate(const moe_shape *s)
     if (s->E > 256 || s->top_k > 64 || s->n_group > 64) return MOE_ERR_UNSUPPORTED;
     if ((s->flags & MOE_EXPERT_MIXED) && (s->flags & (MOE_ACT_Q8 | MOE_TEST_GATEUP_SUMS | MOE_EXPERT_INT8)))
         return MOE_ERR_UNSUPPORTED;
+    if ((s->flags & MOE_REGIME_SMALL) &&
+        ((s->flags & (MOE_REGIME_TILED | MOE_ACT_Q8 | MOE_EXPERT_MIXED)) ||
+         !moe::decode_supported(s->H, s->E, s->top_k, s->I, s->I_shared, s->shared_bits)))
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -118,10 +122,17 @@ struct Layout {
     bool decode;  // the small-batch path serves this shape (MOE_WS_LAYER)
 };
 
+// Largest batch the small-batch regime takes by default: two chunks of 32
+// tokens.  Measured at the Nano shape (one layer, cold weights, bench.py
+// --regime-sweep): the small-batch kernels are faster than the tiled ones up
+// to 64 tokens and slower from 96 on.
+constexpr int DEC_AUTO_MAX_T = 64;
+
 bool use_decode(const moe_shape *s)
 {
     if (s->flags & (MOE_ACT_Q8 | MOE_EXPERT_MIXED | MOE_REGIME_TILED)) return false;  // the tiled kernels
-    return moe::decode_supported(s->T, s->H, s->E, s->top_k, s->I, s->I_shared, s->shared_bits);
+    if (!moe::decode_supported(s->H, s->E, s->top_k, s->I, s->I_shared, s->shared_bits)) return false;
+    return (s->flags & MOE_REGIME_SMALL) || s->T <= DEC_AUTO_MAX_T;
 }
 
 Layout layout(const moe_shape *s, int which)
@@ -145,16 +156,19 @@ Layout layout(const moe_shape *s, int which)
     } else if (which == MOE_WS_EXPERT_FFN) {
         L.hbuf = take(P * (size_t)s->I * 2);  // h, f16
     } else if (use_decode(s)) {
-        // pair-indexed buffers, no permutation: partial logits, routing, and
-        // the experts' partial outputs (one plane per 128-row intermediate chunk)
+        // pair-indexed buffers, no permutation: the routing of the whole
+        // batch; per chunk of tokens (reused by the chunks in turn) the
+        // partial logits and the experts' partial outputs (one f16 plane per
+        // 128-row intermediate unit)
         L.decode = true;
-        L.zpart = take(moe::DEC_LOGIT_PLANES * T * E * 4);
+        const size_t Tc = T < (size_t)moe::DEC_CHUNK_TOKENS ? T : (size_t)moe::DEC_CHUNK_TOKENS, Pc = Tc * k;
+        L.zpart = take(moe::DEC_LOGIT_PLANES * Tc * E * 4);
         L.ids = take(P * 4);
         L.w = take(P * 4);
         L.gap = take(T * 4);
         L.pscale = take(P * 4);
-        L.ypair = take((size_t)(s->I / moe::DEC_CHUNK_ROWS) * P * (size_t)s->H * 2);  // f16
-        if (s->shared_bits) L.shy = take((size_t)(s->I_shared / moe::DEC_CHUNK_ROWS) * T * (size_t)s->H * 2);
+        L.ypair = take((size_t)(s->I / moe::DEC_CHUNK_ROWS) * Pc * (size_t)s->H * 2);
+        if (s->shared_bits) L.shy = take((size_t)(s->I_shared / moe::DEC_CHUNK_ROWS) * Tc * (size_t)s->H * 2);
     } else {
         L.zpart = take((size_t)KS * T * E * 4);
         L.sbc = take(nsb * E * 4);
@@ -501,7 +515,8 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     const uint8_t *ebits = (s->flags & MOE_EXPERT_MIXED) ? w->expert_bits : nullptr;
     const Layout L = layout(s, MOE_WS_LAYER);
     hipStream_t hs = (hipStream_t)stream;
-    if ((s->flags & (MOE_STAGE_EXPERTS_ONLY | MOE_LOGITS_GIVEN)) && !L.decode) return MOE_ERR_UNSUPPORTED;
+    if ((s->flags & (MOE_STAGE_EXPERTS_ONLY | MOE_LOGITS_GIVEN)) && (!L.decode || s->T > moe::DEC_CHUNK_TOKENS))
+        return MOE_ERR_UNSUPPORTED;
     Layout NL;
     if (nw) {
         // chained: the next layer's router logits from this layer's bf16 output
@@ -509,7 +524,9 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         if ((st = validate(ns))) return st;
         if (ns->T != s->T || ns->H != s->H) return MOE_ERR_SHAPE;
         NL = layout(ns, MOE_WS_LAYER);
-        if (!L.decode || !NL.decode || (s->flags & (MOE_OUT_F32 | MOE_STAGE_EXPERTS_ONLY))) return MOE_ERR_UNSUPPORTED;
+        if (!L.decode || !NL.decode || (s->flags & (MOE_OUT_F32 | MOE_STAGE_EXPERTS_ONLY)) ||
+            s->T > moe::DEC_CHUNK_TOKENS)
+            return MOE_ERR_UNSUPPORTED;
         if (!aligned(nw->router_w, 16)) return MOE_ERR_ALIGN;
         if ((st = check_ws(ns, MOE_WS_LAYER, nws, nws_bytes))) return st;
     }
@@ -567,7 +584,29 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
             d.nE = ns->E;
             d.nz = at<float>(nws, NL.zpart);
         }
-        return hip_status(moe::launch_decode(d, hs));
+        // chunks of up to DEC_CHUNK_TOKENS tokens, one after another on the
+        // stream (each reuses the chunk-sized logit and partial-output
+        // buffers); routing and output land at the chunk's rows.  The events
+        // bracket the first chunk's expert kernel through the last's.
+        const int CT = moe::DEC_CHUNK_TOKENS, nchunk = (s->T + CT - 1) / CT;
+        const size_t osz = d.out_f32 ? 4 : 2;
+        for (int c = 0; c < nchunk; ++c) {
+            const int t0 = c * CT;
+            moe::DecLaunch dc = d;
+            dc.T = s->T - t0 < CT ? s->T - t0 : CT;
+            dc.x = d.x + (size_t)t0 * s->H;
+            dc.ids = d.ids + (size_t)t0 * s->top_k;
+            dc.w = d.w + (size_t)t0 * s->top_k;
+            dc.gap = d.gap + t0;
+            dc.pscale = d.pscale + (size_t)t0 * s->top_k;
+            if (d.res) dc.res = d.res + (size_t)t0 * s->H;
+            dc.out = (char *)out + (size_t)t0 * s->H * osz;
+            dc.ev0 = c == 0 ? d.ev0 : nullptr;
+            dc.ev1 = c == nchunk - 1 ? d.ev1 : nullptr;
+            const hipError_t e = moe::launch_decode(dc, hs);
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        return MOE_OK;
     }
     const int P = s->T * s->top_k;
     const int KS = moe::router_ks(s->T, s->H, s->E);

@@ -62,7 +62,9 @@ struct DecLaunch {
 };
 constexpr int DEC_LOGIT_PLANES = 4;  // partial-logit planes of the small-batch router
 constexpr int DEC_CHUNK_ROWS = 128;  // intermediate rows per small-batch expert unit (one output plane each)
-bool decode_supported(int T, int H, int E, int k, int I, int Ish, int sh_bits);
+constexpr int DEC_CHUNK_TOKENS = 32; // tokens per small-batch launch (a larger batch runs in chunks)
+// shapes the small-batch kernels serve (any T, in chunks of DEC_CHUNK_TOKENS)
+bool decode_supported(int H, int E, int k, int I, int Ish, int sh_bits);
 hipError_t launch_decode(const DecLaunch &d, hipStream_t st);
 
 int router_ks(int T, int H, int E);

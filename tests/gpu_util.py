@@ -122,7 +122,7 @@ def check_output(cfg, d, hidden, got, exempt, tokens=None, residual=False, bf16_
 def is_decode(cfg, T=None) -> bool:
     """Whether moe_layer_forward takes the small-batch path for this shape."""
     T = cfg.T if T is None else T
-    return (T <= 32 and cfg.E <= 256 and cfg.k <= 16 and cfg.H % 1024 == 0 and cfg.I % 512 == 0
+    return (T <= 64 and cfg.E <= 256 and cfg.k <= 16 and cfg.H % 1024 == 0 and cfg.I % 512 == 0
             and (cfg.shared_bits == 0 or cfg.I_sh % 512 == 0))
 
 

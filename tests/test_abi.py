@@ -61,6 +61,10 @@ def good(moe, **kw):
     (dict(I_shared=2000), -3),
     (dict(E=512, top_k=2), -3),
     (dict(shared_bits=0, I_shared=0), 0),
+    (dict(T=100, flags=0x8000), 0),                     # MOE_REGIME_SMALL on a shape it serves
+    (dict(H=1152, flags=0x8000), -3),                   # ... on one it does not (H % 1024)
+    (dict(flags=0x8000 | 0x4000), -3),                  # with MOE_REGIME_TILED
+    (dict(flags=0x8000 | 0x1000), -3),                  # with MOE_ACT_Q8
     (dict(E=256, top_k=8, n_group=8, topk_group=4, H=6144, I=2048, rsf=2.5), 0),
     (dict(flags=0x1000), 0),            # MOE_ACT_Q8
     (dict(flags=0x2000), 0),            # MOE_EXPERT_MIXED
@@ -138,7 +142,7 @@ def test_errors_before_any_enqueue(moe):
                                          None) == moe.MOE_ERR_WORKSPACE
     assert lib.moe_layer_forward_noalloc(ctypes.byref(good(moe, H=1023)), ctypes.byref(w), vp(FAKE), vp(FAKE),
                                          None) == moe.MOE_ERR_SHAPE
-    # the experts-only profiling stage exists only in the small-batch regime (T <= 32, H % 1024 == 0)
+    # the experts-only profiling stage exists only in the small-batch regime, for one chunk (T <= 32)
     big = good(moe, T=64, flags=moe.MOE_STAGE_EXPERTS_ONLY)
     need_big = moe.moe_workspace_bytes(big, moe.MOE_WS_LAYER)
     assert lib.moe_layer_forward(ctypes.byref(big), ctypes.byref(w), vp(FAKE), vp(FAKE), vp(FAKE), need_big,
@@ -153,6 +157,30 @@ def test_errors_before_any_enqueue(moe):
     assert lib.moe_combine(ctypes.byref(s), None, vp(FAKE), None, None, None, vp(FAKE), None) == moe.MOE_ERR_NULL
     assert lib.moe_expert_ffn(ctypes.byref(good(moe, I=1024, flags=moe.MOE_TEST_GATEUP_SUMS)), vp(FAKE), ctypes.byref(w),
                               vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_regime_rule(moe):
+    """The small-batch regime (no sorted pair list) serves T <= 64 by default
+    (two chunks of 32), the tiled one from 65 on; MOE_REGIME_SMALL and
+    MOE_REGIME_TILED decide at any T (host-side pointer arithmetic only)."""
+    lib = moe.load()
+    ws = ctypes.c_void_p(FAKE)
+
+    def decode(sh):
+        need = moe.moe_workspace_bytes(sh, moe.MOE_WS_LAYER)
+        off = ctypes.POINTER(ctypes.c_int32)()
+        assert lib.moe_layer_routing(ctypes.byref(sh), ws, need, None, None, ctypes.byref(off), None) == 0
+        return not bool(off)
+
+    assert decode(good(moe, T=1)) and decode(good(moe, T=32)) and decode(good(moe, T=33)) and decode(good(moe, T=64))
+    assert not decode(good(moe, T=65)) and not decode(good(moe, T=4096))
+    assert decode(good(moe, T=1000, flags=moe.MOE_REGIME_SMALL))
+    assert not decode(good(moe, T=8, flags=moe.MOE_REGIME_TILED))
+    assert not decode(good(moe, T=8, flags=moe.MOE_ACT_Q8))
+    # the small-batch workspace holds the routing of the whole batch and one chunk's buffers
+    w64 = moe.moe_workspace_bytes(good(moe, T=64), moe.MOE_WS_LAYER)
+    w32 = moe.moe_workspace_bytes(good(moe, T=32), moe.MOE_WS_LAYER)
+    assert w32 < w64 < 2 * w32
 
 
 def test_product_path_has_no_fallback(moe, tmp_path, monkeypatch):
@@ -216,9 +244,10 @@ def _fake_weights(moe):
     ("f32 out", -3),
     ("tiled regime", -3),
     ("logits given, tiled", -3),
+    ("two chunks", -3),      # the small-batch regime at T = 64 runs in two chunks: not chainable
 ])
 def test_chain_validation(moe, case, code):
-    T = 64 if "tiled" in case else 32
+    T = 100 if "tiled" in case else 64 if case == "two chunks" else 32
     flags = moe.MOE_OUT_F32 if case == "f32 out" else 0
     if case == "logits given, tiled":
         flags |= moe.MOE_LOGITS_GIVEN

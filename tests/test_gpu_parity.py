@@ -48,6 +48,10 @@ SMALL = {
     "dec_H2048_T9": synth.CONFIGS["c0"].with_(T=9, H=2048, I=1024, I_sh=1536, seed=27),
     "dec_no_shared_T32": synth.CONFIGS["c0"].with_(T=32, shared_bits=0, seed=28),
     "dec_grouped_T20": synth.CONFIGS["c3"].with_(T=20, H=1024, I=512, I_sh=1024, seed=29),
+    # the small-batch regime in two chunks of up to 32 tokens (33 <= T <= 64)
+    "dec_chunked_T33": synth.CONFIGS["c0"].with_(T=33, seed=34),
+    "dec_chunked_T64": synth.CONFIGS["c0"].with_(T=64, seed=35),
+    "dec_chunked_grouped_T50": synth.CONFIGS["c3"].with_(T=50, H=1024, I=512, I_sh=1024, seed=36),
 }
 
 
@@ -59,6 +63,25 @@ def test_layer_parity_small(name):
     got, ids, w, offsets, srt = run_layer(cfg, d)
     ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag=name)
     check_output(cfg, d, d["hidden"], got, ex, tag=f"{name} (exempt {int(ex.sum())})")
+
+
+def test_small_regime_in_chunks():
+    """MOE_REGIME_SMALL at T = 100 (four chunks, the last of 4 tokens): the
+    oracle's routing and outputs on every token, and each chunk's rows
+    bit-equal to a call on that chunk's tokens alone."""
+    import torch
+    cfg = synth.CONFIGS["c0"].with_(T=100, seed=37)
+    d = synth.layer(cfg)
+    flags = moe.MOE_OUT_F32 | moe.MOE_REGIME_SMALL
+    got, ids, w, offsets, srt = run_layer(cfg, d, flags=flags)
+    assert offsets is None and srt is None
+    ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag="small regime T=100")
+    check_output(cfg, d, d["hidden"], got, ex, tag="small regime T=100")
+    for t0, t1 in ((32, 64), (96, 100)):
+        part, pids, pw, _, _ = run_layer(cfg.with_(T=t1 - t0), d, flags=moe.MOE_OUT_F32,
+                                         hidden=np.ascontiguousarray(d["hidden"][t0:t1]))
+        assert np.array_equal(part, got[t0:t1]), f"chunk {t0}:{t1} differs from its own call"
+        assert np.array_equal(pids, ids[t0:t1]) and np.array_equal(pw, w[t0:t1])
 
 
 @pytest.mark.parametrize("T", [1, 16, 32])
