@@ -247,8 +247,12 @@ int moe_combine(const moe_shape *shape, const float *y_pairs, const int32_t *inv
  * combine) and colibri README at 0d2fb6f, "Never wait for the disk twice"
  * (the per-token expert path).  Routed experts must be packed int4 (or int4
  * and int2 with MOE_EXPERT_MIXED); MOE_EXPERT_INT8 is MOE_ERR_UNSUPPORTED here.
- * out: [T][H] f32 or bf16 per MOE_OUT_F32.  The regime (small-batch weight
- * streaming or tiled grouped GEMM) is chosen from the shape.  In the tiled
+ * out: [T][H] f32 or bf16 per MOE_OUT_F32.  Inside the layer the routed and
+ * shared output rows (in the small-batch regime each 128-row unit's partial
+ * rows) are carried in f16, each value rounded once to nearest even (so
+ * |value| must stay below 65504), and summed in f32 in a fixed order.  The
+ * regime (small-batch weight streaming or tiled grouped GEMM) is chosen from
+ * the shape and T, as moe_layer_routing describes.  In the tiled
  * regime the shared expert runs on a second stream of the current device
  * (created on first use, default priority), forked from and joined back to
  * `stream` with events, so the call stays ordered on `stream` and a captured
