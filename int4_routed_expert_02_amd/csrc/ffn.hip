@@ -243,15 +243,17 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs &a, int e, int row0, int 
                     o[a.N + n] = acc[1][i][j][r] - corr;
                 }
             } else {
-                const float ps = (a.pscale && a.pair_of_row) ? a.pscale[a.pair_of_row[row]] : 1.f;
+                const int pr = a.pair_of_row ? a.pair_of_row[row] : row;
+                const float ps = (a.pscale && a.pair_of_row) ? a.pscale[pr] : 1.f;
+                const size_t orow = a.out_by_pair ? (size_t)pr : (size_t)row;
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int n = n0 + wn * (BN / WN) + j * 16 + (lane & 15);
                     const float v = (acc[0][i][j][r] - corr) * sc0[n] * ps;
                     if (a.out_f16)
-                        ((uint16_t *)a.out)[(size_t)row * a.ldo + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                        ((uint16_t *)a.out)[orow * a.ldo + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
                     else
-                        ((float *)a.out)[(size_t)row * a.ldo + n] = v;
+                        ((float *)a.out)[orow * a.ldo + n] = v;
                 }
             }
         }
@@ -679,16 +681,18 @@ epilogue:
                     *(f32x4 *)((float *)a.out + o + a.N + j * 16) = acc[1][i][j] + c;
                 }
             } else {
-                const float ps = (a.pscale && a.pair_of_row) ? a.pscale[a.pair_of_row[row]] : 1.f;
+                const int pr = a.pair_of_row ? a.pair_of_row[row] : row;
+                const float ps = (a.pscale && a.pair_of_row) ? a.pscale[pr] : 1.f;
+                const size_t ob = a.out_by_pair ? (size_t)pr * a.ldo + n0 + nloc : o;
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     f32x4 v;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) v[q] = (acc[0][i][j][q] + c) * sv[j][q] * ps;
                     if (a.out_f16)
-                        *(u32x2 *)((uint16_t *)a.out + o + j * 16) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
+                        *(u32x2 *)((uint16_t *)a.out + ob + j * 16) = u32x2{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])};
                     else
-                        *(f32x4 *)((float *)a.out + o + j * 16) = v;
+                        *(f32x4 *)((float *)a.out + ob + j * 16) = v;
                 }
             }
         }

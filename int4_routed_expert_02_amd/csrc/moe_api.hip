@@ -267,7 +267,8 @@ int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qma
     return run_ffn_down(s, wbits, down, I, offsets, sorted, E, rows, pscale, hbuf, y, st, ebits, y_f16);
 }
 
-// The down GEMM on h (f16) of sorted rows; y in f32, or (y_f16) f16.
+// The down GEMM on h (f16) of sorted rows; y: f32 rows in sorted order (the
+// split API), or (y_f16: the layer's own rows) f16 rows in pair order.
 int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
                  const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, void *y,
                  hipStream_t st, const uint8_t *ebits, bool y_f16)
@@ -293,6 +294,7 @@ int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, con
     d.pscale = pscale;
     d.ebits = ebits;
     d.out_f16 = y_f16 ? 1 : 0;
+    d.out_by_pair = y_f16 ? 1 : 0;
     return hip_status(moe::launch_ffn(1, wbits, d, rows, offsets ? E : 1, st));
 }
 
@@ -484,7 +486,7 @@ int moe_combine(const moe_shape *s, const float *y_pairs, const int32_t *inv_pos
         (residual && !aligned(residual, 8)))
         return MOE_ERR_ALIGN;
     return hip_status(moe::launch_combine(y_pairs, inv_pos, topk_w, s->routed_scaling_factor, shared_out, residual,
-                                          out, s->T, s->H, s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, 0,
+                                          out, s->T, s->H, s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, 0, 0,
                                           (hipStream_t)stream));
 }
 
@@ -651,7 +653,7 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         return hip_status(moe::launch_combine(ypair, inv, nullptr, 1.f,
                                               s->shared_bits ? at<float>(ws, L.shy) : nullptr,
                                               (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr, out, s->T, s->H,
-                                              s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, 0, hs));
+                                              s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, 0, 0, hs));
     }
 
     // the shared expert (no dependence on the routing) on the side stream,
@@ -714,7 +716,7 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     const uint16_t *shy = s->shared_bits ? at<uint16_t>(ws, L.shy) : nullptr;
     return hip_status(moe::launch_combine(ypair, inv, nullptr, 1.f, shy,
                                           (s->flags & MOE_ADD_RESIDUAL) ? hidden : nullptr, out, s->T, s->H,
-                                          s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, 1, hs));
+                                          s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, 1, 1, hs));
 }
 
 }  // namespace

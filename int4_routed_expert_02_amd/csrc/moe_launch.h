@@ -29,6 +29,7 @@ struct FfnArgs {
     const float *ad;  // Q8 mode: f32 scale of every 32 activation codes, [rows of A][K/32]
     const uint8_t *ebits;  // per-expert format (4 or 2) of a mixed family, or null (all WBITS)
     int out_f16;           // MODE 1: output rows in f16 (rounded to nearest even) instead of f32
+    int out_by_pair;       // MODE 1: row r is written at row pair_of_row[r] (pair order) instead of r
 };
 
 // small-batch regime (decode.hip)
@@ -86,8 +87,10 @@ hipError_t launch_quant_act_q8(const void *src, int src_bf16, long rows, int col
 hipError_t launch_bias_update(int E, const int32_t *counts, float *bias, float gamma, hipStream_t st);
 hipError_t launch_quantize(const void *src, int src_bf16, long rows, int cols, int bits, void *q, float *qs,
                            hipStream_t st);
-// y and sh in f32, or (y_f16) both in f16
+// y and sh in f32, or (y_f16) both in f16; y rows in sorted order (row inv[p]
+// for pair p), or (y_by_pair) in pair order (row p)
 hipError_t launch_combine(const void *y, const int32_t *inv, const float *topk_w, float rsf, const void *sh,
-                          const uint16_t *res, void *out, int T, int H, int k, int out_f32, int y_f16, hipStream_t st);
+                          const uint16_t *res, void *out, int T, int H, int k, int out_f32, int y_f16, int y_by_pair,
+                          hipStream_t st);
 
 }  // namespace moe

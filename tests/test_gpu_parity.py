@@ -419,3 +419,52 @@ def test_tiled_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {r} differs"
         _ = (x.float() * 2).sum().item()
+
+
+def test_decode_graph_replays_match_eager():
+    """The benchmark's way of running the small-batch path: a chained stack
+    (four layers, T = 32, MOE_LOGITS_GIVEN after the first) and a two-chunk
+    layer (T = 64) captured in one HIP graph and replayed several times with
+    eager work between the replays: every replay gives the eager bits."""
+    import torch
+    cfg = synth.CONFIGS["c1"]
+    T, L = cfg.T, 4
+    flags = moe.MOE_ADD_RESIDUAL
+    layers = [moe.MoeLayer(cfg, synth.layer(cfg, l, with_hidden=False)) for l in range(L)]
+    wss = [ly.workspace(T, flags) for ly in layers]
+    xs = [torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda") for _ in range(L + 1)]
+    xs[0].copy_(dev_bf16(synth.hidden(cfg, 0)))
+    c2 = synth.CONFIGS["c0"].with_(T=64, seed=52)
+    d2 = synth.layer(c2)
+    ly2 = moe.MoeLayer(c2, d2)
+    x2 = dev_bf16(d2["hidden"])
+    ws2 = ly2.workspace(64, moe.MOE_OUT_F32)
+    out2 = torch.empty((64, c2.H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def step():
+        for l in range(L):
+            nxt = layers[l + 1] if l + 1 < L else None
+            layers[l].forward_chain(xs[l], xs[l + 1], wss[l], flags | (moe.MOE_LOGITS_GIVEN if l else 0), nxt,
+                                    wss[l + 1] if nxt is not None else None, stream=stream)
+        ly2.forward(x2, out2, ws2, moe.MOE_OUT_F32, stream=stream)
+
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in xs[1:]] + [out2.clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for x in xs[1:]:
+            x.zero_()
+        out2.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = xs[1:] + [out2]
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {r}: output {i} differs"
+        _ = (x2.float() * 2).sum().item()
