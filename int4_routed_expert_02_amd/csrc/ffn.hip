@@ -758,7 +758,11 @@ int ffn_bm(int mode, int wbits, int rows, int groups, int nt)
 {
     const int mean = groups > 0 ? rows / groups : rows;
     if (mean < 24) return 16;
-    if (mode == 1 && wbits == 4) return 64;
+    // the int4 down GEMM of a narrow output (fewer than 32 128-column tiles)
+    // takes 64-row tiles, its stage being small and more workgroups hiding the
+    // short k loop's prologue; a wide one (H = 6144) follows the rule below,
+    // which reads each expert's weights fewer times
+    if (mode == 1 && wbits == 4 && nt < 32) return 64;
     const long t128 = ((long)rows / 128 + (groups > 1 ? groups / 2 : 0)) * nt;
     const long slots = 512;
     if (t128 < slots * 9 / 10) return 64;
@@ -808,6 +812,8 @@ static hipError_t launch_mode(const FfnArgs &a, int rows_total, int groups, hipS
                 return launch_three<MODE, WBITS, 64, 256>(a, slots, st);
             return launch_three<MODE, WBITS, 64>(a, slots, st);
         }
+        if constexpr (MODE == 1 && WBITS == 4)
+            if (a.N % 256 == 0 && a.N >= 4096) return launch_three<MODE, WBITS, 128, 256>(a, slots, st);
         return launch_three<MODE, WBITS, 128>(a, slots, st);
     }
     if (bm == 16) return launch_one<MODE, WBITS, 16, 64, 1, 4>(a, slots, st);
