@@ -802,17 +802,15 @@ __device__ __forceinline__ int dx_logical_unit(int b)
 
 __host__ __device__ __forceinline__ int dx_token_halves(int T) { return (T + 15) / 16; }
 
+// Logical unit L in the weight format of its expert (WBITS: the shared
+// expert's format for its units, int4 for the routed ones).
 template <int WBITS, int EPL>
-__global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nunits)
+__device__ __forceinline__ void dec_unit(const DecArgs &a, DxSmem<WBITS> &sm, int L)
 {
-    __shared__ DxSmem<WBITS> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
     const int nth = dx_token_halves(a.T);
     const int nsh = a.sh_bits ? (a.Ish / DX_ROWS) * nth : 0;
-    const int L = dx_logical_unit(blockIdx.x);
-    if (L >= nunits) return;
     const bool shared = L < nsh;
-    if ((shared ? a.sh_bits : 4) != WBITS) return;  // the launch instantiates one weight format
     const size_t rbytes = (size_t)a.H * WBITS / 8;
     const uint8_t *grow, *urow, *dq;
     const float *dsc;
@@ -866,6 +864,31 @@ __global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nun
         expert_body<WBITS, 1>(a, sm, n, nr, pr, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
     else
         expert_body<WBITS, 2>(a, sm, n, nr, pr, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
+}
+
+// One launch for every unit.  SH8 (an int8 shared expert): its units take
+// the int8 body, the routed ones the int4 body, in one LDS area sized for
+// either, so the routed units do not wait for a separate shared-expert
+// launch to drain; otherwise every unit takes the int4 body.
+template <bool SH8, int EPL>
+__global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nunits)
+{
+    const int L = dx_logical_unit(blockIdx.x);
+    if (L >= nunits) return;
+    if constexpr (SH8) {
+        __shared__ union {
+            DxSmem<4> s4;
+            DxSmem<8> s8;
+        } sm;
+        const int nsh = (a.Ish / DX_ROWS) * dx_token_halves(a.T);
+        if (L < nsh)
+            dec_unit<8, EPL>(a, sm.s8, L);
+        else
+            dec_unit<4, EPL>(a, sm.s4, L);
+    } else {
+        __shared__ DxSmem<4> sm;
+        dec_unit<4, EPL>(a, sm, L);
+    }
 }
 
 // ---------------------------------------------------------------- combine
@@ -1207,13 +1230,14 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
         e = hipEventRecord(d.ev0, st);
         if (e != hipSuccess) return e;
     }
-    if (d.sh_bits == 8) hipLaunchKernelGGL((k_dec_expert<8, 1>), dim3(grid), dim3(DX_THREADS), 0, st, a, nunits);
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(grid), dim3(DX_THREADS), 0, st, a, nunits); };
+    const bool sh8 = d.sh_bits == 8;
     if (d.E <= 64)
-        hipLaunchKernelGGL((k_dec_expert<4, 1>), dim3(grid), dim3(DX_THREADS), 0, st, a, nunits);
+        sh8 ? go(k_dec_expert<true, 1>) : go(k_dec_expert<false, 1>);
     else if (d.E <= 128)
-        hipLaunchKernelGGL((k_dec_expert<4, 2>), dim3(grid), dim3(DX_THREADS), 0, st, a, nunits);
+        sh8 ? go(k_dec_expert<true, 2>) : go(k_dec_expert<false, 2>);
     else
-        hipLaunchKernelGGL((k_dec_expert<4, 4>), dim3(grid), dim3(DX_THREADS), 0, st, a, nunits);
+        sh8 ? go(k_dec_expert<true, 4>) : go(k_dec_expert<false, 4>);
     e = hipGetLastError();
     if (e == hipSuccess && d.ev1) e = hipEventRecord(d.ev1, st);
     if (e != hipSuccess || d.experts_only) return e;
