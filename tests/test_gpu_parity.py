@@ -340,15 +340,24 @@ def test_decode_chain_against_oracle():
             assert np.all(np.abs(a - b) <= np.maximum(ulp, 1e-4 * rms)), f"layer {l}: {diff}"
 
 
-def test_decode_chain_matches_unchained():
+CHAIN_STACKS = {
+    "c1": synth.CONFIGS["c1"],
+    # an int8 shared expert: its units share the expert launch with the int4 routed ones
+    "c4_int8_shared_T32": synth.CONFIGS["c4"].with_(T=32, layers=4, seed=37),
+}
+
+
+@pytest.mark.parametrize("cname", sorted(CHAIN_STACKS))
+def test_decode_chain_matches_unchained(cname):
     """The chained decode step (moe_layer_forward_chain: each combine takes the
-    next layer's router logits) over the 23-layer stack, on its own
-    trajectory.  At every layer the chained call is compared with the
-    unchained moe_layer_forward on the same input -- the path
+    next layer's router logits) over a layer stack (the 23-layer c1 step, and
+    four c4-shape layers with an int8 shared expert), on its own trajectory.
+    At every layer the chained call is compared with the unchained
+    moe_layer_forward on the same input -- the path
     test_decode_stack_on_oracle_trajectory checks against the oracle: the
     routing (ids bit-exact outside near ties, w within 1e-5) and the output."""
     import torch
-    cfg = synth.CONFIGS["c1"]
+    cfg = CHAIN_STACKS[cname]
     T, k, H = cfg.T, cfg.k, cfg.H
     flags = moe.MOE_ADD_RESIDUAL
     layers = [moe.MoeLayer(cfg, synth.layer(cfg, l, with_hidden=False)) for l in range(cfg.layers)]
