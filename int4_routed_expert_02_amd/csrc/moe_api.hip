@@ -667,11 +667,23 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         side = side_stream(hs);
         if (!side) side_lock.unlock();
     }
+    // Launch order, set by measurement: where the shared expert holds at least
+    // as much work as the routed experts (I_shared >= top_k * I) the router is
+    // enqueued first, so its workgroups are not queued behind the shared
+    // GEMM's and the shared tiles fill the machine around the small selection
+    // and scatter grids (c2 layer 144 -> 130 us; c4 unchanged); where the
+    // routed work dominates (c3) the shared expert goes first (router first
+    // measured 1% slower there).
+    const bool router_first = (long)s->I_shared >= (long)s->top_k * s->I;
+    auto shared_side = [&]() -> int {
+        if (!side) return MOE_OK;
+        return run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr, 1,
+                       1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<uint16_t>(ws, L.shy), side->st, false, nullptr,
+                       true);
+    };
     auto routed = [&]() -> int {
-        if (side) {
-            int r = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr,
-                            nullptr, 1, 1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<uint16_t>(ws, L.shy), side->st,
-                            false, nullptr, true);
+        if (!router_first) {
+            const int r = shared_side();
             if (r) return r;
         }
         hipError_t e = moe::launch_router(hidden, w->router_w, w->router_bias, s->T, s->H, s->E, s->top_k,
@@ -679,6 +691,10 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
                                           at<float>(ws, L.zpart), KS, ids, at<float>(ws, L.w), at<float>(ws, L.gap),
                                           pscale, sbc, hs);
         if (e != hipSuccess) return MOE_ERR_HIP;
+        if (router_first) {
+            const int r = shared_side();
+            if (r) return r;
+        }
         e = moe::launch_scatter(ids, sbc, nsb, P, s->E, sbt * s->top_k, counts, offsets, sorted, inv, hs);
         if (e != hipSuccess) return MOE_ERR_HIP;
         if (ev_start && hipEventRecord((hipEvent_t)ev_start, hs) != hipSuccess) return MOE_ERR_HIP;
