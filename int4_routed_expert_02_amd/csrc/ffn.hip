@@ -336,8 +336,11 @@ __device__ __forceinline__ u32x4 weight_fragment(const uint8_t *bp)
 }
 
 // One (m-tile, n-tile) of expert e in the WBITS format; smem3 / sCor: the
-// kernel's LDS (the stage ring, dynamic, and the row corrections).
-template <int MODE, int WBITS, int BM, int BN = 128>
+// kernel's LDS (the stage ring, dynamic, and the row corrections).  RS: the
+// row sums of A come precomputed (a.rsum) instead of from an MFMA against a
+// constant fragment at every k-step (which every n-tile of a row block would
+// repeat).
+template <int MODE, int WBITS, int BM, int BN = 128, bool RS = false>
 __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int rows, int n0, uint8_t *smem3,
                                           float *sCor)
 {
@@ -348,6 +351,7 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
     constexpr int NB = BN / 4 / 16;     // 16-column blocks per wave and matrix
     constexpr int CB = MB / 4;          // offset-correction blocks per wave
     static_assert(MB % 4 == 0, "row blocks split evenly over the waves");
+    static_assert(!RS || WBITS != 2, "precomputed row sums: int4 and int8 families");
     const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(wn);  // the same, known wave-uniform
 
@@ -455,13 +459,15 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
                 // (the correction blocks depend on the wave, so their fragments
                 // are read again rather than picked from af by a run-time index;
                 // a block past the valid ones is skipped, by a wave-uniform test)
+                if constexpr (!RS) {
 #pragma unroll
-                for (int c = 0; c < CB; ++c) {
-                    if (4 * c >= MV) break;
-                    if (4 * c + 3 >= MV && wu + 4 * c >= MV) continue;
-                    const int r = (wn + 4 * c) * 16 + (lane & 15);
-                    const int chunk = ks * 4 + (lane >> 4);
-                    cor[c] = mma(cneg, *(const u32x4 *)(sa + r * 128 + ((chunk ^ aswz(r)) * 16)), cor[c]);
+                    for (int c = 0; c < CB; ++c) {
+                        if (4 * c >= MV) break;
+                        if (4 * c + 3 >= MV && wu + 4 * c >= MV) continue;
+                        const int r = (wn + 4 * c) * 16 + (lane & 15);
+                        const int chunk = ks * 4 + (lane >> 4);
+                        cor[c] = mma(cneg, *(const u32x4 *)(sa + r * 128 + ((chunk ^ aswz(r)) * 16)), cor[c]);
+                    }
                 }
 #pragma unroll
                 for (int x = 0; x < NMAT; ++x)
@@ -547,12 +553,14 @@ __device__ __forceinline__ void ffn3_tile(const FfnArgs &a, int e, int row0, int
                     const int r = i * 16 + (lane & 15);
                     af[i] = *(const u32x4 *)(sa + r * 256 + ((chunk ^ (r & 15)) * 16));
                 }
+                if constexpr (!RS) {
 #pragma unroll
-                for (int c = 0; c < CB; ++c) {
-                    if (4 * c >= MV) break;
-                    if (4 * c + 3 >= MV && wu + 4 * c >= MV) continue;
-                    const int r = (wn + 4 * c) * 16 + (lane & 15);
-                    cor[c] = mma(cneg, *(const u32x4 *)(sa + r * 256 + ((chunk ^ (r & 15)) * 16)), cor[c]);
+                    for (int c = 0; c < CB; ++c) {
+                        if (4 * c >= MV) break;
+                        if (4 * c + 3 >= MV && wu + 4 * c >= MV) continue;
+                        const int r = (wn + 4 * c) * 16 + (lane & 15);
+                        cor[c] = mma(cneg, *(const u32x4 *)(sa + r * 256 + ((chunk ^ (r & 15)) * 16)), cor[c]);
+                    }
                 }
 #pragma unroll
                 for (int x = 0; x < NMAT; ++x)
@@ -616,9 +624,26 @@ epilogue:
     // Epilogue.  Lane l holds, for block (i, j), row m = 16 i + l % 16 and the
     // columns 4 (l / 16) .. 4 (l / 16) + 3 of its 16 x 16 block; the offset
     // correction of every row comes back from sCor.
+    if constexpr (RS) {
+        // minus the unpack offset times the row's sum: MODE 0/2 one sum per
+        // source row of A, MODE 1 rsum_parts partials added in order
+        constexpr float CF = F16 ? (WBITS == 4 ? -1032.f : -1152.f) : (WBITS == 4 ? -136.f : -128.f);
+        for (int m = tid; m < rows; m += 256) {
+            const int row = row0 + m;
+            float sum = 0.f;
+            if constexpr (MODE == 1) {
+                const float *pp = a.rsum + (size_t)row * a.rsum_parts;
+                for (int p = 0; p < a.rsum_parts; ++p) sum += pp[p];
+            } else {
+                sum = a.rsum[a.gather ? a.gather[row] / a.kdiv : row];
+            }
+            sCor[m] = CF * sum;
+        }
+    } else {
 #pragma unroll
-    for (int c = 0; c < CB; ++c)
-        if (lane < 16) sCor[(wn + 4 * c) * 16 + lane] = cor[c][0];
+        for (int c = 0; c < CB; ++c)
+            if (lane < 16) sCor[(wn + 4 * c) * 16 + lane] = cor[c][0];
+    }
     const int mloc = lane & 15;
     const int nloc = wn * (BN / 4) + 4 * (lane >> 4);
     const size_t sbase = (size_t)e * a.sstride + n0 + nloc;
@@ -657,6 +682,21 @@ epilogue:
             const int m = ci / CPR, ch = ci % CPR;
             if (m >= rows) continue;
             u32x4 v = *(const u32x4 *)(smem3 + m * HP + ch * 16);
+            // (128-column tiles: a row's sixteen chunks are consecutive lanes)
+            if (BN == 128 && a.hsum) {
+                // the row's sum over the tile's columns of the f16 values the
+                // down GEMM reads: a lane's eight in order, then the row's
+                // sixteen lanes by a fixed butterfly
+                float hs = 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    hs += (float)__builtin_bit_cast(_Float16, (uint16_t)(v[q] & 0xFFFFu));
+                    hs += (float)__builtin_bit_cast(_Float16, (uint16_t)(v[q] >> 16));
+                }
+#pragma unroll
+                for (int o = 1; o < CPR; o <<= 1) hs += __shfl_xor(hs, o, WAVE);
+                if (ch == 0) a.hsum[(size_t)(row0 + m) * (a.N / BN) + n0 / BN] = hs;
+            }
             if (WBITS == 4) v = interleave_bf16x8(v);
             *(u32x4 *)((uint16_t *)a.out + (size_t)(row0 + m) * a.ldo + n0 + ch * 8) = v;
         }
@@ -699,7 +739,7 @@ epilogue:
     }
 }
 
-template <int MODE, int WBITS, int BM, int BN = 128>
+template <int MODE, int WBITS, int BM, int BN = 128, bool RS = false>
 __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
 {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem3[];
@@ -710,7 +750,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn3(FfnArgs a)
     const int slot = (q / NT) * 8 + xcd;
     int e, row0, rows;
     if (!find_tile<BM>(a, slot, e, row0, rows)) return;
-    ffn3_tile<MODE, WBITS, BM, BN>(a, e, row0, rows, nt * BN, smem3, sCor);
+    ffn3_tile<MODE, WBITS, BM, BN, RS>(a, e, row0, rows, nt * BN, smem3, sCor);
 }
 
 // A family whose experts are int4 or int2 each (a.ebits): the tile's expert
@@ -788,7 +828,10 @@ static hipError_t launch_three(const FfnArgs &a, int slots, hipStream_t st)
     const long grid = (long)((slots + 7) / 8 * 8) * NT;
     if (grid <= 0) return hipSuccess;
     const size_t lds = (size_t)Ff3<MODE, WBITS, BM, BN>::RING;
-    hipLaunchKernelGGL((k_ffn3<MODE, WBITS, BM, BN>), dim3((unsigned)grid), dim3(256), lds, st, a);
+    if (a.rsum)
+        hipLaunchKernelGGL((k_ffn3<MODE, WBITS, BM, BN, true>), dim3((unsigned)grid), dim3(256), lds, st, a);
+    else
+        hipLaunchKernelGGL((k_ffn3<MODE, WBITS, BM, BN, false>), dim3((unsigned)grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
@@ -1066,6 +1109,45 @@ static hipError_t launch_mix(const FfnArgs &a, int slots, hipStream_t st)
 // int4/int2 families: the register-staged tiles, 16 or 64 rows by the mean
 // rows per expert, 64 columns.
 int ffn_bm(int mode, int wbits, int rows, int groups, int nt);
+
+bool ffn3_taken(int mode, int wbits, int rows_total, int groups, int N)
+{
+    return N % 128 == 0 && ffn_bm(mode, wbits, rows_total, groups, N / 128) != 16;
+}
+
+// f32 sum of each bf16 row (K values, rows lda elements apart): one wave per
+// row, 16-byte loads where the rows allow them; a lane adds its values in
+// order, the wave by a fixed butterfly.
+__global__ __launch_bounds__(256) void k_rowsum_bf16(const uint16_t *__restrict__ A, int lda, int rows, int K,
+                                                      float *__restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const uint16_t *r = A + (size_t)row * lda;
+    auto bf = [](uint32_t u) { return __uint_as_float(u << 16); };
+    float sum = 0.f;
+    const int K8 = (lda & 7) ? 0 : K / 8 * 8;
+    for (int k = lane * 8; k < K8; k += WAVE * 8) {
+        const u32x4 v = *(const u32x4 *)(r + k);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            sum += bf(v[q] & 0xFFFFu);
+            sum += bf(v[q] >> 16);
+        }
+    }
+    for (int k = K8 + lane; k < K; k += WAVE) sum += bf(r[k]);
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) sum += __shfl_xor(sum, o, WAVE);
+    if (lane == 0) out[row] = sum;
+}
+
+hipError_t launch_rowsum_bf16(const uint16_t *A, int lda, int rows, int K, float *out, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rowsum_bf16, dim3((rows + 3) / 4), dim3(256), 0, st, A, lda, rows, K, out);
+    return hipGetLastError();
+}
 
 template <int MODE>
 static hipError_t launch_mix_mode(const FfnArgs &a, int rows_total, int groups, hipStream_t st)

@@ -15,11 +15,13 @@ using moe::FfnArgs;
 // A second stream per device (default priority, non-blocking) for work that
 // does not depend on the routing: the tiled regime runs the shared expert on it
 // while the router, the permutation and the routed GEMMs run on the caller's
-// stream, forked and joined with events (a captured graph gets two branches).
-// The mutex keeps one call's fork/join pair from interleaving with another's.
+// stream, forked and joined with events (a captured graph gets two branches);
+// `xs` marks the layer input's row sums, which the side stream computes and
+// the routed GEMMs wait for.  The mutex keeps one call's events from
+// interleaving with another's.
 struct SideStream {
     hipStream_t st = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr, xs = nullptr;
 };
 constexpr int MAX_DEVICES = 64;
 SideStream g_side[MAX_DEVICES];
@@ -34,12 +36,14 @@ SideStream *side_stream(hipStream_t caller)
         // not created under graph capture: the caller's stream then runs everything
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-        // all three or none: a partial set is released and the next call tries again
+        // all four or none: a partial set is released and the next call tries again
         SideStream n;
         if (hipStreamCreateWithFlags(&n.st, hipStreamNonBlocking) != hipSuccess) return nullptr;
         if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+            hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&n.xs, hipEventDisableTiming) != hipSuccess) {
             if (n.fork) (void)hipEventDestroy(n.fork);
+            if (n.join) (void)hipEventDestroy(n.join);
             (void)hipStreamDestroy(n.st);
             return nullptr;
         }
@@ -117,6 +121,9 @@ int check_qmat(const moe_qmat &m)
 // Workspace sections, in bytes, each 256-aligned.
 struct Layout {
     size_t zpart, sbc, ids, w, gap, pscale, counts, offsets, sorted, inv, hbuf, shh, ypair, shy, total;
+    // row sums: of the layer input (T), of the routed and shared h rows
+    // (partials per 128-column tile of the gate/up GEMM)
+    size_t xsum, hsum, shsum;
     // Q8_0-style activations: x codes and block scales, h (f32), its codes and scales (routed, shared)
     size_t xq, xd, hf, hq, hd, shf, shq, shd;
     bool decode;  // the small-batch path serves this shape (MOE_WS_LAYER)
@@ -155,6 +162,8 @@ Layout layout(const moe_shape *s, int which)
         L.zpart = L.sbc = take(a > b ? a : b);
     } else if (which == MOE_WS_EXPERT_FFN) {
         L.hbuf = take(P * (size_t)s->I * 2);  // h, f16
+        L.xsum = take(T * 4);
+        L.hsum = take(P * (size_t)((s->I + 127) / 128) * 4);
     } else if (use_decode(s)) {
         // pair-indexed buffers, no permutation: the routing of the whole
         // batch; per chunk of tokens (reused by the chunks in turn) the
@@ -181,6 +190,9 @@ Layout layout(const moe_shape *s, int which)
         L.sorted = take(P * 4);
         L.inv = take(P * 4);
         L.hbuf = take(P * (size_t)s->I * 2);  // h, f16
+        L.xsum = take(T * 4);
+        L.hsum = take(P * (size_t)((s->I + 127) / 128) * 4);
+        if (s->shared_bits) L.shsum = take(T * (size_t)((s->I_shared + 127) / 128) * 4);
         // the routed and shared output rows: f16, f32 in the Q8 mode
         const size_t yb = (s->flags & MOE_ACT_Q8) ? 4 : 2;
         L.ypair = take(P * (size_t)s->H * yb);
@@ -225,7 +237,22 @@ int check_ws(const moe_shape *s, int which, void *ws, size_t ws_bytes)
 
 int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
                  const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, void *y,
-                 hipStream_t st, const uint8_t *ebits = nullptr, bool y_f16 = false);
+                 hipStream_t st, const uint8_t *ebits = nullptr, bool y_f16 = false, const float *hsum = nullptr);
+
+// Precomputed row sums (of x for gate/up, of h for down) in place of the
+// offset-correction MFMA of every k-step pay where the contraction is long:
+// measured at K = 6144 (gate/up) and 2048 (down) of the GLM-class layer
+// (layer 1.951 -> 1.909 ms on one box), and slower at the Nano shape's
+// K = 1024 and 512 (c2 130 -> 137 us), whose short k loops gain little and
+// pay the extra row-sum work.
+constexpr int RS_MIN_K = 2048;
+
+// The h-row sum partials a gate/up launch leaves in hsum (its pipelined
+// tiles write them, where the down GEMM takes precomputed sums), or null.
+const float *gateup_hsum(int wbits, int rows, int groups, int I, const uint8_t *ebits, const float *hsum)
+{
+    return hsum && !ebits && I >= RS_MIN_K && moe::ffn3_taken(0, wbits, rows, groups, I) ? hsum : nullptr;
+}
 
 // gate and up of a family with more than one expert share one expert stride
 // (the kernels step both by it); a single expert's strides are never used.
@@ -239,7 +266,7 @@ bool strides_ok(const moe_qmat &gate, const moe_qmat &up, int E)
 int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qmat &gate, const moe_qmat &up,
             const moe_qmat &down, int I, const int32_t *offsets, const int32_t *sorted, int E, int kdiv, int rows,
             const float *pscale, uint16_t *hbuf, void *y, hipStream_t st, bool gateup_only = false,
-            const uint8_t *ebits = nullptr, bool y_f16 = false)
+            const uint8_t *ebits = nullptr, bool y_f16 = false, const float *xsum = nullptr, float *hsum = nullptr)
 {
     FfnArgs g;
     memset(&g, 0, sizeof(g));
@@ -261,17 +288,23 @@ int run_ffn(const moe_shape *s, int wbits, const uint16_t *hidden, const moe_qma
     g.out = hbuf;
     g.ldo = I;
     g.ebits = ebits;
+    // precomputed x row sums and the h row sums for the down GEMM (the
+    // pipelined int4/int8 tiles; mixed families take the MFMA corrections)
+    g.rsum = (ebits || s->H < RS_MIN_K) ? nullptr : xsum;
+    g.rsum_parts = 1;
+    const float *hs = gateup_hsum(wbits, rows, offsets ? E : 1, I, ebits, hsum);
+    g.hsum = (float *)hs;
     hipError_t e = moe::launch_ffn(0, wbits, g, rows, offsets ? E : 1, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (gateup_only) return MOE_OK;
-    return run_ffn_down(s, wbits, down, I, offsets, sorted, E, rows, pscale, hbuf, y, st, ebits, y_f16);
+    return run_ffn_down(s, wbits, down, I, offsets, sorted, E, rows, pscale, hbuf, y, st, ebits, y_f16, hs);
 }
 
 // The down GEMM on h (f16) of sorted rows; y: f32 rows in sorted order (the
 // split API), or (y_f16: the layer's own rows) f16 rows in pair order.
 int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, const int32_t *offsets,
                  const int32_t *sorted, int E, int rows, const float *pscale, const uint16_t *hbuf, void *y,
-                 hipStream_t st, const uint8_t *ebits, bool y_f16)
+                 hipStream_t st, const uint8_t *ebits, bool y_f16, const float *hsum)
 {
     FfnArgs d;
     memset(&d, 0, sizeof(d));
@@ -295,6 +328,8 @@ int run_ffn_down(const moe_shape *s, int wbits, const moe_qmat &down, int I, con
     d.ebits = ebits;
     d.out_f16 = y_f16 ? 1 : 0;
     d.out_by_pair = y_f16 ? 1 : 0;
+    d.rsum = hsum;  // the gate/up tiles' partials, one per 128 columns of h
+    d.rsum_parts = I / 128;
     return hip_status(moe::launch_ffn(1, wbits, d, rows, offsets ? E : 1, st));
 }
 
@@ -446,8 +481,14 @@ int moe_expert_ffn(const moe_shape *s, const moe_bf16 *hidden, const moe_weights
     if (!strides_ok(w->gate, w->up, s->E)) return MOE_ERR_UNSUPPORTED;
     const Layout L = layout(s, MOE_WS_EXPERT_FFN);
     const int wbits = (s->flags & MOE_EXPERT_INT8) ? 8 : 4;
+    if ((s->flags & MOE_TEST_GATEUP_SUMS) && (wbits != 4 || 2 * s->I > s->H)) return MOE_ERR_UNSUPPORTED;
+    if ((s->flags & MOE_EXPERT_MIXED) && !w->expert_bits) return MOE_ERR_NULL;
+    float *xsum = at<float>(ws, L.xsum);
+    // (the exactness test takes the precomputed sums at any K)
+    if ((s->H >= RS_MIN_K || (s->flags & MOE_TEST_GATEUP_SUMS)) &&
+        moe::launch_rowsum_bf16(hidden, s->H, s->T, s->H, xsum, (hipStream_t)stream) != hipSuccess)
+        return MOE_ERR_HIP;
     if (s->flags & MOE_TEST_GATEUP_SUMS) {
-        if (wbits != 4 || 2 * s->I > s->H) return MOE_ERR_UNSUPPORTED;
         FfnArgs g;
         memset(&g, 0, sizeof(g));
         g.A = hidden;
@@ -466,13 +507,14 @@ int moe_expert_ffn(const moe_shape *s, const moe_bf16 *hidden, const moe_weights
         g.N = s->I;
         g.out = y_pairs;
         g.ldo = s->H;
+        g.rsum = xsum;
+        g.rsum_parts = 1;
         return hip_status(moe::launch_ffn(2, 4, g, s->T * s->top_k, s->E, (hipStream_t)stream));
     }
-    if ((s->flags & MOE_EXPERT_MIXED) && !w->expert_bits) return MOE_ERR_NULL;
     return run_ffn(s, wbits, hidden, w->gate, w->up, w->down, s->I, offsets, sorted_pairs, s->E, s->top_k,
                    s->T * s->top_k, pair_scale, at<uint16_t>(ws, L.hbuf), y_pairs, (hipStream_t)stream,
                    (s->flags & MOE_STAGE_GATEUP_ONLY) != 0,
-                   (s->flags & MOE_EXPERT_MIXED) ? w->expert_bits : nullptr);
+                   (s->flags & MOE_EXPERT_MIXED) ? w->expert_bits : nullptr, false, xsum, at<float>(ws, L.hsum));
 }
 
 int moe_combine(const moe_shape *s, const float *y_pairs, const int32_t *inv_pos, const float *topk_w,
@@ -656,6 +698,13 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
                                               s->top_k, (s->flags & MOE_OUT_F32) ? 1 : 0, 0, 0, hs));
     }
 
+    // row sums of the layer input (the gate/up GEMMs' offset correction),
+    // read by the routed and the shared experts: computed first thing on the
+    // side stream where there is one (the routed gate/up waits for its event,
+    // long since recorded by then), else on the caller's stream
+    float *xsum = at<float>(ws, L.xsum), *hsum = at<float>(ws, L.hsum);
+    const bool xrs = s->H >= RS_MIN_K;  // the gate/up GEMMs take precomputed x row sums
+
     // the shared expert (no dependence on the routing) on the side stream,
     // except in the profiled call, whose events time the routed gate/up alone.
     // Once forked, the side stream is joined back on every path, errors too,
@@ -677,9 +726,12 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
     const bool router_first = (long)s->I_shared >= (long)s->top_k * s->I;
     auto shared_side = [&]() -> int {
         if (!side) return MOE_OK;
+        if (xrs && (moe::launch_rowsum_bf16(hidden, s->H, s->T, s->H, xsum, side->st) != hipSuccess ||
+                    hipEventRecord(side->xs, side->st) != hipSuccess))
+            return MOE_ERR_HIP;
         return run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr, 1,
                        1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<uint16_t>(ws, L.shy), side->st, false, nullptr,
-                       true);
+                       true, xsum, at<float>(ws, L.shsum));
     };
     auto routed = [&]() -> int {
         if (!router_first) {
@@ -697,15 +749,20 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         }
         e = moe::launch_scatter(ids, sbc, nsb, P, s->E, sbt * s->top_k, counts, offsets, sorted, inv, hs);
         if (e != hipSuccess) return MOE_ERR_HIP;
+        if (xrs && side) {
+            if (hipStreamWaitEvent(hs, side->xs, 0) != hipSuccess) return MOE_ERR_HIP;
+        } else if (xrs && moe::launch_rowsum_bf16(hidden, s->H, s->T, s->H, xsum, hs) != hipSuccess) {
+            return MOE_ERR_HIP;
+        }
         if (ev_start && hipEventRecord((hipEvent_t)ev_start, hs) != hipSuccess) return MOE_ERR_HIP;
         int r = run_ffn(s, 4, hidden, w->gate, w->up, w->down, s->I, offsets, sorted, s->E, s->top_k, P, pscale,
-                        at<uint16_t>(ws, L.hbuf), ypair, hs, ev_stop != nullptr, ebits, true);
+                        at<uint16_t>(ws, L.hbuf), ypair, hs, ev_stop != nullptr, ebits, true, xsum, hsum);
         if (r) return r;
         if (ev_stop) {
             // profiled: the routed gate/up kernel ran alone between the events; now the down GEMM
             if (hipEventRecord((hipEvent_t)ev_stop, hs) != hipSuccess) return MOE_ERR_HIP;
             r = run_ffn_down(s, 4, w->down, s->I, offsets, sorted, s->E, P, pscale, at<uint16_t>(ws, L.hbuf),
-                             ypair, hs, ebits, true);
+                             ypair, hs, ebits, true, gateup_hsum(4, P, s->E, s->I, ebits, hsum));
             if (r) return r;
         }
         return MOE_OK;
@@ -725,7 +782,7 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         if (s->shared_bits) {
             st = run_ffn(s, s->shared_bits, hidden, w->sh_gate, w->sh_up, w->sh_down, s->I_shared, nullptr, nullptr,
                          1, 1, s->T, nullptr, at<uint16_t>(ws, L.shh), at<uint16_t>(ws, L.shy), hs, false, nullptr,
-                         true);
+                         true, xsum, at<float>(ws, L.shsum));
             if (st) return st;
         }
     }

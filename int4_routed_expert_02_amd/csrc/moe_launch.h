@@ -30,6 +30,15 @@ struct FfnArgs {
     const uint8_t *ebits;  // per-expert format (4 or 2) of a mixed family, or null (all WBITS)
     int out_f16;           // MODE 1: output rows in f16 (rounded to nearest even) instead of f32
     int out_by_pair;       // MODE 1: row r is written at row pair_of_row[r] (pair order) instead of r
+    // Row sums of A, precomputed (null: the kernels take them with an MFMA
+    // per k-step): MODE 0/2 one f32 per source row of A (indexed like A, by
+    // gather / kdiv); MODE 1 rsum_parts partials per row, added in order.
+    const float *rsum;
+    int rsum_parts;
+    // MODE 0 (pipelined tiles): where set, the sum of each h row's f16
+    // values over the tile's columns, [rows][N / 128] (partials of the down
+    // GEMM's rsum)
+    float *hsum;
 };
 
 // small-batch regime (decode.hip)
@@ -79,6 +88,11 @@ hipError_t launch_pair_hist(const int32_t *ids, int P, int E, int chunk, int nbl
 hipError_t launch_scatter(const int32_t *ids, const int32_t *bcounts, int nblocks, int P, int E, int chunk,
                           int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *inv, hipStream_t st);
 hipError_t launch_ffn(int mode, int wbits, const FfnArgs &a, int rows_total, int groups, hipStream_t st);
+// Whether launch_ffn (no mixed family) takes the pipelined tiles, which use
+// rsum and write hsum, for this shape.
+bool ffn3_taken(int mode, int wbits, int rows_total, int groups, int N);
+// f32 sum of each bf16 row of A (rows x K, row stride lda elements).
+hipError_t launch_rowsum_bf16(const uint16_t *A, int lda, int rows, int K, float *out, hipStream_t st);
 // Q8_0-style int8 activations (A = int8 codes, ad = their block scales);
 // mode 0 writes h as f32, mode 1 the down rows
 hipError_t launch_ffn_q8(int mode, int wbits, const FfnArgs &a, int rows_total, int groups, hipStream_t st);
