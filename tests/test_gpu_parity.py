@@ -156,10 +156,18 @@ def test_integer_exact_gateup_sums(T):
     assert np.array_equal(yc[:, cfg.I:2 * cfg.I], u_ref)
 
 
-def test_split_api_matches_oracle():
+SPLIT_CFGS = {
+    "c0_T64": synth.CONFIGS["c0"].with_(T=64, seed=61, rsf=1.5),
+    # contractions of 2048 and more: the gate/up and down GEMMs take precomputed row sums
+    "H2048_T64": synth.CONFIGS["c0"].with_(T=64, H=2048, I=2048, I_sh=2048, seed=62, rsf=1.5),
+}
+
+
+@pytest.mark.parametrize("cname", sorted(SPLIT_CFGS))
+def test_split_api_matches_oracle(cname):
     """router -> permute -> expert_ffn (routed, pre-scaled) -> expert_ffn (shared) -> combine."""
     import torch
-    cfg = synth.CONFIGS["c0"].with_(T=64, seed=61, rsf=1.5)
+    cfg = SPLIT_CFGS[cname]
     d = synth.layer(cfg)
     layer = moe.MoeLayer(cfg, d)
     T, k, E, H = cfg.T, cfg.k, cfg.E, cfg.H
