@@ -1,0 +1,90 @@
+"""GPU parity over a seeded sweep of layer shapes (both regimes, both tile
+paths, with and without precomputed row sums): the HIP path through the C
+ABI against the CPU oracle, at the bars of test_gpu_parity.py.  The shapes
+are drawn once from a fixed seed and kept where moe_validate_shape accepts
+them and the oracle finishes quickly."""
+import numpy as np
+import pytest
+
+import int4_routed_expert_02_amd as moe
+import synth
+from gpu_util import check_output, check_routing, run_layer, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _sweep(n=14, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = {}
+    tries = 0
+    while len(out) < n and tries < 2000:
+        tries += 1
+        E = int(rng.choice([4, 8, 16, 32, 64, 128, 256]))
+        k = int(rng.integers(1, min(8, E) + 1))
+        H = int(rng.choice([256, 512, 1024, 2048, 3072]))
+        I = int(rng.choice([64, 128, 192, 256, 512, 1024, 2048]))
+        shared = int(rng.choice([0, 4, 4, 8]))
+        I_sh = int(rng.choice([128, 512, 2048])) if shared else 128
+        T = int(rng.choice([1, 7, 16, 33, 64, 65, 130, 257, 400]))
+        n_group, topk_group = 1, 1
+        if E >= 16 and rng.random() < 0.4:
+            n_group = int(rng.choice([g for g in (2, 4, 8) if E % g == 0]))
+            topk_group = int(rng.integers(1, n_group + 1))
+            if k > topk_group * (E // n_group):
+                continue
+        rsf = float(rng.choice([1.0, 2.5]))
+        cost = T * (k * 3 * H * I + (3 * H * I_sh if shared else 0))
+        if cost > 6e8:
+            continue
+        cfg = synth.LayerConfig(f"sweep{len(out)}", T=T, H=H, E=E, k=k, I=I, I_sh=I_sh, n_group=n_group,
+                                topk_group=topk_group, rsf=rsf, shared_bits=shared, seed=7000 + len(out))
+        out[cfg.name] = cfg
+    return out
+
+
+def _sweep_tiled(n=10, seed=20261204):
+    """Few experts and enough rows per expert for the pipelined tiles, with
+    contractions of 2048 and more (precomputed row sums) mixed in."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    tries = 0
+    while len(out) < n and tries < 2000:
+        tries += 1
+        E = int(rng.choice([4, 8]))
+        k = int(rng.integers(1, 3))
+        H = int(rng.choice([1024, 2048, 3072]))
+        I = int(rng.choice([256, 512, 2048]))
+        shared = int(rng.choice([0, 4, 8]))
+        I_sh = int(rng.choice([512, 2048])) if shared else 128
+        T = int(rng.choice([100, 130, 257]))
+        rsf = float(rng.choice([1.0, 2.5]))
+        cost = T * (k * 3 * H * I + (3 * H * I_sh if shared else 0))
+        if cost > 2e9:
+            continue
+        cfg = synth.LayerConfig(f"tiled{len(out)}", T=T, H=H, E=E, k=k, I=I, I_sh=I_sh, rsf=rsf,
+                                shared_bits=shared, seed=7100 + len(out))
+        out[cfg.name] = cfg
+    return out
+
+
+SWEEP = {**_sweep(), **_sweep_tiled()}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.load()
+
+
+@pytest.mark.parametrize("name", sorted(SWEEP))
+def test_sweep_layer_parity(name):
+    cfg = SWEEP[name]
+    if moe.moe_validate_shape(moe.shape_of(cfg)) != moe.MOE_OK:
+        pytest.skip("shape outside what the kernels cover")
+    say(f"[sweep] {name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} I_sh={cfg.I_sh} "
+        f"shared={cfg.shared_bits} groups={cfg.n_group}/{cfg.topk_group} rsf={cfg.rsf}")
+    d = synth.layer(cfg)
+    got, ids, w, offsets, srt = run_layer(cfg, d)
+    ex = check_routing(cfg, d, d["hidden"], ids, w, offsets, srt, tag=name)
+    check_output(cfg, d, d["hidden"], got, ex, tag=f"{name} (exempt {int(ex.sum())})")
