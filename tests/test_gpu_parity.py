@@ -407,13 +407,21 @@ def test_decode_chain_matches_unchained(cname):
         x = out
 
 
-def test_tiled_graph_replays_match_eager():
+GRAPH_TILED = {
+    "c2_T700": synth.CONFIGS["c2"].with_(T=700, seed=51),
+    # H = 6144: the x row sums on the second stream, waited for by an event
+    "c3_H6144_T300": synth.CONFIGS["c3"].with_(T=300, E=32, k=4, n_group=4, topk_group=2, seed=52),
+}
+
+
+@pytest.mark.parametrize("cname", sorted(GRAPH_TILED))
+def test_tiled_graph_replays_match_eager(cname):
     """The tiled path (the shared expert forked onto the library's second
     stream and joined back) captured in a HIP graph and replayed several
     times with eager work between the replays: every replay gives the eager
     call's bits."""
     import torch
-    cfg = synth.CONFIGS["c2"].with_(T=700, seed=51)
+    cfg = GRAPH_TILED[cname]
     d = synth.layer(cfg)
     ly = moe.MoeLayer(cfg, d)
     x = dev_bf16(d["hidden"])
