@@ -256,8 +256,9 @@ int moe_combine(const moe_shape *shape, const float *y_pairs, const int32_t *inv
  * regime the shared expert runs on a second stream of the current device
  * (created on first use, default priority), forked from and joined back to
  * `stream` with events, so the call stays ordered on `stream` and a captured
- * graph gets two branches.  Calls from several host threads are serialised
- * around that fork and join.
+ * graph gets two branches; for H >= 2048 the input's row sums are computed
+ * there first and the routed GEMMs wait for them by one more event.  Calls
+ * from several host threads are serialised around these events.
  * Workspace: moe_workspace_bytes(shape, MOE_WS_LAYER).
  */
 int moe_layer_forward(const moe_shape *shape, const moe_weights *weights, const moe_bf16 *hidden, void *out,
