@@ -803,6 +803,12 @@ int ffn_bm(int mode, int wbits, int rows, int groups, int nt)
     // short k loop's prologue; a wide one (H = 6144) follows the rule below,
     // which reads each expert's weights fewer times
     if (mode == 1 && wbits == 4 && nt < 32) return 64;
+    // a single group of at least 1024 rows (the shared expert) takes 128-row
+    // tiles even where they leave slots free: it runs beside the routed
+    // experts on the second stream, whose workgroups take those slots (the
+    // GLM-class layer's shared gate/up: 1.832 -> 1.816 ms, three alternating
+    // pairs on one box)
+    if (groups == 1 && rows >= 1024) return 128;
     const long t128 = ((long)rows / 128 + (groups > 1 ? groups / 2 : 0)) * nt;
     const long slots = 512;
     if (t128 < slots * 9 / 10) return 64;
