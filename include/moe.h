@@ -91,9 +91,10 @@ extern "C" {
                                gives; a dot is s_w * sum over blocks of d * (integer sum of code products).
                                Always the tiled kernels (v_mfma_i32_16x16x32_i8); the router is unchanged.
                                moe_expert_ffn and moe_layer_forward_chain return MOE_ERR_UNSUPPORTED */
-#define MOE_EXPERT_MIXED 0x2000u /* routed experts in int4 or int2 per weights->expert_bits (the tiled kernels at
-                               any T; with MOE_ACT_Q8, MOE_TEST_GATEUP_SUMS or in a chained call:
-                               MOE_ERR_UNSUPPORTED) */
+#define MOE_EXPERT_MIXED 0x2000u /* routed experts in int4 or int2 per weights->expert_bits, in both regimes
+                               (the small-batch kernel loads an int2 expert's rows at half the bytes and
+                               widens them to int4 in registers); with MOE_ACT_Q8 or MOE_TEST_GATEUP_SUMS:
+                               MOE_ERR_UNSUPPORTED */
 #define MOE_REGIME_TILED 0x4000u /* moe_layer_forward(_profiled, _noalloc): take the tiled grouped-GEMM kernels at
                                any T (the small-batch weight-streaming kernels are otherwise chosen for
                                the shapes moe_layer_routing names); for measuring the two regimes side by
@@ -102,9 +103,8 @@ extern "C" {
 #define MOE_REGIME_SMALL 0x8000u /* moe_layer_forward(_profiled, _noalloc): take the small-batch kernels at any T,
                                in chunks of 32 tokens (each chunk streams its experts' weights again), for a
                                shape they serve (top_k <= 16, H % 1024 == 0, I and I_shared % 512 == 0),
-                               else MOE_ERR_UNSUPPORTED; with MOE_REGIME_TILED, MOE_ACT_Q8 or
-                               MOE_EXPERT_MIXED: MOE_ERR_UNSUPPORTED.  For measuring the two regimes side
-                               by side */
+                               else MOE_ERR_UNSUPPORTED; with MOE_REGIME_TILED or MOE_ACT_Q8:
+                               MOE_ERR_UNSUPPORTED.  For measuring the two regimes side by side */
 #define MOE_TEST_GATEUP_SUMS 0x100u /* moe_expert_ffn, testing only: write the raw integer-weight sums
                                sum_h x*q of gate into y_pairs[r][0:I] and of up into y_pairs[r][I:2I]
                                (no scale, no activation, no down projection); needs 2*I <= H, int4 */
@@ -344,8 +344,8 @@ const char *moe_status_string(int status);
  * regime serves T <= 64 (at most two chunks of 32 tokens: the measured
  * crossover with the tiled kernels lies between 64 and 96 tokens at the Nano
  * shape), top_k <= 16, H % 1024 == 0, I % 512 == 0 and I_shared % 512 == 0,
- * unless MOE_REGIME_TILED or MOE_REGIME_SMALL decides; MOE_ACT_Q8 and
- * MOE_EXPERT_MIXED always take the tiled kernels.  Chained calls
+ * unless MOE_REGIME_TILED or MOE_REGIME_SMALL decides; MOE_ACT_Q8 always
+ * takes the tiled kernels.  Chained calls
  * (moe_layer_forward_chain), MOE_LOGITS_GIVEN and MOE_STAGE_EXPERTS_ONLY need
  * T <= 32 (one chunk), else MOE_ERR_UNSUPPORTED. */
 int moe_layer_routing(const moe_shape *shape, void *ws, size_t ws_bytes, int32_t **topk_ids, float **topk_w,

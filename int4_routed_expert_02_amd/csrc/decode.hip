@@ -424,6 +424,7 @@ struct DecArgs {
     const float *gs, *us, *ds;
     int64_t qstride, dqstride, sstride, dsstride;
     int I;
+    const uint8_t *ebits;  // [E] each routed expert's format, 4 or 2 (packed int2); null: all int4
     // shared expert
     const uint8_t *sgq, *suq, *sdq;
     const float *sgs, *sus, *sds;
@@ -529,6 +530,54 @@ __device__ __forceinline__ void load_down(DownW<WBITS> &w, f32x4 &sd, const uint
     }
 }
 
+// Int2 experts (element 4c + j of a row in bits 2j..2j+1 of byte c, two's
+// complement) run the int4 body on the same values: each 16-byte chunk of an
+// int4 row (32 values) is 8 bytes of the int2 row, loaded at half the width
+// and widened in registers to the int4 packing (element 2c + i in nibble i
+// of byte c): each 2-bit field spread to the low bits of its own nibble,
+// then its sign bit copied into the nibble's top two bits (-2..1 is the same
+// two's complement value in four bits).  Sixteen codes per 32-bit word.
+__device__ __forceinline__ u32x2 int2_to_int4x16(uint32_t w)
+{
+    u32x2 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t x = (w >> (16 * h)) & 0xFFFFu;
+        x = (x | (x << 8)) & 0x00FF00FFu;
+        x = (x | (x << 4)) & 0x0F0F0F0Fu;
+        x = (x | (x << 2)) & 0x33333333u;
+        const uint32_t sgn = (x >> 1) & 0x11111111u;  // each field's sign bit, at bit 0 of its nibble
+        r[h] = x | (sgn << 2) | (sgn << 3);
+    }
+    return r;
+}
+
+// the int4 chunk of 32 values from its 8-byte int2 form (or the chunk itself)
+__device__ __forceinline__ u32x4 int4_chunk(const u32x4 &c) { return c; }
+__device__ __forceinline__ u32x4 int4_chunk(const u32x2 &c)
+{
+    const u32x2 lo = int2_to_int4x16(c[0]), hi = int2_to_int4x16(c[1]);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// The down slice of an int2 expert: as load_down<4>, each tile's 32 values
+// in 8 bytes (rstride: bytes of an int2 row), widened where they are used.
+struct DownW2 {
+    u32x2 d[DX_TILES];
+};
+
+__device__ __forceinline__ void load_down2(DownW2 &w, f32x4 &sd, const uint8_t *dq, const float *dsc, int64_t rstride,
+                                           int H, int col0, int i0)
+{
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    sd = *(const f32x4 *)(dsc + col0 + 4 * (lane & 31));
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(dq, (uint32_t)(H * rstride));
+    const int voff = (int)((col0 + n) * rstride + (i0 + 32 * g) / 4);
+#pragma unroll
+    for (int tt = 0; tt < DX_TILES; ++tt)
+        w.d[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, (int)(tt * 16 * rstride), 0));
+}
+
 // Position of intermediate j in a row of the on-chip h chunk: with int4
 // weights each 8-group is stored in the unpack's k-slot order
 // (j0, j4, j1, j5, j2, j6, j3, j7).
@@ -605,14 +654,16 @@ __device__ __forceinline__ void xstage_store(const XStage<WBITS> &xs, DxSmem<WBI
 // complete in issue order) while the weights stream behind them.  Weight
 // loads are issued gate/up first, then the down slice, a few chunks ahead of
 // the MFMAs that consume them.
-template <int WBITS, int NMB>
+template <int WBITS, int NMB, bool I2 = false>
 __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm, int n, int nr, const PairRows &pr,
                                             float rsum, const uint8_t *grow, const uint8_t *urow, float sg,
                                             float su, const uint8_t *dq, const float *dsc, int64_t drstride,
                                             int i0, uint16_t *out, int nrows)
 {
+    static_assert(!I2 || WBITS == 4, "int2 experts run the int4 body");
     constexpr int CPL = GU_CPL;
     constexpr int SB = CPL * 64;           // weight bytes of a row per super-stage (512)
+    constexpr int CB = I2 ? 32 : 64;       // bytes of a row per chunk step (an int2 row: half)
     constexpr int KS = DxSmem<WBITS>::KS;  // columns per super-stage (1024 int4, 512 int8)
     constexpr int LDA = DxSmem<WBITS>::LDA;
     constexpr int NCH = NMB == 1 ? 2 : 1;  // independent accumulator chains per matrix (register budget)
@@ -629,9 +680,14 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
     const uint16_t *ap[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) ap[mb] = sm.u.a + (mb * 16 + ln < n ? mb * 16 + ln : 0) * LDA;
-    DownW<WBITS> dw;
+    std::conditional_t<I2, DownW2, DownW<WBITS>> dw;
     f32x4 sdv;
-    u32x4 wg[CPL], wu[CPL];
+    using WChunk = std::conditional_t<I2, u32x2, u32x4>;  // a lane's chunk as loaded
+    WChunk wg[CPL], wu[CPL];
+    auto down_load = [&](int col) {
+        if constexpr (I2) load_down2(dw, sdv, dq, dsc, drstride, a.H, col, i0);
+        else load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, col, i0);
+    };
     // One super-stage; the last one (a separate instance, LAST set) also
     // issues the down slice, so its loads stay where they are written
     // instead of moving to the loop's exit, behind the gate/up MFMAs.
@@ -640,8 +696,8 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
         // gate and up chunk c in adjacent requests: the MFMAs on chunk c can
         // start once its pair has arrived
         auto issue_gu = [&](int c) {
-            wg[c] = *(const u32x4 *)(grow + (size_t)ss * SB + c * 64);
-            wu[c] = *(const u32x4 *)(urow + (size_t)ss * SB + c * 64);
+            wg[c] = *(const WChunk *)(grow + (size_t)ss * (SB / 64 * CB) + c * CB);
+            wu[c] = *(const WChunk *)(urow + (size_t)ss * (SB / 64 * CB) + c * CB);
         };
         XStage<WBITS> xs;
         xstage_load<WBITS>(xs, a, nr, ss, pr);
@@ -669,14 +725,15 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
         for (int c = 0; c < CPL; ++c) {
             if (c + GU_AHEAD < CPL) issue_gu(c + GU_AHEAD);
             else if (LAST && c + GU_AHEAD == CPL) {
-                load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, wave * DX_WCOLS, i0);
+                down_load(wave * DX_WCOLS);
                 asm volatile("" ::: "memory");  // keeps the compiler from sinking these loads to their use
             }
             if constexpr (WBITS == 4) {
+                const u32x4 cg = int4_chunk(wg[c]), cu = int4_chunk(wu[c]);
 #pragma unroll
                 for (int wd = 0; wd < 4; ++wd) {
-                    const u32x4 bg = unpack_int4x8(wg[c][wd]);
-                    const u32x4 bu = unpack_int4x8(wu[c][wd]);
+                    const u32x4 bg = unpack_int4x8(cg[wd]);
+                    const u32x4 bu = unpack_int4x8(cu[wd]);
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
                         const u32x4 af = *(const u32x4 *)(ap[mb] + (4 * c + g) * 32 + 8 * wd);
@@ -733,7 +790,7 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
     float *yl = sm.u.y[wave];
     for (int c0 = 0; c0 < a.H; c0 += DX_RCOLS) {
         const int col0 = c0 + wave * DX_WCOLS;
-        if (c0 > 0) load_down<WBITS>(dw, sdv, dq, dsc, drstride, a.H, col0, i0);
+        if (c0 > 0) down_load(col0);
 #pragma unroll 1
         for (int mb = 0; mb < NMB; ++mb) {
             if (mb * 16 >= n) break;
@@ -750,10 +807,14 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
 #pragma unroll
             for (int tt = 0; tt < DX_TILES; ++tt) {
                 f32x4 d = d0;
+                u32x4 q4 = {0u, 0u, 0u, 0u};  // the tile's int4 words (int4 and int2 experts)
+                if constexpr (I2) q4 = int4_chunk(dw.d[tt]);
+                else if constexpr (WBITS == 4) q4 = u32x4{dw.d[tt][0], dw.d[tt][1], dw.d[tt][2], dw.d[tt][3]};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const u32x4 b = WBITS == 4 ? unpack_int4x8_f16(dw.d[tt][s])
-                                               : unpack_int8x8_f16(u32x2{dw.d[tt][2 * s], dw.d[tt][2 * s + 1]});
+                    u32x4 b;
+                    if constexpr (WBITS == 4) b = unpack_int4x8_f16(q4[s]);
+                    else b = unpack_int8x8_f16(u32x2{dw.d[tt][2 * s], dw.d[tt][2 * s + 1]});
                     d = mfma_f16(fh[s], b, d);
                 }
 #pragma unroll
@@ -804,7 +865,9 @@ __host__ __device__ __forceinline__ int dx_token_halves(int T) { return (T + 15)
 
 // Logical unit L in the weight format of its expert (WBITS: the shared
 // expert's format for its units, int4 for the routed ones).
-template <int WBITS, int EPL>
+// MIX: a family of int4 and int2 experts (a.ebits), a separate instance so
+// that int4-only layers run without the int2 body.
+template <int WBITS, int EPL, bool MIX>
 __device__ __forceinline__ void dec_unit(const DecArgs &a, DxSmem<WBITS> &sm, int L)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
@@ -817,17 +880,21 @@ __device__ __forceinline__ void dec_unit(const DecArgs &a, DxSmem<WBITS> &sm, in
     float sg, su;
     int64_t drs;
     int i0;
+    // (wb: the bits of the expert's rows, WBITS or 2 for an int2 routed
+    // expert, whose 32-value chunks are 8 bytes instead of 16)
     auto locate = [&](const uint8_t *gq, const uint8_t *uq, const uint8_t *dqq, const float *gsc, const float *usc,
-                      const float *dscc, int K, int chunk0) {
+                      const float *dscc, int K, int chunk0, int wb) {
         i0 = chunk0;
         const int row = i0 + wave * 16 + (lane & 15);
-        grow = gq + (size_t)row * rbytes + g * 16;
-        urow = uq + (size_t)row * rbytes + g * 16;
+        const size_t rb = wb == WBITS ? rbytes : (size_t)a.H * wb / 8;
+        const int cb = wb == 2 ? 8 : 16;
+        grow = gq + (size_t)row * rb + g * cb;
+        urow = uq + (size_t)row * rb + g * cb;
         sg = gsc[row];
         su = usc[row];
         dq = dqq;
         dsc = dscc;
-        drs = (int64_t)K * WBITS / 8;
+        drs = (int64_t)K * wb / 8;
     };
     int n, nrows, nr;
     uint16_t *out;
@@ -838,7 +905,7 @@ __device__ __forceinline__ void dec_unit(const DecArgs &a, DxSmem<WBITS> &sm, in
         n = a.T - 16 * th < 16 ? a.T - 16 * th : 16;
         nr = n;
         const PairRows pr{16 * th + lane, 16 * th + lane, 1.0f};
-        locate(a.sgq, a.suq, a.sdq, a.sgs, a.sus, a.sds, a.Ish, (L / nth) * DX_ROWS);
+        locate(a.sgq, a.suq, a.sdq, a.sgs, a.sus, a.sds, a.Ish, (L / nth) * DX_ROWS, WBITS);
         nrows = a.T;
         out = a.ysp;
         expert_body<WBITS, 1>(a, sm, n, nr, pr, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
@@ -847,6 +914,14 @@ __device__ __forceinline__ void dec_unit(const DecArgs &a, DxSmem<WBITS> &sm, in
     // routed: the routing decision, then the unit's expert and pairs; only
     // the rows of those pairs are staged (row r = token of pair r)
     const int v = L - nsh, per = a.I / DX_ROWS;
+    // the experts' formats (a mixed int4/int2 family): four per lane, loaded
+    // now so that the routing hides the load
+    uint32_t fmt4 = 0x04040404u;
+    if (MIX) {
+        fmt4 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fmt4 |= (uint32_t)(4 * lane + j < a.E ? a.ebits[4 * lane + j] : 4) << (8 * j);
+    }
     dec_route<EPL>(a, a.T, a.E, a.k, sm.ids, sm.w, v == 0);
     PairRows pr;
     const int2 un = dec_locate_wave<EPL>(sm.ids, a.T * a.k, a.k, a.E, v / per, pr);
@@ -855,11 +930,21 @@ __device__ __forceinline__ void dec_unit(const DecArgs &a, DxSmem<WBITS> &sm, in
     n = __builtin_amdgcn_readfirstlane(un.y);
     nr = n;
     pr.psc = lane < n ? a.rsf * sm.w[pr.pair] : 0.f;
+    const bool i2 = MIX && WBITS == 4 && ((__shfl(fmt4, e / 4, WAVE) >> (8 * (e % 4))) & 0xFFu) == 2u;  // wave-uniform
     locate(a.gq + (size_t)e * a.qstride, a.uq + (size_t)e * a.qstride, a.dq + (size_t)e * a.dqstride,
            a.gs + (size_t)e * a.sstride, a.us + (size_t)e * a.sstride, a.ds + (size_t)e * a.dsstride, a.I,
-           (v % per) * DX_ROWS);
+           (v % per) * DX_ROWS, i2 ? 2 : WBITS);
     nrows = a.T * a.k;
     out = a.yp;
+    if constexpr (MIX && WBITS == 4) {
+        if (i2) {
+            if (n <= 16)
+                expert_body<4, 1, true>(a, sm, n, nr, pr, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
+            else
+                expert_body<4, 2, true>(a, sm, n, nr, pr, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
+            return;
+        }
+    }
     if (n <= 16)
         expert_body<WBITS, 1>(a, sm, n, nr, pr, rsum, grow, urow, sg, su, dq, dsc, drs, i0, out, nrows);
     else
@@ -870,7 +955,7 @@ __device__ __forceinline__ void dec_unit(const DecArgs &a, DxSmem<WBITS> &sm, in
 // the int8 body, the routed ones the int4 body, in one LDS area sized for
 // either, so the routed units do not wait for a separate shared-expert
 // launch to drain; otherwise every unit takes the int4 body.
-template <bool SH8, int EPL>
+template <bool SH8, int EPL, bool MIX>
 __global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nunits)
 {
     const int L = dx_logical_unit(blockIdx.x);
@@ -882,12 +967,12 @@ __global__ __launch_bounds__(DX_THREADS, 1) void k_dec_expert(DecArgs a, int nun
         } sm;
         const int nsh = (a.Ish / DX_ROWS) * dx_token_halves(a.T);
         if (L < nsh)
-            dec_unit<8, EPL>(a, sm.s8, L);
+            dec_unit<8, EPL, false>(a, sm.s8, L);
         else
-            dec_unit<4, EPL>(a, sm.s4, L);
+            dec_unit<4, EPL, MIX>(a, sm.s4, L);
     } else {
         __shared__ DxSmem<4> sm;
-        dec_unit<4, EPL>(a, sm, L);
+        dec_unit<4, EPL, MIX>(a, sm, L);
     }
 }
 
@@ -1202,6 +1287,7 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     a.sstride = d.sstride;
     a.dsstride = d.dsstride;
     a.I = d.I;
+    a.ebits = d.ebits;
     a.sgq = d.sgq;
     a.suq = d.suq;
     a.sdq = d.sdq;
@@ -1232,12 +1318,17 @@ hipError_t launch_decode(const DecLaunch &d, hipStream_t st)
     }
     auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(grid), dim3(DX_THREADS), 0, st, a, nunits); };
     const bool sh8 = d.sh_bits == 8;
-    if (d.E <= 64)
-        sh8 ? go(k_dec_expert<true, 1>) : go(k_dec_expert<false, 1>);
-    else if (d.E <= 128)
-        sh8 ? go(k_dec_expert<true, 2>) : go(k_dec_expert<false, 2>);
-    else
-        sh8 ? go(k_dec_expert<true, 4>) : go(k_dec_expert<false, 4>);
+    auto pick = [&](auto mixc) {
+        constexpr bool MX = decltype(mixc)::value;
+        if (d.E <= 64)
+            sh8 ? go(k_dec_expert<true, 1, MX>) : go(k_dec_expert<false, 1, MX>);
+        else if (d.E <= 128)
+            sh8 ? go(k_dec_expert<true, 2, MX>) : go(k_dec_expert<false, 2, MX>);
+        else
+            sh8 ? go(k_dec_expert<true, 4, MX>) : go(k_dec_expert<false, 4, MX>);
+    };
+    if (d.ebits) pick(std::true_type{});
+    else pick(std::false_type{});
     e = hipGetLastError();
     if (e == hipSuccess && d.ev1) e = hipEventRecord(d.ev1, st);
     if (e != hipSuccess || d.experts_only) return e;

@@ -103,7 +103,7 @@ int validate(const moe_shape *s)
     if ((s->flags & MOE_EXPERT_MIXED) && (s->flags & (MOE_ACT_Q8 | MOE_TEST_GATEUP_SUMS | MOE_EXPERT_INT8)))
         return MOE_ERR_UNSUPPORTED;
     if ((s->flags & MOE_REGIME_SMALL) &&
-        ((s->flags & (MOE_REGIME_TILED | MOE_ACT_Q8 | MOE_EXPERT_MIXED)) ||
+        ((s->flags & (MOE_REGIME_TILED | MOE_ACT_Q8)) ||
          !moe::decode_supported(s->H, s->E, s->top_k, s->I, s->I_shared, s->shared_bits)))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
@@ -137,7 +137,7 @@ constexpr int DEC_AUTO_MAX_T = 64;
 
 bool use_decode(const moe_shape *s)
 {
-    if (s->flags & (MOE_ACT_Q8 | MOE_EXPERT_MIXED | MOE_REGIME_TILED)) return false;  // the tiled kernels
+    if (s->flags & (MOE_ACT_Q8 | MOE_REGIME_TILED)) return false;  // the tiled kernels
     if (!moe::decode_supported(s->H, s->E, s->top_k, s->I, s->I_shared, s->shared_bits)) return false;
     return (s->flags & MOE_REGIME_SMALL) || s->T <= DEC_AUTO_MAX_T;
 }
@@ -604,6 +604,7 @@ int forward_impl(const moe_shape *s, const moe_weights *w, const moe_bf16 *hidde
         d.sstride = w->gate.qs_stride_floats;
         d.dsstride = w->down.qs_stride_floats;
         d.I = s->I;
+        d.ebits = ebits;
         if (s->shared_bits) {
             d.sgq = (const uint8_t *)w->sh_gate.q;
             d.suq = (const uint8_t *)w->sh_up.q;

@@ -54,6 +54,7 @@ struct DecLaunch {
     const float *gs, *us, *ds;
     int64_t qstride, dqstride, sstride, dsstride;
     int I;
+    const uint8_t *ebits;  // [E] each routed expert's format, 4 or 2 (packed int2); null: all int4
     const uint8_t *sgq, *suq, *sdq;
     const float *sgs, *sus, *sds;
     int Ish, sh_bits;

@@ -65,6 +65,7 @@ def good(moe, **kw):
     (dict(H=1152, flags=0x8000), -3),                   # ... on one it does not (H % 1024)
     (dict(flags=0x8000 | 0x4000), -3),                  # with MOE_REGIME_TILED
     (dict(flags=0x8000 | 0x1000), -3),                  # with MOE_ACT_Q8
+    (dict(flags=0x8000 | 0x2000), 0),                   # with MOE_EXPERT_MIXED (int2 experts widened in registers)
     (dict(E=256, top_k=8, n_group=8, topk_group=4, H=6144, I=2048, rsf=2.5), 0),
     (dict(flags=0x1000), 0),            # MOE_ACT_Q8
     (dict(flags=0x2000), 0),            # MOE_EXPERT_MIXED
@@ -77,12 +78,15 @@ def test_validation(moe, kw, code):
 
 def test_workspace_sizes(moe):
     s = good(moe)
-    # the int8-activation and mixed-format modes take the tiled layout (the
-    # Q8 one adds code and scale buffers)
+    # the int8-activation mode takes the tiled layout (with its code and
+    # scale buffers); the mixed-format mode takes the regime's own layout
     dec = moe.moe_workspace_bytes(s, moe.MOE_WS_LAYER)
     q8 = moe.moe_workspace_bytes(good(moe, flags=moe.MOE_ACT_Q8), moe.MOE_WS_LAYER)
     mixed = moe.moe_workspace_bytes(good(moe, flags=moe.MOE_EXPERT_MIXED), moe.MOE_WS_LAYER)
-    assert q8 > mixed > 0 and dec > 0 and mixed != dec
+    tiled = moe.moe_workspace_bytes(good(moe, flags=moe.MOE_REGIME_TILED), moe.MOE_WS_LAYER)
+    mixed_tiled = moe.moe_workspace_bytes(good(moe, flags=moe.MOE_EXPERT_MIXED | moe.MOE_REGIME_TILED),
+                                          moe.MOE_WS_LAYER)
+    assert q8 > tiled > 0 and dec > 0 and mixed == dec and mixed_tiled == tiled != dec
     assert moe.moe_workspace_bytes(s, moe.MOE_WS_LAYER) > 16 * 2 * 1024 * 4
     assert moe.moe_workspace_bytes(s, moe.MOE_WS_PERMUTE) > 0
     assert moe.moe_workspace_bytes(s, moe.MOE_WS_EXPERT_FFN) >= 32 * 512 * 2

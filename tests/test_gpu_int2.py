@@ -10,7 +10,7 @@ import pytest
 
 import int4_routed_expert_02_amd as moe
 import synth
-from gpu_util import check_output, check_routing, check_routing_top_p, run_layer, say, small_cfg
+from gpu_util import check_output, check_routing, check_routing_top_p, is_decode, run_layer, say, small_cfg
 
 pytestmark = pytest.mark.gpu
 
@@ -36,13 +36,20 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_mixed_int2_layer_parity(name):
+# every case in the regime the layer picks; the shapes the small-batch kernel
+# takes (T <= 64) also forced through the tiled kernels
+REGIMES = [(n, "auto") for n in CASES] + [(n, "tiled") for n, c in CASES.items() if is_decode(c)]
+
+
+@pytest.mark.parametrize("name,regime", REGIMES)
+def test_mixed_int2_layer_parity(name, regime):
     cfg = CASES[name]
     d = synth.layer(cfg)
-    got, ids, w, offsets, srt = run_layer(cfg, d)
+    flags = moe.MOE_OUT_F32 | (moe.MOE_REGIME_TILED if regime == "tiled" else 0)
+    got, ids, w, offsets, srt = run_layer(cfg, d, flags=flags)
+    assert (offsets is None) == (regime == "auto" and is_decode(cfg)), f"{name}: regime {regime} not taken"
     chk = check_routing_top_p if cfg.top_p else check_routing
-    ex = chk(cfg, d, d["hidden"], ids, w, offsets, srt, tag=f"int2 {name}")
+    ex = chk(cfg, d, d["hidden"], ids, w, offsets, srt, tag=f"int2 {name} {regime}")
     cold = np.isin(ids, np.nonzero(d["expert_bits"] == 2)[0])
     say(f"int2 {name}: {int(cold.sum())} of {ids.size} pairs on int2 experts")
     assert cold.any()
@@ -51,6 +58,52 @@ def test_mixed_int2_layer_parity(name):
         rng = np.random.default_rng(9)
         toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 48, replace=False)]))
     check_output(cfg, d, d["hidden"], got, ex, tokens=toks, tag=f"int2 {name}")
+
+
+def _int4_reencoding(cfg, d):
+    """The same layer with every int2 expert's codes stored as packed int4
+    (element 2c + i in nibble i of byte c, two's complement) and no format
+    array: the same weight values, all in the int4 format."""
+    H, I = cfg.H, cfg.I
+    mat = I * H // 2
+
+    def widen(b2, rows, cols):
+        b = b2.reshape(rows, cols // 4)
+        f = np.stack([(b >> (2 * j)) & 3 for j in range(4)], -1).reshape(rows, cols).astype(np.int8)
+        f[f >= 2] -= 4
+        n = (f.astype(np.uint8) & 0xF).reshape(rows, cols // 2, 2)
+        return (n[..., 0] | (n[..., 1] << 4)).astype(np.uint8).ravel()
+
+    q = d["experts_q"].copy()
+    for e in np.nonzero(d["expert_bits"] == 2)[0]:
+        src = d["experts_q"][e]
+        q[e, 0:mat] = widen(src[0:mat // 2], I, H)
+        q[e, mat:2 * mat] = widen(src[mat:mat + mat // 2], I, H)
+        q[e, 2 * mat:3 * mat] = widen(src[2 * mat:2 * mat + mat // 2], H, I)
+    d4 = {k: v for k, v in d.items() if k != "expert_bits"}
+    d4["experts_q"] = q
+    return cfg.with_(int2_frac=0.0), d4
+
+
+@pytest.mark.parametrize("T,frac", [(1, 1.0), (16, 0.25), (32, 1.0), (50, 0.5)])
+def test_small_batch_int2_equals_int4_reencoding(T, frac):
+    """The small-batch kernel widens an int2 expert's codes to int4 in
+    registers and runs the int4 body on them: the layer must give the same
+    bits as the same weights stored as int4 (T = 50: two chunks)."""
+    import torch
+    cfg = synth.CONFIGS["c0"].with_(T=T, seed=90 + T, int2_frac=frac)
+    assert is_decode(cfg)
+    d = synth.layer(cfg)
+    got, ids, _, offsets, _ = run_layer(cfg, d)
+    assert offsets is None, "the small-batch regime was not taken"
+    cfg4, d4 = _int4_reencoding(cfg, d)
+    ref, ids4, _, _, _ = run_layer(cfg4, d4)
+    assert np.array_equal(ids, ids4)
+    cold = np.isin(ids, np.nonzero(d["expert_bits"] == 2)[0])
+    say(f"int2 = int4 re-encoding, T={T}: {int(cold.sum())} of {ids.size} pairs on int2 experts")
+    assert cold.any()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
+        f"max diff {float(np.max(np.abs(got - ref)))}"
 
 
 def test_mixed_residual_bf16():

@@ -352,6 +352,8 @@ CHAIN_STACKS = {
     "c1": synth.CONFIGS["c1"],
     # an int8 shared expert: its units share the expert launch with the int4 routed ones
     "c4_int8_shared_T32": synth.CONFIGS["c4"].with_(T=32, layers=4, seed=37),
+    # a quarter of the routed experts in int2 (widened to int4 in the expert kernel)
+    "c1_int2_quarter": synth.CONFIGS["c1"].with_(layers=4, seed=38, int2_frac=0.25),
 }
 
 
