@@ -149,8 +149,8 @@ def main():
                 sys.exit("--act-q8 is a mode of the tiled configurations (c2, c3, c4)")
             cfg = cfg.with_(act_q8=True)
         if args.int2_frac:
-            if cfg.T <= 32:
-                sys.exit("--int2-frac is a mode of the tiled configurations (c2, c3, c4)")
+            if cfg.T <= 32 and cfg.layers == 1:
+                sys.exit("--int2-frac is a mode of the tiled configurations (c2, c3, c4) and of the c1 decode step")
             cfg = cfg.with_(int2_frac=args.int2_frac)
         return cfg
 
@@ -286,25 +286,30 @@ def bench_decode(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread):
     torch.cuda.synchronize()
     avg_ms = ea.elapsed_time(eb) / (args.roofline_reps * L)
 
-    n_act, p_kept = [], []
+    n_act, p_kept, act_w = [], [], []
     for l in range(L):
         pid, _, _, _ = moe.moe_layer_routing(moe.shape_of(cfg, T, flags), wss[l])
         base = wss[l].data_ptr()
         ids = wss[l][pid - base:pid - base + 4 * P].view(torch.int32).cpu().numpy()
-        n_act.append(int(np.unique(ids[ids >= 0]).size))  # (-1: a pair dropped by adaptive top-p)
+        act = np.unique(ids[ids >= 0])  # (-1: a pair dropped by adaptive top-p)
+        n_act.append(int(act.size))
         p_kept.append(int((ids >= 0).sum()))
+        # the chosen experts' rows in their own formats (int2 cold-tail experts: half the bytes) and f32 scales
+        eb = arrays[l].get("expert_bits")
+        bits = eb[act].astype(np.int64) if eb is not None else np.full(act.size, 4, dtype=np.int64)
+        act_w.append(int(np.sum(3 * cfg.I * H * bits // 8)) + int(act.size) * 4 * (2 * cfg.I + H))
     # algorithmic bytes of one expert-kernel launch: the weights (int4 rows and
     # f32 row scales) of every chosen routed expert and of the shared expert,
     # the activations and router logits read once, the layer output written
     # once (bf16)
     sh_w = (3 * cfg.I_sh * H * cfg.shared_bits // 8 + 4 * (2 * cfg.I_sh + H)) if cfg.shared_bits else 0
-    ex_bytes = [na * (3 * cfg.I * H // 2 + 4 * (2 * cfg.I + H)) + sh_w + 2 * T * H + 4 * T * cfg.E + 2 * T * H
-                for na in n_act]
+    ex_bytes = [aw + sh_w + 2 * T * H + 4 * T * cfg.E + 2 * T * H for aw in act_w]
     alg_per_launch = float(np.mean(ex_bytes))
     achieved = alg_per_launch / (avg_ms / 1e3) / 1e9  # GB/s
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("k_dec_expert_c1_traffic", ["decode.hip"]),
+                "traffic": (measured_traffic("k_dec_expert_c1_traffic", ["decode.hip"])
+                            if not cfg.int2_frac and not cfg.top_p else None),
                 "kernel": "k_dec_expert (fused gate/up/SwiGLU/down of the chosen and shared experts)",
                 "avg_launch_us": round(avg_ms * 1e3, 2), "alg_bytes_per_launch": int(alg_per_launch),
                 "launches_timed": args.roofline_reps * L, "active_experts_mean": round(float(np.mean(n_act)), 2)}
@@ -312,7 +317,7 @@ def bench_decode(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread):
     # step-level HBM fraction: algorithmic bytes of the whole step / step time
     step_bytes = 0
     for l in range(L):
-        step_bytes += n_act[l] * (3 * cfg.I * H // 2 + 4 * (2 * cfg.I + H))
+        step_bytes += act_w[l]
         if cfg.shared_bits:
             step_bytes += 3 * cfg.I_sh * H * cfg.shared_bits // 8 + 4 * (2 * cfg.I_sh + H)
         step_bytes += 4 * cfg.E * H + 4 * cfg.E + 2 * T * H * 2 + 8 * T * cfg.k
@@ -353,7 +358,8 @@ def bench_decode(args, cfg, moe, synth, torch, np, dev, cpu_s, one_thread):
         "data": "synthetic (seeded, random-init weights of the Colibri-Nano MoE layer shape)",
         "config": {"workload": cfg.name, "T": T, "layers": L, "H": H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
                    "I_shared": cfg.I_sh, "global_batch": T, "parallelism": "single GPU",
-                   "chained": "each layer's combine takes the next layer's router logits", "top_p": cfg.top_p},
+                   "chained": "each layer's combine takes the next layer's router logits", "top_p": cfg.top_p,
+                   "int2_frac": cfg.int2_frac},
         "step_hbm_GBs": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_alg_bytes": int(step_bytes),

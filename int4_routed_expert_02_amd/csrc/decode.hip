@@ -531,37 +531,30 @@ __device__ __forceinline__ void load_down(DownW<WBITS> &w, f32x4 &sd, const uint
 }
 
 // Int2 experts (element 4c + j of a row in bits 2j..2j+1 of byte c, two's
-// complement) run the int4 body on the same values: each 16-byte chunk of an
-// int4 row (32 values) is 8 bytes of the int2 row, loaded at half the width
-// and widened in registers to the int4 packing (element 2c + i in nibble i
-// of byte c): each 2-bit field spread to the low bits of its own nibble,
-// then its sign bit copied into the nibble's top two bits (-2..1 is the same
-// two's complement value in four bits).  Sixteen codes per 32-bit word.
-__device__ __forceinline__ u32x2 int2_to_int4x16(uint32_t w)
+// complement) run the int4 body's arithmetic: each 16-byte chunk of an int4
+// row (32 values) is 8 bytes of the int2 row, loaded at half the width, and
+// eight codes (a 16-bit field) unpack straight to the bit patterns the int4
+// unpacks give for the same values: 2^e + (code + 8), bf16 (HI = 0x4300) or
+// f16 (0x6400), in their k-slot order (e0,e4),(e1,e5),(e2,e6),(e3,e7).
+// t = w | w << 8 puts element j + 4 sixteen bits above element j; a field
+// XOR 2 is code + 2 (0..3), plus 6 is code + 8 (6..9).  So the products and
+// sums are those of the same weights stored as int4, bit for bit.
+template <uint32_t HI>
+__device__ __forceinline__ u32x4 unpack_int2x8_ks(uint32_t w)
 {
-    u32x2 r;
+    const uint32_t t = (w & 0xFFFFu) | ((w & 0xFFFFu) << 8);
+    u32x4 r;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint32_t x = (w >> (16 * h)) & 0xFFFFu;
-        x = (x | (x << 8)) & 0x00FF00FFu;
-        x = (x | (x << 4)) & 0x0F0F0F0Fu;
-        x = (x | (x << 2)) & 0x33333333u;
-        const uint32_t sgn = (x >> 1) & 0x11111111u;  // each field's sign bit, at bit 0 of its nibble
-        r[h] = x | (sgn << 2) | (sgn << 3);
-    }
+    for (int i = 0; i < 4; ++i)
+        r[i] = ((((t >> (2 * i)) & 0x00030003u) ^ 0x00020002u) + 0x00060006u) | (HI | (HI << 16));
     return r;
 }
 
-// the int4 chunk of 32 values from its 8-byte int2 form (or the chunk itself)
-__device__ __forceinline__ u32x4 int4_chunk(const u32x4 &c) { return c; }
-__device__ __forceinline__ u32x4 int4_chunk(const u32x2 &c)
-{
-    const u32x2 lo = int2_to_int4x16(c[0]), hi = int2_to_int4x16(c[1]);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
+// codes 8 wd .. 8 wd + 7 of a lane's 32 in an int2 chunk (two 32-bit words)
+__device__ __forceinline__ uint32_t int2_group(const u32x2 &c, int wd) { return c[wd >> 1] >> (16 * (wd & 1)); }
 
 // The down slice of an int2 expert: as load_down<4>, each tile's 32 values
-// in 8 bytes (rstride: bytes of an int2 row), widened where they are used.
+// in 8 bytes (rstride: bytes of an int2 row), unpacked where they are used.
 struct DownW2 {
     u32x2 d[DX_TILES];
 };
@@ -729,11 +722,16 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
                 asm volatile("" ::: "memory");  // keeps the compiler from sinking these loads to their use
             }
             if constexpr (WBITS == 4) {
-                const u32x4 cg = int4_chunk(wg[c]), cu = int4_chunk(wu[c]);
 #pragma unroll
                 for (int wd = 0; wd < 4; ++wd) {
-                    const u32x4 bg = unpack_int4x8(cg[wd]);
-                    const u32x4 bu = unpack_int4x8(cu[wd]);
+                    u32x4 bg, bu;
+                    if constexpr (I2) {
+                        bg = unpack_int2x8_ks<0x4300u>(int2_group(wg[c], wd));
+                        bu = unpack_int2x8_ks<0x4300u>(int2_group(wu[c], wd));
+                    } else {
+                        bg = unpack_int4x8(wg[c][wd]);
+                        bu = unpack_int4x8(wu[c][wd]);
+                    }
 #pragma unroll
                     for (int mb = 0; mb < NMB; ++mb) {
                         const u32x4 af = *(const u32x4 *)(ap[mb] + (4 * c + g) * 32 + 8 * wd);
@@ -807,13 +805,11 @@ __device__ __forceinline__ void expert_body(const DecArgs &a, DxSmem<WBITS> &sm,
 #pragma unroll
             for (int tt = 0; tt < DX_TILES; ++tt) {
                 f32x4 d = d0;
-                u32x4 q4 = {0u, 0u, 0u, 0u};  // the tile's int4 words (int4 and int2 experts)
-                if constexpr (I2) q4 = int4_chunk(dw.d[tt]);
-                else if constexpr (WBITS == 4) q4 = u32x4{dw.d[tt][0], dw.d[tt][1], dw.d[tt][2], dw.d[tt][3]};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     u32x4 b;
-                    if constexpr (WBITS == 4) b = unpack_int4x8_f16(q4[s]);
+                    if constexpr (I2) b = unpack_int2x8_ks<0x6400u>(int2_group(dw.d[tt], s));
+                    else if constexpr (WBITS == 4) b = unpack_int4x8_f16(dw.d[tt][s]);
                     else b = unpack_int8x8_f16(u32x2{dw.d[tt][2 * s], dw.d[tt][2 * s + 1]});
                     d = mfma_f16(fh[s], b, d);
                 }

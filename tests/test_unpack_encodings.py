@@ -126,3 +126,30 @@ def test_int2_forms_every_word():
                 r = (((t >> (4 * i)) & 0x00030003) ^ 0x00020002) | (hi | (hi << 16))
                 vals += [fn(r & 0xFFFF), fn(r >> 16)]
             assert vals == [float(c + off) for c in codes], hex(w)
+
+
+def test_int2_small_batch_form_matches_int4_bits():
+    """unpack_int2x8_ks (the small-batch kernel's int2 unpack): for every one
+    of the 65536 eight-code words, the same 32-bit words that unpack_int4x8
+    (bf16, 0x4300) and unpack_int4x8_f16 (0x6400) give for the same eight
+    values packed as int4 (nibble j = element j, two's complement), so an
+    int2 expert runs the int4 path's arithmetic bit for bit.  The k-slot
+    order pairs elements (i, i + 4); the int2 field of element j sits at
+    bits 2j..2j+1."""
+    for w in range(1 << 16):
+        t = w | (w << 8)
+        codes = [((w >> (2 * j)) & 3) - (4 if (w >> (2 * j)) & 2 else 0) for j in range(8)]
+        w4 = 0
+        for j, c in enumerate(codes):
+            w4 |= (c & 0xF) << (4 * j)
+        for hi in (0x4300, 0x6400):
+            h2 = hi | (hi << 16)
+            r2 = [((((t >> (2 * i)) & 0x00030003) ^ 0x00020002) + 0x00060006) | h2 for i in range(4)]
+            r4 = [(((w4 >> (4 * i)) ^ 0x00080008) & 0x000F000F) | h2 for i in range(4)]
+            assert r2 == r4, hex(w)
+        # and the int4 form is q + 136 in bf16, pair i = (element i, element i + 4)
+        vals = []
+        for i in range(4):
+            r = (((w4 >> (4 * i)) ^ 0x00080008) & 0x000F000F) | 0x43004300
+            vals += [bf16(r & 0xFFFF), bf16(r >> 16)]
+        assert vals == [float(codes[j] + 136) for i in range(4) for j in (i, i + 4)], hex(w)
