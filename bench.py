@@ -88,7 +88,7 @@ def parse():
     ap.add_argument("--act-q8", action="store_true",
                     help="Q8_0-style int8 activations for the expert matmuls (tiled configurations)")
     ap.add_argument("--int2-frac", type=float, default=0.0,
-                    help="fraction of routed experts stored as packed int2 (cold-tail experts; tiled configurations)")
+                    help="fraction of routed experts stored as packed int2 (cold-tail experts; the tiled configurations and the c1 decode step)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the headline's CPU-oracle sample")
     ap.add_argument("--cpu-seconds-extra", type=float, default=4.0,
                     help="budget of each other CPU-oracle sample (the extras and the one-thread runs)")
