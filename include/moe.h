@@ -93,8 +93,8 @@ extern "C" {
                                moe_expert_ffn and moe_layer_forward_chain return MOE_ERR_UNSUPPORTED */
 #define MOE_EXPERT_MIXED 0x2000u /* routed experts in int4 or int2 per weights->expert_bits, in both regimes
                                (the small-batch kernel loads an int2 expert's rows at half the bytes and
-                               unpacks them to the int4 path's operand bits); with MOE_ACT_Q8 or MOE_TEST_GATEUP_SUMS:
-                               MOE_ERR_UNSUPPORTED */
+                               unpacks them to the int4 path's operand bits); with MOE_ACT_Q8 or
+                               MOE_TEST_GATEUP_SUMS: MOE_ERR_UNSUPPORTED */
 #define MOE_REGIME_TILED 0x4000u /* moe_layer_forward(_profiled, _noalloc): take the tiled grouped-GEMM kernels at
                                any T (the small-batch weight-streaming kernels are otherwise chosen for
                                the shapes moe_layer_routing names); for measuring the two regimes side by
